@@ -1,0 +1,334 @@
+/*
+ * CPU oracle for the NVFP4 block-scaled fused-MoE layer.
+ *
+ * TEST INFRASTRUCTURE. Only tests/, __graft_entry__.smoke() and the
+ * cpu_baseline leg of bench.py may load or call this library. It shares no
+ * code, header, table or helper with the HIP path; both sides only share the
+ * seeded input generator in synth/.
+ *
+ * Plain, slow and written to be checked by eye: FP64 everywhere except the
+ * NVFP4 quantizer, whose result is a discrete encoding defined by binary32
+ * operations and is therefore evaluated in binary32. Nearest-value encoders
+ * are brute-force searches over every code, not bit tricks.
+ *
+ * Sources (the three web pages this method is described on):
+ *   [b12x]     "b12x" README (github local-inference-lab/b12x)
+ *   [vllm.cpp] "vllm.cpp docs/STATUS.md"
+ *   [megamoe]  "nvfp4-megamoe-kernel" compare page (pre-b1...master)
+ *
+ * Parity pins: every function below is pinned by a test in tests/test_oracle_*.py
+ * against something other than itself (hand tables, torch's float8 decoder,
+ * brute force, closed forms, textbook special cases). None is unpinned.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+int orc_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/* ------------------------------------------------------------------ decode */
+
+/* E2M1 (float4_e2m1fn) nibble: bit 3 sign, bits 2..0 magnitude code.
+ * [megamoe] README "NVFP4 throughout": weights are E2M1 packed two per byte
+ * (float4_e2m1fn_x2); archived CORRECTNESS_BACKLOG §7: FP4 max = 6.
+ * The eight magnitudes of the format are 0, 0.5, 1, 1.5, 2, 3, 4, 6. */
+static const double E2M1_MAG[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+double orc_e2m1(uint32_t nib) {
+  double m = E2M1_MAG[nib & 7u];
+  return (nib & 8u) ? -m : m;
+}
+
+/* E4M3fn (float8_e4m3fn) byte: 1 sign, 4 exponent (bias 7), 3 mantissa bits,
+ * no infinities, S.1111.111 is NaN, largest finite 448.
+ * [megamoe] README "NVFP4 throughout" (FP8 E4M3 block scales, one per
+ * 16-element microblock); archived CORRECTNESS_BACKLOG §7: E4M3 max = 448. */
+double orc_e4m3fn(uint32_t byte) {
+  uint32_t s = (byte >> 7) & 1u, e = (byte >> 3) & 15u, m = byte & 7u;
+  double v;
+  if (e == 15u && m == 7u) return NAN;
+  if (e == 0u)
+    v = ldexp((double)m, -9);                 /* subnormal: m/8 * 2^(1-7) */
+  else
+    v = ldexp(1.0 + (double)m / 8.0, (int)e - 7);
+  return s ? -v : v;
+}
+
+/* bfloat16 bit pattern -> value (the upper half of a binary32). */
+double orc_bf16(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+/* One NVFP4 weight element W[n][k] of an [N][K] projection, in the operand
+ * layout the pages use: packed [N][K/2] (element 2i in the low nibble of byte
+ * i, 2i+1 in the high nibble), block scales [N][K/16] (E4M3, block = 16
+ * consecutive k), one FP32 global scale for the projection.
+ * [vllm.cpp] capability table, GGUF loading row: the (weight_packed [N,K/2],
+ * weight_scale [N,K/16]) operand pair and a per-expert weight_scale_2;
+ * [megamoe] WALKING_BACK_SOME_QUANTS, "First: the CUDA illegal-memory-access":
+ * dequant = E2M1 value * weight_scale repeated over 16 columns * weight_scale_2;
+ * archived CORRECTNESS_BACKLOG §7: the weight global scale is weight_scale_2.
+ * The product of an E2M1 value, an E4M3 value and a binary32 is exact in FP64. */
+double orc_weight(const uint8_t* packed, const uint8_t* scales, float gs, int K, int n, int k) {
+  uint8_t byte = packed[(size_t)n * (K / 2) + k / 2];
+  uint32_t nib = (k & 1) ? (byte >> 4) : (byte & 15u);
+  return orc_e2m1(nib) * orc_e4m3fn(scales[(size_t)n * (K / 16) + k / 16]) * (double)gs;
+}
+
+/* --------------------------------------------------------------- quantizer */
+
+/* Nearest non-negative finite E4M3fn value to v >= 0, ties to the even code
+ * (the even mantissa), values >= 448 saturate to 448 (code 0x7E).
+ * Brute force over the 127 codes 0x00..0x7E. */
+static double E4M3_VALUE[0x7F];               /* decoded codes 0x00..0x7E */
+
+__attribute__((constructor)) static void orc_init_tables(void) {
+  for (uint32_t c = 0; c <= 0x7E; ++c) E4M3_VALUE[c] = orc_e4m3fn(c);
+}
+
+uint8_t orc_e4m3_encode(float v) {
+  if (!(v > 0.0f)) return 0;                  /* 0, -0 (and NaN, not produced) */
+  if (v >= 448.0f) return 0x7E;
+  uint32_t best = 0;
+  double bestd = (double)v;                   /* distance to code 0 (value 0) */
+  for (uint32_t c = 1; c <= 0x7E; ++c) {
+    double d = fabs(E4M3_VALUE[c] - (double)v);
+    if (d < bestd || (d == bestd && (c & 1u) == 0 && (best & 1u) == 1)) {
+      best = c;
+      bestd = d;
+    }
+  }
+  return (uint8_t)best;
+}
+
+/* Nearest E2M1 magnitude code (0..7) to r >= 0, ties to the even code,
+ * r > 6 saturates to 6 (code 7). Brute force over the 8 magnitudes. */
+uint8_t orc_e2m1_encode(float r) {
+  if (!(r > 0.0f)) return 0;
+  if (r >= 6.0f) return 7;
+  uint32_t best = 0;
+  double bestd = (double)r;
+  for (uint32_t c = 1; c < 8; ++c) {
+    double d = fabs(E2M1_MAG[c] - (double)r);
+    if (d < bestd || (d == bestd && (c & 1u) == 0 && (best & 1u) == 1)) {
+      best = c;
+      bestd = d;
+    }
+  }
+  return (uint8_t)best;
+}
+
+/* NVFP4 quantizer for rows[i][0..K), K a multiple of 16. Rows are grouped
+ * `rows_per_gs` at a time; each group shares one FP32 global scale (1 row per
+ * group for activations, all rows of a projection for a weight tensor).
+ *
+ * Global scale: [megamoe] archived CORRECTNESS_BACKLOG §7, "Runtime Activation
+ * Global Scale": gs = max|x| / (6.0 * 448.0), so that no block scale overflows
+ * E4M3. Block scales per 16 consecutive elements and E2M1 codes are the NVFP4
+ * format of README "NVFP4 throughout"; the order of binary32 operations below
+ * is the reading recorded with the design (the pages do not spell it out):
+ *   A   = max |x| over the group                       (exact)
+ *   gs  = A / 2688                                     (binary32 division)
+ *   a_b = max |x| over block b                         (exact)
+ *   s_b = gs == 0 ? 0 : E4M3_nearest(a_b / (6 * gs))   (binary32 mul, then div)
+ *   d_b = value(s_b) * gs                              (binary32 mul)
+ *   q_k = sign(x_k) | (d_b == 0 ? 0 : E2M1_nearest(|x_k| / d_b))
+ * Outputs: packed [rows][K/2] (even k in the low nibble), scales [rows][K/16],
+ * gs [rows / rows_per_gs]. */
+void orc_quantize(const float* x, int64_t rows, int K, int64_t rows_per_gs,
+                  uint8_t* packed, uint8_t* scales, float* gs_out) {
+  int64_t groups = rows / rows_per_gs;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t g = 0; g < groups; ++g) {
+    const float* xg = x + (size_t)g * rows_per_gs * K;
+    float A = 0.0f;
+    for (int64_t i = 0; i < rows_per_gs * K; ++i)
+      if (fabsf(xg[i]) > A) A = fabsf(xg[i]);
+    gs_out[g] = A / 2688.0f;
+  }
+#pragma omp parallel for schedule(static)
+  for (int64_t row = 0; row < rows; ++row) {
+    float gs = gs_out[row / rows_per_gs];
+    const float* xr = x + (size_t)row * K;
+    for (int b = 0; b < K / 16; ++b) {
+      float ab = 0.0f;
+      for (int j = 0; j < 16; ++j)
+        if (fabsf(xr[b * 16 + j]) > ab) ab = fabsf(xr[b * 16 + j]);
+      uint8_t s = 0;
+      if (gs != 0.0f) {
+        float six_gs = 6.0f * gs;
+        s = orc_e4m3_encode(ab / six_gs);
+      }
+      scales[(size_t)row * (K / 16) + b] = s;
+      float d = (float)orc_e4m3fn(s) * gs;
+      for (int j = 0; j < 16; ++j) {
+        int k = b * 16 + j;
+        float v = xr[k];
+        uint32_t code = signbit(v) ? 8u : 0u;
+        if (d != 0.0f) code |= orc_e2m1_encode(fabsf(v) / d);
+        uint8_t* p = &packed[(size_t)row * (K / 2) + k / 2];
+        if ((k & 1) == 0)
+          *p = (uint8_t)((*p & 0xF0u) | code);
+        else
+          *p = (uint8_t)((*p & 0x0Fu) | (code << 4));
+      }
+    }
+  }
+}
+
+/* ----------------------------------------------------------------- routing */
+
+/* Top-k routing of T tokens over E experts.
+ * Selection: experts ordered by FP32 logit, larger first, equal values broken
+ * by the lower expert index ([vllm.cpp] "DeepSeek-V4-Flash decode ds4-gap -
+ * Lever 3": argmax under the strict total order (value, lower index)); every
+ * token gets k distinct experts ([b12x] "DeepSeek V4 Flash 0731 MoE
+ * reproduction": no duplicate expert inside one token). ids[t][j] is the j-th
+ * pick. Comparison is numeric, so -0 and +0 tie.
+ * Weights, renormalised over the k picks ([b12x] "What's in here": routing
+ * scores kept in FP32 internally; [vllm.cpp] Lever 3 "exact renorm"):
+ *   score 0 (softmax): w_j = exp(l_j - l_max) / sum_i exp(l_i - l_max), i over picks
+ *   score 1 (sigmoid): w_j = sig(l_j) / sum_i sig(l_i),  sig(z) = 1/(1+exp(-z))
+ * ([vllm.cpp] capability table: sigmoid noaux_tc routers without the group step). */
+void orc_route(const float* logits, int T, int E, int k, int score, int32_t* ids, double* w) {
+  char* taken = (char*)malloc((size_t)E);
+  for (int t = 0; t < T; ++t) {
+    const float* l = logits + (size_t)t * E;
+    memset(taken, 0, (size_t)E);
+    for (int j = 0; j < k; ++j) {
+      int best = -1;
+      for (int e = 0; e < E; ++e)
+        if (!taken[e] && (best < 0 || l[e] > l[best])) best = e;
+      taken[best] = 1;
+      ids[(size_t)t * k + j] = best;
+    }
+    double sum = 0.0, v[1024];
+    for (int j = 0; j < k; ++j) {
+      double lj = (double)l[ids[(size_t)t * k + j]];
+      if (score == 0)
+        v[j] = exp(lj - (double)l[ids[(size_t)t * k]]);
+      else
+        v[j] = 1.0 / (1.0 + exp(-lj));
+      sum += v[j];
+    }
+    for (int j = 0; j < k; ++j) w[(size_t)t * k + j] = v[j] / sum;
+  }
+  free(taken);
+}
+
+/* Per-expert counts, exclusive-scan offsets (offsets[E] = T*k), and the
+ * expert-major permutation of the T*k (token, slot) pairs, tokens ascending
+ * inside an expert; entries are t*k + j. inv[t*k+j] is the position of that
+ * pair in perm. ([megamoe] CUDA_GRAPH_SYNC_INVENTORY: per-expert counts kept on
+ * device in a fixed-shape buffer, expert offsets as device tensors; [vllm.cpp]
+ * "Device-resident decode campaign": device topk_ids feed the grouped GEMM.) */
+void orc_plan(const int32_t* ids, int T, int E, int k, int32_t* counts, int32_t* offsets,
+              int32_t* perm, int32_t* inv) {
+  for (int e = 0; e < E; ++e) counts[e] = 0;
+  for (int64_t i = 0; i < (int64_t)T * k; ++i) counts[ids[i]]++;
+  offsets[0] = 0;
+  for (int e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
+  int64_t pos = 0;
+  for (int e = 0; e < E; ++e)
+    for (int t = 0; t < T; ++t)
+      for (int j = 0; j < k; ++j)
+        if (ids[(size_t)t * k + j] == e) {
+          perm[pos] = t * k + j;
+          inv[(size_t)t * k + j] = (int32_t)pos;
+          pos++;
+        }
+}
+
+/* ------------------------------------------------------------- expert FFN */
+
+typedef struct {
+  const uint8_t* w1_packed;  /* [G][2I][H/2]; rows 0..I-1 gate, I..2I-1 up */
+  const uint8_t* w1_scales;  /* [G][2I][H/16] */
+  const float* w1_gs;        /* [G] */
+  const uint8_t* w2_packed;  /* [G][H][I/2] */
+  const uint8_t* w2_scales;  /* [G][H][I/16] */
+  const float* w2_gs;        /* [G] */
+} orc_proj_set;
+
+/* One expert's SwiGLU MLP on one input row, FP64:
+ *   g_i = sum_k W1[i][k] x_k,  u_i = sum_k W1[I+i][k] x_k,
+ *   h_i = silu(g_i) * u_i = g_i / (1 + exp(-g_i)) * u_i,   y_n = sum_i W2[n][i] h_i.
+ * ([megamoe] README "MoE kernel": fused SwiGLU grouped GEMM for gate/up, then
+ * the down projection; [b12x] "What's in here": SiLU/SwiGLU activations.)
+ * Weights are decoded element by element with orc_weight. */
+void orc_expert_ffn(const orc_proj_set* P, int g, int H, int I, const double* x, double* y) {
+  size_t w1_pk = (size_t)2 * I * (H / 2), w1_sc = (size_t)2 * I * (H / 16);
+  size_t w2_pk = (size_t)H * (I / 2), w2_sc = (size_t)H * (I / 16);
+  const uint8_t* p1 = P->w1_packed + (size_t)g * w1_pk;
+  const uint8_t* s1 = P->w1_scales + (size_t)g * w1_sc;
+  const uint8_t* p2 = P->w2_packed + (size_t)g * w2_pk;
+  const uint8_t* s2 = P->w2_scales + (size_t)g * w2_sc;
+  double* h = (double*)malloc(sizeof(double) * (size_t)I);
+  for (int i = 0; i < I; ++i) {
+    double gi = 0.0, ui = 0.0;
+    for (int k = 0; k < H; ++k) {
+      gi += orc_weight(p1, s1, P->w1_gs[g], H, i, k) * x[k];
+      ui += orc_weight(p1, s1, P->w1_gs[g], H, I + i, k) * x[k];
+    }
+    h[i] = gi / (1.0 + exp(-gi)) * ui;
+  }
+  for (int n = 0; n < H; ++n) {
+    double yn = 0.0;
+    for (int i = 0; i < I; ++i) yn += orc_weight(p2, s2, P->w2_gs[g], I, n, i) * h[i];
+    y[n] = yn;
+  }
+  free(h);
+}
+
+/* Layer output for a list of tokens, FP64, never rounded:
+ *   out[t] = sum_j w[t][j] * FFN_{ids[t][j]}(x_t)   (+ FFN_shared(x_t), weight 1)
+ * ([vllm.cpp] "Device-resident decode campaign", MoeCombineKernel: the
+ * weighted sum of the expert outputs with topk_weights; [megamoe] archived
+ * CORRECTNESS_BACKLOG §6: an always-on shared expert beside the routed ones.)
+ * x: [n_tok][H] decoded inputs of the listed tokens; ids, w: [T][k] routing;
+ * out: [n_tok][H]. */
+void orc_moe_tokens(const orc_proj_set* routed, const orc_proj_set* shared, int num_shared,
+                    int H, int I, int k, int n_tok, const int32_t* tokens, const double* x,
+                    const int32_t* ids, const double* w, double* out) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int i = 0; i < n_tok; ++i) {
+    int t = tokens[i];
+    double* y = (double*)malloc(sizeof(double) * (size_t)H);
+    double* o = out + (size_t)i * H;
+    for (int n = 0; n < H; ++n) o[n] = 0.0;
+    for (int j = 0; j < k; ++j) {
+      orc_expert_ffn(routed, ids[(size_t)t * k + j], H, I, x + (size_t)i * H, y);
+      for (int n = 0; n < H; ++n) o[n] += w[(size_t)t * k + j] * y[n];
+    }
+    for (int s = 0; s < num_shared; ++s) {
+      orc_expert_ffn(shared, s, H, I, x + (size_t)i * H, y);
+      for (int n = 0; n < H; ++n) o[n] += y[n];
+    }
+    free(y);
+  }
+}
+
+/* Decoded NVFP4 activations: x[i][k] = E2M1(code) * E4M3(scale) * gs[i]. */
+void orc_dequant_rows(const uint8_t* packed, const uint8_t* scales, const float* gs,
+                      int64_t rows, int K, double* x) {
+  for (int64_t r = 0; r < rows; ++r)
+    for (int k = 0; k < K; ++k) x[(size_t)r * K + k] = orc_weight(packed, scales, gs[r], K, (int)r, k);
+}
+
+/* Decoded bf16 activations. */
+void orc_bf16_rows(const uint16_t* b, int64_t n, double* x) {
+  for (int64_t i = 0; i < n; ++i) x[i] = orc_bf16(b[i]);
+}

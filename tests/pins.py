@@ -1,0 +1,408 @@
+"""Pins for the CPU oracle: checks against things other than the oracle itself.
+
+Each ``pin_*`` function takes an ``oracle.Oracle`` instance and raises
+``AssertionError`` when the oracle disagrees with an independent source:
+hand tables from ``tests/golden/`` (constants the pages state), PyTorch's own
+float8_e4m3fn / bfloat16 decoders, numpy/scipy library routines (stable
+argsort, matmul, softmax, expit), brute force on tiny inputs, closed forms and
+invariants. ``tests/test_oracle_mutation.py`` plants mistakes in copies of
+``oracle.c`` and requires that some pin fails for each.
+"""
+from __future__ import annotations
+
+import math
+import os
+
+import numpy as np
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _read_golden(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line.split())
+    return rows
+
+
+# ------------------------------------------------------ independent decoders
+
+def e2m1_table() -> np.ndarray:
+    """E2M1 code -> value from the hand-written golden table."""
+    t = np.zeros(16)
+    for code, val in _read_golden("e2m1_codes.txt"):
+        t[int(code)] = float(val)
+    return t
+
+
+def e4m3_table_torch() -> np.ndarray:
+    """E4M3fn byte -> value via PyTorch's float8_e4m3fn decoder (NaN for 0x7F/0xFF)."""
+    b = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn)
+    return b.to(torch.float64).numpy()
+
+
+def e4m3_encode_torch(v: np.ndarray) -> np.ndarray:
+    """float32 -> E4M3fn byte by PyTorch's round-to-nearest-even conversion."""
+    t = torch.from_numpy(np.ascontiguousarray(v, np.float32))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def decode_nvfp4(packed: np.ndarray, scales: np.ndarray, gs) -> np.ndarray:
+    """[..., N, K/2] codes + [..., N, K/16] scales (+ scalar gs) -> FP64 [..., N, K]."""
+    e2 = e2m1_table()
+    e4 = e4m3_table_torch()
+    lo = e2[packed & 15]
+    hi = e2[packed >> 4]
+    q = np.stack([lo, hi], axis=-1).reshape(*packed.shape[:-1], packed.shape[-1] * 2)
+    s = np.repeat(e4[scales], 16, axis=-1)
+    return q * s * np.float64(gs)
+
+
+def bf16_to_f64(b: np.ndarray) -> np.ndarray:
+    t = torch.from_numpy(np.ascontiguousarray(b, np.uint16).view(np.int16)).view(torch.bfloat16)
+    return t.to(torch.float64).numpy()
+
+
+def silu(z):
+    return z / (1.0 + np.exp(-z))
+
+
+# ------------------------------------------------------------------ codecs
+
+def pin_e2m1_table(o):
+    t = e2m1_table()
+    for c in range(16):
+        assert o.e2m1(c) == t[c] and math.copysign(1, o.e2m1(c)) == math.copysign(1, t[c]), c
+
+
+def pin_e4m3_points(o):
+    for b, v in _read_golden("e4m3fn_points.txt"):
+        got = o.e4m3fn(int(b, 16))
+        if v == "nan":
+            assert math.isnan(got), b
+        else:
+            assert got == float(v) and math.copysign(1, got) == math.copysign(1, float(v)), (b, got, v)
+
+
+def pin_e4m3_exhaustive(o):
+    ref = e4m3_table_torch()
+    for b in range(256):
+        got = o.e4m3fn(b)
+        if math.isnan(ref[b]):
+            assert math.isnan(got), b
+        else:
+            assert got == ref[b], (b, got, ref[b])
+
+
+def pin_bf16(o):
+    rng = np.random.default_rng(5)
+    bits = rng.integers(0, 1 << 16, 4000, dtype=np.uint16)
+    bits = bits[(bits & 0x7F80) != 0x7F80]          # finite patterns
+    ref = bf16_to_f64(bits)
+    got = o.bf16_rows(bits)
+    assert np.array_equal(got, ref)
+
+
+def pin_weight_decode(o):
+    # nibble order by hand: byte 0x21 holds k=0 -> code 1 (0.5), k=1 -> code 2 (1.0)
+    packed = np.zeros((1, 8), np.uint8)
+    packed[0, 0] = 0x21
+    scales = np.full((1, 1), 0x38, np.uint8)      # E4M3 1.0
+    assert o.weight(packed, scales, 1.0, 0, 0) == 0.5
+    assert o.weight(packed, scales, 1.0, 0, 1) == 1.0
+    # random tensor vs the independent decoder
+    rng = np.random.default_rng(7)
+    N, K = 6, 64
+    packed = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    scales = rng.integers(0, 0x7F, (N, K // 16), dtype=np.uint8)  # finite, non-negative
+    gs = np.float32(0.0123)
+    ref = decode_nvfp4(packed, scales, gs)
+    for n in range(N):
+        for k in range(K):
+            assert o.weight(packed, scales, gs, n, k) == ref[n, k], (n, k)
+
+
+def pin_layout_sizes(o):
+    lim = {k: int(v) for k, v in _read_golden("nvfp4_limits.txt")}
+    x = np.linspace(-1, 1, 512, dtype=np.float32).reshape(1, 512)
+    p, s, g = o.quantize(x)
+    assert p.shape == (1, 512 // lim["packed_cols_div"]) and s.shape == (1, 512 // lim["scale_cols_div"])
+    assert p.nbytes + s.nbytes == lim["row512_bytes"]
+
+
+# --------------------------------------------------------------- encoders
+
+def pin_e4m3_encode(o):
+    lim = {k: int(v) for k, v in _read_golden("nvfp4_limits.txt")}
+    vals = e4m3_table_torch()[:0x7F]
+    pts = []
+    for a, b in zip(vals[:-1], vals[1:]):
+        mid = np.float32((a + b) / 2)
+        pts += [np.float32(a), mid, np.nextafter(mid, np.float32(0)), np.nextafter(mid, np.float32(1e9))]
+    rng = np.random.default_rng(11)
+    pts += list((np.exp(rng.uniform(math.log(1e-5), math.log(447.9), 3000))).astype(np.float32))
+    pts = np.array([p for p in pts if 0 < p < lim["e4m3_max"]], np.float32)
+    ref = e4m3_encode_torch(pts)
+    got = np.array([o.e4m3_encode(float(p)) for p in pts], np.uint8)
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, [(float(pts[i]), int(got[i]), int(ref[i])) for i in bad[:5]]
+    assert o.e4m3_encode(0.0) == 0
+    for v in (448.0, 460.0, 464.0, 1e30, float("inf")):
+        assert o.e4m3_encode(v) == 0x7E, v                # saturates to the E4M3 max
+    # survey example: 7.5 * 2^-9 is the midpoint of 0x07 and 0x08 -> even code 0x08
+    assert o.e4m3_encode(7.5 * 2 ** -9) == 0x08
+
+
+def pin_e2m1_encode(o):
+    for r, code in _read_golden("e2m1_rounding.txt"):
+        assert o.e2m1_encode(float(np.float32(float(r)))) == int(code), r
+
+
+# -------------------------------------------------------------- quantizer
+
+def quant_rows_fixture():
+    rng = np.random.default_rng(13)
+    rows = [rng.standard_normal(64).astype(np.float32) for _ in range(6)]
+    rows.append(np.zeros(64, np.float32))                          # all zero
+    r = np.zeros(64, np.float32); r[37] = -3.5; rows.append(r)      # one non-zero
+    r = np.full(64, -0.0, np.float32); r[5] = 1e-3; rows.append(r)  # negative zeros
+    rows.append((rng.standard_normal(64) * 1e4).astype(np.float32))  # large
+    rows.append((rng.standard_normal(64) * 1e-6).astype(np.float32))  # small
+    r = rng.standard_normal(64).astype(np.float32); r[:16] *= 1e-6; rows.append(r)  # underflowing block
+    return np.stack(rows)
+
+
+def pin_quantize(o):
+    lim = {k: int(v) for k, v in _read_golden("nvfp4_limits.txt")}
+    e2 = e2m1_table()
+    e4 = e4m3_table_torch()
+    x = quant_rows_fixture()
+    p, s, g = o.quantize(x, rows_per_gs=1)
+    for i, row in enumerate(x):
+        A = np.float32(np.max(np.abs(row)))
+        gs = A / np.float32(lim["gs_divisor"])                   # the page's formula, binary32
+        assert g[i] == gs, (i, g[i], gs)
+        codes = np.stack([p[i] & 15, p[i] >> 4], -1).reshape(-1)
+        for b in range(row.size // 16):
+            blk = row[16 * b:16 * b + 16]
+            ab = np.float32(np.max(np.abs(blk)))
+            if gs == 0:
+                exp_s = 0
+            else:
+                ratio = ab / (np.float32(6.0) * gs)
+                exp_s = 0x7E if ratio >= lim["e4m3_max"] else int(e4m3_encode_torch(np.array([ratio]))[0])
+            assert s[i, b] == exp_s, (i, b, s[i, b], exp_s)
+            d = np.float32(np.float32(e4[s[i, b]]) * gs)
+            for j in range(16):
+                v = blk[j]
+                c = int(codes[16 * b + j])
+                assert (c >> 3) == int(np.signbit(v)), (i, b, j)
+                if d == 0:
+                    assert (c & 7) == 0
+                    continue
+                r = np.float32(abs(v) / d)
+                # brute-force optimality of the magnitude code on the binary32 ratio, ties to even
+                dist = np.abs(e2[:8] - np.float64(r))
+                best = np.flatnonzero(dist == dist.min())
+                want = int(best[0]) if best.size == 1 else int([c_ for c_ in best if c_ % 2 == 0][0])
+                assert (c & 7) == want, (i, b, j, float(r), c & 7, want)
+    # the row maximum lands on the largest code with the largest scale
+    i = 0
+    k = int(np.argmax(np.abs(x[i])))
+    code = (p[i, k // 2] >> (4 * (k & 1))) & 7
+    assert s[i, k // 16] == 0x7E and code == 7
+
+
+def pin_quantize_error_bound(o):
+    """|x - x_hat| <= half the E2M1 spacing times d (no clipping inside the range)."""
+    rng = np.random.default_rng(17)
+    x = rng.standard_normal((4, 256)).astype(np.float32)
+    p, s, g = o.quantize(x)
+    xh = decode_nvfp4(p, s, 1.0) * g[:, None].astype(np.float64)
+    e4 = e4m3_table_torch()
+    d = np.repeat(e4[s] * g[:, None].astype(np.float64), 16, axis=1)
+    r = np.abs(x) / d
+    half = np.where(r <= 2, 0.25, np.where(r <= 4, 0.5, 1.0))
+    assert np.all(np.abs(x - xh) <= half * d * (1 + 1e-6))
+
+
+def pin_quantize_groups(o):
+    """rows_per_gs = N: one global scale for the whole matrix (per expert weight tensor)."""
+    rng = np.random.default_rng(19)
+    w = (rng.standard_normal((8, 32)) * 0.02).astype(np.float32)
+    p, s, g = o.quantize(w, rows_per_gs=8)
+    assert g.shape == (1,) and g[0] == np.float32(np.max(np.abs(w))) / np.float32(2688)
+    p1, s1, g1 = o.quantize(w, rows_per_gs=1)
+    assert np.all(g1 <= g[0]) and g1.max() == g[0]
+
+
+# ----------------------------------------------------------------- routing
+
+def route_fixture():
+    rng = np.random.default_rng(23)
+    l = rng.standard_normal((40, 16)).astype(np.float32)
+    l[0] = 0.25                                    # all equal -> ids 0..k-1
+    l[1] = np.round(l[1] * 4) / 4                  # many ties
+    l[2, :] = -1.0; l[2, 9] = 0.0; l[2, 3] = -0.0  # -0 == +0 -> lower index first
+    l[3] = np.round(l[3])
+    return l
+
+
+def pin_route_sort(o):
+    l = route_fixture()
+    for k in (1, 2, 5, 16):
+        ids, w = o.route(l, k, "softmax")
+        for t in range(l.shape[0]):
+            order = sorted(range(l.shape[1]), key=lambda e: (-float(l[t, e]), e))
+            assert list(ids[t]) == order[:k], (t, k, list(ids[t]), order[:k])
+    ids, _ = o.route(l, 4, "softmax")
+    assert list(ids[0]) == [0, 1, 2, 3]
+    assert list(ids[2][:2]) == [3, 9]
+
+
+def pin_route_softmax(o):
+    l = route_fixture()
+    ids, w = o.route(l, 16, "softmax")              # k = E: plain softmax over all experts
+    ref = torch.softmax(torch.from_numpy(l.astype(np.float64)), dim=1).numpy()
+    for t in range(l.shape[0]):
+        assert np.allclose(w[t], ref[t, ids[t]], rtol=1e-13, atol=0)
+    ids, w = o.route(l, 3, "softmax")
+    for t in range(l.shape[0]):
+        sel = l[t, ids[t]].astype(np.float64)
+        ref = torch.softmax(torch.from_numpy(sel), 0).numpy()
+        assert np.allclose(w[t], ref, rtol=1e-13, atol=0)
+        assert abs(w[t].sum() - 1) < 1e-14 and np.all(np.diff(w[t]) <= 0)
+    _, w1 = o.route(l, 1, "softmax")
+    assert np.all(w1 == 1.0)
+
+
+def pin_route_sigmoid(o):
+    from scipy.special import expit
+    l = route_fixture()
+    ids, w = o.route(l, 4, "sigmoid")
+    ids_s, _ = o.route(l, 4, "softmax")
+    assert np.array_equal(ids, ids_s)               # selection does not depend on the score
+    for t in range(l.shape[0]):
+        sg = expit(l[t, ids[t]].astype(np.float64))
+        assert np.allclose(w[t], sg / sg.sum(), rtol=1e-13, atol=0)
+        assert abs(w[t].sum() - 1) < 1e-14
+
+
+def pin_plan(o):
+    rng = np.random.default_rng(29)
+    l = rng.standard_normal((37, 12)).astype(np.float32)
+    ids, _ = o.route(l, 3, "softmax")
+    counts, offsets, perm, inv = o.plan(ids, 12)
+    flat = ids.reshape(-1)
+    assert np.array_equal(counts, np.bincount(flat, minlength=12))
+    assert np.array_equal(offsets, np.concatenate([[0], np.cumsum(counts)]))
+    assert np.array_equal(perm, np.argsort(flat, kind="stable"))
+    assert np.array_equal(inv, np.argsort(perm, kind="stable"))
+    assert counts.sum() == ids.size and all(len(set(r)) == 3 for r in ids)
+
+
+# -------------------------------------------------------------------- MLP
+
+def random_weights(rng, G, N, K, sigma=0.02):
+    """A small random NVFP4 projection set [G][N][K] via the oracle-independent route:
+    raw codes and scales drawn directly (finite, non-negative scales)."""
+    packed = rng.integers(0, 256, (G, N, K // 2), dtype=np.uint8)
+    scales = rng.integers(0x20, 0x48, (G, N, K // 16), dtype=np.uint8)
+    gs = (rng.uniform(0.5, 2.0, G) * sigma / 6).astype(np.float32)
+    return packed, scales, gs
+
+
+def pin_ffn_textbook(o):
+    """E=1, k=1: the textbook SwiGLU MLP W2 (silu(Wg x) * (Wu x)) with numpy matmuls."""
+    rng = np.random.default_rng(31)
+    H, I = 64, 32
+    W1 = random_weights(rng, 1, 2 * I, H)
+    W2 = random_weights(rng, 1, H, I)
+    x = rng.standard_normal(H)
+    y = o.expert_ffn(W1, W2, 0, x)
+    D1 = decode_nvfp4(W1[0][0], W1[1][0], W1[2][0])
+    D2 = decode_nvfp4(W2[0][0], W2[1][0], W2[2][0])
+    ref = D2 @ (silu(D1[:I] @ x) * (D1[I:] @ x))
+    assert np.allclose(y, ref, rtol=1e-12, atol=1e-15 * np.abs(ref).max())
+
+
+def pin_ffn_hand(o):
+    g = {k: float(v) for k, v in _read_golden("hand_ffn.txt")}
+    H, I = int(g["H"]), int(g["I"])
+    W1 = (np.full((1, 2 * I, H // 2), 0x22, np.uint8), np.full((1, 2 * I, H // 16), 0x38, np.uint8),
+          np.ones(1, np.float32))
+    W2 = (np.full((1, H, I // 2), 0x22, np.uint8), np.full((1, H, I // 16), 0x38, np.uint8),
+          np.ones(1, np.float32))
+    y = o.expert_ffn(W1, W2, 0, np.ones(H))
+    assert np.allclose(y, g["y"], rtol=1e-14, atol=0)
+
+
+def moe_small(rng, T=12, H=32, I=16, E=6, k=2, shared=0):
+    W1 = random_weights(rng, E, 2 * I, H)
+    W2 = random_weights(rng, E, H, I)
+    WS1 = random_weights(rng, shared, 2 * I, H) if shared else None
+    WS2 = random_weights(rng, shared, H, I) if shared else None
+    x = rng.standard_normal((T, H))
+    l = rng.standard_normal((T, E)).astype(np.float32)
+    return W1, W2, WS1, WS2, x, l
+
+
+def pin_moe_dense(o):
+    """All experts on every token with a dense gate matrix (zeros off-route):
+    out = sum_e G[t, e] * MLP_e(x_t) (+ shared), by numpy matmuls."""
+    rng = np.random.default_rng(37)
+    for score, shared in (("softmax", 0), ("sigmoid", 1)):
+        T, H, I, E, k = 12, 32, 16, 6, 2
+        W1, W2, WS1, WS2, x, l = moe_small(rng, T, H, I, E, k, shared)
+        ids, w = o.route(l, k, score)
+        out = o.moe_tokens(W1, W2, WS1, WS2, np.arange(T), x, ids, w)
+        G = np.zeros((T, E))
+        for t in range(T):
+            G[t, ids[t]] = w[t]
+        ref = np.zeros((T, H))
+        for e in range(E):
+            D1 = decode_nvfp4(W1[0][e], W1[1][e], W1[2][e])
+            D2 = decode_nvfp4(W2[0][e], W2[1][e], W2[2][e])
+            Y = (silu(x @ D1[:I].T) * (x @ D1[I:].T)) @ D2.T
+            ref += G[:, e:e + 1] * Y
+        for s in range(shared):
+            D1 = decode_nvfp4(WS1[0][s], WS1[1][s], WS1[2][s])
+            D2 = decode_nvfp4(WS2[0][s], WS2[1][s], WS2[2][s])
+            ref += (silu(x @ D1[:I].T) * (x @ D1[I:].T)) @ D2.T
+        assert np.allclose(out, ref, rtol=1e-11, atol=1e-13 * np.abs(ref).max())
+
+
+def pin_moe_invariance(o):
+    """Expert relabelling and token subsets do not change a token's output."""
+    rng = np.random.default_rng(41)
+    T, H, I, E, k = 10, 32, 16, 6, 3
+    W1, W2, _, _, x, l = moe_small(rng, T, H, I, E, k)
+    ids, w = o.route(l, k, "softmax")
+    out = o.moe_tokens(W1, W2, None, None, np.arange(T), x, ids, w)
+    P = rng.permutation(E)                       # new label P[e] for old expert e
+    W1p = tuple(a[np.argsort(P)] for a in W1)
+    W2p = tuple(a[np.argsort(P)] for a in W2)
+    lp = np.empty_like(l)
+    lp[:, P] = l
+    ids_p, w_p = o.route(lp, k, "softmax")
+    out_p = o.moe_tokens(W1p, W2p, None, None, np.arange(T), x, ids_p, w_p)
+    assert np.allclose(out, out_p, rtol=1e-13, atol=1e-15)
+    sub = np.array([7, 2])
+    out_s = o.moe_tokens(W1, W2, None, None, sub, x[sub], ids, w)
+    assert np.array_equal(out_s, out[sub])
+
+
+def pin_dequant_rows(o):
+    rng = np.random.default_rng(43)
+    x = rng.standard_normal((5, 64)).astype(np.float32)
+    p, s, g = o.quantize(x)
+    got = o.dequant_rows(p, s, g)
+    ref = decode_nvfp4(p, s, 1.0) * g[:, None].astype(np.float64)
+    assert np.array_equal(got, ref)
+
+
+ALL_PINS = [v for k, v in dict(globals()).items() if k.startswith("pin_")]

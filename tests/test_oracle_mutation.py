@@ -1,0 +1,64 @@
+"""Plant mistakes in copies of oracle.c (on the CPU) and require that the pins catch each.
+
+A pin that cannot tell a plausible mistake from the right answer pins nothing;
+this is the check that the pins in tests/pins.py have teeth. Every planted
+snippet must occur exactly once in oracle.c, so this test fails loudly if the
+oracle source drifts away from the mutation list.
+"""
+import os
+
+import pytest
+
+import pins
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "oracle.c")
+
+MUTANTS = {
+    "nibble_order": ("uint32_t nib = (k & 1) ? (byte >> 4) : (byte & 15u);",
+                     "uint32_t nib = (k & 1) ? (byte & 15u) : (byte >> 4);"),
+    "scale_index": ("scales[(size_t)n * (K / 16) + k / 16]", "scales[(size_t)n * (K / 16) + (k + 1) / 16 % (K / 16)]"),
+    "e4m3_bias": ("ldexp(1.0 + (double)m / 8.0, (int)e - 7)", "ldexp(1.0 + (double)m / 8.0, (int)e - 8)"),
+    "e4m3_subnormal": ("ldexp((double)m, -9)", "ldexp((double)m, -10)"),
+    "e2m1_table": ("{0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0}", "{0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 5.0}"),
+    "tie_to_higher_id": ("(best < 0 || l[e] > l[best])", "(best < 0 || l[e] >= l[best])"),
+    "sigmoid_sign": ("v[j] = 1.0 / (1.0 + exp(-lj));", "v[j] = 1.0 / (1.0 + exp(lj));"),
+    "perm_tokens_descending": ("for (int e = 0; e < E; ++e)\n    for (int t = 0; t < T; ++t)",
+                               "for (int e = 0; e < E; ++e)\n    for (int t = T - 1; t >= 0; --t)"),
+    "gate_up_swapped": ("gi += orc_weight(p1, s1, P->w1_gs[g], H, i, k) * x[k];",
+                        "gi += orc_weight(p1, s1, P->w1_gs[g], H, I + i, k) * x[k];"),
+    "silu_dropped": ("h[i] = gi / (1.0 + exp(-gi)) * ui;", "h[i] = gi * ui;"),
+    "combine_unweighted": ("o[n] += w[(size_t)t * k + j] * y[n];", "o[n] += y[n] / k;"),
+    "shared_weight_half": ("      for (int n = 0; n < H; ++n) o[n] += y[n];",
+                           "      for (int n = 0; n < H; ++n) o[n] += 0.5 * y[n];"),
+    "gs_divisor": ("gs_out[g] = A / 2688.0f;", "gs_out[g] = A / 2687.0f;"),
+    "block_scale_factor": ("float six_gs = 6.0f * gs;", "float six_gs = 4.0f * gs;"),
+    "quant_sign_lost": ("uint32_t code = signbit(v) ? 8u : 0u;", "uint32_t code = 0u;"),
+    "e4m3_ties_odd": ("if (d < bestd || (d == bestd && (c & 1u) == 0 && (best & 1u) == 1)) {\n      best = c;\n      bestd = d;\n    }\n  }\n  return (uint8_t)best;\n}\n\n/* Nearest E2M1",
+                      "if (d < bestd || (d == bestd && (c & 1u) == 1)) {\n      best = c;\n      bestd = d;\n    }\n  }\n  return (uint8_t)best;\n}\n\n/* Nearest E2M1"),
+}
+
+
+@pytest.fixture(scope="module")
+def source():
+    with open(SRC) as f:
+        return f.read()
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, source, tmp_path):
+    import oracle
+    import oracle.build
+    old, new = MUTANTS[name]
+    assert source.count(old) == 1, f"mutation site for {name} not found exactly once"
+    src = tmp_path / "oracle_mut.c"
+    src.write_text(source.replace(old, new))
+    lib = oracle.build.build(str(src), str(tmp_path / "liboracle_mut.so"))
+    mutant = oracle.Oracle(lib)
+    failed = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(mutant)
+        except AssertionError:
+            failed.append(pin.__name__)
+    assert failed, f"no pin catches the planted mistake {name}"
