@@ -1,0 +1,258 @@
+"""Benchmark of the NVFP4 block-scaled fused-MoE layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Default workload: the Qwen3-30B-A3B-shaped decode layer (H=2048, I=768, E=128,
+top-8, NVFP4 weights, BF16 activations). One step runs the whole layer once for
+each decode batch T in {1, 8, 32, 64} (105 tokens), each batch with its own
+seeded weights, inputs and logits, so the 1.36 GB of weights the step streams
+exceed the 256 MB Infinity Cache. Inputs are resident in HBM before timing;
+W warmup steps, then exactly K timed steps between two device synchronisations.
+
+Prints one JSON line: tokens/s of the whole step (value), plus
+  roofline:     the dominant kernel (the gate/up grouped GEMM) timed with HIP
+                events recorded on its launch stream over K further steps:
+                algorithmic bytes per launch / mean launch time vs 8 TB/s HBM
+                (decode) or algorithmic FLOPs / time vs 2.5 PFLOP/s bf16 MFMA
+                (prefill workloads);
+  cpu_baseline: the CPU oracle (FP64, OpenMP) on a bounded sample of the same
+                workload, on this host's cores.
+Other workloads (--workload qwen3-30b-a3b-prefill | deepseek-v3 | skewed-w4a4 |
+tiny) print the same line for that configuration.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+import synth  # noqa: E402
+import nvfp4_block_scaled_router_amd as m  # noqa: E402
+from nvfp4_block_scaled_router_amd.weights import quantize_projection  # noqa: E402
+
+METRIC = "NVFP4 fused-MoE tokens/s; decode HBM GB/s and prefill TFLOP/s vs peak"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+NVFP4_BYTES_PER_WEIGHT = 0.5 + 1.0 / 16.0      # E2M1 nibble + one E4M3 byte per 16
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def workload(name):
+    if name == "qwen3-30b-a3b-decode":
+        return [synth.qwen3_decode(T) for T in synth.DECODE_TOKENS], "hbm"
+    if name == "qwen3-30b-a3b-prefill":
+        return [synth.qwen3_prefill()], "mfma"
+    if name == "deepseek-v3":
+        return [synth.deepseek_v3()], "mfma"
+    if name == "skewed-w4a4":
+        return [synth.skewed_w4a4()], "hbm"
+    if name == "tiny":
+        return [synth.tiny()], "hbm"
+    raise SystemExit(f"unknown workload {name}")
+
+
+class Batch:
+    """One configuration resident on the GPU: packed weights, inputs, routing info."""
+
+    def __init__(self, cfg, dev):
+        self.cfg = cfg
+        log(f"[bench] preparing {cfg.name}: T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} k={cfg.k}")
+        projs = ["w1", "w2"] + (["ws1", "ws2"] if cfg.shared else [])
+        W = []
+        for w in projs:
+            G = cfg.shared if w.startswith("ws") else cfg.E
+            N, K = (2 * cfg.I, cfg.H) if w in ("w1", "ws1") else (cfg.H, cfg.I)
+            W.append(quantize_projection(G, N, K, lambda e0, c, w=w: synth.expert_weights_f32(cfg, w, e0, c), dev))
+        self.layer = m.MoeLayer.from_config(cfg, device=dev)
+        self.layer.pack(W[0], W[1], W[2] if cfg.shared else None, W[3] if cfg.shared else None)
+        del W
+        x = synth.activations(cfg)
+        self.x = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+        self.logits = torch.from_numpy(synth.logits(cfg)).to(dev)
+        self.out = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device=dev)
+        bufs, rout = self.layer.routing_buffers(cfg.T)
+        self.layer(self.x, self.logits, out=self.out, routing=rout)
+        torch.cuda.synchronize()
+        counts = bufs["expert_counts"].cpu().numpy()
+        self.touched = int((counts > 0).sum())
+        self.rows = cfg.T * cfg.k
+        torch.cuda.synchronize()
+
+    def run(self):
+        self.layer(self.x, self.logits, out=self.out)
+
+    def run_timed(self, events):
+        L = self.layer
+        m.moe_run_timed(L.plan, L.packed, self.cfg.T, self.x, self.logits, self.out, None, L.workspace,
+                        L.workspace_bytes, None, events)
+
+    # algorithmic work of the gate/up launch (the dominant kernel) and of the layer
+    def gate_up_bytes(self):
+        c = self.cfg
+        w = self.touched * (2 * c.I * c.H * NVFP4_BYTES_PER_WEIGHT + 4) + c.shared * (2 * c.I * c.H * NVFP4_BYTES_PER_WEIGHT + 4)
+        act = c.T * c.H * (2 if c.act == "bf16" else NVFP4_BYTES_PER_WEIGHT + 4.0 / c.H)
+        h = (self.rows + c.shared * c.T) * c.I * 2
+        return w + act + h
+
+    def gate_up_flops(self):
+        c = self.cfg
+        return 2.0 * (self.rows + c.shared * c.T) * 2 * c.I * c.H
+
+    def layer_bytes(self):
+        c = self.cfg
+        w = (self.touched + c.shared) * 3 * c.I * c.H * NVFP4_BYTES_PER_WEIGHT
+        return w + c.T * c.H * 2 + c.T * c.E * 4 + c.T * c.H * 2
+
+    def layer_flops(self):
+        c = self.cfg
+        return 6.0 * (self.rows + c.shared * c.T) * c.I * c.H
+
+
+def cpu_baseline(cfgs, budget_s=6.0):
+    """The CPU oracle, untouched, on a bounded sample: the largest decode batch of the
+    workload (or 16 tokens of a prefill workload), repeated until budget_s has passed."""
+    import oracle
+    import oracle.moe as omoe
+    o = oracle.default()
+    cfg = max(cfgs, key=lambda c: c.T)
+    tokens = np.arange(cfg.T, dtype=np.int32) if cfg.T <= 64 else synth.token_sample(cfg, 16)
+    logits = synth.logits(cfg)
+    ids, _ = o.route(logits, cfg.k, cfg.score)
+    need = sorted(set(ids[tokens].reshape(-1).tolist()))
+    log(f"[bench] cpu baseline: quantising {len(need)} experts for the oracle (untimed)")
+    W1 = omoe.quantized_weights(cfg, "w1", need)
+    W2 = omoe.quantized_weights(cfg, "w2", need)
+    WS1 = omoe.quantized_weights(cfg, "ws1") if cfg.shared else None
+    WS2 = omoe.quantized_weights(cfg, "ws2") if cfg.shared else None
+    x = synth.activations(cfg)
+    n_tok, t0, reps = 0, time.perf_counter(), 0
+    while True:
+        omoe.forward(cfg, x, logits, W1, W2, WS1, WS2, tokens=tokens, o=o)
+        n_tok += len(tokens)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {"value": n_tok / el, "unit": "tokens/s", "cores": min(o.threads(), len(tokens)), "kind": "oracle",
+            "sample": f"{cfg.name}: {len(tokens)} tokens (routing, {'activation quantisation, ' if cfg.act == 'nvfp4' else ''}"
+                      f"FP64 expert MLPs of their {cfg.k} experts, combine) x {reps} repeats, {el:.1f} s; "
+                      f"weight quantisation untimed"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="qwen3-30b-a3b-decode")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run one 1 GiB device copy (counter calibration for --pmc runs)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the layer has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    cfgs, bound = workload(args.workload)
+    batches = [Batch(c, dev) for c in cfgs]
+
+    if args.copy_probe:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    for _ in range(args.warmup):
+        for b in batches:
+            b.run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for b in batches:
+            b.run()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / args.steps
+    tokens = sum(c.T for c in cfgs)
+    value = tokens / (ms / 1e3)
+
+    # dominant kernel: gate/up GEMM, timed by HIP events recorded on its launch stream
+    # (moe_run_timed records them around each stage on the stream moe_run uses)
+    stage_tot = {b.cfg.name: [0.0] * m.MOE_NUM_STAGES for b in batches}
+    all_ev = {b.cfg.name: [torch.cuda.Event(enable_timing=True) for _ in range(2 * m.MOE_NUM_STAGES)]
+              for b in batches}
+    for ev in all_ev.values():                  # materialise the HIP events before handing them over
+        for e in ev:
+            e.record()
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        for b in batches:
+            ev = all_ev[b.cfg.name]
+            b.run_timed([e.cuda_event for e in ev])
+        torch.cuda.synchronize()
+        for b in batches:
+            ev = all_ev[b.cfg.name]
+            for s in range(m.MOE_NUM_STAGES):
+                if s == m.MOE_STAGE_QUANT and b.cfg.act != "nvfp4":
+                    continue
+                stage_tot[b.cfg.name][s] += ev[2 * s].elapsed_time(ev[2 * s + 1])
+    per_launch = {n: [t / args.steps for t in v] for n, v in stage_tot.items()}
+    gu_time = sum(v[m.MOE_STAGE_GATE_UP] for v in per_launch.values())          # ms per step
+    if bound == "hbm":
+        work = sum(b.gate_up_bytes() for b in batches)
+        achieved = work / (gu_time / 1e3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": None}
+    else:
+        work = sum(b.gate_up_flops() for b in batches)
+        achieved = work / (gu_time / 1e3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None}
+    roof["kernel"] = "gate_up grouped GEMM (+SwiGLU)"
+    roof["launch_ms"] = gu_time / len(batches)
+
+    layer_bytes = sum(b.layer_bytes() for b in batches)
+    layer_flops = sum(b.layer_flops() for b in batches)
+    detail = {}
+    for b in batches:
+        st = per_launch[b.cfg.name]
+        detail[b.cfg.name] = {
+            "T": b.cfg.T, "touched_experts": b.touched,
+            "stage_ms": {m.STAGE_NAMES[s]: round(st[s], 5) for s in range(m.MOE_NUM_STAGES)},
+            "gate_up_GBps": b.gate_up_bytes() / (st[m.MOE_STAGE_GATE_UP] / 1e3) / 1e9,
+            "gate_up_TFLOPs": b.gate_up_flops() / (st[m.MOE_STAGE_GATE_UP] / 1e3) / 1e12,
+        }
+
+    res = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": args.workload, "T": [c.T for c in cfgs], "H": cfgs[0].H, "I": cfgs[0].I,
+                   "E": cfgs[0].E, "top_k": cfgs[0].k, "score": cfgs[0].score, "shared": cfgs[0].shared,
+                   "activations": cfgs[0].act, "weights": "nvfp4 e2m1 + e4m3/16 + fp32 per expert"},
+        "layer_GBps": layer_bytes / (ms / 1e3) / 1e9,
+        "layer_TFLOPs": layer_flops / (ms / 1e3) / 1e12,
+        "roofline": roof,
+        "per_batch": detail,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(cfgs)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

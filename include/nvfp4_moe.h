@@ -1,0 +1,242 @@
+/*
+ * nvfp4_moe.h — C ABI of libnvfp4moe.so, an NVFP4 block-scaled fused
+ * mixture-of-experts layer for AMD Instinct MI355X (gfx950).
+ *
+ * The layer (all steps run as HIP kernels on the caller's stream):
+ *   1. route: top-k of the FP32 router logits under (value desc, expert id asc),
+ *      weights renormalised over the k picks (softmax or sigmoid scores);
+ *   2. per-expert counts, exclusive-scan offsets, stable expert-major permutation;
+ *   3. optional (W4A4) NVFP4 row quantisation of the activations;
+ *   4. grouped gate/up GEMM over E2M1 weights with per-16 E4M3 block scales and an
+ *      FP32 per-expert global scale, fused SwiGLU (silu(gate) * up) epilogue;
+ *   5. grouped down GEMM;
+ *   6. weighted combine of the k expert outputs (+ an always-on shared expert).
+ *
+ * Sources (web pages the method is described on):
+ *   [b12x]     "b12x" README (github local-inference-lab/b12x)
+ *   [vllm.cpp] "vllm.cpp docs/STATUS.md"
+ *   [megamoe]  "nvfp4-megamoe-kernel" compare page (pre-b1...master)
+ *
+ * Conventions for every entry point:
+ *   - Device pointers are HIP device (or managed) memory allocated and owned
+ *     by the caller; the library allocates no device memory and keeps no
+ *     device pointer between calls. Host pointers are marked "host".
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Calls enqueue work and return; none synchronises or reads device memory
+ *     on the host, so a call sequence with fixed pointers can be captured in a
+ *     HIP graph. (Graph-safety rule of [megamoe] GETTING_CUDAGRAPH_READY: no
+ *     host branch on a device value.)
+ *   - Return codes ([megamoe] dsv4/kernels/attention/fmha_mixed_fp8_capi.cu:
+ *     the launcher returns a negative code for a rejected shape, else the
+ *     CUDA error; the Python wrapper raises on non-zero):
+ *       0  enqueued
+ *      <0  rejected on the host before anything was enqueued (MOE_ERR_*)
+ *      >0  the hipError_t reported right after the enqueue
+ *   - No call falls back to another path ([megamoe] fmha_mixed_fp8_op.py:
+ *     hard error only).
+ *   - Results are bit-identical across repeated calls: no floating-point
+ *     atomics, fixed reduction orders.
+ */
+#ifndef NVFP4_MOE_H
+#define NVFP4_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Bumped on any change of a struct layout or of an entry point's contract
+ * ([vllm.cpp] capability table: a versioned C ABI). */
+#define MOE_ABI_VERSION 1u
+
+#define MOE_OK 0
+#define MOE_ERR_NULL (-1)      /* a required pointer is NULL */
+#define MOE_ERR_SHAPE (-2)     /* unsupported shape or descriptor field */
+#define MOE_ERR_SIZE (-3)      /* packed or workspace buffer too small */
+#define MOE_ERR_TOKENS (-4)    /* T < 0 or T > max_tokens */
+#define MOE_ERR_ALIGN (-5)     /* a device pointer is not 16-byte aligned */
+#define MOE_ERR_ABI (-6)       /* desc->abi_version != MOE_ABI_VERSION */
+#define MOE_ERR_ENUM (-7)      /* invalid enum value */
+#define MOE_ERR_WEIGHT (-8)    /* invalid weight data (host validation) */
+
+/* Router score ([b12x] "What's in here": routing scores kept in FP32;
+ * [vllm.cpp] capability table: sigmoid noaux_tc routers, ungrouped). */
+#define MOE_SCORE_SOFTMAX 0
+#define MOE_SCORE_SIGMOID 1
+
+/* Gate/up activation format ([b12x] "What's in here", moe: W4A16 = BF16
+ * activations with inline FP4 weight dequant; [megamoe] FINAL_STRETCH B0:
+ * expert weights and activations both float4_e2m1fn_x2 = W4A4). */
+#define MOE_ACT_BF16 0
+#define MOE_ACT_NVFP4_ROWQ 1
+
+/* Layer descriptor. Limits: hidden and inter multiples of 128 (hidden <= 16384,
+ * inter <= 16384), 1 <= top_k <= min(64, num_experts), num_experts <= 1024,
+ * 1 <= max_tokens <= 65536, renormalize == 1, num_shared in {0, 1}. */
+typedef struct {
+  uint32_t abi_version;     /* MOE_ABI_VERSION */
+  int32_t hidden;           /* H */
+  int32_t inter;            /* I, per expert (the shared expert uses the same I) */
+  int32_t num_experts;      /* E routed experts */
+  int32_t top_k;            /* k experts per token */
+  int32_t max_tokens;       /* T_max: capacity the workspace is sized for */
+  int32_t score_fn;         /* MOE_SCORE_* */
+  int32_t renormalize;      /* must be 1: weights renormalised over the k picks */
+  int32_t act_format;       /* MOE_ACT_* */
+  int32_t num_shared;       /* 0 or 1 always-on shared expert, weight 1.0 */
+} moe_desc;
+
+/* Opaque plan: host memory, immutable after moe_plan, safe to share between
+ * threads. Concurrent moe_run calls need distinct workspaces. */
+typedef struct moe_plan moe_plan_t;
+
+/* One NVFP4 projection of G experts in the pages' operand layout ([vllm.cpp]
+ * capability table, GGUF loading row: weight_packed [N,K/2] + weight_scale
+ * [N,K/16] + per-expert weight_scale_2; [megamoe] archived CORRECTNESS_BACKLOG
+ * §7: the weight global scale is weight_scale_2). Device pointers:
+ *   packed       u8  [G][N][K/2]   E2M1 codes, element 2i in the low nibble of
+ *                                  byte i, 2i+1 in the high nibble
+ *   scales       u8  [G][N][K/16]  E4M3fn block scales, block = 16 consecutive k
+ *   global_scale f32 [G]           per-expert global scale
+ * W[g][n][k] = E2M1(code) * E4M3(scale[g][n][k/16]) * global_scale[g].
+ * gate_up: N = 2I, K = H, rows 0..I-1 are the gate, rows I..2I-1 the up
+ * projection; down: N = H, K = I. */
+typedef struct {
+  const uint8_t* packed;
+  const uint8_t* scales;
+  const float* global_scale;
+} moe_nvfp4_tensor;
+
+/* Optional outputs of moe_run (every pointer may be NULL; device memory,
+ * 4-byte aligned):
+ *   topk_ids       i32 [T][k]  expert of pick j, picks in selection order
+ *   topk_weights   f32 [T][k]  renormalised routing weight of pick j
+ *   expert_counts  i32 [E]     rows routed to each expert
+ *   expert_offsets i32 [E+1]   exclusive scan of counts, offsets[E] = T*k
+ *   perm           i32 [T*k]   perm[offsets[e] + r] = t*k + j: expert-major,
+ *                              tokens ascending inside an expert
+ *   act_packed     u8  [T][H/2]   (W4A4 only) quantised activations, as
+ *   act_scales     u8  [T][H/16]   moe_quantize_nvfp4_rows writes them
+ *   act_global     f32 [T]        */
+typedef struct {
+  int32_t* topk_ids;
+  float* topk_weights;
+  int32_t* expert_counts;
+  int32_t* expert_offsets;
+  int32_t* perm;
+  uint8_t* act_packed;
+  uint8_t* act_scales;
+  float* act_global;
+} moe_routing_out;
+
+/* Declare a layer. Host only, no HIP call, allocates only the host plan
+ * ([b12x] "Using it": a plan declares the work, allocates no device storage
+ * and compiles nothing; "What's in here": fixed-capacity scratch with live
+ * row counts as runtime values). On success *plan is set and the two sizes
+ * are the bytes the caller must provide for the packed weights and for the
+ * workspace of any T <= max_tokens. */
+int moe_plan(const moe_desc* desc, moe_plan_t** plan, size_t* packed_bytes,
+             size_t* workspace_bytes);
+
+/* Free a plan (NULL is ignored). */
+void moe_plan_destroy(moe_plan_t* plan);
+
+/* Re-lay the boundary-layout weights into the plan's packed buffer: a pure
+ * byte permutation (gate/up 16-row interleave, 128-column K tiles in the
+ * order the GEMM waves read them, block scales grouped per lane) plus a copy
+ * of the global scales. ([vllm.cpp] capability table, GGUF row: NVFP4 weights
+ * repacked at load as a pure byte permutation; [megamoe] CUDA_GRAPH_SYNC_INVENTORY
+ * and WALKING_BACK_SOME_QUANTS: raw row-major scales re-laid once at finalize.)
+ * gate_up and down describe the E routed experts; shared_gate_up/shared_down
+ * the num_shared shared experts (NULL when num_shared == 0). The inputs must
+ * stay valid until the enqueued work completes; `packed` must be 16-byte
+ * aligned and at least packed_bytes long. The same inputs always produce the
+ * same packed bytes. */
+int moe_pack_weights(const moe_plan_t* plan, const moe_nvfp4_tensor* gate_up,
+                     const moe_nvfp4_tensor* down, const moe_nvfp4_tensor* shared_gate_up,
+                     const moe_nvfp4_tensor* shared_down, void* packed, size_t packed_bytes,
+                     void* stream);
+
+/* Run the layer on T live tokens (0 <= T <= max_tokens; T is a host int).
+ *   packed        the buffer moe_pack_weights filled
+ *   x             bf16 [T][H] activations (16-byte aligned)
+ *   router_logits f32  [T][E] (16-byte aligned); finite values
+ *   out           bf16 [T][H] = sum_j w[t][j] * FFN_{ids[t][j]}(x_t) (+ shared),
+ *                 summed in FP32 in pick order, rounded to bf16 (RNE)
+ *   routing       optional outputs (may be NULL)
+ *   workspace     at least workspace_bytes, 16-byte aligned; contents on entry
+ *                 are ignored, on return undefined
+ * Intermediates: gate/up accumulate in FP32 and stay in registers through the
+ * SwiGLU; h = silu(g*gs)*(u*gs) is kept as a pair of bf16 (hi = bf16(h),
+ * lo = bf16(h - hi)) that the down GEMM consumes as two bf16 operands; expert
+ * outputs stay fp32.
+ * ([megamoe] README "MoE kernel": fused SwiGLU grouped GEMM epilogue in
+ * registers; [b12x] "What's in here": FP32 internal, BF16 boundary;
+ * [vllm.cpp] "Device-resident decode campaign": device routing ids feed the
+ * grouped GEMM, routing weights feed MoeCombineKernel.) T == 0 enqueues nothing. */
+int moe_run(const moe_plan_t* plan, const void* packed, int32_t T, const uint16_t* x,
+            const float* router_logits, uint16_t* out, const moe_routing_out* routing,
+            void* workspace, size_t workspace_bytes, void* stream);
+
+/* Stages of moe_run, in launch order (for moe_run_timed). */
+#define MOE_STAGE_QUANT 0      /* W4A4 activation quantisation (absent for bf16 activations) */
+#define MOE_STAGE_ROUTE 1      /* top-k, counts, offsets, permutation, tile list */
+#define MOE_STAGE_GATE_UP 2    /* grouped gate/up GEMM + SwiGLU */
+#define MOE_STAGE_DOWN 3       /* grouped down GEMM */
+#define MOE_STAGE_COMBINE 4    /* weighted combine */
+#define MOE_NUM_STAGES 5
+
+/* moe_run with per-stage timing: stage_events holds 2*MOE_NUM_STAGES hipEvent_t
+ * handles (as void*, any may be NULL); events[2s] is recorded on `stream` right
+ * before stage s is enqueued and events[2s+1] right after, so the elapsed time
+ * between them is that stage's GPU time. The events must have been created by the
+ * caller. Results are identical to moe_run. ([b12x] "Using it": per-kernel timing
+ * logs for tuning.) */
+int moe_run_timed(const moe_plan_t* plan, const void* packed, int32_t T, const uint16_t* x,
+                  const float* router_logits, uint16_t* out, const moe_routing_out* routing,
+                  void* workspace, size_t workspace_bytes, void* stream, void* const* stage_events);
+
+/* NVFP4 row quantiser (the W4A4 activation step of moe_run, callable alone):
+ * for each of `rows` bf16 rows of K elements (K a multiple of 16, <= 16384):
+ *   gs   = max|x| / 2688                        ([megamoe] archived
+ *          CORRECTNESS_BACKLOG §7 "Runtime Activation Global Scale":
+ *          gsa = max(|x|) / (6.0 * 448.0))
+ *   s_b  = E4M3 nearest-even of a_b / (6 gs), saturating at 448; 0 if gs == 0
+ *   d_b  = E4M3(s_b) * gs
+ *   code = sign | E2M1 nearest-even of |x| / d_b, saturating at 6; 0 if d_b == 0
+ * every step a binary32 operation rounded to nearest even (division correctly
+ * rounded). Outputs packed u8 [rows][K/2], scales u8 [rows][K/16],
+ * row_global f32 [rows]; all device pointers 16-byte aligned. */
+int moe_quantize_nvfp4_rows(const uint16_t* x, int32_t rows, int32_t K, uint8_t* packed,
+                            uint8_t* scales, float* row_global, void* stream);
+
+/* The same quantiser with one global scale per group of `rows_per_group`
+ * consecutive fp32 rows (a weight projection [N][K] is one group of N rows):
+ * gs[g] = max|x| over the group / 2688, then blocks and codes as above.
+ * Input w f32 [groups*rows_per_group][K]; outputs packed [..][K/2],
+ * scales [..][K/16], group_global f32 [groups]. Used to prepare weights. */
+int moe_quantize_nvfp4_weights(const float* w, int32_t groups, int32_t rows_per_group, int32_t K,
+                               uint8_t* packed, uint8_t* scales, float* group_global,
+                               void* stream);
+
+/* Host-side weight check (host pointers, G experts of one projection):
+ * rejects NaN block scales (E4M3fn S.1111.111), negative block scales and
+ * non-finite or negative global scales with MOE_ERR_WEIGHT. which: 0 gate_up,
+ * 1 down (routed, G = E), 2 shared gate_up, 3 shared down (G = num_shared).
+ * ([megamoe] WALKING_BACK_SOME_QUANTS: validate scale sizes and contents at
+ * the boundary instead of faulting inside a kernel.) */
+int moe_validate_weights_host(const moe_desc* desc, const moe_nvfp4_tensor* host_copy, int32_t which);
+
+/* Static description of a return code. */
+const char* moe_strerror(int code);
+
+/* MOE_ABI_VERSION of the loaded library. */
+uint32_t moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_MOE_H */

@@ -1,0 +1,374 @@
+// C ABI of libnvfp4moe.so: host validation, buffer layout and launch order.
+// Declared in include/nvfp4_moe.h; see there for the contract of each entry point.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <new>
+
+#include "../../include/nvfp4_moe.h"
+#include "common.hpp"
+#include "kernels.hpp"
+
+using namespace nvmoe;
+
+namespace {
+
+constexpr size_t ALIGN = 256;
+constexpr int MAX_HIDDEN = 16384;
+constexpr int MAX_EXPERTS = 1024;
+constexpr int MAX_TOPK = 64;
+constexpr int MAX_TOKENS = 65536;
+constexpr int FUSED_ROUTE_MAX_T = 128;   // route inside the single plan workgroup up to this T
+
+size_t align_up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+// Upper bound on the GEMM tile list for T tokens and tile height M:
+// sum over groups of ceil(c/M) <= rows/M + (non-empty groups).
+int tile_bound(int T, int k, int E, int S, int M) {
+  const long rows = (long)T * k;
+  long b = rows / M + std::min<long>(E, rows);
+  b += (long)S * ((T + M - 1) / M);
+  return (int)b;
+}
+
+bool use_decode(int T, int k, int E) { return (long)T * k <= 16L * E; }
+
+}  // namespace
+
+struct moe_plan {
+  moe_desc d;
+  int G;
+  ProjLayout w1, w2;
+  size_t off_w1f, off_w1s, off_w1g, off_w2f, off_w2s, off_w2g, packed_bytes;
+  size_t ws_ids, ws_w, ws_counts, ws_offsets, ws_perm, ws_inv, ws_tok, ws_tgrp, ws_trow, ws_tcnt;
+  size_t ws_xq, ws_xs, ws_xg, ws_h, ws_y, ws_bytes;
+  int max_tiles;
+};
+
+extern "C" {
+
+uint32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_strerror(int code) {
+  switch (code) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "null pointer argument";
+    case MOE_ERR_SHAPE: return "unsupported shape or descriptor field";
+    case MOE_ERR_SIZE: return "packed or workspace buffer too small";
+    case MOE_ERR_TOKENS: return "token count outside [0, max_tokens]";
+    case MOE_ERR_ALIGN: return "device pointer not 16-byte aligned";
+    case MOE_ERR_ABI: return "ABI version mismatch";
+    case MOE_ERR_ENUM: return "invalid enum value";
+    case MOE_ERR_WEIGHT: return "invalid weight data (NaN/negative scale or bad global scale)";
+    default: break;
+  }
+  if (code > 0) return hipGetErrorString((hipError_t)code);
+  return "unknown error";
+}
+
+static int check_desc(const moe_desc* d) {
+  if (!d) return MOE_ERR_NULL;
+  if (d->abi_version != MOE_ABI_VERSION) return MOE_ERR_ABI;
+  if (d->score_fn != MOE_SCORE_SOFTMAX && d->score_fn != MOE_SCORE_SIGMOID) return MOE_ERR_ENUM;
+  if (d->act_format != MOE_ACT_BF16 && d->act_format != MOE_ACT_NVFP4_ROWQ) return MOE_ERR_ENUM;
+  if (d->hidden < 128 || d->hidden > MAX_HIDDEN || d->hidden % 128) return MOE_ERR_SHAPE;
+  if (d->inter < 128 || d->inter > MAX_HIDDEN || d->inter % 128) return MOE_ERR_SHAPE;
+  if (d->num_experts < 1 || d->num_experts > MAX_EXPERTS) return MOE_ERR_SHAPE;
+  if (d->top_k < 1 || d->top_k > MAX_TOPK || d->top_k > d->num_experts) return MOE_ERR_SHAPE;
+  if (d->max_tokens < 1 || d->max_tokens > MAX_TOKENS) return MOE_ERR_SHAPE;
+  if (d->renormalize != 1) return MOE_ERR_SHAPE;
+  if (d->num_shared < 0 || d->num_shared > 1) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
+int moe_plan(const moe_desc* desc, moe_plan_t** plan, size_t* packed_bytes, size_t* workspace_bytes) {
+  if (!plan) return MOE_ERR_NULL;
+  *plan = nullptr;
+  const int rc = check_desc(desc);
+  if (rc) return rc;
+  struct moe_plan* p = new (std::nothrow) struct moe_plan;
+  if (!p) return MOE_ERR_SIZE;
+  std::memset(p, 0, sizeof(*p));
+  p->d = *desc;
+  const int H = desc->hidden, I = desc->inter, E = desc->num_experts, k = desc->top_k;
+  const int S = desc->num_shared, Tm = desc->max_tokens;
+  p->G = E + S;
+  p->w1 = proj_layout(2 * I, H);
+  p->w2 = proj_layout(H, I);
+  size_t o = 0;
+  p->off_w1f = o; o = align_up(o + p->w1.fp4_expert * p->G);
+  p->off_w1s = o; o = align_up(o + p->w1.sc_expert * p->G);
+  p->off_w1g = o; o = align_up(o + sizeof(float) * p->G);
+  p->off_w2f = o; o = align_up(o + p->w2.fp4_expert * p->G);
+  p->off_w2s = o; o = align_up(o + p->w2.sc_expert * p->G);
+  p->off_w2g = o; o = align_up(o + sizeof(float) * p->G);
+  p->packed_bytes = o;
+
+  const size_t routed = (size_t)Tm * k, rows = routed + (size_t)S * Tm;
+  p->max_tiles = std::max(tile_bound(Tm, k, E, S, DECODE_TILE_ROWS), tile_bound(Tm, k, E, S, PREFILL_TILE_ROWS));
+  o = 0;
+  p->ws_ids = o; o = align_up(o + 4 * routed);
+  p->ws_w = o; o = align_up(o + 4 * routed);
+  p->ws_counts = o; o = align_up(o + 4 * (size_t)p->G);
+  p->ws_offsets = o; o = align_up(o + 4 * ((size_t)p->G + 1));
+  p->ws_perm = o; o = align_up(o + 4 * routed);
+  p->ws_inv = o; o = align_up(o + 4 * routed);
+  p->ws_tok = o; o = align_up(o + 4 * rows);
+  p->ws_tgrp = o; o = align_up(o + 4 * (size_t)p->max_tiles);
+  p->ws_trow = o; o = align_up(o + 4 * (size_t)p->max_tiles);
+  p->ws_tcnt = o; o = align_up(o + 16);
+  p->ws_xq = o; o = align_up(o + (desc->act_format == MOE_ACT_NVFP4_ROWQ ? (size_t)Tm * H / 2 : 0));
+  p->ws_xs = o; o = align_up(o + (desc->act_format == MOE_ACT_NVFP4_ROWQ ? (size_t)Tm * H / 16 : 0));
+  p->ws_xg = o; o = align_up(o + (desc->act_format == MOE_ACT_NVFP4_ROWQ ? 4 * (size_t)Tm : 0));
+  p->ws_h = o; o = align_up(o + 2 * 2 * rows * I);   // h_hi and h_lo planes
+  p->ws_y = o; o = align_up(o + 4 * rows * H);
+  p->ws_bytes = o;
+  if (packed_bytes) *packed_bytes = p->packed_bytes;
+  if (workspace_bytes) *workspace_bytes = p->ws_bytes;
+  *plan = p;
+  return MOE_OK;
+}
+
+void moe_plan_destroy(moe_plan_t* plan) { delete plan; }
+
+static int check_tensor(const moe_nvfp4_tensor* t) {
+  if (!t || !t->packed || !t->scales || !t->global_scale) return MOE_ERR_NULL;
+  if (!aligned16(t->packed) || !aligned16(t->scales) || !aligned4(t->global_scale)) return MOE_ERR_ALIGN;
+  return MOE_OK;
+}
+
+int moe_pack_weights(const moe_plan_t* plan, const moe_nvfp4_tensor* gate_up, const moe_nvfp4_tensor* down,
+                     const moe_nvfp4_tensor* shared_gate_up, const moe_nvfp4_tensor* shared_down, void* packed,
+                     size_t packed_bytes, void* stream) {
+  if (!plan || !packed) return MOE_ERR_NULL;
+  int rc = check_tensor(gate_up);
+  if (!rc) rc = check_tensor(down);
+  if (!rc && plan->d.num_shared) {
+    rc = check_tensor(shared_gate_up);
+    if (!rc) rc = check_tensor(shared_down);
+  }
+  if (rc) return rc;
+  if (!aligned16(packed)) return MOE_ERR_ALIGN;
+  if (packed_bytes < plan->packed_bytes) return MOE_ERR_SIZE;
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t* base = (uint8_t*)packed;
+  const int E = plan->d.num_experts;
+  const moe_nvfp4_tensor* srcs[2][2] = {{gate_up, down}, {shared_gate_up, shared_down}};
+  for (int shared = 0; shared <= (plan->d.num_shared ? 1 : 0); ++shared) {
+    for (int proj = 0; proj < 2; ++proj) {
+      const ProjLayout& L = proj ? plan->w2 : plan->w1;
+      const moe_nvfp4_tensor* t = srcs[shared][proj];
+      const size_t g0 = shared ? (size_t)E : 0;
+      PackArgs a;
+      a.packed = t->packed;
+      a.scales = t->scales;
+      a.gs = t->global_scale;
+      a.G = shared ? plan->d.num_shared : E;
+      a.N = L.N;
+      a.K = L.K;
+      a.gate_up = proj == 0;
+      a.fp4_out = base + (proj ? plan->off_w2f : plan->off_w1f) + g0 * L.fp4_expert;
+      a.sc_out = base + (proj ? plan->off_w2s : plan->off_w1s) + g0 * L.sc_expert;
+      a.gs_out = (float*)(base + (proj ? plan->off_w2g : plan->off_w1g)) + g0;
+      const hipError_t e = launch_pack(a, s);
+      if (e != hipSuccess) return (int)e;
+    }
+  }
+  return MOE_OK;
+}
+
+static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const uint16_t* x,
+                    const float* router_logits, uint16_t* out, const moe_routing_out* routing, void* workspace,
+                    size_t workspace_bytes, void* stream, void* const* ev);
+
+int moe_run(const moe_plan_t* plan, const void* packed, int32_t T, const uint16_t* x, const float* router_logits,
+            uint16_t* out, const moe_routing_out* routing, void* workspace, size_t workspace_bytes, void* stream) {
+  return run_impl(plan, packed, T, x, router_logits, out, routing, workspace, workspace_bytes, stream, nullptr);
+}
+
+int moe_run_timed(const moe_plan_t* plan, const void* packed, int32_t T, const uint16_t* x,
+                  const float* router_logits, uint16_t* out, const moe_routing_out* routing, void* workspace,
+                  size_t workspace_bytes, void* stream, void* const* stage_events) {
+  return run_impl(plan, packed, T, x, router_logits, out, routing, workspace, workspace_bytes, stream,
+                  stage_events);
+}
+
+static hipError_t mark(void* const* ev, int idx, hipStream_t s) {
+  if (!ev || !ev[idx]) return hipSuccess;
+  return hipEventRecord((hipEvent_t)ev[idx], s);
+}
+
+static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const uint16_t* x,
+                    const float* router_logits, uint16_t* out, const moe_routing_out* routing, void* workspace,
+                    size_t workspace_bytes, void* stream, void* const* ev) {
+  if (!plan || !packed || !x || !router_logits || !out || !workspace) return MOE_ERR_NULL;
+  const moe_desc& d = plan->d;
+  if (T < 0 || T > d.max_tokens) return MOE_ERR_TOKENS;
+  if (!aligned16(packed) || !aligned16(x) || !aligned16(router_logits) || !aligned16(out) || !aligned16(workspace))
+    return MOE_ERR_ALIGN;
+  if (workspace_bytes < plan->ws_bytes) return MOE_ERR_SIZE;
+  moe_routing_out r;
+  std::memset(&r, 0, sizeof(r));
+  if (routing) {
+    r = *routing;
+    const void* p4[] = {r.topk_ids, r.topk_weights, r.expert_counts, r.expert_offsets, r.perm, r.act_global};
+    for (const void* q : p4)
+      if (q && !aligned4(q)) return MOE_ERR_ALIGN;
+    if ((r.act_packed && !aligned16(r.act_packed)) || (r.act_scales && !aligned16(r.act_scales)))
+      return MOE_ERR_ALIGN;
+  }
+  if (T == 0) return MOE_OK;
+
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t* ws = (uint8_t*)workspace;
+  const uint8_t* pk = (const uint8_t*)packed;
+  const int H = d.hidden, I = d.inter, E = d.num_experts, k = d.top_k, S = d.num_shared;
+  const bool fp4 = d.act_format == MOE_ACT_NVFP4_ROWQ;
+  hipError_t e;
+
+  uint8_t* xq = r.act_packed ? r.act_packed : ws + plan->ws_xq;
+  uint8_t* xs = r.act_scales ? r.act_scales : ws + plan->ws_xs;
+  float* xg = r.act_global ? r.act_global : (float*)(ws + plan->ws_xg);
+  if (fp4) {
+    if ((e = mark(ev, 2 * MOE_STAGE_QUANT, s)) != hipSuccess) return (int)e;
+    e = launch_quant_rows_bf16(x, T, H, xq, xs, xg, s);
+    if (e != hipSuccess) return (int)e;
+    if ((e = mark(ev, 2 * MOE_STAGE_QUANT + 1, s)) != hipSuccess) return (int)e;
+  }
+
+  const bool decode = use_decode(T, k, E);
+  const int M = decode ? DECODE_TILE_ROWS : PREFILL_TILE_ROWS;
+  RouteArgs ra;
+  ra.logits = router_logits;
+  ra.T = T;
+  ra.E = E;
+  ra.k = k;
+  ra.score = d.score_fn;
+  ra.ids = (int32_t*)(ws + plan->ws_ids);
+  ra.w = (float*)(ws + plan->ws_w);
+  ra.ids_user = r.topk_ids;
+  ra.w_user = r.topk_weights;
+  PlanArgs pa;
+  pa.ids = ra.ids;
+  pa.T = T;
+  pa.E = E;
+  pa.k = k;
+  pa.G = plan->G;
+  pa.tile_rows = M;
+  pa.counts = (int32_t*)(ws + plan->ws_counts);
+  pa.offsets = (int32_t*)(ws + plan->ws_offsets);
+  pa.perm = (int32_t*)(ws + plan->ws_perm);
+  pa.inv = (int32_t*)(ws + plan->ws_inv);
+  pa.tok = (int32_t*)(ws + plan->ws_tok);
+  pa.tile_group = (int32_t*)(ws + plan->ws_tgrp);
+  pa.tile_row0 = (int32_t*)(ws + plan->ws_trow);
+  pa.tile_count = (int32_t*)(ws + plan->ws_tcnt);
+  pa.counts_user = r.expert_counts;
+  pa.offsets_user = r.expert_offsets;
+  pa.perm_user = r.perm;
+  if ((e = mark(ev, 2 * MOE_STAGE_ROUTE, s)) != hipSuccess) return (int)e;
+  e = launch_route_plan(ra, pa, T <= FUSED_ROUTE_MAX_T, s);
+  if (e != hipSuccess) return (int)e;
+  if ((e = mark(ev, 2 * MOE_STAGE_ROUTE + 1, s)) != hipSuccess) return (int)e;
+
+  const int max_tiles = tile_bound(T, k, E, S, M);
+  GemmArgs g1;
+  std::memset(&g1, 0, sizeof(g1));
+  g1.wfp4 = pk + plan->off_w1f;
+  g1.wsc = pk + plan->off_w1s;
+  g1.wgs = (const float*)(pk + plan->off_w1g);
+  g1.N = 2 * I;
+  g1.K = H;
+  g1.tok = pa.tok;
+  g1.x = x;
+  g1.xq = xq;
+  g1.xs = xs;
+  g1.xg = xg;
+  g1.tile_group = pa.tile_group;
+  g1.tile_row0 = pa.tile_row0;
+  g1.tile_count = pa.tile_count;
+  g1.offsets = pa.offsets;
+  g1.out = (uint16_t*)(ws + plan->ws_h);
+  const size_t hplane = ((size_t)d.max_tokens * k + (size_t)S * d.max_tokens) * I;
+  g1.out_lo = g1.out + hplane;
+  if ((e = mark(ev, 2 * MOE_STAGE_GATE_UP, s)) != hipSuccess) return (int)e;
+  e = launch_gemm(fp4 ? GEMM_GATEUP_FP4 : GEMM_GATEUP_BF16, decode, max_tiles, g1, s);
+  if (e != hipSuccess) return (int)e;
+  if ((e = mark(ev, 2 * MOE_STAGE_GATE_UP + 1, s)) != hipSuccess) return (int)e;
+
+  GemmArgs g2 = g1;
+  g2.wfp4 = pk + plan->off_w2f;
+  g2.wsc = pk + plan->off_w2s;
+  g2.wgs = (const float*)(pk + plan->off_w2g);
+  g2.N = H;
+  g2.K = I;
+  g2.x = g1.out;
+  g2.xlo = g1.out_lo;
+  g2.out = nullptr;
+  g2.yout = (float*)(ws + plan->ws_y);
+  if ((e = mark(ev, 2 * MOE_STAGE_DOWN, s)) != hipSuccess) return (int)e;
+  e = launch_gemm(GEMM_DOWN, decode, max_tiles, g2, s);
+  if (e != hipSuccess) return (int)e;
+  if ((e = mark(ev, 2 * MOE_STAGE_DOWN + 1, s)) != hipSuccess) return (int)e;
+
+  CombineArgs c;
+  c.y = (const float*)(ws + plan->ws_y);
+  c.w = ra.w;
+  c.inv = pa.inv;
+  c.T = T;
+  c.H = H;
+  c.k = k;
+  c.S = S;
+  c.out = out;
+  if ((e = mark(ev, 2 * MOE_STAGE_COMBINE, s)) != hipSuccess) return (int)e;
+  e = launch_combine(c, s);
+  if (e != hipSuccess) return (int)e;
+  return (int)mark(ev, 2 * MOE_STAGE_COMBINE + 1, s);
+}
+
+int moe_quantize_nvfp4_rows(const uint16_t* x, int32_t rows, int32_t K, uint8_t* packed, uint8_t* scales,
+                            float* row_global, void* stream) {
+  if (!x || !packed || !scales || !row_global) return MOE_ERR_NULL;
+  if (rows < 0 || K < 16 || K > MAX_HIDDEN || K % 16) return MOE_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(packed) || !aligned4(row_global)) return MOE_ERR_ALIGN;
+  return (int)launch_quant_rows_bf16(x, rows, K, packed, scales, row_global, (hipStream_t)stream);
+}
+
+int moe_quantize_nvfp4_weights(const float* w, int32_t groups, int32_t rows_per_group, int32_t K, uint8_t* packed,
+                               uint8_t* scales, float* group_global, void* stream) {
+  if (!w || !packed || !scales || !group_global) return MOE_ERR_NULL;
+  if (groups < 0 || rows_per_group < 1 || K < 16 || K > MAX_HIDDEN || K % 16) return MOE_ERR_SHAPE;
+  if ((long)groups * rows_per_group > (1L << 30)) return MOE_ERR_SHAPE;
+  if (!aligned16(w) || !aligned16(packed) || !aligned4(group_global)) return MOE_ERR_ALIGN;
+  return (int)launch_quant_groups_f32(w, groups, rows_per_group, K, packed, scales, group_global,
+                                      (hipStream_t)stream);
+}
+
+int moe_validate_weights_host(const moe_desc* desc, const moe_nvfp4_tensor* t, int32_t which) {
+  const int rc = check_desc(desc);
+  if (rc) return rc;
+  if (!t || !t->packed || !t->scales || !t->global_scale) return MOE_ERR_NULL;
+  if (which < 0 || which > 3) return MOE_ERR_ENUM;
+  const int G = which >= 2 ? desc->num_shared : desc->num_experts;
+  const bool up = (which & 1) == 0;
+  const size_t N = up ? 2 * (size_t)desc->inter : (size_t)desc->hidden;
+  const size_t K = up ? (size_t)desc->hidden : (size_t)desc->inter;
+  const size_t nsc = (size_t)G * N * (K / 16);
+  for (size_t i = 0; i < nsc; ++i) {
+    const uint8_t b = t->scales[i];
+    if ((b & 0x7Fu) == 0x7Fu || (b & 0x80u)) return MOE_ERR_WEIGHT;
+  }
+  for (int g = 0; g < G; ++g) {
+    const float v = t->global_scale[g];
+    if (!std::isfinite(v) || v < 0.0f) return MOE_ERR_WEIGHT;
+  }
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,86 @@
+// Device-side helpers shared by the HIP kernels of libnvfp4moe.so (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvmoe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int WAVE = 64;
+constexpr int KCHUNK = 128;        // K elements per pipeline chunk (64 bytes of E2M1 per row)
+constexpr int SCALE_GROUP = 8;     // K chunks whose block scales one lane loads at once (16 bytes)
+
+// ------------------------------------------------------------------ packed layout
+// One NVFP4 projection of G experts, N rows, K columns, after moe_pack_weights:
+//   fp4 tiles   [G][N/16][K/128][64 lanes][16 B]  lane l of a 16-row tile holds row
+//               (l % 16), columns 32*(l/16) .. +31 of the 128-column chunk
+//   scale tiles [G][N/16][ceil(K/1024)][64 lanes][16 B]  byte 2c+h of lane l holds the
+//               block scale of row (l % 16), block 8*(8*sg + c) + 2*(l/16) + h
+//   global      [G] f32
+// For gate_up the 16-row tiles alternate gate and up: tile 2q is gate rows 16q..16q+15,
+// tile 2q+1 is up rows 16q..16q+15 (boundary rows I+16q..), so one wave holds the gate
+// and up accumulators of the same output columns.
+struct ProjLayout {
+  int N, K, KC, KSG;               // rows, columns, K chunks, scale groups
+  size_t fp4_expert, sc_expert;    // bytes per expert
+};
+
+__host__ __device__ inline ProjLayout proj_layout(int N, int K) {
+  ProjLayout p;
+  p.N = N;
+  p.K = K;
+  p.KC = K / KCHUNK;
+  p.KSG = (p.KC + SCALE_GROUP - 1) / SCALE_GROUP;
+  p.fp4_expert = (size_t)(N / 16) * p.KC * WAVE * 16;
+  p.sc_expert = (size_t)(N / 16) * p.KSG * WAVE * 16;
+  return p;
+}
+
+// ------------------------------------------------------------------ number formats
+
+// E4M3fn byte -> fp32 (exact). 0x7F/0xFF (NaN) are rejected by host validation.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+  float v = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+  return (b & 0x80u) ? -v : v;
+}
+
+// Eight E2M1 codes (nibble i of w = element i) times one fp32 block scale, as bf16.
+// q * s has at most 2 + 4 significant bits and lies in [2^-10, 2688], so the fp32
+// product is exact and its upper half is the exact bf16 value.
+__device__ __forceinline__ bf16x8 dequant8(uint32_t w, float s) {
+  u32x4 o;
+  f32x2 f;
+  f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+  o.x = __builtin_amdgcn_perm(__float_as_uint(f.y * s), __float_as_uint(f.x * s), 0x07060302u);
+  f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+  o.y = __builtin_amdgcn_perm(__float_as_uint(f.y * s), __float_as_uint(f.x * s), 0x07060302u);
+  f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+  o.z = __builtin_amdgcn_perm(__float_as_uint(f.y * s), __float_as_uint(f.x * s), 0x07060302u);
+  f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+  o.w = __builtin_amdgcn_perm(__float_as_uint(f.y * s), __float_as_uint(f.x * s), 0x07060302u);
+  return __builtin_bit_cast(bf16x8, o);
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+
+}  // namespace nvmoe

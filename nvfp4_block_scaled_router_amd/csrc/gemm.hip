@@ -1,0 +1,412 @@
+// Grouped NVFP4 GEMMs of the MoE layer on gfx950 MFMA, and the weighted combine.
+//
+//   gate_up: [g|u][row] = W1_e . x_row  (W1_e = E2M1 x E4M3(per 16 along H) x gs_e),
+//            epilogue h = silu(g*sc) * (u*sc), sc = gs_e (x the row's activation global
+//            scale for NVFP4 activations), stored as two bf16 planes hi = bf16(h),
+//            lo = bf16(h - hi), which hold h to about 2^-17 relative
+//   down:    y[row] = W2_e . (h_hi + h_lo)_row * gs_e -> fp32 (kept in fp32 until the
+//            combine): each dequantised weight tile meets both planes in two MFMAs
+// ([megamoe] README "MoE kernel": grouped GEMM with the global scale, SwiGLU and
+// clamping applied in registers in the epilogue; [vllm.cpp] "Device-resident decode
+// campaign": grouped kernels with a per-group weight-row index, then MoeCombineKernel.)
+//
+// Dequant route: the per-16 E4M3 block scale is not a power of two and covers half
+// an E8M0 block of the scaled MFMA, so each weight is rebuilt exactly as a bf16
+// (E2M1 x E4M3 has at most 6 significant bits) by the fp4->fp32 convert, one fp32
+// multiply and a truncating pack, and fed to V_MFMA_F32_16X16X32_BF16 with fp32
+// accumulation. Global scales (per expert, per activation row) are constant over K
+// and are applied once in the epilogue.
+//
+// Operand roles: MFMA A = 16 weight rows x 32 k (one lane: row l%16, 8 consecutive
+// k of a 32-wide lane group), MFMA B = 32 k x 16 tokens (lane: token l%16, the same
+// 8 k). Inside a 128-column chunk, lane group g = l/16 owns columns 32g..32g+31 and
+// feeds 8 of them to each of the chunk's 4 MFMAs; A and B use the same k order, so
+// the dot products are unchanged. D: lane l holds rows 4*(l/16)+r, r < 4, of token
+// l%16, i.e. 4 consecutive output features of one token.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace nvmoe {
+
+// ----------------------------------------------------------------------- helpers
+
+__device__ __forceinline__ uint32_t pick_dword(const u32x4& v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+// The two block scales (fp32) of chunk c (0..7 inside its scale group) for this lane.
+__device__ __forceinline__ void chunk_scales(const u32x4& sg, int c, float& s0, float& s1) {
+  const uint32_t pair = pick_dword(sg, c >> 1) >> (16 * (c & 1));
+  s0 = e4m3_to_f32(pair & 0xFFu);
+  s1 = e4m3_to_f32((pair >> 8) & 0xFFu);
+}
+
+__device__ __forceinline__ const u32x4* fp4_tile(const GemmArgs& a, const ProjLayout& L, int g, int q, int kc) {
+  const size_t tile = ((size_t)g * (L.N / 16) + q) * L.KC + kc;
+  return (const u32x4*)(a.wfp4 + tile * (WAVE * 16)) + (threadIdx.x & (WAVE - 1));
+}
+
+__device__ __forceinline__ const u32x4* sc_tile(const GemmArgs& a, const ProjLayout& L, int g, int q, int sg) {
+  const size_t tile = ((size_t)g * (L.N / 16) + q) * L.KSG + sg;
+  return (const u32x4*)(a.wsc + tile * (WAVE * 16)) + (threadIdx.x & (WAVE - 1));
+}
+
+__device__ __forceinline__ void store_bf16x4(uint16_t* p, float v0, float v1, float v2, float v3) {
+  *(u32x2*)p = u32x2{f32_to_bf16_rne(v0) | (f32_to_bf16_rne(v1) << 16),
+                     f32_to_bf16_rne(v2) | (f32_to_bf16_rne(v3) << 16)};
+}
+
+// Epilogue for one 16-feature x 16-token D tile pair / single.
+template <int MODE>
+__device__ __forceinline__ void epilogue_pair(const GemmArgs& a, const f32x4& gacc, const f32x4& uacc, float sc,
+                                              int row, int hs) {
+  const int lg = (threadIdx.x & (WAVE - 1)) >> 4;
+  const int NO = a.N / 2;
+  const size_t off = (size_t)row * NO + hs * 16 + 4 * lg;
+  const float h[4] = {silu_mul(gacc.x * sc, uacc.x * sc), silu_mul(gacc.y * sc, uacc.y * sc),
+                      silu_mul(gacc.z * sc, uacc.z * sc), silu_mul(gacc.w * sc, uacc.w * sc)};
+  uint32_t hi[4];
+  float lo[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    hi[i] = f32_to_bf16_rne(h[i]);
+    lo[i] = h[i] - bf16_to_f32(hi[i]);          // exact in fp32
+  }
+  *(u32x2*)(a.out + off) = u32x2{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)};
+  store_bf16x4(a.out_lo + off, lo[0], lo[1], lo[2], lo[3]);
+}
+
+__device__ __forceinline__ void epilogue_single(const GemmArgs& a, const f32x4& acc, float sc, int row, int q) {
+  const int lg = (threadIdx.x & (WAVE - 1)) >> 4;
+  float* p = a.yout + (size_t)row * a.N + q * 16 + 4 * lg;
+  *(f32x4*)p = acc * sc;
+}
+
+// ------------------------------------------------------------------ decode GEMM
+// Small row counts per expert (<= 16 rows per tile): weight streaming bound. A
+// workgroup owns NSUB 16-row weight tiles of one expert and one 16-row token tile;
+// its 4 waves split K into contiguous ranges and reduce through LDS. Token operands
+// are read straight from global memory (they are tiny and shared through L2).
+template <int MODE, int NSUB>
+__global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs a) {
+  const int slot = blockIdx.y;
+  if (slot >= a.tile_count[0]) return;
+  const ProjLayout L = proj_layout(a.N, a.K);
+  const int q0 = blockIdx.x * NSUB;
+  const int g = a.tile_group[slot];
+  const int row0 = a.tile_row0[slot];
+  const int nvalid = min(DECODE_TILE_ROWS, a.offsets[g + 1] - row0);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & (WAVE - 1);
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int row = row0 + min(l16, nvalid - 1);            // clamp: extra columns are never stored
+  const int kc0 = (wave * L.KC) / 4, kc1 = ((wave + 1) * L.KC) / 4;
+
+  const uint16_t* xrow = nullptr;
+  const uint16_t* xlrow = nullptr;
+  const uint8_t* qrow = nullptr;
+  const uint8_t* srow = nullptr;
+  if (MODE == GEMM_DOWN) {
+    xrow = a.x + (size_t)row * L.K;
+    xlrow = a.xlo + (size_t)row * L.K;
+  } else if (MODE == GEMM_GATEUP_BF16) {
+    xrow = a.x + (size_t)a.tok[row] * L.K;
+  } else {
+    const int t = a.tok[row];
+    qrow = a.xq + (size_t)t * (L.K / 2);
+    srow = a.xs + (size_t)t * (L.K / 16);
+  }
+
+  f32x4 acc[NSUB];
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s) acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  u32x4 sgv[NSUB];
+  int sg_loaded = -1;
+  for (int kc = kc0; kc < kc1; ++kc) {
+    if ((kc >> 3) != sg_loaded) {
+      sg_loaded = kc >> 3;
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s) sgv[s] = *sc_tile(a, L, g, q0 + s, sg_loaded);
+    }
+    u32x4 wv[NSUB];
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) wv[s] = *fp4_tile(a, L, g, q0 + s, kc);
+    bf16x8 bop[4], blo[4];
+    if (MODE == GEMM_DOWN) {
+      const u32x4* lsrc = (const u32x4*)(xlrow + (size_t)kc * KCHUNK + lg * 32);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) blo[j] = __builtin_bit_cast(bf16x8, lsrc[j]);
+    }
+    if (MODE == GEMM_GATEUP_FP4) {
+      const u32x4 xv = *(const u32x4*)(qrow + (size_t)kc * 64 + lg * 16);
+      const uint32_t sp = *(const uint16_t*)(srow + (size_t)kc * 8 + 2 * lg);
+      const float xs0 = e4m3_to_f32(sp & 0xFFu), xs1 = e4m3_to_f32(sp >> 8);
+      bop[0] = dequant8(xv.x, xs0);
+      bop[1] = dequant8(xv.y, xs0);
+      bop[2] = dequant8(xv.z, xs1);
+      bop[3] = dequant8(xv.w, xs1);
+    } else {
+      const u32x4* src = (const u32x4*)(xrow + (size_t)kc * KCHUNK + lg * 32);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bop[j] = __builtin_bit_cast(bf16x8, src[j]);
+    }
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) {
+      float s0, s1;
+      chunk_scales(sgv[s], kc & 7, s0, s1);
+      const bf16x8 a0 = dequant8(wv[s].x, s0), a1 = dequant8(wv[s].y, s0);
+      const bf16x8 a2 = dequant8(wv[s].z, s1), a3 = dequant8(wv[s].w, s1);
+      acc[s] = mfma16x16x32(a0, bop[0], acc[s]);
+      acc[s] = mfma16x16x32(a1, bop[1], acc[s]);
+      acc[s] = mfma16x16x32(a2, bop[2], acc[s]);
+      acc[s] = mfma16x16x32(a3, bop[3], acc[s]);
+      if (MODE == GEMM_DOWN) {
+        acc[s] = mfma16x16x32(a0, blo[0], acc[s]);
+        acc[s] = mfma16x16x32(a1, blo[1], acc[s]);
+        acc[s] = mfma16x16x32(a2, blo[2], acc[s]);
+        acc[s] = mfma16x16x32(a3, blo[3], acc[s]);
+      }
+    }
+  }
+
+  __shared__ f32x4 red[4][NSUB][WAVE];
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s) red[wave][s][lane] = acc[s];
+  __syncthreads();
+  if (wave != 0 || l16 >= nvalid) return;
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s) acc[s] = ((red[0][s][lane] + red[1][s][lane]) + red[2][s][lane]) + red[3][s][lane];
+  const int orow = row0 + l16;
+  float sc = a.wgs[g];
+  if (MODE == GEMM_GATEUP_FP4) sc *= a.xg[a.tok[orow]];
+  if (MODE == GEMM_DOWN) {
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) epilogue_single(a, acc[s], sc, orow, q0 + s);
+  } else {
+#pragma unroll
+    for (int s = 0; s < NSUB; s += 2) epilogue_pair<MODE>(a, acc[s], acc[s + 1], sc, orow, (q0 + s) >> 1);
+  }
+}
+
+// ----------------------------------------------------------------- prefill GEMM
+// Tiles of TSUB*16 rows of one expert x (4 waves x NSUB) 16-row weight tiles. Token
+// rows are gathered (through the row->token map) chunk by chunk into a double-buffered
+// LDS tile shared by the 4 waves; each wave streams its own weight tiles straight into
+// registers and dequantises them there. LDS rows are 256 bytes (one 128-column chunk
+// of bf16); 16-byte piece c of row r is stored at piece c ^ (r % 16) so the 16 lanes
+// of a lane group read 16 different bank groups.
+template <int MODE, int NSUB, int TSUB>
+__global__ __launch_bounds__(256) void gemm_prefill_kernel(GemmArgs a) {
+  constexpr int M = TSUB * 16;
+  constexpr int PLANES = MODE == GEMM_DOWN ? 2 : 1;   // down: h_hi and h_lo
+  __shared__ u32x4 tile[2][PLANES][M * 16];
+  const int slot = blockIdx.y;
+  if (slot >= a.tile_count[0]) return;
+  const ProjLayout L = proj_layout(a.N, a.K);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & (WAVE - 1);
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int q0 = (blockIdx.x * 4 + wave) * NSUB;
+  const bool active = q0 < L.N / 16;                     // wave owns weight tiles
+  const int g = a.tile_group[slot];
+  const int row0 = a.tile_row0[slot];
+  const int nvalid = min(M, a.offsets[g + 1] - row0);
+
+  // staging assignment: bf16 modes move 16-byte pieces (8 columns), TSUB per thread;
+  // the NVFP4 mode moves 16-column pieces (8 code bytes + 1 scale byte), TSUB/2 per thread
+  constexpr int NPIECE = (MODE == GEMM_GATEUP_FP4) ? TSUB / 2 : TSUB;
+  const uint16_t* xsrc[NPIECE];
+  const uint16_t* xlsrc[NPIECE];
+  const uint8_t* qsrc[NPIECE];
+  const uint8_t* ssrc[NPIECE];
+  int prow[NPIECE], pcol[NPIECE];
+#pragma unroll
+  for (int i = 0; i < NPIECE; ++i) {
+    const int p = threadIdx.x + 256 * i;
+    const int per_row = (MODE == GEMM_GATEUP_FP4) ? 8 : 16;
+    prow[i] = p / per_row;
+    pcol[i] = p % per_row;
+    const int r = row0 + min(prow[i], nvalid - 1);
+    if (MODE == GEMM_DOWN) {
+      xsrc[i] = a.x + (size_t)r * L.K + pcol[i] * 8;
+      xlsrc[i] = a.xlo + (size_t)r * L.K + pcol[i] * 8;
+    } else if (MODE == GEMM_GATEUP_BF16) {
+      xsrc[i] = a.x + (size_t)a.tok[r] * L.K + pcol[i] * 8;
+    } else {
+      const int t = a.tok[r];
+      qsrc[i] = a.xq + (size_t)t * (L.K / 2) + pcol[i] * 8;
+      ssrc[i] = a.xs + (size_t)t * (L.K / 16) + pcol[i];
+    }
+  }
+  u32x4 stg[NPIECE], stg_lo[NPIECE];
+  uint32_t stg_s[NPIECE];
+  u32x2 stg_q[NPIECE];
+  auto stage_load = [&](int kc) {
+#pragma unroll
+    for (int i = 0; i < NPIECE; ++i) {
+      if (MODE == GEMM_GATEUP_FP4) {
+        stg_q[i] = *(const u32x2*)(qsrc[i] + (size_t)kc * 64);
+        stg_s[i] = ssrc[i][(size_t)kc * 8];
+      } else {
+        stg[i] = *(const u32x4*)(xsrc[i] + (size_t)kc * KCHUNK);
+        if (MODE == GEMM_DOWN) stg_lo[i] = *(const u32x4*)(xlsrc[i] + (size_t)kc * KCHUNK);
+      }
+    }
+  };
+  auto stage_store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < NPIECE; ++i) {
+      const int r = prow[i];
+      if (MODE == GEMM_GATEUP_FP4) {
+        const float s = e4m3_to_f32(stg_s[i]);
+        const bf16x8 lo = dequant8(stg_q[i].x, s), hi = dequant8(stg_q[i].y, s);
+        const int c = 2 * pcol[i];
+        tile[buf][0][r * 16 + (c ^ (r & 15))] = __builtin_bit_cast(u32x4, lo);
+        tile[buf][0][r * 16 + ((c + 1) ^ (r & 15))] = __builtin_bit_cast(u32x4, hi);
+      } else {
+        tile[buf][0][r * 16 + (pcol[i] ^ (r & 15))] = stg[i];
+        if (MODE == GEMM_DOWN) tile[buf][PLANES - 1][r * 16 + (pcol[i] ^ (r & 15))] = stg_lo[i];
+      }
+    }
+  };
+
+  f32x4 acc[NSUB][TSUB];
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s)
+#pragma unroll
+    for (int t = 0; t < TSUB; ++t) acc[s][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  u32x4 wcur[NSUB], wnext[NSUB], scur[NSUB], snext[NSUB];
+  if (active) {
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) {
+      wnext[s] = *fp4_tile(a, L, g, q0 + s, 0);
+      snext[s] = *sc_tile(a, L, g, q0 + s, 0);
+    }
+  }
+  stage_load(0);
+  for (int kc = 0; kc < L.KC; ++kc) {
+    const int buf = kc & 1;
+    stage_store(buf);
+    if (kc + 1 < L.KC) stage_load(kc + 1);
+    if (active) {
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s) {
+        wcur[s] = wnext[s];
+        if ((kc & 7) == 0) scur[s] = snext[s];
+      }
+      if (kc + 1 < L.KC) {
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s) {
+          wnext[s] = *fp4_tile(a, L, g, q0 + s, kc + 1);
+          if (((kc + 1) & 7) == 0) snext[s] = *sc_tile(a, L, g, q0 + s, (kc + 1) >> 3);
+        }
+      }
+    }
+    __syncthreads();
+    if (active) {
+      float s0[NSUB], s1[NSUB];
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s) chunk_scales(scur[s], kc & 7, s0[s], s1[s]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bf16x8 aop[NSUB];
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s) aop[s] = dequant8(pick_dword(wcur[s], j), j < 2 ? s0[s] : s1[s]);
+        const int c = lg * 4 + j;
+#pragma unroll
+        for (int t = 0; t < TSUB; ++t) {
+          const int r = t * 16 + l16;
+          const bf16x8 bop = __builtin_bit_cast(bf16x8, tile[buf][0][r * 16 + (c ^ l16)]);
+#pragma unroll
+          for (int s = 0; s < NSUB; ++s) acc[s][t] = mfma16x16x32(aop[s], bop, acc[s][t]);
+          if (MODE == GEMM_DOWN) {
+            const bf16x8 blo = __builtin_bit_cast(bf16x8, tile[buf][PLANES - 1][r * 16 + (c ^ l16)]);
+#pragma unroll
+            for (int s = 0; s < NSUB; ++s) acc[s][t] = mfma16x16x32(aop[s], blo, acc[s][t]);
+          }
+        }
+      }
+    }
+  }
+
+  if (!active) return;
+  const float wgs = a.wgs[g];
+#pragma unroll
+  for (int t = 0; t < TSUB; ++t) {
+    const int rr = t * 16 + l16;
+    if (rr >= nvalid) continue;
+    const int orow = row0 + rr;
+    float sc = wgs;
+    if (MODE == GEMM_GATEUP_FP4) sc *= a.xg[a.tok[orow]];
+    if (MODE == GEMM_DOWN) {
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s) epilogue_single(a, acc[s][t], sc, orow, q0 + s);
+    } else {
+#pragma unroll
+      for (int s = 0; s < NSUB; s += 2) epilogue_pair<MODE>(a, acc[s][t], acc[s + 1][t], sc, orow, (q0 + s) >> 1);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------- launch
+
+constexpr int DEC_NSUB = 2;       // decode: 32 weight rows per workgroup
+constexpr int PRE_NSUB_GU = 4;    // prefill gate_up: 2 gate + 2 up tiles per wave
+constexpr int PRE_NSUB_DN = 2;    // prefill down: 32 rows per wave (each tile meets h_hi and h_lo)
+constexpr int PRE_TSUB = 8;       // prefill: 128 token rows per tile
+
+template <int MODE>
+static void launch_mode(bool decode, int max_tiles, const GemmArgs& a, hipStream_t s) {
+  const int nsub16 = a.N / 16;
+  if (decode) {
+    dim3 grid((nsub16 + DEC_NSUB - 1) / DEC_NSUB, max_tiles);
+    hipLaunchKernelGGL((gemm_decode_kernel<MODE, DEC_NSUB>), grid, dim3(256), 0, s, a);
+  } else {
+    constexpr int NS = MODE == GEMM_DOWN ? PRE_NSUB_DN : PRE_NSUB_GU;
+    dim3 grid((nsub16 + 4 * NS - 1) / (4 * NS), max_tiles);
+    hipLaunchKernelGGL((gemm_prefill_kernel<MODE, NS, PRE_TSUB>), grid, dim3(256), 0, s, a);
+  }
+}
+
+hipError_t launch_gemm(GemmMode mode, bool decode, int max_tiles, const GemmArgs& a, hipStream_t s) {
+  if (max_tiles <= 0) return hipSuccess;
+  switch (mode) {
+    case GEMM_GATEUP_BF16: launch_mode<GEMM_GATEUP_BF16>(decode, max_tiles, a, s); break;
+    case GEMM_GATEUP_FP4: launch_mode<GEMM_GATEUP_FP4>(decode, max_tiles, a, s); break;
+    case GEMM_DOWN: launch_mode<GEMM_DOWN>(decode, max_tiles, a, s); break;
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------- combine
+// out[t] = bf16( sum_j w[t][j] * y[inv[t][j]]  (+ y_shared[t]) ), fp32, picks in
+// order, shared expert last ([vllm.cpp] "Device-resident decode campaign",
+// MoeCombineKernel: device FMA of the topk_weights over the expert outputs).
+__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
+  const int t = blockIdx.x;
+  const int rows = a.T * a.k;
+  for (int c = threadIdx.x; c < a.H / 4; c += blockDim.x) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < a.k; ++j) {
+      const int r = a.inv[t * a.k + j];
+      const float wj = a.w[t * a.k + j];
+      const f32x4 v = *(const f32x4*)(a.y + (size_t)r * a.H + c * 4);
+      acc.x = __builtin_fmaf(wj, v.x, acc.x);
+      acc.y = __builtin_fmaf(wj, v.y, acc.y);
+      acc.z = __builtin_fmaf(wj, v.z, acc.z);
+      acc.w = __builtin_fmaf(wj, v.w, acc.w);
+    }
+    for (int sh = 0; sh < a.S; ++sh) acc += *(const f32x4*)(a.y + (size_t)(rows + sh * a.T + t) * a.H + c * 4);
+    *(u32x2*)(a.out + (size_t)t * a.H + c * 4) =
+        u32x2{f32_to_bf16_rne(acc.x) | (f32_to_bf16_rne(acc.y) << 16),
+              f32_to_bf16_rne(acc.z) | (f32_to_bf16_rne(acc.w) << 16)};
+  }
+}
+
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
+  if (a.T <= 0) return hipSuccess;
+  hipLaunchKernelGGL(combine_kernel, dim3(a.T), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace nvmoe

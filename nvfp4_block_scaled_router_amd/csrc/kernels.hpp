@@ -1,0 +1,102 @@
+// Internal launcher interface between api.cpp (host validation, planning) and the
+// HIP kernels. Not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace nvmoe {
+
+constexpr int PLAN_CHUNK = 1024;   // tokens per permutation pass (one per plan thread)
+constexpr int DECODE_TILE_ROWS = 16;
+constexpr int PREFILL_TILE_ROWS = 128;
+
+struct RouteArgs {
+  const float* logits;   // [T][E]
+  int T, E, k, score;
+  int32_t* ids;          // [T][k] workspace
+  float* w;              // [T][k] workspace
+  int32_t* ids_user;     // optional copies for the caller
+  float* w_user;
+};
+
+struct PlanArgs {
+  const int32_t* ids;    // [T][k]
+  int T, E, k, G;        // G = E + shared groups
+  int tile_rows;         // M of the GEMM tiles
+  int32_t* counts;       // [G]
+  int32_t* offsets;      // [G+1]
+  int32_t* perm;         // [T*k]
+  int32_t* inv;          // [T*k]
+  int32_t* tok;          // [T*k + S*T] token of each row
+  int32_t* tile_group;   // [max tiles]
+  int32_t* tile_row0;    // [max tiles]
+  int32_t* tile_count;   // [1]
+  int32_t* counts_user;  // optional [E]
+  int32_t* offsets_user; // optional [E+1]
+  int32_t* perm_user;    // optional [T*k]
+};
+
+hipError_t launch_route_plan(const RouteArgs& r, const PlanArgs& p, bool fused, hipStream_t s);
+
+// Activation / weight quantiser.
+hipError_t launch_quant_rows_bf16(const uint16_t* x, int rows, int K, uint8_t* packed, uint8_t* scales,
+                                  float* gs, hipStream_t s);
+hipError_t launch_quant_groups_f32(const float* x, int groups, int rows_per_group, int K, uint8_t* packed,
+                                   uint8_t* scales, float* gs, hipStream_t s);
+
+// Weight re-layout.
+struct PackArgs {
+  const uint8_t* packed;   // boundary layout [G][N][K/2]
+  const uint8_t* scales;   // [G][N][K/16]
+  const float* gs;         // [G]
+  int G, N, K;
+  int gate_up;             // 1: interleave gate/up 16-row tiles
+  uint8_t* fp4_out;        // [G][N/16][KC][64][16]
+  uint8_t* sc_out;         // [G][N/16][KSG][64][16]
+  float* gs_out;           // [G]
+};
+hipError_t launch_pack(const PackArgs& a, hipStream_t s);
+
+// Grouped GEMMs.
+enum GemmMode { GEMM_GATEUP_BF16 = 0, GEMM_GATEUP_FP4 = 1, GEMM_DOWN = 2 };
+
+struct GemmArgs {
+  // weights (packed layout of one projection, G groups)
+  const uint8_t* wfp4;
+  const uint8_t* wsc;
+  const float* wgs;        // [G]
+  int N, K;                // projection rows, columns
+  // token rows
+  const int32_t* tok;      // row -> token (gather modes)
+  const uint16_t* x;       // bf16 [T][K] (GATEUP_BF16) or h_hi [rows][K] (DOWN)
+  const uint16_t* xlo;     // h_lo [rows][K] (DOWN): h = h_hi + h_lo
+  const uint8_t* xq;       // [T][K/2]  (GATEUP_FP4)
+  const uint8_t* xs;       // [T][K/16]
+  const float* xg;         // [T]
+  // tile list
+  const int32_t* tile_group;
+  const int32_t* tile_row0;
+  const int32_t* tile_count;
+  const int32_t* offsets;  // [G+1] row ranges of the groups
+  // output: gate_up -> h as two bf16 planes [rows][N/2] (hi = bf16(h), lo = bf16(h - hi));
+  // down -> y fp32 [rows][N]
+  uint16_t* out;
+  uint16_t* out_lo;
+  float* yout;
+};
+hipError_t launch_gemm(GemmMode mode, bool decode, int max_tiles, const GemmArgs& a, hipStream_t s);
+
+struct CombineArgs {
+  const float* y;          // fp32 [rows_total][H] expert outputs
+  const float* w;          // [T][k]
+  const int32_t* inv;      // [T*k]
+  int T, H, k, S;
+  uint16_t* out;           // bf16 [T][H]
+};
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+
+size_t plan_lds_bytes(int E, int G);
+
+}  // namespace nvmoe

@@ -1,0 +1,177 @@
+// NVFP4 quantiser: per-group FP32 global scale, per-16 E4M3 block scales, E2M1 codes.
+//
+// Global scale gs = max|x| / (6 * 448) ([megamoe] archived CORRECTNESS_BACKLOG §7,
+// "Runtime Activation Global Scale": computed at run time from the activation so
+// that no E4M3 block scale overflows). The blocks follow the NVFP4 format of
+// [megamoe] README "NVFP4 throughout" (16-element microblocks, E4M3 scales, E2M1
+// values). Every step is one binary32 operation rounded to nearest even; this
+// file is compiled without contraction and with correctly rounded division, so
+// the bytes are a pure function of the input bits:
+//   s_b  = gs == 0 ? 0 : E4M3_rne_sat(a_b / (6 * gs))
+//   d_b  = E4M3(s_b) * gs
+//   code = signbit(x) << 3 | (d_b == 0 ? 0 : E2M1_rne_sat(|x| / d_b))
+// One wave quantises one row (activations) or the rows of a group after a
+// reduction kernel has produced the group's global scale (weights).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace nvmoe {
+
+// Nearest E4M3fn code to v >= 0, ties to even, v >= 448 saturates to 0x7E.
+__device__ __forceinline__ uint32_t e4m3_encode_rne_sat(float v) {
+  if (!(v > 0.0f)) return 0u;
+  if (v >= 448.0f) return 0x7Eu;
+  if (v < 0.015625f) return (uint32_t)__builtin_rintf(v * 512.0f);  // subnormals: multiples of 2^-9
+  const int e = (int)((__float_as_uint(v) >> 23) & 0xFFu) - 127;     // v in [2^e, 2^(e+1))
+  const float scale = __uint_as_float((uint32_t)(3 - e + 127) << 23); // exact 2^(3-e)
+  uint32_t m = (uint32_t)__builtin_rintf(v * scale);                 // 8..16
+  int ee = e;
+  if (m == 16u) {
+    m = 8u;
+    ++ee;
+  }
+  return ((uint32_t)(ee + 7) << 3) | (m - 8u);
+}
+
+// Nearest E2M1 magnitude code to r >= 0 (ties to the even code), saturating at 6.
+__device__ __forceinline__ uint32_t e2m1_encode_rne_sat(float r) {
+  return (uint32_t)(r > 0.25f) + (uint32_t)(r >= 0.75f) + (uint32_t)(r > 1.25f) + (uint32_t)(r >= 1.75f) +
+         (uint32_t)(r > 2.5f) + (uint32_t)(r >= 3.5f) + (uint32_t)(r > 5.0f);
+}
+
+__device__ __forceinline__ void load16(const uint16_t* p, float* v) {
+  const u32x4 a = *(const u32x4*)p;
+  const u32x4 b = *(const u32x4*)(p + 8);
+  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+
+__device__ __forceinline__ void load16(const float* p, float* v) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f32x4 a = *(const f32x4*)(p + 4 * i);
+    v[4 * i] = a.x;
+    v[4 * i + 1] = a.y;
+    v[4 * i + 2] = a.z;
+    v[4 * i + 3] = a.w;
+  }
+}
+
+// Quantise one 16-element block with global scale gs; writes 8 code bytes and 1 scale byte.
+__device__ __forceinline__ void quant_block(const float* v, float gs, uint8_t* packed, uint8_t* scale) {
+  float ab = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) ab = fmaxf(ab, fabsf(v[i]));
+  uint32_t s = 0u;
+  if (gs != 0.0f) {
+    const float six_gs = 6.0f * gs;
+    s = e4m3_encode_rne_sat(ab / six_gs);
+  }
+  const float d = e4m3_to_f32(s) * gs;
+  uint32_t lo = 0u, hi = 0u;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    uint32_t code = (__float_as_uint(v[i]) >> 31) << 3;
+    if (d != 0.0f) code |= e2m1_encode_rne_sat(fabsf(v[i]) / d);
+    if (i < 8)
+      lo |= code << (4 * i);
+    else
+      hi |= code << (4 * (i - 8));
+  }
+  *(u32x2*)packed = u32x2{lo, hi};
+  *scale = (uint8_t)s;
+}
+
+template <typename T>
+__device__ __forceinline__ float wave_row_absmax(const T* row, int K) {
+  const int lane = threadIdx.x & (WAVE - 1);
+  float m = 0.0f;
+  for (int b = lane; b < K / 16; b += WAVE) {
+    float v[16];
+    load16(row + (size_t)b * 16, v);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
+  }
+#pragma unroll
+  for (int off = WAVE / 2; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, WAVE));
+  return m;
+}
+
+template <typename T>
+__device__ __forceinline__ void wave_quant_row(const T* row, int K, float gs, uint8_t* packed, uint8_t* scales) {
+  const int lane = threadIdx.x & (WAVE - 1);
+  for (int b = lane; b < K / 16; b += WAVE) {
+    float v[16];
+    load16(row + (size_t)b * 16, v);
+    quant_block(v, gs, packed + (size_t)b * 8, scales + b);
+  }
+}
+
+// One wave per row: global scale of the row, then its blocks.
+__global__ __launch_bounds__(256) void quant_rows_bf16_kernel(const uint16_t* __restrict__ x, int rows, int K,
+                                                              uint8_t* __restrict__ packed,
+                                                              uint8_t* __restrict__ scales, float* __restrict__ gs) {
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const uint16_t* row = x + (size_t)r * K;
+  const float A = wave_row_absmax(row, K);
+  const float g = A / 2688.0f;
+  if ((threadIdx.x & (WAVE - 1)) == 0) gs[r] = g;
+  wave_quant_row(row, K, g, packed + (size_t)r * (K / 2), scales + (size_t)r * (K / 16));
+}
+
+// Group maxima: one 1024-thread workgroup per group, fixed reduction tree.
+__global__ __launch_bounds__(1024) void group_gs_f32_kernel(const float* __restrict__ x, int rows_per_group, int K,
+                                                            float* __restrict__ gs) {
+  __shared__ float part[16];
+  const float* base = x + (size_t)blockIdx.x * rows_per_group * K;
+  const size_t n = (size_t)rows_per_group * K;
+  float m = 0.0f;
+  for (size_t i = (size_t)threadIdx.x * 4; i < n; i += (size_t)blockDim.x * 4) {
+    const f32x4 a = *(const f32x4*)(base + i);
+    m = fmaxf(m, fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))));
+  }
+#pragma unroll
+  for (int off = WAVE / 2; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, WAVE));
+  if ((threadIdx.x & (WAVE - 1)) == 0) part[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float A = 0.0f;
+    for (int i = 0; i < (int)(blockDim.x >> 6); ++i) A = fmaxf(A, part[i]);
+    gs[blockIdx.x] = A / 2688.0f;
+  }
+}
+
+__global__ __launch_bounds__(256) void quant_rows_f32_kernel(const float* __restrict__ x, int rows, int K,
+                                                             int rows_per_group, const float* __restrict__ gs,
+                                                             uint8_t* __restrict__ packed,
+                                                             uint8_t* __restrict__ scales) {
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  wave_quant_row(x + (size_t)r * K, K, gs[r / rows_per_group], packed + (size_t)r * (K / 2),
+                 scales + (size_t)r * (K / 16));
+}
+
+hipError_t launch_quant_rows_bf16(const uint16_t* x, int rows, int K, uint8_t* packed, uint8_t* scales,
+                                  float* gs, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(quant_rows_bf16_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, x, rows, K, packed, scales,
+                     gs);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_groups_f32(const float* x, int groups, int rows_per_group, int K, uint8_t* packed,
+                                   uint8_t* scales, float* gs, hipStream_t s) {
+  if (groups <= 0) return hipSuccess;
+  hipLaunchKernelGGL(group_gs_f32_kernel, dim3(groups), dim3(1024), 0, s, x, rows_per_group, K, gs);
+  const int rows = groups * rows_per_group;
+  hipLaunchKernelGGL(quant_rows_f32_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, x, rows, K, rows_per_group,
+                     gs, packed, scales);
+  return hipGetLastError();
+}
+
+}  // namespace nvmoe

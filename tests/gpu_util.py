@@ -1,0 +1,108 @@
+"""Helpers shared by the GPU parity tests (inputs from synth, expected values from
+the oracle, device results through the C ABI)."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import synth
+import oracle
+import oracle.moe as omoe
+import nvfp4_block_scaled_router_amd as m
+from nvfp4_block_scaled_router_amd.weights import quantize_projection
+
+DEV = torch.device("cuda:0")
+
+# Output tolerance of the layer (fixed for every configuration).
+REL_L2 = 5e-3
+MAX_OVER_RMS = 2e-2
+W_ABS = 1e-6       # routing weights, fp32 vs fp64
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def up(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def bf16(x_u16: np.ndarray) -> torch.Tensor:
+    return up(x_u16.view(np.int16)).view(torch.bfloat16)
+
+
+def out_metrics(o_gpu: torch.Tensor, ref: np.ndarray):
+    o = o_gpu.float().cpu().numpy().astype(np.float64)
+    rel = np.linalg.norm(o - ref) / np.linalg.norm(ref)
+    mx = np.abs(o - ref).max() / np.sqrt(np.mean(ref * ref))
+    return rel, mx
+
+
+def check_out(o_gpu, ref, what=""):
+    rel, mx = out_metrics(o_gpu, ref)
+    log(f"  {what} relL2 {rel:.3e} (<= {REL_L2}), max|d|/rms {mx:.3e} (<= {MAX_OVER_RMS})")
+    assert rel <= REL_L2 and mx <= MAX_OVER_RMS, (rel, mx)
+    assert np.all(np.isfinite(o_gpu.float().cpu().numpy()))
+
+
+def gpu_weights(cfg, which):
+    """Weights quantised on the device by the library from the synth fp32 draws."""
+    G = cfg.shared if which.startswith("ws") else cfg.E
+    N, K = (2 * cfg.I, cfg.H) if which in ("w1", "ws1") else (cfg.H, cfg.I)
+    return quantize_projection(G, N, K, lambda e0, c: synth.expert_weights_f32(cfg, which, e0, c), DEV,
+                               progress=log)
+
+
+_WCACHE = {}
+
+
+def oracle_weights(cfg, which, experts):
+    """Oracle-quantised weights, cached per (config, projection, expert set)."""
+    key = (cfg, which, None if experts is None else tuple(experts))
+    if key not in _WCACHE:
+        if len(_WCACHE) > 8:
+            _WCACHE.clear()
+        _WCACHE[key] = omoe.quantized_weights(cfg, which, experts)
+    return _WCACHE[key]
+
+
+class Case:
+    """One configuration on both sides: oracle expectations and the device layer."""
+
+    def __init__(self, cfg, tokens=None, weights="oracle"):
+        self.cfg = cfg
+        self.x = synth.activations(cfg)
+        self.logits = synth.logits(cfg)
+        o = oracle.default()
+        self.ids_ref, self.w_ref = o.route(self.logits, cfg.k, cfg.score)
+        self.tokens = np.arange(cfg.T, dtype=np.int32) if tokens is None else np.asarray(tokens, np.int32)
+        need = sorted(set(self.ids_ref[self.tokens].reshape(-1).tolist()))
+        if weights == "oracle":
+            W = [oracle_weights(cfg, w, need if w in ("w1", "w2") else None)
+                 for w in (["w1", "w2"] + (["ws1", "ws2"] if cfg.shared else []))]
+            dev = [[up(a) for a in Wi] for Wi in W]
+        else:  # device quantiser for every expert; oracle quantises the experts it needs
+            dev = [gpu_weights(cfg, w) for w in (["w1", "w2"] + (["ws1", "ws2"] if cfg.shared else []))]
+            W = [omoe.quantized_weights(cfg, w, need if w in ("w1", "w2") else None)
+                 for w in (["w1", "w2"] + (["ws1", "ws2"] if cfg.shared else []))]
+            for Wi, Di in zip(W, dev):               # the two quantisers agree on what the oracle uses
+                sel = need if Wi[0].shape[0] == cfg.E else list(range(Wi[0].shape[0]))
+                for a, d in zip(Wi, Di):
+                    assert np.array_equal(a[sel], d[sel].cpu().numpy()), "device weight quantiser differs"
+        self.W = W
+        self.dev_w = dev
+        self.need = need
+
+    def reference(self):
+        W1, W2 = self.W[0], self.W[1]
+        WS1, WS2 = (self.W[2], self.W[3]) if self.cfg.shared else (None, None)
+        return omoe.forward(self.cfg, self.x, self.logits, W1, W2, WS1, WS2, tokens=self.tokens)
+
+    def layer(self, max_tokens=None):
+        L = m.MoeLayer.from_config(self.cfg, max_tokens=max_tokens, device=DEV)
+        ws = self.dev_w
+        L.pack(ws[0], ws[1], ws[2] if self.cfg.shared else None, ws[3] if self.cfg.shared else None)
+        return L

@@ -1,0 +1,131 @@
+"""The C-ABI library on the CPU: it loads, exports every entry point the header
+declares, and its host-side validation returns the documented codes before
+anything is enqueued (no call here reaches a GPU)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import nvfp4_block_scaled_router_amd as m
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4_moe.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**\s*(moe_[a-z0-9_]+)\s*\(", text,
+                                 flags=re.M)))
+
+
+def test_header_declares_the_binding_names():
+    assert declared_functions() == sorted(m.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    L = m.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    assert m.moe_abi_version() == m.MOE_ABI_VERSION
+
+
+def desc(**kw):
+    base = dict(hidden=256, inter=128, num_experts=8, top_k=2, max_tokens=16)
+    base.update(kw)
+    extra = {k: base.pop(k) for k in ("score", "act", "num_shared", "abi_version") if k in base}
+    return m.make_desc(**base, **extra)
+
+
+def plan_rc(d):
+    plan, pb, wb = ctypes.c_void_p(), ctypes.c_size_t(), ctypes.c_size_t()
+    rc = m.lib().moe_plan(ctypes.byref(d), ctypes.byref(plan), ctypes.byref(pb), ctypes.byref(wb))
+    if rc == 0:
+        m.moe_plan_destroy(plan.value)
+    return rc
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(), m.MOE_OK),
+    (dict(abi_version=7), m.MOE_ERR_ABI),
+    (dict(hidden=200), m.MOE_ERR_SHAPE),
+    (dict(hidden=0), m.MOE_ERR_SHAPE),
+    (dict(inter=96), m.MOE_ERR_SHAPE),
+    (dict(num_experts=0), m.MOE_ERR_SHAPE),
+    (dict(num_experts=1025), m.MOE_ERR_SHAPE),
+    (dict(top_k=9), m.MOE_ERR_SHAPE),
+    (dict(top_k=0), m.MOE_ERR_SHAPE),
+    (dict(max_tokens=0), m.MOE_ERR_SHAPE),
+    (dict(num_shared=2), m.MOE_ERR_SHAPE),
+    (dict(score=5), m.MOE_ERR_ENUM),
+    (dict(act=3), m.MOE_ERR_ENUM),
+])
+def test_plan_validation(kw, code):
+    assert plan_rc(desc(**kw)) == code
+
+
+def test_plan_sizes_cover_the_layout():
+    # deepseek-v3-shaped layer: packed bytes are 0.5625 B per weight plus small tile padding
+    d = desc(hidden=7168, inter=2048, num_experts=256, top_k=8, max_tokens=8192, score="sigmoid", num_shared=1)
+    plan, pb, wb = m.moe_plan(d)
+    m.moe_plan_destroy(plan)
+    weights = 257 * 3 * 2048 * 7168
+    assert weights * 0.5625 <= pb <= weights * 0.5625 * 1.01
+    rows = 8192 * 9
+    assert wb >= rows * (2048 * 4 + 7168 * 4)  # h as two bf16 planes, expert outputs in fp32
+
+
+def test_run_rejects_before_enqueue():
+    plan, pb, wb = m.moe_plan(desc())
+    L = m.lib()
+    fake = 1 << 20        # 16-byte aligned addresses that are never dereferenced
+    try:
+        assert L.moe_run(None, fake, 4, fake, fake, fake, None, fake, wb, None) == m.MOE_ERR_NULL
+        assert L.moe_run(plan, fake, 17, fake, fake, fake, None, fake, wb, None) == m.MOE_ERR_TOKENS
+        assert L.moe_run(plan, fake, -1, fake, fake, fake, None, fake, wb, None) == m.MOE_ERR_TOKENS
+        assert L.moe_run(plan, fake, 4, fake, fake, fake, None, fake, wb - 1, None) == m.MOE_ERR_SIZE
+        assert L.moe_run(plan, fake + 2, 4, fake, fake, fake, None, fake, wb, None) == m.MOE_ERR_ALIGN
+        assert L.moe_run(plan, fake, 4, fake, fake, fake, None, fake + 8, wb, None) == m.MOE_ERR_ALIGN
+        assert L.moe_run(plan, fake, 0, fake, fake, fake, None, fake, wb, None) == m.MOE_OK   # nothing to do
+        r = m.routing_out(topk_ids=fake + 2)
+        assert L.moe_run(plan, fake, 4, fake, fake, fake, ctypes.byref(r), fake, wb, None) == m.MOE_ERR_ALIGN
+        t = m.nvfp4_tensor(fake, fake, fake)
+        assert L.moe_pack_weights(plan, ctypes.byref(t), ctypes.byref(t), None, None, fake, pb - 1, None) == m.MOE_ERR_SIZE
+        assert L.moe_pack_weights(plan, ctypes.byref(t), None, None, None, fake, pb, None) == m.MOE_ERR_NULL
+        assert L.moe_quantize_nvfp4_rows(fake, 4, 40, fake, fake, fake, None) == m.MOE_ERR_SHAPE
+        assert L.moe_quantize_nvfp4_rows(fake + 4, 4, 64, fake, fake, fake, None) == m.MOE_ERR_ALIGN
+        assert L.moe_quantize_nvfp4_weights(fake, 1, 0, 64, fake, fake, fake, None) == m.MOE_ERR_SHAPE
+    finally:
+        m.moe_plan_destroy(plan)
+    with pytest.raises(RuntimeError, match="token count"):
+        p2, _, w2 = m.moe_plan(desc())
+        try:
+            m.moe_run(p2, fake, 99, fake, fake, fake, None, fake, w2, stream=0)
+        finally:
+            m.moe_plan_destroy(p2)
+
+
+def test_validate_weights_host():
+    d = desc()
+    G, N, K = 8, 256, 256
+    packed = np.zeros((G, N, K // 2), np.uint8)
+    scales = np.full((G, N, K // 16), 0x38, np.uint8)
+    gs = np.ones(G, np.float32)
+    t = m.nvfp4_tensor(packed.ctypes.data, scales.ctypes.data, gs.ctypes.data)
+    assert m.moe_validate_weights_host(d, t, 0) == m.MOE_OK
+    scales[3, 7, 2] = 0x7F                              # E4M3fn NaN
+    assert m.moe_validate_weights_host(d, t, 0) == m.MOE_ERR_WEIGHT
+    scales[3, 7, 2] = 0xB8                              # negative scale
+    assert m.moe_validate_weights_host(d, t, 0) == m.MOE_ERR_WEIGHT
+    scales[3, 7, 2] = 0x38
+    gs[5] = np.inf
+    assert m.moe_validate_weights_host(d, t, 0) == m.MOE_ERR_WEIGHT
+    gs[5] = 1.0
+    assert m.moe_validate_weights_host(d, t, 4) == m.MOE_ERR_ENUM
+
+
+def test_strerror_covers_every_code():
+    for code in range(-8, 1):
+        assert m.moe_strerror(code) and m.moe_strerror(code) != "unknown error"

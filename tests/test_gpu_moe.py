@@ -1,0 +1,118 @@
+"""GPU parity of the whole layer against the CPU oracle (through the C ABI)."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_util import Case, DEV, bf16, check_out, log, up, W_ABS
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_and_check(case: Case):
+    cfg = case.cfg
+    log(f"[{cfg.name}] T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} k={cfg.k} act={cfg.act} shared={cfg.shared} "
+        f"checked tokens {len(case.tokens)}")
+    ref = case.reference()
+    L = case.layer()
+    x = bf16(case.x)
+    lg = up(case.logits)
+    bufs, rout = L.routing_buffers(cfg.T)
+    out = L(x, lg, routing=rout)
+    torch.cuda.synchronize()
+    assert np.array_equal(bufs["topk_ids"].cpu().numpy(), ref["ids"]), "topk ids"
+    assert np.abs(bufs["topk_weights"].cpu().numpy() - ref["w"]).max() <= W_ABS, "topk weights"
+    assert np.array_equal(bufs["expert_counts"].cpu().numpy(), ref["counts"]), "counts"
+    assert np.array_equal(bufs["expert_offsets"].cpu().numpy(), ref["offsets"]), "offsets"
+    assert np.array_equal(bufs["perm"].cpu().numpy(), ref["perm"]), "perm"
+    if cfg.act == "nvfp4":
+        assert np.array_equal(bufs["act_packed"].cpu().numpy(), ref["xq"]), "quantised activation codes"
+        assert np.array_equal(bufs["act_scales"].cpu().numpy(), ref["xs"]), "quantised activation scales"
+        assert np.array_equal(bufs["act_global"].cpu().numpy().view(np.uint32), ref["xg"].view(np.uint32))
+    check_out(out[torch.from_numpy(case.tokens).long().to(DEV)], ref["out"], cfg.name)
+    return L, x, lg, out
+
+
+SMALL = [
+    synth.tiny(),
+    synth.with_tokens(synth.tiny(), 13, "tiny-t13"),
+    synth.with_tokens(synth.tiny(), 200, "tiny-prefill-t200"),
+    synth.with_tokens(synth.skewed_w4a4(), 48, "skewed-w4a4-t48"),
+    synth.with_tokens(synth.qwen3_prefill(), 300, "qwen3-prefill-t300"),
+    synth.MoeConfig("one-expert", T=5, H=128, I=128, E=1, k=1, seed=11),
+    synth.MoeConfig("all-experts", T=40, H=256, I=128, E=8, k=8, score="sigmoid", seed=12),
+    synth.MoeConfig("shared-small", T=70, H=256, I=256, E=16, k=4, score="sigmoid", shared=1, seed=13),
+    synth.MoeConfig("shared-small-w4a4", T=150, H=512, I=128, E=8, k=2, shared=1, act="nvfp4", seed=14),
+]
+
+
+@pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
+def test_small(cfg):
+    _run_and_check(Case(cfg))
+
+
+@pytest.mark.parametrize("T", synth.DECODE_TOKENS)
+def test_qwen3_decode(T):
+    _run_and_check(Case(synth.qwen3_decode(T)))
+
+
+def test_qwen3_prefill_sampled():
+    cfg = synth.qwen3_prefill()
+    _run_and_check(Case(cfg, tokens=synth.token_sample(cfg, 48)))
+
+
+def test_skewed_w4a4_sampled():
+    cfg = synth.skewed_w4a4()
+    _run_and_check(Case(cfg, tokens=synth.token_sample(cfg, 64)))
+
+
+def test_deepseek_v3_sampled():
+    cfg = synth.deepseek_v3()
+    _run_and_check(Case(cfg, tokens=synth.token_sample(cfg, 6), weights="gpu"))
+
+
+def test_deterministic_and_graph_replay():
+    """Byte-identical repeats, and HIP-graph replays equal to the eager result."""
+    cfg = synth.with_tokens(synth.qwen3_prefill(), 300, "qwen3-prefill-t300")
+    case = Case(cfg)
+    L = case.layer()
+    x, lg = bf16(case.x), up(case.logits)
+    a = L(x, lg).clone()
+    b = L(x, lg).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    out = torch.empty_like(a)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        L(x, lg, out=out)                       # warm on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        L(x, lg, out=out)
+    for i in range(3):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), a.view(torch.int16)), f"replay {i}"
+        c = L(x, lg).clone()                    # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(c.view(torch.int16), a.view(torch.int16))
+
+
+def test_token_counts_within_capacity():
+    """One plan (T_max = 300) serves smaller live T (both kernel regimes); T = 0 enqueues nothing."""
+    cfg = synth.with_tokens(synth.qwen3_prefill(), 300, "qwen3-prefill-t300")
+    case = Case(cfg)
+    ref = case.reference()["out"]
+    L = case.layer()
+    x, lg = bf16(case.x), up(case.logits)
+    for T in (1, 17, 129, 300):
+        part = L(x[:T], lg[:T])
+        torch.cuda.synchronize()
+        check_out(part, ref[:T], f"T={T} of capacity 300")   # a token's output depends on that token only
+    sentinel = torch.full((1, cfg.H), 7.0, dtype=torch.bfloat16, device=DEV)
+    import nvfp4_block_scaled_router_amd as m
+    m.moe_run(L.plan, L.packed, 0, x, lg, sentinel, None, L.workspace, L.workspace_bytes)
+    torch.cuda.synchronize()
+    assert torch.all(sentinel == 7.0)
