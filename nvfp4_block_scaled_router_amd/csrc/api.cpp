@@ -21,7 +21,6 @@ constexpr int MAX_HIDDEN = 16384;
 constexpr int MAX_EXPERTS = 1024;
 constexpr int MAX_TOPK = 64;
 constexpr int MAX_TOKENS = 65536;
-constexpr int FUSED_ROUTE_MAX_T = 128;   // route inside the single plan workgroup up to this T
 
 size_t align_up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
 
@@ -46,8 +45,8 @@ struct moe_plan {
   int G;
   ProjLayout w1, w2;
   size_t off_w1f, off_w1s, off_w1g, off_w2f, off_w2s, off_w2g, packed_bytes;
-  size_t ws_ids, ws_w, ws_counts, ws_offsets, ws_perm, ws_inv, ws_tok, ws_tgrp, ws_trow, ws_tcnt;
-  size_t ws_xq, ws_xs, ws_xg, ws_h, ws_y, ws_bytes;
+  size_t ws_ids, ws_w, ws_counts, ws_offsets, ws_perm, ws_inv, ws_tok, ws_tgrp, ws_trow, ws_tcnt, ws_plan;
+  size_t ws_xq, ws_xs, ws_xg, ws_x16, ws_h, ws_y, ws_bytes;
   int max_tiles;
 };
 
@@ -123,9 +122,11 @@ int moe_plan(const moe_desc* desc, moe_plan_t** plan, size_t* packed_bytes, size
   p->ws_tgrp = o; o = align_up(o + 4 * (size_t)p->max_tiles);
   p->ws_trow = o; o = align_up(o + 4 * (size_t)p->max_tiles);
   p->ws_tcnt = o; o = align_up(o + 16);
+  p->ws_plan = o; o = align_up(o + 4 * plan_scratch_ints(Tm, k, E));
   p->ws_xq = o; o = align_up(o + (desc->act_format == MOE_ACT_NVFP4_ROWQ ? (size_t)Tm * H / 2 : 0));
   p->ws_xs = o; o = align_up(o + (desc->act_format == MOE_ACT_NVFP4_ROWQ ? (size_t)Tm * H / 16 : 0));
-  p->ws_xg = o; o = align_up(o + (desc->act_format == MOE_ACT_NVFP4_ROWQ ? 4 * (size_t)Tm : 0));
+  p->ws_xg = o; o = align_up(o + 4 * (size_t)Tm);      // per-row activation factor (either format)
+  p->ws_x16 = o; o = align_up(o + (desc->act_format == MOE_ACT_BF16 ? 2 * (size_t)Tm * H : 0));
   p->ws_h = o; o = align_up(o + 2 * 2 * rows * I);   // h_hi and h_lo planes
   p->ws_y = o; o = align_up(o + 4 * rows * H);
   p->ws_bytes = o;
@@ -232,18 +233,21 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
   const bool fp4 = d.act_format == MOE_ACT_NVFP4_ROWQ;
   hipError_t e;
 
-  uint8_t* xq = r.act_packed ? r.act_packed : ws + plan->ws_xq;
-  uint8_t* xs = r.act_scales ? r.act_scales : ws + plan->ws_xs;
-  float* xg = r.act_global ? r.act_global : (float*)(ws + plan->ws_xg);
-  if (fp4) {
-    if ((e = mark(ev, 2 * MOE_STAGE_QUANT, s)) != hipSuccess) return (int)e;
+  uint8_t* xq = (fp4 && r.act_packed) ? r.act_packed : ws + plan->ws_xq;
+  uint8_t* xs = (fp4 && r.act_scales) ? r.act_scales : ws + plan->ws_xs;
+  float* xg = (fp4 && r.act_global) ? r.act_global : (float*)(ws + plan->ws_xg);
+  uint16_t* x16 = (uint16_t*)(ws + plan->ws_x16);
+  if ((e = mark(ev, 2 * MOE_STAGE_QUANT, s)) != hipSuccess) return (int)e;
+  if (fp4)
     e = launch_quant_rows_bf16(x, T, H, xq, xs, xg, s);
-    if (e != hipSuccess) return (int)e;
-    if ((e = mark(ev, 2 * MOE_STAGE_QUANT + 1, s)) != hipSuccess) return (int)e;
-  }
+  else
+    e = launch_rows_to_f16(x, T, H, x16, xg, s);
+  if (e != hipSuccess) return (int)e;
+  if ((e = mark(ev, 2 * MOE_STAGE_QUANT + 1, s)) != hipSuccess) return (int)e;
 
   const bool decode = use_decode(T, k, E);
   const int M = decode ? DECODE_TILE_ROWS : PREFILL_TILE_ROWS;
+  const GemmRegime regime = decode ? REGIME_DECODE_KSPLIT : REGIME_PREFILL;
   RouteArgs ra;
   ra.logits = router_logits;
   ra.T = T;
@@ -273,7 +277,7 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
   pa.offsets_user = r.expert_offsets;
   pa.perm_user = r.perm;
   if ((e = mark(ev, 2 * MOE_STAGE_ROUTE, s)) != hipSuccess) return (int)e;
-  e = launch_route_plan(ra, pa, T <= FUSED_ROUTE_MAX_T, s);
+  e = launch_route_plan(ra, pa, (int32_t*)(ws + plan->ws_plan), s);
   if (e != hipSuccess) return (int)e;
   if ((e = mark(ev, 2 * MOE_STAGE_ROUTE + 1, s)) != hipSuccess) return (int)e;
 
@@ -286,7 +290,7 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
   g1.N = 2 * I;
   g1.K = H;
   g1.tok = pa.tok;
-  g1.x = x;
+  g1.x = x16;
   g1.xq = xq;
   g1.xs = xs;
   g1.xg = xg;
@@ -298,7 +302,7 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
   const size_t hplane = ((size_t)d.max_tokens * k + (size_t)S * d.max_tokens) * I;
   g1.out_lo = g1.out + hplane;
   if ((e = mark(ev, 2 * MOE_STAGE_GATE_UP, s)) != hipSuccess) return (int)e;
-  e = launch_gemm(fp4 ? GEMM_GATEUP_FP4 : GEMM_GATEUP_BF16, decode, max_tiles, g1, s);
+  e = launch_gemm(fp4 ? GEMM_GATEUP_FP4 : GEMM_GATEUP_BF16, regime, max_tiles, g1, s);
   if (e != hipSuccess) return (int)e;
   if ((e = mark(ev, 2 * MOE_STAGE_GATE_UP + 1, s)) != hipSuccess) return (int)e;
 
@@ -313,7 +317,7 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
   g2.out = nullptr;
   g2.yout = (float*)(ws + plan->ws_y);
   if ((e = mark(ev, 2 * MOE_STAGE_DOWN, s)) != hipSuccess) return (int)e;
-  e = launch_gemm(GEMM_DOWN, decode, max_tiles, g2, s);
+  e = launch_gemm(GEMM_DOWN, regime, max_tiles, g2, s);
   if (e != hipSuccess) return (int)e;
   if ((e = mark(ev, 2 * MOE_STAGE_DOWN + 1, s)) != hipSuccess) return (int)e;
 

@@ -7,6 +7,8 @@
 namespace nvmoe {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -66,6 +68,35 @@ __device__ __forceinline__ bf16x8 dequant8(uint32_t w, float s) {
   f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
   o.w = __builtin_amdgcn_perm(__float_as_uint(f.y * s), __float_as_uint(f.x * s), 0x07060302u);
   return __builtin_bit_cast(bf16x8, o);
+}
+
+// An E4M3 block scale s split as s = p2 * sig: p2 a power of two (fp32, for the exponent-only
+// scale operand of the fp4 convert) and sig its significand as an fp16 pair for
+// v_pk_mul_f16: normal s = 2^(e-7) * (1 + m/8); subnormal s = 2^-9 * m (sig = m, 0..7).
+__device__ __forceinline__ void e4m3_split(uint32_t b, float& p2, uint32_t& sig2) {
+  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+  // fp16 bits of 0..7: 0, 1, 2, 3, 4, 5, 6, 7
+  const uint32_t small = m == 0u ? 0u : (m == 1u ? 0x3C00u : (m < 4u ? 0x4000u | ((m - 2u) << 9) : 0x4400u | ((m - 4u) << 8)));
+  const uint32_t sig = e ? (0x3C00u | (m << 7)) : small;
+  p2 = __uint_as_float((e ? e + 120u : 118u) << 23);
+  sig2 = sig | (sig << 16);
+}
+
+// Eight E2M1 codes times one E4M3 block scale as fp16: the convert applies the power of two,
+// one packed fp16 multiply applies the significand. q * s has at most 6 significant bits and
+// lies in [2^-10, 2688], inside fp16's normal range, so both steps are exact.
+__device__ __forceinline__ f16x8 dequant8_f16(uint32_t w, float p2, uint32_t sig2) {
+  const f16x2 sg = __builtin_bit_cast(f16x2, sig2);
+  u32x4 o;
+  o.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, p2, 0) * sg);
+  o.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, p2, 1) * sg);
+  o.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, p2, 2) * sg);
+  o.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, p2, 3) * sg);
+  return __builtin_bit_cast(f16x8, o);
+}
+
+__device__ __forceinline__ f32x4 mfma16x16x32_f16(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
 // fp32 -> bf16 bits, round to nearest even (finite inputs).

@@ -11,11 +11,17 @@
 // campaign": grouped kernels with a per-group weight-row index, then MoeCombineKernel.)
 //
 // Dequant route: the per-16 E4M3 block scale is not a power of two and covers half
-// an E8M0 block of the scaled MFMA, so each weight is rebuilt exactly as a bf16
-// (E2M1 x E4M3 has at most 6 significant bits) by the fp4->fp32 convert, one fp32
-// multiply and a truncating pack, and fed to V_MFMA_F32_16X16X32_BF16 with fp32
-// accumulation. Global scales (per expert, per activation row) are constant over K
-// and are applied once in the epilogue.
+// an E8M0 block of the scaled MFMA, so each weight q*s (at most 6 significant bits) is
+// rebuilt exactly in registers and fed to a 16-bit MFMA with fp32 accumulation:
+//  - gate_up (2/3 of the weight bytes): fp16. The convert applies the power of two of
+//    s (its scale operand is exponent-only), one packed fp16 multiply the significand:
+//    1 VALU op per weight. Activations are fp16 too: bf16 rows rescaled exactly by a
+//    power of two into fp16 range (undone in the epilogue), NVFP4 rows decoded the
+//    same way as the weights. V_MFMA_F32_16X16X32_F16.
+//  - down: bf16 (h's range is not known when it is written): fp4->fp32 convert, fp32
+//    multiply, truncating pack, 2 VALU ops per weight. V_MFMA_F32_16X16X32_BF16.
+// Global scales (per expert, per activation row) are constant over K and are applied
+// once in the epilogue.
 //
 // Operand roles: MFMA A = 16 weight rows x 32 k (one lane: row l%16, 8 consecutive
 // k of a 32-wide lane group), MFMA B = 32 k x 16 tokens (lane: token l%16, the same
@@ -34,11 +40,46 @@ __device__ __forceinline__ uint32_t pick_dword(const u32x4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
-// The two block scales (fp32) of chunk c (0..7 inside its scale group) for this lane.
-__device__ __forceinline__ void chunk_scales(const u32x4& sg, int c, float& s0, float& s1) {
-  const uint32_t pair = pick_dword(sg, c >> 1) >> (16 * (c & 1));
-  s0 = e4m3_to_f32(pair & 0xFFu);
-  s1 = e4m3_to_f32((pair >> 8) & 0xFFu);
+// The two raw block-scale bytes of chunk c of this lane.
+__device__ __forceinline__ uint32_t chunk_scale_bytes(const u32x4& sg, int c) {
+  return (pick_dword(sg, c >> 1) >> (16 * (c & 1))) & 0xFFFFu;
+}
+
+// Dequantised MFMA A operands of one 16-row weight tile for one 128-column chunk: fp16
+// for gate_up, bf16 for down (j-th operand = columns 32*(l/16) + 8j .. +7 of the lane).
+template <bool F16>
+struct WOps;
+template <>
+struct WOps<true> {
+  f16x8 v[4];
+  __device__ __forceinline__ void make(const u32x4& w, uint32_t sb) {
+    float pa, pb;
+    uint32_t sa, sb2;
+    e4m3_split(sb & 0xFFu, pa, sa);
+    e4m3_split(sb >> 8, pb, sb2);
+    v[0] = dequant8_f16(w.x, pa, sa);
+    v[1] = dequant8_f16(w.y, pa, sa);
+    v[2] = dequant8_f16(w.z, pb, sb2);
+    v[3] = dequant8_f16(w.w, pb, sb2);
+  }
+};
+template <>
+struct WOps<false> {
+  bf16x8 v[4];
+  __device__ __forceinline__ void make(const u32x4& w, uint32_t sb) {
+    const float s0 = e4m3_to_f32(sb & 0xFFu), s1 = e4m3_to_f32(sb >> 8);
+    v[0] = dequant8(w.x, s0);
+    v[1] = dequant8(w.y, s0);
+    v[2] = dequant8(w.z, s1);
+    v[3] = dequant8(w.w, s1);
+  }
+};
+
+__device__ __forceinline__ f32x4 mfma_any(const f16x8& a, const u32x4& b, f32x4 c) {
+  return mfma16x16x32_f16(a, __builtin_bit_cast(f16x8, b), c);
+}
+__device__ __forceinline__ f32x4 mfma_any(const bf16x8& a, const u32x4& b, f32x4 c) {
+  return mfma16x16x32(a, __builtin_bit_cast(bf16x8, b), c);
 }
 
 __device__ __forceinline__ const u32x4* fp4_tile(const GemmArgs& a, const ProjLayout& L, int g, int q, int kc) {
@@ -84,14 +125,20 @@ __device__ __forceinline__ void epilogue_single(const GemmArgs& a, const f32x4& 
 
 // ------------------------------------------------------------------ decode GEMM
 // Small row counts per expert (<= 16 rows per tile): weight streaming bound. A
-// workgroup owns NSUB 16-row weight tiles of one expert and one 16-row token tile;
-// its 4 waves split K into contiguous ranges and reduce through LDS. Token operands
-// are read straight from global memory (they are tiny and shared through L2).
+// workgroup owns NSUB 16-row weight tiles of one expert and one 16-row token tile; its
+// NW = min(K/128, 4) waves split K into contiguous chunk ranges (a wider split, up to one
+// chunk per wave, measured slower: fewer workgroups fit a CU). Partial tiles are reduced through
+// LDS in wave order (deterministic). Token operands come straight from global memory
+// (tiny, shared through L2).
+constexpr int DEC_MAX_WAVES = 4;   // measured best of 4 / 8 / 16 on the decode workloads
+
 template <int MODE, int NSUB>
 __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs a) {
+  constexpr bool F16 = MODE != GEMM_DOWN;
   const int slot = blockIdx.y;
   if (slot >= a.tile_count[0]) return;
   const ProjLayout L = proj_layout(a.N, a.K);
+  const int NW = blockDim.x >> 6;
   const int q0 = blockIdx.x * NSUB;
   const int g = a.tile_group[slot];
   const int row0 = a.tile_row0[slot];
@@ -99,10 +146,10 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & (WAVE - 1);
   const int l16 = lane & 15, lg = lane >> 4;
   const int row = row0 + min(l16, nvalid - 1);            // clamp: extra columns are never stored
-  const int kc0 = (wave * L.KC) / 4, kc1 = ((wave + 1) * L.KC) / 4;
+  const int kc0 = (wave * L.KC) / NW, kc1 = ((wave + 1) * L.KC) / NW;
 
-  const uint16_t* xrow = nullptr;
-  const uint16_t* xlrow = nullptr;
+  const uint16_t* xrow = nullptr;                          // 16-bit token rows (fp16 x, bf16 h_hi)
+  const uint16_t* xlrow = nullptr;                         // bf16 h_lo
   const uint8_t* qrow = nullptr;
   const uint8_t* srow = nullptr;
   if (MODE == GEMM_DOWN) {
@@ -131,60 +178,62 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs a) {
     u32x4 wv[NSUB];
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) wv[s] = *fp4_tile(a, L, g, q0 + s, kc);
-    bf16x8 bop[4], blo[4];
-    if (MODE == GEMM_DOWN) {
-      const u32x4* lsrc = (const u32x4*)(xlrow + (size_t)kc * KCHUNK + lg * 32);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) blo[j] = __builtin_bit_cast(bf16x8, lsrc[j]);
-    }
+    u32x4 bop[4], blo[4];
     if (MODE == GEMM_GATEUP_FP4) {
       const u32x4 xv = *(const u32x4*)(qrow + (size_t)kc * 64 + lg * 16);
       const uint32_t sp = *(const uint16_t*)(srow + (size_t)kc * 8 + 2 * lg);
-      const float xs0 = e4m3_to_f32(sp & 0xFFu), xs1 = e4m3_to_f32(sp >> 8);
-      bop[0] = dequant8(xv.x, xs0);
-      bop[1] = dequant8(xv.y, xs0);
-      bop[2] = dequant8(xv.z, xs1);
-      bop[3] = dequant8(xv.w, xs1);
+      WOps<true> xo;
+      xo.make(xv, sp);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bop[j] = __builtin_bit_cast(u32x4, xo.v[j]);
     } else {
       const u32x4* src = (const u32x4*)(xrow + (size_t)kc * KCHUNK + lg * 32);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) bop[j] = __builtin_bit_cast(bf16x8, src[j]);
+      for (int j = 0; j < 4; ++j) bop[j] = src[j];
+      if (MODE == GEMM_DOWN) {
+        const u32x4* lsrc = (const u32x4*)(xlrow + (size_t)kc * KCHUNK + lg * 32);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) blo[j] = lsrc[j];
+      }
     }
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) {
-      float s0, s1;
-      chunk_scales(sgv[s], kc & 7, s0, s1);
-      const bf16x8 a0 = dequant8(wv[s].x, s0), a1 = dequant8(wv[s].y, s0);
-      const bf16x8 a2 = dequant8(wv[s].z, s1), a3 = dequant8(wv[s].w, s1);
-      acc[s] = mfma16x16x32(a0, bop[0], acc[s]);
-      acc[s] = mfma16x16x32(a1, bop[1], acc[s]);
-      acc[s] = mfma16x16x32(a2, bop[2], acc[s]);
-      acc[s] = mfma16x16x32(a3, bop[3], acc[s]);
+      WOps<F16> w;
+      w.make(wv[s], chunk_scale_bytes(sgv[s], kc & 7));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[s] = mfma_any(w.v[j], bop[j], acc[s]);
       if (MODE == GEMM_DOWN) {
-        acc[s] = mfma16x16x32(a0, blo[0], acc[s]);
-        acc[s] = mfma16x16x32(a1, blo[1], acc[s]);
-        acc[s] = mfma16x16x32(a2, blo[2], acc[s]);
-        acc[s] = mfma16x16x32(a3, blo[3], acc[s]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[s] = mfma_any(w.v[j], blo[j], acc[s]);
       }
     }
   }
 
-  __shared__ f32x4 red[4][NSUB][WAVE];
+  __shared__ f32x4 red[DEC_MAX_WAVES][NSUB][WAVE];
 #pragma unroll
   for (int s = 0; s < NSUB; ++s) red[wave][s][lane] = acc[s];
   __syncthreads();
-  if (wave != 0 || l16 >= nvalid) return;
-#pragma unroll
-  for (int s = 0; s < NSUB; ++s) acc[s] = ((red[0][s][lane] + red[1][s][lane]) + red[2][s][lane]) + red[3][s][lane];
+  // wave w finishes tiles w, w + NW, ...: fixed-order sum over the K ranges
+  if (l16 >= nvalid) return;
   const int orow = row0 + l16;
   float sc = a.wgs[g];
-  if (MODE == GEMM_GATEUP_FP4) sc *= a.xg[a.tok[orow]];
+  if (MODE != GEMM_DOWN) sc *= a.xg[a.tok[orow]];
   if (MODE == GEMM_DOWN) {
-#pragma unroll
-    for (int s = 0; s < NSUB; ++s) epilogue_single(a, acc[s], sc, orow, q0 + s);
+    for (int s = wave; s < NSUB; s += NW) {
+      f32x4 sum = red[0][s][lane];
+      for (int w = 1; w < NW; ++w) sum += red[w][s][lane];
+      epilogue_single(a, sum, sc, orow, q0 + s);
+    }
   } else {
-#pragma unroll
-    for (int s = 0; s < NSUB; s += 2) epilogue_pair<MODE>(a, acc[s], acc[s + 1], sc, orow, (q0 + s) >> 1);
+    // gate (even tile) and up (odd tile) of the same columns are finished together
+    for (int s = 2 * wave; s < NSUB; s += 2 * NW) {
+      f32x4 gsum = red[0][s][lane], usum = red[0][s + 1][lane];
+      for (int w = 1; w < NW; ++w) {
+        gsum += red[w][s][lane];
+        usum += red[w][s + 1][lane];
+      }
+      epilogue_pair<MODE>(a, gsum, usum, sc, orow, (q0 + s) >> 1);
+    }
   }
 }
 
@@ -213,7 +262,9 @@ __global__ __launch_bounds__(256) void gemm_prefill_kernel(GemmArgs a) {
 
   // staging assignment: bf16 modes move 16-byte pieces (8 columns), TSUB per thread;
   // the NVFP4 mode moves 16-column pieces (8 code bytes + 1 scale byte), TSUB/2 per thread
-  constexpr int NPIECE = (MODE == GEMM_GATEUP_FP4) ? TSUB / 2 : TSUB;
+  constexpr int PER_ROW = (MODE == GEMM_GATEUP_FP4) ? 8 : 16;
+  constexpr int NPIECE = (M * PER_ROW + 255) / 256;
+  constexpr bool ALL_PIECES = (M * PER_ROW) % 256 == 0;   // else the last round is partial
   const uint16_t* xsrc[NPIECE];
   const uint16_t* xlsrc[NPIECE];
   const uint8_t* qsrc[NPIECE];
@@ -221,10 +272,9 @@ __global__ __launch_bounds__(256) void gemm_prefill_kernel(GemmArgs a) {
   int prow[NPIECE], pcol[NPIECE];
 #pragma unroll
   for (int i = 0; i < NPIECE; ++i) {
-    const int p = threadIdx.x + 256 * i;
-    const int per_row = (MODE == GEMM_GATEUP_FP4) ? 8 : 16;
-    prow[i] = p / per_row;
-    pcol[i] = p % per_row;
+    const int p = min((int)threadIdx.x + 256 * i, M * PER_ROW - 1);   // surplus threads mirror the last piece
+    prow[i] = p / PER_ROW;
+    pcol[i] = p % PER_ROW;
     const int r = row0 + min(prow[i], nvalid - 1);
     if (MODE == GEMM_DOWN) {
       xsrc[i] = a.x + (size_t)r * L.K + pcol[i] * 8;
@@ -255,10 +305,13 @@ __global__ __launch_bounds__(256) void gemm_prefill_kernel(GemmArgs a) {
   auto stage_store = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < NPIECE; ++i) {
+      if (!ALL_PIECES && (int)threadIdx.x + 256 * i >= M * PER_ROW) continue;
       const int r = prow[i];
       if (MODE == GEMM_GATEUP_FP4) {
-        const float s = e4m3_to_f32(stg_s[i]);
-        const bf16x8 lo = dequant8(stg_q[i].x, s), hi = dequant8(stg_q[i].y, s);
+        float p2;
+        uint32_t sg2;
+        e4m3_split(stg_s[i], p2, sg2);
+        const f16x8 lo = dequant8_f16(stg_q[i].x, p2, sg2), hi = dequant8_f16(stg_q[i].y, p2, sg2);
         const int c = 2 * pcol[i];
         tile[buf][0][r * 16 + (c ^ (r & 15))] = __builtin_bit_cast(u32x4, lo);
         tile[buf][0][r * 16 + ((c + 1) ^ (r & 15))] = __builtin_bit_cast(u32x4, hi);
@@ -304,25 +357,22 @@ __global__ __launch_bounds__(256) void gemm_prefill_kernel(GemmArgs a) {
     }
     __syncthreads();
     if (active) {
-      float s0[NSUB], s1[NSUB];
+      WOps<MODE != GEMM_DOWN> aop[NSUB];
 #pragma unroll
-      for (int s = 0; s < NSUB; ++s) chunk_scales(scur[s], kc & 7, s0[s], s1[s]);
+      for (int s = 0; s < NSUB; ++s) aop[s].make(wcur[s], chunk_scale_bytes(scur[s], kc & 7));
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        bf16x8 aop[NSUB];
-#pragma unroll
-        for (int s = 0; s < NSUB; ++s) aop[s] = dequant8(pick_dword(wcur[s], j), j < 2 ? s0[s] : s1[s]);
         const int c = lg * 4 + j;
 #pragma unroll
         for (int t = 0; t < TSUB; ++t) {
           const int r = t * 16 + l16;
-          const bf16x8 bop = __builtin_bit_cast(bf16x8, tile[buf][0][r * 16 + (c ^ l16)]);
+          const u32x4 bop = tile[buf][0][r * 16 + (c ^ l16)];
 #pragma unroll
-          for (int s = 0; s < NSUB; ++s) acc[s][t] = mfma16x16x32(aop[s], bop, acc[s][t]);
+          for (int s = 0; s < NSUB; ++s) acc[s][t] = mfma_any(aop[s].v[j], bop, acc[s][t]);
           if (MODE == GEMM_DOWN) {
-            const bf16x8 blo = __builtin_bit_cast(bf16x8, tile[buf][PLANES - 1][r * 16 + (c ^ l16)]);
+            const u32x4 blo = tile[buf][PLANES - 1][r * 16 + (c ^ l16)];
 #pragma unroll
-            for (int s = 0; s < NSUB; ++s) acc[s][t] = mfma16x16x32(aop[s], blo, acc[s][t]);
+            for (int s = 0; s < NSUB; ++s) acc[s][t] = mfma_any(aop[s].v[j], blo, acc[s][t]);
           }
         }
       }
@@ -337,7 +387,7 @@ __global__ __launch_bounds__(256) void gemm_prefill_kernel(GemmArgs a) {
     if (rr >= nvalid) continue;
     const int orow = row0 + rr;
     float sc = wgs;
-    if (MODE == GEMM_GATEUP_FP4) sc *= a.xg[a.tok[orow]];
+    if (MODE != GEMM_DOWN) sc *= a.xg[a.tok[orow]];
     if (MODE == GEMM_DOWN) {
 #pragma unroll
       for (int s = 0; s < NSUB; ++s) epilogue_single(a, acc[s][t], sc, orow, q0 + s);
@@ -356,11 +406,12 @@ constexpr int PRE_NSUB_DN = 2;    // prefill down: 32 rows per wave (each tile m
 constexpr int PRE_TSUB = 8;       // prefill: 128 token rows per tile
 
 template <int MODE>
-static void launch_mode(bool decode, int max_tiles, const GemmArgs& a, hipStream_t s) {
+static void launch_mode(GemmRegime regime, int max_tiles, const GemmArgs& a, hipStream_t s) {
   const int nsub16 = a.N / 16;
-  if (decode) {
+  if (regime == REGIME_DECODE_KSPLIT) {
+    const int nw = min(a.K / KCHUNK, DEC_MAX_WAVES);
     dim3 grid((nsub16 + DEC_NSUB - 1) / DEC_NSUB, max_tiles);
-    hipLaunchKernelGGL((gemm_decode_kernel<MODE, DEC_NSUB>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((gemm_decode_kernel<MODE, DEC_NSUB>), grid, dim3(64 * nw), 0, s, a);
   } else {
     constexpr int NS = MODE == GEMM_DOWN ? PRE_NSUB_DN : PRE_NSUB_GU;
     dim3 grid((nsub16 + 4 * NS - 1) / (4 * NS), max_tiles);
@@ -368,12 +419,12 @@ static void launch_mode(bool decode, int max_tiles, const GemmArgs& a, hipStream
   }
 }
 
-hipError_t launch_gemm(GemmMode mode, bool decode, int max_tiles, const GemmArgs& a, hipStream_t s) {
+hipError_t launch_gemm(GemmMode mode, GemmRegime regime, int max_tiles, const GemmArgs& a, hipStream_t s) {
   if (max_tiles <= 0) return hipSuccess;
   switch (mode) {
-    case GEMM_GATEUP_BF16: launch_mode<GEMM_GATEUP_BF16>(decode, max_tiles, a, s); break;
-    case GEMM_GATEUP_FP4: launch_mode<GEMM_GATEUP_FP4>(decode, max_tiles, a, s); break;
-    case GEMM_DOWN: launch_mode<GEMM_DOWN>(decode, max_tiles, a, s); break;
+    case GEMM_GATEUP_BF16: launch_mode<GEMM_GATEUP_BF16>(regime, max_tiles, a, s); break;
+    case GEMM_GATEUP_FP4: launch_mode<GEMM_GATEUP_FP4>(regime, max_tiles, a, s); break;
+    case GEMM_DOWN: launch_mode<GEMM_DOWN>(regime, max_tiles, a, s); break;
   }
   return hipGetLastError();
 }
@@ -382,30 +433,54 @@ hipError_t launch_gemm(GemmMode mode, bool decode, int max_tiles, const GemmArgs
 // out[t] = bf16( sum_j w[t][j] * y[inv[t][j]]  (+ y_shared[t]) ), fp32, picks in
 // order, shared expert last ([vllm.cpp] "Device-resident decode campaign",
 // MoeCombineKernel: device FMA of the topk_weights over the expert outputs).
-__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
+// Grid (T, H / 512): a 128-thread workgroup owns 512 columns of one token; the k row
+// indices and weights are staged in LDS first so that all k row loads of a thread are
+// independent and in flight together.
+constexpr int COMBINE_COLS = 512;
+__global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
+  __shared__ int s_inv[64];
+  __shared__ float s_w[64];
   const int t = blockIdx.x;
   const int rows = a.T * a.k;
-  for (int c = threadIdx.x; c < a.H / 4; c += blockDim.x) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < a.k; ++j) {
-      const int r = a.inv[t * a.k + j];
-      const float wj = a.w[t * a.k + j];
-      const f32x4 v = *(const f32x4*)(a.y + (size_t)r * a.H + c * 4);
-      acc.x = __builtin_fmaf(wj, v.x, acc.x);
-      acc.y = __builtin_fmaf(wj, v.y, acc.y);
-      acc.z = __builtin_fmaf(wj, v.z, acc.z);
-      acc.w = __builtin_fmaf(wj, v.w, acc.w);
-    }
-    for (int sh = 0; sh < a.S; ++sh) acc += *(const f32x4*)(a.y + (size_t)(rows + sh * a.T + t) * a.H + c * 4);
-    *(u32x2*)(a.out + (size_t)t * a.H + c * 4) =
-        u32x2{f32_to_bf16_rne(acc.x) | (f32_to_bf16_rne(acc.y) << 16),
-              f32_to_bf16_rne(acc.z) | (f32_to_bf16_rne(acc.w) << 16)};
+  if ((int)threadIdx.x < a.k) {
+    s_inv[threadIdx.x] = a.inv[t * a.k + threadIdx.x];
+    s_w[threadIdx.x] = a.w[t * a.k + threadIdx.x];
   }
+  __syncthreads();
+  const int c = blockIdx.y * (COMBINE_COLS / 4) + threadIdx.x;   // float4 column index
+  if (c >= a.H / 4) return;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  int j = 0;
+  for (; j + 4 <= a.k; j += 4) {
+    f32x4 v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = *(const f32x4*)(a.y + (size_t)s_inv[j + q] * a.H + c * 4);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float wj = s_w[j + q];
+      acc.x = __builtin_fmaf(wj, v[q].x, acc.x);
+      acc.y = __builtin_fmaf(wj, v[q].y, acc.y);
+      acc.z = __builtin_fmaf(wj, v[q].z, acc.z);
+      acc.w = __builtin_fmaf(wj, v[q].w, acc.w);
+    }
+  }
+  for (; j < a.k; ++j) {
+    const f32x4 v = *(const f32x4*)(a.y + (size_t)s_inv[j] * a.H + c * 4);
+    const float wj = s_w[j];
+    acc.x = __builtin_fmaf(wj, v.x, acc.x);
+    acc.y = __builtin_fmaf(wj, v.y, acc.y);
+    acc.z = __builtin_fmaf(wj, v.z, acc.z);
+    acc.w = __builtin_fmaf(wj, v.w, acc.w);
+  }
+  for (int sh = 0; sh < a.S; ++sh) acc += *(const f32x4*)(a.y + (size_t)(rows + sh * a.T + t) * a.H + c * 4);
+  *(u32x2*)(a.out + (size_t)t * a.H + c * 4) =
+      u32x2{f32_to_bf16_rne(acc.x) | (f32_to_bf16_rne(acc.y) << 16),
+            f32_to_bf16_rne(acc.z) | (f32_to_bf16_rne(acc.w) << 16)};
 }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
-  hipLaunchKernelGGL(combine_kernel, dim3(a.T), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(combine_kernel, dim3(a.T, (a.H + COMBINE_COLS - 1) / COMBINE_COLS), dim3(128), 0, s, a);
   return hipGetLastError();
 }
 

@@ -8,7 +8,6 @@
 
 namespace nvmoe {
 
-constexpr int PLAN_CHUNK = 1024;   // tokens per permutation pass (one per plan thread)
 constexpr int DECODE_TILE_ROWS = 16;
 constexpr int PREFILL_TILE_ROWS = 128;
 
@@ -38,11 +37,16 @@ struct PlanArgs {
   int32_t* perm_user;    // optional [T*k]
 };
 
-hipError_t launch_route_plan(const RouteArgs& r, const PlanArgs& p, bool fused, hipStream_t s);
+// scratch: plan_scratch_ints(T, k, E) ints of workspace (large-T path only)
+hipError_t launch_route_plan(const RouteArgs& r, const PlanArgs& p, int32_t* scratch, hipStream_t s);
+size_t plan_scratch_ints(int T, int k, int E);
+bool plan_small_ok(int T, int k);
 
 // Activation / weight quantiser.
 hipError_t launch_quant_rows_bf16(const uint16_t* x, int rows, int K, uint8_t* packed, uint8_t* scales,
                                   float* gs, hipStream_t s);
+// bf16 rows -> fp16 rows scaled by 2^p (p per row puts max|x| in [2^14, 2^15)); xf = 2^-p.
+hipError_t launch_rows_to_f16(const uint16_t* x, int rows, int K, uint16_t* x16, float* xf, hipStream_t s);
 hipError_t launch_quant_groups_f32(const float* x, int groups, int rows_per_group, int K, uint8_t* packed,
                                    uint8_t* scales, float* gs, hipStream_t s);
 
@@ -70,11 +74,11 @@ struct GemmArgs {
   int N, K;                // projection rows, columns
   // token rows
   const int32_t* tok;      // row -> token (gather modes)
-  const uint16_t* x;       // bf16 [T][K] (GATEUP_BF16) or h_hi [rows][K] (DOWN)
+  const uint16_t* x;       // fp16 rescaled activations [T][K] (GATEUP_BF16) or h_hi [rows][K] (DOWN)
   const uint16_t* xlo;     // h_lo [rows][K] (DOWN): h = h_hi + h_lo
   const uint8_t* xq;       // [T][K/2]  (GATEUP_FP4)
   const uint8_t* xs;       // [T][K/16]
-  const float* xg;         // [T]
+  const float* xg;         // [T] per-row activation factor applied in the gate_up epilogue
   // tile list
   const int32_t* tile_group;
   const int32_t* tile_row0;
@@ -86,7 +90,11 @@ struct GemmArgs {
   uint16_t* out_lo;
   float* yout;
 };
-hipError_t launch_gemm(GemmMode mode, bool decode, int max_tiles, const GemmArgs& a, hipStream_t s);
+// Kernel families: decode (<= 16 rows per tile, K split across the waves of a workgroup,
+// direct token loads), N split with a 16-row LDS token tile (kept for experiments), and
+// prefill (N split, 128-row LDS token tiles).
+enum GemmRegime { REGIME_DECODE_KSPLIT = 0, REGIME_DECODE_NSPLIT = 1, REGIME_PREFILL = 2 };
+hipError_t launch_gemm(GemmMode mode, GemmRegime regime, int max_tiles, const GemmArgs& a, hipStream_t s);
 
 struct CombineArgs {
   const float* y;          // fp32 [rows_total][H] expert outputs
@@ -97,6 +105,5 @@ struct CombineArgs {
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 
-size_t plan_lds_bytes(int E, int G);
 
 }  // namespace nvmoe
