@@ -39,6 +39,29 @@ __device__ __forceinline__ void dpp_max64(uint32_t& hi, uint32_t& lo) {
   lo = take ? olo : lo;
 }
 
+// 64-bit key = (order_key(logit) << 32) | ~expert: the maximum is the largest logit with
+// the lowest expert id. Finite logits give a non-zero high word, so 0 marks an empty or
+// already taken slot.
+__device__ __forceinline__ uint64_t pick_key(uint32_t okey, int e) {
+  return ((uint64_t)okey << 32) | (uint32_t)~(uint32_t)e;
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_max_u64(uint64_t v) {
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)v, CTRL, 0xF, 0xF, false);
+  const uint64_t o = ((uint64_t)hi << 32) | lo;
+  return o > v ? o : v;
+}
+
+// Max over the 16 lanes of a row; every lane of the row gets it.
+__device__ __forceinline__ uint64_t row_max_u64(uint64_t v) {
+  v = dpp_max_u64<0xB1>(v);    // quad_perm [1,0,3,2]
+  v = dpp_max_u64<0x4E>(v);    // quad_perm [2,3,0,1]
+  v = dpp_max_u64<0x141>(v);   // row_half_mirror
+  return dpp_max_u64<0x140>(v);   // row_mirror
+}
+
 __device__ __forceinline__ void wave_max64(uint32_t& hi, uint32_t& lo) {
   dpp_max64<0xB1>(hi, lo);    // quad_perm [1,0,3,2]
   dpp_max64<0x4E>(hi, lo);    // quad_perm [2,3,0,1]
@@ -146,13 +169,6 @@ __device__ __forceinline__ void route_token(const float* __restrict__ lg, int E,
 // at once and the pick reduction (4 DPP butterflies on the 64-bit key) never leaves the
 // row: no cross-row lane reads, no scalar branches. Used when E <= 256.
 
-__device__ __forceinline__ void row_max64(uint32_t& hi, uint32_t& lo) {
-  dpp_max64<0xB1>(hi, lo);    // quad_perm [1,0,3,2]
-  dpp_max64<0x4E>(hi, lo);    // quad_perm [2,3,0,1]
-  dpp_max64<0x141>(hi, lo);   // row_half_mirror
-  dpp_max64<0x140>(hi, lo);   // row_mirror: every lane of the row holds the row max
-}
-
 // Sum over the 16 lanes of a row, identical in every lane of the row (a fixed butterfly;
 // each addition is commutative, so all lanes compute the same bits).
 __device__ __forceinline__ float row_sum(float v) {
@@ -163,76 +179,58 @@ __device__ __forceinline__ float row_sum(float v) {
   return v;
 }
 
-// Row r16-lanes: lane r16 holds experts r16, r16+16, ... (EPR = ceil(E/16) <= 16).
-// Pick j (k <= 64) is kept by lane j % 16 in slot j / 16.
+// Lane r16 of the row holds experts r16, r16+16, ... (EPR = ceil(E/16) <= 16) as 64-bit
+// pick keys; its candidate is the max of its keys, a picked expert's key is cleared to 0.
+// Everything is branch free except the final stores. Pick j (k <= 64) is kept by lane
+// j % 16 in slot j / 16.
 template <int EPR>
 __device__ __forceinline__ void route_token_row(const float* __restrict__ lg, int E, int k, int score, int t,
                                                 int32_t* __restrict__ ids, float* __restrict__ w,
                                                 int32_t* __restrict__ ids_user, float* __restrict__ w_user,
                                                 int32_t* s_ids) {
   const int r16 = threadIdx.x & 15;
-  uint32_t key[EPR];
+  uint64_t key[EPR];
 #pragma unroll
   for (int i = 0; i < EPR; ++i) {
     const int e = r16 + 16 * i;
-    key[i] = e < E ? order_key(lg[(size_t)t * E + e]) : 0u;
+    key[i] = e < E ? pick_key(order_key(lg[(size_t)t * E + e]), e) : 0ull;
   }
-  uint32_t taken = 0, ch = 0, cl = 0;
-  auto local_best = [&]() {
-    ch = 0u;
-    cl = 0u;
-#pragma unroll
-    for (int i = 0; i < EPR; ++i) {
-      const int e = r16 + 16 * i;
-      const uint32_t l = ~(uint32_t)e;
-      if (e < E && !((taken >> i) & 1u) && (key[i] > ch || (key[i] == ch && l > cl))) {
-        ch = key[i];
-        cl = l;
-      }
-    }
-  };
-  local_best();
-  uint32_t pk[4] = {0u, 0u, 0u, 0u};
-  int pid[4] = {0, 0, 0, 0};
-  uint32_t key0 = 0u;
+  uint64_t pk[4] = {0ull, 0ull, 0ull, 0ull};
+  uint64_t key0 = 0ull;
   for (int j = 0; j < k; ++j) {
-    uint32_t wh = ch, wl = cl;
-    row_max64(wh, wl);
-    const int e = (int)~wl;
-    if (j == 0) key0 = wh;
-    if (r16 == (e & 15)) {
-      taken |= 1u << (e >> 4);
-      local_best();
-    }
+    uint64_t cand = key[0];
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if ((j >> 4) == q && r16 == (j & 15)) {
-        pk[q] = wh;
-        pid[q] = e;
-      }
+    for (int i = 1; i < EPR; ++i) cand = key[i] > cand ? key[i] : cand;
+    const uint64_t win = row_max_u64(cand);           // row-uniform
+    const int e = (int)~(uint32_t)win;
+    if (j == 0) key0 = win;
+#pragma unroll
+    for (int i = 0; i < EPR; ++i) key[i] = (r16 + 16 * i == e) ? 0ull : key[i];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) pk[q] = (16 * q + r16 == j) ? win : pk[q];
   }
-  const float lmax = key_value(key0);
-  float sv[4], part = 0.0f;
+  const float lmax = key_value((uint32_t)(key0 >> 32));
+  float sv[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     sv[q] = 0.0f;
     if (r16 + 16 * q < k) {
-      const float v = key_value(pk[q]);
+      const float v = key_value((uint32_t)(pk[q] >> 32));
       sv[q] = score == 0 ? __expf(v - lmax) : 1.0f / (1.0f + __expf(-v));
     }
   }
-  part = ((sv[0] + sv[1]) + sv[2]) + sv[3];
-  const float sum = row_sum(part);
+  const float sum = row_sum(((sv[0] + sv[1]) + sv[2]) + sv[3]);
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int j = r16 + 16 * q;
     if (j < k) {
       const float wj = sv[q] / sum;
-      ids[(size_t)t * k + j] = pid[q];
+      const int id = (int)~(uint32_t)pk[q];
+      ids[(size_t)t * k + j] = id;
       w[(size_t)t * k + j] = wj;
-      if (ids_user) ids_user[(size_t)t * k + j] = pid[q];
+      if (ids_user) ids_user[(size_t)t * k + j] = id;
       if (w_user) w_user[(size_t)t * k + j] = wj;
-      if (s_ids) s_ids[t * k + j] = pid[q];
+      if (s_ids) s_ids[t * k + j] = id;
     }
   }
 }
