@@ -237,15 +237,18 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
   uint8_t* xs = (fp4 && r.act_scales) ? r.act_scales : ws + plan->ws_xs;
   float* xg = (fp4 && r.act_global) ? r.act_global : (float*)(ws + plan->ws_xg);
   uint16_t* x16 = (uint16_t*)(ws + plan->ws_x16);
+  const bool decode = use_decode(T, k, E);
+  // Activation preparation: NVFP4 row quantisation, or (large bf16 batches) the exact
+  // power-of-two rescale into fp16; small bf16 batches feed their rows to the GEMM as they are.
+  const GemmMode gu_mode = fp4 ? GEMM_GATEUP_FP4 : decode ? GEMM_GATEUP_BF16 : GEMM_GATEUP_F16;
   if ((e = mark(ev, 2 * MOE_STAGE_QUANT, s)) != hipSuccess) return (int)e;
   if (fp4)
     e = launch_quant_rows_bf16(x, T, H, xq, xs, xg, s);
-  else
+  else if (gu_mode == GEMM_GATEUP_F16)
     e = launch_rows_to_f16(x, T, H, x16, xg, s);
   if (e != hipSuccess) return (int)e;
   if ((e = mark(ev, 2 * MOE_STAGE_QUANT + 1, s)) != hipSuccess) return (int)e;
 
-  const bool decode = use_decode(T, k, E);
   const int M = decode ? DECODE_TILE_ROWS : PREFILL_TILE_ROWS;
   const GemmRegime regime = decode ? REGIME_DECODE_KSPLIT : REGIME_PREFILL;
   RouteArgs ra;
@@ -282,6 +285,7 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
   if ((e = mark(ev, 2 * MOE_STAGE_ROUTE + 1, s)) != hipSuccess) return (int)e;
 
   const int max_tiles = tile_bound(T, k, E, S, M);
+  const int est_tiles = std::min(T * k, E) + S * ((T + M - 1) / M);   // exact when no expert overflows a tile
   GemmArgs g1;
   std::memset(&g1, 0, sizeof(g1));
   g1.wfp4 = pk + plan->off_w1f;
@@ -290,7 +294,7 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
   g1.N = 2 * I;
   g1.K = H;
   g1.tok = pa.tok;
-  g1.x = x16;
+  g1.x = gu_mode == GEMM_GATEUP_BF16 ? x : x16;
   g1.xq = xq;
   g1.xs = xs;
   g1.xg = xg;
@@ -302,7 +306,7 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
   const size_t hplane = ((size_t)d.max_tokens * k + (size_t)S * d.max_tokens) * I;
   g1.out_lo = g1.out + hplane;
   if ((e = mark(ev, 2 * MOE_STAGE_GATE_UP, s)) != hipSuccess) return (int)e;
-  e = launch_gemm(fp4 ? GEMM_GATEUP_FP4 : GEMM_GATEUP_BF16, regime, max_tiles, g1, s);
+  e = launch_gemm(gu_mode, regime, max_tiles, est_tiles, g1, s);
   if (e != hipSuccess) return (int)e;
   if ((e = mark(ev, 2 * MOE_STAGE_GATE_UP + 1, s)) != hipSuccess) return (int)e;
 
@@ -317,7 +321,7 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
   g2.out = nullptr;
   g2.yout = (float*)(ws + plan->ws_y);
   if ((e = mark(ev, 2 * MOE_STAGE_DOWN, s)) != hipSuccess) return (int)e;
-  e = launch_gemm(GEMM_DOWN, regime, max_tiles, g2, s);
+  e = launch_gemm(GEMM_DOWN, regime, max_tiles, est_tiles, g2, s);
   if (e != hipSuccess) return (int)e;
   if ((e = mark(ev, 2 * MOE_STAGE_DOWN + 1, s)) != hipSuccess) return (int)e;
 

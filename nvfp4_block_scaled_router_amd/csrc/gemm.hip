@@ -13,13 +13,16 @@
 // Dequant route: the per-16 E4M3 block scale is not a power of two and covers half
 // an E8M0 block of the scaled MFMA, so each weight q*s (at most 6 significant bits) is
 // rebuilt exactly in registers and fed to a 16-bit MFMA with fp32 accumulation:
-//  - gate_up (2/3 of the weight bytes): fp16. The convert applies the power of two of
-//    s (its scale operand is exponent-only), one packed fp16 multiply the significand:
-//    1 VALU op per weight. Activations are fp16 too: bf16 rows rescaled exactly by a
-//    power of two into fp16 range (undone in the epilogue), NVFP4 rows decoded the
-//    same way as the weights. V_MFMA_F32_16X16X32_F16.
-//  - down: bf16 (h's range is not known when it is written): fp4->fp32 convert, fp32
-//    multiply, truncating pack, 2 VALU ops per weight. V_MFMA_F32_16X16X32_BF16.
+//  - gate_up of large batches (2/3 of the weight bytes, each weight used by up to 128
+//    rows): fp16. The convert applies the power of two of s (its scale operand is
+//    exponent-only), one packed fp16 multiply the significand: 1 VALU op per weight.
+//    Activations are fp16 too: bf16 rows rescaled exactly by a power of two into fp16
+//    range (undone in the epilogue), NVFP4 rows decoded the same way as the weights.
+//    V_MFMA_F32_16X16X32_F16. Small batches are weight-streaming bound, not VALU bound:
+//    their bf16 rows go straight into the bf16 route below (no activation pass).
+//  - down, and gate_up of small bf16 batches: bf16 (h's range is not known when it is
+//    written): fp4->fp32 convert, fp32 multiply, truncating pack, 2 VALU ops per weight.
+//    V_MFMA_F32_16X16X32_BF16. Both routes form every product q*s*x exactly.
 // Global scales (per expert, per activation row) are constant over K and are applied
 // once in the epilogue.
 //
@@ -44,6 +47,16 @@ __device__ __forceinline__ uint32_t pick_dword(const u32x4& v, int i) {
 __device__ __forceinline__ uint32_t chunk_scale_bytes(const u32x4& sg, int c) {
   return (pick_dword(sg, c >> 1) >> (16 * (c & 1))) & 0xFFFFu;
 }
+
+// h column f is stored at h_pos(f): inside each 128-column chunk, the 8-column piece for
+// (lane group g, MFMA step j) -- columns 32g + 8j .. +7, see the operand roles above -- sits
+// at piece 4j + g, so the 4 lane groups' loads for one MFMA step read 64 contiguous bytes
+// of a row (half the cache lines of the unpermuted order).
+__device__ __forceinline__ int h_pos(int f) {
+  return (f & ~127) | (((f >> 3) & 3) << 5) | (((f >> 5) & 3) << 3) | (f & 7);
+}
+// 16-byte piece index inside a chunk: stored piece p holds k-piece h_piece(p).
+__device__ __forceinline__ int h_piece(int p) { return ((p & 3) << 2) | (p >> 2); }
 
 // Dequantised MFMA A operands of one 16-row weight tile for one 128-column chunk: fp16
 // for gate_up, bf16 for down (j-th operand = columns 32*(l/16) + 8j .. +7 of the lane).
@@ -103,7 +116,7 @@ __device__ __forceinline__ void epilogue_pair(const GemmArgs& a, const f32x4& ga
                                               int row, int hs) {
   const int lg = (threadIdx.x & (WAVE - 1)) >> 4;
   const int NO = a.N / 2;
-  const size_t off = (size_t)row * NO + hs * 16 + 4 * lg;
+  const size_t off = (size_t)row * NO + h_pos(hs * 16 + 4 * lg);   // 4 columns stay contiguous
   const float h[4] = {silu_mul(gacc.x * sc, uacc.x * sc), silu_mul(gacc.y * sc, uacc.y * sc),
                       silu_mul(gacc.z * sc, uacc.z * sc), silu_mul(gacc.w * sc, uacc.w * sc)};
   uint32_t hi[4];
@@ -126,15 +139,15 @@ __device__ __forceinline__ void epilogue_single(const GemmArgs& a, const f32x4& 
 // ------------------------------------------------------------------ decode GEMM
 // Small row counts per expert (<= 16 rows per tile): weight streaming bound. A
 // workgroup owns NSUB 16-row weight tiles of one expert and one 16-row token tile; its
-// NW = min(K/128, 4) waves split K into contiguous chunk ranges (a wider split, up to one
-// chunk per wave, measured slower: fewer workgroups fit a CU). Partial tiles are reduced through
+// NW <= 4 waves split K into contiguous chunk ranges (a wider split, up to one chunk per
+// wave, measured slower: fewer workgroups fit a CU). Partial tiles are reduced through
 // LDS in wave order (deterministic). Token operands come straight from global memory
-// (tiny, shared through L2).
+// (tiny, shared through L2); each lane's token-operand load is reused by NSUB tiles.
 constexpr int DEC_MAX_WAVES = 4;   // measured best of 4 / 8 / 16 on the decode workloads
 
 template <int MODE, int NSUB>
 __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs a) {
-  constexpr bool F16 = MODE != GEMM_DOWN;
+  constexpr bool F16 = MODE == GEMM_GATEUP_F16 || MODE == GEMM_GATEUP_FP4;
   const int slot = blockIdx.y;
   if (slot >= a.tile_count[0]) return;
   const ProjLayout L = proj_layout(a.N, a.K);
@@ -155,12 +168,12 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs a) {
   if (MODE == GEMM_DOWN) {
     xrow = a.x + (size_t)row * L.K;
     xlrow = a.xlo + (size_t)row * L.K;
-  } else if (MODE == GEMM_GATEUP_BF16) {
-    xrow = a.x + (size_t)a.tok[row] * L.K;
-  } else {
+  } else if (MODE == GEMM_GATEUP_FP4) {
     const int t = a.tok[row];
     qrow = a.xq + (size_t)t * (L.K / 2);
     srow = a.xs + (size_t)t * (L.K / 16);
+  } else {
+    xrow = a.x + (size_t)a.tok[row] * L.K;
   }
 
   f32x4 acc[NSUB];
@@ -186,15 +199,17 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs a) {
       xo.make(xv, sp);
 #pragma unroll
       for (int j = 0; j < 4; ++j) bop[j] = __builtin_bit_cast(u32x4, xo.v[j]);
+    } else if (MODE == GEMM_DOWN) {   // h planes: piece (g, j) at 4j + g
+      const uint16_t* src = xrow + (size_t)kc * KCHUNK + lg * 8;
+      const uint16_t* lsrc = xlrow + (size_t)kc * KCHUNK + lg * 8;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bop[j] = *(const u32x4*)(src + 32 * j);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) blo[j] = *(const u32x4*)(lsrc + 32 * j);
     } else {
       const u32x4* src = (const u32x4*)(xrow + (size_t)kc * KCHUNK + lg * 32);
 #pragma unroll
       for (int j = 0; j < 4; ++j) bop[j] = src[j];
-      if (MODE == GEMM_DOWN) {
-        const u32x4* lsrc = (const u32x4*)(xlrow + (size_t)kc * KCHUNK + lg * 32);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) blo[j] = lsrc[j];
-      }
     }
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) {
@@ -217,7 +232,7 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs a) {
   if (l16 >= nvalid) return;
   const int orow = row0 + l16;
   float sc = a.wgs[g];
-  if (MODE != GEMM_DOWN) sc *= a.xg[a.tok[orow]];
+  if (MODE == GEMM_GATEUP_F16 || MODE == GEMM_GATEUP_FP4) sc *= a.xg[a.tok[orow]];
   if (MODE == GEMM_DOWN) {
     for (int s = wave; s < NSUB; s += NW) {
       f32x4 sum = red[0][s][lane];
@@ -279,7 +294,7 @@ __global__ __launch_bounds__(256) void gemm_prefill_kernel(GemmArgs a) {
     if (MODE == GEMM_DOWN) {
       xsrc[i] = a.x + (size_t)r * L.K + pcol[i] * 8;
       xlsrc[i] = a.xlo + (size_t)r * L.K + pcol[i] * 8;
-    } else if (MODE == GEMM_GATEUP_BF16) {
+    } else if (MODE == GEMM_GATEUP_F16) {
       xsrc[i] = a.x + (size_t)a.tok[r] * L.K + pcol[i] * 8;
     } else {
       const int t = a.tok[r];
@@ -316,8 +331,9 @@ __global__ __launch_bounds__(256) void gemm_prefill_kernel(GemmArgs a) {
         tile[buf][0][r * 16 + (c ^ (r & 15))] = __builtin_bit_cast(u32x4, lo);
         tile[buf][0][r * 16 + ((c + 1) ^ (r & 15))] = __builtin_bit_cast(u32x4, hi);
       } else {
-        tile[buf][0][r * 16 + (pcol[i] ^ (r & 15))] = stg[i];
-        if (MODE == GEMM_DOWN) tile[buf][PLANES - 1][r * 16 + (pcol[i] ^ (r & 15))] = stg_lo[i];
+        const int c = MODE == GEMM_DOWN ? h_piece(pcol[i]) : pcol[i];   // LDS holds k order
+        tile[buf][0][r * 16 + (c ^ (r & 15))] = stg[i];
+        if (MODE == GEMM_DOWN) tile[buf][PLANES - 1][r * 16 + (c ^ (r & 15))] = stg_lo[i];
       }
     }
   };
@@ -400,31 +416,46 @@ __global__ __launch_bounds__(256) void gemm_prefill_kernel(GemmArgs a) {
 
 // ---------------------------------------------------------------------- launch
 
-constexpr int DEC_NSUB = 2;       // decode: 32 weight rows per workgroup
 constexpr int PRE_NSUB_GU = 4;    // prefill gate_up: 2 gate + 2 up tiles per wave
 constexpr int PRE_NSUB_DN = 2;    // prefill down: 32 rows per wave (each tile meets h_hi and h_lo)
 constexpr int PRE_TSUB = 8;       // prefill: 128 token rows per tile
+constexpr int DEC_MIN_WGS = 2048; // decode: 8 workgroups per CU before 4 tiles per workgroup are used
+
+// Decode split: 4 weight tiles per workgroup (twice the reuse of each token-operand load)
+// when that still gives about 8 workgroups per CU, else 2; the K chunks go to the largest
+// of 4 / 3 / 2 waves that divides them evenly (4 if none does).
+template <int MODE>
+static void launch_decode(int max_tiles, int est_tiles, const GemmArgs& a, hipStream_t s) {
+  const int nsub16 = a.N / 16, kc = a.K / KCHUNK;
+  int nw = kc % 4 == 0 ? 4 : kc % 3 == 0 ? 3 : kc % 2 == 0 ? 2 : 4;
+  nw = min(nw, kc);
+  if (nsub16 % 4 == 0 && (long)est_tiles * (nsub16 / 4) >= DEC_MIN_WGS) {
+    hipLaunchKernelGGL((gemm_decode_kernel<MODE, 4>), dim3(nsub16 / 4, max_tiles), dim3(64 * nw), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((gemm_decode_kernel<MODE, 2>), dim3(nsub16 / 2, max_tiles), dim3(64 * nw), 0, s, a);
+  }
+}
 
 template <int MODE>
-static void launch_mode(GemmRegime regime, int max_tiles, const GemmArgs& a, hipStream_t s) {
-  const int nsub16 = a.N / 16;
+static void launch_mode(GemmRegime regime, int max_tiles, int est_tiles, const GemmArgs& a, hipStream_t s) {
   if (regime == REGIME_DECODE_KSPLIT) {
-    const int nw = min(a.K / KCHUNK, DEC_MAX_WAVES);
-    dim3 grid((nsub16 + DEC_NSUB - 1) / DEC_NSUB, max_tiles);
-    hipLaunchKernelGGL((gemm_decode_kernel<MODE, DEC_NSUB>), grid, dim3(64 * nw), 0, s, a);
-  } else {
+    launch_decode<MODE>(max_tiles, est_tiles, a, s);
+  } else if constexpr (MODE != GEMM_GATEUP_BF16) {
     constexpr int NS = MODE == GEMM_DOWN ? PRE_NSUB_DN : PRE_NSUB_GU;
-    dim3 grid((nsub16 + 4 * NS - 1) / (4 * NS), max_tiles);
+    dim3 grid((a.N / 16 + 4 * NS - 1) / (4 * NS), max_tiles);
     hipLaunchKernelGGL((gemm_prefill_kernel<MODE, NS, PRE_TSUB>), grid, dim3(256), 0, s, a);
   }
 }
 
-hipError_t launch_gemm(GemmMode mode, GemmRegime regime, int max_tiles, const GemmArgs& a, hipStream_t s) {
+hipError_t launch_gemm(GemmMode mode, GemmRegime regime, int max_tiles, int est_tiles, const GemmArgs& a,
+                       hipStream_t s) {
   if (max_tiles <= 0) return hipSuccess;
+  if (mode == GEMM_GATEUP_BF16 && regime != REGIME_DECODE_KSPLIT) return hipErrorInvalidValue;
   switch (mode) {
-    case GEMM_GATEUP_BF16: launch_mode<GEMM_GATEUP_BF16>(regime, max_tiles, a, s); break;
-    case GEMM_GATEUP_FP4: launch_mode<GEMM_GATEUP_FP4>(regime, max_tiles, a, s); break;
-    case GEMM_DOWN: launch_mode<GEMM_DOWN>(regime, max_tiles, a, s); break;
+    case GEMM_GATEUP_F16: launch_mode<GEMM_GATEUP_F16>(regime, max_tiles, est_tiles, a, s); break;
+    case GEMM_GATEUP_BF16: launch_mode<GEMM_GATEUP_BF16>(regime, max_tiles, est_tiles, a, s); break;
+    case GEMM_GATEUP_FP4: launch_mode<GEMM_GATEUP_FP4>(regime, max_tiles, est_tiles, a, s); break;
+    case GEMM_DOWN: launch_mode<GEMM_DOWN>(regime, max_tiles, est_tiles, a, s); break;
   }
   return hipGetLastError();
 }

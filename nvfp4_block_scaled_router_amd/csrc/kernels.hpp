@@ -64,7 +64,9 @@ struct PackArgs {
 hipError_t launch_pack(const PackArgs& a, hipStream_t s);
 
 // Grouped GEMMs.
-enum GemmMode { GEMM_GATEUP_BF16 = 0, GEMM_GATEUP_FP4 = 1, GEMM_DOWN = 2 };
+// gate_up modes: F16 = activations pre-scaled into fp16 (x16) and fp16 MFMA; BF16 = the
+// caller's bf16 rows read directly, bf16 MFMA; FP4 = NVFP4 activation rows.
+enum GemmMode { GEMM_GATEUP_F16 = 0, GEMM_GATEUP_FP4 = 1, GEMM_DOWN = 2, GEMM_GATEUP_BF16 = 3 };
 
 struct GemmArgs {
   // weights (packed layout of one projection, G groups)
@@ -74,7 +76,8 @@ struct GemmArgs {
   int N, K;                // projection rows, columns
   // token rows
   const int32_t* tok;      // row -> token (gather modes)
-  const uint16_t* x;       // fp16 rescaled activations [T][K] (GATEUP_BF16) or h_hi [rows][K] (DOWN)
+  const uint16_t* x;       // activations [T][K]: fp16 rescaled (GATEUP_F16) or bf16 (GATEUP_BF16);
+                           // h_hi [rows][K] (DOWN)
   const uint16_t* xlo;     // h_lo [rows][K] (DOWN): h = h_hi + h_lo
   const uint8_t* xq;       // [T][K/2]  (GATEUP_FP4)
   const uint8_t* xs;       // [T][K/16]
@@ -84,7 +87,8 @@ struct GemmArgs {
   const int32_t* tile_row0;
   const int32_t* tile_count;
   const int32_t* offsets;  // [G+1] row ranges of the groups
-  // output: gate_up -> h as two bf16 planes [rows][N/2] (hi = bf16(h), lo = bf16(h - hi));
+  // output: gate_up -> h as two bf16 planes [rows][N/2] (hi = bf16(h), lo = bf16(h - hi)),
+  // columns permuted inside each 128-column chunk (see h_pos);
   // down -> y fp32 [rows][N]
   uint16_t* out;
   uint16_t* out_lo;
@@ -94,7 +98,9 @@ struct GemmArgs {
 // direct token loads), N split with a 16-row LDS token tile (kept for experiments), and
 // prefill (N split, 128-row LDS token tiles).
 enum GemmRegime { REGIME_DECODE_KSPLIT = 0, REGIME_DECODE_NSPLIT = 1, REGIME_PREFILL = 2 };
-hipError_t launch_gemm(GemmMode mode, GemmRegime regime, int max_tiles, const GemmArgs& a, hipStream_t s);
+// est_tiles: expected number of valid tile slots (sizes the decode split); max_tiles: grid bound.
+hipError_t launch_gemm(GemmMode mode, GemmRegime regime, int max_tiles, int est_tiles, const GemmArgs& a,
+                       hipStream_t s);
 
 struct CombineArgs {
   const float* y;          // fp32 [rows_total][H] expert outputs
