@@ -149,12 +149,16 @@ template <int MODE, int NSUB>
 __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs a) {
   constexpr bool F16 = MODE == GEMM_GATEUP_F16 || MODE == GEMM_GATEUP_FP4;
   const int slot = blockIdx.y;
-  if (slot >= a.tile_count[0]) return;
+  // the slot's entries are read together with the count (slots past it hold stale values
+  // that are never used), saving one dependent round trip before the weight loads
+  const int ntiles = a.tile_count[0];
+  const int g = a.tile_group[slot];
+  const int row0 = a.tile_row0[slot];
+  if (slot >= ntiles) return;
   const ProjLayout L = proj_layout(a.N, a.K);
   const int NW = blockDim.x >> 6;
   const int q0 = blockIdx.x * NSUB;
-  const int g = a.tile_group[slot];
-  const int row0 = a.tile_row0[slot];
+  const float wgs = a.wgs[g];
   const int nvalid = min(DECODE_TILE_ROWS, a.offsets[g + 1] - row0);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & (WAVE - 1);
   const int l16 = lane & 15, lg = lane >> 4;
@@ -165,15 +169,19 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs a) {
   const uint16_t* xlrow = nullptr;                         // bf16 h_lo
   const uint8_t* qrow = nullptr;
   const uint8_t* srow = nullptr;
+  float sc = wgs;                                          // epilogue factor, loaded before the loop
   if (MODE == GEMM_DOWN) {
     xrow = a.x + (size_t)row * L.K;
     xlrow = a.xlo + (size_t)row * L.K;
-  } else if (MODE == GEMM_GATEUP_FP4) {
-    const int t = a.tok[row];
-    qrow = a.xq + (size_t)t * (L.K / 2);
-    srow = a.xs + (size_t)t * (L.K / 16);
   } else {
-    xrow = a.x + (size_t)a.tok[row] * L.K;
+    const int t = a.tok[row];
+    if (MODE == GEMM_GATEUP_FP4) {
+      qrow = a.xq + (size_t)t * (L.K / 2);
+      srow = a.xs + (size_t)t * (L.K / 16);
+    } else {
+      xrow = a.x + (size_t)t * L.K;
+    }
+    if (F16) sc *= a.xg[t];
   }
 
   f32x4 acc[NSUB];
@@ -230,9 +238,7 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs a) {
   __syncthreads();
   // wave w finishes tiles w, w + NW, ...: fixed-order sum over the K ranges
   if (l16 >= nvalid) return;
-  const int orow = row0 + l16;
-  float sc = a.wgs[g];
-  if (MODE == GEMM_GATEUP_F16 || MODE == GEMM_GATEUP_FP4) sc *= a.xg[a.tok[orow]];
+  const int orow = row0 + l16;                             // == row on the lanes that remain
   if (MODE == GEMM_DOWN) {
     for (int s = wave; s < NSUB; s += NW) {
       f32x4 sum = red[0][s][lane];
@@ -427,9 +433,10 @@ constexpr int DEC_MIN_WGS = 2048; // decode: 8 workgroups per CU before 4 tiles 
 template <int MODE>
 static void launch_decode(int max_tiles, int est_tiles, const GemmArgs& a, hipStream_t s) {
   const int nsub16 = a.N / 16, kc = a.K / KCHUNK;
+  const bool wide = nsub16 % 4 == 0 && (long)est_tiles * (nsub16 / 4) >= DEC_MIN_WGS;
   int nw = kc % 4 == 0 ? 4 : kc % 3 == 0 ? 3 : kc % 2 == 0 ? 2 : 4;
   nw = min(nw, kc);
-  if (nsub16 % 4 == 0 && (long)est_tiles * (nsub16 / 4) >= DEC_MIN_WGS) {
+  if (wide) {
     hipLaunchKernelGGL((gemm_decode_kernel<MODE, 4>), dim3(nsub16 / 4, max_tiles), dim3(64 * nw), 0, s, a);
   } else {
     hipLaunchKernelGGL((gemm_decode_kernel<MODE, 2>), dim3(nsub16 / 2, max_tiles), dim3(64 * nw), 0, s, a);
