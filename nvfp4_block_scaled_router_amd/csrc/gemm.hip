@@ -66,21 +66,19 @@ template <>
 struct WOps<true> {
   f16x8 v[4];
   __device__ __forceinline__ void make(const u32x4& w, uint32_t sb) {
-    float pa, pb;
-    uint32_t sa, sb2;
-    e4m3_split(sb & 0xFFu, pa, sa);
-    e4m3_split(sb >> 8, pb, sb2);
-    v[0] = dequant8_f16(w.x, pa, sa);
-    v[1] = dequant8_f16(w.y, pa, sa);
-    v[2] = dequant8_f16(w.z, pb, sb2);
-    v[3] = dequant8_f16(w.w, pb, sb2);
+    const f16x2 s = e4m3x2_to_f16x2(sb);
+    const f16x2 sa = {s.x, s.x}, sc = {s.y, s.y};
+    v[0] = dequant8_f16(w.x, sa);
+    v[1] = dequant8_f16(w.y, sa);
+    v[2] = dequant8_f16(w.z, sc);
+    v[3] = dequant8_f16(w.w, sc);
   }
 };
 template <>
 struct WOps<false> {
   bf16x8 v[4];
   __device__ __forceinline__ void make(const u32x4& w, uint32_t sb) {
-    const float s0 = e4m3_to_f32(sb & 0xFFu), s1 = e4m3_to_f32(sb >> 8);
+    const float s0 = e4m3_to_f32(sb & 0xFFu), s1 = e4m3_to_f32((sb >> 8) & 0xFFu);
     v[0] = dequant8(w.x, s0);
     v[1] = dequant8(w.y, s0);
     v[2] = dequant8(w.z, s1);
@@ -329,10 +327,9 @@ __global__ __launch_bounds__(256) void gemm_prefill_kernel(GemmArgs a) {
       if (!ALL_PIECES && (int)threadIdx.x + 256 * i >= M * PER_ROW) continue;
       const int r = prow[i];
       if (MODE == GEMM_GATEUP_FP4) {
-        float p2;
-        uint32_t sg2;
-        e4m3_split(stg_s[i], p2, sg2);
-        const f16x8 lo = dequant8_f16(stg_q[i].x, p2, sg2), hi = dequant8_f16(stg_q[i].y, p2, sg2);
+        const f16x2 s1 = e4m3x2_to_f16x2(stg_s[i]);
+        const f16x2 s2 = {s1.x, s1.x};
+        const f16x8 lo = dequant8_f16(stg_q[i].x, s2), hi = dequant8_f16(stg_q[i].y, s2);
         const int c = 2 * pcol[i];
         tile[buf][0][r * 16 + (c ^ (r & 15))] = __builtin_bit_cast(u32x4, lo);
         tile[buf][0][r * 16 + ((c + 1) ^ (r & 15))] = __builtin_bit_cast(u32x4, hi);
@@ -420,11 +417,180 @@ __global__ __launch_bounds__(256) void gemm_prefill_kernel(GemmArgs a) {
   }
 }
 
+// ------------------------------------------------------ prefill GEMM, LDS DMA staging
+// Same tiling as gemm_prefill_kernel for 16-bit token operands (fp16 x for gate_up; the
+// h_hi / h_lo planes for down), but the token tile moves global -> LDS with
+// global_load_lds_dwordx4 (no staging registers, no LDS store instructions) through an
+// NBUF-deep ring of LDS stages, chunk kc + NBUF - 1 in flight while chunk kc is consumed.
+// One DMA instruction writes 64 consecutive 16-byte LDS slots (lane i -> slot i), so the
+// XOR swizzle is applied on the global side: the lane that fills slot (r, c) fetches piece
+// c ^ (r % 16) of row r.
+__device__ __forceinline__ void dma16(const void* src, const void* lds_dst) {
+  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
+                                   (void __attribute__((address_space(3)))*)lds_dst, 16, 0, 0);
+}
+
+// s_waitcnt immediate: vmcnt(vm) lgkmcnt(lgkm), expcnt not waited.
+constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8); }
+
+template <int MODE, int NSUB, int TSUB, int NBUF>
+__global__ __launch_bounds__(256) void gemm_prefill_dma_kernel(GemmArgs a) {
+  static_assert(MODE == GEMM_GATEUP_F16 || MODE == GEMM_DOWN, "16-bit token operands only");
+  static_assert(NBUF == 2 || NBUF == 3, "LDS ring depth");
+  constexpr int M = TSUB * 16;
+  constexpr int PLANES = MODE == GEMM_DOWN ? 2 : 1;   // down: h_hi and h_lo
+  constexpr int PLANE = M * 16;                       // 16-byte slots per plane per stage
+  constexpr int STAGE = PLANES * PLANE;
+  constexpr int D = PLANES * TSUB;                    // DMA instructions per lane per chunk
+  constexpr bool F16 = MODE == GEMM_GATEUP_F16;
+  __shared__ u32x4 tile[NBUF * STAGE];
+
+  const int slot = blockIdx.y;
+  const int ntiles = a.tile_count[0];
+  const int g = a.tile_group[slot];
+  const int row0 = a.tile_row0[slot];
+  if (slot >= ntiles) return;
+  const ProjLayout L = proj_layout(a.N, a.K);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int q0 = (blockIdx.x * 4 + wave) * NSUB;          // the launch covers N exactly
+  const int nvalid = min(M, a.offsets[g + 1] - row0);
+
+  // DMA instruction i of this wave fills slots (4i + wave) * 64 .. +63 of a plane: row
+  // r = 4 (4i + wave) + lane / 16, slot column lane % 16. Byte offsets (32-bit) from the
+  // plane's chunk base.
+  uint32_t src_off[TSUB];
+#pragma unroll
+  for (int i = 0; i < TSUB; ++i) {
+    const int r = 4 * (4 * i + wave) + lg;
+    const int rr = row0 + min(r, nvalid - 1);            // rows past the group repeat its last row
+    const int kp = l16 ^ (r & 15);                       // k-order piece this slot holds
+    if (MODE == GEMM_DOWN)
+      src_off[i] = ((uint32_t)rr * L.K + h_piece(kp) * 8) * 2;   // h planes: piece (g, j) at 4j + g
+    else
+      src_off[i] = ((uint32_t)a.tok[rr] * L.K + kp * 8) * 2;
+  }
+  auto dma = [&](int kc, int st) {
+#pragma unroll
+    for (int pl = 0; pl < PLANES; ++pl) {
+      const char* base = (const char*)(pl == 0 ? a.x : a.xlo) + (size_t)kc * (KCHUNK * 2);
+#pragma unroll
+      for (int i = 0; i < TSUB; ++i) dma16(base + src_off[i], &tile[st * STAGE + pl * PLANE + (4 * i + wave) * 64]);
+    }
+  };
+
+  // weight tiles of this wave: fp4 16 B per lane per chunk, the chunk's two block-scale
+  // bytes loaded chunk by chunk (2 B of the lane's 16-byte scale-group entry)
+  const u32x4* wp[NSUB];
+  const uint8_t* sp[NSUB];
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s) {
+    wp[s] = fp4_tile(a, L, g, q0 + s, 0);
+    sp[s] = (const uint8_t*)sc_tile(a, L, g, q0 + s, 0);
+  }
+  // (the dword holding them: a 16-bit load would be zero-extended right after it, which
+  // makes the compiler wait for the load at once)
+  auto load_w = [&](int kc, u32x4 (&w)[NSUB], uint32_t (&sb)[NSUB]) {
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) {
+      w[s] = wp[s][(size_t)kc * WAVE];
+      sb[s] = *(const uint32_t*)(sp[s] + (size_t)(kc >> 3) * (WAVE * 16) + (kc & 6) * 2);
+    }
+  };
+
+  f32x4 acc[NSUB][TSUB];
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s)
+#pragma unroll
+    for (int t = 0; t < TSUB; ++t) acc[s][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  u32x4 wA[NSUB], wB[NSUB];
+  uint32_t sA[NSUB], sB[NSUB];
+  load_w(0, wA, sA);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int c = 0; c < NBUF - 1; ++c) dma(min(c, L.KC - 1), c);
+
+  // Iteration kc: wait for chunk kc in LDS (older loads complete, the newest NBUF - 2
+  // chunks may stay in flight), barrier, issue the weights of kc + 1 and the DMA of
+  // kc + NBUF - 1 (clamped to the last chunk near the end, so every iteration issues the
+  // same loads and one wait count fits all), then consume chunk kc. The two weight
+  // register sets alternate (no copies, which would wait for the loads in flight).
+  auto step = [&](int kc, const u32x4 (&wc)[NSUB], const uint32_t (&sc)[NSUB], u32x4 (&wn)[NSUB],
+                  uint32_t (&sn)[NSUB]) {
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(D * (NBUF - 2), 0));
+    __builtin_amdgcn_s_barrier();
+    // issue order is what the wait count above relies on: weights, then DMA, then compute
+    __builtin_amdgcn_sched_barrier(0);
+    load_w(min(kc + 1, L.KC - 1), wn, sn);
+    __builtin_amdgcn_sched_barrier(0);
+    dma(min(kc + NBUF - 1, L.KC - 1), (kc + NBUF - 1) % NBUF);
+    __builtin_amdgcn_sched_barrier(0);
+    const u32x4* T0 = &tile[(kc % NBUF) * STAGE];
+    WOps<F16> w[NSUB];
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) w[s].make(wc[s], sc[s] >> ((kc & 1) * 16));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = (lg * 4 + j) ^ l16;
+      u32x4 bop[TSUB];
+#pragma unroll
+      for (int t = 0; t < TSUB; ++t) bop[t] = T0[(t * 16 + l16) * 16 + c];
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s)
+#pragma unroll
+        for (int t = 0; t < TSUB; ++t) acc[s][t] = mfma_any(w[s].v[j], bop[t], acc[s][t]);
+      if (MODE == GEMM_DOWN) {
+#pragma unroll
+        for (int t = 0; t < TSUB; ++t) bop[t] = T0[PLANE + (t * 16 + l16) * 16 + c];
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s)
+#pragma unroll
+          for (int t = 0; t < TSUB; ++t) acc[s][t] = mfma_any(w[s].v[j], bop[t], acc[s][t]);
+      }
+    }
+  };
+  // pairs of steps with fixed register roles (a conditional second step would make the
+  // compiler copy registers that still have loads in flight); an odd count peels chunk 0
+  if (L.KC & 1) {
+    step(0, wA, sA, wB, sB);
+    for (int kc = 1; kc < L.KC; kc += 2) {
+      step(kc, wB, sB, wA, sA);
+      step(kc + 1, wA, sA, wB, sB);
+    }
+  } else {
+    for (int kc = 0; kc < L.KC; kc += 2) {
+      step(kc, wA, sA, wB, sB);
+      step(kc + 1, wB, sB, wA, sA);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));   // the clamped tail DMAs land before the workgroup exits
+
+  const float wgs = a.wgs[g];
+#pragma unroll
+  for (int t = 0; t < TSUB; ++t) {
+    const int rr = t * 16 + l16;
+    if (rr >= nvalid) continue;
+    const int orow = row0 + rr;
+    float scl = wgs;
+    if (F16) scl *= a.xg[a.tok[orow]];
+    if (MODE == GEMM_DOWN) {
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s) epilogue_single(a, acc[s][t], scl, orow, q0 + s);
+    } else {
+#pragma unroll
+      for (int s = 0; s < NSUB; s += 2) epilogue_pair<MODE>(a, acc[s][t], acc[s + 1][t], scl, orow, (q0 + s) >> 1);
+    }
+  }
+}
+
 // ---------------------------------------------------------------------- launch
 
 constexpr int PRE_NSUB_GU = 4;    // prefill gate_up: 2 gate + 2 up tiles per wave
-constexpr int PRE_NSUB_DN = 2;    // prefill down: 32 rows per wave (each tile meets h_hi and h_lo)
+constexpr int PRE_NSUB_DN = 4;    // prefill down: 64 rows per wave (each tile meets h_hi and h_lo)
 constexpr int PRE_TSUB = 8;       // prefill: 128 token rows per tile
+constexpr int PRE_NBUF_GU = 3;    // prefill gate_up: LDS ring depth (3 x 32 KiB)
 constexpr int DEC_MIN_WGS = 2048; // decode: 8 workgroups per CU before 4 tiles per workgroup are used
 
 // Decode split: 4 weight tiles per workgroup (twice the reuse of each token-operand load)
@@ -447,8 +613,16 @@ template <int MODE>
 static void launch_mode(GemmRegime regime, int max_tiles, int est_tiles, const GemmArgs& a, hipStream_t s) {
   if (regime == REGIME_DECODE_KSPLIT) {
     launch_decode<MODE>(max_tiles, est_tiles, a, s);
-  } else if constexpr (MODE != GEMM_GATEUP_BF16) {
+  } else if constexpr (MODE == GEMM_GATEUP_F16 || MODE == GEMM_DOWN) {
     constexpr int NS = MODE == GEMM_DOWN ? PRE_NSUB_DN : PRE_NSUB_GU;
+    constexpr int NB = MODE == GEMM_DOWN ? 2 : PRE_NBUF_GU;
+    dim3 grid((a.N / 16 + 4 * NS - 1) / (4 * NS), max_tiles);
+    if ((a.N / 16) % (4 * NS) == 0)
+      hipLaunchKernelGGL((gemm_prefill_dma_kernel<MODE, NS, PRE_TSUB, NB>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((gemm_prefill_kernel<MODE, NS, PRE_TSUB>), grid, dim3(256), 0, s, a);
+  } else if constexpr (MODE == GEMM_GATEUP_FP4) {
+    constexpr int NS = PRE_NSUB_GU;
     dim3 grid((a.N / 16 + 4 * NS - 1) / (4 * NS), max_tiles);
     hipLaunchKernelGGL((gemm_prefill_kernel<MODE, NS, PRE_TSUB>), grid, dim3(256), 0, s, a);
   }
