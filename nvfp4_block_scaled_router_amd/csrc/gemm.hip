@@ -256,13 +256,22 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs a) {
   }
 }
 
+// LDS slot swizzle of the prefill token tiles: piece c of row r sits at slot c ^ lds_swz(r).
+// An MFMA operand read has lane (l%16, l/16) fetch row 16t + l%16, piece 4(l/16) + j. With
+// lds_swz(r) = G((r >> 1) & 7) ^ 4 (r & 1), G(q) = (q & 3) | 2 (q & 4), these 16-byte reads
+// measured free of bank conflicts on gfx950 (SQ_LDS_BANK_CONFLICT = 0, the speed of a
+// linear read), where the plain c ^ (r % 16) costs 4 conflict cycles per read.
+__device__ __forceinline__ int lds_swz(int r) {
+  const int q = (r >> 1) & 7;
+  return ((q & 3) | ((q & 4) << 1)) ^ ((r & 1) << 2);
+}
+
 // ----------------------------------------------------------------- prefill GEMM
 // Tiles of TSUB*16 rows of one expert x (4 waves x NSUB) 16-row weight tiles. Token
 // rows are gathered (through the row->token map) chunk by chunk into a double-buffered
 // LDS tile shared by the 4 waves; each wave streams its own weight tiles straight into
 // registers and dequantises them there. LDS rows are 256 bytes (one 128-column chunk
-// of bf16); 16-byte piece c of row r is stored at piece c ^ (r % 16) so the 16 lanes
-// of a lane group read 16 different bank groups.
+// of 16-bit values); 16-byte piece c of row r is stored at slot c ^ lds_swz(r).
 template <int MODE, int NSUB, int TSUB>
 __global__ __launch_bounds__(256) void gemm_prefill_kernel(GemmArgs a) {
   constexpr int M = TSUB * 16;
@@ -331,12 +340,12 @@ __global__ __launch_bounds__(256) void gemm_prefill_kernel(GemmArgs a) {
         const f16x2 s2 = {s1.x, s1.x};
         const f16x8 lo = dequant8_f16(stg_q[i].x, s2), hi = dequant8_f16(stg_q[i].y, s2);
         const int c = 2 * pcol[i];
-        tile[buf][0][r * 16 + (c ^ (r & 15))] = __builtin_bit_cast(u32x4, lo);
-        tile[buf][0][r * 16 + ((c + 1) ^ (r & 15))] = __builtin_bit_cast(u32x4, hi);
+        tile[buf][0][r * 16 + (c ^ lds_swz(r))] = __builtin_bit_cast(u32x4, lo);
+        tile[buf][0][r * 16 + ((c + 1) ^ lds_swz(r))] = __builtin_bit_cast(u32x4, hi);
       } else {
         const int c = MODE == GEMM_DOWN ? h_piece(pcol[i]) : pcol[i];   // LDS holds k order
-        tile[buf][0][r * 16 + (c ^ (r & 15))] = stg[i];
-        if (MODE == GEMM_DOWN) tile[buf][PLANES - 1][r * 16 + (c ^ (r & 15))] = stg_lo[i];
+        tile[buf][0][r * 16 + (c ^ lds_swz(r))] = stg[i];
+        if (MODE == GEMM_DOWN) tile[buf][PLANES - 1][r * 16 + (c ^ lds_swz(r))] = stg_lo[i];
       }
     }
   };
@@ -385,11 +394,11 @@ __global__ __launch_bounds__(256) void gemm_prefill_kernel(GemmArgs a) {
 #pragma unroll
         for (int t = 0; t < TSUB; ++t) {
           const int r = t * 16 + l16;
-          const u32x4 bop = tile[buf][0][r * 16 + (c ^ l16)];
+          const u32x4 bop = tile[buf][0][r * 16 + (c ^ lds_swz(l16))];
 #pragma unroll
           for (int s = 0; s < NSUB; ++s) acc[s][t] = mfma_any(aop[s].v[j], bop, acc[s][t]);
           if (MODE == GEMM_DOWN) {
-            const u32x4 blo = tile[buf][PLANES - 1][r * 16 + (c ^ l16)];
+            const u32x4 blo = tile[buf][PLANES - 1][r * 16 + (c ^ lds_swz(l16))];
 #pragma unroll
             for (int s = 0; s < NSUB; ++s) acc[s][t] = mfma_any(aop[s].v[j], blo, acc[s][t]);
           }
@@ -423,8 +432,8 @@ __global__ __launch_bounds__(256) void gemm_prefill_kernel(GemmArgs a) {
 // global_load_lds_dwordx4 (no staging registers, no LDS store instructions) through an
 // NBUF-deep ring of LDS stages, chunk kc + NBUF - 1 in flight while chunk kc is consumed.
 // One DMA instruction writes 64 consecutive 16-byte LDS slots (lane i -> slot i), so the
-// XOR swizzle is applied on the global side: the lane that fills slot (r, c) fetches piece
-// c ^ (r % 16) of row r.
+// swizzle is applied on the global side: the lane that fills slot (r, c) fetches piece
+// c ^ lds_swz(r) of row r.
 __device__ __forceinline__ void dma16(const void* src, const void* lds_dst) {
   __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
                                    (void __attribute__((address_space(3)))*)lds_dst, 16, 0, 0);
@@ -465,7 +474,7 @@ __global__ __launch_bounds__(256) void gemm_prefill_dma_kernel(GemmArgs a) {
   for (int i = 0; i < TSUB; ++i) {
     const int r = 4 * (4 * i + wave) + lg;
     const int rr = row0 + min(r, nvalid - 1);            // rows past the group repeat its last row
-    const int kp = l16 ^ (r & 15);                       // k-order piece this slot holds
+    const int kp = l16 ^ lds_swz(r);                     // k-order piece this slot holds
     if (MODE == GEMM_DOWN)
       src_off[i] = ((uint32_t)rr * L.K + h_piece(kp) * 8) * 2;   // h planes: piece (g, j) at 4j + g
     else
@@ -533,7 +542,7 @@ __global__ __launch_bounds__(256) void gemm_prefill_dma_kernel(GemmArgs a) {
     for (int s = 0; s < NSUB; ++s) w[s].make(wc[s], sc[s] >> ((kc & 1) * 16));
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int c = (lg * 4 + j) ^ l16;
+      const int c = (lg * 4 + j) ^ lds_swz(l16);
       u32x4 bop[TSUB];
 #pragma unroll
       for (int t = 0; t < TSUB; ++t) bop[t] = T0[(t * 16 + l16) * 16 + c];
@@ -587,10 +596,11 @@ __global__ __launch_bounds__(256) void gemm_prefill_dma_kernel(GemmArgs a) {
 
 // ---------------------------------------------------------------------- launch
 
-constexpr int PRE_NSUB_GU = 4;    // prefill gate_up: 2 gate + 2 up tiles per wave
+constexpr int PRE_NSUB_GU = 2;    // prefill gate_up: 1 gate + 1 up tile per wave (2 workgroups per CU)
 constexpr int PRE_NSUB_DN = 4;    // prefill down: 64 rows per wave (each tile meets h_hi and h_lo)
 constexpr int PRE_TSUB = 8;       // prefill: 128 token rows per tile
-constexpr int PRE_NBUF_GU = 3;    // prefill gate_up: LDS ring depth (3 x 32 KiB)
+constexpr int PRE_NBUF_GU = 2;    // prefill gate_up: LDS ring depth (2 x 32 KiB; measured faster than 1 workgroup
+                                  // per CU with 4 tiles per wave and 3 stages)
 constexpr int DEC_MIN_WGS = 2048; // decode: 8 workgroups per CU before 4 tiles per workgroup are used
 
 // Decode split: 4 weight tiles per workgroup (twice the reuse of each token-operand load)
