@@ -21,6 +21,15 @@ Prints one JSON line: tokens/s of the whole step (value), plus
                 workload, on this host's cores.
 Other workloads (--workload qwen3-30b-a3b-prefill | deepseek-v3 | skewed-w4a4 |
 tiny) print the same line for that configuration.
+
+roofline.traffic is the HBM traffic of one gate/up launch measured by rocprofv3
+counters (FETCH_SIZE and WRITE_SIZE runs, each scaled by the reading of a 1 GiB
+device copy), taken from the record in profiles/ whose kernel-source hash matches
+the sources built now (null otherwise). The records and the kernel-trace
+summaries in profiles/ are made from rocprofv3 output by this script:
+
+    python bench.py --trace-summary RESULTS_DB --title T --command C
+    python bench.py --traffic-summary FETCH_CSV WRITE_CSV --workload W --title T --command C
 """
 from __future__ import annotations
 
@@ -152,6 +161,137 @@ def cpu_baseline(cfgs, budget_s=6.0):
                       f"weight quantisation untimed"}
 
 
+# ------------------------------------------------------------ rocprofv3 summaries
+
+STAGE_OF_MODE = {"0": "gate_up", "1": "gate_up", "3": "gate_up", "2": "down"}
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ("gemm.hip", "common.hpp", "kernels.hpp")
+
+
+def kernel_source_hash():
+    """sha256 over the GEMM kernel sources (a traffic record is valid only for these)."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "nvfp4_block_scaled_router_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def kernel_stage(name):
+    """Layer stage of a kernel name from the trace (gate_up / down / route / ...)."""
+    import re
+    mm = re.search(r"gemm_\w+_kernel<(\d+)", name)
+    if mm:
+        return STAGE_OF_MODE.get(mm.group(1), "gemm")
+    for key, st in (("plan", "route"), ("route", "route"), ("combine", "combine"), ("quant", "quant"),
+                    ("rows_to_f16", "quant"), ("pack", "pack"), ("group_gs", "pack")):
+        if key in name:
+            return st
+    return "other"
+
+
+def trace_summary(db, title, command):
+    import sqlite3
+    cur = sqlite3.connect(db).cursor()
+    rows = cur.execute("select name, count(*), avg(duration), min(duration), max(duration), sum(duration), "
+                       "max(grid_x), max(grid_y), max(workgroup_x), max(vgpr_count), max(accum_vgpr_count), "
+                       "max(lds_size) from kernels group by name order by sum(duration) desc").fetchall()
+    out = [f"# {title}", "", "Command (on one MI355X, from the repository root):", "", "```", command, "```", "",
+           "| kernel | stage | calls | avg us | min us | max us | total ms | grid (x,y) | wg | vgpr/agpr | lds B |",
+           "|---|---|---|---|---|---|---|---|---|---|---|"]
+    stage = {}
+    for n, c, a, mn, mx, t, gx, gy, wg, v, ag, lds in rows:
+        short = n.replace("nvmoe::", "").split("(")[0]
+        st = kernel_stage(short)
+        stage.setdefault(st, [0, 0.0])
+        stage[st][0] += c
+        stage[st][1] += t
+        out.append(f"| `{short}` | {st} | {c} | {a / 1e3:.2f} | {mn / 1e3:.2f} | {mx / 1e3:.2f} | {t / 1e6:.3f} | "
+                   f"{gx},{gy} | {wg} | {v}/{ag} | {lds} |")
+    out += ["", "Per stage (all launches of the stage's kernels):", "", "| stage | launches | avg us per launch |",
+            "|---|---|---|"]
+    for st, (c, t) in sorted(stage.items(), key=lambda kv: -kv[1][1]):
+        out.append(f"| {st} | {c} | {t / c / 1e3:.2f} |")
+    return "\n".join(out)
+
+
+def _pmc_per_dispatch(path, counter):
+    """{dispatch_id: (kernel name, grid, value summed over the counter's instances)} from a rocprofv3 csv."""
+    import csv
+    res = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        d = int(r["Dispatch_Id"])
+        name = r["Kernel_Name"].replace("nvmoe::", "").split("(")[0]
+        prev = res.get(d, (name, int(r["Grid_Size"]), 0.0))
+        res[d] = (name, int(r["Grid_Size"]), prev[2] + float(r["Counter_Value"]))
+    return res
+
+
+def traffic_summary(fetch_csv, write_csv, workload_name, title, command):
+    """HBM bytes per gate/up launch from FETCH_SIZE / WRITE_SIZE runs (KiB per dispatch),
+    each scaled by what the counter reads for the 1 GiB device copy of --copy-probe."""
+    fetch = _pmc_per_dispatch(fetch_csv, "FETCH_SIZE")
+    write = _pmc_per_dispatch(write_csv, "WRITE_SIZE")
+    gib_kib = float(1 << 20)
+
+    def copy_kib(d):
+        big = [v for (n, g, v) in d.values() if "copy" in n.lower() or "elementwise" in n.lower()]
+        return max(big) if big else None
+    cf, cw = copy_kib(fetch), copy_kib(write)
+    f_scale = gib_kib / cf if cf else 1.0
+    w_scale = gib_kib / cw if cw else 1.0
+    out = [f"# {title}", "", "Commands (on one MI355X, from the repository root):", "", "```", command, "```", "",
+           f"Calibration: the 1 GiB device copy reads FETCH_SIZE {cf:.0f} KiB and WRITE_SIZE {cw:.0f} KiB, "
+           f"so FETCH_SIZE is scaled by {f_scale:.3f} and WRITE_SIZE by {w_scale:.3f} (1 GiB = {gib_kib:.0f} KiB).",
+           "", "| kernel | stage | grid | dispatches | FETCH MB (scaled) | WRITE MB (scaled) |", "|---|---|---|---|---|---|"]
+    groups = {}
+    for d, (n, g, v) in fetch.items():
+        key = (n, g)
+        wv = write.get(d, (n, g, None))[2]
+        groups.setdefault(key, []).append((v * f_scale * 1024, None if wv is None else wv * w_scale * 1024))
+    # the write run has its own dispatch ids; pair by (kernel, grid) and order
+    wgroups = {}
+    for d, (n, g, v) in sorted(write.items()):
+        wgroups.setdefault((n, g), []).append(v * w_scale * 1024)
+    gu = []
+    for (n, g), lst in sorted(groups.items()):
+        fb = [a for a, _ in lst]
+        wb = wgroups.get((n, g), [])
+        st = kernel_stage(n)
+        fmean = sum(fb) / len(fb)
+        wmean = sum(wb) / len(wb) if wb else float("nan")
+        out.append(f"| `{n}` | {st} | {g} | {len(fb)} | {fmean / 1e6:.2f} | {wmean / 1e6:.2f} |")
+        if st == "gate_up":
+            gu.append((g, fmean, wmean))
+    per_launch = sum(f + w for _, f, w in gu) / len(gu) if gu else None
+    rec = {"workload": workload_name, "kernel": "gate_up", "bytes_per_launch": per_launch,
+           "launches_averaged": len(gu), "source_sha256": kernel_source_hash()}
+    out += ["", "Mean HBM traffic (FETCH + WRITE, scaled) per gate/up launch: "
+            + ("n/a" if per_launch is None else f"{per_launch / 1e6:.2f} MB"), "",
+            "traffic-record: " + json.dumps(rec)]
+    return "\n".join(out)
+
+
+def traffic_record(workload_name):
+    """The measured gate/up traffic per launch for this workload if its record matches the
+    kernel sources built now, else None."""
+    if not os.path.isdir(PROFILES):
+        return None
+    want = kernel_source_hash()
+    for f in sorted(os.listdir(PROFILES)):
+        if not f.endswith(".md"):
+            continue
+        for line in open(os.path.join(PROFILES, f)):
+            if line.startswith("traffic-record: "):
+                rec = json.loads(line[len("traffic-record: "):])
+                if rec.get("workload") == workload_name and rec.get("source_sha256") == want:
+                    return rec.get("bytes_per_launch")
+    return None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -161,7 +301,19 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one 1 GiB device copy (counter calibration for --pmc runs)")
+    ap.add_argument("--trace-summary", metavar="RESULTS_DB", help="summarise a rocprofv3 kernel trace and exit")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="summarise FETCH_SIZE / WRITE_SIZE counter runs and exit")
+    ap.add_argument("--title", default="")
+    ap.add_argument("--command", default="")
     args = ap.parse_args()
+    if args.trace_summary:
+        print(trace_summary(args.trace_summary, args.title, args.command))
+        return
+    if args.traffic_summary:
+        print(traffic_summary(args.traffic_summary[0], args.traffic_summary[1], args.workload, args.title,
+                              args.command))
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
               "(the layer has no multi-GPU path)", file=sys.stderr)
@@ -246,6 +398,8 @@ def main():
                 "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None}
     roof["kernel"] = "gate_up grouped GEMM (+SwiGLU)"
     roof["launch_ms"] = gu_time / len(batches)
+    roof["algorithmic_bytes_per_launch"] = sum(b.gate_up_bytes() for b in batches) / len(batches)
+    roof["traffic"] = traffic_record(args.workload)
 
     layer_bytes = sum(b.layer_bytes() for b in batches)
     layer_flops = sum(b.layer_flops() for b in batches)

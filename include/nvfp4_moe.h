@@ -191,20 +191,21 @@ int moe_run(const moe_plan_t* plan, const void* packed, int32_t T, const uint16_
 #define MOE_NUM_STAGES 5
 
 /* moe_run with per-stage timing: stage_events holds 2*MOE_NUM_STAGES hipEvent_t
- * handles (as void*, any may be NULL); events[2s] is recorded on `stream` right
- * before stage s is enqueued and events[2s+1] right after, so the elapsed time
- * between them is that stage's GPU time. The events must have been created by the
- * caller. Results are identical to moe_run. ([b12x] "Using it": per-kernel timing
- * logs for tuning.) */
+ * handles (as void*, any may be NULL), created by the caller with timing enabled.
+ * For the single-kernel stages (GATE_UP, DOWN, COMBINE) events[2s] and events[2s+1]
+ * are stamped by the kernel launch itself at the kernel's start and end, so their
+ * elapsed time is the kernel's duration; for the others (QUANT, ROUTE: zero to four
+ * kernels) they are recorded on `stream` right before and after the stage. Results
+ * are identical to moe_run. ([b12x] "Using it": per-kernel timing logs for tuning.) */
 int moe_run_timed(const moe_plan_t* plan, const void* packed, int32_t T, const uint16_t* x,
                   const float* router_logits, uint16_t* out, const moe_routing_out* routing,
                   void* workspace, size_t workspace_bytes, void* stream, void* const* stage_events);
 
 /* NVFP4 row quantiser (the W4A4 activation step of moe_run, callable alone):
  * for each of `rows` bf16 rows of K elements (K a multiple of 16, <= 16384):
- *   gs   = max|x| / 2688                        ([megamoe] archived
- *          CORRECTNESS_BACKLOG §7 "Runtime Activation Global Scale":
- *          gsa = max(|x|) / (6.0 * 448.0))
+ *   gs   = max|x| / 2688, 2688 = 6 * 448 the largest E2M1 value times the largest
+ *          E4M3 value ([megamoe] archived CORRECTNESS_BACKLOG §7, runtime activation
+ *          global scale)
  *   s_b  = E4M3 nearest-even of a_b / (6 gs), saturating at 448; 0 if gs == 0
  *   d_b  = E4M3(s_b) * gs
  *   code = sign | E2M1 nearest-even of |x| / d_b, saturating at 6; 0 if d_b == 0

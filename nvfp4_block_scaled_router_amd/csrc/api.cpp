@@ -200,9 +200,20 @@ int moe_run_timed(const moe_plan_t* plan, const void* packed, int32_t T, const u
                   stage_events);
 }
 
+// Stages of several (or no) kernels are bracketed by event records on the stream; the
+// single-kernel stages (the GEMMs, the combine) get kernel-stamped events instead.
 static hipError_t mark(void* const* ev, int idx, hipStream_t s) {
   if (!ev || !ev[idx]) return hipSuccess;
   return hipEventRecord((hipEvent_t)ev[idx], s);
+}
+
+static LaunchEvents stage_events(void* const* ev, int stage) {
+  LaunchEvents le;
+  if (ev) {
+    le.start = (hipEvent_t)ev[2 * stage];
+    le.stop = (hipEvent_t)ev[2 * stage + 1];
+  }
+  return le;
 }
 
 static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const uint16_t* x,
@@ -305,10 +316,8 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
   g1.out = (uint16_t*)(ws + plan->ws_h);
   const size_t hplane = ((size_t)d.max_tokens * k + (size_t)S * d.max_tokens) * I;
   g1.out_lo = g1.out + hplane;
-  if ((e = mark(ev, 2 * MOE_STAGE_GATE_UP, s)) != hipSuccess) return (int)e;
-  e = launch_gemm(gu_mode, regime, max_tiles, est_tiles, g1, s);
+  e = launch_gemm(gu_mode, regime, max_tiles, est_tiles, g1, s, stage_events(ev, MOE_STAGE_GATE_UP));
   if (e != hipSuccess) return (int)e;
-  if ((e = mark(ev, 2 * MOE_STAGE_GATE_UP + 1, s)) != hipSuccess) return (int)e;
 
   GemmArgs g2 = g1;
   g2.wfp4 = pk + plan->off_w2f;
@@ -320,10 +329,8 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
   g2.xlo = g1.out_lo;
   g2.out = nullptr;
   g2.yout = (float*)(ws + plan->ws_y);
-  if ((e = mark(ev, 2 * MOE_STAGE_DOWN, s)) != hipSuccess) return (int)e;
-  e = launch_gemm(GEMM_DOWN, regime, max_tiles, est_tiles, g2, s);
+  e = launch_gemm(GEMM_DOWN, regime, max_tiles, est_tiles, g2, s, stage_events(ev, MOE_STAGE_DOWN));
   if (e != hipSuccess) return (int)e;
-  if ((e = mark(ev, 2 * MOE_STAGE_DOWN + 1, s)) != hipSuccess) return (int)e;
 
   CombineArgs c;
   c.y = (const float*)(ws + plan->ws_y);
@@ -334,10 +341,7 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
   c.k = k;
   c.S = S;
   c.out = out;
-  if ((e = mark(ev, 2 * MOE_STAGE_COMBINE, s)) != hipSuccess) return (int)e;
-  e = launch_combine(c, s);
-  if (e != hipSuccess) return (int)e;
-  return (int)mark(ev, 2 * MOE_STAGE_COMBINE + 1, s);
+  return (int)launch_combine(c, s, stage_events(ev, MOE_STAGE_COMBINE));
 }
 
 int moe_quantize_nvfp4_rows(const uint16_t* x, int32_t rows, int32_t K, uint8_t* packed, uint8_t* scales,

@@ -32,6 +32,8 @@
 // feeds 8 of them to each of the chunk's 4 MFMAs; A and B use the same k order, so
 // the dot products are unchanged. D: lane l holds rows 4*(l/16)+r, r < 4, of token
 // l%16, i.e. 4 consecutive output features of one token.
+#include <hip/hip_ext.h>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -256,6 +258,27 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs a) {
   }
 }
 
+// XCD-aware work order of the prefill GEMMs. Workgroups are handed to the 8 XCDs (each
+// with its own L2) round-robin by linear id, so consecutive ids never share an L2. The
+// grid is (n-blocks) x (slot bound rounded up to 8); workgroup id i runs on XCD i % 8 and
+// is given the (i / 8)-th item of that XCD's list: a contiguous run of ceil(ntiles / 8)
+// tile slots, each with all its n-blocks. The n-blocks of one token tile then share its
+// rows in one L2, and consecutive slots (mostly of one expert) share its weight tiles.
+struct PrefillItem {
+  int slot, nb;
+};
+__device__ __forceinline__ PrefillItem prefill_item(int ntiles) {
+  const int NB = gridDim.x;
+  const int lin = blockIdx.y * NB + blockIdx.x;
+  const int xcd = lin & 7, j = lin >> 3;
+  const int per_xcd = (ntiles + 7) >> 3;
+  PrefillItem it;
+  const int k = j / NB;
+  it.nb = j - k * NB;
+  it.slot = k < per_xcd ? xcd * per_xcd + k : ntiles;   // past the list: no work
+  return it;
+}
+
 // LDS slot swizzle of the prefill token tiles: piece c of row r sits at slot c ^ lds_swz(r).
 // An MFMA operand read has lane (l%16, l/16) fetch row 16t + l%16, piece 4(l/16) + j. With
 // lds_swz(r) = G((r >> 1) & 7) ^ 4 (r & 1), G(q) = (q & 3) | 2 (q & 4), these 16-byte reads
@@ -277,12 +300,14 @@ __global__ __launch_bounds__(256) void gemm_prefill_kernel(GemmArgs a) {
   constexpr int M = TSUB * 16;
   constexpr int PLANES = MODE == GEMM_DOWN ? 2 : 1;   // down: h_hi and h_lo
   __shared__ u32x4 tile[2][PLANES][M * 16];
-  const int slot = blockIdx.y;
-  if (slot >= a.tile_count[0]) return;
+  const int ntiles = a.tile_count[0];
+  const PrefillItem item = prefill_item(ntiles);
+  const int slot = item.slot;
+  if (slot >= ntiles) return;
   const ProjLayout L = proj_layout(a.N, a.K);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & (WAVE - 1);
   const int l16 = lane & 15, lg = lane >> 4;
-  const int q0 = (blockIdx.x * 4 + wave) * NSUB;
+  const int q0 = (item.nb * 4 + wave) * NSUB;
   const bool active = q0 < L.N / 16;                     // wave owns weight tiles
   const int g = a.tile_group[slot];
   const int row0 = a.tile_row0[slot];
@@ -454,16 +479,17 @@ __global__ __launch_bounds__(256) void gemm_prefill_dma_kernel(GemmArgs a) {
   constexpr bool F16 = MODE == GEMM_GATEUP_F16;
   __shared__ u32x4 tile[NBUF * STAGE];
 
-  const int slot = blockIdx.y;
   const int ntiles = a.tile_count[0];
+  const PrefillItem item = prefill_item(ntiles);
+  const int slot = item.slot;
+  if (slot >= ntiles) return;
   const int g = a.tile_group[slot];
   const int row0 = a.tile_row0[slot];
-  if (slot >= ntiles) return;
   const ProjLayout L = proj_layout(a.N, a.K);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & (WAVE - 1);
   const int l16 = lane & 15, lg = lane >> 4;
-  const int q0 = (blockIdx.x * 4 + wave) * NSUB;          // the launch covers N exactly
+  const int q0 = (item.nb * 4 + wave) * NSUB;             // the launch covers N exactly
   const int nvalid = min(M, a.offsets[g + 1] - row0);
 
   // DMA instruction i of this wave fills slots (4i + wave) * 64 .. +63 of a plane: row
@@ -596,6 +622,15 @@ __global__ __launch_bounds__(256) void gemm_prefill_dma_kernel(GemmArgs a) {
 
 // ---------------------------------------------------------------------- launch
 
+template <typename K>
+static void launch_k(K kernel, dim3 grid, dim3 block, hipStream_t s, const LaunchEvents& ev, const GemmArgs& a) {
+  if (ev.start || ev.stop)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, ev.start, ev.stop, 0, a);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, s, a);
+}
+
+
 constexpr int PRE_NSUB_GU = 2;    // prefill gate_up: 1 gate + 1 up tile per wave (2 workgroups per CU)
 constexpr int PRE_NSUB_DN = 4;    // prefill down: 64 rows per wave (each tile meets h_hi and h_lo)
 constexpr int PRE_TSUB = 8;       // prefill: 128 token rows per tile
@@ -607,46 +642,48 @@ constexpr int DEC_MIN_WGS = 2048; // decode: 8 workgroups per CU before 4 tiles 
 // when that still gives about 8 workgroups per CU, else 2; the K chunks go to the largest
 // of 4 / 3 / 2 waves that divides them evenly (4 if none does).
 template <int MODE>
-static void launch_decode(int max_tiles, int est_tiles, const GemmArgs& a, hipStream_t s) {
+static void launch_decode(int max_tiles, int est_tiles, const GemmArgs& a, hipStream_t s,
+                          const LaunchEvents& ev) {
   const int nsub16 = a.N / 16, kc = a.K / KCHUNK;
   const bool wide = nsub16 % 4 == 0 && (long)est_tiles * (nsub16 / 4) >= DEC_MIN_WGS;
   int nw = kc % 4 == 0 ? 4 : kc % 3 == 0 ? 3 : kc % 2 == 0 ? 2 : 4;
   nw = min(nw, kc);
   if (wide) {
-    hipLaunchKernelGGL((gemm_decode_kernel<MODE, 4>), dim3(nsub16 / 4, max_tiles), dim3(64 * nw), 0, s, a);
+    launch_k(gemm_decode_kernel<MODE, 4>, dim3(nsub16 / 4, max_tiles), dim3(64 * nw), s, ev, a);
   } else {
-    hipLaunchKernelGGL((gemm_decode_kernel<MODE, 2>), dim3(nsub16 / 2, max_tiles), dim3(64 * nw), 0, s, a);
+    launch_k(gemm_decode_kernel<MODE, 2>, dim3(nsub16 / 2, max_tiles), dim3(64 * nw), s, ev, a);
   }
 }
 
 template <int MODE>
-static void launch_mode(GemmRegime regime, int max_tiles, int est_tiles, const GemmArgs& a, hipStream_t s) {
+static void launch_mode(GemmRegime regime, int max_tiles, int est_tiles, const GemmArgs& a, hipStream_t s,
+                        const LaunchEvents& ev) {
   if (regime == REGIME_DECODE_KSPLIT) {
-    launch_decode<MODE>(max_tiles, est_tiles, a, s);
+    launch_decode<MODE>(max_tiles, est_tiles, a, s, ev);
   } else if constexpr (MODE == GEMM_GATEUP_F16 || MODE == GEMM_DOWN) {
     constexpr int NS = MODE == GEMM_DOWN ? PRE_NSUB_DN : PRE_NSUB_GU;
     constexpr int NB = MODE == GEMM_DOWN ? 2 : PRE_NBUF_GU;
-    dim3 grid((a.N / 16 + 4 * NS - 1) / (4 * NS), max_tiles);
+    dim3 grid((a.N / 16 + 4 * NS - 1) / (4 * NS), (max_tiles + 7) / 8 * 8);
     if ((a.N / 16) % (4 * NS) == 0)
-      hipLaunchKernelGGL((gemm_prefill_dma_kernel<MODE, NS, PRE_TSUB, NB>), grid, dim3(256), 0, s, a);
+      launch_k(gemm_prefill_dma_kernel<MODE, NS, PRE_TSUB, NB>, grid, dim3(256), s, ev, a);
     else
-      hipLaunchKernelGGL((gemm_prefill_kernel<MODE, NS, PRE_TSUB>), grid, dim3(256), 0, s, a);
+      launch_k(gemm_prefill_kernel<MODE, NS, PRE_TSUB>, grid, dim3(256), s, ev, a);
   } else if constexpr (MODE == GEMM_GATEUP_FP4) {
     constexpr int NS = PRE_NSUB_GU;
-    dim3 grid((a.N / 16 + 4 * NS - 1) / (4 * NS), max_tiles);
-    hipLaunchKernelGGL((gemm_prefill_kernel<MODE, NS, PRE_TSUB>), grid, dim3(256), 0, s, a);
+    dim3 grid((a.N / 16 + 4 * NS - 1) / (4 * NS), (max_tiles + 7) / 8 * 8);
+    launch_k(gemm_prefill_kernel<MODE, NS, PRE_TSUB>, grid, dim3(256), s, ev, a);
   }
 }
 
 hipError_t launch_gemm(GemmMode mode, GemmRegime regime, int max_tiles, int est_tiles, const GemmArgs& a,
-                       hipStream_t s) {
+                       hipStream_t s, const LaunchEvents& ev) {
   if (max_tiles <= 0) return hipSuccess;
   if (mode == GEMM_GATEUP_BF16 && regime != REGIME_DECODE_KSPLIT) return hipErrorInvalidValue;
   switch (mode) {
-    case GEMM_GATEUP_F16: launch_mode<GEMM_GATEUP_F16>(regime, max_tiles, est_tiles, a, s); break;
-    case GEMM_GATEUP_BF16: launch_mode<GEMM_GATEUP_BF16>(regime, max_tiles, est_tiles, a, s); break;
-    case GEMM_GATEUP_FP4: launch_mode<GEMM_GATEUP_FP4>(regime, max_tiles, est_tiles, a, s); break;
-    case GEMM_DOWN: launch_mode<GEMM_DOWN>(regime, max_tiles, est_tiles, a, s); break;
+    case GEMM_GATEUP_F16: launch_mode<GEMM_GATEUP_F16>(regime, max_tiles, est_tiles, a, s, ev); break;
+    case GEMM_GATEUP_BF16: launch_mode<GEMM_GATEUP_BF16>(regime, max_tiles, est_tiles, a, s, ev); break;
+    case GEMM_GATEUP_FP4: launch_mode<GEMM_GATEUP_FP4>(regime, max_tiles, est_tiles, a, s, ev); break;
+    case GEMM_DOWN: launch_mode<GEMM_DOWN>(regime, max_tiles, est_tiles, a, s, ev); break;
   }
   return hipGetLastError();
 }
@@ -700,9 +737,13 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
             f32_to_bf16_rne(acc.z) | (f32_to_bf16_rne(acc.w) << 16)};
 }
 
-hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s, const LaunchEvents& ev) {
   if (a.T <= 0) return hipSuccess;
-  hipLaunchKernelGGL(combine_kernel, dim3(a.T, (a.H + COMBINE_COLS - 1) / COMBINE_COLS), dim3(128), 0, s, a);
+  const dim3 grid(a.T, (a.H + COMBINE_COLS - 1) / COMBINE_COLS);
+  if (ev.start || ev.stop)
+    hipExtLaunchKernelGGL(combine_kernel, grid, dim3(128), 0, s, ev.start, ev.stop, 0, a);
+  else
+    hipLaunchKernelGGL(combine_kernel, grid, dim3(128), 0, s, a);
   return hipGetLastError();
 }
 

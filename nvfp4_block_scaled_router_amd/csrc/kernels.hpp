@@ -98,9 +98,16 @@ struct GemmArgs {
 // direct token loads), N split with a 16-row LDS token tile (kept for experiments), and
 // prefill (N split, 128-row LDS token tiles).
 enum GemmRegime { REGIME_DECODE_KSPLIT = 0, REGIME_DECODE_NSPLIT = 1, REGIME_PREFILL = 2 };
+// Optional timing of a single-kernel stage: when set, the kernel is launched with
+// hipExtLaunchKernelGGL, which stamps the events at the kernel's own start and end (no
+// enqueue or dispatch gap inside the measured interval).
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+
 // est_tiles: expected number of valid tile slots (sizes the decode split); max_tiles: grid bound.
 hipError_t launch_gemm(GemmMode mode, GemmRegime regime, int max_tiles, int est_tiles, const GemmArgs& a,
-                       hipStream_t s);
+                       hipStream_t s, const LaunchEvents& ev = LaunchEvents());
 
 struct CombineArgs {
   const float* y;          // fp32 [rows_total][H] expert outputs
@@ -109,7 +116,7 @@ struct CombineArgs {
   int T, H, k, S;
   uint16_t* out;           // bf16 [T][H]
 };
-hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s, const LaunchEvents& ev = LaunchEvents());
 
 
 }  // namespace nvmoe

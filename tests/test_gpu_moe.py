@@ -116,3 +116,28 @@ def test_token_counts_within_capacity():
     m.moe_run(L.plan, L.packed, 0, x, lg, sentinel, None, L.workspace, L.workspace_bytes)
     torch.cuda.synchronize()
     assert torch.all(sentinel == 7.0)
+
+
+@pytest.mark.parametrize("T", [8, 300])
+def test_run_timed_matches_run(T):
+    """moe_run_timed gives moe_run's bytes and a positive time for every stage that runs
+    kernels (decode regime at T = 8, prefill regime at T = 300)."""
+    import nvfp4_block_scaled_router_amd as m
+    cfg = synth.with_tokens(synth.qwen3_prefill(), T, f"qwen3-t{T}")
+    case = Case(cfg)
+    L = case.layer()
+    x, lg = bf16(case.x), up(case.logits)
+    a = L(x, lg).clone()
+    out = torch.empty_like(a)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * m.MOE_NUM_STAGES)]
+    for e in ev:
+        e.record()
+    torch.cuda.synchronize()
+    m.moe_run_timed(L.plan, L.packed, T, x, lg, out, None, L.workspace, L.workspace_bytes, None,
+                    [e.cuda_event for e in ev])
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), a.view(torch.int16))
+    for s in (m.MOE_STAGE_ROUTE, m.MOE_STAGE_GATE_UP, m.MOE_STAGE_DOWN, m.MOE_STAGE_COMBINE):
+        t = ev[2 * s].elapsed_time(ev[2 * s + 1])
+        log(f"T={T} stage {m.STAGE_NAMES[s]}: {t * 1e3:.1f} us")
+        assert 0.0 < t < 1000.0
