@@ -23,7 +23,10 @@ SOURCES = {
     "route.hip": [],
     "quant.hip": ["-ffp-contract=off"],
     "pack.hip": [],
-    "gemm.hip": [],
+    # MFMA accumulators in architectural VGPRs: the default AGPR form makes the register
+    # allocator shuttle accumulators between the two files inside the K loops
+    # (v_accvgpr_read/write, about one per MFMA) and raises the register count.
+    "gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
 }
 
 

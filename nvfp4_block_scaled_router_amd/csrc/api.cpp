@@ -46,7 +46,7 @@ struct moe_plan {
   ProjLayout w1, w2;
   size_t off_w1f, off_w1s, off_w1g, off_w2f, off_w2s, off_w2g, packed_bytes;
   size_t ws_ids, ws_w, ws_counts, ws_offsets, ws_perm, ws_inv, ws_tok, ws_tgrp, ws_trow, ws_tcnt, ws_plan;
-  size_t ws_xq, ws_xs, ws_xg, ws_x16, ws_h, ws_y, ws_bytes;
+  size_t ws_xq, ws_xs, ws_xg, ws_x16, ws_h, ws_hexp, ws_hmin, ws_y, ws_bytes;
   int max_tiles;
 };
 
@@ -127,7 +127,9 @@ int moe_plan(const moe_desc* desc, moe_plan_t** plan, size_t* packed_bytes, size
   p->ws_xs = o; o = align_up(o + (desc->act_format == MOE_ACT_NVFP4_ROWQ ? (size_t)Tm * H / 16 : 0));
   p->ws_xg = o; o = align_up(o + 4 * (size_t)Tm);      // per-row activation factor (either format)
   p->ws_x16 = o; o = align_up(o + (desc->act_format == MOE_ACT_BF16 ? 2 * (size_t)Tm * H : 0));
-  p->ws_h = o; o = align_up(o + 2 * 2 * rows * I);   // h_hi and h_lo planes
+  p->ws_h = o; o = align_up(o + 2 * rows * I);        // h16
+  p->ws_hexp = o; o = align_up(o + rows * (I / 16));  // per-16-column h exponents
+  p->ws_hmin = o; o = align_up(o + 4 * rows);         // per-row minimum h exponent
   p->ws_y = o; o = align_up(o + 4 * rows * H);
   p->ws_bytes = o;
   if (packed_bytes) *packed_bytes = p->packed_bytes;
@@ -287,6 +289,7 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
   pa.tile_group = (int32_t*)(ws + plan->ws_tgrp);
   pa.tile_row0 = (int32_t*)(ws + plan->ws_trow);
   pa.tile_count = (int32_t*)(ws + plan->ws_tcnt);
+  pa.hmin = (int32_t*)(ws + plan->ws_hmin);
   pa.counts_user = r.expert_counts;
   pa.offsets_user = r.expert_offsets;
   pa.perm_user = r.perm;
@@ -314,8 +317,8 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
   g1.tile_count = pa.tile_count;
   g1.offsets = pa.offsets;
   g1.out = (uint16_t*)(ws + plan->ws_h);
-  const size_t hplane = ((size_t)d.max_tokens * k + (size_t)S * d.max_tokens) * I;
-  g1.out_lo = g1.out + hplane;
+  g1.hexp = (int8_t*)(ws + plan->ws_hexp);
+  g1.hmin = decode ? nullptr : pa.hmin;
   e = launch_gemm(gu_mode, regime, max_tiles, est_tiles, g1, s, stage_events(ev, MOE_STAGE_GATE_UP));
   if (e != hipSuccess) return (int)e;
 
@@ -326,7 +329,6 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
   g2.N = H;
   g2.K = I;
   g2.x = g1.out;
-  g2.xlo = g1.out_lo;
   g2.out = nullptr;
   g2.yout = (float*)(ws + plan->ws_y);
   e = launch_gemm(GEMM_DOWN, regime, max_tiles, est_tiles, g2, s, stage_events(ev, MOE_STAGE_DOWN));

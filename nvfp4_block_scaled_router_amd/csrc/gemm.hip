@@ -105,12 +105,11 @@ __device__ __forceinline__ const u32x4* sc_tile(const GemmArgs& a, const ProjLay
   return (const u32x4*)(a.wsc + tile * (WAVE * 16)) + (threadIdx.x & (WAVE - 1));
 }
 
-__device__ __forceinline__ void store_bf16x4(uint16_t* p, float v0, float v1, float v2, float v3) {
-  *(u32x2*)p = u32x2{f32_to_bf16_rne(v0) | (f32_to_bf16_rne(v1) << 16),
-                     f32_to_bf16_rne(v2) | (f32_to_bf16_rne(v3) << 16)};
-}
-
-// Epilogue for one 16-feature x 16-token D tile pair / single.
+// Epilogue for one 16-feature x 16-token D tile pair (gate, up) of gate_up: h = silu(g) u
+// for the 16 h columns hs*16 .. +15 of token row `row` (lane: 4 of them), stored as fp16
+// scaled by 2^e with e chosen on the block's largest |h| (the 4 lanes of the row share it
+// through two lane swaps) and recorded in hexp. All 4 lanes of a row must be active
+// together (they are: they hold the same token).
 template <int MODE>
 __device__ __forceinline__ void epilogue_pair(const GemmArgs& a, const f32x4& gacc, const f32x4& uacc, float sc,
                                               int row, int hs) {
@@ -119,16 +118,40 @@ __device__ __forceinline__ void epilogue_pair(const GemmArgs& a, const f32x4& ga
   const size_t off = (size_t)row * NO + h_pos(hs * 16 + 4 * lg);   // 4 columns stay contiguous
   const float h[4] = {silu_mul(gacc.x * sc, uacc.x * sc), silu_mul(gacc.y * sc, uacc.y * sc),
                       silu_mul(gacc.z * sc, uacc.z * sc), silu_mul(gacc.w * sc, uacc.w * sc)};
-  uint32_t hi[4];
-  float lo[4];
+  float mx = fmaxf(fmaxf(fabsf(h[0]), fabsf(h[1])), fmaxf(fabsf(h[2]), fabsf(h[3])));
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  // mx = f 2^x with f in [0.5, 1): mx 2^(15 - x) lies in [2^14, 2^15)
+  const int e = min(max(15 - __builtin_amdgcn_frexp_expf(mx), -H_EXP_MAX), H_EXP_MAX);
+  uint32_t q[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    hi[i] = f32_to_bf16_rne(h[i]);
-    lo[i] = h[i] - bf16_to_f32(hi[i]);          // exact in fp32
+  for (int i = 0; i < 4; ++i) q[i] = __builtin_bit_cast(uint16_t, (_Float16)__builtin_ldexpf(h[i], e));
+  *(u32x2*)(a.out + off) = u32x2{q[0] | (q[1] << 16), q[2] | (q[3] << 16)};
+  if (lg == 0) {
+    a.hexp[(size_t)row * (NO / 16) + hs] = (int8_t)e;
+    if (a.hmin) atomicMin(&a.hmin[row], e);
   }
-  *(u32x2*)(a.out + off) = u32x2{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)};
-  store_bf16x4(a.out_lo + off, lo[0], lo[1], lo[2], lo[3]);
 }
+
+// Smallest h block exponent of a row (nblk bytes, nblk a multiple of 8), read as 8-byte
+// words split over the row's 4 lanes l16 + 16 lg and combined through two lane swaps.
+__device__ __forceinline__ int row_exp_min4(const int8_t* erow, int nblk, int lg) {
+  int m = H_EXP_INIT;
+  for (int w = lg; w < nblk / 8; w += 4) {
+    const u32x2 v = *(const u32x2*)(erow + 8 * w);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      m = min(m, (int)(int8_t)(v.x >> (8 * b)));
+      m = min(m, (int)(int8_t)(v.y >> (8 * b)));
+    }
+  }
+  m = min(m, __shfl_xor(m, 16));
+  return min(m, __shfl_xor(m, 32));
+}
+
+// 2^d for d <= 0 as fp16 (0 below the fp16 range): the per-block factor that brings h16
+// of a block with exponent e to the row's common scale 2^P, d = P - e.
+__device__ __forceinline__ _Float16 h_factor(int d) { return (_Float16)__builtin_ldexpf(1.0f, d); }
 
 __device__ __forceinline__ void epilogue_single(const GemmArgs& a, const f32x4& acc, float sc, int row, int q) {
   const int lg = (threadIdx.x & (WAVE - 1)) >> 4;
@@ -147,7 +170,7 @@ constexpr int DEC_MAX_WAVES = 4;   // measured best of 4 / 8 / 16 on the decode 
 
 template <int MODE, int NSUB>
 __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs a) {
-  constexpr bool F16 = MODE == GEMM_GATEUP_F16 || MODE == GEMM_GATEUP_FP4;
+  constexpr bool F16 = MODE != GEMM_GATEUP_BF16;           // fp16 MFMA (bf16 x: bf16 MFMA)
   const int slot = blockIdx.y;
   // the slot's entries are read together with the count (slots past it hold stale values
   // that are never used), saving one dependent round trip before the weight loads
@@ -165,14 +188,17 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs a) {
   const int row = row0 + min(l16, nvalid - 1);            // clamp: extra columns are never stored
   const int kc0 = (wave * L.KC) / NW, kc1 = ((wave + 1) * L.KC) / NW;
 
-  const uint16_t* xrow = nullptr;                          // 16-bit token rows (fp16 x, bf16 h_hi)
-  const uint16_t* xlrow = nullptr;                         // bf16 h_lo
+  const uint16_t* xrow = nullptr;                          // 16-bit token rows (fp16/bf16 x, h16)
+  const int8_t* erow = nullptr;                            // h block exponents of the row
   const uint8_t* qrow = nullptr;
   const uint8_t* srow = nullptr;
   float sc = wgs;                                          // epilogue factor, loaded before the loop
+  int hm = 0;                                              // the row's common h exponent
   if (MODE == GEMM_DOWN) {
     xrow = a.x + (size_t)row * L.K;
-    xlrow = a.xlo + (size_t)row * L.K;
+    erow = a.hexp + (size_t)row * (L.K / 16);
+    hm = a.hmin ? a.hmin[row] : row_exp_min4(erow, L.K / 16, lg);
+    sc = __builtin_ldexpf(wgs, -hm);
   } else {
     const int t = a.tok[row];
     if (MODE == GEMM_GATEUP_FP4) {
@@ -199,7 +225,7 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs a) {
     u32x4 wv[NSUB];
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) wv[s] = *fp4_tile(a, L, g, q0 + s, kc);
-    u32x4 bop[4], blo[4];
+    u32x4 bop[4];
     if (MODE == GEMM_GATEUP_FP4) {
       const u32x4 xv = *(const u32x4*)(qrow + (size_t)kc * 64 + lg * 16);
       const uint32_t sp = *(const uint16_t*)(srow + (size_t)kc * 8 + 2 * lg);
@@ -207,13 +233,15 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs a) {
       xo.make(xv, sp);
 #pragma unroll
       for (int j = 0; j < 4; ++j) bop[j] = __builtin_bit_cast(u32x4, xo.v[j]);
-    } else if (MODE == GEMM_DOWN) {   // h planes: piece (g, j) at 4j + g
+    } else if (MODE == GEMM_DOWN) {   // h16: piece (g, j) at 4j + g; blocks 2g (j < 2), 2g + 1
       const uint16_t* src = xrow + (size_t)kc * KCHUNK + lg * 8;
-      const uint16_t* lsrc = xlrow + (size_t)kc * KCHUNK + lg * 8;
+      const uint32_t eb = *(const uint16_t*)(erow + kc * 8 + 2 * lg);
+      const _Float16 f0 = h_factor(hm - (int)(int8_t)(eb & 0xFFu)), f1 = h_factor(hm - (int)(int8_t)(eb >> 8));
 #pragma unroll
-      for (int j = 0; j < 4; ++j) bop[j] = *(const u32x4*)(src + 32 * j);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) blo[j] = *(const u32x4*)(lsrc + 32 * j);
+      for (int j = 0; j < 4; ++j) {
+        const f16x8 v = *(const f16x8*)(src + 32 * j);
+        bop[j] = __builtin_bit_cast(u32x4, v * (j < 2 ? f0 : f1));
+      }
     } else {
       const u32x4* src = (const u32x4*)(xrow + (size_t)kc * KCHUNK + lg * 32);
 #pragma unroll
@@ -225,10 +253,6 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs a) {
       w.make(wv[s], chunk_scale_bytes(sgv[s], kc & 7));
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[s] = mfma_any(w.v[j], bop[j], acc[s]);
-      if (MODE == GEMM_DOWN) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[s] = mfma_any(w.v[j], blo[j], acc[s]);
-      }
     }
   }
 
@@ -290,175 +314,20 @@ __device__ __forceinline__ int lds_swz(int r) {
 }
 
 // ----------------------------------------------------------------- prefill GEMM
-// Tiles of TSUB*16 rows of one expert x (4 waves x NSUB) 16-row weight tiles. Token
-// rows are gathered (through the row->token map) chunk by chunk into a double-buffered
-// LDS tile shared by the 4 waves; each wave streams its own weight tiles straight into
-// registers and dequantises them there. LDS rows are 256 bytes (one 128-column chunk
-// of 16-bit values); 16-byte piece c of row r is stored at slot c ^ lds_swz(r).
-template <int MODE, int NSUB, int TSUB>
-__global__ __launch_bounds__(256) void gemm_prefill_kernel(GemmArgs a) {
-  constexpr int M = TSUB * 16;
-  constexpr int PLANES = MODE == GEMM_DOWN ? 2 : 1;   // down: h_hi and h_lo
-  __shared__ u32x4 tile[2][PLANES][M * 16];
-  const int ntiles = a.tile_count[0];
-  const PrefillItem item = prefill_item(ntiles);
-  const int slot = item.slot;
-  if (slot >= ntiles) return;
-  const ProjLayout L = proj_layout(a.N, a.K);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & (WAVE - 1);
-  const int l16 = lane & 15, lg = lane >> 4;
-  const int q0 = (item.nb * 4 + wave) * NSUB;
-  const bool active = q0 < L.N / 16;                     // wave owns weight tiles
-  const int g = a.tile_group[slot];
-  const int row0 = a.tile_row0[slot];
-  const int nvalid = min(M, a.offsets[g + 1] - row0);
-
-  // staging assignment: bf16 modes move 16-byte pieces (8 columns), TSUB per thread;
-  // the NVFP4 mode moves 16-column pieces (8 code bytes + 1 scale byte), TSUB/2 per thread
-  constexpr int PER_ROW = (MODE == GEMM_GATEUP_FP4) ? 8 : 16;
-  constexpr int NPIECE = (M * PER_ROW + 255) / 256;
-  constexpr bool ALL_PIECES = (M * PER_ROW) % 256 == 0;   // else the last round is partial
-  const uint16_t* xsrc[NPIECE];
-  const uint16_t* xlsrc[NPIECE];
-  const uint8_t* qsrc[NPIECE];
-  const uint8_t* ssrc[NPIECE];
-  int prow[NPIECE], pcol[NPIECE];
-#pragma unroll
-  for (int i = 0; i < NPIECE; ++i) {
-    const int p = min((int)threadIdx.x + 256 * i, M * PER_ROW - 1);   // surplus threads mirror the last piece
-    prow[i] = p / PER_ROW;
-    pcol[i] = p % PER_ROW;
-    const int r = row0 + min(prow[i], nvalid - 1);
-    if (MODE == GEMM_DOWN) {
-      xsrc[i] = a.x + (size_t)r * L.K + pcol[i] * 8;
-      xlsrc[i] = a.xlo + (size_t)r * L.K + pcol[i] * 8;
-    } else if (MODE == GEMM_GATEUP_F16) {
-      xsrc[i] = a.x + (size_t)a.tok[r] * L.K + pcol[i] * 8;
-    } else {
-      const int t = a.tok[r];
-      qsrc[i] = a.xq + (size_t)t * (L.K / 2) + pcol[i] * 8;
-      ssrc[i] = a.xs + (size_t)t * (L.K / 16) + pcol[i];
-    }
-  }
-  u32x4 stg[NPIECE], stg_lo[NPIECE];
-  uint32_t stg_s[NPIECE];
-  u32x2 stg_q[NPIECE];
-  auto stage_load = [&](int kc) {
-#pragma unroll
-    for (int i = 0; i < NPIECE; ++i) {
-      if (MODE == GEMM_GATEUP_FP4) {
-        stg_q[i] = *(const u32x2*)(qsrc[i] + (size_t)kc * 64);
-        stg_s[i] = ssrc[i][(size_t)kc * 8];
-      } else {
-        stg[i] = *(const u32x4*)(xsrc[i] + (size_t)kc * KCHUNK);
-        if (MODE == GEMM_DOWN) stg_lo[i] = *(const u32x4*)(xlsrc[i] + (size_t)kc * KCHUNK);
-      }
-    }
-  };
-  auto stage_store = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < NPIECE; ++i) {
-      if (!ALL_PIECES && (int)threadIdx.x + 256 * i >= M * PER_ROW) continue;
-      const int r = prow[i];
-      if (MODE == GEMM_GATEUP_FP4) {
-        const f16x2 s1 = e4m3x2_to_f16x2(stg_s[i]);
-        const f16x2 s2 = {s1.x, s1.x};
-        const f16x8 lo = dequant8_f16(stg_q[i].x, s2), hi = dequant8_f16(stg_q[i].y, s2);
-        const int c = 2 * pcol[i];
-        tile[buf][0][r * 16 + (c ^ lds_swz(r))] = __builtin_bit_cast(u32x4, lo);
-        tile[buf][0][r * 16 + ((c + 1) ^ lds_swz(r))] = __builtin_bit_cast(u32x4, hi);
-      } else {
-        const int c = MODE == GEMM_DOWN ? h_piece(pcol[i]) : pcol[i];   // LDS holds k order
-        tile[buf][0][r * 16 + (c ^ lds_swz(r))] = stg[i];
-        if (MODE == GEMM_DOWN) tile[buf][PLANES - 1][r * 16 + (c ^ lds_swz(r))] = stg_lo[i];
-      }
-    }
-  };
-
-  f32x4 acc[NSUB][TSUB];
-#pragma unroll
-  for (int s = 0; s < NSUB; ++s)
-#pragma unroll
-    for (int t = 0; t < TSUB; ++t) acc[s][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  u32x4 wcur[NSUB], wnext[NSUB], scur[NSUB], snext[NSUB];
-  if (active) {
-#pragma unroll
-    for (int s = 0; s < NSUB; ++s) {
-      wnext[s] = *fp4_tile(a, L, g, q0 + s, 0);
-      snext[s] = *sc_tile(a, L, g, q0 + s, 0);
-    }
-  }
-  stage_load(0);
-  for (int kc = 0; kc < L.KC; ++kc) {
-    const int buf = kc & 1;
-    stage_store(buf);
-    if (kc + 1 < L.KC) stage_load(kc + 1);
-    if (active) {
-#pragma unroll
-      for (int s = 0; s < NSUB; ++s) {
-        wcur[s] = wnext[s];
-        if ((kc & 7) == 0) scur[s] = snext[s];
-      }
-      if (kc + 1 < L.KC) {
-#pragma unroll
-        for (int s = 0; s < NSUB; ++s) {
-          wnext[s] = *fp4_tile(a, L, g, q0 + s, kc + 1);
-          if (((kc + 1) & 7) == 0) snext[s] = *sc_tile(a, L, g, q0 + s, (kc + 1) >> 3);
-        }
-      }
-    }
-    __syncthreads();
-    if (active) {
-      WOps<MODE != GEMM_DOWN> aop[NSUB];
-#pragma unroll
-      for (int s = 0; s < NSUB; ++s) aop[s].make(wcur[s], chunk_scale_bytes(scur[s], kc & 7));
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int c = lg * 4 + j;
-#pragma unroll
-        for (int t = 0; t < TSUB; ++t) {
-          const int r = t * 16 + l16;
-          const u32x4 bop = tile[buf][0][r * 16 + (c ^ lds_swz(l16))];
-#pragma unroll
-          for (int s = 0; s < NSUB; ++s) acc[s][t] = mfma_any(aop[s].v[j], bop, acc[s][t]);
-          if (MODE == GEMM_DOWN) {
-            const u32x4 blo = tile[buf][PLANES - 1][r * 16 + (c ^ lds_swz(l16))];
-#pragma unroll
-            for (int s = 0; s < NSUB; ++s) acc[s][t] = mfma_any(aop[s].v[j], blo, acc[s][t]);
-          }
-        }
-      }
-    }
-  }
-
-  if (!active) return;
-  const float wgs = a.wgs[g];
-#pragma unroll
-  for (int t = 0; t < TSUB; ++t) {
-    const int rr = t * 16 + l16;
-    if (rr >= nvalid) continue;
-    const int orow = row0 + rr;
-    float sc = wgs;
-    if (MODE != GEMM_DOWN) sc *= a.xg[a.tok[orow]];
-    if (MODE == GEMM_DOWN) {
-#pragma unroll
-      for (int s = 0; s < NSUB; ++s) epilogue_single(a, acc[s][t], sc, orow, q0 + s);
-    } else {
-#pragma unroll
-      for (int s = 0; s < NSUB; s += 2) epilogue_pair<MODE>(a, acc[s][t], acc[s + 1][t], sc, orow, (q0 + s) >> 1);
-    }
-  }
-}
-
-// ------------------------------------------------------ prefill GEMM, LDS DMA staging
-// Same tiling as gemm_prefill_kernel for 16-bit token operands (fp16 x for gate_up; the
-// h_hi / h_lo planes for down), but the token tile moves global -> LDS with
-// global_load_lds_dwordx4 (no staging registers, no LDS store instructions) through an
-// NBUF-deep ring of LDS stages, chunk kc + NBUF - 1 in flight while chunk kc is consumed.
-// One DMA instruction writes 64 consecutive 16-byte LDS slots (lane i -> slot i), so the
-// swizzle is applied on the global side: the lane that fills slot (r, c) fetches piece
-// c ^ lds_swz(r) of row r.
+// Tiles of TSUB*16 token rows of one expert x (4 waves x NSUB) 16-row weight tiles. The
+// token tile of each 128-column chunk sits in LDS (rows of 256 bytes: one chunk of 16-bit
+// values, 16-byte piece c of row r at slot c ^ lds_swz(r)), shared by the 4 waves; each
+// wave streams its own weight tiles straight into registers (two alternating register
+// sets, one chunk ahead) and dequantises them there. Token tiles arrive by
+//  - LDS DMA (fp16 activations, GATEUP_F16): global_load_lds_dwordx4 straight into an
+//    NBUF-deep ring of stages, no staging registers, chunk kc + NBUF - 1 in flight while
+//    chunk kc is consumed. One DMA instruction writes 64 consecutive 16-byte slots (lane i
+//    -> slot i), so the swizzle is applied on the global side: the lane that fills slot
+//    (r, c) fetches piece c ^ lds_swz(r) of row r;
+//  - registers (NVFP4 activations, GATEUP_FP4; h16, DOWN), converted on the way in: E2M1
+//    codes x E4M3 block scale -> fp16, or h16 x 2^(P - hexp) -> the row's common scale 2^P;
+//    two stages, chunk kc + 1 loaded while chunk kc is consumed.
+// Issue order inside a chunk is pinned with scheduling barriers (the wait counts rely on it).
 __device__ __forceinline__ void dma16(const void* src, const void* lds_dst) {
   __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
                                    (void __attribute__((address_space(3)))*)lds_dst, 16, 0, 0);
@@ -468,16 +337,18 @@ __device__ __forceinline__ void dma16(const void* src, const void* lds_dst) {
 constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8); }
 
 template <int MODE, int NSUB, int TSUB, int NBUF>
-__global__ __launch_bounds__(256) void gemm_prefill_dma_kernel(GemmArgs a) {
-  static_assert(MODE == GEMM_GATEUP_F16 || MODE == GEMM_DOWN, "16-bit token operands only");
-  static_assert(NBUF == 2 || NBUF == 3, "LDS ring depth");
+__global__ __launch_bounds__(256, 2) void gemm_prefill_kernel(GemmArgs a) {
+  static_assert(MODE == GEMM_GATEUP_F16 || MODE == GEMM_GATEUP_FP4 || MODE == GEMM_DOWN, "prefill modes");
+  constexpr bool DMA = MODE == GEMM_GATEUP_F16;
+  static_assert(!DMA || NBUF == 2 || NBUF == 3, "LDS ring depth");
+  constexpr int NST = DMA ? NBUF : 2;                 // LDS stages
   constexpr int M = TSUB * 16;
-  constexpr int PLANES = MODE == GEMM_DOWN ? 2 : 1;   // down: h_hi and h_lo
-  constexpr int PLANE = M * 16;                       // 16-byte slots per plane per stage
-  constexpr int STAGE = PLANES * PLANE;
-  constexpr int D = PLANES * TSUB;                    // DMA instructions per lane per chunk
-  constexpr bool F16 = MODE == GEMM_GATEUP_F16;
-  __shared__ u32x4 tile[NBUF * STAGE];
+  constexpr int STAGE = M * 16;                       // 16-byte slots per stage
+  constexpr int D = TSUB;                             // DMA instructions per lane per chunk
+  // register staging: DOWN moves 16-byte h16 pieces (TSUB per thread), FP4 moves 16-column
+  // pieces (8 code bytes + 1 scale byte, TSUB/2 per thread, TSUB even)
+  constexpr int NPC = MODE == GEMM_DOWN ? TSUB : TSUB / 2;
+  __shared__ u32x4 tile[NST * STAGE];
 
   const int ntiles = a.tile_count[0];
   const PrefillItem item = prefill_item(ntiles);
@@ -492,31 +363,82 @@ __global__ __launch_bounds__(256) void gemm_prefill_dma_kernel(GemmArgs a) {
   const int q0 = (item.nb * 4 + wave) * NSUB;             // the launch covers N exactly
   const int nvalid = min(M, a.offsets[g + 1] - row0);
 
-  // DMA instruction i of this wave fills slots (4i + wave) * 64 .. +63 of a plane: row
-  // r = 4 (4i + wave) + lane / 16, slot column lane % 16. Byte offsets (32-bit) from the
-  // plane's chunk base.
-  uint32_t src_off[TSUB];
+  // ---- token-tile staging
+  // DMA: instruction i of this wave fills slots (4i + wave) * 64 .. +63: row
+  // r = 4 (4i + wave) + lane / 16, slot column lane % 16; byte offsets from the chunk base.
+  uint32_t src_off[DMA ? TSUB : 1];
+  // registers: piece i of this thread is piece (threadIdx.x + 256 i) of the tile, in row
+  // r0 + 16 i (DOWN) or r0 + 32 i (FP4): the same r % 16 for every i, so one slot base
+  // (+ 256 i) serves all; sources as 32-bit offsets from the chunk-0 base
+  uint32_t poff[DMA || MODE == GEMM_DOWN ? 1 : NPC];     // FP4: bytes into xq
+  int phm[MODE == GEMM_DOWN ? NPC : 1];                   // DOWN: the row's common exponent P
+  const int pcol = MODE == GEMM_DOWN ? (int)(threadIdx.x & 15) : (int)(threadIdx.x & 7);
+  const int r0 = MODE == GEMM_DOWN ? (int)(threadIdx.x >> 4) : (int)(threadIdx.x >> 3);
+  const int swz0 = lds_swz(r0);
+  // DOWN: stored piece pcol of a chunk holds k-piece h_piece(pcol), of h block 8 kc + kp / 2
+  if constexpr (DMA) {
 #pragma unroll
-  for (int i = 0; i < TSUB; ++i) {
-    const int r = 4 * (4 * i + wave) + lg;
-    const int rr = row0 + min(r, nvalid - 1);            // rows past the group repeat its last row
-    const int kp = l16 ^ lds_swz(r);                     // k-order piece this slot holds
-    if (MODE == GEMM_DOWN)
-      src_off[i] = ((uint32_t)rr * L.K + h_piece(kp) * 8) * 2;   // h planes: piece (g, j) at 4j + g
-    else
+    for (int i = 0; i < TSUB; ++i) {
+      const int r = 4 * (4 * i + wave) + lg;
+      const int rr = row0 + min(r, nvalid - 1);          // rows past the group repeat its last row
+      const int kp = l16 ^ lds_swz(r);                   // k-order piece this slot holds
       src_off[i] = ((uint32_t)a.tok[rr] * L.K + kp * 8) * 2;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NPC; ++i) {
+      const int r = r0 + (MODE == GEMM_DOWN ? 16 : 32) * i;
+      const int rr = row0 + min(r, nvalid - 1);
+      if constexpr (MODE == GEMM_DOWN) {
+        phm[i] = a.hmin[rr];                             // prefill: gate_up kept the row minimum
+      } else {
+        poff[i] = (uint32_t)a.tok[rr] * (L.K / 2) + pcol * 8;   // its scale byte: poff / 8 into xs
+      }
+    }
   }
+  const int slot0 = MODE == GEMM_DOWN ? r0 * 16 + (h_piece(pcol) ^ swz0) : r0 * 16;
   auto dma = [&](int kc, int st) {
+    const char* base = (const char*)a.x + (size_t)kc * (KCHUNK * 2);
 #pragma unroll
-    for (int pl = 0; pl < PLANES; ++pl) {
-      const char* base = (const char*)(pl == 0 ? a.x : a.xlo) + (size_t)kc * (KCHUNK * 2);
+    for (int i = 0; i < TSUB; ++i) dma16(base + src_off[i], &tile[st * STAGE + (4 * i + wave) * 64]);
+  };
+  u32x4 sv[DMA ? 1 : NPC];      // staged pieces (DOWN: 8 h16; FP4: codes in .x .y)
+  uint32_t se[DMA ? 1 : NPC];   // DOWN: block exponent byte; FP4: scale byte
+  const int kp_blk = h_piece(pcol) >> 1;
+  auto stage_load = [&](int kc) {
 #pragma unroll
-      for (int i = 0; i < TSUB; ++i) dma16(base + src_off[i], &tile[st * STAGE + pl * PLANE + (4 * i + wave) * 64]);
+    for (int i = 0; i < NPC; ++i) {
+      if constexpr (MODE == GEMM_DOWN) {   // row offsets recomputed per chunk: fewer live registers
+        const uint32_t rr = row0 + min(r0 + 16 * i, nvalid - 1);
+        sv[i] = *(const u32x4*)((const char*)a.x + (size_t)kc * (KCHUNK * 2) + (rr * L.K + pcol * 8) * 2);
+        se[i] = *(const uint8_t*)((const uint8_t*)a.hexp + kc * 8 + rr * (L.K / 16) + kp_blk);
+      } else {
+        const u32x2 q = *(const u32x2*)(a.xq + (size_t)kc * 64 + poff[i]);
+        sv[i] = u32x4{q.x, q.y, 0u, 0u};
+        se[i] = a.xs[(size_t)kc * 8 + poff[i] / 8];
+      }
+    }
+  };
+  auto stage_store = [&](int st) {
+#pragma unroll
+    for (int i = 0; i < NPC; ++i) {
+      if constexpr (MODE == GEMM_DOWN) {
+        const _Float16 f = h_factor(phm[i] - (int)(int8_t)se[i]);
+        tile[st * STAGE + slot0 + 256 * i] = __builtin_bit_cast(u32x4, __builtin_bit_cast(f16x8, sv[i]) * f);
+      } else {
+        const f16x2 s1 = e4m3x2_to_f16x2(se[i]);
+        const f16x2 s2 = {s1.x, s1.x};
+        const f16x8 lo = dequant8_f16(sv[i].x, s2), hi = dequant8_f16(sv[i].y, s2);
+        const int c = 2 * pcol;
+        tile[st * STAGE + slot0 + 512 * i + (c ^ swz0)] = __builtin_bit_cast(u32x4, lo);
+        tile[st * STAGE + slot0 + 512 * i + ((c + 1) ^ swz0)] = __builtin_bit_cast(u32x4, hi);
+      }
     }
   };
 
-  // weight tiles of this wave: fp4 16 B per lane per chunk, the chunk's two block-scale
-  // bytes loaded chunk by chunk (2 B of the lane's 16-byte scale-group entry)
+  // ---- weights of this wave: fp4 16 B per lane per chunk; the chunk's two block-scale
+  // bytes come from the dword holding them (a 16-bit load would be zero-extended right
+  // after it, which makes the compiler wait for the load at once)
   const u32x4* wp[NSUB];
   const uint8_t* sp[NSUB];
 #pragma unroll
@@ -524,8 +446,6 @@ __global__ __launch_bounds__(256) void gemm_prefill_dma_kernel(GemmArgs a) {
     wp[s] = fp4_tile(a, L, g, q0 + s, 0);
     sp[s] = (const uint8_t*)sc_tile(a, L, g, q0 + s, 0);
   }
-  // (the dword holding them: a 16-bit load would be zero-extended right after it, which
-  // makes the compiler wait for the load at once)
   auto load_w = [&](int kc, u32x4 (&w)[NSUB], uint32_t (&sb)[NSUB]) {
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) {
@@ -544,26 +464,16 @@ __global__ __launch_bounds__(256) void gemm_prefill_dma_kernel(GemmArgs a) {
   uint32_t sA[NSUB], sB[NSUB];
   load_w(0, wA, sA);
   __builtin_amdgcn_sched_barrier(0);
+  if constexpr (DMA) {
 #pragma unroll
-  for (int c = 0; c < NBUF - 1; ++c) dma(min(c, L.KC - 1), c);
+    for (int c = 0; c < NBUF - 1; ++c) dma(min(c, L.KC - 1), c);
+  } else {
+    stage_load(0);
+  }
 
-  // Iteration kc: wait for chunk kc in LDS (older loads complete, the newest NBUF - 2
-  // chunks may stay in flight), barrier, issue the weights of kc + 1 and the DMA of
-  // kc + NBUF - 1 (clamped to the last chunk near the end, so every iteration issues the
-  // same loads and one wait count fits all), then consume chunk kc. The two weight
-  // register sets alternate (no copies, which would wait for the loads in flight).
-  auto step = [&](int kc, const u32x4 (&wc)[NSUB], const uint32_t (&sc)[NSUB], u32x4 (&wn)[NSUB],
-                  uint32_t (&sn)[NSUB]) {
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm(D * (NBUF - 2), 0));
-    __builtin_amdgcn_s_barrier();
-    // issue order is what the wait count above relies on: weights, then DMA, then compute
-    __builtin_amdgcn_sched_barrier(0);
-    load_w(min(kc + 1, L.KC - 1), wn, sn);
-    __builtin_amdgcn_sched_barrier(0);
-    dma(min(kc + NBUF - 1, L.KC - 1), (kc + NBUF - 1) % NBUF);
-    __builtin_amdgcn_sched_barrier(0);
-    const u32x4* T0 = &tile[(kc % NBUF) * STAGE];
-    WOps<F16> w[NSUB];
+  auto compute = [&](int kc, const u32x4 (&wc)[NSUB], const uint32_t (&sc)[NSUB]) {
+    const u32x4* T0 = &tile[(kc % NST) * STAGE];
+    WOps<true> w[NSUB];
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) w[s].make(wc[s], sc[s] >> ((kc & 1) * 16));
 #pragma unroll
@@ -576,15 +486,35 @@ __global__ __launch_bounds__(256) void gemm_prefill_dma_kernel(GemmArgs a) {
       for (int s = 0; s < NSUB; ++s)
 #pragma unroll
         for (int t = 0; t < TSUB; ++t) acc[s][t] = mfma_any(w[s].v[j], bop[t], acc[s][t]);
-      if (MODE == GEMM_DOWN) {
-#pragma unroll
-        for (int t = 0; t < TSUB; ++t) bop[t] = T0[PLANE + (t * 16 + l16) * 16 + c];
-#pragma unroll
-        for (int s = 0; s < NSUB; ++s)
-#pragma unroll
-          for (int t = 0; t < TSUB; ++t) acc[s][t] = mfma_any(w[s].v[j], bop[t], acc[s][t]);
-      }
     }
+  };
+  // DMA chunk kc: wait for chunk kc in LDS (older loads complete, the newest NBUF - 2
+  // chunks may stay in flight), barrier, issue the weights of kc + 1 and the DMA of
+  // kc + NBUF - 1 (clamped to the last chunk near the end, so every chunk issues the same
+  // loads and one wait count fits all), consume chunk kc.
+  // Register chunk kc: store the staged chunk kc (its loads were issued one chunk
+  // earlier), issue the loads of chunk kc + 1 and its weights, barrier, consume chunk kc.
+  // The two weight register sets alternate (no copies, which would wait for loads).
+  auto step = [&](int kc, const u32x4 (&wc)[NSUB], const uint32_t (&sc)[NSUB], u32x4 (&wn)[NSUB],
+                  uint32_t (&sn)[NSUB]) {
+    if constexpr (DMA) {
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(D * (NBUF - 2), 0));
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      load_w(min(kc + 1, L.KC - 1), wn, sn);
+      __builtin_amdgcn_sched_barrier(0);
+      dma(min(kc + NBUF - 1, L.KC - 1), (kc + NBUF - 1) % NBUF);
+      __builtin_amdgcn_sched_barrier(0);
+    } else {
+      stage_store(kc & 1);
+      __builtin_amdgcn_sched_barrier(0);
+      stage_load(min(kc + 1, L.KC - 1));
+      load_w(min(kc + 1, L.KC - 1), wn, sn);
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));      // this thread's LDS stores done
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    compute(kc, wc, sc);
   };
   // pairs of steps with fixed register roles (a conditional second step would make the
   // compiler copy registers that still have loads in flight); an odd count peels chunk 0
@@ -600,7 +530,7 @@ __global__ __launch_bounds__(256) void gemm_prefill_dma_kernel(GemmArgs a) {
       step(kc + 1, wB, sB, wA, sA);
     }
   }
-  __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));   // the clamped tail DMAs land before the workgroup exits
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));   // the clamped tail loads land before the workgroup exits
 
   const float wgs = a.wgs[g];
 #pragma unroll
@@ -608,12 +538,12 @@ __global__ __launch_bounds__(256) void gemm_prefill_dma_kernel(GemmArgs a) {
     const int rr = t * 16 + l16;
     if (rr >= nvalid) continue;
     const int orow = row0 + rr;
-    float scl = wgs;
-    if (F16) scl *= a.xg[a.tok[orow]];
     if (MODE == GEMM_DOWN) {
+      const float scl = __builtin_ldexpf(wgs, -a.hmin[orow]);
 #pragma unroll
       for (int s = 0; s < NSUB; ++s) epilogue_single(a, acc[s][t], scl, orow, q0 + s);
     } else {
+      const float scl = wgs * a.xg[a.tok[orow]];
 #pragma unroll
       for (int s = 0; s < NSUB; s += 2) epilogue_pair<MODE>(a, acc[s][t], acc[s + 1][t], scl, orow, (q0 + s) >> 1);
     }
@@ -632,10 +562,10 @@ static void launch_k(K kernel, dim3 grid, dim3 block, hipStream_t s, const Launc
 
 
 constexpr int PRE_NSUB_GU = 2;    // prefill gate_up: 1 gate + 1 up tile per wave (2 workgroups per CU)
-constexpr int PRE_NSUB_DN = 4;    // prefill down: 64 rows per wave (each tile meets h_hi and h_lo)
+constexpr int PRE_NSUB_DN = 2;    // prefill down: 2 tiles per wave (2 workgroups per CU)
 constexpr int PRE_TSUB = 8;       // prefill: 128 token rows per tile
-constexpr int PRE_NBUF_GU = 2;    // prefill gate_up: LDS ring depth (2 x 32 KiB; measured faster than 1 workgroup
-                                  // per CU with 4 tiles per wave and 3 stages)
+constexpr int PRE_NBUF_GU = 2;    // prefill gate_up: LDS DMA ring depth (2 x 32 KiB; measured faster than 1
+                                  // workgroup per CU with 4 tiles per wave and 3 stages)
 constexpr int DEC_MIN_WGS = 2048; // decode: 8 workgroups per CU before 4 tiles per workgroup are used
 
 // Decode split: 4 weight tiles per workgroup (twice the reuse of each token-operand load)
@@ -660,18 +590,10 @@ static void launch_mode(GemmRegime regime, int max_tiles, int est_tiles, const G
                         const LaunchEvents& ev) {
   if (regime == REGIME_DECODE_KSPLIT) {
     launch_decode<MODE>(max_tiles, est_tiles, a, s, ev);
-  } else if constexpr (MODE == GEMM_GATEUP_F16 || MODE == GEMM_DOWN) {
+  } else if constexpr (MODE != GEMM_GATEUP_BF16) {
     constexpr int NS = MODE == GEMM_DOWN ? PRE_NSUB_DN : PRE_NSUB_GU;
-    constexpr int NB = MODE == GEMM_DOWN ? 2 : PRE_NBUF_GU;
-    dim3 grid((a.N / 16 + 4 * NS - 1) / (4 * NS), (max_tiles + 7) / 8 * 8);
-    if ((a.N / 16) % (4 * NS) == 0)
-      launch_k(gemm_prefill_dma_kernel<MODE, NS, PRE_TSUB, NB>, grid, dim3(256), s, ev, a);
-    else
-      launch_k(gemm_prefill_kernel<MODE, NS, PRE_TSUB>, grid, dim3(256), s, ev, a);
-  } else if constexpr (MODE == GEMM_GATEUP_FP4) {
-    constexpr int NS = PRE_NSUB_GU;
-    dim3 grid((a.N / 16 + 4 * NS - 1) / (4 * NS), (max_tiles + 7) / 8 * 8);
-    launch_k(gemm_prefill_kernel<MODE, NS, PRE_TSUB>, grid, dim3(256), s, ev, a);
+    const dim3 grid(a.N / 16 / (4 * NS), (max_tiles + 7) / 8 * 8);
+    launch_k(gemm_prefill_kernel<MODE, NS, PRE_TSUB, PRE_NBUF_GU>, grid, dim3(256), s, ev, a);
   }
 }
 

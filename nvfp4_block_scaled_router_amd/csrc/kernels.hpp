@@ -32,6 +32,7 @@ struct PlanArgs {
   int32_t* tile_group;   // [max tiles]
   int32_t* tile_row0;    // [max tiles]
   int32_t* tile_count;   // [1]
+  int32_t* hmin;         // [T*k + S*T] per-row minimum h exponent, set to H_EXP_INIT here
   int32_t* counts_user;  // optional [E]
   int32_t* offsets_user; // optional [E+1]
   int32_t* perm_user;    // optional [T*k]
@@ -77,8 +78,7 @@ struct GemmArgs {
   // token rows
   const int32_t* tok;      // row -> token (gather modes)
   const uint16_t* x;       // activations [T][K]: fp16 rescaled (GATEUP_F16) or bf16 (GATEUP_BF16);
-                           // h_hi [rows][K] (DOWN)
-  const uint16_t* xlo;     // h_lo [rows][K] (DOWN): h = h_hi + h_lo
+                           // h16 [rows][K] (DOWN)
   const uint8_t* xq;       // [T][K/2]  (GATEUP_FP4)
   const uint8_t* xs;       // [T][K/16]
   const float* xg;         // [T] per-row activation factor applied in the gate_up epilogue
@@ -87,17 +87,26 @@ struct GemmArgs {
   const int32_t* tile_row0;
   const int32_t* tile_count;
   const int32_t* offsets;  // [G+1] row ranges of the groups
-  // output: gate_up -> h as two bf16 planes [rows][N/2] (hi = bf16(h), lo = bf16(h - hi)),
-  // columns permuted inside each 128-column chunk (see h_pos);
-  // down -> y fp32 [rows][N]
-  uint16_t* out;
-  uint16_t* out_lo;
-  float* yout;
+  // h = silu(g) u between the GEMMs, as h16 [rows][I] fp16 (columns permuted inside each
+  // 128-column chunk, see h_pos) with, per row and 16-column block b, an exponent
+  // hexp[row][b] such that h16 = fp16(h * 2^hexp) has the block's largest |h| in
+  // [2^14, 2^15). gate_up writes both; down takes the row's smallest exponent P and
+  // multiplies each block by 2^(P - hexp) so that a whole row shares the scale 2^P, undone
+  // in its epilogue. With hmin set (large batches), gate_up also folds each block exponent
+  // into hmin[row] (atomicMin) and down reads P there; without it (small batches, where a
+  // few rows would take every block's atomic) down takes the minimum over the row's hexp.
+  uint16_t* out;           // gate_up: h16
+  int8_t* hexp;            // [rows][I/16]
+  int32_t* hmin;           // [rows] or nullptr
+  float* yout;             // down: y fp32 [rows][N]
 };
 // Kernel families: decode (<= 16 rows per tile, K split across the waves of a workgroup,
 // direct token loads), N split with a 16-row LDS token tile (kept for experiments), and
 // prefill (N split, 128-row LDS token tiles).
 enum GemmRegime { REGIME_DECODE_KSPLIT = 0, REGIME_DECODE_NSPLIT = 1, REGIME_PREFILL = 2 };
+constexpr int H_EXP_INIT = 127;   // above any block exponent (start of a minimum)
+constexpr int H_EXP_MAX = 120;    // block exponents are clamped to [-H_EXP_MAX, H_EXP_MAX]
+
 // Optional timing of a single-kernel stage: when set, the kernel is launched with
 // hipExtLaunchKernelGGL, which stamps the events at the kernel's own start and end (no
 // enqueue or dispatch gap inside the measured interval).

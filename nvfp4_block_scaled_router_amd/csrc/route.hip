@@ -336,9 +336,13 @@ __global__ __launch_bounds__(1024) void plan_small_kernel(RouteArgs r, PlanArgs 
     a.perm[pos] = i;
     a.inv[i] = pos;
     a.tok[pos] = t;
+    a.hmin[pos] = H_EXP_INIT;
     if (a.perm_user) a.perm_user[pos] = i;
   }
-  for (int q = tid; q < T * (G - E); q += nthr) a.tok[rows + q] = q % T;
+  for (int q = tid; q < T * (G - E); q += nthr) {
+    a.tok[rows + q] = q % T;
+    a.hmin[rows + q] = H_EXP_INIT;
+  }
   for (int g = tid; g <= G; g += nthr) {
     a.offsets[g] = off[g];
     if (g < G) a.counts[g] = cnt[g];
@@ -442,9 +446,11 @@ __global__ __launch_bounds__(256) void plan_scatter_kernel(PlanArgs a, const int
     a.perm[pos] = i;
     a.inv[i] = pos;
     a.tok[pos] = t;
+    a.hmin[pos] = H_EXP_INIT;
     if (a.perm_user) a.perm_user[pos] = i;
   } else if (i < rows + a.T * (a.G - a.E)) {
     a.tok[i] = (i - rows) % a.T;    // shared-expert rows read token (row - rows) % T
+    a.hmin[i] = H_EXP_INIT;
   }
 }
 
