@@ -336,18 +336,21 @@ __device__ __forceinline__ void dma16(const void* src, const void* lds_dst) {
 // s_waitcnt immediate: vmcnt(vm) lgkmcnt(lgkm), expcnt not waited.
 constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8); }
 
-template <int MODE, int NSUB, int TSUB, int NBUF>
-__global__ __launch_bounds__(256, 2) void gemm_prefill_kernel(GemmArgs a) {
+template <int MODE, int NSUB, int TSUB, int NBUF, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void gemm_prefill_kernel(GemmArgs a) {
   static_assert(MODE == GEMM_GATEUP_F16 || MODE == GEMM_GATEUP_FP4 || MODE == GEMM_DOWN, "prefill modes");
+  static_assert(WAVES == 4 || WAVES == 8, "4 or 8 waves");
   constexpr bool DMA = MODE == GEMM_GATEUP_F16;
   static_assert(!DMA || NBUF == 2 || NBUF == 3, "LDS ring depth");
   constexpr int NST = DMA ? NBUF : 2;                 // LDS stages
   constexpr int M = TSUB * 16;
   constexpr int STAGE = M * 16;                       // 16-byte slots per stage
-  constexpr int D = TSUB;                             // DMA instructions per lane per chunk
-  // register staging: DOWN moves 16-byte h16 pieces (TSUB per thread), FP4 moves 16-column
-  // pieces (8 code bytes + 1 scale byte, TSUB/2 per thread, TSUB even)
-  constexpr int NPC = MODE == GEMM_DOWN ? TSUB : TSUB / 2;
+  constexpr int NT = 64 * WAVES;                      // threads
+  constexpr int D = STAGE / NT;                       // DMA instructions per lane per chunk
+  // register staging: DOWN moves 16-byte h16 pieces (D per thread), FP4 moves 16-column
+  // pieces (8 code bytes + 1 scale byte, D/2 per thread)
+  constexpr int NPC = MODE == GEMM_DOWN ? D : D / 2;
+  static_assert(D >= 2 && STAGE % NT == 0, "tile size");
   __shared__ u32x4 tile[NST * STAGE];
 
   const int ntiles = a.tile_count[0];
@@ -360,16 +363,16 @@ __global__ __launch_bounds__(256, 2) void gemm_prefill_kernel(GemmArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & (WAVE - 1);
   const int l16 = lane & 15, lg = lane >> 4;
-  const int q0 = (item.nb * 4 + wave) * NSUB;             // the launch covers N exactly
+  const int q0 = (item.nb * WAVES + wave) * NSUB;         // the launch covers N exactly
   const int nvalid = min(M, a.offsets[g + 1] - row0);
 
   // ---- token-tile staging
-  // DMA: instruction i of this wave fills slots (4i + wave) * 64 .. +63: row
-  // r = 4 (4i + wave) + lane / 16, slot column lane % 16; byte offsets from the chunk base.
-  uint32_t src_off[DMA ? TSUB : 1];
-  // registers: piece i of this thread is piece (threadIdx.x + 256 i) of the tile, in row
-  // r0 + 16 i (DOWN) or r0 + 32 i (FP4): the same r % 16 for every i, so one slot base
-  // (+ 256 i) serves all; sources as 32-bit offsets from the chunk-0 base
+  // DMA: instruction i of this wave fills slots (WAVES i + wave) * 64 .. +63: row
+  // r = 4 (WAVES i + wave) + lane / 16, slot column lane % 16; byte offsets from the chunk base.
+  uint32_t src_off[DMA ? D : 1];
+  // registers: piece i of this thread is piece (threadIdx.x + NT i) of the tile, in row
+  // r0 + (NT/16) i (DOWN) or r0 + (NT/8) i (FP4): the same r % 16 for every i, so one slot
+  // base (+ NT i or 2 NT i) serves all; sources as 32-bit offsets from the chunk-0 base
   uint32_t poff[DMA || MODE == GEMM_DOWN ? 1 : NPC];     // FP4: bytes into xq
   int phm[MODE == GEMM_DOWN ? NPC : 1];                   // DOWN: the row's common exponent P
   const int pcol = MODE == GEMM_DOWN ? (int)(threadIdx.x & 15) : (int)(threadIdx.x & 7);
@@ -378,8 +381,8 @@ __global__ __launch_bounds__(256, 2) void gemm_prefill_kernel(GemmArgs a) {
   // DOWN: stored piece pcol of a chunk holds k-piece h_piece(pcol), of h block 8 kc + kp / 2
   if constexpr (DMA) {
 #pragma unroll
-    for (int i = 0; i < TSUB; ++i) {
-      const int r = 4 * (4 * i + wave) + lg;
+    for (int i = 0; i < D; ++i) {
+      const int r = 4 * (WAVES * i + wave) + lg;
       const int rr = row0 + min(r, nvalid - 1);          // rows past the group repeat its last row
       const int kp = l16 ^ lds_swz(r);                   // k-order piece this slot holds
       src_off[i] = ((uint32_t)a.tok[rr] * L.K + kp * 8) * 2;
@@ -387,7 +390,7 @@ __global__ __launch_bounds__(256, 2) void gemm_prefill_kernel(GemmArgs a) {
   } else {
 #pragma unroll
     for (int i = 0; i < NPC; ++i) {
-      const int r = r0 + (MODE == GEMM_DOWN ? 16 : 32) * i;
+      const int r = r0 + (MODE == GEMM_DOWN ? NT / 16 : NT / 8) * i;
       const int rr = row0 + min(r, nvalid - 1);
       if constexpr (MODE == GEMM_DOWN) {
         phm[i] = a.hmin[rr];                             // prefill: gate_up kept the row minimum
@@ -400,7 +403,7 @@ __global__ __launch_bounds__(256, 2) void gemm_prefill_kernel(GemmArgs a) {
   auto dma = [&](int kc, int st) {
     const char* base = (const char*)a.x + (size_t)kc * (KCHUNK * 2);
 #pragma unroll
-    for (int i = 0; i < TSUB; ++i) dma16(base + src_off[i], &tile[st * STAGE + (4 * i + wave) * 64]);
+    for (int i = 0; i < D; ++i) dma16(base + src_off[i], &tile[st * STAGE + (WAVES * i + wave) * 64]);
   };
   u32x4 sv[DMA ? 1 : NPC];      // staged pieces (DOWN: 8 h16; FP4: codes in .x .y)
   uint32_t se[DMA ? 1 : NPC];   // DOWN: block exponent byte; FP4: scale byte
@@ -409,7 +412,7 @@ __global__ __launch_bounds__(256, 2) void gemm_prefill_kernel(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < NPC; ++i) {
       if constexpr (MODE == GEMM_DOWN) {   // row offsets recomputed per chunk: fewer live registers
-        const uint32_t rr = row0 + min(r0 + 16 * i, nvalid - 1);
+        const uint32_t rr = row0 + min(r0 + (NT / 16) * i, nvalid - 1);
         sv[i] = *(const u32x4*)((const char*)a.x + (size_t)kc * (KCHUNK * 2) + (rr * L.K + pcol * 8) * 2);
         se[i] = *(const uint8_t*)((const uint8_t*)a.hexp + kc * 8 + rr * (L.K / 16) + kp_blk);
       } else {
@@ -424,14 +427,14 @@ __global__ __launch_bounds__(256, 2) void gemm_prefill_kernel(GemmArgs a) {
     for (int i = 0; i < NPC; ++i) {
       if constexpr (MODE == GEMM_DOWN) {
         const _Float16 f = h_factor(phm[i] - (int)(int8_t)se[i]);
-        tile[st * STAGE + slot0 + 256 * i] = __builtin_bit_cast(u32x4, __builtin_bit_cast(f16x8, sv[i]) * f);
+        tile[st * STAGE + slot0 + NT * i] = __builtin_bit_cast(u32x4, __builtin_bit_cast(f16x8, sv[i]) * f);
       } else {
         const f16x2 s1 = e4m3x2_to_f16x2(se[i]);
         const f16x2 s2 = {s1.x, s1.x};
         const f16x8 lo = dequant8_f16(sv[i].x, s2), hi = dequant8_f16(sv[i].y, s2);
         const int c = 2 * pcol;
-        tile[st * STAGE + slot0 + 512 * i + (c ^ swz0)] = __builtin_bit_cast(u32x4, lo);
-        tile[st * STAGE + slot0 + 512 * i + ((c + 1) ^ swz0)] = __builtin_bit_cast(u32x4, hi);
+        tile[st * STAGE + slot0 + 2 * NT * i + (c ^ swz0)] = __builtin_bit_cast(u32x4, lo);
+        tile[st * STAGE + slot0 + 2 * NT * i + ((c + 1) ^ swz0)] = __builtin_bit_cast(u32x4, hi);
       }
     }
   };
@@ -460,9 +463,24 @@ __global__ __launch_bounds__(256, 2) void gemm_prefill_kernel(GemmArgs a) {
 #pragma unroll
     for (int t = 0; t < TSUB; ++t) acc[s][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 wA[NSUB], wB[NSUB];
+  // Weights: two raw register sets (rA/rB, chunk parity). With PIPE (NVFP4 gate_up),
+  // also two dequantised sets (WA/WB): chunk kc + 2's raw weights are fetched at the start
+  // of chunk kc and chunk kc + 1's are dequantised in the middle of chunk kc, between its
+  // MFMAs, so the VALU work of the dequant runs beside the MFMA pipe instead of ahead of
+  // it. Without PIPE, chunk kc + 1's raw weights are fetched at the start of chunk kc and
+  // chunk kc's are dequantised right before its MFMAs: down has no registers left for a
+  // second set, and the fp16 gate_up measured slower pipelined (its second workgroup on
+  // the CU already fills the MFMA pipe during the dequant).
+  constexpr bool PIPE = MODE == GEMM_GATEUP_FP4;
+  u32x4 rA[NSUB], rB[NSUB];
   uint32_t sA[NSUB], sB[NSUB];
-  load_w(0, wA, sA);
+  WOps<true> WA[NSUB], WB[PIPE ? NSUB : 1];
+  load_w(0, rA, sA);
+  if constexpr (PIPE) {
+    load_w(min(1, L.KC - 1), rB, sB);
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) WA[s].make(rA[s], sA[s]);
+  }
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (DMA) {
 #pragma unroll
@@ -471,37 +489,31 @@ __global__ __launch_bounds__(256, 2) void gemm_prefill_kernel(GemmArgs a) {
     stage_load(0);
   }
 
-  auto compute = [&](int kc, const u32x4 (&wc)[NSUB], const uint32_t (&sc)[NSUB]) {
+  auto mma = [&](int kc, int j, const WOps<true> (&W)[NSUB]) {
     const u32x4* T0 = &tile[(kc % NST) * STAGE];
-    WOps<true> w[NSUB];
+    const int c = (lg * 4 + j) ^ lds_swz(l16);
+    u32x4 bop[TSUB];
 #pragma unroll
-    for (int s = 0; s < NSUB; ++s) w[s].make(wc[s], sc[s] >> ((kc & 1) * 16));
+    for (int t = 0; t < TSUB; ++t) bop[t] = T0[(t * 16 + l16) * 16 + c];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int c = (lg * 4 + j) ^ lds_swz(l16);
-      u32x4 bop[TSUB];
+    for (int s = 0; s < NSUB; ++s)
 #pragma unroll
-      for (int t = 0; t < TSUB; ++t) bop[t] = T0[(t * 16 + l16) * 16 + c];
-#pragma unroll
-      for (int s = 0; s < NSUB; ++s)
-#pragma unroll
-        for (int t = 0; t < TSUB; ++t) acc[s][t] = mfma_any(w[s].v[j], bop[t], acc[s][t]);
-    }
+      for (int t = 0; t < TSUB; ++t) acc[s][t] = mfma_any(W[s].v[j], bop[t], acc[s][t]);
   };
   // DMA chunk kc: wait for chunk kc in LDS (older loads complete, the newest NBUF - 2
-  // chunks may stay in flight), barrier, issue the weights of kc + 1 and the DMA of
-  // kc + NBUF - 1 (clamped to the last chunk near the end, so every chunk issues the same
-  // loads and one wait count fits all), consume chunk kc.
+  // chunks may stay in flight), barrier, issue the raw weights ahead and the DMA of
+  // kc + NBUF - 1 (both clamped to the last chunk near the end, so every chunk issues the
+  // same loads and one wait count fits all), consume chunk kc.
   // Register chunk kc: store the staged chunk kc (its loads were issued one chunk
-  // earlier), issue the loads of chunk kc + 1 and its weights, barrier, consume chunk kc.
-  // The two weight register sets alternate (no copies, which would wait for loads).
-  auto step = [&](int kc, const u32x4 (&wc)[NSUB], const uint32_t (&sc)[NSUB], u32x4 (&wn)[NSUB],
-                  uint32_t (&sn)[NSUB]) {
+  // earlier), issue the loads of chunk kc + 1 and the raw weights ahead, barrier,
+  // consume chunk kc. Register roles alternate with the chunk parity (no copies, which
+  // would wait for loads in flight).
+  auto sync = [&](int kc, int kw, u32x4 (&rf)[NSUB], uint32_t (&sf)[NSUB]) {
     if constexpr (DMA) {
       __builtin_amdgcn_s_waitcnt(waitcnt_imm(D * (NBUF - 2), 0));
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
-      load_w(min(kc + 1, L.KC - 1), wn, sn);
+      load_w(min(kw, L.KC - 1), rf, sf);
       __builtin_amdgcn_sched_barrier(0);
       dma(min(kc + NBUF - 1, L.KC - 1), (kc + NBUF - 1) % NBUF);
       __builtin_amdgcn_sched_barrier(0);
@@ -509,25 +521,56 @@ __global__ __launch_bounds__(256, 2) void gemm_prefill_kernel(GemmArgs a) {
       stage_store(kc & 1);
       __builtin_amdgcn_sched_barrier(0);
       stage_load(min(kc + 1, L.KC - 1));
-      load_w(min(kc + 1, L.KC - 1), wn, sn);
+      load_w(min(kw, L.KC - 1), rf, sf);
       __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));      // this thread's LDS stores done
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
     }
-    compute(kc, wc, sc);
   };
-  // pairs of steps with fixed register roles (a conditional second step would make the
-  // compiler copy registers that still have loads in flight); an odd count peels chunk 0
-  if (L.KC & 1) {
-    step(0, wA, sA, wB, sB);
-    for (int kc = 1; kc < L.KC; kc += 2) {
-      step(kc, wB, sB, wA, sA);
-      step(kc + 1, wA, sA, wB, sB);
+  if constexpr (PIPE) {
+    auto step = [&](int kc, const WOps<true> (&Wc)[NSUB], WOps<true> (&Wn)[NSUB], const u32x4 (&rn)[NSUB],
+                    const uint32_t (&sn)[NSUB], u32x4 (&rf)[NSUB], uint32_t (&sf)[NSUB]) {
+      sync(kc, kc + 2, rf, sf);
+      mma(kc, 0, Wc);
+      mma(kc, 1, Wc);
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s) Wn[s].make(rn[s], sn[s] >> (((kc + 1) & 1) * 16));
+      mma(kc, 2, Wc);
+      mma(kc, 3, Wc);
+    };
+    // pairs of steps with fixed register roles; an odd count peels chunk 0
+    if (L.KC & 1) {
+      step(0, WA, WB, rB, sB, rA, sA);
+      for (int kc = 1; kc < L.KC; kc += 2) {
+        step(kc, WB, WA, rA, sA, rB, sB);
+        step(kc + 1, WA, WB, rB, sB, rA, sA);
+      }
+    } else {
+      for (int kc = 0; kc < L.KC; kc += 2) {
+        step(kc, WA, WB, rB, sB, rA, sA);
+        step(kc + 1, WB, WA, rA, sA, rB, sB);
+      }
     }
   } else {
-    for (int kc = 0; kc < L.KC; kc += 2) {
-      step(kc, wA, sA, wB, sB);
-      step(kc + 1, wB, sB, wA, sA);
+    auto step = [&](int kc, const u32x4 (&rc)[NSUB], const uint32_t (&sc)[NSUB], u32x4 (&rf)[NSUB],
+                    uint32_t (&sf)[NSUB]) {
+      sync(kc, kc + 1, rf, sf);
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s) WA[s].make(rc[s], sc[s] >> ((kc & 1) * 16));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) mma(kc, j, WA);
+    };
+    if (L.KC & 1) {
+      step(0, rA, sA, rB, sB);
+      for (int kc = 1; kc < L.KC; kc += 2) {
+        step(kc, rB, sB, rA, sA);
+        step(kc + 1, rA, sA, rB, sB);
+      }
+    } else {
+      for (int kc = 0; kc < L.KC; kc += 2) {
+        step(kc, rA, sA, rB, sB);
+        step(kc + 1, rB, sB, rA, sA);
+      }
     }
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));   // the clamped tail loads land before the workgroup exits
@@ -566,6 +609,9 @@ constexpr int PRE_NSUB_DN = 2;    // prefill down: 2 tiles per wave (2 workgroup
 constexpr int PRE_TSUB = 8;       // prefill: 128 token rows per tile
 constexpr int PRE_NBUF_GU = 2;    // prefill gate_up: LDS DMA ring depth (2 x 32 KiB; measured faster than 1
                                   // workgroup per CU with 4 tiles per wave and 3 stages)
+constexpr int PRE_WAVES_GU = 4;   // prefill fp16 gate_up: 4 waves, 2 workgroups per CU
+constexpr int PRE_WAVES_RS = 8;   // register-staged prefill (down, NVFP4 gate_up): 8 waves, 1 workgroup per CU
+                                  // (fewer staged pieces per thread; measured faster for down)
 constexpr int DEC_MIN_WGS = 2048; // decode: 8 workgroups per CU before 4 tiles per workgroup are used
 
 // Decode split: 4 weight tiles per workgroup (twice the reuse of each token-operand load)
@@ -592,8 +638,15 @@ static void launch_mode(GemmRegime regime, int max_tiles, int est_tiles, const G
     launch_decode<MODE>(max_tiles, est_tiles, a, s, ev);
   } else if constexpr (MODE != GEMM_GATEUP_BF16) {
     constexpr int NS = MODE == GEMM_DOWN ? PRE_NSUB_DN : PRE_NSUB_GU;
-    const dim3 grid(a.N / 16 / (4 * NS), (max_tiles + 7) / 8 * 8);
-    launch_k(gemm_prefill_kernel<MODE, NS, PRE_TSUB, PRE_NBUF_GU>, grid, dim3(256), s, ev, a);
+    constexpr int W = MODE == GEMM_GATEUP_F16 ? PRE_WAVES_GU : PRE_WAVES_RS;
+    const int ny = (max_tiles + 7) / 8 * 8;
+    if (a.N % (16 * W * NS) == 0) {
+      launch_k(gemm_prefill_kernel<MODE, NS, PRE_TSUB, PRE_NBUF_GU, W>, dim3(a.N / (16 * W * NS), ny),
+               dim3(64 * W), s, ev, a);
+    } else {   // N a multiple of 128 only: 4 waves cover it exactly
+      launch_k(gemm_prefill_kernel<MODE, NS, PRE_TSUB, PRE_NBUF_GU, 4>, dim3(a.N / (16 * 4 * NS), ny),
+               dim3(64 * 4), s, ev, a);
+    }
   }
 }
 

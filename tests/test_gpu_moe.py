@@ -43,6 +43,9 @@ SMALL = [
     synth.MoeConfig("all-experts", T=40, H=256, I=128, E=8, k=8, score="sigmoid", seed=12),
     synth.MoeConfig("shared-small", T=70, H=256, I=256, E=16, k=4, score="sigmoid", shared=1, seed=13),
     synth.MoeConfig("shared-small-w4a4", T=150, H=512, I=128, E=8, k=2, shared=1, act="nvfp4", seed=14),
+    # hidden 128 / 384: the prefill down launch cannot use its widest workgroup and narrows
+    synth.MoeConfig("prefill-h128", T=260, H=128, I=256, E=4, k=2, seed=15),
+    synth.MoeConfig("prefill-h384-w4a4", T=300, H=384, I=128, E=4, k=2, act="nvfp4", seed=16),
 ]
 
 
