@@ -333,6 +333,8 @@ __device__ __forceinline__ void dma16(const void* src, const void* lds_dst) {
                                    (void __attribute__((address_space(3)))*)lds_dst, 16, 0, 0);
 }
 
+template <int V> struct IntC { static constexpr int value = V; };
+
 // s_waitcnt immediate: vmcnt(vm) lgkmcnt(lgkm), expcnt not waited.
 constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8); }
 
@@ -457,140 +459,153 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void gemm_prefill_kernel(Gem
     }
   };
 
-  f32x4 acc[NSUB][TSUB];
-#pragma unroll
-  for (int s = 0; s < NSUB; ++s)
-#pragma unroll
-    for (int t = 0; t < TSUB; ++t) acc[s][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // Weights: two raw register sets (rA/rB, chunk parity). With PIPE (NVFP4 gate_up),
-  // also two dequantised sets (WA/WB): chunk kc + 2's raw weights are fetched at the start
-  // of chunk kc and chunk kc + 1's are dequantised in the middle of chunk kc, between its
-  // MFMAs, so the VALU work of the dequant runs beside the MFMA pipe instead of ahead of
-  // it. Without PIPE, chunk kc + 1's raw weights are fetched at the start of chunk kc and
-  // chunk kc's are dequantised right before its MFMAs: down has no registers left for a
-  // second set, and the fp16 gate_up measured slower pipelined (its second workgroup on
-  // the CU already fills the MFMA pipe during the dequant).
-  constexpr bool PIPE = MODE == GEMM_GATEUP_FP4;
-  u32x4 rA[NSUB], rB[NSUB];
-  uint32_t sA[NSUB], sB[NSUB];
-  WOps<true> WA[NSUB], WB[PIPE ? NSUB : 1];
-  load_w(0, rA, sA);
-  if constexpr (PIPE) {
-    load_w(min(1, L.KC - 1), rB, sB);
-#pragma unroll
-    for (int s = 0; s < NSUB; ++s) WA[s].make(rA[s], sA[s]);
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  if constexpr (DMA) {
-#pragma unroll
-    for (int c = 0; c < NBUF - 1; ++c) dma(min(c, L.KC - 1), c);
-  } else {
-    stage_load(0);
-  }
-
-  auto mma = [&](int kc, int j, const WOps<true> (&W)[NSUB]) {
-    const u32x4* T0 = &tile[(kc % NST) * STAGE];
-    const int c = (lg * 4 + j) ^ lds_swz(l16);
-    u32x4 bop[TSUB];
-#pragma unroll
-    for (int t = 0; t < TSUB; ++t) bop[t] = T0[(t * 16 + l16) * 16 + c];
+  // The MFMAs (and their LDS reads) cover only the 16-row slices up to the tile's last valid
+  // row, in steps of 2 slices: an expert's last tile is partly empty (about half a tile per
+  // expert on average), and the staging above still moves whole tiles so that every
+  // workgroup issues the same loads and waits.
+  static_assert(TSUB == 8, "row tiers assume 8 slices");
+  auto body = [&](auto tvc) {
+    constexpr int TV = decltype(tvc)::value;
+    f32x4 acc[NSUB][TV];
 #pragma unroll
     for (int s = 0; s < NSUB; ++s)
 #pragma unroll
-      for (int t = 0; t < TSUB; ++t) acc[s][t] = mfma_any(W[s].v[j], bop[t], acc[s][t]);
-  };
-  // DMA chunk kc: wait for chunk kc in LDS (older loads complete, the newest NBUF - 2
-  // chunks may stay in flight), barrier, issue the raw weights ahead and the DMA of
-  // kc + NBUF - 1 (both clamped to the last chunk near the end, so every chunk issues the
-  // same loads and one wait count fits all), consume chunk kc.
-  // Register chunk kc: store the staged chunk kc (its loads were issued one chunk
-  // earlier), issue the loads of chunk kc + 1 and the raw weights ahead, barrier,
-  // consume chunk kc. Register roles alternate with the chunk parity (no copies, which
-  // would wait for loads in flight).
-  auto sync = [&](int kc, int kw, u32x4 (&rf)[NSUB], uint32_t (&sf)[NSUB]) {
-    if constexpr (DMA) {
-      __builtin_amdgcn_s_waitcnt(waitcnt_imm(D * (NBUF - 2), 0));
-      __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-      load_w(min(kw, L.KC - 1), rf, sf);
-      __builtin_amdgcn_sched_barrier(0);
-      dma(min(kc + NBUF - 1, L.KC - 1), (kc + NBUF - 1) % NBUF);
-      __builtin_amdgcn_sched_barrier(0);
-    } else {
-      stage_store(kc & 1);
-      __builtin_amdgcn_sched_barrier(0);
-      stage_load(min(kc + 1, L.KC - 1));
-      load_w(min(kw, L.KC - 1), rf, sf);
-      __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));      // this thread's LDS stores done
-      __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-  if constexpr (PIPE) {
-    auto step = [&](int kc, const WOps<true> (&Wc)[NSUB], WOps<true> (&Wn)[NSUB], const u32x4 (&rn)[NSUB],
-                    const uint32_t (&sn)[NSUB], u32x4 (&rf)[NSUB], uint32_t (&sf)[NSUB]) {
-      sync(kc, kc + 2, rf, sf);
-      mma(kc, 0, Wc);
-      mma(kc, 1, Wc);
-#pragma unroll
-      for (int s = 0; s < NSUB; ++s) Wn[s].make(rn[s], sn[s] >> (((kc + 1) & 1) * 16));
-      mma(kc, 2, Wc);
-      mma(kc, 3, Wc);
-    };
-    // pairs of steps with fixed register roles; an odd count peels chunk 0
-    if (L.KC & 1) {
-      step(0, WA, WB, rB, sB, rA, sA);
-      for (int kc = 1; kc < L.KC; kc += 2) {
-        step(kc, WB, WA, rA, sA, rB, sB);
-        step(kc + 1, WA, WB, rB, sB, rA, sA);
-      }
-    } else {
-      for (int kc = 0; kc < L.KC; kc += 2) {
-        step(kc, WA, WB, rB, sB, rA, sA);
-        step(kc + 1, WB, WA, rA, sA, rB, sB);
-      }
-    }
-  } else {
-    auto step = [&](int kc, const u32x4 (&rc)[NSUB], const uint32_t (&sc)[NSUB], u32x4 (&rf)[NSUB],
-                    uint32_t (&sf)[NSUB]) {
-      sync(kc, kc + 1, rf, sf);
-#pragma unroll
-      for (int s = 0; s < NSUB; ++s) WA[s].make(rc[s], sc[s] >> ((kc & 1) * 16));
-#pragma unroll
-      for (int j = 0; j < 4; ++j) mma(kc, j, WA);
-    };
-    if (L.KC & 1) {
-      step(0, rA, sA, rB, sB);
-      for (int kc = 1; kc < L.KC; kc += 2) {
-        step(kc, rB, sB, rA, sA);
-        step(kc + 1, rA, sA, rB, sB);
-      }
-    } else {
-      for (int kc = 0; kc < L.KC; kc += 2) {
-        step(kc, rA, sA, rB, sB);
-        step(kc + 1, rB, sB, rA, sA);
-      }
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));   // the clamped tail loads land before the workgroup exits
+      for (int t = 0; t < TV; ++t) acc[s][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const float wgs = a.wgs[g];
+    // Weights: two raw register sets (rA/rB, chunk parity). With PIPE (NVFP4 gate_up),
+    // also two dequantised sets (WA/WB): chunk kc + 2's raw weights are fetched at the start
+    // of chunk kc and chunk kc + 1's are dequantised in the middle of chunk kc, between its
+    // MFMAs, so the VALU work of the dequant runs beside the MFMA pipe instead of ahead of
+    // it. Without PIPE, chunk kc + 1's raw weights are fetched at the start of chunk kc and
+    // chunk kc's are dequantised right before its MFMAs: down has no registers left for a
+    // second set, and the fp16 gate_up measured slower pipelined (its second workgroup on
+    // the CU already fills the MFMA pipe during the dequant).
+    constexpr bool PIPE = MODE == GEMM_GATEUP_FP4;
+    u32x4 rA[NSUB], rB[NSUB];
+    uint32_t sA[NSUB], sB[NSUB];
+    WOps<true> WA[NSUB], WB[PIPE ? NSUB : 1];
+    load_w(0, rA, sA);
+    if constexpr (PIPE) {
+      load_w(min(1, L.KC - 1), rB, sB);
 #pragma unroll
-  for (int t = 0; t < TSUB; ++t) {
-    const int rr = t * 16 + l16;
-    if (rr >= nvalid) continue;
-    const int orow = row0 + rr;
-    if (MODE == GEMM_DOWN) {
-      const float scl = __builtin_ldexpf(wgs, -a.hmin[orow]);
-#pragma unroll
-      for (int s = 0; s < NSUB; ++s) epilogue_single(a, acc[s][t], scl, orow, q0 + s);
-    } else {
-      const float scl = wgs * a.xg[a.tok[orow]];
-#pragma unroll
-      for (int s = 0; s < NSUB; s += 2) epilogue_pair<MODE>(a, acc[s][t], acc[s + 1][t], scl, orow, (q0 + s) >> 1);
+      for (int s = 0; s < NSUB; ++s) WA[s].make(rA[s], sA[s]);
     }
-  }
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (DMA) {
+#pragma unroll
+      for (int c = 0; c < NBUF - 1; ++c) dma(min(c, L.KC - 1), c);
+    } else {
+      stage_load(0);
+    }
+
+    auto mma = [&](int kc, int j, const WOps<true> (&W)[NSUB]) {
+      const u32x4* T0 = &tile[(kc % NST) * STAGE];
+      const int c = (lg * 4 + j) ^ lds_swz(l16);
+      u32x4 bop[TV];
+#pragma unroll
+      for (int t = 0; t < TV; ++t) bop[t] = T0[(t * 16 + l16) * 16 + c];
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s)
+#pragma unroll
+        for (int t = 0; t < TV; ++t) acc[s][t] = mfma_any(W[s].v[j], bop[t], acc[s][t]);
+    };
+    // DMA chunk kc: wait for chunk kc in LDS (older loads complete, the newest NBUF - 2
+    // chunks may stay in flight), barrier, issue the raw weights ahead and the DMA of
+    // kc + NBUF - 1 (both clamped to the last chunk near the end, so every chunk issues the
+    // same loads and one wait count fits all), consume chunk kc.
+    // Register chunk kc: store the staged chunk kc (its loads were issued one chunk
+    // earlier), issue the loads of chunk kc + 1 and the raw weights ahead, barrier,
+    // consume chunk kc. Register roles alternate with the chunk parity (no copies, which
+    // would wait for loads in flight).
+    auto sync = [&](int kc, int kw, u32x4 (&rf)[NSUB], uint32_t (&sf)[NSUB]) {
+      if constexpr (DMA) {
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(D * (NBUF - 2), 0));
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        load_w(min(kw, L.KC - 1), rf, sf);
+        __builtin_amdgcn_sched_barrier(0);
+        dma(min(kc + NBUF - 1, L.KC - 1), (kc + NBUF - 1) % NBUF);
+        __builtin_amdgcn_sched_barrier(0);
+      } else {
+        stage_store(kc & 1);
+        __builtin_amdgcn_sched_barrier(0);
+        stage_load(min(kc + 1, L.KC - 1));
+        load_w(min(kw, L.KC - 1), rf, sf);
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));      // this thread's LDS stores done
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    if constexpr (PIPE) {
+      auto step = [&](int kc, const WOps<true> (&Wc)[NSUB], WOps<true> (&Wn)[NSUB], const u32x4 (&rn)[NSUB],
+                      const uint32_t (&sn)[NSUB], u32x4 (&rf)[NSUB], uint32_t (&sf)[NSUB]) {
+        sync(kc, kc + 2, rf, sf);
+        mma(kc, 0, Wc);
+        mma(kc, 1, Wc);
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s) Wn[s].make(rn[s], sn[s] >> (((kc + 1) & 1) * 16));
+        mma(kc, 2, Wc);
+        mma(kc, 3, Wc);
+      };
+      // pairs of steps with fixed register roles; an odd count peels chunk 0
+      if (L.KC & 1) {
+        step(0, WA, WB, rB, sB, rA, sA);
+        for (int kc = 1; kc < L.KC; kc += 2) {
+          step(kc, WB, WA, rA, sA, rB, sB);
+          step(kc + 1, WA, WB, rB, sB, rA, sA);
+        }
+      } else {
+        for (int kc = 0; kc < L.KC; kc += 2) {
+          step(kc, WA, WB, rB, sB, rA, sA);
+          step(kc + 1, WB, WA, rA, sA, rB, sB);
+        }
+      }
+    } else {
+      auto step = [&](int kc, const u32x4 (&rc)[NSUB], const uint32_t (&sc)[NSUB], u32x4 (&rf)[NSUB],
+                      uint32_t (&sf)[NSUB]) {
+        sync(kc, kc + 1, rf, sf);
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s) WA[s].make(rc[s], sc[s] >> ((kc & 1) * 16));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mma(kc, j, WA);
+      };
+      if (L.KC & 1) {
+        step(0, rA, sA, rB, sB);
+        for (int kc = 1; kc < L.KC; kc += 2) {
+          step(kc, rB, sB, rA, sA);
+          step(kc + 1, rA, sA, rB, sB);
+        }
+      } else {
+        for (int kc = 0; kc < L.KC; kc += 2) {
+          step(kc, rA, sA, rB, sB);
+          step(kc + 1, rB, sB, rA, sA);
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));   // the clamped tail loads land before the workgroup exits
+
+    const float wgs = a.wgs[g];
+#pragma unroll
+    for (int t = 0; t < TV; ++t) {
+      const int rr = t * 16 + l16;
+      if (rr >= nvalid) continue;
+      const int orow = row0 + rr;
+      if (MODE == GEMM_DOWN) {
+        const float scl = __builtin_ldexpf(wgs, -a.hmin[orow]);
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s) epilogue_single(a, acc[s][t], scl, orow, q0 + s);
+      } else {
+        const float scl = wgs * a.xg[a.tok[orow]];
+#pragma unroll
+        for (int s = 0; s < NSUB; s += 2) epilogue_pair<MODE>(a, acc[s][t], acc[s + 1][t], scl, orow, (q0 + s) >> 1);
+      }
+    }
+  };
+  const int tv = (nvalid + 15) >> 4;
+  if (tv > 6) body(IntC<8>());
+  else if (tv > 4) body(IntC<6>());
+  else if (tv > 2) body(IntC<4>());
+  else body(IntC<2>());
 }
 
 // ---------------------------------------------------------------------- launch
@@ -637,15 +652,19 @@ static void launch_mode(GemmRegime regime, int max_tiles, int est_tiles, const G
   if (regime == REGIME_DECODE_KSPLIT) {
     launch_decode<MODE>(max_tiles, est_tiles, a, s, ev);
   } else if constexpr (MODE != GEMM_GATEUP_BF16) {
-    constexpr int NS = MODE == GEMM_DOWN ? PRE_NSUB_DN : PRE_NSUB_GU;
-    constexpr int W = MODE == GEMM_GATEUP_F16 ? PRE_WAVES_GU : PRE_WAVES_RS;
     const int ny = (max_tiles + 7) / 8 * 8;
-    if (a.N % (16 * W * NS) == 0) {
+    if constexpr (MODE == GEMM_DOWN) {
+      constexpr int W = PRE_WAVES_RS, NS = PRE_NSUB_DN;
+      if (a.N % (16 * W * NS) == 0)
+        launch_k(gemm_prefill_kernel<MODE, NS, PRE_TSUB, PRE_NBUF_GU, W>, dim3(a.N / (16 * W * NS), ny),
+                 dim3(64 * W), s, ev, a);
+      else   // hidden a multiple of 128 only: one 16-column tile per wave covers it exactly
+        launch_k(gemm_prefill_kernel<MODE, 1, PRE_TSUB, PRE_NBUF_GU, W>, dim3(a.N / (16 * W), ny),
+                 dim3(64 * W), s, ev, a);
+    } else {   // N = 2I, a multiple of 256: both widths cover it exactly
+      constexpr int W = MODE == GEMM_GATEUP_F16 ? PRE_WAVES_GU : PRE_WAVES_RS, NS = PRE_NSUB_GU;
       launch_k(gemm_prefill_kernel<MODE, NS, PRE_TSUB, PRE_NBUF_GU, W>, dim3(a.N / (16 * W * NS), ny),
                dim3(64 * W), s, ev, a);
-    } else {   // N a multiple of 128 only: 4 waves cover it exactly
-      launch_k(gemm_prefill_kernel<MODE, NS, PRE_TSUB, PRE_NBUF_GU, 4>, dim3(a.N / (16 * 4 * NS), ny),
-               dim3(64 * 4), s, ev, a);
     }
   }
 }
