@@ -58,9 +58,11 @@ class Oracle:
         L.orc_quantize.argtypes = [_vp, _i64, _i32, _i64, _vp, _vp, _vp]
         L.orc_route.argtypes = [_vp, _i32, _i32, _i32, _i32, _vp, _vp]
         L.orc_plan.argtypes = [_vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp]
+        L.orc_route_general.argtypes = [_vp, _i32, _i32, _i32, _i32, _vp, _i32, _i32, _i32, _f64, _vp, _vp]
         L.orc_expert_ffn.argtypes = [ctypes.POINTER(ProjSet), _i32, _i32, _i32, _vp, _vp]
-        L.orc_moe_tokens.argtypes = [ctypes.POINTER(ProjSet), ctypes.POINTER(ProjSet), _i32, _i32,
-                                     _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp]
+        L.orc_expert_ffn_clamp.argtypes = [ctypes.POINTER(ProjSet), _i32, _i32, _i32, _vp, _vp, _i32, _f64]
+        L.orc_moe_tokens_clamp.argtypes = [ctypes.POINTER(ProjSet), ctypes.POINTER(ProjSet), _i32, _i32,
+                                           _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _f64]
         L.orc_dequant_rows.argtypes = [_vp, _vp, _vp, _i64, _i32, _vp]
         L.orc_bf16_rows.argtypes = [_vp, _i64, _vp]
         self.L = L
@@ -111,6 +113,24 @@ class Oracle:
                          ids.ctypes.data, w.ctypes.data)
         return ids, w
 
+    SCORES = {"softmax": 0, "sigmoid": 1, "sqrt_softplus": 2}
+
+    def route_general(self, logits: np.ndarray, k: int, score: str = "sigmoid",
+                      bias: Optional[np.ndarray] = None, n_group: int = 1, topk_group: int = 1,
+                      renorm: bool = True, scaling: float = 1.0):
+        """Generalised router (score functions, selection-only bias, group step, routed
+        scaling): ids [T][k] int32 and FP64 weights [T][k]."""
+        logits = np.ascontiguousarray(logits, dtype=np.float32)
+        T, E = logits.shape
+        assert E % n_group == 0 and 1 <= topk_group <= n_group and topk_group * (E // n_group) >= k
+        b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+        ids = np.zeros((T, k), np.int32)
+        w = np.zeros((T, k), np.float64)
+        self.L.orc_route_general(logits.ctypes.data, T, E, k, self.SCORES[score], _ptr(b), n_group,
+                                 topk_group, int(bool(renorm)), float(scaling), ids.ctypes.data,
+                                 w.ctypes.data)
+        return ids, w
+
     def plan(self, ids: np.ndarray, E: int):
         ids = np.ascontiguousarray(ids, dtype=np.int32)
         T, k = ids.shape
@@ -142,18 +162,23 @@ class Oracle:
         ps.w2_packed, ps.w2_scales, ps.w2_gs = _ptr(W2[0]), _ptr(W2[1]), _ptr(W2[2])
         return ps
 
-    def expert_ffn(self, W1, W2, g: int, x: np.ndarray) -> np.ndarray:
-        """W1 = (packed [G][2I][H/2], scales [G][2I][H/16], gs [G]); W2 likewise [G][H][I/..]."""
+    def expert_ffn(self, W1, W2, g: int, x: np.ndarray, swiglu_limit: Optional[float] = None) -> np.ndarray:
+        """W1 = (packed [G][2I][H/2], scales [G][2I][H/16], gs [G]); W2 likewise [G][H][I/..].
+        swiglu_limit: None for the plain SwiGLU, else the clamp limit L >= 0."""
         H = W1[0].shape[-1] * 2
         I = W2[0].shape[-1] * 2
         x = np.ascontiguousarray(x, dtype=np.float64)
         y = np.zeros(H, np.float64)
         ps = self._projset(W1, W2)
-        self.L.orc_expert_ffn(ctypes.byref(ps), g, H, I, x.ctypes.data, y.ctypes.data)
+        clamp = swiglu_limit is not None
+        self.L.orc_expert_ffn_clamp(ctypes.byref(ps), g, H, I, x.ctypes.data, y.ctypes.data, int(clamp),
+                                    float(swiglu_limit) if clamp else 0.0)
         return y
 
-    def moe_tokens(self, W1, W2, WS1, WS2, tokens, x_rows, ids, w) -> np.ndarray:
-        """FP64 layer output for `tokens` (x_rows: their decoded inputs [n][H])."""
+    def moe_tokens(self, W1, W2, WS1, WS2, tokens, x_rows, ids, w,
+                   swiglu_limit: Optional[float] = None) -> np.ndarray:
+        """FP64 layer output for `tokens` (x_rows: their decoded inputs [n][H]); the clamp
+        (swiglu_limit not None) applies to the routed experts."""
         H = W1[0].shape[-1] * 2
         I = W2[0].shape[-1] * 2
         T, k = ids.shape
@@ -165,9 +190,11 @@ class Oracle:
         routed = self._projset(W1, W2)
         num_shared = 0 if WS1 is None else WS1[0].shape[0]
         shared = self._projset(WS1, WS2) if num_shared else ProjSet()
-        self.L.orc_moe_tokens(ctypes.byref(routed), ctypes.byref(shared), num_shared, H, I, k,
-                              len(tokens), tokens.ctypes.data, x_rows.ctypes.data, ids.ctypes.data,
-                              w.ctypes.data, out.ctypes.data)
+        clamp = swiglu_limit is not None
+        self.L.orc_moe_tokens_clamp(ctypes.byref(routed), ctypes.byref(shared), num_shared, H, I, k,
+                                    len(tokens), tokens.ctypes.data, x_rows.ctypes.data, ids.ctypes.data,
+                                    w.ctypes.data, out.ctypes.data, int(clamp),
+                                    float(swiglu_limit) if clamp else 0.0)
         return out
 
 

@@ -3,7 +3,8 @@
 TEST INFRASTRUCTURE (see ``oracle/__init__.py``). Composes the plain C
 functions of ``oracle.c`` in the order the method runs them:
 
-1. route the FP32 logits (top-k, renormalised weights), then count/offset/permute;
+1. route the FP32 logits (top-k, renormalised weights; or the generalised router of the
+   variant layers), then count/offset/permute;
 2. activations: bf16 decoded exactly, or (W4A4) NVFP4 row-quantised with the
    binary32 quantizer and decoded exactly;
 3. per token, the k expert SwiGLU MLPs in FP64, weighted sum, plus the shared
@@ -73,7 +74,11 @@ def forward(cfg: synth.MoeConfig, x_bf16: np.ndarray, logits: np.ndarray, W1, W2
     o = o or default()
     T = x_bf16.shape[0]
     tokens = np.arange(T, dtype=np.int32) if tokens is None else np.asarray(tokens, np.int32)
-    ids, w = o.route(logits, cfg.k, cfg.score)
+    if cfg.variant_router:
+        ids, w = o.route_general(logits, cfg.k, cfg.score, synth.router_bias(cfg), cfg.n_group,
+                                 cfg.topk_group, cfg.renorm, cfg.routed_scaling)
+    else:
+        ids, w = o.route(logits, cfg.k, cfg.score)
     counts, offsets, perm, inv = o.plan(ids, cfg.E)
     res = dict(ids=ids, w=w, counts=counts, offsets=offsets, perm=perm, inv=inv, tokens=tokens)
     if cfg.act == "nvfp4":
@@ -83,5 +88,5 @@ def forward(cfg: synth.MoeConfig, x_bf16: np.ndarray, logits: np.ndarray, W1, W2
         x_rows = o.dequant_rows(xq[tokens], xs[tokens], xg[tokens])
     else:
         x_rows = o.bf16_rows(x_bf16[tokens])
-    res["out"] = o.moe_tokens(W1, W2, WS1, WS2, tokens, x_rows, ids, w)
+    res["out"] = o.moe_tokens(W1, W2, WS1, WS2, tokens, x_rows, ids, w, cfg.swiglu_limit)
     return res

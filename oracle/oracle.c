@@ -229,6 +229,105 @@ void orc_route(const float* logits, int T, int E, int k, int score, int32_t* ids
   free(taken);
 }
 
+/* Generalised router: the score functions and selection rules the pages name
+ * beside the plain top-k of orc_route.
+ *   score s_e in FP64:
+ *     0 softmax over all E experts: exp(l_e - l_max) / sum_i exp(l_i - l_max)
+ *     1 sigmoid: 1 / (1 + exp(-l_e))
+ *     2 sqrt-softplus: sqrt(log(1 + exp(l_e))), evaluated as
+ *       sqrt(max(l,0) + log1p(exp(-|l|))) (the same number, no overflow)
+ *       ([vllm.cpp] DeepSeek-V4 bring-up log, W6 sqrtsoftplus + hash-routed
+ *       MoE: the V4 router score, distinct from V2/V3's sigmoid/softmax;
+ *       [megamoe] archived CORRECTNESS_BACKLOG §5, Dense Router);
+ *   selection key in binary32: key_e = fp32(s_e), plus bias_e (a binary32 add)
+ *     when a bias is given. The bias steers selection only; the weights come from
+ *     the unbiased scores ([vllm.cpp] DeepSeek-V4 bring-up log, W6: the correction
+ *     bias enters selection only, the weights are gathered unbiased);
+ *   group step (n_group > 1): the E experts form n_group equal groups of
+ *     consecutive ids; a group's score is the binary32 sum of its two largest keys
+ *     (its one key if the group has one expert); the topk_group groups with the
+ *     largest scores are kept (lower group id on ties) and only their experts can
+ *     be picked. The pages name this step of the DeepSeek-V3 noaux_tc router
+ *     without spelling it out ([vllm.cpp] capability table: Laguna's router is
+ *     noaux_tc minus the group step); this is DeepSeek-V3's definition;
+ *   picks: the k largest keys among the pickable experts, lower id on ties
+ *     (the total order of orc_route, on keys instead of logits);
+ *   weights: w_j = s_j / sum_i s_i over the picks (renorm) or w_j = s_j, times
+ *     `scaling` ([vllm.cpp] capability table: noaux_tc sigmoid router with
+ *     routed scaling). */
+static double orc_score(int score, double l, double lmax, double denom) {
+  if (score == 0) return exp(l - lmax) / denom;
+  if (score == 1) return 1.0 / (1.0 + exp(-l));
+  return sqrt(fmax(l, 0.0) + log1p(exp(-fabs(l))));
+}
+
+void orc_route_general(const float* logits, int T, int E, int k, int score, const float* bias,
+                       int n_group, int topk_group, int renorm, double scaling, int32_t* ids,
+                       double* w) {
+  double* s = (double*)malloc(sizeof(double) * (size_t)E);
+  float* key = (float*)malloc(sizeof(float) * (size_t)E);
+  char* pickable = (char*)malloc((size_t)E);
+  char* taken = (char*)malloc((size_t)E);
+  float* gscore = (float*)malloc(sizeof(float) * (size_t)n_group);
+  char* gkeep = (char*)malloc((size_t)n_group);
+  const int gsz = E / n_group;
+  for (int t = 0; t < T; ++t) {
+    const float* l = logits + (size_t)t * E;
+    double lmax = l[0], denom = 0.0;
+    for (int e = 1; e < E; ++e) lmax = fmax(lmax, (double)l[e]);
+    if (score == 0)
+      for (int e = 0; e < E; ++e) denom += exp((double)l[e] - lmax);
+    for (int e = 0; e < E; ++e) {
+      s[e] = orc_score(score, (double)l[e], lmax, denom);
+      key[e] = (float)s[e];
+      if (bias) key[e] = key[e] + bias[e];
+    }
+    /* group step: each group's two largest keys (lower id first on ties) */
+    for (int q = 0; q < n_group; ++q) {
+      int a = -1, b = -1;
+      for (int e = q * gsz; e < (q + 1) * gsz; ++e) {
+        if (a < 0 || key[e] > key[a]) {
+          b = a;
+          a = e;
+        } else if (b < 0 || key[e] > key[b]) {
+          b = e;
+        }
+      }
+      gscore[q] = b < 0 ? key[a] : key[a] + key[b];
+      gkeep[q] = 0;
+    }
+    for (int r = 0; r < topk_group; ++r) {
+      int best = -1;
+      for (int q = 0; q < n_group; ++q)
+        if (!gkeep[q] && (best < 0 || gscore[q] > gscore[best])) best = q;
+      gkeep[best] = 1;
+    }
+    for (int e = 0; e < E; ++e) {
+      pickable[e] = gkeep[e / gsz];
+      taken[e] = 0;
+    }
+    double sum = 0.0;
+    for (int j = 0; j < k; ++j) {
+      int best = -1;
+      for (int e = 0; e < E; ++e)
+        if (pickable[e] && !taken[e] && (best < 0 || key[e] > key[best])) best = e;
+      taken[best] = 1;
+      ids[(size_t)t * k + j] = best;
+      sum += s[best];
+    }
+    for (int j = 0; j < k; ++j) {
+      const double sj = s[ids[(size_t)t * k + j]];
+      w[(size_t)t * k + j] = (renorm ? sj / sum : sj) * scaling;
+    }
+  }
+  free(s);
+  free(key);
+  free(pickable);
+  free(taken);
+  free(gscore);
+  free(gkeep);
+}
+
 /* Per-expert counts, exclusive-scan offsets (offsets[E] = T*k), and the
  * expert-major permutation of the T*k (token, slot) pairs, tokens ascending
  * inside an expert; entries are t*k + j. inv[t*k+j] is the position of that
@@ -268,8 +367,15 @@ typedef struct {
  *   h_i = silu(g_i) * u_i = g_i / (1 + exp(-g_i)) * u_i,   y_n = sum_i W2[n][i] h_i.
  * ([megamoe] README "MoE kernel": fused SwiGLU grouped GEMM for gate/up, then
  * the down projection; [b12x] "What's in here": SiLU/SwiGLU activations.)
+ * With clamp != 0 the clamped SwiGLU with limit L >= 0:
+ *   h_i = silu(min(g_i, L)) * min(max(u_i, -L), L)
+ * (gate clamped from above only, up from both sides: [vllm.cpp] DeepSeek-V4
+ * bring-up log, W6; a limit of 0 zeroes the expert: the same log, ds4-file
+ * loadability entry; limit 10: [b12x] "DeepSeek V4 Flash 0731 MoE reproduction",
+ * [megamoe] archived CORRECTNESS_BACKLOG §6, Nvfp4MoE.)
  * Weights are decoded element by element with orc_weight. */
-void orc_expert_ffn(const orc_proj_set* P, int g, int H, int I, const double* x, double* y) {
+void orc_expert_ffn_clamp(const orc_proj_set* P, int g, int H, int I, const double* x, double* y,
+                          int clamp, double limit) {
   size_t w1_pk = (size_t)2 * I * (H / 2), w1_sc = (size_t)2 * I * (H / 16);
   size_t w2_pk = (size_t)H * (I / 2), w2_sc = (size_t)H * (I / 16);
   const uint8_t* p1 = P->w1_packed + (size_t)g * w1_pk;
@@ -283,6 +389,10 @@ void orc_expert_ffn(const orc_proj_set* P, int g, int H, int I, const double* x,
       gi += orc_weight(p1, s1, P->w1_gs[g], H, i, k) * x[k];
       ui += orc_weight(p1, s1, P->w1_gs[g], H, I + i, k) * x[k];
     }
+    if (clamp) {
+      gi = fmin(gi, limit);
+      ui = fmin(fmax(ui, -limit), limit);
+    }
     h[i] = gi / (1.0 + exp(-gi)) * ui;
   }
   for (int n = 0; n < H; ++n) {
@@ -293,16 +403,23 @@ void orc_expert_ffn(const orc_proj_set* P, int g, int H, int I, const double* x,
   free(h);
 }
 
+void orc_expert_ffn(const orc_proj_set* P, int g, int H, int I, const double* x, double* y) {
+  orc_expert_ffn_clamp(P, g, H, I, x, y, 0, 0.0);
+}
+
 /* Layer output for a list of tokens, FP64, never rounded:
  *   out[t] = sum_j w[t][j] * FFN_{ids[t][j]}(x_t)   (+ FFN_shared(x_t), weight 1)
  * ([vllm.cpp] "Device-resident decode campaign", MoeCombineKernel: the
  * weighted sum of the expert outputs with topk_weights; [megamoe] archived
  * CORRECTNESS_BACKLOG §6: an always-on shared expert beside the routed ones.)
  * x: [n_tok][H] decoded inputs of the listed tokens; ids, w: [T][k] routing;
- * out: [n_tok][H]. */
-void orc_moe_tokens(const orc_proj_set* routed, const orc_proj_set* shared, int num_shared,
-                    int H, int I, int k, int n_tok, const int32_t* tokens, const double* x,
-                    const int32_t* ids, const double* w, double* out) {
+ * out: [n_tok][H]. clamp/limit select the clamped SwiGLU for the routed experts
+ * (the pages state the limit for the routed experts and a plain SwiGLU for the
+ * shared one: [megamoe] archived CORRECTNESS_BACKLOG §6, Nvfp4MoE and
+ * Nvfp4SharedExpert). */
+void orc_moe_tokens_clamp(const orc_proj_set* routed, const orc_proj_set* shared, int num_shared,
+                          int H, int I, int k, int n_tok, const int32_t* tokens, const double* x,
+                          const int32_t* ids, const double* w, double* out, int clamp, double limit) {
 #pragma omp parallel for schedule(dynamic, 1)
   for (int i = 0; i < n_tok; ++i) {
     int t = tokens[i];
@@ -310,7 +427,7 @@ void orc_moe_tokens(const orc_proj_set* routed, const orc_proj_set* shared, int 
     double* o = out + (size_t)i * H;
     for (int n = 0; n < H; ++n) o[n] = 0.0;
     for (int j = 0; j < k; ++j) {
-      orc_expert_ffn(routed, ids[(size_t)t * k + j], H, I, x + (size_t)i * H, y);
+      orc_expert_ffn_clamp(routed, ids[(size_t)t * k + j], H, I, x + (size_t)i * H, y, clamp, limit);
       for (int n = 0; n < H; ++n) o[n] += w[(size_t)t * k + j] * y[n];
     }
     for (int s = 0; s < num_shared; ++s) {
@@ -319,6 +436,12 @@ void orc_moe_tokens(const orc_proj_set* routed, const orc_proj_set* shared, int 
     }
     free(y);
   }
+}
+
+void orc_moe_tokens(const orc_proj_set* routed, const orc_proj_set* shared, int num_shared,
+                    int H, int I, int k, int n_tok, const int32_t* tokens, const double* x,
+                    const int32_t* ids, const double* w, double* out) {
+  orc_moe_tokens_clamp(routed, shared, num_shared, H, I, k, n_tok, tokens, x, ids, w, out, 0, 0.0);
 }
 
 /* Decoded NVFP4 activations: x[i][k] = E2M1(code) * E4M3(scale) * gs[i]. */

@@ -16,6 +16,7 @@ README, "MoE kernel"). Recipe, per tensor:
 * routed down W2      : f32(N(0, 0.02)), [E][H][I]             stream 4
 * shared gate_up/down : same, 1 expert                          streams 5, 6
 * Zipf rank permutation (skewed workload)                       stream 7
+* router selection bias (variant routers)   : f32(N(0, sigma)) stream 8
 
 The generator is counter based (see ``synth.c``): element ``i`` of a stream
 depends only on (seed, stream, i).
@@ -34,6 +35,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsynth.so")
 
 STREAM_X, STREAM_LOGITS, STREAM_W1, STREAM_W2, STREAM_WS1, STREAM_WS2, STREAM_ZIPF = 1, 2, 3, 4, 5, 6, 7
+STREAM_BIAS = 8
 WEIGHT_SIGMA = 0.02
 
 _lib = None
@@ -68,11 +70,24 @@ class MoeConfig:
     I: int                  # expert intermediate size
     E: int                  # routed experts
     k: int                  # experts per token
-    score: str = "softmax"  # "softmax" | "sigmoid"  (renormalised over the k selected)
+    score: str = "softmax"  # "softmax" | "sigmoid" | "sqrt_softplus"
     shared: int = 0         # always-on shared experts (0 or 1), intermediate size I
     act: str = "bf16"       # "bf16" (W4A16) | "nvfp4" (row-quantised activations, W4A4)
     zipf_s: float = 0.0     # > 0: add -s*ln(rank_e) to every logit of expert e
     seed: int = 0
+    # router / activation variants (the defaults are the plain layer)
+    bias_sigma: float = 0.0         # > 0: a per-expert selection bias N(0, sigma) (stream 8)
+    n_group: int = 1                # group step: E in n_group groups, topk_group of them kept
+    topk_group: int = 1
+    renorm: bool = True             # weights renormalised over the k picks
+    routed_scaling: float = 1.0     # factor on the routed weights
+    swiglu_limit: Optional[float] = None   # clamped SwiGLU limit (routed experts), None = plain
+
+    @property
+    def variant_router(self) -> bool:
+        """True when the router is not the plain top-k (needs the generalised router)."""
+        return (self.score == "sqrt_softplus" or self.bias_sigma > 0 or self.n_group > 1
+                or not self.renorm or self.routed_scaling != 1.0)
 
     @property
     def rows(self) -> int:
@@ -103,6 +118,21 @@ def deepseek_v3() -> MoeConfig:
 def skewed_w4a4() -> MoeConfig:
     return MoeConfig("skewed-w4a4", T=512, H=4096, I=1536, E=64, k=4, act="nvfp4",
                      zipf_s=1.2, seed=501)
+
+
+def deepseek_v3_router(T: int = 256) -> MoeConfig:
+    """DeepSeek-V3's router on the DeepSeek-V3 layer shape: sigmoid scores, a selection
+    bias, 8 groups of 32 experts with 4 kept, routed scaling 2.5."""
+    return MoeConfig(f"deepseek-v3-noaux-t{T}", T=T, H=7168, I=2048, E=256, k=8, score="sigmoid",
+                     shared=1, seed=411, bias_sigma=0.05, n_group=8, topk_group=4, routed_scaling=2.5)
+
+
+def deepseek_v4_flash(T: int = 64) -> MoeConfig:
+    """DeepSeek-V4-Flash routed layer at one rank's share of a 2-way split of each expert's
+    intermediate width: 256 experts, top 6, hidden 4096, intermediate 1024, sqrt-softplus
+    scores with a selection bias, SwiGLU clamped at 10, one shared expert."""
+    return MoeConfig(f"deepseek-v4-flash-t{T}", T=T, H=4096, I=1024, E=256, k=6, score="sqrt_softplus",
+                     shared=1, seed=421, bias_sigma=0.5, swiglu_limit=10.0)
 
 
 def all_configs():
@@ -141,6 +171,13 @@ def zipf_bias(cfg: MoeConfig) -> Optional[np.ndarray]:
     ranks = np.empty(cfg.E, dtype=np.int32)
     lib().synth_permutation(cfg.seed, STREAM_ZIPF, cfg.E, ranks.ctypes.data)
     return np.array([-cfg.zipf_s * math.log(int(r)) for r in ranks], dtype=np.float64)
+
+
+def router_bias(cfg: MoeConfig) -> Optional[np.ndarray]:
+    """Per-expert selection bias, float32 [E] (None if bias_sigma == 0)."""
+    if cfg.bias_sigma <= 0:
+        return None
+    return normal_f32(cfg.seed, STREAM_BIAS, 0, cfg.E, cfg.bias_sigma)
 
 
 def activations(cfg: MoeConfig) -> np.ndarray:

@@ -292,6 +292,121 @@ def pin_route_sigmoid(o):
         assert abs(w[t].sum() - 1) < 1e-14
 
 
+# ------------------------------------------------ generalised router (variants)
+
+def _scores_library(l64: np.ndarray, score: str) -> np.ndarray:
+    """FP64 router scores by library routines: torch softmax / sigmoid / softplus."""
+    t = torch.from_numpy(l64)
+    if score == "softmax":
+        return torch.softmax(t, dim=-1).numpy()
+    if score == "sigmoid":
+        return torch.sigmoid(t).numpy()
+    return torch.sqrt(torch.nn.functional.softplus(t)).numpy()
+
+
+def _brute_topk(keys: np.ndarray, cand, k: int):
+    """The k-subset of `cand` every member of which beats every non-member under the order
+    (key desc, id asc), found by trying all subsets; returned in that order."""
+    import itertools
+    better = lambda a, b: (keys[a] > keys[b]) or (keys[a] == keys[b] and a < b)
+    found = [S for S in itertools.combinations(cand, k)
+             if all(better(a, b) for a in S for b in cand if b not in S)]
+    assert len(found) == 1
+    return sorted(found[0], key=lambda e: (-keys[e], e))
+
+
+def _brute_route(l: np.ndarray, k: int, score: str, bias, n_group: int, topk_group: int,
+                 renorm: bool, scaling: float):
+    T, E = l.shape
+    gsz = E // n_group
+    ids = np.zeros((T, k), np.int32)
+    w = np.zeros((T, k))
+    for t in range(T):
+        s = _scores_library(l[t].astype(np.float64), score)
+        keys = s.astype(np.float32)
+        if bias is not None:
+            keys = (keys + bias.astype(np.float32)).astype(np.float32)
+        gsc = np.zeros(n_group, np.float32)
+        for q in range(n_group):
+            top = sorted(keys[q * gsz:(q + 1) * gsz].tolist(), reverse=True)[:2]
+            gsc[q] = np.float32(top[0]) if len(top) == 1 else np.float32(top[0]) + np.float32(top[1])
+        groups = _brute_topk(gsc, list(range(n_group)), topk_group)
+        cand = [e for e in range(E) if e // gsz in groups]
+        ids[t] = _brute_topk(keys, cand, k)
+        sel = s[ids[t]]
+        w[t] = (sel / sel.sum() if renorm else sel) * scaling
+    return ids, w
+
+
+def route_general_fixture(T=24, E=16, seed=47):
+    rng = np.random.default_rng(seed)
+    l = (rng.standard_normal((T, E)) * 2).astype(np.float32)
+    bias = (rng.standard_normal(E) * 0.3).astype(np.float32)
+    return l, bias
+
+
+def pin_route_general_bruteforce(o):
+    """Every score function, with and without the selection bias and the group step, against
+    library scores and an all-subsets search; weights from the unbiased scores."""
+    l, bias = route_general_fixture()
+    cases = [("sqrt_softplus", None, 1, 1, True, 1.0), ("sqrt_softplus", bias, 1, 1, True, 1.0),
+             ("sigmoid", bias, 4, 2, True, 2.5), ("softmax", bias, 8, 3, True, 1.0),
+             ("sigmoid", None, 4, 3, False, 1.5), ("softmax", None, 2, 1, False, 1.0),
+             ("sqrt_softplus", bias, 16, 5, True, 1.0)]
+    for score, b, ng, tg, rn, sc in cases:
+        k = 3
+        ids, w = o.route_general(l, k, score, b, ng, tg, rn, sc)
+        rids, rw = _brute_route(l, k, score, b, ng, tg, rn, sc)
+        assert np.array_equal(ids, rids), (score, ng, tg)
+        assert np.allclose(w, rw, rtol=1e-12, atol=0), (score, ng, tg)
+
+
+def pin_route_general_bias_selection_only(o):
+    """The bias changes which experts are picked but never their weights: the weight of a
+    pick is its unbiased score share, the same as without the bias when the picks agree."""
+    l, bias = route_general_fixture(T=64, seed=53)
+    big = bias * 4
+    ids_b, w_b = o.route_general(l, 4, "sigmoid", big)
+    ids_n, w_n = o.route_general(l, 4, "sigmoid")
+    assert np.any(ids_b != ids_n)                      # the bias matters for selection
+    for t in range(l.shape[0]):
+        s = _scores_library(l[t].astype(np.float64), "sigmoid")[ids_b[t]]
+        assert np.allclose(w_b[t], s / s.sum(), rtol=1e-13, atol=0)
+        if np.array_equal(np.sort(ids_b[t]), np.sort(ids_n[t])):
+            order = np.argsort(ids_n[t])
+            assert np.allclose(np.sort(w_b[t]), np.sort(w_n[t]), rtol=1e-13, atol=0)
+    zero = np.zeros(l.shape[1], np.float32)
+    assert np.array_equal(o.route_general(l, 4, "sigmoid", zero)[0], ids_n)
+
+
+def pin_route_general_special_cases(o):
+    """Reductions to simpler routers: all groups kept = no group step; one expert per group
+    with k groups kept = plain top-k on the keys; the plain router's picks and weights when
+    no variant is on; weights summing to the routed scale; un-renormalised softmax weights
+    = the full softmax; equal keys -> lower ids."""
+    l, bias = route_general_fixture(T=40, seed=59)
+    E, k = l.shape[1], 4
+    for score in ("softmax", "sigmoid", "sqrt_softplus"):
+        a = o.route_general(l, k, score, bias, 4, 4)
+        b = o.route_general(l, k, score, bias, 1, 1)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+        c = o.route_general(l, k, score, bias, E, k)
+        assert np.array_equal(c[0], b[0])
+    for score in ("softmax", "sigmoid"):
+        ids_p, w_p = o.route(l, k, score)
+        ids_g, w_g = o.route_general(l, k, score)
+        assert np.array_equal(ids_p, ids_g)
+        assert np.allclose(w_p, w_g, rtol=1e-13, atol=0)
+    _, w = o.route_general(l, k, "sigmoid", bias, 2, 1, True, 2.5)
+    assert np.allclose(w.sum(axis=1), 2.5, rtol=1e-14, atol=0)
+    ids, w = o.route_general(l, k, "softmax", None, 1, 1, False, 1.0)
+    full = _scores_library(l.astype(np.float64), "softmax")
+    assert np.allclose(w, np.take_along_axis(full, ids, axis=1), rtol=1e-13, atol=0)
+    eq = np.full((3, 8), 0.5, np.float32)
+    ids, _ = o.route_general(eq, 3, "sqrt_softplus", np.zeros(8, np.float32), 4, 2)
+    assert np.all(ids == np.array([0, 1, 2]))
+
+
 def pin_plan(o):
     rng = np.random.default_rng(29)
     l = rng.standard_normal((37, 12)).astype(np.float32)
@@ -339,6 +454,61 @@ def pin_ffn_hand(o):
           np.ones(1, np.float32))
     y = o.expert_ffn(W1, W2, 0, np.ones(H))
     assert np.allclose(y, g["y"], rtol=1e-14, atol=0)
+
+
+def _hand_weights(H, I):
+    W1 = (np.full((1, 2 * I, H // 2), 0x22, np.uint8), np.full((1, 2 * I, H // 16), 0x38, np.uint8),
+          np.ones(1, np.float32))
+    W2 = (np.full((1, H, I // 2), 0x22, np.uint8), np.full((1, H, I // 16), 0x38, np.uint8),
+          np.ones(1, np.float32))
+    return W1, W2
+
+
+def pin_ffn_clamped_hand(o):
+    """The hand-worked clamped examples: both clamp sides, the unclamped side of the gate,
+    and a zero limit zeroing the expert."""
+    g = {k: float(v) for k, v in _read_golden("hand_ffn_clamped.txt")}
+    H, I, L = int(g["H"]), int(g["I"]), g["L"]
+    W1, W2 = _hand_weights(H, I)
+    y = o.expert_ffn(W1, W2, 0, np.ones(H), swiglu_limit=L)
+    assert np.allclose(y, g["y_pos"], rtol=1e-14, atol=0)
+    y = o.expert_ffn(W1, W2, 0, -np.ones(H), swiglu_limit=L)
+    assert np.allclose(y, g["y_neg"], rtol=1e-12, atol=0)
+    for x in (np.ones(H), -np.ones(H), np.linspace(-3, 3, H)):
+        assert np.all(o.expert_ffn(W1, W2, 0, x, swiglu_limit=0.0) == 0.0)
+
+
+def pin_ffn_clamped_textbook(o):
+    """Random weights: the clamped MLP equals W2 (silu(min(Wg x, L)) * clip(Wu x, -L, L)) with
+    numpy matmuls and np.minimum / np.clip, and a limit above every |g|, |u| gives the plain MLP."""
+    rng = np.random.default_rng(37)
+    H, I = 64, 32
+    W1 = random_weights(rng, 1, 2 * I, H, sigma=2.0)
+    W2 = random_weights(rng, 1, H, I)
+    D1 = decode_nvfp4(W1[0][0], W1[1][0], W1[2][0])
+    D2 = decode_nvfp4(W2[0][0], W2[1][0], W2[2][0])
+    for trial in range(4):
+        x = rng.standard_normal(H) * 3
+        gv, uv = D1[:I] @ x, D1[I:] @ x
+        L = float(np.median(np.abs(np.concatenate([gv, uv]))))     # clamps about half of them
+        ref = D2 @ (silu(np.minimum(gv, L)) * np.clip(uv, -L, L))
+        y = o.expert_ffn(W1, W2, 0, x, swiglu_limit=L)
+        assert np.allclose(y, ref, rtol=1e-12, atol=1e-14 * np.abs(ref).max())
+        big = o.expert_ffn(W1, W2, 0, x, swiglu_limit=1e300)
+        assert np.array_equal(big, o.expert_ffn(W1, W2, 0, x))
+
+
+def pin_moe_clamp_routed_only(o):
+    """The clamp reaches the routed experts and leaves the shared one plain: with a zero
+    limit the layer output is the shared expert's output alone."""
+    rng = np.random.default_rng(41)
+    W1, W2, WS1, WS2, x, l = moe_small(rng, shared=1)
+    ids, w = o.route(l, 2, "softmax")
+    T = x.shape[0]
+    toks = np.arange(T, dtype=np.int32)
+    out = o.moe_tokens(W1, W2, WS1, WS2, toks, x, ids, w, swiglu_limit=0.0)
+    ref = np.stack([o.expert_ffn(WS1, WS2, 0, x[t]) for t in range(T)])
+    assert np.array_equal(out, ref)
 
 
 def moe_small(rng, T=12, H=32, I=16, E=6, k=2, shared=0):

@@ -34,6 +34,18 @@ MUTANTS = {
     "gs_divisor": ("gs_out[g] = A / 2688.0f;", "gs_out[g] = A / 2687.0f;"),
     "block_scale_factor": ("float six_gs = 6.0f * gs;", "float six_gs = 4.0f * gs;"),
     "quant_sign_lost": ("uint32_t code = signbit(v) ? 8u : 0u;", "uint32_t code = 0u;"),
+    "score_sqrt_dropped": ("return sqrt(fmax(l, 0.0) + log1p(exp(-fabs(l))));", "return fmax(l, 0.0) + log1p(exp(-fabs(l)));"),
+    "bias_in_weights": ("sum += s[best];", "sum += key[best];\n      s[best] = key[best];"),
+    "bias_not_added": ("if (bias) key[e] = key[e] + bias[e];", "if (bias) key[e] = key[e];"),
+    "group_score_max_only": ("gscore[q] = b < 0 ? key[a] : key[a] + key[b];", "gscore[q] = key[a];"),
+    "group_tie_to_higher_id": ("if (!gkeep[q] && (best < 0 || gscore[q] > gscore[best])) best = q;",
+                               "if (!gkeep[q] && (best < 0 || gscore[q] >= gscore[best])) best = q;"),
+    "routed_scaling_dropped": ("w[(size_t)t * k + j] = (renorm ? sj / sum : sj) * scaling;",
+                               "w[(size_t)t * k + j] = (renorm ? sj / sum : sj);"),
+    "gate_clamped_both_sides": ("      gi = fmin(gi, limit);", "      gi = fmin(fmax(gi, -limit), limit);"),
+    "up_clamped_above_only": ("      ui = fmin(fmax(ui, -limit), limit);", "      ui = fmin(ui, limit);"),
+    "clamp_on_shared": ("      orc_expert_ffn(shared, s, H, I, x + (size_t)i * H, y);",
+                        "      orc_expert_ffn_clamp(shared, s, H, I, x + (size_t)i * H, y, clamp, limit);"),
     "e4m3_ties_odd": ("if (d < bestd || (d == bestd && (c & 1u) == 0 && (best & 1u) == 1)) {\n      best = c;\n      bestd = d;\n    }\n  }\n  return (uint8_t)best;\n}\n\n/* Nearest E2M1",
                       "if (d < bestd || (d == bestd && (c & 1u) == 1)) {\n      best = c;\n      bestd = d;\n    }\n  }\n  return (uint8_t)best;\n}\n\n/* Nearest E2M1"),
 }
