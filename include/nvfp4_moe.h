@@ -4,11 +4,14 @@
  *
  * The layer (all steps run as HIP kernels on the caller's stream):
  *   1. route: top-k of the FP32 router logits under (value desc, expert id asc),
- *      weights renormalised over the k picks (softmax or sigmoid scores);
+ *      weights renormalised over the k picks (softmax or sigmoid scores); or the
+ *      generalised router (sqrt-softplus scores, a selection-only bias, the group
+ *      step, routed scaling, weights without renormalisation);
  *   2. per-expert counts, exclusive-scan offsets, stable expert-major permutation;
  *   3. optional (W4A4) NVFP4 row quantisation of the activations;
  *   4. grouped gate/up GEMM over E2M1 weights with per-16 E4M3 block scales and an
- *      FP32 per-expert global scale, fused SwiGLU (silu(gate) * up) epilogue;
+ *      FP32 per-expert global scale, fused SwiGLU (silu(gate) * up, optionally
+ *      clamped) epilogue;
  *   5. grouped down GEMM;
  *   6. weighted combine of the k expert outputs (+ an always-on shared expert).
  *
@@ -49,7 +52,7 @@ extern "C" {
 
 /* Bumped on any change of a struct layout or of an entry point's contract
  * ([vllm.cpp] capability table: a versioned C ABI). */
-#define MOE_ABI_VERSION 1u
+#define MOE_ABI_VERSION 2u
 
 #define MOE_OK 0
 #define MOE_ERR_NULL (-1)      /* a required pointer is NULL */
@@ -57,14 +60,17 @@ extern "C" {
 #define MOE_ERR_SIZE (-3)      /* packed or workspace buffer too small */
 #define MOE_ERR_TOKENS (-4)    /* T < 0 or T > max_tokens */
 #define MOE_ERR_ALIGN (-5)     /* a device pointer is not 16-byte aligned */
-#define MOE_ERR_ABI (-6)       /* desc->abi_version != MOE_ABI_VERSION */
+#define MOE_ERR_ABI (-6)       /* desc->abi_version is neither 1 nor MOE_ABI_VERSION */
 #define MOE_ERR_ENUM (-7)      /* invalid enum value */
 #define MOE_ERR_WEIGHT (-8)    /* invalid weight data (host validation) */
 
 /* Router score ([b12x] "What's in here": routing scores kept in FP32;
- * [vllm.cpp] capability table: sigmoid noaux_tc routers, ungrouped). */
+ * [vllm.cpp] capability table: sigmoid noaux_tc routers; [vllm.cpp] DeepSeek-V4
+ * bring-up log, W6, and [megamoe] archived CORRECTNESS_BACKLOG §5, Dense Router:
+ * the sqrt(softplus(x)) score). */
 #define MOE_SCORE_SOFTMAX 0
 #define MOE_SCORE_SIGMOID 1
+#define MOE_SCORE_SQRT_SOFTPLUS 2   /* generalised router only */
 
 /* Gate/up activation format ([b12x] "What's in here", moe: W4A16 = BF16
  * activations with inline FP4 weight dequant; [megamoe] FINAL_STRETCH B0:
@@ -74,18 +80,50 @@ extern "C" {
 
 /* Layer descriptor. Limits: hidden and inter multiples of 128 (hidden <= 16384,
  * inter <= 16384), 1 <= top_k <= min(64, num_experts), num_experts <= 1024,
- * 1 <= max_tokens <= 65536, renormalize == 1, num_shared in {0, 1}. */
+ * 1 <= max_tokens <= 65536, num_shared in {0, 1}; renormalize in {0, 1};
+ * n_group divides num_experts, n_group <= 64, 1 <= topk_group <= n_group and
+ * topk_group * (num_experts / n_group) >= top_k; routed_scaling finite and > 0;
+ * swiglu_limit finite and >= 0 when swiglu_clamp is set.
+ * A descriptor with abi_version 1 ends after num_shared; its later fields take the
+ * values of the plain layer (1, 1, 0, 0, 1.0, 0) and it must have renormalize == 1.
+ *
+ * The plain router (score softmax or sigmoid, renormalize 1, no bias, n_group 1,
+ * routed_scaling 1) selects on the logits. Any other setting runs the generalised
+ * router, per token:
+ *   s_e   = score in FP64: softmax over all E experts, sigmoid, or
+ *           sqrt(softplus(l_e)) (MOE_SCORE_SQRT_SOFTPLUS);
+ *   key_e = fp32(s_e) [+ bias_e, a binary32 add]: the bias (moe_pack_router_bias)
+ *           steers selection only ([vllm.cpp] DeepSeek-V4 bring-up log, W6);
+ *   group step (n_group > 1): groups of num_experts / n_group consecutive experts,
+ *           a group's score the binary32 sum of its two largest keys, the topk_group
+ *           best groups kept (lower group id on ties), picks only from those (the
+ *           DeepSeek-V3 noaux_tc step the pages name: [vllm.cpp] capability table);
+ *   picks = the k largest keys, lower id on ties;
+ *   w_j   = s_j / sum of the picks' s (renormalize) or s_j, times routed_scaling
+ *           ([vllm.cpp] capability table: noaux_tc sigmoid router with routed scaling).
+ * swiglu_clamp: the routed experts use h = silu(min(g, L)) * clamp(u, -L, L),
+ * L = swiglu_limit (gate clamped from above only; L = 0 zeroes them); the shared
+ * expert keeps the plain SwiGLU ([vllm.cpp] DeepSeek-V4 bring-up log, W6 and the
+ * ds4-file loadability entry; [megamoe] archived CORRECTNESS_BACKLOG §6, Nvfp4MoE
+ * swiglu_limit 10 and Nvfp4SharedExpert). */
 typedef struct {
-  uint32_t abi_version;     /* MOE_ABI_VERSION */
+  uint32_t abi_version;     /* MOE_ABI_VERSION (or 1, see above) */
   int32_t hidden;           /* H */
   int32_t inter;            /* I, per expert (the shared expert uses the same I) */
   int32_t num_experts;      /* E routed experts */
   int32_t top_k;            /* k experts per token */
   int32_t max_tokens;       /* T_max: capacity the workspace is sized for */
   int32_t score_fn;         /* MOE_SCORE_* */
-  int32_t renormalize;      /* must be 1: weights renormalised over the k picks */
+  int32_t renormalize;      /* 1: weights renormalised over the k picks */
   int32_t act_format;       /* MOE_ACT_* */
   int32_t num_shared;       /* 0 or 1 always-on shared expert, weight 1.0 */
+  /* since ABI 2 */
+  int32_t use_bias;         /* 1: a per-expert selection bias is packed (moe_pack_router_bias) */
+  int32_t n_group;          /* group step: expert groups (1 = none) */
+  int32_t topk_group;       /* groups kept */
+  int32_t swiglu_clamp;     /* 1: clamped SwiGLU for the routed experts */
+  float routed_scaling;     /* factor on the routed weights */
+  float swiglu_limit;       /* clamp limit L */
 } moe_desc;
 
 /* Opaque plan: host memory, immutable after moe_plan, safe to share between
@@ -159,6 +197,15 @@ int moe_pack_weights(const moe_plan_t* plan, const moe_nvfp4_tensor* gate_up,
                      const moe_nvfp4_tensor* shared_down, void* packed, size_t packed_bytes,
                      void* stream);
 
+/* Copy the per-expert selection bias (device f32 [num_experts], finite values) into
+ * the plan's packed buffer; required once per packed buffer when the descriptor has
+ * use_bias = 1 (MOE_ERR_SHAPE otherwise). The bias is a layer parameter like the
+ * weights: it only steers which experts are picked ([vllm.cpp] DeepSeek-V4 bring-up
+ * log, W6; [megamoe] archived CORRECTNESS_BACKLOG §5, Dense Router e_bias). `packed`
+ * as for moe_pack_weights; `bias` must stay valid until the copy completes. */
+int moe_pack_router_bias(const moe_plan_t* plan, const float* bias, void* packed, size_t packed_bytes,
+                         void* stream);
+
 /* Run the layer on T live tokens (0 <= T <= max_tokens; T is a host int).
  *   packed        the buffer moe_pack_weights filled
  *   x             bf16 [T][H] activations (16-byte aligned)
@@ -169,9 +216,10 @@ int moe_pack_weights(const moe_plan_t* plan, const moe_nvfp4_tensor* gate_up,
  *   workspace     at least workspace_bytes, 16-byte aligned; contents on entry
  *                 are ignored, on return undefined
  * Intermediates: gate/up accumulate in FP32 and stay in registers through the
- * SwiGLU; h = silu(g*gs)*(u*gs) is kept as a pair of bf16 (hi = bf16(h),
- * lo = bf16(h - hi)) that the down GEMM consumes as two bf16 operands; expert
- * outputs stay fp32.
+ * SwiGLU; h = silu(g*gs)*(u*gs) is stored as fp16 with one power-of-two exponent
+ * per 16 columns (the block's largest |h| scaled into [2^14, 2^15)), which the
+ * down GEMM brings to a common per-row exponent exactly before its fp16 MFMAs;
+ * expert outputs stay fp32.
  * ([megamoe] README "MoE kernel": fused SwiGLU grouped GEMM epilogue in
  * registers; [b12x] "What's in here": FP32 internal, BF16 boundary;
  * [vllm.cpp] "Device-resident decode campaign": device routing ids feed the

@@ -17,8 +17,8 @@ from typing import Optional
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libnvfp4moe.so")
 
-MOE_ABI_VERSION = 1
-MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
+MOE_ABI_VERSION = 2
+MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID, MOE_SCORE_SQRT_SOFTPLUS = 0, 1, 2
 MOE_ACT_BF16, MOE_ACT_NVFP4_ROWQ = 0, 1
 MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_SIZE, MOE_ERR_TOKENS = 0, -1, -2, -3, -4
 MOE_ERR_ALIGN, MOE_ERR_ABI, MOE_ERR_ENUM, MOE_ERR_WEIGHT = -5, -6, -7, -8
@@ -27,8 +27,9 @@ MOE_STAGE_QUANT, MOE_STAGE_ROUTE, MOE_STAGE_GATE_UP, MOE_STAGE_DOWN, MOE_STAGE_C
 MOE_NUM_STAGES = 5
 STAGE_NAMES = ("quant", "route", "gate_up", "down", "combine")
 
-EXPORTED = ("moe_plan", "moe_plan_destroy", "moe_pack_weights", "moe_run", "moe_run_timed", "moe_quantize_nvfp4_rows",
-            "moe_quantize_nvfp4_weights", "moe_validate_weights_host", "moe_strerror", "moe_abi_version")
+EXPORTED = ("moe_plan", "moe_plan_destroy", "moe_pack_weights", "moe_pack_router_bias", "moe_run", "moe_run_timed",
+            "moe_quantize_nvfp4_rows", "moe_quantize_nvfp4_weights", "moe_validate_weights_host", "moe_strerror",
+            "moe_abi_version")
 
 _i32, _u32, _sz, _vp = ctypes.c_int32, ctypes.c_uint32, ctypes.c_size_t, ctypes.c_void_p
 
@@ -36,7 +37,10 @@ _i32, _u32, _sz, _vp = ctypes.c_int32, ctypes.c_uint32, ctypes.c_size_t, ctypes.
 class moe_desc(ctypes.Structure):
     _fields_ = [("abi_version", _u32), ("hidden", _i32), ("inter", _i32), ("num_experts", _i32),
                 ("top_k", _i32), ("max_tokens", _i32), ("score_fn", _i32), ("renormalize", _i32),
-                ("act_format", _i32), ("num_shared", _i32)]
+                ("act_format", _i32), ("num_shared", _i32),
+                # since ABI 2
+                ("use_bias", _i32), ("n_group", _i32), ("topk_group", _i32), ("swiglu_clamp", _i32),
+                ("routed_scaling", ctypes.c_float), ("swiglu_limit", ctypes.c_float)]
 
 
 class moe_nvfp4_tensor(ctypes.Structure):
@@ -66,6 +70,8 @@ def lib() -> ctypes.CDLL:
         T = ctypes.POINTER(moe_nvfp4_tensor)
         L.moe_pack_weights.restype = _i32
         L.moe_pack_weights.argtypes = [_vp, T, T, T, T, _vp, _sz, _vp]
+        L.moe_pack_router_bias.restype = _i32
+        L.moe_pack_router_bias.argtypes = [_vp, _vp, _vp, _sz, _vp]
         L.moe_run.restype = _i32
         L.moe_run.argtypes = [_vp, _vp, _i32, _vp, _vp, _vp, ctypes.POINTER(moe_routing_out), _vp, _sz, _vp]
         L.moe_run_timed.restype = _i32
@@ -119,14 +125,24 @@ def _stream(stream) -> Optional[int]:
 
 
 def make_desc(hidden: int, inter: int, num_experts: int, top_k: int, max_tokens: int, score: str = "softmax",
-              act: str = "bf16", num_shared: int = 0, abi_version: int = MOE_ABI_VERSION) -> moe_desc:
+              act: str = "bf16", num_shared: int = 0, abi_version: int = MOE_ABI_VERSION, *,
+              use_bias: bool = False, n_group: int = 1, topk_group: int = 1, renormalize: bool = True,
+              routed_scaling: float = 1.0, swiglu_limit: Optional[float] = None) -> moe_desc:
+    """Layer descriptor; the keyword arguments select the router and activation variants
+    (all off by default: the plain layer)."""
     d = moe_desc()
     d.abi_version = abi_version
     d.hidden, d.inter, d.num_experts, d.top_k, d.max_tokens = hidden, inter, num_experts, top_k, max_tokens
-    d.score_fn = {"softmax": MOE_SCORE_SOFTMAX, "sigmoid": MOE_SCORE_SIGMOID}.get(score, score)
-    d.renormalize = 1
+    d.score_fn = {"softmax": MOE_SCORE_SOFTMAX, "sigmoid": MOE_SCORE_SIGMOID,
+                  "sqrt_softplus": MOE_SCORE_SQRT_SOFTPLUS}.get(score, score)
+    d.renormalize = 1 if renormalize else 0
     d.act_format = {"bf16": MOE_ACT_BF16, "nvfp4": MOE_ACT_NVFP4_ROWQ}.get(act, act)
     d.num_shared = num_shared
+    d.use_bias = 1 if use_bias else 0
+    d.n_group, d.topk_group = n_group, topk_group
+    d.routed_scaling = routed_scaling
+    d.swiglu_clamp = 0 if swiglu_limit is None else 1
+    d.swiglu_limit = 0.0 if swiglu_limit is None else swiglu_limit
     return d
 
 
@@ -149,6 +165,11 @@ def nvfp4_tensor(packed, scales, global_scale) -> moe_nvfp4_tensor:
 
 def _tref(t: Optional[moe_nvfp4_tensor]):
     return None if t is None else ctypes.byref(t)
+
+
+def moe_pack_router_bias(plan, bias, packed, packed_bytes: int, stream=None) -> None:
+    """Copy the per-expert selection bias (device f32 [E]) into the packed buffer."""
+    _check(lib().moe_pack_router_bias(plan, _ptr(bias), _ptr(packed), packed_bytes, _stream(stream)))
 
 
 def moe_pack_weights(plan, gate_up: moe_nvfp4_tensor, down: moe_nvfp4_tensor,

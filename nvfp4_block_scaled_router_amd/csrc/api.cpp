@@ -5,6 +5,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <cstddef>
 #include <cstring>
 #include <new>
 
@@ -21,6 +22,7 @@ constexpr int MAX_HIDDEN = 16384;
 constexpr int MAX_EXPERTS = 1024;
 constexpr int MAX_TOPK = 64;
 constexpr int MAX_TOKENS = 65536;
+constexpr int MAX_GROUPS = 64;
 
 size_t align_up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
 
@@ -44,7 +46,7 @@ struct moe_plan {
   moe_desc d;
   int G;
   ProjLayout w1, w2;
-  size_t off_w1f, off_w1s, off_w1g, off_w2f, off_w2s, off_w2g, packed_bytes;
+  size_t off_w1f, off_w1s, off_w1g, off_w2f, off_w2s, off_w2g, off_bias, packed_bytes;
   size_t ws_ids, ws_w, ws_counts, ws_offsets, ws_perm, ws_inv, ws_tok, ws_tgrp, ws_trow, ws_tcnt, ws_plan;
   size_t ws_xq, ws_xs, ws_xg, ws_x16, ws_h, ws_hexp, ws_hmin, ws_y, ws_bytes;
   int max_tiles;
@@ -71,30 +73,61 @@ const char* moe_strerror(int code) {
   return "unknown error";
 }
 
-static int check_desc(const moe_desc* d) {
-  if (!d) return MOE_ERR_NULL;
-  if (d->abi_version != MOE_ABI_VERSION) return MOE_ERR_ABI;
-  if (d->score_fn != MOE_SCORE_SOFTMAX && d->score_fn != MOE_SCORE_SIGMOID) return MOE_ERR_ENUM;
+// Bring a version-1 or current descriptor to the current layout (a version-1 one ends
+// after num_shared; the later fields get the plain layer's values) and validate it.
+static int load_desc(const moe_desc* in, moe_desc* out) {
+  if (!in) return MOE_ERR_NULL;
+  if (in->abi_version == 1u) {
+    std::memset(out, 0, sizeof(*out));
+    std::memcpy(out, in, offsetof(moe_desc, use_bias));
+    out->n_group = 1;
+    out->topk_group = 1;
+    out->routed_scaling = 1.0f;
+    if (in->renormalize != 1) return MOE_ERR_SHAPE;
+  } else if (in->abi_version == MOE_ABI_VERSION) {
+    *out = *in;
+  } else {
+    return MOE_ERR_ABI;
+  }
+  const moe_desc* d = out;
+  if (d->score_fn != MOE_SCORE_SOFTMAX && d->score_fn != MOE_SCORE_SIGMOID && d->score_fn != MOE_SCORE_SQRT_SOFTPLUS)
+    return MOE_ERR_ENUM;
   if (d->act_format != MOE_ACT_BF16 && d->act_format != MOE_ACT_NVFP4_ROWQ) return MOE_ERR_ENUM;
   if (d->hidden < 128 || d->hidden > MAX_HIDDEN || d->hidden % 128) return MOE_ERR_SHAPE;
   if (d->inter < 128 || d->inter > MAX_HIDDEN || d->inter % 128) return MOE_ERR_SHAPE;
   if (d->num_experts < 1 || d->num_experts > MAX_EXPERTS) return MOE_ERR_SHAPE;
   if (d->top_k < 1 || d->top_k > MAX_TOPK || d->top_k > d->num_experts) return MOE_ERR_SHAPE;
   if (d->max_tokens < 1 || d->max_tokens > MAX_TOKENS) return MOE_ERR_SHAPE;
-  if (d->renormalize != 1) return MOE_ERR_SHAPE;
+  if (d->renormalize != 0 && d->renormalize != 1) return MOE_ERR_SHAPE;
   if (d->num_shared < 0 || d->num_shared > 1) return MOE_ERR_SHAPE;
+  if (d->use_bias != 0 && d->use_bias != 1) return MOE_ERR_ENUM;
+  if (d->swiglu_clamp != 0 && d->swiglu_clamp != 1) return MOE_ERR_ENUM;
+  if (d->n_group < 1 || d->n_group > MAX_GROUPS || d->num_experts % d->n_group) return MOE_ERR_SHAPE;
+  if (d->topk_group < 1 || d->topk_group > d->n_group) return MOE_ERR_SHAPE;
+  if ((long)d->topk_group * (d->num_experts / d->n_group) < d->top_k) return MOE_ERR_SHAPE;
+  if (!std::isfinite(d->routed_scaling) || d->routed_scaling <= 0.0f) return MOE_ERR_SHAPE;
+  if (d->swiglu_clamp && (!std::isfinite(d->swiglu_limit) || d->swiglu_limit < 0.0f)) return MOE_ERR_SHAPE;
   return MOE_OK;
+}
+
+// The generalised router runs for anything but the plain top-k with renormalised
+// softmax / sigmoid weights.
+static bool general_router(const moe_desc& d) {
+  return d.score_fn == MOE_SCORE_SQRT_SOFTPLUS || d.use_bias || d.n_group > 1 || d.renormalize == 0 ||
+         d.routed_scaling != 1.0f;
 }
 
 int moe_plan(const moe_desc* desc, moe_plan_t** plan, size_t* packed_bytes, size_t* workspace_bytes) {
   if (!plan) return MOE_ERR_NULL;
   *plan = nullptr;
-  const int rc = check_desc(desc);
+  moe_desc dd;
+  const int rc = load_desc(desc, &dd);
   if (rc) return rc;
   struct moe_plan* p = new (std::nothrow) struct moe_plan;
   if (!p) return MOE_ERR_SIZE;
   std::memset(p, 0, sizeof(*p));
-  p->d = *desc;
+  p->d = dd;
+  desc = &p->d;
   const int H = desc->hidden, I = desc->inter, E = desc->num_experts, k = desc->top_k;
   const int S = desc->num_shared, Tm = desc->max_tokens;
   p->G = E + S;
@@ -107,6 +140,7 @@ int moe_plan(const moe_desc* desc, moe_plan_t** plan, size_t* packed_bytes, size
   p->off_w2f = o; o = align_up(o + p->w2.fp4_expert * p->G);
   p->off_w2s = o; o = align_up(o + p->w2.sc_expert * p->G);
   p->off_w2g = o; o = align_up(o + sizeof(float) * p->G);
+  p->off_bias = o; o = align_up(o + (desc->use_bias ? sizeof(float) * E : 0));
   p->packed_bytes = o;
 
   const size_t routed = (size_t)Tm * k, rows = routed + (size_t)S * Tm;
@@ -184,6 +218,17 @@ int moe_pack_weights(const moe_plan_t* plan, const moe_nvfp4_tensor* gate_up, co
     }
   }
   return MOE_OK;
+}
+
+int moe_pack_router_bias(const moe_plan_t* plan, const float* bias, void* packed, size_t packed_bytes,
+                         void* stream) {
+  if (!plan || !bias || !packed) return MOE_ERR_NULL;
+  if (!plan->d.use_bias) return MOE_ERR_SHAPE;
+  if (!aligned16(packed) || !aligned4(bias)) return MOE_ERR_ALIGN;
+  if (packed_bytes < plan->packed_bytes) return MOE_ERR_SIZE;
+  const hipError_t e = hipMemcpyAsync((uint8_t*)packed + plan->off_bias, bias, sizeof(float) * plan->d.num_experts,
+                                      hipMemcpyDeviceToDevice, (hipStream_t)stream);
+  return e == hipSuccess ? MOE_OK : (int)e;
 }
 
 static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const uint16_t* x,
@@ -274,6 +319,12 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
   ra.w = (float*)(ws + plan->ws_w);
   ra.ids_user = r.topk_ids;
   ra.w_user = r.topk_weights;
+  ra.general = general_router(d) ? 1 : 0;
+  ra.bias = d.use_bias ? (const float*)(pk + plan->off_bias) : nullptr;
+  ra.n_group = d.n_group;
+  ra.topk_group = d.topk_group;
+  ra.renorm = d.renormalize;
+  ra.scaling = d.routed_scaling;
   PlanArgs pa;
   pa.ids = ra.ids;
   pa.T = T;
@@ -319,6 +370,8 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
   g1.out = (uint16_t*)(ws + plan->ws_h);
   g1.hexp = (int8_t*)(ws + plan->ws_hexp);
   g1.hmin = decode ? nullptr : pa.hmin;
+  g1.clamp_groups = d.swiglu_clamp ? E : 0;      // routed experts only
+  g1.swiglu_limit = d.swiglu_limit;
   e = launch_gemm(gu_mode, regime, max_tiles, est_tiles, g1, s, stage_events(ev, MOE_STAGE_GATE_UP));
   if (e != hipSuccess) return (int)e;
 
@@ -364,9 +417,11 @@ int moe_quantize_nvfp4_weights(const float* w, int32_t groups, int32_t rows_per_
                                       (hipStream_t)stream);
 }
 
-int moe_validate_weights_host(const moe_desc* desc, const moe_nvfp4_tensor* t, int32_t which) {
-  const int rc = check_desc(desc);
+int moe_validate_weights_host(const moe_desc* in, const moe_nvfp4_tensor* t, int32_t which) {
+  moe_desc dd;
+  const int rc = load_desc(in, &dd);
   if (rc) return rc;
+  const moe_desc* desc = &dd;
   if (!t || !t->packed || !t->scales || !t->global_scale) return MOE_ERR_NULL;
   if (which < 0 || which > 3) return MOE_ERR_ENUM;
   const int G = which >= 2 ? desc->num_shared : desc->num_experts;

@@ -105,19 +105,23 @@ __device__ __forceinline__ const u32x4* sc_tile(const GemmArgs& a, const ProjLay
   return (const u32x4*)(a.wsc + tile * (WAVE * 16)) + (threadIdx.x & (WAVE - 1));
 }
 
-// Epilogue for one 16-feature x 16-token D tile pair (gate, up) of gate_up: h = silu(g) u
-// for the 16 h columns hs*16 .. +15 of token row `row` (lane: 4 of them), stored as fp16
+// Epilogue for one 16-feature x 16-token D tile pair (gate, up) of gate_up: h = silu(g) u,
+// or with a finite limit L the clamped silu(min(g, L)) min(max(u, -L), L) (L = +inf leaves
+// g and u as they are), for the 16 h columns hs*16 .. +15 of token row `row` (lane: 4 of
+// them), stored as fp16
 // scaled by 2^e with e chosen on the block's largest |h| (the 4 lanes of the row share it
 // through two lane swaps) and recorded in hexp. All 4 lanes of a row must be active
 // together (they are: they hold the same token).
 template <int MODE>
 __device__ __forceinline__ void epilogue_pair(const GemmArgs& a, const f32x4& gacc, const f32x4& uacc, float sc,
-                                              int row, int hs) {
+                                              int row, int hs, float lim) {
   const int lg = (threadIdx.x & (WAVE - 1)) >> 4;
   const int NO = a.N / 2;
   const size_t off = (size_t)row * NO + h_pos(hs * 16 + 4 * lg);   // 4 columns stay contiguous
-  const float h[4] = {silu_mul(gacc.x * sc, uacc.x * sc), silu_mul(gacc.y * sc, uacc.y * sc),
-                      silu_mul(gacc.z * sc, uacc.z * sc), silu_mul(gacc.w * sc, uacc.w * sc)};
+  auto act = [&](float g, float u) {
+    return silu_mul(fminf(g * sc, lim), fminf(fmaxf(u * sc, -lim), lim));
+  };
+  const float h[4] = {act(gacc.x, uacc.x), act(gacc.y, uacc.y), act(gacc.z, uacc.z), act(gacc.w, uacc.w)};
   float mx = fmaxf(fmaxf(fabsf(h[0]), fabsf(h[1])), fmaxf(fabsf(h[2]), fabsf(h[3])));
   mx = fmaxf(mx, __shfl_xor(mx, 16));
   mx = fmaxf(mx, __shfl_xor(mx, 32));
@@ -271,13 +275,14 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs a) {
     }
   } else {
     // gate (even tile) and up (odd tile) of the same columns are finished together
+    const float lim = g < a.clamp_groups ? a.swiglu_limit : INFINITY;
     for (int s = 2 * wave; s < NSUB; s += 2 * NW) {
       f32x4 gsum = red[0][s][lane], usum = red[0][s + 1][lane];
       for (int w = 1; w < NW; ++w) {
         gsum += red[w][s][lane];
         usum += red[w][s + 1][lane];
       }
-      epilogue_pair<MODE>(a, gsum, usum, sc, orow, (q0 + s) >> 1);
+      epilogue_pair<MODE>(a, gsum, usum, sc, orow, (q0 + s) >> 1, lim);
     }
   }
 }
@@ -596,8 +601,10 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void gemm_prefill_kernel(Gem
         for (int s = 0; s < NSUB; ++s) epilogue_single(a, acc[s][t], scl, orow, q0 + s);
       } else {
         const float scl = wgs * a.xg[a.tok[orow]];
+        const float lim = g < a.clamp_groups ? a.swiglu_limit : INFINITY;
 #pragma unroll
-        for (int s = 0; s < NSUB; s += 2) epilogue_pair<MODE>(a, acc[s][t], acc[s + 1][t], scl, orow, (q0 + s) >> 1);
+        for (int s = 0; s < NSUB; s += 2)
+          epilogue_pair<MODE>(a, acc[s][t], acc[s + 1][t], scl, orow, (q0 + s) >> 1, lim);
       }
     }
   };

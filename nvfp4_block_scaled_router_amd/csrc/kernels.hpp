@@ -18,6 +18,12 @@ struct RouteArgs {
   float* w;              // [T][k] workspace
   int32_t* ids_user;     // optional copies for the caller
   float* w_user;
+  // generalised router (general != 0): FP64 scores, binary32 keys with an optional
+  // selection-only bias, the group step, weights optionally renormalised and scaled
+  int general;
+  const float* bias;     // [E] or nullptr
+  int n_group, topk_group, renorm;
+  float scaling;
 };
 
 struct PlanArgs {
@@ -99,6 +105,9 @@ struct GemmArgs {
   int8_t* hexp;            // [rows][I/16]
   int32_t* hmin;           // [rows] or nullptr
   float* yout;             // down: y fp32 [rows][N]
+  // clamped SwiGLU for groups g < clamp_groups (0: none): silu(min(g, L)) * clamp(u, -L, L)
+  int clamp_groups;
+  float swiglu_limit;
 };
 // Kernel families: decode (<= 16 rows per tile, K split across the waves of a workgroup,
 // direct token loads), N split with a 16-row LDS token tile (kept for experiments), and

@@ -287,6 +287,173 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
   route_token<EPL>(a.logits, a.E, a.k, a.score, a.ids, a.w, a.ids_user, a.w_user, t);
 }
 
+// ------------------------------------------------------------------------------
+// Generalised router, one wave per token (lane l holds experts l, l+64, ...):
+//   s_e   FP64 score: softmax over all E (max logit, then the wave's fixed-order FP64
+//         sum of exp), sigmoid, or sqrt(softplus(l)) computed as
+//         sqrt(max(l, 0) + log1p(exp(-|l|)));
+//   key_e binary32: fp32(s_e), plus the bias (a binary32 add) when one is packed;
+//   group step: for each group its best and second-best key (two wave argmaxes),
+//         the binary32 sum as the group score held by lane q, then topk_group wave
+//         argmaxes over the lanes (lower group id on ties); experts of dropped groups
+//         get the empty key 0;
+//   picks: k wave argmaxes over (key, lower id) as in route_token;
+//   w_j   = s_j / (FP64 wave sum of the picks' s) or s_j, times the routed scale.
+// The pages name these variants: sqrt-softplus scores with a selection-only bias
+// ([vllm.cpp] DeepSeek-V4 bring-up log, W6; [megamoe] archived CORRECTNESS_BACKLOG §5,
+// Dense Router), the noaux_tc group step and routed scaling ([vllm.cpp] capability
+// table: GLM-4.7-Flash and Laguna rows).
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int m = 1; m < WAVE; m <<= 1) v += __shfl_xor(v, m);   // same pairs in every lane
+  return v;
+}
+
+__device__ __forceinline__ float wave_max_f32(float v) {
+#pragma unroll
+  for (int m = 1; m < WAVE; m <<= 1) v = fmaxf(v, __shfl_xor(v, m));
+  return v;
+}
+
+template <int EPL>
+__device__ __forceinline__ void route_token_general(const RouteArgs& r, int t, int32_t* s_ids) {
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int E = r.E, k = r.k;
+  const float* lg = r.logits + (size_t)t * E;
+  float lv[EPL];
+  float lmax = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane + WAVE * i;
+    lv[i] = e < E ? lg[e] : 0.0f;
+    if (e < E) lmax = fmaxf(lmax, lv[i]);
+  }
+  double denom = 1.0;
+  if (r.score == 0) {
+    lmax = wave_max_f32(lmax);
+    double d = 0.0;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+      if (lane + WAVE * i < E) d += exp((double)lv[i] - (double)lmax);
+    denom = wave_sum_f64(d);
+  }
+  double sc[EPL];
+  uint32_t key[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane + WAVE * i;
+    sc[i] = 0.0;
+    key[i] = 0u;
+    if (e < E) {
+      const double l = (double)lv[i];
+      double v;
+      if (r.score == 0) v = exp(l - (double)lmax) / denom;
+      else if (r.score == 1) v = 1.0 / (1.0 + exp(-l));
+      else v = sqrt(fmax(l, 0.0) + log1p(exp(-fabs(l))));
+      sc[i] = v;
+      float kf = (float)v;
+      if (r.bias) kf = kf + r.bias[e];
+      key[i] = order_key(kf);
+    }
+  }
+  if (r.n_group > 1) {
+    const int gsz = E / r.n_group;
+    float gscore = 0.0f;                                  // lane q: score of group q
+    for (int q = 0; q < r.n_group; ++q) {
+      uint64_t b1 = 0ull, b2 = 0ull;                      // this lane's two best keys in group q
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) {
+        const int e = lane + WAVE * i;
+        if (e < E && e / gsz == q) {
+          const uint64_t pk = pick_key(key[i], e);
+          if (pk > b1) {
+            b2 = b1;
+            b1 = pk;
+          } else if (pk > b2) {
+            b2 = pk;
+          }
+        }
+      }
+      uint32_t h1 = (uint32_t)(b1 >> 32), l1 = (uint32_t)b1;
+      wave_max64(h1, l1);
+      const uint64_t w1 = ((uint64_t)h1 << 32) | l1;
+      const uint64_t c = b1 == w1 ? b2 : b1;              // the winner's lane offers its second
+      uint32_t h2 = (uint32_t)(c >> 32), l2 = (uint32_t)c;
+      wave_max64(h2, l2);
+      const float g = h2 == 0u ? key_value(h1) : key_value(h1) + key_value(h2);
+      if (lane == q) gscore = g;
+    }
+    uint64_t kept = 0ull;
+    uint32_t gk = lane < r.n_group ? order_key(gscore) : 0u;
+    for (int j = 0; j < r.topk_group; ++j) {
+      uint32_t h = gk, l = gk ? ~(uint32_t)lane : 0u;
+      wave_max64(h, l);
+      const int q = (int)~l;
+      kept |= 1ull << q;
+      if (lane == q) gk = 0u;
+    }
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const int e = lane + WAVE * i;
+      if (e < E && !((kept >> (e / gsz)) & 1ull)) key[i] = 0u;
+    }
+  }
+  // k picks: each lane keeps its best untaken candidate, only the owner rescans
+  uint32_t taken = 0;
+  auto local_best = [&](uint32_t& bh, uint32_t& bl) {
+    bh = 0u;
+    bl = 0u;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const int e = lane + WAVE * i;
+      const uint32_t l = ~(uint32_t)e;
+      if (key[i] != 0u && !((taken >> i) & 1u) && (key[i] > bh || (key[i] == bh && l > bl))) {
+        bh = key[i];
+        bl = l;
+      }
+    }
+  };
+  uint32_t ch, cl;
+  local_best(ch, cl);
+  double my_s = 0.0;
+  int my_id = 0;
+  for (int j = 0; j < k; ++j) {
+    uint32_t wh = ch, wl = cl;
+    wave_max64(wh, wl);
+    const int e = (int)~wl;
+    const int owner = e & (WAVE - 1), slot = e / WAVE;
+    double se = 0.0;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+      if (i == slot) se = sc[i];
+    se = __shfl(se, owner);
+    if (lane == owner) {
+      taken |= 1u << slot;
+      local_best(ch, cl);
+    }
+    if (lane == j) {
+      my_id = e;
+      my_s = se;
+    }
+  }
+  const double sum = wave_sum_f64(lane < k ? my_s : 0.0);
+  if (lane < k) {
+    const float wj = (float)((r.renorm ? my_s / sum : my_s) * (double)r.scaling);
+    r.ids[(size_t)t * k + lane] = my_id;
+    r.w[(size_t)t * k + lane] = wj;
+    if (r.ids_user) r.ids_user[(size_t)t * k + lane] = my_id;
+    if (r.w_user) r.w_user[(size_t)t * k + lane] = wj;
+    if (s_ids) s_ids[t * k + lane] = my_id;
+  }
+}
+
+template <int EPL>
+__global__ __launch_bounds__(256) void route_general_kernel(RouteArgs a) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= a.T) return;   // whole waves leave together
+  route_token_general<EPL>(a, t, nullptr);
+}
+
 // Small batches (T <= 64, T*k <= 4096): routing, counts, offsets, permutation and tile
 // list in one 1024-thread workgroup, everything in LDS. 64 DPP rows route up to 64 tokens
 // at once (E <= 256; wider expert sets use one wave per token); one wave runs the two
@@ -306,7 +473,9 @@ __global__ __launch_bounds__(1024) void plan_small_kernel(RouteArgs r, PlanArgs 
 
   for (int g = tid; g < G; g += nthr) cnt[g] = g < E ? 0 : T;
   for (int i = tid; i < 2 * E; i += nthr) bits[i] = 0u;
-  if constexpr (EPL <= 4) {  // E <= 256: row-level routing, one token per 16-lane row
+  if (r.general) {           // the generalised router ran before: its picks are in r.ids
+    for (int i = tid; i < rows; i += nthr) s_ids[i] = r.ids[i];
+  } else if constexpr (EPL <= 4) {  // E <= 256: row-level routing, one token per 16-lane row
     const int t = tid >> 4;
     if (t < T) route_token_row<EPL * 4>(r.logits, E, k, r.score, t, r.ids, r.w, r.ids_user, r.w_user, s_ids);
   } else {
@@ -467,15 +636,18 @@ bool plan_small_ok(int T, int k) { return T <= 64 && T * k <= 4096; }
 
 template <int EPL>
 static hipError_t launch_route_plan_t(const RouteArgs& r, const PlanArgs& p, int32_t* scratch, hipStream_t s) {
+  if (r.general) hipLaunchKernelGGL(route_general_kernel<EPL>, dim3((r.T + 3) / 4), dim3(256), 0, s, r);
   if (plan_small_ok(p.T, p.k)) {
     hipLaunchKernelGGL(plan_small_kernel<EPL>, dim3(1), dim3(1024), plan_small_lds_bytes(p.T * p.k, p.E, p.G), s,
                        r, p);
     return hipGetLastError();
   }
-  if constexpr (EPL <= 4)
+  if (r.general) {
+  } else if constexpr (EPL <= 4) {
     hipLaunchKernelGGL(route_row_kernel<EPL * 4>, dim3((r.T + 15) / 16), dim3(256), 0, s, r);
-  else
+  } else {
     hipLaunchKernelGGL(route_kernel<EPL>, dim3((r.T + 3) / 4), dim3(256), 0, s, r);
+  }
   const int nb = (p.T + PLAN_BLOCK - 1) / PLAN_BLOCK;
   int32_t* local_rank = scratch;
   int32_t* block_counts = scratch + (size_t)p.T * p.k;

@@ -6,7 +6,7 @@ from typing import Optional, Sequence
 
 import torch
 
-from . import (make_desc, moe_pack_weights, moe_plan, moe_plan_destroy, moe_run, nvfp4_tensor,
+from . import (make_desc, moe_pack_router_bias, moe_pack_weights, moe_plan, moe_plan_destroy, moe_run, nvfp4_tensor,
                routing_out)
 
 
@@ -18,8 +18,8 @@ class MoeLayer:
     (gate_up: N = 2I, rows 0..I-1 gate; down: N = H)."""
 
     def __init__(self, hidden: int, inter: int, num_experts: int, top_k: int, max_tokens: int,
-                 score: str = "softmax", act: str = "bf16", num_shared: int = 0, device="cuda"):
-        self.desc = make_desc(hidden, inter, num_experts, top_k, max_tokens, score, act, num_shared)
+                 score: str = "softmax", act: str = "bf16", num_shared: int = 0, device="cuda", **variants):
+        self.desc = make_desc(hidden, inter, num_experts, top_k, max_tokens, score, act, num_shared, **variants)
         self.plan, self.packed_bytes, self.workspace_bytes = moe_plan(self.desc)
         self.device = torch.device(device)
         self.packed = torch.empty(self.packed_bytes, dtype=torch.uint8, device=self.device)
@@ -29,7 +29,13 @@ class MoeLayer:
 
     @classmethod
     def from_config(cls, cfg, max_tokens: Optional[int] = None, device="cuda") -> "MoeLayer":
-        return cls(cfg.H, cfg.I, cfg.E, cfg.k, max_tokens or cfg.T, cfg.score, cfg.act, cfg.shared, device)
+        return cls(cfg.H, cfg.I, cfg.E, cfg.k, max_tokens or cfg.T, cfg.score, cfg.act, cfg.shared, device,
+                   use_bias=cfg.bias_sigma > 0, n_group=cfg.n_group, topk_group=cfg.topk_group,
+                   renormalize=cfg.renorm, routed_scaling=cfg.routed_scaling, swiglu_limit=cfg.swiglu_limit)
+
+    def pack_router_bias(self, bias: torch.Tensor, stream=None) -> None:
+        """The per-expert selection bias (device f32 [E]) of a layer declared with use_bias."""
+        moe_pack_router_bias(self.plan, bias, self.packed, self.packed_bytes, stream)
 
     def pack(self, w1: Sequence[torch.Tensor], w2: Sequence[torch.Tensor], ws1: Optional[Sequence] = None,
              ws2: Optional[Sequence] = None, stream=None) -> None:

@@ -77,7 +77,12 @@ class Case:
         self.x = synth.activations(cfg)
         self.logits = synth.logits(cfg)
         o = oracle.default()
-        self.ids_ref, self.w_ref = o.route(self.logits, cfg.k, cfg.score)
+        self.bias = synth.router_bias(cfg)
+        if cfg.variant_router:
+            self.ids_ref, self.w_ref = o.route_general(self.logits, cfg.k, cfg.score, self.bias, cfg.n_group,
+                                                       cfg.topk_group, cfg.renorm, cfg.routed_scaling)
+        else:
+            self.ids_ref, self.w_ref = o.route(self.logits, cfg.k, cfg.score)
         self.tokens = np.arange(cfg.T, dtype=np.int32) if tokens is None else np.asarray(tokens, np.int32)
         need = sorted(set(self.ids_ref[self.tokens].reshape(-1).tolist()))
         if weights == "oracle":
@@ -105,4 +110,6 @@ class Case:
         L = m.MoeLayer.from_config(self.cfg, max_tokens=max_tokens, device=DEV)
         ws = self.dev_w
         L.pack(ws[0], ws[1], ws[2] if self.cfg.shared else None, ws[3] if self.cfg.shared else None)
+        if self.bias is not None:
+            L.pack_router_bias(up(self.bias))
         return L

@@ -35,8 +35,7 @@ def test_library_exports_every_declared_symbol():
 def desc(**kw):
     base = dict(hidden=256, inter=128, num_experts=8, top_k=2, max_tokens=16)
     base.update(kw)
-    extra = {k: base.pop(k) for k in ("score", "act", "num_shared", "abi_version") if k in base}
-    return m.make_desc(**base, **extra)
+    return m.make_desc(**base)
 
 
 def plan_rc(d):
@@ -61,9 +60,63 @@ def plan_rc(d):
     (dict(num_shared=2), m.MOE_ERR_SHAPE),
     (dict(score=5), m.MOE_ERR_ENUM),
     (dict(act=3), m.MOE_ERR_ENUM),
+    # router / activation variants (ABI 2)
+    (dict(score="sqrt_softplus", use_bias=True, n_group=4, topk_group=2, routed_scaling=2.5,
+          swiglu_limit=10.0), m.MOE_OK),
+    (dict(renormalize=False), m.MOE_OK),
+    (dict(swiglu_limit=0.0), m.MOE_OK),
+    (dict(n_group=3), m.MOE_ERR_SHAPE),                    # does not divide E = 8
+    (dict(n_group=8, topk_group=1), m.MOE_ERR_SHAPE),      # 1 group of 1 expert < k = 2
+    (dict(n_group=4, topk_group=5), m.MOE_ERR_SHAPE),
+    (dict(n_group=4, topk_group=0), m.MOE_ERR_SHAPE),
+    (dict(routed_scaling=0.0), m.MOE_ERR_SHAPE),
+    (dict(routed_scaling=float("inf")), m.MOE_ERR_SHAPE),
+    (dict(swiglu_limit=-1.0), m.MOE_ERR_SHAPE),
+    (dict(swiglu_limit=float("nan")), m.MOE_ERR_SHAPE),
+    (dict(score=3), m.MOE_ERR_ENUM),
 ])
 def test_plan_validation(kw, code):
     assert plan_rc(desc(**kw)) == code
+
+
+class moe_desc_v1(ctypes.Structure):
+    """The version-1 descriptor: the current one without the fields added in ABI 2."""
+    _fields_ = m.moe_desc._fields_[:10]
+
+
+def test_plan_accepts_version1_descriptor():
+    d2 = desc()
+    d1 = moe_desc_v1()
+    for name, _ in moe_desc_v1._fields_:
+        setattr(d1, name, getattr(d2, name))
+    d1.abi_version = 1
+    as_desc = lambda d: ctypes.cast(ctypes.pointer(d), ctypes.POINTER(m.moe_desc))
+    sizes = []
+    for d in (d1, d2):
+        plan, pb, wb = ctypes.c_void_p(), ctypes.c_size_t(), ctypes.c_size_t()
+        assert m.lib().moe_plan(as_desc(d), ctypes.byref(plan), ctypes.byref(pb), ctypes.byref(wb)) == 0
+        m.moe_plan_destroy(plan.value)
+        sizes.append((pb.value, wb.value))
+    assert sizes[0] == sizes[1]
+    d1.renormalize = 0                                       # version 1 has no un-renormalised weights
+    plan = ctypes.c_void_p()
+    assert m.lib().moe_plan(as_desc(d1), ctypes.byref(plan), None, None) == m.MOE_ERR_SHAPE
+
+
+def test_pack_router_bias_validation():
+    fake = 1 << 20
+    plain, pb, _ = m.moe_plan(desc())
+    biased, pb2, _ = m.moe_plan(desc(use_bias=True))
+    L = m.lib()
+    try:
+        assert pb2 >= pb + 8 * 4
+        assert L.moe_pack_router_bias(plain, fake, fake, pb, None) == m.MOE_ERR_SHAPE    # no bias declared
+        assert L.moe_pack_router_bias(biased, None, fake, pb2, None) == m.MOE_ERR_NULL
+        assert L.moe_pack_router_bias(biased, fake, fake, pb2 - 1, None) == m.MOE_ERR_SIZE
+        assert L.moe_pack_router_bias(biased, fake + 2, fake, pb2, None) == m.MOE_ERR_ALIGN
+    finally:
+        m.moe_plan_destroy(plain)
+        m.moe_plan_destroy(biased)
 
 
 def test_plan_sizes_cover_the_layout():

@@ -54,6 +54,37 @@ def test_small(cfg):
     _run_and_check(Case(cfg))
 
 
+# router and activation variants: sqrt-softplus scores, selection-only bias, the group step,
+# routed scaling, un-renormalised weights, clamped SwiGLU (routed experts only)
+VARIANTS = [
+    synth.MoeConfig("v-sqrtsoftplus-bias-clamp", T=40, H=256, I=128, E=16, k=4, score="sqrt_softplus",
+                    shared=1, seed=21, bias_sigma=0.3, swiglu_limit=0.05),
+    synth.MoeConfig("v-groups-scaled", T=300, H=256, I=256, E=32, k=4, score="sigmoid", seed=22,
+                    bias_sigma=0.05, n_group=8, topk_group=3, routed_scaling=2.5),
+    synth.MoeConfig("v-softmax-norenorm", T=24, H=128, I=128, E=64, k=6, seed=23, renorm=False,
+                    n_group=4, topk_group=2),
+    synth.MoeConfig("v-clamp-zero", T=33, H=256, I=128, E=8, k=2, shared=1, seed=24, swiglu_limit=0.0),
+    synth.MoeConfig("v-w4a4-wide-e", T=130, H=256, I=128, E=600, k=8, act="nvfp4", score="sqrt_softplus",
+                    seed=25, bias_sigma=0.2, n_group=6, topk_group=4),
+    synth.deepseek_v4_flash(8),
+]
+
+
+@pytest.mark.parametrize("cfg", VARIANTS, ids=lambda c: c.name)
+def test_router_activation_variants(cfg):
+    _run_and_check(Case(cfg))
+
+
+def test_deepseek_v4_flash_t64_sampled():
+    cfg = synth.deepseek_v4_flash(64)
+    _run_and_check(Case(cfg, tokens=synth.token_sample(cfg, 8)))
+
+
+def test_deepseek_v3_router_sampled():
+    cfg = synth.deepseek_v3_router(1024)
+    _run_and_check(Case(cfg, tokens=synth.token_sample(cfg, 3), weights="gpu"))
+
+
 @pytest.mark.parametrize("T", synth.DECODE_TOKENS)
 def test_qwen3_decode(T):
     _run_and_check(Case(synth.qwen3_decode(T)))
