@@ -20,7 +20,11 @@ Prints one JSON line: tokens/s of the whole step (value), plus
   cpu_baseline: the CPU oracle (FP64, OpenMP) on a bounded sample of the same
                 workload, on this host's cores.
 Other workloads (--workload qwen3-30b-a3b-prefill | deepseek-v3 | skewed-w4a4 |
-tiny) print the same line for that configuration.
+tiny) print the same line for that configuration, and so do the router/activation
+variants deepseek-v4-flash-decode (256 experts, top-6, H=4096, I=1024, sqrt-softplus
+scores with a selection bias, SwiGLU clamped at 10, one shared expert; T in
+{1, 8, 32, 64}) and deepseek-v3-noaux (the DeepSeek-V3 layer with its grouped
+sigmoid router, selection bias and routed scale 2.5).
 
 roofline.traffic is the HBM traffic of one gate/up launch measured by rocprofv3
 counters (FETCH_SIZE and WRITE_SIZE runs, each scaled by the reading of a 1 GiB
@@ -70,6 +74,12 @@ def workload(name):
         return [synth.skewed_w4a4()], "hbm"
     if name == "tiny":
         return [synth.tiny()], "hbm"
+    # router / activation variants of the layer (sqrt-softplus + bias + clamped SwiGLU;
+    # DeepSeek-V3's grouped sigmoid router with bias and routed scaling)
+    if name == "deepseek-v4-flash-decode":
+        return [synth.deepseek_v4_flash(T) for T in synth.DECODE_TOKENS], "hbm"
+    if name == "deepseek-v3-noaux":
+        return [synth.deepseek_v3_router(8192)], "mfma"
     raise SystemExit(f"unknown workload {name}")
 
 
@@ -87,6 +97,9 @@ class Batch:
             W.append(quantize_projection(G, N, K, lambda e0, c, w=w: synth.expert_weights_f32(cfg, w, e0, c), dev))
         self.layer = m.MoeLayer.from_config(cfg, device=dev)
         self.layer.pack(W[0], W[1], W[2] if cfg.shared else None, W[3] if cfg.shared else None)
+        bias = synth.router_bias(cfg)
+        if bias is not None:
+            self.layer.pack_router_bias(torch.from_numpy(bias).to(dev))
         del W
         x = synth.activations(cfg)
         self.x = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
@@ -139,7 +152,7 @@ def cpu_baseline(cfgs, budget_s=6.0):
     cfg = max(cfgs, key=lambda c: c.T)
     tokens = np.arange(cfg.T, dtype=np.int32) if cfg.T <= 64 else synth.token_sample(cfg, 16)
     logits = synth.logits(cfg)
-    ids, _ = o.route(logits, cfg.k, cfg.score)
+    ids, _ = omoe.route(cfg, logits, o)
     need = sorted(set(ids[tokens].reshape(-1).tolist()))
     log(f"[bench] cpu baseline: quantising {len(need)} experts for the oracle (untimed)")
     W1 = omoe.quantized_weights(cfg, "w1", need)

@@ -64,6 +64,15 @@ def cached_weights(cfg: synth.MoeConfig):
     return W1, W2, WS1, WS2
 
 
+def route(cfg: synth.MoeConfig, logits: np.ndarray, o: Optional[Oracle] = None):
+    """ids [T][k] and FP64 weights of the configuration's router (plain or generalised)."""
+    o = o or default()
+    if cfg.variant_router:
+        return o.route_general(logits, cfg.k, cfg.score, synth.router_bias(cfg), cfg.n_group, cfg.topk_group,
+                               cfg.renorm, cfg.routed_scaling)
+    return o.route(logits, cfg.k, cfg.score)
+
+
 def forward(cfg: synth.MoeConfig, x_bf16: np.ndarray, logits: np.ndarray, W1, W2, WS1=None,
             WS2=None, tokens: Optional[np.ndarray] = None, o: Optional[Oracle] = None) -> Dict:
     """Layer output (FP64, never rounded) for `tokens` (all tokens if None).
@@ -74,11 +83,7 @@ def forward(cfg: synth.MoeConfig, x_bf16: np.ndarray, logits: np.ndarray, W1, W2
     o = o or default()
     T = x_bf16.shape[0]
     tokens = np.arange(T, dtype=np.int32) if tokens is None else np.asarray(tokens, np.int32)
-    if cfg.variant_router:
-        ids, w = o.route_general(logits, cfg.k, cfg.score, synth.router_bias(cfg), cfg.n_group,
-                                 cfg.topk_group, cfg.renorm, cfg.routed_scaling)
-    else:
-        ids, w = o.route(logits, cfg.k, cfg.score)
+    ids, w = route(cfg, logits, o)
     counts, offsets, perm, inv = o.plan(ids, cfg.E)
     res = dict(ids=ids, w=w, counts=counts, offsets=offsets, perm=perm, inv=inv, tokens=tokens)
     if cfg.act == "nvfp4":

@@ -78,11 +78,7 @@ class Case:
         self.logits = synth.logits(cfg)
         o = oracle.default()
         self.bias = synth.router_bias(cfg)
-        if cfg.variant_router:
-            self.ids_ref, self.w_ref = o.route_general(self.logits, cfg.k, cfg.score, self.bias, cfg.n_group,
-                                                       cfg.topk_group, cfg.renorm, cfg.routed_scaling)
-        else:
-            self.ids_ref, self.w_ref = o.route(self.logits, cfg.k, cfg.score)
+        self.ids_ref, self.w_ref = omoe.route(cfg, self.logits, o)
         self.tokens = np.arange(cfg.T, dtype=np.int32) if tokens is None else np.asarray(tokens, np.int32)
         need = sorted(set(self.ids_ref[self.tokens].reshape(-1).tolist()))
         if weights == "oracle":
