@@ -43,6 +43,11 @@ SMALL = [
     synth.MoeConfig("all-experts", T=40, H=256, I=128, E=8, k=8, score="sigmoid", seed=12),
     synth.MoeConfig("shared-small", T=70, H=256, I=256, E=16, k=4, score="sigmoid", shared=1, seed=13),
     synth.MoeConfig("shared-small-w4a4", T=150, H=512, I=128, E=8, k=2, shared=1, act="nvfp4", seed=14),
+    # small bf16 decode batches: a shared expert, 256 experts (16 per lane of a routing
+    # row), a single pick, one token
+    synth.MoeConfig("decode-shared", T=7, H=256, I=128, E=16, k=4, shared=1, seed=17),
+    synth.MoeConfig("decode-e256-k1", T=64, H=256, I=128, E=256, k=1, seed=18),
+    synth.MoeConfig("decode-e200-t1", T=1, H=384, I=256, E=200, k=8, score="sigmoid", seed=19),
     # hidden 128 / 384: the prefill down launch cannot use its widest workgroup and narrows
     synth.MoeConfig("prefill-h128", T=260, H=128, I=256, E=4, k=2, seed=15),
     synth.MoeConfig("prefill-h384-w4a4", T=300, H=384, I=128, E=4, k=2, act="nvfp4", seed=16),
