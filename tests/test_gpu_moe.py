@@ -180,3 +180,24 @@ def test_run_timed_matches_run(T):
         t = ev[2 * s].elapsed_time(ev[2 * s + 1])
         log(f"T={T} stage {m.STAGE_NAMES[s]}: {t * 1e3:.1f} us")
         assert 0.0 < t < 1000.0
+
+
+# the descriptor's limits: hidden and intermediate 16384 (128 K chunks), 65536 tokens
+MAX_SIZES = [
+    synth.MoeConfig("max-hidden-decode", T=16, H=16384, I=128, E=4, k=2, seed=31),
+    synth.MoeConfig("max-hidden-prefill-w4a4", T=200, H=16384, I=128, E=4, k=2, act="nvfp4", seed=32),
+    synth.MoeConfig("max-inter-prefill", T=40, H=128, I=16384, E=4, k=2, shared=1, seed=33),
+    synth.MoeConfig("max-inter-decode", T=3, H=256, I=16384, E=8, k=2, score="sigmoid", seed=35),
+]
+
+
+@pytest.mark.parametrize("cfg", MAX_SIZES, ids=lambda c: c.name)
+def test_max_sizes(cfg):
+    _run_and_check(Case(cfg, tokens=synth.token_sample(cfg, 16)))
+
+
+def test_max_tokens_sampled():
+    """T = 65536 = the token limit: the whole routing (ids, weights, counts, offsets,
+    permutation of 524288 rows) bit-exact, sampled outputs."""
+    cfg = synth.MoeConfig("max-tokens", T=65536, H=128, I=128, E=64, k=8, seed=34)
+    _run_and_check(Case(cfg, tokens=synth.token_sample(cfg, 24)))
