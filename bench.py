@@ -94,7 +94,12 @@ class Batch:
         for w in projs:
             G = cfg.shared if w.startswith("ws") else cfg.E
             N, K = (2 * cfg.I, cfg.H) if w in ("w1", "ws1") else (cfg.H, cfg.I)
-            W.append(quantize_projection(G, N, K, lambda e0, c, w=w: synth.expert_weights_f32(cfg, w, e0, c), dev))
+            if cfg.wfmt == "mxfp4":   # drawn directly in the boundary format
+                codes, scales = synth.mxfp4_weights(cfg, w, 0, G)
+                W.append((torch.from_numpy(codes).to(dev), torch.from_numpy(scales).to(dev), None))
+            else:
+                W.append(quantize_projection(G, N, K, lambda e0, c, w=w: synth.expert_weights_f32(cfg, w, e0, c),
+                                             dev))
         self.layer = m.MoeLayer.from_config(cfg, device=dev)
         self.layer.pack(W[0], W[1], W[2] if cfg.shared else None, W[3] if cfg.shared else None)
         bias = synth.router_bias(cfg)
@@ -122,9 +127,16 @@ class Batch:
                         L.workspace_bytes, None, events)
 
     # algorithmic work of the gate/up launch (the dominant kernel) and of the layer
+    def weight_bytes(self, n: int) -> float:
+        """Algorithmic bytes of n weights of one expert projection in the workload's format:
+        NVFP4 4.5 bits + a 4-byte global scale, MXFP4 4.25 bits (E8M0 per 32, no global scale)."""
+        if self.cfg.wfmt == "mxfp4":
+            return n * (0.5 + 1.0 / 32)
+        return n * NVFP4_BYTES_PER_WEIGHT + 4
+
     def gate_up_bytes(self):
         c = self.cfg
-        w = self.touched * (2 * c.I * c.H * NVFP4_BYTES_PER_WEIGHT + 4) + c.shared * (2 * c.I * c.H * NVFP4_BYTES_PER_WEIGHT + 4)
+        w = (self.touched + c.shared) * self.weight_bytes(2 * c.I * c.H)
         act = c.T * c.H * (2 if c.act == "bf16" else NVFP4_BYTES_PER_WEIGHT + 4.0 / c.H)
         h = (self.rows + c.shared * c.T) * c.I * 2
         return w + act + h
@@ -135,7 +147,7 @@ class Batch:
 
     def layer_bytes(self):
         c = self.cfg
-        w = (self.touched + c.shared) * 3 * c.I * c.H * NVFP4_BYTES_PER_WEIGHT
+        w = (self.touched + c.shared) * (self.weight_bytes(2 * c.I * c.H) + self.weight_bytes(c.H * c.I))
         return w + c.T * c.H * 2 + c.T * c.E * 4 + c.T * c.H * 2
 
     def layer_flops(self):
@@ -154,11 +166,11 @@ def cpu_baseline(cfgs, budget_s=6.0):
     logits = synth.logits(cfg)
     ids, _ = omoe.route(cfg, logits, o)
     need = sorted(set(ids[tokens].reshape(-1).tolist()))
-    log(f"[bench] cpu baseline: quantising {len(need)} experts for the oracle (untimed)")
-    W1 = omoe.quantized_weights(cfg, "w1", need)
-    W2 = omoe.quantized_weights(cfg, "w2", need)
-    WS1 = omoe.quantized_weights(cfg, "ws1") if cfg.shared else None
-    WS2 = omoe.quantized_weights(cfg, "ws2") if cfg.shared else None
+    log(f"[bench] cpu baseline: preparing the weights of {len(need)} experts for the oracle (untimed)")
+    W1 = omoe.projection_weights(cfg, "w1", need)
+    W2 = omoe.projection_weights(cfg, "w2", need)
+    WS1 = omoe.projection_weights(cfg, "ws1") if cfg.shared else None
+    WS2 = omoe.projection_weights(cfg, "ws2") if cfg.shared else None
     x = synth.activations(cfg)
     n_tok, t0, reps = 0, time.perf_counter(), 0
     while True:
@@ -171,7 +183,7 @@ def cpu_baseline(cfgs, budget_s=6.0):
     return {"value": n_tok / el, "unit": "tokens/s", "cores": min(o.threads(), len(tokens)), "kind": "oracle",
             "sample": f"{cfg.name}: {len(tokens)} tokens (routing, {'activation quantisation, ' if cfg.act == 'nvfp4' else ''}"
                       f"FP64 expert MLPs of their {cfg.k} experts, combine) x {reps} repeats, {el:.1f} s; "
-                      f"weight quantisation untimed"}
+                      f"weight preparation untimed"}
 
 
 # ------------------------------------------------------------ rocprofv3 summaries

@@ -78,6 +78,13 @@ extern "C" {
 #define MOE_ACT_BF16 0
 #define MOE_ACT_NVFP4_ROWQ 1
 
+/* Weight format of every projection ([vllm.cpp] capability table, MXFP4 row: E8M0
+ * dequant 2^(byte-127), group 32, no global scale, distinct from NVFP4's group-16 fp8
+ * scale path; [b12x] "DeepSeek V4 Flash 0731 MoE reproduction": MXFP4 E8M0/K32 expert
+ * weights). */
+#define MOE_WEIGHTS_NVFP4 0   /* E2M1 x E4M3 per 16 along K x FP32 per expert */
+#define MOE_WEIGHTS_MXFP4 1   /* E2M1 x E8M0 (2^(byte-127)) per 32 along K */
+
 /* Layer descriptor. Limits: hidden and inter multiples of 128 (hidden <= 16384,
  * inter <= 16384), 1 <= top_k <= min(64, num_experts), num_experts <= 1024,
  * 1 <= max_tokens <= 65536, num_shared in {0, 1}; renormalize in {0, 1};
@@ -85,7 +92,8 @@ extern "C" {
  * topk_group * (num_experts / n_group) >= top_k; routed_scaling finite and > 0;
  * swiglu_limit finite and >= 0 when swiglu_clamp is set.
  * A descriptor with abi_version 1 ends after num_shared; its later fields take the
- * values of the plain layer (1, 1, 0, 0, 1.0, 0) and it must have renormalize == 1.
+ * values of the plain layer (1, 1, 0, 0, 1.0, 0, MOE_WEIGHTS_NVFP4) and it must have
+ * renormalize == 1.
  *
  * The plain router (score softmax or sigmoid, renormalize 1, no bias, n_group 1,
  * routed_scaling 1) selects on the logits. Any other setting runs the generalised
@@ -124,13 +132,14 @@ typedef struct {
   int32_t swiglu_clamp;     /* 1: clamped SwiGLU for the routed experts */
   float routed_scaling;     /* factor on the routed weights */
   float swiglu_limit;       /* clamp limit L */
+  int32_t weight_format;    /* MOE_WEIGHTS_* of every projection */
 } moe_desc;
 
 /* Opaque plan: host memory, immutable after moe_plan, safe to share between
  * threads. Concurrent moe_run calls need distinct workspaces. */
 typedef struct moe_plan moe_plan_t;
 
-/* One NVFP4 projection of G experts in the pages' operand layout ([vllm.cpp]
+/* One FP4 projection of G experts in the pages' operand layout ([vllm.cpp]
  * capability table, GGUF loading row: weight_packed [N,K/2] + weight_scale
  * [N,K/16] + per-expert weight_scale_2; [megamoe] archived CORRECTNESS_BACKLOG
  * §7: the weight global scale is weight_scale_2). Device pointers:
@@ -139,6 +148,13 @@ typedef struct moe_plan moe_plan_t;
  *   scales       u8  [G][N][K/16]  E4M3fn block scales, block = 16 consecutive k
  *   global_scale f32 [G]           per-expert global scale
  * W[g][n][k] = E2M1(code) * E4M3(scale[g][n][k/16]) * global_scale[g].
+ * MXFP4 (weight_format MOE_WEIGHTS_MXFP4): scales u8 [G][N][K/32] E8M0 bytes,
+ * global_scale unused (may be NULL), W[g][n][k] = E2M1(code) * 2^(scale[g][n][k/32]
+ * - 127). Packing turns every MXFP4 expert exactly into the NVFP4 form the kernels
+ * read: per-expert global scale 2^(m - 135), m = the expert's largest scale byte,
+ * and E4M3 block scales 2^(byte - m + 8), exact while byte >= m - 17 (E4M3's
+ * smallest power of two is 2^-9); moe_validate_weights_host rejects wider spans and
+ * the NaN byte 0xFF, and packing flushes blocks below the span to zero.
  * gate_up: N = 2I, K = H, rows 0..I-1 are the gate, rows I..2I-1 the up
  * projection; down: N = H, K = I. */
 typedef struct {

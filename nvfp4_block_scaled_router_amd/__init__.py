@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libnvfp4moe.so")
 MOE_ABI_VERSION = 2
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID, MOE_SCORE_SQRT_SOFTPLUS = 0, 1, 2
 MOE_ACT_BF16, MOE_ACT_NVFP4_ROWQ = 0, 1
+MOE_WEIGHTS_NVFP4, MOE_WEIGHTS_MXFP4 = 0, 1
 MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_SIZE, MOE_ERR_TOKENS = 0, -1, -2, -3, -4
 MOE_ERR_ALIGN, MOE_ERR_ABI, MOE_ERR_ENUM, MOE_ERR_WEIGHT = -5, -6, -7, -8
 
@@ -40,7 +41,7 @@ class moe_desc(ctypes.Structure):
                 ("act_format", _i32), ("num_shared", _i32),
                 # since ABI 2
                 ("use_bias", _i32), ("n_group", _i32), ("topk_group", _i32), ("swiglu_clamp", _i32),
-                ("routed_scaling", ctypes.c_float), ("swiglu_limit", ctypes.c_float)]
+                ("routed_scaling", ctypes.c_float), ("swiglu_limit", ctypes.c_float), ("weight_format", _i32)]
 
 
 class moe_nvfp4_tensor(ctypes.Structure):
@@ -127,7 +128,8 @@ def _stream(stream) -> Optional[int]:
 def make_desc(hidden: int, inter: int, num_experts: int, top_k: int, max_tokens: int, score: str = "softmax",
               act: str = "bf16", num_shared: int = 0, abi_version: int = MOE_ABI_VERSION, *,
               use_bias: bool = False, n_group: int = 1, topk_group: int = 1, renormalize: bool = True,
-              routed_scaling: float = 1.0, swiglu_limit: Optional[float] = None) -> moe_desc:
+              routed_scaling: float = 1.0, swiglu_limit: Optional[float] = None,
+              weights: str = "nvfp4") -> moe_desc:
     """Layer descriptor; the keyword arguments select the router and activation variants
     (all off by default: the plain layer)."""
     d = moe_desc()
@@ -143,6 +145,7 @@ def make_desc(hidden: int, inter: int, num_experts: int, top_k: int, max_tokens:
     d.routed_scaling = routed_scaling
     d.swiglu_clamp = 0 if swiglu_limit is None else 1
     d.swiglu_limit = 0.0 if swiglu_limit is None else swiglu_limit
+    d.weight_format = {"nvfp4": MOE_WEIGHTS_NVFP4, "mxfp4": MOE_WEIGHTS_MXFP4}.get(weights, weights)
     return d
 
 

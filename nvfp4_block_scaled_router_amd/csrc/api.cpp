@@ -107,6 +107,7 @@ static int load_desc(const moe_desc* in, moe_desc* out) {
   if ((long)d->topk_group * (d->num_experts / d->n_group) < d->top_k) return MOE_ERR_SHAPE;
   if (!std::isfinite(d->routed_scaling) || d->routed_scaling <= 0.0f) return MOE_ERR_SHAPE;
   if (d->swiglu_clamp && (!std::isfinite(d->swiglu_limit) || d->swiglu_limit < 0.0f)) return MOE_ERR_SHAPE;
+  if (d->weight_format != MOE_WEIGHTS_NVFP4 && d->weight_format != MOE_WEIGHTS_MXFP4) return MOE_ERR_ENUM;
   return MOE_OK;
 }
 
@@ -174,9 +175,9 @@ int moe_plan(const moe_desc* desc, moe_plan_t** plan, size_t* packed_bytes, size
 
 void moe_plan_destroy(moe_plan_t* plan) { delete plan; }
 
-static int check_tensor(const moe_nvfp4_tensor* t) {
-  if (!t || !t->packed || !t->scales || !t->global_scale) return MOE_ERR_NULL;
-  if (!aligned16(t->packed) || !aligned16(t->scales) || !aligned4(t->global_scale)) return MOE_ERR_ALIGN;
+static int check_tensor(const moe_nvfp4_tensor* t, bool mx) {
+  if (!t || !t->packed || !t->scales || (!mx && !t->global_scale)) return MOE_ERR_NULL;
+  if (!aligned16(t->packed) || !aligned16(t->scales) || (!mx && !aligned4(t->global_scale))) return MOE_ERR_ALIGN;
   return MOE_OK;
 }
 
@@ -184,11 +185,12 @@ int moe_pack_weights(const moe_plan_t* plan, const moe_nvfp4_tensor* gate_up, co
                      const moe_nvfp4_tensor* shared_gate_up, const moe_nvfp4_tensor* shared_down, void* packed,
                      size_t packed_bytes, void* stream) {
   if (!plan || !packed) return MOE_ERR_NULL;
-  int rc = check_tensor(gate_up);
-  if (!rc) rc = check_tensor(down);
+  const bool mx = plan->d.weight_format == MOE_WEIGHTS_MXFP4;
+  int rc = check_tensor(gate_up, mx);
+  if (!rc) rc = check_tensor(down, mx);
   if (!rc && plan->d.num_shared) {
-    rc = check_tensor(shared_gate_up);
-    if (!rc) rc = check_tensor(shared_down);
+    rc = check_tensor(shared_gate_up, mx);
+    if (!rc) rc = check_tensor(shared_down, mx);
   }
   if (rc) return rc;
   if (!aligned16(packed)) return MOE_ERR_ALIGN;
@@ -210,6 +212,7 @@ int moe_pack_weights(const moe_plan_t* plan, const moe_nvfp4_tensor* gate_up, co
       a.N = L.N;
       a.K = L.K;
       a.gate_up = proj == 0;
+      a.mx = mx ? 1 : 0;
       a.fp4_out = base + (proj ? plan->off_w2f : plan->off_w1f) + g0 * L.fp4_expert;
       a.sc_out = base + (proj ? plan->off_w2s : plan->off_w1s) + g0 * L.sc_expert;
       a.gs_out = (float*)(base + (proj ? plan->off_w2g : plan->off_w1g)) + g0;
@@ -422,12 +425,28 @@ int moe_validate_weights_host(const moe_desc* in, const moe_nvfp4_tensor* t, int
   const int rc = load_desc(in, &dd);
   if (rc) return rc;
   const moe_desc* desc = &dd;
-  if (!t || !t->packed || !t->scales || !t->global_scale) return MOE_ERR_NULL;
+  const bool mx = desc->weight_format == MOE_WEIGHTS_MXFP4;
+  if (!t || !t->packed || !t->scales || (!mx && !t->global_scale)) return MOE_ERR_NULL;
   if (which < 0 || which > 3) return MOE_ERR_ENUM;
   const int G = which >= 2 ? desc->num_shared : desc->num_experts;
   const bool up = (which & 1) == 0;
   const size_t N = up ? 2 * (size_t)desc->inter : (size_t)desc->hidden;
   const size_t K = up ? (size_t)desc->hidden : (size_t)desc->inter;
+  if (mx) {
+    // E8M0: no NaN byte, and every block within 17 binades of its expert's largest scale
+    const size_t per = N * (K / 32);
+    for (int g = 0; g < G; ++g) {
+      const uint8_t* sc = t->scales + (size_t)g * per;
+      int m = 0;
+      for (size_t i = 0; i < per; ++i) {
+        if (sc[i] == 0xFFu) return MOE_ERR_WEIGHT;
+        m = std::max(m, (int)sc[i]);
+      }
+      for (size_t i = 0; i < per; ++i)
+        if ((int)sc[i] < m - MX_SCALE_SPAN) return MOE_ERR_WEIGHT;
+    }
+    return MOE_OK;
+  }
   const size_t nsc = (size_t)G * N * (K / 16);
   for (size_t i = 0; i < nsc; ++i) {
     const uint8_t b = t->scales[i];

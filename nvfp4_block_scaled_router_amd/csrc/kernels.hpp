@@ -58,12 +58,17 @@ hipError_t launch_quant_groups_f32(const float* x, int groups, int rows_per_grou
                                    uint8_t* scales, float* gs, hipStream_t s);
 
 // Weight re-layout.
+// MXFP4 packing: the E8M0 scale bytes of an expert lie within MX_SCALE_SPAN of its
+// largest one m, so 2^(byte - m + 8) is an E4M3 value (2^-9 .. 2^8).
+constexpr int MX_SCALE_SPAN = 17;
+
 struct PackArgs {
   const uint8_t* packed;   // boundary layout [G][N][K/2]
-  const uint8_t* scales;   // [G][N][K/16]
-  const float* gs;         // [G]
+  const uint8_t* scales;   // [G][N][K/16] E4M3 (NVFP4) or [G][N][K/32] E8M0 (MXFP4)
+  const float* gs;         // [G] (NVFP4)
   int G, N, K;
   int gate_up;             // 1: interleave gate/up 16-row tiles
+  int mx;                  // 1: MXFP4 input, re-expressed as E4M3 blocks + per-expert gs
   uint8_t* fp4_out;        // [G][N/16][KC][64][16]
   uint8_t* sc_out;         // [G][N/16][KSG][64][16]
   float* gs_out;           // [G]

@@ -9,6 +9,9 @@
 // wave-wide 16-byte load reads 1 KiB of contiguous memory.
 // scale tile (g, q, scale group sg) = 64 lanes x 16 bytes, lane l holding for the 8
 // chunks kc = 8*sg + c the two block scales (8*kc + 2*(l/16), +1) of row (l % 16).
+// MXFP4 input (E2M1 codes with E8M0 scales per 32 k, [vllm.cpp] capability table, MXFP4
+// row) is re-expressed exactly in this form: per expert gs = 2^(m - 135), m its largest
+// scale byte, and both E4M3 block scales of a 32-column block = 2^(byte - m + 8).
 // For gate_up, tile q maps to boundary rows 16*(q/2) + r (q even: gate) or
 // I + 16*(q/2) + r (q odd: up), so gate and up tiles of the same columns alternate.
 #include "common.hpp"
@@ -37,6 +40,32 @@ __global__ __launch_bounds__(256) void pack_fp4_kernel(PackArgs a) {
   }
 }
 
+// E4M3 byte of 2^p: normal for p in [-6, 8] (exponent field p + 7), subnormal m 2^-9 for
+// p in [-9, -7]; below that 0 (outside the span the host validation admits).
+__device__ __forceinline__ uint8_t e4m3_pow2(int p) {
+  if (p >= -6) return (uint8_t)((p + 7) << 3);
+  if (p >= -9) return (uint8_t)(1 << (p + 9));
+  return 0;
+}
+
+// MXFP4: per expert the largest E8M0 byte m -> gs_out[g] = 2^(m - 135) (one workgroup per
+// expert, a max over its N x K/32 scale bytes).
+__global__ __launch_bounds__(256) void pack_mx_gs_kernel(PackArgs a) {
+  __shared__ int red[256];
+  const int g = blockIdx.x;
+  const size_t per = (size_t)a.N * (a.K / 32);
+  const uint8_t* sc = a.scales + (size_t)g * per;
+  int m = 0;
+  for (size_t i = threadIdx.x; i < per; i += blockDim.x) m = max(m, (int)sc[i]);
+  red[threadIdx.x] = m;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] = max(red[threadIdx.x], red[threadIdx.x + w]);
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) a.gs_out[g] = ldexpf(1.0f, red[0] - 135);
+}
+
 __global__ __launch_bounds__(256) void pack_scales_kernel(PackArgs a) {
   const ProjLayout L = proj_layout(a.N, a.K);
   const size_t units = (size_t)a.G * (a.N / 16) * L.KSG * WAVE;
@@ -48,14 +77,28 @@ __global__ __launch_bounds__(256) void pack_scales_kernel(PackArgs a) {
     const int q = (int)(rest % (a.N / 16));
     const int g = (int)(rest / (a.N / 16));
     const int row = boundary_row(q, lane % 16, a.N, a.gate_up);
-    const uint8_t* src = a.scales + ((size_t)g * a.N + row) * (a.K / 16);
     uint8_t b[16];
+    if (a.mx) {
+      // MXFP4: the lane's 32 columns of chunk kc are one E8M0 block, re-expressed as two
+      // equal E4M3 block scales 2^(byte - m + 8) against the expert's gs = 2^(m - 135)
+      const int m = ilogbf(a.gs_out[g]) + 135;
+      const uint8_t* src = a.scales + ((size_t)g * a.N + row) * (a.K / 32);
 #pragma unroll
-    for (int c = 0; c < SCALE_GROUP; ++c) {
-      const int kc = sg * SCALE_GROUP + c;
-      const bool in = kc < L.KC;
-      b[2 * c] = in ? src[kc * 8 + 2 * (lane / 16)] : 0;
-      b[2 * c + 1] = in ? src[kc * 8 + 2 * (lane / 16) + 1] : 0;
+      for (int c = 0; c < SCALE_GROUP; ++c) {
+        const int kc = sg * SCALE_GROUP + c;
+        const uint8_t e4 = kc < L.KC ? e4m3_pow2((int)src[kc * 4 + lane / 16] - m + 8) : 0;
+        b[2 * c] = e4;
+        b[2 * c + 1] = e4;
+      }
+    } else {
+      const uint8_t* src = a.scales + ((size_t)g * a.N + row) * (a.K / 16);
+#pragma unroll
+      for (int c = 0; c < SCALE_GROUP; ++c) {
+        const int kc = sg * SCALE_GROUP + c;
+        const bool in = kc < L.KC;
+        b[2 * c] = in ? src[kc * 8 + 2 * (lane / 16)] : 0;
+        b[2 * c + 1] = in ? src[kc * 8 + 2 * (lane / 16) + 1] : 0;
+      }
     }
     u32x4 v;
     v.x = b[0] | (b[1] << 8) | (b[2] << 16) | ((uint32_t)b[3] << 24);
@@ -64,13 +107,14 @@ __global__ __launch_bounds__(256) void pack_scales_kernel(PackArgs a) {
     v.w = b[12] | (b[13] << 8) | (b[14] << 16) | ((uint32_t)b[15] << 24);
     *(u32x4*)(a.sc_out + u * 16) = v;
   }
-  if (blockIdx.x == 0)
+  if (blockIdx.x == 0 && !a.mx)
     for (int g = threadIdx.x; g < a.G; g += blockDim.x) a.gs_out[g] = a.gs[g];
 }
 
 hipError_t launch_pack(const PackArgs& a, hipStream_t s) {
   if (a.G <= 0) return hipSuccess;
   hipLaunchKernelGGL(pack_fp4_kernel, dim3(2048), dim3(256), 0, s, a);
+  if (a.mx) hipLaunchKernelGGL(pack_mx_gs_kernel, dim3(a.G), dim3(256), 0, s, a);
   hipLaunchKernelGGL(pack_scales_kernel, dim3(1024), dim3(256), 0, s, a);
   return hipGetLastError();
 }

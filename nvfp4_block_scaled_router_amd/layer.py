@@ -31,7 +31,8 @@ class MoeLayer:
     def from_config(cls, cfg, max_tokens: Optional[int] = None, device="cuda") -> "MoeLayer":
         return cls(cfg.H, cfg.I, cfg.E, cfg.k, max_tokens or cfg.T, cfg.score, cfg.act, cfg.shared, device,
                    use_bias=cfg.bias_sigma > 0, n_group=cfg.n_group, topk_group=cfg.topk_group,
-                   renormalize=cfg.renorm, routed_scaling=cfg.routed_scaling, swiglu_limit=cfg.swiglu_limit)
+                   renormalize=cfg.renorm, routed_scaling=cfg.routed_scaling, swiglu_limit=cfg.swiglu_limit,
+                   weights=cfg.wfmt)
 
     def pack_router_bias(self, bias: torch.Tensor, stream=None) -> None:
         """The per-expert selection bias (device f32 [E]) of a layer declared with use_bias."""

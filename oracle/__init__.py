@@ -28,7 +28,7 @@ _i32, _i64, _u32, _f32, _f64, _u16 = (ctypes.c_int32, ctypes.c_int64, ctypes.c_u
 
 class ProjSet(ctypes.Structure):
     _fields_ = [("w1_packed", _vp), ("w1_scales", _vp), ("w1_gs", _vp),
-                ("w2_packed", _vp), ("w2_scales", _vp), ("w2_gs", _vp)]
+                ("w2_packed", _vp), ("w2_scales", _vp), ("w2_gs", _vp), ("mx", ctypes.c_int32)]
 
 
 def _ptr(a: Optional[np.ndarray]):
@@ -51,6 +51,10 @@ class Oracle:
         L.orc_bf16.argtypes = [_u16]
         L.orc_weight.restype = _f64
         L.orc_weight.argtypes = [_vp, _vp, _f32, _i32, _i32, _i32]
+        L.orc_e8m0.restype = _f64
+        L.orc_e8m0.argtypes = [_u32]
+        L.orc_weight_mx.restype = _f64
+        L.orc_weight_mx.argtypes = [_vp, _vp, _i32, _i32, _i32]
         L.orc_e4m3_encode.restype = ctypes.c_uint8
         L.orc_e4m3_encode.argtypes = [_f32]
         L.orc_e2m1_encode.restype = ctypes.c_uint8
@@ -155,11 +159,21 @@ class Oracle:
         self.L.orc_bf16_rows(b.ctypes.data, b.size, out.ctypes.data)
         return out
 
+    def e8m0(self, b: int) -> float:
+        return self.L.orc_e8m0(b)
+
+    def weight_mx(self, packed, scales, n, k) -> float:
+        K = packed.shape[-1] * 2
+        return self.L.orc_weight_mx(packed.ctypes.data, scales.ctypes.data, K, n, k)
+
     @staticmethod
     def _projset(W1, W2):
+        """W = (packed, scales, gs) for NVFP4, (packed, scales, None) for MXFP4 (the format is
+        told by the scale width: K/16 vs K/32 bytes per row)."""
         ps = ProjSet()
         ps.w1_packed, ps.w1_scales, ps.w1_gs = _ptr(W1[0]), _ptr(W1[1]), _ptr(W1[2])
         ps.w2_packed, ps.w2_scales, ps.w2_gs = _ptr(W2[0]), _ptr(W2[1]), _ptr(W2[2])
+        ps.mx = 1 if W1[2] is None else 0
         return ps
 
     def expert_ffn(self, W1, W2, g: int, x: np.ndarray, swiglu_limit: Optional[float] = None) -> np.ndarray:

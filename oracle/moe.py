@@ -54,6 +54,26 @@ def quantized_weights(cfg: synth.MoeConfig, which: str, experts: Optional[Iterab
     return packed, scales, gs
 
 
+def projection_weights(cfg: synth.MoeConfig, which: str, experts: Optional[Iterable[int]] = None,
+                       o: Optional[Oracle] = None):
+    """The configuration's weights of one projection as the oracle reads them: NVFP4
+    (packed, scales, gs) quantised from the fp32 draws, or MXFP4 (packed, scales, None) as
+    drawn. With `experts` given, only those experts are filled (the rest stay zero)."""
+    if cfg.wfmt != "mxfp4":
+        return quantized_weights(cfg, which, experts, o)
+    G = cfg.shared if which.startswith("ws") else cfg.E
+    N, K = (2 * cfg.I, cfg.H) if which in ("w1", "ws1") else (cfg.H, cfg.I)
+    if experts is None:
+        codes, scales = synth.mxfp4_weights(cfg, which, 0, G)
+        return codes, scales, None
+    codes = np.zeros((G, N, K // 2), np.uint8)
+    scales = np.zeros((G, N, K // 32), np.uint8)
+    for e in sorted(set(int(e) for e in experts)):
+        c, sc = synth.mxfp4_weights(cfg, which, e, 1)
+        codes[e], scales[e] = c[0], sc[0]
+    return codes, scales, None
+
+
 @functools.lru_cache(maxsize=4)
 def cached_weights(cfg: synth.MoeConfig):
     """All routed and shared weights of a (small) configuration."""

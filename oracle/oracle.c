@@ -82,10 +82,27 @@ double orc_bf16(uint16_t b) {
  * dequant = E2M1 value * weight_scale repeated over 16 columns * weight_scale_2;
  * archived CORRECTNESS_BACKLOG §7: the weight global scale is weight_scale_2.
  * The product of an E2M1 value, an E4M3 value and a binary32 is exact in FP64. */
-double orc_weight(const uint8_t* packed, const uint8_t* scales, float gs, int K, int n, int k) {
+static uint32_t orc_nibble(const uint8_t* packed, int K, int n, int k) {
   uint8_t byte = packed[(size_t)n * (K / 2) + k / 2];
-  uint32_t nib = (k & 1) ? (byte >> 4) : (byte & 15u);
-  return orc_e2m1(nib) * orc_e4m3fn(scales[(size_t)n * (K / 16) + k / 16]) * (double)gs;
+  return (k & 1) ? (byte >> 4) : (byte & 15u);
+}
+
+double orc_weight(const uint8_t* packed, const uint8_t* scales, float gs, int K, int n, int k) {
+  return orc_e2m1(orc_nibble(packed, K, n, k)) * orc_e4m3fn(scales[(size_t)n * (K / 16) + k / 16]) * (double)gs;
+}
+
+/* MXFP4 weight element (the second weight format): E2M1 code times an E8M0 block
+ * scale 2^(byte - 127) shared by 32 consecutive k, no global scale; byte 0xFF is
+ * NaN. ([vllm.cpp] capability table, MXFP4 (compressed-tensors mxfp4-pack-quantized)
+ * row: E8M0 dequant 2^(byte-127), group 32, no global scale; [b12x] "DeepSeek V4
+ * Flash 0731 MoE reproduction": MXFP4 E8M0/K32 expert weights.) Exact in FP64. */
+double orc_e8m0(uint32_t byte) {
+  if (byte == 0xFFu) return NAN;
+  return ldexp(1.0, (int)byte - 127);
+}
+
+double orc_weight_mx(const uint8_t* packed, const uint8_t* scales, int K, int n, int k) {
+  return orc_e2m1(orc_nibble(packed, K, n, k)) * orc_e8m0(scales[(size_t)n * (K / 32) + k / 32]);
 }
 
 /* --------------------------------------------------------------- quantizer */
@@ -355,12 +372,22 @@ void orc_plan(const int32_t* ids, int T, int E, int k, int32_t* counts, int32_t*
 
 typedef struct {
   const uint8_t* w1_packed;  /* [G][2I][H/2]; rows 0..I-1 gate, I..2I-1 up */
-  const uint8_t* w1_scales;  /* [G][2I][H/16] */
-  const float* w1_gs;        /* [G] */
+  const uint8_t* w1_scales;  /* [G][2I][H/16] (NVFP4) or [G][2I][H/32] (MXFP4) */
+  const float* w1_gs;        /* [G] (NVFP4 only) */
   const uint8_t* w2_packed;  /* [G][H][I/2] */
-  const uint8_t* w2_scales;  /* [G][H][I/16] */
+  const uint8_t* w2_scales;  /* [G][H][I/16] or [G][H][I/32] */
   const float* w2_gs;        /* [G] */
+  int32_t mx;                /* 0: NVFP4 (orc_weight), 1: MXFP4 (orc_weight_mx) */
 } orc_proj_set;
+
+/* Element (n, k) of expert g's projection in the set's format. */
+static double proj_weight(const orc_proj_set* P, int second, int g, int N, int K, int n, int k) {
+  const uint8_t* pk = (second ? P->w2_packed : P->w1_packed) + (size_t)g * N * (K / 2);
+  const int bs = P->mx ? 32 : 16;
+  const uint8_t* sc = (second ? P->w2_scales : P->w1_scales) + (size_t)g * N * (K / bs);
+  if (P->mx) return orc_weight_mx(pk, sc, K, n, k);
+  return orc_weight(pk, sc, (second ? P->w2_gs : P->w1_gs)[g], K, n, k);
+}
 
 /* One expert's SwiGLU MLP on one input row, FP64:
  *   g_i = sum_k W1[i][k] x_k,  u_i = sum_k W1[I+i][k] x_k,
@@ -373,21 +400,16 @@ typedef struct {
  * bring-up log, W6; a limit of 0 zeroes the expert: the same log, ds4-file
  * loadability entry; limit 10: [b12x] "DeepSeek V4 Flash 0731 MoE reproduction",
  * [megamoe] archived CORRECTNESS_BACKLOG §6, Nvfp4MoE.)
- * Weights are decoded element by element with orc_weight. */
+ * Weights are decoded element by element in the set's format (orc_weight or
+ * orc_weight_mx). */
 void orc_expert_ffn_clamp(const orc_proj_set* P, int g, int H, int I, const double* x, double* y,
                           int clamp, double limit) {
-  size_t w1_pk = (size_t)2 * I * (H / 2), w1_sc = (size_t)2 * I * (H / 16);
-  size_t w2_pk = (size_t)H * (I / 2), w2_sc = (size_t)H * (I / 16);
-  const uint8_t* p1 = P->w1_packed + (size_t)g * w1_pk;
-  const uint8_t* s1 = P->w1_scales + (size_t)g * w1_sc;
-  const uint8_t* p2 = P->w2_packed + (size_t)g * w2_pk;
-  const uint8_t* s2 = P->w2_scales + (size_t)g * w2_sc;
   double* h = (double*)malloc(sizeof(double) * (size_t)I);
   for (int i = 0; i < I; ++i) {
     double gi = 0.0, ui = 0.0;
     for (int k = 0; k < H; ++k) {
-      gi += orc_weight(p1, s1, P->w1_gs[g], H, i, k) * x[k];
-      ui += orc_weight(p1, s1, P->w1_gs[g], H, I + i, k) * x[k];
+      gi += proj_weight(P, 0, g, 2 * I, H, i, k) * x[k];
+      ui += proj_weight(P, 0, g, 2 * I, H, I + i, k) * x[k];
     }
     if (clamp) {
       gi = fmin(gi, limit);
@@ -397,7 +419,7 @@ void orc_expert_ffn_clamp(const orc_proj_set* P, int g, int H, int I, const doub
   }
   for (int n = 0; n < H; ++n) {
     double yn = 0.0;
-    for (int i = 0; i < I; ++i) yn += orc_weight(p2, s2, P->w2_gs[g], I, n, i) * h[i];
+    for (int i = 0; i < I; ++i) yn += proj_weight(P, 1, g, H, I, n, i) * h[i];
     y[n] = yn;
   }
   free(h);

@@ -17,6 +17,10 @@ README, "MoE kernel"). Recipe, per tensor:
 * shared gate_up/down : same, 1 expert                          streams 5, 6
 * Zipf rank permutation (skewed workload)                       stream 7
 * router selection bias (variant routers)   : f32(N(0, sigma)) stream 8
+* MXFP4 weights (second weight format), drawn directly in the boundary format:
+  E2M1 code bytes uniform over 0..255 and E8M0 scales uniform over 117..124
+  (2^-10 .. 2^-3)                                         streams 20 + 2p, 21 + 2p
+  (p = 0 w1, 1 w2, 2 ws1, 3 ws2)
 
 The generator is counter based (see ``synth.c``): element ``i`` of a stream
 depends only on (seed, stream, i).
@@ -57,6 +61,7 @@ def lib():
         L.synth_normal_bf16.argtypes = [u64, u64, u64, i64, f64, vp]
         L.synth_permutation.argtypes = [u64, u64, i32, vp]
         L.synth_logits.argtypes = [u64, u64, u64, i32, i32, vp, vp]
+        L.synth_bytes.argtypes = [u64, u64, u64, i64, ctypes.c_uint32, ctypes.c_uint32, vp]
         _lib = L
     return _lib
 
@@ -82,6 +87,7 @@ class MoeConfig:
     renorm: bool = True             # weights renormalised over the k picks
     routed_scaling: float = 1.0     # factor on the routed weights
     swiglu_limit: Optional[float] = None   # clamped SwiGLU limit (routed experts), None = plain
+    wfmt: str = "nvfp4"             # weight format: "nvfp4" (quantised fp32 draws) | "mxfp4" (drawn directly)
 
     @property
     def variant_router(self) -> bool:
@@ -129,10 +135,10 @@ def deepseek_v3_router(T: int = 256) -> MoeConfig:
 
 def deepseek_v4_flash(T: int = 64) -> MoeConfig:
     """DeepSeek-V4-Flash routed layer at one rank's share of a 2-way split of each expert's
-    intermediate width: 256 experts, top 6, hidden 4096, intermediate 1024, sqrt-softplus
-    scores with a selection bias, SwiGLU clamped at 10, one shared expert."""
+    intermediate width: 256 experts, top 6, hidden 4096, intermediate 1024, MXFP4 weights,
+    sqrt-softplus scores with a selection bias, SwiGLU clamped at 10, one shared expert."""
     return MoeConfig(f"deepseek-v4-flash-t{T}", T=T, H=4096, I=1024, E=256, k=6, score="sqrt_softplus",
-                     shared=1, seed=421, bias_sigma=0.5, swiglu_limit=10.0)
+                     shared=1, seed=421, bias_sigma=0.5, swiglu_limit=10.0, wfmt="mxfp4")
 
 
 def all_configs():
@@ -171,6 +177,24 @@ def zipf_bias(cfg: MoeConfig) -> Optional[np.ndarray]:
     ranks = np.empty(cfg.E, dtype=np.int32)
     lib().synth_permutation(cfg.seed, STREAM_ZIPF, cfg.E, ranks.ctypes.data)
     return np.array([-cfg.zipf_s * math.log(int(r)) for r in ranks], dtype=np.float64)
+
+
+MX_SCALE_LO, MX_SCALE_SPAN = 117, 8
+_MX_PROJ = {"w1": 0, "w2": 1, "ws1": 2, "ws2": 3}
+
+
+def mxfp4_weights(cfg: MoeConfig, which: str, first: int, count: int):
+    """MXFP4 projection of experts first..first+count-1 in the boundary layout: codes
+    u8 [count][N][K/2] (element 2i in the low nibble), E8M0 scales u8 [count][N][K/32]."""
+    N, K = _proj_shape(cfg, which)
+    p = _MX_PROJ[which]
+    codes = np.empty(count * N * K // 2, np.uint8)
+    scales = np.empty(count * N * K // 32, np.uint8)
+    if codes.size:
+        lib().synth_bytes(cfg.seed, 20 + 2 * p, first * N * K // 2, codes.size, 0, 256, codes.ctypes.data)
+        lib().synth_bytes(cfg.seed, 21 + 2 * p, first * N * K // 32, scales.size, MX_SCALE_LO, MX_SCALE_SPAN,
+                          scales.ctypes.data)
+    return codes.reshape(count, N, K // 2), scales.reshape(count, N, K // 32)
 
 
 def router_bias(cfg: MoeConfig) -> Optional[np.ndarray]:

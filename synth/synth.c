@@ -83,3 +83,10 @@ void synth_logits(uint64_t seed, uint64_t stream, uint64_t offset, int32_t T, in
     out[i] = (float)(synth_normal(seed, stream, offset + (uint64_t)i) + b);
   }
 }
+
+/* n bytes: byte i = lo + (bits(seed, stream, offset + i) mod span) (span in 1..256). */
+void synth_bytes(uint64_t seed, uint64_t stream, uint64_t offset, int64_t n, uint32_t lo, uint32_t span,
+                 uint8_t* out) {
+  for (int64_t i = 0; i < n; ++i)
+    out[i] = (uint8_t)(lo + synth_bits(seed, stream, offset + (uint64_t)i) % span);
+}

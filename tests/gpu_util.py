@@ -81,7 +81,12 @@ class Case:
         self.ids_ref, self.w_ref = omoe.route(cfg, self.logits, o)
         self.tokens = np.arange(cfg.T, dtype=np.int32) if tokens is None else np.asarray(tokens, np.int32)
         need = sorted(set(self.ids_ref[self.tokens].reshape(-1).tolist()))
-        if weights == "oracle":
+        projs = ["w1", "w2"] + (["ws1", "ws2"] if cfg.shared else [])
+        if cfg.wfmt == "mxfp4":   # drawn directly in the boundary format: one set serves both sides
+            W = [tuple(synth.mxfp4_weights(cfg, w, 0, cfg.shared if w.startswith("ws") else cfg.E)) + (None,)
+                 for w in projs]
+            dev = [[up(Wi[0]), up(Wi[1]), None] for Wi in W]
+        elif weights == "oracle":
             W = [oracle_weights(cfg, w, need if w in ("w1", "w2") else None)
                  for w in (["w1", "w2"] + (["ws1", "ws2"] if cfg.shared else []))]
             dev = [[up(a) for a in Wi] for Wi in W]

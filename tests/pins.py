@@ -511,6 +511,76 @@ def pin_moe_clamp_routed_only(o):
     assert np.array_equal(out, ref)
 
 
+# ------------------------------------------------------------ MXFP4 weights
+
+def e8m0_table_torch() -> np.ndarray:
+    """E8M0 byte -> value via PyTorch's float8_e8m0fnu decoder (NaN for 0xFF)."""
+    b = torch.arange(256, dtype=torch.uint8).view(torch.float8_e8m0fnu)
+    return b.to(torch.float64).numpy()
+
+
+def decode_mxfp4(packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """[..., N, K/2] codes + [..., N, K/32] E8M0 scales -> FP64 [..., N, K]."""
+    e2 = e2m1_table()
+    lo = e2[packed & 15]
+    hi = e2[packed >> 4]
+    q = np.stack([lo, hi], axis=-1).reshape(*packed.shape[:-1], packed.shape[-1] * 2)
+    return q * np.repeat(e8m0_table_torch()[scales], 32, axis=-1)
+
+
+def random_mx_weights(rng, G, N, K):
+    """Raw MXFP4 codes and E8M0 scales drawn directly (scales 2^-10 .. 2^-3)."""
+    packed = rng.integers(0, 256, (G, N, K // 2), dtype=np.uint8)
+    scales = rng.integers(117, 125, (G, N, K // 32), dtype=np.uint8)
+    return packed, scales, None
+
+
+def pin_e8m0(o):
+    ref = e8m0_table_torch()
+    for b in range(256):
+        v = o.e8m0(b)
+        assert (math.isnan(v) and math.isnan(ref[b])) or v == ref[b], (b, v, ref[b])
+
+
+def pin_mx_weight_decode(o):
+    rng = np.random.default_rng(61)
+    packed, scales, _ = random_mx_weights(rng, 1, 8, 96)
+    ref = decode_mxfp4(packed[0], scales[0])
+    for n in range(8):
+        for k in range(96):
+            assert o.weight_mx(packed[0], scales[0], n, k) == ref[n, k], (n, k)
+
+
+def pin_mx_ffn_textbook(o):
+    """MXFP4 expert MLP = the textbook SwiGLU MLP on the library-decoded weights."""
+    rng = np.random.default_rng(67)
+    H, I = 64, 64
+    W1 = random_mx_weights(rng, 2, 2 * I, H)
+    W2 = random_mx_weights(rng, 2, H, I)
+    x = rng.standard_normal(H)
+    for g in range(2):
+        y = o.expert_ffn(W1, W2, g, x)
+        D1 = decode_mxfp4(W1[0][g], W1[1][g])
+        D2 = decode_mxfp4(W2[0][g], W2[1][g])
+        ref = D2 @ (silu(D1[:I] @ x) * (D1[I:] @ x))
+        assert np.allclose(y, ref, rtol=1e-12, atol=1e-15 * np.abs(ref).max())
+
+
+def pin_mx_unit_scales_equal_nvfp4(o):
+    """MXFP4 with every scale 2^0 is the NVFP4 tensor with every block scale 1.0 and
+    global scale 1.0: identical expert outputs."""
+    rng = np.random.default_rng(71)
+    H, I = 64, 32
+    p1 = rng.integers(0, 256, (1, 2 * I, H // 2), dtype=np.uint8)
+    p2 = rng.integers(0, 256, (1, H, I // 2), dtype=np.uint8)
+    mx1 = (p1, np.full((1, 2 * I, H // 32), 127, np.uint8), None)
+    mx2 = (p2, np.full((1, H, I // 32), 127, np.uint8), None)
+    nv1 = (p1, np.full((1, 2 * I, H // 16), 0x38, np.uint8), np.ones(1, np.float32))
+    nv2 = (p2, np.full((1, H, I // 16), 0x38, np.uint8), np.ones(1, np.float32))
+    x = rng.standard_normal(H)
+    assert np.array_equal(o.expert_ffn(mx1, mx2, 0, x), o.expert_ffn(nv1, nv2, 0, x))
+
+
 def moe_small(rng, T=12, H=32, I=16, E=6, k=2, shared=0):
     W1 = random_weights(rng, E, 2 * I, H)
     W2 = random_weights(rng, E, H, I)

@@ -74,6 +74,8 @@ def plan_rc(d):
     (dict(swiglu_limit=-1.0), m.MOE_ERR_SHAPE),
     (dict(swiglu_limit=float("nan")), m.MOE_ERR_SHAPE),
     (dict(score=3), m.MOE_ERR_ENUM),
+    (dict(weights="mxfp4"), m.MOE_OK),
+    (dict(weights=2), m.MOE_ERR_ENUM),
 ])
 def test_plan_validation(kw, code):
     assert plan_rc(desc(**kw)) == code
@@ -182,3 +184,21 @@ def test_validate_weights_host():
 def test_strerror_covers_every_code():
     for code in range(-8, 1):
         assert m.moe_strerror(code) and m.moe_strerror(code) != "unknown error"
+
+
+def test_validate_mxfp4_weights_host():
+    d = desc(weights="mxfp4")
+    G, N, K = 8, 256, 256
+    packed = np.zeros((G, N, K // 2), np.uint8)
+    scales = np.full((G, N, K // 32), 120, np.uint8)
+    t = m.nvfp4_tensor(packed.ctypes.data, scales.ctypes.data, None)     # no global scale
+    assert m.moe_validate_weights_host(d, t, 0) == m.MOE_OK
+    scales[2, 5, 1] = 120 - 17                         # the widest exact span
+    assert m.moe_validate_weights_host(d, t, 0) == m.MOE_OK
+    scales[2, 5, 1] = 120 - 18
+    assert m.moe_validate_weights_host(d, t, 0) == m.MOE_ERR_WEIGHT
+    scales[2, 5, 1] = 0xFF                             # E8M0 NaN
+    assert m.moe_validate_weights_host(d, t, 0) == m.MOE_ERR_WEIGHT
+    scales[2, 5, 1] = 120
+    t_nv = m.nvfp4_tensor(packed.ctypes.data, scales.ctypes.data, None)
+    assert m.moe_validate_weights_host(desc(), t_nv, 0) == m.MOE_ERR_NULL   # NVFP4 needs its global scale

@@ -72,6 +72,12 @@ VARIANTS = [
     synth.MoeConfig("v-w4a4-wide-e", T=130, H=256, I=128, E=600, k=8, act="nvfp4", score="sqrt_softplus",
                     seed=25, bias_sigma=0.2, n_group=6, topk_group=4),
     synth.deepseek_v4_flash(8),
+    # MXFP4 weights (E8M0 per 32, no global scale): decode, prefill with a shared expert, W4A4
+    synth.MoeConfig("mx-decode", T=8, H=256, I=128, E=16, k=4, seed=41, wfmt="mxfp4"),
+    synth.MoeConfig("mx-prefill-shared", T=300, H=512, I=256, E=8, k=2, shared=1, seed=42, wfmt="mxfp4"),
+    # (the output is bf16, so max|d| >= 2^-9 max|out| for any exact kernel: inputs keep
+    # max|out| < 10 RMS for the 2e-2 RMS bound to be reachable; 6.97 here)
+    synth.MoeConfig("mx-w4a4", T=100, H=512, I=256, E=8, k=2, act="nvfp4", seed=45, wfmt="mxfp4"),
 ]
 
 

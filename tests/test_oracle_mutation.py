@@ -15,8 +15,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "oracle.c")
 
 MUTANTS = {
-    "nibble_order": ("uint32_t nib = (k & 1) ? (byte >> 4) : (byte & 15u);",
-                     "uint32_t nib = (k & 1) ? (byte & 15u) : (byte >> 4);"),
+    "nibble_order": ("return (k & 1) ? (byte >> 4) : (byte & 15u);",
+                     "return (k & 1) ? (byte & 15u) : (byte >> 4);"),
     "scale_index": ("scales[(size_t)n * (K / 16) + k / 16]", "scales[(size_t)n * (K / 16) + (k + 1) / 16 % (K / 16)]"),
     "e4m3_bias": ("ldexp(1.0 + (double)m / 8.0, (int)e - 7)", "ldexp(1.0 + (double)m / 8.0, (int)e - 8)"),
     "e4m3_subnormal": ("ldexp((double)m, -9)", "ldexp((double)m, -10)"),
@@ -25,8 +25,12 @@ MUTANTS = {
     "sigmoid_sign": ("v[j] = 1.0 / (1.0 + exp(-lj));", "v[j] = 1.0 / (1.0 + exp(lj));"),
     "perm_tokens_descending": ("for (int e = 0; e < E; ++e)\n    for (int t = 0; t < T; ++t)",
                                "for (int e = 0; e < E; ++e)\n    for (int t = T - 1; t >= 0; --t)"),
-    "gate_up_swapped": ("gi += orc_weight(p1, s1, P->w1_gs[g], H, i, k) * x[k];",
-                        "gi += orc_weight(p1, s1, P->w1_gs[g], H, I + i, k) * x[k];"),
+    "gate_up_swapped": ("gi += proj_weight(P, 0, g, 2 * I, H, i, k) * x[k];",
+                        "gi += proj_weight(P, 0, g, 2 * I, H, I + i, k) * x[k];"),
+    "e8m0_bias_128": ("return ldexp(1.0, (int)byte - 127);", "return ldexp(1.0, (int)byte - 128);"),
+    "mx_block_16": ("orc_e8m0(scales[(size_t)n * (K / 32) + k / 32])",
+                    "orc_e8m0(scales[(size_t)n * (K / 32) + k / 16 % (K / 32)])"),
+    "mx_expert_stride_nvfp4": ("const int bs = P->mx ? 32 : 16;", "const int bs = 16;"),
     "silu_dropped": ("h[i] = gi / (1.0 + exp(-gi)) * ui;", "h[i] = gi * ui;"),
     "combine_unweighted": ("o[n] += w[(size_t)t * k + j] * y[n];", "o[n] += y[n] / k;"),
     "shared_weight_half": ("      for (int n = 0; n < H; ++n) o[n] += y[n];",
