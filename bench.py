@@ -34,6 +34,7 @@ summaries in profiles/ are made from rocprofv3 output by this script:
 
     python bench.py --trace-summary RESULTS_DB --title T --command C
     python bench.py --traffic-summary FETCH_CSV WRITE_CSV --workload W --title T --command C
+    python bench.py --counter-summary PMC_CSV [PMC_CSV ...] --title T --command C
 """
 from __future__ import annotations
 
@@ -300,6 +301,50 @@ def traffic_summary(fetch_csv, write_csv, workload_name, title, command):
     return "\n".join(out)
 
 
+def counter_summary(csvs, title, command):
+    """Per-kernel means of every counter in one or more rocprofv3 --pmc runs (values summed
+    over a dispatch's instances, then averaged over the kernel's dispatches of one grid),
+    plus the derived figures the dequant route is judged by: VALU instructions per MFMA,
+    MFMA-pipe busy share (SQ_VALU_MFMA_BUSY_CYCLES over 1024 SIMDs x GRBM_GUI_ACTIVE / 8
+    XCDs), the clock the kernel ran at (GRBM_GUI_ACTIVE / 8 / duration) and LDS
+    instructions per MFMA."""
+    import csv
+    rows = {}
+    for path in csvs:
+        per = {}
+        for r in csv.DictReader(open(path)):
+            name = r["Kernel_Name"].replace("nvmoe::", "").replace("void ", "").split("(")[0]
+            key = (name, int(r["Grid_Size"]))
+            d = (path, int(r["Dispatch_Id"]))
+            c = r["Counter_Name"]
+            e = per.setdefault(d, {"key": key, "dur": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+            e[c] = e.get(c, 0.0) + float(r["Counter_Value"])
+        for d, e in per.items():
+            agg = rows.setdefault(e["key"], {})
+            for c, v in e.items():
+                if c != "key":
+                    agg.setdefault(c, []).append(v)
+    out = [f"# {title}", "", "Commands (on one MI355X, from the repository root):", "", "```", command, "```", "",
+           "| kernel | stage | grid | dispatches | counter means per dispatch | VALU/MFMA | LDS/MFMA | MFMA busy | clock GHz |",
+           "|---|---|---|---|---|---|---|---|---|"]
+    for (n, g), agg in sorted(rows.items(), key=lambda kv: (kernel_stage(kv[0][0]), kv[0])):
+        st = kernel_stage(n)
+        if st not in ("gate_up", "down"):
+            continue
+        m = {c: sum(v) / len(v) for c, v in agg.items()}
+        ndisp = max(len(v) for c, v in agg.items() if c != "dur")
+        mf = m.get("SQ_INSTS_MFMA")
+        ratio = lambda c: f"{m[c] / mf:.2f}" if mf and c in m else "-"
+        gui = m.get("GRBM_GUI_ACTIVE")
+        busy = (f"{m['SQ_VALU_MFMA_BUSY_CYCLES'] / (1024 * gui / 8):.3f}"
+                if gui and "SQ_VALU_MFMA_BUSY_CYCLES" in m else "-")
+        clk = f"{gui / 8 / m['dur']:.2f}" if gui and m.get("dur") else "-"
+        cs = ", ".join(f"{c.replace('SQ_', '')} {v:.4g}" for c, v in sorted(m.items()) if c != "dur")
+        out.append(f"| `{n}` | {st} | {g} | {ndisp} | {cs} | {ratio('SQ_INSTS_VALU')} | {ratio('SQ_INSTS_LDS')} | "
+                   f"{busy} | {clk} |")
+    return "\n".join(out)
+
+
 def traffic_record(workload_name):
     """The measured gate/up traffic per launch for this workload if its record matches the
     kernel sources built now, else None."""
@@ -329,11 +374,16 @@ def main():
     ap.add_argument("--trace-summary", metavar="RESULTS_DB", help="summarise a rocprofv3 kernel trace and exit")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarise FETCH_SIZE / WRITE_SIZE counter runs and exit")
+    ap.add_argument("--counter-summary", nargs="+", metavar="PMC_CSV",
+                    help="tabulate the counters of rocprofv3 --pmc runs per GEMM kernel and exit")
     ap.add_argument("--title", default="")
     ap.add_argument("--command", default="")
     args = ap.parse_args()
     if args.trace_summary:
         print(trace_summary(args.trace_summary, args.title, args.command))
+        return
+    if args.counter_summary:
+        print(counter_summary(args.counter_summary, args.title, args.command))
         return
     if args.traffic_summary:
         print(traffic_summary(args.traffic_summary[0], args.traffic_summary[1], args.workload, args.title,
