@@ -9,7 +9,7 @@
 namespace nvmoe {
 
 constexpr int DECODE_TILE_ROWS = 16;
-constexpr int PREFILL_TILE_ROWS = 128;
+constexpr int PREFILL_TILE_ROWS = 96;
 
 struct RouteArgs {
   const float* logits;   // [T][E]
