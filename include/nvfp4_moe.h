@@ -235,7 +235,8 @@ int moe_pack_router_bias(const moe_plan_t* plan, const float* bias, void* packed
  * SwiGLU; h = silu(g*gs)*(u*gs) is stored as fp16 with one power-of-two exponent
  * per 16 columns (the block's largest |h| scaled into [2^14, 2^15)), which the
  * down GEMM brings to a common per-row exponent exactly before its fp16 MFMAs;
- * expert outputs stay fp32.
+ * expert outputs are stored the same way (fp16 with a power-of-two exponent per 16
+ * columns) and summed by the combine in fp32.
  * ([megamoe] README "MoE kernel": fused SwiGLU grouped GEMM epilogue in
  * registers; [b12x] "What's in here": FP32 internal, BF16 boundary;
  * [vllm.cpp] "Device-resident decode campaign": device routing ids feed the

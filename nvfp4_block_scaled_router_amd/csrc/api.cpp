@@ -48,7 +48,7 @@ struct moe_plan {
   ProjLayout w1, w2;
   size_t off_w1f, off_w1s, off_w1g, off_w2f, off_w2s, off_w2g, off_bias, packed_bytes;
   size_t ws_ids, ws_w, ws_counts, ws_offsets, ws_perm, ws_inv, ws_tok, ws_tgrp, ws_trow, ws_tcnt, ws_plan;
-  size_t ws_xq, ws_xs, ws_xg, ws_x16, ws_h, ws_hexp, ws_hmin, ws_y, ws_bytes;
+  size_t ws_xq, ws_xs, ws_xg, ws_x16, ws_h, ws_hexp, ws_hmin, ws_y, ws_yexp, ws_bytes;
   int max_tiles;
 };
 
@@ -165,7 +165,8 @@ int moe_plan(const moe_desc* desc, moe_plan_t** plan, size_t* packed_bytes, size
   p->ws_h = o; o = align_up(o + 2 * rows * I);        // h16
   p->ws_hexp = o; o = align_up(o + rows * (I / 16));  // per-16-column h exponents
   p->ws_hmin = o; o = align_up(o + 4 * rows);         // per-row minimum h exponent
-  p->ws_y = o; o = align_up(o + 4 * rows * H);
+  p->ws_y = o; o = align_up(o + 2 * rows * H);         // y16
+  p->ws_yexp = o; o = align_up(o + rows * (H / 16));  // per-16-column y exponents
   p->ws_bytes = o;
   if (packed_bytes) *packed_bytes = p->packed_bytes;
   if (workspace_bytes) *workspace_bytes = p->ws_bytes;
@@ -386,12 +387,14 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
   g2.K = I;
   g2.x = g1.out;
   g2.out = nullptr;
-  g2.yout = (float*)(ws + plan->ws_y);
+  g2.yout = (uint16_t*)(ws + plan->ws_y);
+  g2.yexp = (int8_t*)(ws + plan->ws_yexp);
   e = launch_gemm(GEMM_DOWN, regime, max_tiles, est_tiles, g2, s, stage_events(ev, MOE_STAGE_DOWN));
   if (e != hipSuccess) return (int)e;
 
   CombineArgs c;
-  c.y = (const float*)(ws + plan->ws_y);
+  c.y = (const uint16_t*)(ws + plan->ws_y);
+  c.yexp = (const int8_t*)(ws + plan->ws_yexp);
   c.w = ra.w;
   c.inv = pa.inv;
   c.T = T;

@@ -157,10 +157,24 @@ __device__ __forceinline__ int row_exp_min4(const int8_t* erow, int nblk, int lg
 // of a block with exponent e to the row's common scale 2^P, d = P - e.
 __device__ __forceinline__ _Float16 h_factor(int d) { return (_Float16)__builtin_ldexpf(1.0f, d); }
 
+// Down epilogue for one 16-feature x 16-token D tile: y = acc * sc for the features
+// q*16 .. +15 of token row `row` (lane: 4 of them), stored as fp16 scaled by 2^e with e
+// chosen on the block's largest |y| (shared by the row's 4 lanes through two lane swaps,
+// as for h) and recorded in yexp; half the bytes of fp32 y for the combine to read, with
+// an 11-bit significand. All 4 lanes of a row must be active together.
 __device__ __forceinline__ void epilogue_single(const GemmArgs& a, const f32x4& acc, float sc, int row, int q) {
   const int lg = (threadIdx.x & (WAVE - 1)) >> 4;
-  float* p = a.yout + (size_t)row * a.N + q * 16 + 4 * lg;
-  *(f32x4*)p = acc * sc;
+  const f32x4 v = acc * sc;
+  float mx = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const int e = min(max(15 - __builtin_amdgcn_frexp_expf(mx), -H_EXP_MAX), H_EXP_MAX);
+  const uint32_t q0 = __builtin_bit_cast(uint16_t, (_Float16)__builtin_ldexpf(v.x, e));
+  const uint32_t q1 = __builtin_bit_cast(uint16_t, (_Float16)__builtin_ldexpf(v.y, e));
+  const uint32_t q2 = __builtin_bit_cast(uint16_t, (_Float16)__builtin_ldexpf(v.z, e));
+  const uint32_t q3 = __builtin_bit_cast(uint16_t, (_Float16)__builtin_ldexpf(v.w, e));
+  *(u32x2*)(a.yout + (size_t)row * a.N + q * 16 + 4 * lg) = u32x2{q0 | (q1 << 16), q2 | (q3 << 16)};
+  if (lg == 0) a.yexp[(size_t)row * (a.N / 16) + q] = (int8_t)e;
 }
 
 // ------------------------------------------------------------------ decode GEMM
@@ -726,14 +740,21 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
     s_w[threadIdx.x] = a.w[t * a.k + threadIdx.x];
   }
   __syncthreads();
-  const int c = blockIdx.y * (COMBINE_COLS / 4) + threadIdx.x;   // float4 column index
+  const int c = blockIdx.y * (COMBINE_COLS / 4) + threadIdx.x;   // 4-column group index
   if (c >= a.H / 4) return;
+  // row r's columns 4c .. 4c+3: fp16 values and their block's exponent, exactly in fp32
+  auto load = [&](int r) {
+    const u32x2 q = *(const u32x2*)(a.y + (size_t)r * a.H + c * 4);
+    const int e = a.yexp[(size_t)r * (a.H / 16) + (c >> 2)];
+    auto f = [&](uint32_t b) { return __builtin_ldexpf((float)__builtin_bit_cast(_Float16, (uint16_t)b), -e); };
+    return f32x4{f(q.x & 0xFFFFu), f(q.x >> 16), f(q.y & 0xFFFFu), f(q.y >> 16)};
+  };
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   int j = 0;
   for (; j + 4 <= a.k; j += 4) {
     f32x4 v[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) v[q] = *(const f32x4*)(a.y + (size_t)s_inv[j + q] * a.H + c * 4);
+    for (int q = 0; q < 4; ++q) v[q] = load(s_inv[j + q]);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const float wj = s_w[j + q];
@@ -744,14 +765,14 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
     }
   }
   for (; j < a.k; ++j) {
-    const f32x4 v = *(const f32x4*)(a.y + (size_t)s_inv[j] * a.H + c * 4);
+    const f32x4 v = load(s_inv[j]);
     const float wj = s_w[j];
     acc.x = __builtin_fmaf(wj, v.x, acc.x);
     acc.y = __builtin_fmaf(wj, v.y, acc.y);
     acc.z = __builtin_fmaf(wj, v.z, acc.z);
     acc.w = __builtin_fmaf(wj, v.w, acc.w);
   }
-  for (int sh = 0; sh < a.S; ++sh) acc += *(const f32x4*)(a.y + (size_t)(rows + sh * a.T + t) * a.H + c * 4);
+  for (int sh = 0; sh < a.S; ++sh) acc += load(rows + sh * a.T + t);
   *(u32x2*)(a.out + (size_t)t * a.H + c * 4) =
       u32x2{f32_to_bf16_rne(acc.x) | (f32_to_bf16_rne(acc.y) << 16),
             f32_to_bf16_rne(acc.z) | (f32_to_bf16_rne(acc.w) << 16)};

@@ -109,7 +109,10 @@ struct GemmArgs {
   uint16_t* out;           // gate_up: h16
   int8_t* hexp;            // [rows][I/16]
   int32_t* hmin;           // [rows] or nullptr
-  float* yout;             // down: y fp32 [rows][N]
+  // down: y as fp16 [rows][N] with one exponent per row and 16-column block, the
+  // block's largest |y| scaled into [2^14, 2^15): y = y16 * 2^-yexp
+  uint16_t* yout;
+  int8_t* yexp;            // [rows][N/16]
   // clamped SwiGLU for groups g < clamp_groups (0: none): silu(min(g, L)) * clamp(u, -L, L)
   int clamp_groups;
   float swiglu_limit;
@@ -133,7 +136,8 @@ hipError_t launch_gemm(GemmMode mode, GemmRegime regime, int max_tiles, int est_
                        hipStream_t s, const LaunchEvents& ev = LaunchEvents());
 
 struct CombineArgs {
-  const float* y;          // fp32 [rows_total][H] expert outputs
+  const uint16_t* y;       // fp16 [rows_total][H] expert outputs, scaled per 16-column block
+  const int8_t* yexp;      // [rows_total][H/16]: y = y16 * 2^-yexp
   const float* w;          // [T][k]
   const int32_t* inv;      // [T*k]
   int T, H, k, S;

@@ -129,7 +129,8 @@ def test_plan_sizes_cover_the_layout():
     weights = 257 * 3 * 2048 * 7168
     assert weights * 0.5625 <= pb <= weights * 0.5625 * 1.01
     rows = 8192 * 9
-    assert wb >= rows * (2048 * 2 + 2048 // 16 + 4 + 7168 * 4)  # h16, its block exponents and row minimum, fp32 outputs
+    # h16 with its block exponents and row minimum, y16 with its block exponents
+    assert wb >= rows * (2048 * 2 + 2048 // 16 + 4 + 7168 * 2 + 7168 // 16)
 
 
 def test_run_rejects_before_enqueue():
