@@ -154,8 +154,9 @@ int moe_plan(const moe_desc* desc, moe_plan_t** plan, size_t* packed_bytes, size
   p->ws_perm = o; o = align_up(o + 4 * routed);
   p->ws_inv = o; o = align_up(o + 4 * routed);
   p->ws_tok = o; o = align_up(o + 4 * rows);
-  p->ws_tgrp = o; o = align_up(o + 4 * (size_t)p->max_tiles);
-  p->ws_trow = o; o = align_up(o + 4 * (size_t)p->max_tiles);
+  // twice the bound: a second-list launch reads ahead of its count from anywhere in the list
+  p->ws_tgrp = o; o = align_up(o + 8 * (size_t)p->max_tiles);
+  p->ws_trow = o; o = align_up(o + 8 * (size_t)p->max_tiles);
   p->ws_tcnt = o; o = align_up(o + 16);
   p->ws_plan = o; o = align_up(o + 4 * plan_scratch_ints(Tm, k, E));
   p->ws_xq = o; o = align_up(o + (desc->act_format == MOE_ACT_NVFP4_ROWQ ? (size_t)Tm * H / 2 : 0));
@@ -336,6 +337,10 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
   pa.k = k;
   pa.G = plan->G;
   pa.tile_rows = M;
+  // prefill batches averaging at most 64 rows per expert: experts with few rows (skewed
+  // routing) go to the decode GEMM through a second tile list
+  const bool split = !decode && (long)T * k <= 64L * E;
+  pa.cold_rows = split ? DECODE_TILE_ROWS : 0;
   pa.counts = (int32_t*)(ws + plan->ws_counts);
   pa.offsets = (int32_t*)(ws + plan->ws_offsets);
   pa.perm = (int32_t*)(ws + plan->ws_perm);
@@ -376,7 +381,20 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
   g1.hmin = decode ? nullptr : pa.hmin;
   g1.clamp_groups = d.swiglu_clamp ? E : 0;      // routed experts only
   g1.swiglu_limit = d.swiglu_limit;
-  e = launch_gemm(gu_mode, regime, max_tiles, est_tiles, g1, s, stage_events(ev, MOE_STAGE_GATE_UP));
+  // second-list (cold) launches: the decode GEMM over list 2, at most one tile per group
+  const int cold_tiles = split ? std::min(plan->G, T * k + S) : 0;
+  auto second = [&](GemmArgs g) {
+    g.tile_first = pa.tile_count;
+    g.tile_count = pa.tile_count + 1;
+    return g;
+  };
+  {
+    const LaunchEvents le = stage_events(ev, MOE_STAGE_GATE_UP);
+    e = launch_gemm(gu_mode, regime, max_tiles, est_tiles, g1, s, split ? LaunchEvents{le.start, nullptr} : le);
+    if (e == hipSuccess && split)
+      e = launch_gemm(gu_mode, REGIME_DECODE_KSPLIT, cold_tiles, cold_tiles, second(g1), s,
+                      LaunchEvents{nullptr, le.stop});
+  }
   if (e != hipSuccess) return (int)e;
 
   GemmArgs g2 = g1;
@@ -389,7 +407,13 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
   g2.out = nullptr;
   g2.yout = (uint16_t*)(ws + plan->ws_y);
   g2.yexp = (int8_t*)(ws + plan->ws_yexp);
-  e = launch_gemm(GEMM_DOWN, regime, max_tiles, est_tiles, g2, s, stage_events(ev, MOE_STAGE_DOWN));
+  {
+    const LaunchEvents le = stage_events(ev, MOE_STAGE_DOWN);
+    e = launch_gemm(GEMM_DOWN, regime, max_tiles, est_tiles, g2, s, split ? LaunchEvents{le.start, nullptr} : le);
+    if (e == hipSuccess && split)
+      e = launch_gemm(GEMM_DOWN, REGIME_DECODE_KSPLIT, cold_tiles, cold_tiles, second(g2), s,
+                      LaunchEvents{nullptr, le.stop});
+  }
   if (e != hipSuccess) return (int)e;
 
   CombineArgs c;

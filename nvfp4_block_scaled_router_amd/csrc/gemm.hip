@@ -191,10 +191,12 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs a) {
   constexpr bool F16 = MODE != GEMM_GATEUP_BF16;           // fp16 MFMA (bf16 x: bf16 MFMA)
   const int slot = blockIdx.y;
   // the slot's entries are read together with the count (slots past it hold stale values
-  // that are never used), saving one dependent round trip before the weight loads
+  // that are never used; the tile arrays have room for any grid), saving one dependent
+  // round trip before the weight loads; a second-list launch starts after the first list
+  const int first = a.tile_first ? a.tile_first[0] : 0;
   const int ntiles = a.tile_count[0];
-  const int g = a.tile_group[slot];
-  const int row0 = a.tile_row0[slot];
+  const int g = a.tile_group[first + slot];
+  const int row0 = a.tile_row0[first + slot];
   if (slot >= ntiles) return;
   const ProjLayout L = proj_layout(a.N, a.K);
   const int NW = blockDim.x >> 6;

@@ -30,6 +30,8 @@ struct PlanArgs {
   const int32_t* ids;    // [T][k]
   int T, E, k, G;        // G = E + shared groups
   int tile_rows;         // M of the GEMM tiles
+  int cold_rows;         // > 0: groups with 1..cold_rows rows get one DECODE_TILE_ROWS tile in a
+                         // second list (for the decode GEMM) after the first list's tiles
   int32_t* counts;       // [G]
   int32_t* offsets;      // [G+1]
   int32_t* perm;         // [T*k]
@@ -37,7 +39,7 @@ struct PlanArgs {
   int32_t* tok;          // [T*k + S*T] token of each row
   int32_t* tile_group;   // [max tiles]
   int32_t* tile_row0;    // [max tiles]
-  int32_t* tile_count;   // [1]
+  int32_t* tile_count;   // [2]: tiles of list 1, of list 2
   int32_t* hmin;         // [T*k + S*T] per-row minimum h exponent, set to H_EXP_INIT here
   int32_t* counts_user;  // optional [E]
   int32_t* offsets_user; // optional [E+1]
@@ -97,6 +99,7 @@ struct GemmArgs {
   const int32_t* tile_group;
   const int32_t* tile_row0;
   const int32_t* tile_count;
+  const int32_t* tile_first; // nullptr, or the index of the launch's first tile (list 2: &tile_count[0])
   const int32_t* offsets;  // [G+1] row ranges of the groups
   // h = silu(g) u between the GEMMs, as h16 [rows][I] fp16 (columns permuted inside each
   // 128-column chunk, see h_pos) with, per row and 16-column block b, an exponent

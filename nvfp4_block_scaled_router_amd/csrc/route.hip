@@ -197,6 +197,37 @@ __global__ __launch_bounds__(256) void route_general_kernel(RouteArgs a) {
   route_token_general<EPL>(a, t, nullptr);
 }
 
+// Tile counts per group before the scans: list 1 takes groups with more than cold rows in
+// ceil(c / M)-row tiles, list 2 groups with 1 .. cold rows in one DECODE_TILE_ROWS tile
+// (cold = 0: every group in list 1).
+__device__ __forceinline__ void tile_counts(int c, int M, int cold, int* tl, int* ct) {
+  *tl = c > cold ? (c + M - 1) / M : 0;
+  *ct = c > 0 && c <= cold ? 1 : 0;
+}
+
+// The tile lists from the scanned offsets (off), list-1 tile starts (tl) and list-2 slots
+// (ct): list 1 in slots 0 .. tl[G]-1, list 2 right after it; tile_count = {tl[G], ct[G]}.
+__device__ __forceinline__ void write_tiles(const PlanArgs& a, const int* cnt, const int* off, const int* tl,
+                                            const int* ct, int G, int tid, int nthr) {
+  const int M = a.tile_rows;
+  for (int g = tid; g < G; g += nthr) {
+    if (cnt[g] > a.cold_rows) {
+      const int n = (cnt[g] + M - 1) / M;
+      for (int q = 0; q < n; ++q) {
+        a.tile_group[tl[g] + q] = g;
+        a.tile_row0[tl[g] + q] = off[g] + q * M;
+      }
+    } else if (cnt[g] > 0) {
+      a.tile_group[tl[G] + ct[g]] = g;
+      a.tile_row0[tl[G] + ct[g]] = off[g];
+    }
+  }
+  if (tid == 0) {
+    a.tile_count[0] = tl[G];
+    a.tile_count[1] = ct[G];
+  }
+}
+
 // Small batches (T <= 64, T*k <= 4096): routing, counts, offsets, permutation and tile
 // list in one 1024-thread workgroup, everything in LDS. 64 DPP rows route up to 64 tokens
 // at once (E <= 256; wider expert sets use one wave per token); one wave runs the two
@@ -211,8 +242,9 @@ __global__ __launch_bounds__(1024) void plan_small_kernel(RouteArgs r, PlanArgs 
   int* s_ids = lds;                          // [rows]
   int* cnt = s_ids + rows;                   // [G]
   int* off = cnt + G;                        // [G+1] row offsets
-  int* tl = off + G + 1;                     // [G+1] tile starts
-  uint32_t* bits = (uint32_t*)(tl + G + 1);  // [E][2] token bitmaps
+  int* tl = off + G + 1;                     // [G+1] list-1 tile starts
+  int* ct = tl + G + 1;                      // [G+1] list-2 slots
+  uint32_t* bits = (uint32_t*)(ct + G + 1);  // [E][2] token bitmaps
 
   for (int g = tid; g < G; g += nthr) cnt[g] = g < E ? 0 : T;
   for (int i = tid; i < 2 * E; i += nthr) bits[i] = 0u;
@@ -235,9 +267,10 @@ __global__ __launch_bounds__(1024) void plan_small_kernel(RouteArgs r, PlanArgs 
   if (tid < 64) {
     for (int g = tid; g < G; g += 64) {
       off[g] = cnt[g];
-      tl[g] = (cnt[g] + M - 1) / M;
+      tile_counts(cnt[g], M, a.cold_rows, &tl[g], &ct[g]);
     }
     wave_dual_scan(off, tl, G);   // same wave wrote the inputs: no barrier needed
+    wave_scan(ct, G);
   }
   __syncthreads();
   for (int i = tid; i < rows; i += nthr) {
@@ -261,14 +294,7 @@ __global__ __launch_bounds__(1024) void plan_small_kernel(RouteArgs r, PlanArgs 
     if (g <= E && a.offsets_user) a.offsets_user[g] = off[g];
     if (g < E && a.counts_user) a.counts_user[g] = cnt[g];
   }
-  for (int g = tid; g < G; g += nthr) {
-    const int n = (cnt[g] + M - 1) / M;
-    for (int q = 0; q < n; ++q) {
-      a.tile_group[tl[g] + q] = g;
-      a.tile_row0[tl[g] + q] = off[g] + q * M;
-    }
-  }
-  if (tid == 0) a.tile_count[0] = tl[G];
+  write_tiles(a, cnt, off, tl, ct, G, tid, nthr);
 }
 
 // ------------------------------------------------------------------------------
@@ -313,6 +339,7 @@ __global__ __launch_bounds__(1024) void plan_scan_kernel(PlanArgs a, int32_t* bl
   int* cnt = sh;               // [G]
   int* off = cnt + G;          // [G+1]
   int* tl = off + G + 1;       // [G+1]
+  int* ct = tl + G + 1;        // [G+1]
   // per expert: running base over blocks (block_counts -> exclusive prefix in place)
   for (int e = tid; e < G; e += blockDim.x) {
     if (e < E) {
@@ -327,10 +354,13 @@ __global__ __launch_bounds__(1024) void plan_scan_kernel(PlanArgs a, int32_t* bl
       cnt[e] = T;
     }
     off[e] = cnt[e];
-    tl[e] = (cnt[e] + M - 1) / M;
+    tile_counts(cnt[e], M, a.cold_rows, &tl[e], &ct[e]);
   }
   __syncthreads();
-  if (tid < 64) wave_dual_scan(off, tl, G);
+  if (tid < 64) {
+    wave_dual_scan(off, tl, G);
+    wave_scan(ct, G);
+  }
   __syncthreads();
   for (int g = tid; g <= G; g += blockDim.x) {
     a.offsets[g] = off[g];
@@ -338,14 +368,7 @@ __global__ __launch_bounds__(1024) void plan_scan_kernel(PlanArgs a, int32_t* bl
     if (g <= E && a.offsets_user) a.offsets_user[g] = off[g];
     if (g < E && a.counts_user) a.counts_user[g] = cnt[g];
   }
-  for (int g = tid; g < G; g += blockDim.x) {
-    const int n = (cnt[g] + M - 1) / M;
-    for (int q = 0; q < n; ++q) {
-      a.tile_group[tl[g] + q] = g;
-      a.tile_row0[tl[g] + q] = off[g] + q * M;
-    }
-  }
-  if (tid == 0) a.tile_count[0] = tl[G];
+  write_tiles(a, cnt, off, tl, ct, G, tid, blockDim.x);
 }
 
 __global__ __launch_bounds__(256) void plan_scatter_kernel(PlanArgs a, const int32_t* local_rank,
@@ -372,7 +395,7 @@ size_t plan_scratch_ints(int T, int k, int E) {
 }
 
 static size_t plan_small_lds_bytes(int rows, int E, int G) {
-  return sizeof(int) * ((size_t)rows + G + 2 * ((size_t)G + 1) + 2 * (size_t)E);
+  return sizeof(int) * ((size_t)rows + G + 3 * ((size_t)G + 1) + 2 * (size_t)E);
 }
 
 bool plan_small_ok(int T, int k) { return T <= 64 && T * k <= 4096; }
@@ -396,7 +419,7 @@ static hipError_t launch_route_plan_t(const RouteArgs& r, const PlanArgs& p, int
   int32_t* block_counts = scratch + (size_t)p.T * p.k;
   const size_t count_lds = sizeof(uint32_t) * (size_t)p.E * (PLAN_BLOCK / 32);
   hipLaunchKernelGGL(plan_count_kernel, dim3(nb), dim3(PLAN_BLOCK), count_lds, s, p, local_rank, block_counts);
-  hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(1024), sizeof(int) * (3 * (size_t)p.G + 2), s, p, block_counts,
+  hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(1024), sizeof(int) * (4 * (size_t)p.G + 3), s, p, block_counts,
                      nb);
   const int n = p.T * p.k + p.T * (p.G - p.E);
   hipLaunchKernelGGL(plan_scatter_kernel, dim3((n + 255) / 256), dim3(256), 0, s, p, local_rank, block_counts);

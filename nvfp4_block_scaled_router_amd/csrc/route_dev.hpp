@@ -265,4 +265,20 @@ __device__ __forceinline__ void wave_dual_scan(int* a, int* b, int n) {
   }
 }
 
+// Executed by one whole wave: exclusive scan of a[0..n) in LDS (in place), total in a[n].
+__device__ __forceinline__ void wave_scan(int* a, int n) {
+  const int lane = threadIdx.x & 63;
+  const int seg = (n + 63) / 64, i0 = lane * seg, i1 = min(n, i0 + seg);
+  int sa = 0;
+  for (int i = i0; i < i1; ++i) sa += a[i];
+  const int ia = wave_inclusive_scan(sa);
+  int ra = ia - sa;
+  for (int i = i0; i < i1; ++i) {
+    const int ca = a[i];
+    a[i] = ra;
+    ra += ca;
+  }
+  if (lane == 63) a[n] = ia;
+}
+
 }  // namespace nvmoe
