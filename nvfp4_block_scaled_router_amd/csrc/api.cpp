@@ -23,6 +23,8 @@ constexpr int MAX_EXPERTS = 1024;
 constexpr int MAX_TOPK = 64;
 constexpr int MAX_TOKENS = 65536;
 constexpr int MAX_GROUPS = 64;
+// prefill: experts with at most this many rows run through the decode GEMM (second tile list)
+constexpr int COLD_ROWS = 16;
 
 size_t align_up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
 
@@ -340,7 +342,7 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
   // prefill batches averaging at most 64 rows per expert: experts with few rows (skewed
   // routing) go to the decode GEMM through a second tile list
   const bool split = !decode && (long)T * k <= 64L * E;
-  pa.cold_rows = split ? DECODE_TILE_ROWS : 0;
+  pa.cold_rows = split ? COLD_ROWS : 0;
   pa.counts = (int32_t*)(ws + plan->ws_counts);
   pa.offsets = (int32_t*)(ws + plan->ws_offsets);
   pa.perm = (int32_t*)(ws + plan->ws_perm);
@@ -381,8 +383,8 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
   g1.hmin = decode ? nullptr : pa.hmin;
   g1.clamp_groups = d.swiglu_clamp ? E : 0;      // routed experts only
   g1.swiglu_limit = d.swiglu_limit;
-  // second-list (cold) launches: the decode GEMM over list 2, at most one tile per group
-  const int cold_tiles = split ? std::min(plan->G, T * k + S) : 0;
+  // second-list (cold) launches: the decode GEMM over list 2
+  const int cold_tiles = split ? tile_bound(T, k, E, S, DECODE_TILE_ROWS) : 0;
   auto second = [&](GemmArgs g) {
     g.tile_first = pa.tile_count;
     g.tile_count = pa.tile_count + 1;

@@ -198,11 +198,11 @@ __global__ __launch_bounds__(256) void route_general_kernel(RouteArgs a) {
 }
 
 // Tile counts per group before the scans: list 1 takes groups with more than cold rows in
-// ceil(c / M)-row tiles, list 2 groups with 1 .. cold rows in one DECODE_TILE_ROWS tile
+// ceil(c / M)-row tiles, list 2 groups with 1 .. cold rows in DECODE_TILE_ROWS-row tiles
 // (cold = 0: every group in list 1).
 __device__ __forceinline__ void tile_counts(int c, int M, int cold, int* tl, int* ct) {
   *tl = c > cold ? (c + M - 1) / M : 0;
-  *ct = c > 0 && c <= cold ? 1 : 0;
+  *ct = c > 0 && c <= cold ? (c + DECODE_TILE_ROWS - 1) / DECODE_TILE_ROWS : 0;
 }
 
 // The tile lists from the scanned offsets (off), list-1 tile starts (tl) and list-2 slots
@@ -217,9 +217,12 @@ __device__ __forceinline__ void write_tiles(const PlanArgs& a, const int* cnt, c
         a.tile_group[tl[g] + q] = g;
         a.tile_row0[tl[g] + q] = off[g] + q * M;
       }
-    } else if (cnt[g] > 0) {
-      a.tile_group[tl[G] + ct[g]] = g;
-      a.tile_row0[tl[G] + ct[g]] = off[g];
+    } else {
+      const int n = (cnt[g] + DECODE_TILE_ROWS - 1) / DECODE_TILE_ROWS;
+      for (int q = 0; q < n; ++q) {
+        a.tile_group[tl[G] + ct[g] + q] = g;
+        a.tile_row0[tl[G] + ct[g] + q] = off[g] + q * DECODE_TILE_ROWS;
+      }
     }
   }
   if (tid == 0) {
