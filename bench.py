@@ -24,7 +24,10 @@ tiny) print the same line for that configuration, and so do the router/activatio
 variants deepseek-v4-flash-decode (256 experts, top-6, H=4096, I=1024, sqrt-softplus
 scores with a selection bias, SwiGLU clamped at 10, one shared expert; T in
 {1, 8, 32, 64}) and deepseek-v3-noaux (the DeepSeek-V3 layer with its grouped
-sigmoid router, selection bias and routed scale 2.5).
+sigmoid router, selection bias and routed scale 2.5), and deepseek-v4-flash-sharing (one
+rank's routed V4-Flash MoE on the sharing workloads: T = 6 with 0, 20, .., 100% of the
+(token, expert) picks reused across the batch, T = 4, 5, 8 at 40%; each batch line records
+its expert row counts and useful weight bytes).
 
 roofline.traffic is the HBM traffic of one gate/up launch measured by rocprofv3
 counters (FETCH_SIZE and WRITE_SIZE runs, each scaled by the reading of a 1 GiB
@@ -81,6 +84,11 @@ def workload(name):
         return [synth.deepseek_v4_flash(T) for T in synth.DECODE_TOKENS], "hbm"
     if name == "deepseek-v3-noaux":
         return [synth.deepseek_v3_router(8192)], "mfma"
+    # one rank's routed DeepSeek-V4-Flash MoE on the sharing workloads: T = 6 at 0..100%
+    # reuse of (token, expert) picks, and T = 4, 5, 8 at 40%
+    if name == "deepseek-v4-flash-sharing":
+        return ([synth.deepseek_v4_flash_sharing(6, lv) for lv in synth.SHARING_LEVELS]
+                + [synth.deepseek_v4_flash_sharing(T, 0.4) for T in (4, 5, 8)]), "hbm"
     raise SystemExit(f"unknown workload {name}")
 
 
@@ -116,6 +124,7 @@ class Batch:
         torch.cuda.synchronize()
         counts = bufs["expert_counts"].cpu().numpy()
         self.touched = int((counts > 0).sum())
+        self.expert_rows = sorted((int(c) for c in counts if c > 0), reverse=True)
         self.rows = cfg.T * cfg.k
         torch.cuda.synchronize()
 
@@ -484,6 +493,9 @@ def main():
         detail[b.cfg.name] = {
             "T": b.cfg.T, "touched_experts": b.touched,
             "stage_ms": {m.STAGE_NAMES[s]: round(st[s], 5) for s in range(m.MOE_NUM_STAGES)},
+            "expert_rows": b.expert_rows,
+            "useful_weight_bytes": (b.touched + b.cfg.shared) * (b.weight_bytes(2 * b.cfg.I * b.cfg.H)
+                                                                 + b.weight_bytes(b.cfg.H * b.cfg.I)),
             "gate_up_GBps": b.gate_up_bytes() / (st[m.MOE_STAGE_GATE_UP] / 1e3) / 1e9,
             "gate_up_TFLOPs": b.gate_up_flops() / (st[m.MOE_STAGE_GATE_UP] / 1e3) / 1e12,
         }

@@ -17,6 +17,9 @@ README, "MoE kernel"). Recipe, per tensor:
 * shared gate_up/down : same, 1 expert                          streams 5, 6
 * Zipf rank permutation (skewed workload)                       stream 7
 * router selection bias (variant routers)   : f32(N(0, sigma)) stream 8
+* sharing workloads: a seeded expert pool order                 stream 9
+  (token t's k picks are pool[(t k + j) mod U], U = max(k, round(T k (1 - sharing)))
+  distinct experts in all; their logits are set to 20 - j / 4, above every N(0, 1) draw)
 * MXFP4 weights (second weight format), drawn directly in the boundary format:
   E2M1 code bytes uniform over 0..255 and E8M0 scales uniform over 117..124
   (2^-10 .. 2^-3)                                         streams 20 + 2p, 21 + 2p
@@ -40,6 +43,7 @@ LIB_PATH = os.path.join(_HERE, "libsynth.so")
 
 STREAM_X, STREAM_LOGITS, STREAM_W1, STREAM_W2, STREAM_WS1, STREAM_WS2, STREAM_ZIPF = 1, 2, 3, 4, 5, 6, 7
 STREAM_BIAS = 8
+STREAM_SHARE = 9
 WEIGHT_SIGMA = 0.02
 
 _lib = None
@@ -88,6 +92,7 @@ class MoeConfig:
     routed_scaling: float = 1.0     # factor on the routed weights
     swiglu_limit: Optional[float] = None   # clamped SwiGLU limit (routed experts), None = plain
     wfmt: str = "nvfp4"             # weight format: "nvfp4" (quantised fp32 draws) | "mxfp4" (drawn directly)
+    sharing: float = -1.0           # >= 0: the fraction of (token, expert) picks reused across the batch
 
     @property
     def variant_router(self) -> bool:
@@ -139,6 +144,19 @@ def deepseek_v4_flash(T: int = 64) -> MoeConfig:
     sqrt-softplus scores with a selection bias, SwiGLU clamped at 10, one shared expert."""
     return MoeConfig(f"deepseek-v4-flash-t{T}", T=T, H=4096, I=1024, E=256, k=6, score="sqrt_softplus",
                      shared=1, seed=421, bias_sigma=0.5, swiglu_limit=10.0, wfmt="mxfp4")
+
+
+SHARING_LEVELS = (0.0, 0.2, 0.4, 0.6, 0.8, 1.0)
+
+
+def deepseek_v4_flash_sharing(T: int, sharing: float) -> MoeConfig:
+    """One rank's routed DeepSeek-V4-Flash MoE (no shared expert) on a sharing workload:
+    the fraction `sharing` of the T x 6 (token, expert) picks reuses experts across the
+    batch (at T = 6: 36, 29, 22, 14, 7, 6 distinct experts for 0 .. 100%)."""
+    level = int(round(sharing * 100))
+    return MoeConfig(f"deepseek-v4-flash-t{T}-shared{level}", T=T, H=4096, I=1024, E=256, k=6,
+                     score="sqrt_softplus", shared=0, seed=440 + 10 * T + level // 20, bias_sigma=0.5,
+                     swiglu_limit=10.0, wfmt="mxfp4", sharing=sharing)
 
 
 def all_configs():
@@ -209,13 +227,30 @@ def activations(cfg: MoeConfig) -> np.ndarray:
     return normal_bf16(cfg.seed, STREAM_X, 0, cfg.T * cfg.H).reshape(cfg.T, cfg.H)
 
 
+def sharing_experts(cfg: MoeConfig) -> np.ndarray:
+    """The designated picks [T][k] of a sharing workload: U = max(k, round(T k (1 - sharing)))
+    experts of a seeded pool, token t taking pool[(t k + j) mod U] (k distinct per token)."""
+    A = cfg.T * cfg.k
+    U = min(cfg.E, max(cfg.k, int(round(A * (1.0 - cfg.sharing)))))
+    ranks = np.empty(cfg.E, dtype=np.int32)
+    lib().synth_permutation(cfg.seed, STREAM_SHARE, cfg.E, ranks.ctypes.data)
+    pool = np.argsort(ranks, kind="stable")[:U]
+    idx = (np.arange(cfg.T)[:, None] * cfg.k + np.arange(cfg.k)[None, :]) % U
+    return pool[idx].astype(np.int32)
+
+
 def logits(cfg: MoeConfig) -> np.ndarray:
     """Router logits, float32 [T][E]."""
     out = np.empty(cfg.T * cfg.E, dtype=np.float32)
     bias = zipf_bias(cfg)
     bptr = bias.ctypes.data if bias is not None else None
     lib().synth_logits(cfg.seed, STREAM_LOGITS, 0, cfg.T, cfg.E, bptr, out.ctypes.data)
-    return out.reshape(cfg.T, cfg.E)
+    out = out.reshape(cfg.T, cfg.E)
+    if cfg.sharing >= 0:
+        picks = sharing_experts(cfg)
+        for j in range(cfg.k):
+            out[np.arange(cfg.T), picks[:, j]] = np.float32(20.0 - 0.25 * j)
+    return out
 
 
 def _proj_shape(cfg: MoeConfig, which: str):

@@ -84,9 +84,14 @@ void synth_logits(uint64_t seed, uint64_t stream, uint64_t offset, int32_t T, in
   }
 }
 
-/* n bytes: byte i = lo + (bits(seed, stream, offset + i) mod span) (span in 1..256). */
+/* n bytes: byte i = lo + (b_i mod span) (span in 1..256), b_i = byte (i mod 8) of
+ * bits(seed, stream, i / 8) (little-endian), i counted from offset. */
 void synth_bytes(uint64_t seed, uint64_t stream, uint64_t offset, int64_t n, uint32_t lo, uint32_t span,
                  uint8_t* out) {
-  for (int64_t i = 0; i < n; ++i)
-    out[i] = (uint8_t)(lo + synth_bits(seed, stream, offset + (uint64_t)i) % span);
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) {
+    const uint64_t j = offset + (uint64_t)i;
+    const uint32_t b = (uint32_t)(synth_bits(seed, stream, j >> 3) >> (8 * (j & 7))) & 0xFFu;
+    out[i] = (uint8_t)(lo + b % span);
+  }
 }

@@ -75,9 +75,13 @@ VARIANTS = [
     # MXFP4 weights (E8M0 per 32, no global scale): decode, prefill with a shared expert, W4A4
     synth.MoeConfig("mx-decode", T=8, H=256, I=128, E=16, k=4, seed=41, wfmt="mxfp4"),
     synth.MoeConfig("mx-prefill-shared", T=300, H=512, I=256, E=8, k=2, shared=1, seed=42, wfmt="mxfp4"),
-    # (the output is bf16, so max|d| >= 2^-9 max|out| for any exact kernel: inputs keep
-    # max|out| < 10 RMS for the 2e-2 RMS bound to be reachable; 6.97 here)
+    # (uniform random E2M1 codes give heavy output tails: max|out| is 6-8 RMS here, where
+    # the bf16 rounding of the exact output alone reaches 2e-2 RMS)
     synth.MoeConfig("mx-w4a4", T=100, H=512, I=256, E=8, k=2, act="nvfp4", seed=45, wfmt="mxfp4"),
+    # sharing workloads (a fraction of the picks reused across the batch)
+    synth.MoeConfig("share40-small", T=6, H=256, I=128, E=64, k=6, score="sqrt_softplus", seed=27,
+                    bias_sigma=0.5, wfmt="mxfp4", sharing=0.4),
+    synth.deepseek_v4_flash_sharing(6, 0.8),
 ]
 
 
