@@ -65,8 +65,11 @@ class Oracle:
         L.orc_route_general.argtypes = [_vp, _i32, _i32, _i32, _i32, _vp, _i32, _i32, _i32, _f64, _vp, _vp]
         L.orc_expert_ffn.argtypes = [ctypes.POINTER(ProjSet), _i32, _i32, _i32, _vp, _vp]
         L.orc_expert_ffn_clamp.argtypes = [ctypes.POINTER(ProjSet), _i32, _i32, _i32, _vp, _vp, _i32, _f64]
+        L.orc_expert_ffn_q.argtypes = [ctypes.POINTER(ProjSet), _i32, _i32, _i32, _vp, _vp, _i32, _f64, _i32]
         L.orc_moe_tokens_clamp.argtypes = [ctypes.POINTER(ProjSet), ctypes.POINTER(ProjSet), _i32, _i32,
                                            _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _f64]
+        L.orc_moe_tokens_q.argtypes = [ctypes.POINTER(ProjSet), ctypes.POINTER(ProjSet), _i32, _i32,
+                                       _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _f64, _i32]
         L.orc_dequant_rows.argtypes = [_vp, _vp, _vp, _i64, _i32, _vp]
         L.orc_bf16_rows.argtypes = [_vp, _i64, _vp]
         self.L = L
@@ -176,23 +179,26 @@ class Oracle:
         ps.mx = 1 if W1[2] is None else 0
         return ps
 
-    def expert_ffn(self, W1, W2, g: int, x: np.ndarray, swiglu_limit: Optional[float] = None) -> np.ndarray:
+    def expert_ffn(self, W1, W2, g: int, x: np.ndarray, swiglu_limit: Optional[float] = None,
+                   hq: bool = False) -> np.ndarray:
         """W1 = (packed [G][2I][H/2], scales [G][2I][H/16], gs [G]); W2 likewise [G][H][I/..].
-        swiglu_limit: None for the plain SwiGLU, else the clamp limit L >= 0."""
+        swiglu_limit: None for the plain SwiGLU, else the clamp limit L >= 0; hq: the down
+        projection takes h row-quantised to NVFP4."""
         H = W1[0].shape[-1] * 2
         I = W2[0].shape[-1] * 2
         x = np.ascontiguousarray(x, dtype=np.float64)
         y = np.zeros(H, np.float64)
         ps = self._projset(W1, W2)
         clamp = swiglu_limit is not None
-        self.L.orc_expert_ffn_clamp(ctypes.byref(ps), g, H, I, x.ctypes.data, y.ctypes.data, int(clamp),
-                                    float(swiglu_limit) if clamp else 0.0)
+        self.L.orc_expert_ffn_q(ctypes.byref(ps), g, H, I, x.ctypes.data, y.ctypes.data, int(clamp),
+                                float(swiglu_limit) if clamp else 0.0, int(hq))
         return y
 
     def moe_tokens(self, W1, W2, WS1, WS2, tokens, x_rows, ids, w,
-                   swiglu_limit: Optional[float] = None) -> np.ndarray:
+                   swiglu_limit: Optional[float] = None, hq: bool = False) -> np.ndarray:
         """FP64 layer output for `tokens` (x_rows: their decoded inputs [n][H]); the clamp
-        (swiglu_limit not None) applies to the routed experts."""
+        (swiglu_limit not None) applies to the routed experts, hq (h row-quantised to NVFP4
+        before the down projection) to every expert."""
         H = W1[0].shape[-1] * 2
         I = W2[0].shape[-1] * 2
         T, k = ids.shape
@@ -205,10 +211,10 @@ class Oracle:
         num_shared = 0 if WS1 is None else WS1[0].shape[0]
         shared = self._projset(WS1, WS2) if num_shared else ProjSet()
         clamp = swiglu_limit is not None
-        self.L.orc_moe_tokens_clamp(ctypes.byref(routed), ctypes.byref(shared), num_shared, H, I, k,
-                                    len(tokens), tokens.ctypes.data, x_rows.ctypes.data, ids.ctypes.data,
-                                    w.ctypes.data, out.ctypes.data, int(clamp),
-                                    float(swiglu_limit) if clamp else 0.0)
+        self.L.orc_moe_tokens_q(ctypes.byref(routed), ctypes.byref(shared), num_shared, H, I, k,
+                                len(tokens), tokens.ctypes.data, x_rows.ctypes.data, ids.ctypes.data,
+                                w.ctypes.data, out.ctypes.data, int(clamp),
+                                float(swiglu_limit) if clamp else 0.0, int(hq))
         return out
 
 

@@ -400,10 +400,16 @@ static double proj_weight(const orc_proj_set* P, int second, int g, int N, int K
  * bring-up log, W6; a limit of 0 zeroes the expert: the same log, ds4-file
  * loadability entry; limit 10: [b12x] "DeepSeek V4 Flash 0731 MoE reproduction",
  * [megamoe] archived CORRECTNESS_BACKLOG §6, Nvfp4MoE.)
+ * With hq != 0 the down projection takes NVFP4 activations as the gate/up one
+ * does in W4A4 ([megamoe] FINAL_STRETCH, Part B, B0: expert weights and
+ * activations both E2M1 with E4M3 block scales; [megamoe] README, "NVFP4
+ * throughout": FP4 activations once the epilogue quantises them): the row h is
+ * rounded to binary32, quantised by orc_quantize as one row with its own global
+ * scale (per row, as for x), and y uses its exact decode.
  * Weights are decoded element by element in the set's format (orc_weight or
  * orc_weight_mx). */
-void orc_expert_ffn_clamp(const orc_proj_set* P, int g, int H, int I, const double* x, double* y,
-                          int clamp, double limit) {
+void orc_expert_ffn_q(const orc_proj_set* P, int g, int H, int I, const double* x, double* y,
+                      int clamp, double limit, int hq) {
   double* h = (double*)malloc(sizeof(double) * (size_t)I);
   for (int i = 0; i < I; ++i) {
     double gi = 0.0, ui = 0.0;
@@ -417,6 +423,18 @@ void orc_expert_ffn_clamp(const orc_proj_set* P, int g, int H, int I, const doub
     }
     h[i] = gi / (1.0 + exp(-gi)) * ui;
   }
+  if (hq) {
+    float* h32 = (float*)malloc(sizeof(float) * (size_t)I);
+    uint8_t* hp = (uint8_t*)calloc((size_t)I / 2, 1);
+    uint8_t* hs = (uint8_t*)malloc((size_t)I / 16);
+    float hg;
+    for (int i = 0; i < I; ++i) h32[i] = (float)h[i];
+    orc_quantize(h32, 1, I, 1, hp, hs, &hg);
+    for (int i = 0; i < I; ++i) h[i] = orc_weight(hp, hs, hg, I, 0, i);
+    free(h32);
+    free(hp);
+    free(hs);
+  }
   for (int n = 0; n < H; ++n) {
     double yn = 0.0;
     for (int i = 0; i < I; ++i) yn += proj_weight(P, 1, g, H, I, n, i) * h[i];
@@ -425,8 +443,13 @@ void orc_expert_ffn_clamp(const orc_proj_set* P, int g, int H, int I, const doub
   free(h);
 }
 
+void orc_expert_ffn_clamp(const orc_proj_set* P, int g, int H, int I, const double* x, double* y,
+                          int clamp, double limit) {
+  orc_expert_ffn_q(P, g, H, I, x, y, clamp, limit, 0);
+}
+
 void orc_expert_ffn(const orc_proj_set* P, int g, int H, int I, const double* x, double* y) {
-  orc_expert_ffn_clamp(P, g, H, I, x, y, 0, 0.0);
+  orc_expert_ffn_q(P, g, H, I, x, y, 0, 0.0, 0);
 }
 
 /* Layer output for a list of tokens, FP64, never rounded:
@@ -438,10 +461,10 @@ void orc_expert_ffn(const orc_proj_set* P, int g, int H, int I, const double* x,
  * out: [n_tok][H]. clamp/limit select the clamped SwiGLU for the routed experts
  * (the pages state the limit for the routed experts and a plain SwiGLU for the
  * shared one: [megamoe] archived CORRECTNESS_BACKLOG §6, Nvfp4MoE and
- * Nvfp4SharedExpert). */
-void orc_moe_tokens_clamp(const orc_proj_set* routed, const orc_proj_set* shared, int num_shared,
-                          int H, int I, int k, int n_tok, const int32_t* tokens, const double* x,
-                          const int32_t* ids, const double* w, double* out, int clamp, double limit) {
+ * Nvfp4SharedExpert); hq quantises h of every expert, routed and shared. */
+void orc_moe_tokens_q(const orc_proj_set* routed, const orc_proj_set* shared, int num_shared,
+                      int H, int I, int k, int n_tok, const int32_t* tokens, const double* x,
+                      const int32_t* ids, const double* w, double* out, int clamp, double limit, int hq) {
 #pragma omp parallel for schedule(dynamic, 1)
   for (int i = 0; i < n_tok; ++i) {
     int t = tokens[i];
@@ -449,21 +472,27 @@ void orc_moe_tokens_clamp(const orc_proj_set* routed, const orc_proj_set* shared
     double* o = out + (size_t)i * H;
     for (int n = 0; n < H; ++n) o[n] = 0.0;
     for (int j = 0; j < k; ++j) {
-      orc_expert_ffn_clamp(routed, ids[(size_t)t * k + j], H, I, x + (size_t)i * H, y, clamp, limit);
+      orc_expert_ffn_q(routed, ids[(size_t)t * k + j], H, I, x + (size_t)i * H, y, clamp, limit, hq);
       for (int n = 0; n < H; ++n) o[n] += w[(size_t)t * k + j] * y[n];
     }
     for (int s = 0; s < num_shared; ++s) {
-      orc_expert_ffn(shared, s, H, I, x + (size_t)i * H, y);
+      orc_expert_ffn_q(shared, s, H, I, x + (size_t)i * H, y, 0, 0.0, hq);
       for (int n = 0; n < H; ++n) o[n] += y[n];
     }
     free(y);
   }
 }
 
+void orc_moe_tokens_clamp(const orc_proj_set* routed, const orc_proj_set* shared, int num_shared,
+                          int H, int I, int k, int n_tok, const int32_t* tokens, const double* x,
+                          const int32_t* ids, const double* w, double* out, int clamp, double limit) {
+  orc_moe_tokens_q(routed, shared, num_shared, H, I, k, n_tok, tokens, x, ids, w, out, clamp, limit, 0);
+}
+
 void orc_moe_tokens(const orc_proj_set* routed, const orc_proj_set* shared, int num_shared,
                     int H, int I, int k, int n_tok, const int32_t* tokens, const double* x,
                     const int32_t* ids, const double* w, double* out) {
-  orc_moe_tokens_clamp(routed, shared, num_shared, H, I, k, n_tok, tokens, x, ids, w, out, 0, 0.0);
+  orc_moe_tokens_q(routed, shared, num_shared, H, I, k, n_tok, tokens, x, ids, w, out, 0, 0.0, 0);
 }
 
 /* Decoded NVFP4 activations: x[i][k] = E2M1(code) * E4M3(scale) * gs[i]. */

@@ -511,6 +511,79 @@ def pin_moe_clamp_routed_only(o):
     assert np.array_equal(out, ref)
 
 
+def quantize_row_brute(row: np.ndarray) -> np.ndarray:
+    """The NVFP4 row quantiser written from its definition, independently of the oracle:
+    binary32 gs = A / 2688, each block's E4M3 scale by PyTorch's round-to-nearest-even
+    float8 conversion (saturating at 448), each magnitude the nearest E2M1 value by a
+    search over all 8 (ties to the even code); returns the exact FP64 decode."""
+    lim = {k: int(v) for k, v in _read_golden("nvfp4_limits.txt")}
+    e2 = e2m1_table()
+    e4 = e4m3_table_torch()
+    row = np.asarray(row, np.float32)
+    gs = np.float32(np.max(np.abs(row))) / np.float32(lim["gs_divisor"])
+    out = np.zeros(row.size, np.float64)
+    for b in range(row.size // 16):
+        blk = row[16 * b:16 * b + 16]
+        if gs == 0:
+            continue
+        ratio = np.float32(np.max(np.abs(blk))) / (np.float32(6.0) * gs)
+        s = 0x7E if ratio >= lim["e4m3_max"] else int(e4m3_encode_torch(np.array([ratio]))[0])
+        d = np.float32(np.float32(e4[s]) * gs)
+        if d == 0:
+            continue
+        for j in range(16):
+            r = np.float64(np.float32(abs(blk[j]) / d))
+            dist = np.abs(e2[:8] - r)
+            best = np.flatnonzero(dist == dist.min())
+            c = int(best[0]) if best.size == 1 else int([q for q in best if q % 2 == 0][0])
+            out[16 * b + j] = np.copysign(e2[c] * float(e4[s]) * float(gs), blk[j])
+    return out
+
+
+def pin_ffn_hq_textbook(o):
+    """W4A4 down: the MLP equals W2 . Q(fp32(h)) with h the textbook SwiGLU (numpy matmuls)
+    and Q the row quantiser written from its definition above; every h row gets its own
+    global scale, and h far from quantisation (hq off) is the plain MLP."""
+    rng = np.random.default_rng(43)
+    H, I = 64, 64
+    W1 = random_weights(rng, 1, 2 * I, H, sigma=0.5)
+    W2 = random_weights(rng, 1, H, I)
+    D1 = decode_nvfp4(W1[0][0], W1[1][0], W1[2][0])
+    D2 = decode_nvfp4(W2[0][0], W2[1][0], W2[2][0])
+    for trial in range(3):
+        x = rng.standard_normal(H) * (1.0 + trial)
+        h = silu(D1[:I] @ x) * (D1[I:] @ x)
+        hq = quantize_row_brute(h.astype(np.float32))
+        assert np.max(np.abs(hq - h)) > 1e-3 * np.max(np.abs(h))     # the quantisation is visible
+        ref = D2 @ hq
+        y = o.expert_ffn(W1, W2, 0, x, hq=True)
+        assert np.allclose(y, ref, rtol=1e-12, atol=1e-14 * np.abs(ref).max()), np.abs(y - ref).max()
+        yc = o.expert_ffn(W1, W2, 0, x, swiglu_limit=0.5, hq=True)
+        hc = silu(np.minimum(D1[:I] @ x, 0.5)) * np.clip(D1[I:] @ x, -0.5, 0.5)
+        refc = D2 @ quantize_row_brute(hc.astype(np.float32))
+        assert np.allclose(yc, refc, rtol=1e-12, atol=1e-14 * np.abs(refc).max())
+
+
+def pin_moe_hq_every_expert(o):
+    """h quantisation reaches the routed and the shared experts: the layer output equals
+    sum_j w_j FFN_q(e_j) + FFN_q(shared), each FFN_q the textbook MLP on the quantised h."""
+    rng = np.random.default_rng(47)
+    W1, W2, WS1, WS2, x, l = moe_small(rng, T=6, shared=1)
+    ids, w = o.route(l, 2, "softmax")
+    T = x.shape[0]
+    I = W2[0].shape[-1] * 2
+
+    def ffn(Wa, Wb, e, xt):
+        D1 = decode_nvfp4(Wa[0][e], Wa[1][e], Wa[2][e])
+        D2 = decode_nvfp4(Wb[0][e], Wb[1][e], Wb[2][e])
+        return D2 @ quantize_row_brute((silu(D1[:I] @ xt) * (D1[I:] @ xt)).astype(np.float32))
+
+    out = o.moe_tokens(W1, W2, WS1, WS2, np.arange(T, dtype=np.int32), x, ids, w, hq=True)
+    for t in range(T):
+        ref = sum(w[t, j] * ffn(W1, W2, ids[t, j], x[t]) for j in range(2)) + ffn(WS1, WS2, 0, x[t])
+        assert np.allclose(out[t], ref, rtol=1e-11, atol=1e-13 * np.abs(ref).max())
+
+
 # ------------------------------------------------------------ MXFP4 weights
 
 def e8m0_table_torch() -> np.ndarray:

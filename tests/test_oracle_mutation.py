@@ -48,8 +48,13 @@ MUTANTS = {
                                "w[(size_t)t * k + j] = (renorm ? sj / sum : sj);"),
     "gate_clamped_both_sides": ("      gi = fmin(gi, limit);", "      gi = fmin(fmax(gi, -limit), limit);"),
     "up_clamped_above_only": ("      ui = fmin(fmax(ui, -limit), limit);", "      ui = fmin(ui, limit);"),
-    "clamp_on_shared": ("      orc_expert_ffn(shared, s, H, I, x + (size_t)i * H, y);",
-                        "      orc_expert_ffn_clamp(shared, s, H, I, x + (size_t)i * H, y, clamp, limit);"),
+    "clamp_on_shared": ("      orc_expert_ffn_q(shared, s, H, I, x + (size_t)i * H, y, 0, 0.0, hq);",
+                        "      orc_expert_ffn_q(shared, s, H, I, x + (size_t)i * H, y, clamp, limit, hq);"),
+    "hq_skipped": ("  if (hq) {", "  if (0) {"),
+    "hq_not_on_shared": ("      orc_expert_ffn_q(shared, s, H, I, x + (size_t)i * H, y, 0, 0.0, hq);",
+                         "      orc_expert_ffn_q(shared, s, H, I, x + (size_t)i * H, y, 0, 0.0, 0);"),
+    "hq_decode_gs_halved": ("    orc_quantize(h32, 1, I, 1, hp, hs, &hg);",
+                        "    orc_quantize(h32, 1, I, 1, hp, hs, &hg);\n    hg = hg * 0.5f;"),
     "e4m3_ties_odd": ("if (d < bestd || (d == bestd && (c & 1u) == 0 && (best & 1u) == 1)) {\n      best = c;\n      bestd = d;\n    }\n  }\n  return (uint8_t)best;\n}\n\n/* Nearest E2M1",
                       "if (d < bestd || (d == bestd && (c & 1u) == 1)) {\n      best = c;\n      bestd = d;\n    }\n  }\n  return (uint8_t)best;\n}\n\n/* Nearest E2M1"),
 }
