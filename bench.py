@@ -20,7 +20,7 @@ Prints one JSON line: tokens/s of the whole step (value), plus
   cpu_baseline: the CPU oracle (FP64, OpenMP) on a bounded sample of the same
                 workload, on this host's cores.
 Other workloads (--workload qwen3-30b-a3b-prefill | deepseek-v3 | skewed-w4a4 |
-tiny) print the same line for that configuration, and so do the router/activation
+skewed-w4a4-all (h quantised to NVFP4 too) | tiny) print the same line for that configuration, and so do the router/activation
 variants deepseek-v4-flash-decode (256 experts, top-6, H=4096, I=1024, sqrt-softplus
 scores with a selection bias, SwiGLU clamped at 10, one shared expert; T in
 {1, 8, 32, 64}) and deepseek-v3-noaux (the DeepSeek-V3 layer with its grouped
@@ -76,6 +76,8 @@ def workload(name):
         return [synth.deepseek_v3()], "mfma"
     if name == "skewed-w4a4":
         return [synth.skewed_w4a4()], "hbm"
+    if name == "skewed-w4a4-all":        # the same layer with h quantised to NVFP4 as well
+        return [synth.skewed_w4a4_all()], "hbm"
     if name == "tiny":
         return [synth.tiny()], "hbm"
     # router / activation variants of the layer (sqrt-softplus + bias + clamped SwiGLU;
@@ -148,7 +150,7 @@ class Batch:
         c = self.cfg
         w = (self.touched + c.shared) * self.weight_bytes(2 * c.I * c.H)
         act = c.T * c.H * (2 if c.act == "bf16" else NVFP4_BYTES_PER_WEIGHT + 4.0 / c.H)
-        h = (self.rows + c.shared * c.T) * c.I * 2
+        h = (self.rows + c.shared * c.T) * c.I * (4 if c.act == "nvfp4_all" else 2)   # fp32 h / h16
         return w + act + h
 
     def gate_up_flops(self):
@@ -191,14 +193,14 @@ def cpu_baseline(cfgs, budget_s=6.0):
         if el >= budget_s:
             break
     return {"value": n_tok / el, "unit": "tokens/s", "cores": min(o.threads(), len(tokens)), "kind": "oracle",
-            "sample": f"{cfg.name}: {len(tokens)} tokens (routing, {'activation quantisation, ' if cfg.act == 'nvfp4' else ''}"
+            "sample": f"{cfg.name}: {len(tokens)} tokens (routing, {'activation quantisation, ' if cfg.act != 'bf16' else ''}"
                       f"FP64 expert MLPs of their {cfg.k} experts, combine) x {reps} repeats, {el:.1f} s; "
                       f"weight preparation untimed"}
 
 
 # ------------------------------------------------------------ rocprofv3 summaries
 
-STAGE_OF_MODE = {"0": "gate_up", "1": "gate_up", "3": "gate_up", "2": "down"}
+STAGE_OF_MODE = {"0": "gate_up", "1": "gate_up", "3": "gate_up", "2": "down", "4": "down"}
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ("gemm.hip", "common.hpp", "kernels.hpp")
 

@@ -72,11 +72,19 @@ extern "C" {
 #define MOE_SCORE_SIGMOID 1
 #define MOE_SCORE_SQRT_SOFTPLUS 2   /* generalised router only */
 
-/* Gate/up activation format ([b12x] "What's in here", moe: W4A16 = BF16
- * activations with inline FP4 weight dequant; [megamoe] FINAL_STRETCH B0:
- * expert weights and activations both float4_e2m1fn_x2 = W4A4). */
+/* Activation format ([b12x] "What's in here", moe: W4A16 = BF16 activations with
+ * inline FP4 weight dequant; [megamoe] FINAL_STRETCH B0: expert weights and
+ * activations both float4_e2m1fn_x2 = W4A4; [megamoe] README "NVFP4 throughout":
+ * FP4 activations once the epilogue quantises them).
+ *   MOE_ACT_BF16        both expert GEMMs take 16-bit activations (W4A16);
+ *   MOE_ACT_NVFP4_ROWQ  x is row-quantised to NVFP4 (binary32 quantiser, one FP32
+ *                       global scale per token row) before the gate/up GEMM;
+ *   MOE_ACT_NVFP4_ALL   x as above, and h = silu(g)*u of every expert row (routed and
+ *                       shared) is rounded to binary32 and row-quantised the same way,
+ *                       with its own global scale, before the down GEMM. */
 #define MOE_ACT_BF16 0
 #define MOE_ACT_NVFP4_ROWQ 1
+#define MOE_ACT_NVFP4_ALL 2
 
 /* Weight format of every projection ([vllm.cpp] capability table, MXFP4 row: E8M0
  * dequant 2^(byte-127), group 32, no global scale, distinct from NVFP4's group-16 fp8
@@ -171,7 +179,7 @@ typedef struct {
  *   expert_offsets i32 [E+1]   exclusive scan of counts, offsets[E] = T*k
  *   perm           i32 [T*k]   perm[offsets[e] + r] = t*k + j: expert-major,
  *                              tokens ascending inside an expert
- *   act_packed     u8  [T][H/2]   (W4A4 only) quantised activations, as
+ *   act_packed     u8  [T][H/2]   (NVFP4 x only) quantised activations, as
  *   act_scales     u8  [T][H/16]   moe_quantize_nvfp4_rows writes them
  *   act_global     f32 [T]        */
 typedef struct {
@@ -236,7 +244,9 @@ int moe_pack_router_bias(const moe_plan_t* plan, const float* bias, void* packed
  * per 16 columns (the block's largest |h| scaled into [2^14, 2^15)), which the
  * down GEMM brings to a common per-row exponent exactly before its fp16 MFMAs;
  * expert outputs are stored the same way (fp16 with a power-of-two exponent per 16
- * columns) and summed by the combine in fp32.
+ * columns) and summed by the combine in fp32. With MOE_ACT_NVFP4_ALL, h is stored
+ * as fp32, row-quantised (codes, E4M3 block scales, FP32 row global scale) and the
+ * down GEMM decodes it exactly, applying the row's global scale in its epilogue.
  * ([megamoe] README "MoE kernel": fused SwiGLU grouped GEMM epilogue in
  * registers; [b12x] "What's in here": FP32 internal, BF16 boundary;
  * [vllm.cpp] "Device-resident decode campaign": device routing ids feed the
@@ -251,7 +261,8 @@ int moe_run(const moe_plan_t* plan, const void* packed, int32_t T, const uint16_
                                   batches above the small-batch limit; empty below it) */
 #define MOE_STAGE_ROUTE 1      /* top-k, counts, offsets, permutation, tile list */
 #define MOE_STAGE_GATE_UP 2    /* grouped gate/up GEMM + SwiGLU */
-#define MOE_STAGE_DOWN 3       /* grouped down GEMM */
+#define MOE_STAGE_DOWN 3       /* grouped down GEMM (with MOE_ACT_NVFP4_ALL: the h row
+                                  quantisation before it) */
 #define MOE_STAGE_COMBINE 4    /* weighted combine */
 #define MOE_NUM_STAGES 5
 
@@ -259,8 +270,9 @@ int moe_run(const moe_plan_t* plan, const void* packed, int32_t T, const uint16_
  * handles (as void*, any may be NULL), created by the caller with timing enabled.
  * For the single-kernel stages (GATE_UP, DOWN, COMBINE) events[2s] and events[2s+1]
  * are stamped by the kernel launch itself at the kernel's start and end, so their
- * elapsed time is the kernel's duration; for the others (QUANT, ROUTE: zero to four
- * kernels) they are recorded on `stream` right before and after the stage. Results
+ * elapsed time is the kernel's duration (DOWN with MOE_ACT_NVFP4_ALL: the start is
+ * recorded on `stream` before the h quantisation); for the others (QUANT, ROUTE: zero
+ * to four kernels) they are recorded on `stream` right before and after the stage. Results
  * are identical to moe_run. ([b12x] "Using it": per-kernel timing logs for tuning.) */
 int moe_run_timed(const moe_plan_t* plan, const void* packed, int32_t T, const uint16_t* x,
                   const float* router_logits, uint16_t* out, const moe_routing_out* routing,

@@ -50,7 +50,7 @@ struct moe_plan {
   ProjLayout w1, w2;
   size_t off_w1f, off_w1s, off_w1g, off_w2f, off_w2s, off_w2g, off_bias, packed_bytes;
   size_t ws_ids, ws_w, ws_counts, ws_offsets, ws_perm, ws_inv, ws_tok, ws_tgrp, ws_trow, ws_tcnt, ws_plan;
-  size_t ws_xq, ws_xs, ws_xg, ws_x16, ws_h, ws_hexp, ws_hmin, ws_y, ws_yexp, ws_bytes;
+  size_t ws_xq, ws_xs, ws_xg, ws_x16, ws_h, ws_hexp, ws_hmin, ws_hf, ws_hq, ws_hs, ws_hg, ws_y, ws_yexp, ws_bytes;
   int max_tiles;
 };
 
@@ -94,7 +94,8 @@ static int load_desc(const moe_desc* in, moe_desc* out) {
   const moe_desc* d = out;
   if (d->score_fn != MOE_SCORE_SOFTMAX && d->score_fn != MOE_SCORE_SIGMOID && d->score_fn != MOE_SCORE_SQRT_SOFTPLUS)
     return MOE_ERR_ENUM;
-  if (d->act_format != MOE_ACT_BF16 && d->act_format != MOE_ACT_NVFP4_ROWQ) return MOE_ERR_ENUM;
+  if (d->act_format != MOE_ACT_BF16 && d->act_format != MOE_ACT_NVFP4_ROWQ && d->act_format != MOE_ACT_NVFP4_ALL)
+    return MOE_ERR_ENUM;
   if (d->hidden < 128 || d->hidden > MAX_HIDDEN || d->hidden % 128) return MOE_ERR_SHAPE;
   if (d->inter < 128 || d->inter > MAX_HIDDEN || d->inter % 128) return MOE_ERR_SHAPE;
   if (d->num_experts < 1 || d->num_experts > MAX_EXPERTS) return MOE_ERR_SHAPE;
@@ -161,13 +162,18 @@ int moe_plan(const moe_desc* desc, moe_plan_t** plan, size_t* packed_bytes, size
   p->ws_trow = o; o = align_up(o + 8 * (size_t)p->max_tiles);
   p->ws_tcnt = o; o = align_up(o + 16);
   p->ws_plan = o; o = align_up(o + 4 * plan_scratch_ints(Tm, k, E));
-  p->ws_xq = o; o = align_up(o + (desc->act_format == MOE_ACT_NVFP4_ROWQ ? (size_t)Tm * H / 2 : 0));
-  p->ws_xs = o; o = align_up(o + (desc->act_format == MOE_ACT_NVFP4_ROWQ ? (size_t)Tm * H / 16 : 0));
+  const bool fp4x = desc->act_format != MOE_ACT_BF16, fp4h = desc->act_format == MOE_ACT_NVFP4_ALL;
+  p->ws_xq = o; o = align_up(o + (fp4x ? (size_t)Tm * H / 2 : 0));
+  p->ws_xs = o; o = align_up(o + (fp4x ? (size_t)Tm * H / 16 : 0));
   p->ws_xg = o; o = align_up(o + 4 * (size_t)Tm);      // per-row activation factor (either format)
   p->ws_x16 = o; o = align_up(o + (desc->act_format == MOE_ACT_BF16 ? 2 * (size_t)Tm * H : 0));
-  p->ws_h = o; o = align_up(o + 2 * rows * I);        // h16
-  p->ws_hexp = o; o = align_up(o + rows * (I / 16));  // per-16-column h exponents
-  p->ws_hmin = o; o = align_up(o + 4 * rows);         // per-row minimum h exponent
+  p->ws_h = o; o = align_up(o + (fp4h ? 0 : 2 * rows * I));        // h16
+  p->ws_hexp = o; o = align_up(o + (fp4h ? 0 : rows * (I / 16)));  // per-16-column h exponents
+  p->ws_hmin = o; o = align_up(o + 4 * rows);                       // per-row minimum h exponent
+  p->ws_hf = o; o = align_up(o + (fp4h ? 4 * rows * I : 0));       // NVFP4 h: fp32 h rows,
+  p->ws_hq = o; o = align_up(o + (fp4h ? rows * I / 2 : 0));       // their codes,
+  p->ws_hs = o; o = align_up(o + (fp4h ? rows * (I / 16) : 0));    // block scales
+  p->ws_hg = o; o = align_up(o + (fp4h ? 4 * rows : 0));           // and global scales
   p->ws_y = o; o = align_up(o + 2 * rows * H);         // y16
   p->ws_yexp = o; o = align_up(o + rows * (H / 16));  // per-16-column y exponents
   p->ws_bytes = o;
@@ -295,7 +301,8 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
   uint8_t* ws = (uint8_t*)workspace;
   const uint8_t* pk = (const uint8_t*)packed;
   const int H = d.hidden, I = d.inter, E = d.num_experts, k = d.top_k, S = d.num_shared;
-  const bool fp4 = d.act_format == MOE_ACT_NVFP4_ROWQ;
+  const bool fp4 = d.act_format != MOE_ACT_BF16;            // x row-quantised to NVFP4
+  const bool fp4h = d.act_format == MOE_ACT_NVFP4_ALL;      // h too, before the down GEMM
   hipError_t e;
 
   uint8_t* xq = (fp4 && r.act_packed) ? r.act_packed : ws + plan->ws_xq;
@@ -381,6 +388,7 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
   g1.out = (uint16_t*)(ws + plan->ws_h);
   g1.hexp = (int8_t*)(ws + plan->ws_hexp);
   g1.hmin = decode ? nullptr : pa.hmin;
+  g1.hf = fp4h ? (float*)(ws + plan->ws_hf) : nullptr;
   g1.clamp_groups = d.swiglu_clamp ? E : 0;      // routed experts only
   g1.swiglu_limit = d.swiglu_limit;
   // second-list (cold) launches: the decode GEMM over list 2
@@ -407,13 +415,25 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
   g2.K = I;
   g2.x = g1.out;
   g2.out = nullptr;
+  g2.hf = nullptr;
   g2.yout = (uint16_t*)(ws + plan->ws_y);
   g2.yexp = (int8_t*)(ws + plan->ws_yexp);
+  const GemmMode dn_mode = fp4h ? GEMM_DOWN_FP4 : GEMM_DOWN;
   {
     const LaunchEvents le = stage_events(ev, MOE_STAGE_DOWN);
-    e = launch_gemm(GEMM_DOWN, regime, max_tiles, est_tiles, g2, s, split ? LaunchEvents{le.start, nullptr} : le);
+    LaunchEvents first = split ? LaunchEvents{le.start, nullptr} : le;
+    if (fp4h) {   // every h row (T*k routed, T per shared expert) quantised with its own global scale
+      g2.xq = ws + plan->ws_hq;
+      g2.xs = ws + plan->ws_hs;
+      g2.xg = (const float*)(ws + plan->ws_hg);
+      if ((e = mark(ev, 2 * MOE_STAGE_DOWN, s)) != hipSuccess) return (int)e;
+      first.start = nullptr;
+      e = launch_quant_rows_f32(g1.hf, T * k + S * T, I, ws + plan->ws_hq, ws + plan->ws_hs,
+                                (float*)(ws + plan->ws_hg), s);
+    }
+    if (e == hipSuccess) e = launch_gemm(dn_mode, regime, max_tiles, est_tiles, g2, s, first);
     if (e == hipSuccess && split)
-      e = launch_gemm(GEMM_DOWN, REGIME_DECODE_KSPLIT, cold_tiles, cold_tiles, second(g2), s,
+      e = launch_gemm(dn_mode, REGIME_DECODE_KSPLIT, cold_tiles, cold_tiles, second(g2), s,
                       LaunchEvents{nullptr, le.stop});
   }
   if (e != hipSuccess) return (int)e;

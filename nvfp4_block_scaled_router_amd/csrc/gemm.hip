@@ -1,11 +1,14 @@
 // Grouped NVFP4 GEMMs of the MoE layer on gfx950 MFMA, and the weighted combine.
 //
 //   gate_up: [g|u][row] = W1_e . x_row  (W1_e = E2M1 x E4M3(per 16 along H) x gs_e),
-//            epilogue h = silu(g*sc) * (u*sc), sc = gs_e (x the row's activation global
-//            scale for NVFP4 activations), stored as two bf16 planes hi = bf16(h),
-//            lo = bf16(h - hi), which hold h to about 2^-17 relative
-//   down:    y[row] = W2_e . (h_hi + h_lo)_row * gs_e -> fp32 (kept in fp32 until the
-//            combine): each dequantised weight tile meets both planes in two MFMAs
+//            epilogue h = silu(g*sc) * (u*sc), sc = gs_e (x the row's activation factor),
+//            stored as fp16 scaled by 2^e per 16-column block (e puts the block's largest
+//            |h| in [2^14, 2^15)), or as fp32 for the row quantiser when the down GEMM
+//            takes NVFP4 activations;
+//   down:    y[row] = W2_e . h_row * gs_e, h brought to one scale per row (h16) or decoded
+//            from its NVFP4 row (codes x E4M3 block scales, the row's global scale in the
+//            epilogue); y stored as fp16 scaled per 16-column block like h;
+//   combine: out[t] = bf16(sum_j w_j y[inv[t][j]] (+ shared)), fp32.
 // ([megamoe] README "MoE kernel": grouped GEMM with the global scale, SwiGLU and
 // clamping applied in registers in the epilogue; [vllm.cpp] "Device-resident decode
 // campaign": grouped kernels with a per-group weight-row index, then MoeCombineKernel.)
@@ -13,18 +16,16 @@
 // Dequant route: the per-16 E4M3 block scale is not a power of two and covers half
 // an E8M0 block of the scaled MFMA, so each weight q*s (at most 6 significant bits) is
 // rebuilt exactly in registers and fed to a 16-bit MFMA with fp32 accumulation:
-//  - gate_up of large batches (2/3 of the weight bytes, each weight used by up to 128
-//    rows): fp16. The convert applies the power of two of s (its scale operand is
-//    exponent-only), one packed fp16 multiply the significand: 1 VALU op per weight.
-//    Activations are fp16 too: bf16 rows rescaled exactly by a power of two into fp16
-//    range (undone in the epilogue), NVFP4 rows decoded the same way as the weights.
-//    V_MFMA_F32_16X16X32_F16. Small batches are weight-streaming bound, not VALU bound:
-//    their bf16 rows go straight into the bf16 route below (no activation pass).
-//  - down, and gate_up of small bf16 batches: bf16 (h's range is not known when it is
-//    written): fp4->fp32 convert, fp32 multiply, truncating pack, 2 VALU ops per weight.
-//    V_MFMA_F32_16X16X32_BF16. Both routes form every product q*s*x exactly.
-// Global scales (per expert, per activation row) are constant over K and are applied
-// once in the epilogue.
+//  - fp16 (prefill GEMMs, decode down, NVFP4 activations): the convert applies the power
+//    of two of s (its scale operand is exponent-only), one packed fp16 multiply the
+//    significand: 1 VALU op per weight. Activations are fp16 too: bf16 rows rescaled
+//    exactly by a power of two into fp16 range (undone in the epilogue), NVFP4 rows
+//    decoded the same way as the weights, h16 as stored. V_MFMA_F32_16X16X32_F16.
+//  - bf16 (gate_up of small bf16 batches, weight-streaming bound): the caller's bf16 rows
+//    go straight into the MFMA with no activation pass; fp4->fp32 convert, fp32 multiply,
+//    truncating pack, 2 VALU ops per weight. V_MFMA_F32_16X16X32_BF16.
+// Both routes form every product q*s*x exactly. Global scales (per expert, per activation
+// row) are constant over K and are applied once in the epilogue.
 //
 // Operand roles: MFMA A = 16 weight rows x 32 k (one lane: row l%16, 8 consecutive
 // k of a 32-wide lane group), MFMA B = 32 k x 16 tokens (lane: token l%16, the same
@@ -122,6 +123,10 @@ __device__ __forceinline__ void epilogue_pair(const GemmArgs& a, const f32x4& ga
     return silu_mul(fminf(g * sc, lim), fminf(fmaxf(u * sc, -lim), lim));
   };
   const float h[4] = {act(gacc.x, uacc.x), act(gacc.y, uacc.y), act(gacc.z, uacc.z), act(gacc.w, uacc.w)};
+  if (a.hf) {   // fp32 h in column order for the row quantiser (NVFP4 down GEMM)
+    *(f32x4*)(a.hf + (size_t)row * NO + hs * 16 + 4 * lg) = f32x4{h[0], h[1], h[2], h[3]};
+    return;
+  }
   float mx = fmaxf(fmaxf(fabsf(h[0]), fabsf(h[1])), fmaxf(fabsf(h[2]), fabsf(h[3])));
   mx = fmaxf(mx, __shfl_xor(mx, 16));
   mx = fmaxf(mx, __shfl_xor(mx, 32));
@@ -219,6 +224,10 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs a) {
     erow = a.hexp + (size_t)row * (L.K / 16);
     hm = a.hmin ? a.hmin[row] : row_exp_min4(erow, L.K / 16, lg);
     sc = __builtin_ldexpf(wgs, -hm);
+  } else if (MODE == GEMM_DOWN_FP4) {                       // NVFP4 h rows, addressed by row
+    qrow = a.xq + (size_t)row * (L.K / 2);
+    srow = a.xs + (size_t)row * (L.K / 16);
+    sc *= a.xg[row];
   } else {
     const int t = a.tok[row];
     if (MODE == GEMM_GATEUP_FP4) {
@@ -246,7 +255,7 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs a) {
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) wv[s] = *fp4_tile(a, L, g, q0 + s, kc);
     u32x4 bop[4];
-    if (MODE == GEMM_GATEUP_FP4) {
+    if (MODE == GEMM_GATEUP_FP4 || MODE == GEMM_DOWN_FP4) {
       const u32x4 xv = *(const u32x4*)(qrow + (size_t)kc * 64 + lg * 16);
       const uint32_t sp = *(const uint16_t*)(srow + (size_t)kc * 8 + 2 * lg);
       WOps<true> xo;
@@ -283,7 +292,7 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs a) {
   // wave w finishes tiles w, w + NW, ...: fixed-order sum over the K ranges
   if (l16 >= nvalid) return;
   const int orow = row0 + l16;                             // == row on the lanes that remain
-  if (MODE == GEMM_DOWN) {
+  if (MODE == GEMM_DOWN || MODE == GEMM_DOWN_FP4) {
     for (int s = wave; s < NSUB; s += NW) {
       f32x4 sum = red[0][s][lane];
       for (int w = 1; w < NW; ++w) sum += red[w][s][lane];
@@ -361,7 +370,9 @@ constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 1
 
 template <int MODE, int NSUB, int TSUB, int NBUF, int WAVES, int OCC>
 __global__ __launch_bounds__(64 * WAVES, OCC) void gemm_prefill_kernel(GemmArgs a) {
-  static_assert(MODE == GEMM_GATEUP_F16 || MODE == GEMM_GATEUP_FP4 || MODE == GEMM_DOWN, "prefill modes");
+  static_assert(MODE == GEMM_GATEUP_F16 || MODE == GEMM_GATEUP_FP4 || MODE == GEMM_DOWN || MODE == GEMM_DOWN_FP4,
+                "prefill modes");
+  constexpr bool FP4A = MODE == GEMM_GATEUP_FP4 || MODE == GEMM_DOWN_FP4;   // NVFP4 activation rows
   static_assert(WAVES == 4 || WAVES == 8, "4 or 8 waves");
   constexpr bool DMA = MODE == GEMM_GATEUP_F16;
   static_assert(!DMA || NBUF == 2 || NBUF == 3, "LDS ring depth");
@@ -374,7 +385,7 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void gemm_prefill_kernel(GemmArgs 
   // pieces (8 code bytes + 1 scale byte, D/2 per thread)
   constexpr int NPC = MODE == GEMM_DOWN ? D : D / 2;
   static_assert(D >= 2 && STAGE % NT == 0, "tile size");
-  static_assert(MODE != GEMM_GATEUP_FP4 || D % 2 == 0, "NVFP4 pieces pair up");
+  static_assert(!FP4A || D % 2 == 0, "NVFP4 pieces pair up");
   __shared__ u32x4 tile[NST * STAGE];
 
   const int ntiles = a.tile_count[0];
@@ -419,7 +430,8 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void gemm_prefill_kernel(GemmArgs 
       if constexpr (MODE == GEMM_DOWN) {
         phm[i] = a.hmin[rr];                             // prefill: gate_up kept the row minimum
       } else {
-        poff[i] = (uint32_t)a.tok[rr] * (L.K / 2) + pcol * 8;   // its scale byte: poff / 8 into xs
+        // its scale byte: poff / 8 into xs; gate_up gathers token rows, down reads its own rows
+        poff[i] = (uint32_t)(MODE == GEMM_DOWN_FP4 ? rr : a.tok[rr]) * (L.K / 2) + pcol * 8;
       }
     }
   }
@@ -495,7 +507,7 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void gemm_prefill_kernel(GemmArgs 
 #pragma unroll
       for (int t = 0; t < TV; ++t) acc[s][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // Weights: two raw register sets (rA/rB, chunk parity). With PIPE (NVFP4 gate_up),
+    // Weights: two raw register sets (rA/rB, chunk parity). With PIPE (NVFP4 activations),
     // also two dequantised sets (WA/WB): chunk kc + 2's raw weights are fetched at the start
     // of chunk kc and chunk kc + 1's are dequantised in the middle of chunk kc, between its
     // MFMAs, so the VALU work of the dequant runs beside the MFMA pipe instead of ahead of
@@ -503,7 +515,7 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void gemm_prefill_kernel(GemmArgs 
     // chunk kc's are dequantised right before its MFMAs: down has no registers left for a
     // second set, and the fp16 gate_up measured slower pipelined (its second workgroup on
     // the CU already fills the MFMA pipe during the dequant).
-    constexpr bool PIPE = MODE == GEMM_GATEUP_FP4;
+    constexpr bool PIPE = FP4A;
     u32x4 rA[NSUB], rB[NSUB];
     uint32_t sA[NSUB], sB[NSUB];
     WOps<true> WA[NSUB], WB[PIPE ? NSUB : 1];
@@ -613,8 +625,8 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void gemm_prefill_kernel(GemmArgs 
       const int rr = t * 16 + l16;
       if (rr >= nvalid) continue;
       const int orow = row0 + rr;
-      if (MODE == GEMM_DOWN) {
-        const float scl = __builtin_ldexpf(wgs, -a.hmin[orow]);
+      if (MODE == GEMM_DOWN || MODE == GEMM_DOWN_FP4) {
+        const float scl = MODE == GEMM_DOWN ? __builtin_ldexpf(wgs, -a.hmin[orow]) : wgs * a.xg[orow];
 #pragma unroll
         for (int s = 0; s < NSUB; ++s) epilogue_single(a, acc[s][t], scl, orow, q0 + s);
       } else {
@@ -699,6 +711,10 @@ static void launch_mode(GemmRegime regime, int max_tiles, int est_tiles, const G
       else   // hidden a multiple of 128 only: one 16-column tile per wave covers it exactly
         launch_k(gemm_prefill_kernel<MODE, 1, PRE_TSUB, PRE_NBUF_GU, W, PRE_OCC_RS>, dim3(a.N / (16 * W), ny),
                  dim3(64 * W), s, ev, a);
+    } else if constexpr (MODE == GEMM_DOWN_FP4) {     // N = H, a multiple of 128
+      constexpr int W = PRE_WAVES_FP4, NS = PRE_NSUB_DN;
+      launch_k(gemm_prefill_kernel<MODE, NS, PRE_TSUB, PRE_NBUF_GU, W, PRE_OCC_FP4>, dim3(a.N / (16 * W * NS), ny),
+               dim3(64 * W), s, ev, a);
     } else if constexpr (MODE == GEMM_GATEUP_F16) {   // N = 2I, a multiple of 256
       constexpr int W = PRE_WAVES_GU, NS = PRE_NSUB_GU;
       launch_k(gemm_prefill_kernel<MODE, NS, PRE_TSUB, PRE_NBUF_GU, W, PRE_OCC_GU>, dim3(a.N / (16 * W * NS), ny),
@@ -720,6 +736,8 @@ hipError_t launch_gemm(GemmMode mode, GemmRegime regime, int max_tiles, int est_
     case GEMM_GATEUP_BF16: launch_mode<GEMM_GATEUP_BF16>(regime, max_tiles, est_tiles, a, s, ev); break;
     case GEMM_GATEUP_FP4: launch_mode<GEMM_GATEUP_FP4>(regime, max_tiles, est_tiles, a, s, ev); break;
     case GEMM_DOWN: launch_mode<GEMM_DOWN>(regime, max_tiles, est_tiles, a, s, ev); break;
+    case GEMM_DOWN_FP4: launch_mode<GEMM_DOWN_FP4>(regime, max_tiles, est_tiles, a, s, ev); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

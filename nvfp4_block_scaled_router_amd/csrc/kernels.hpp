@@ -54,6 +54,9 @@ bool plan_small_ok(int T, int k);
 // Activation / weight quantiser.
 hipError_t launch_quant_rows_bf16(const uint16_t* x, int rows, int K, uint8_t* packed, uint8_t* scales,
                                   float* gs, hipStream_t s);
+// fp32 rows (h before the NVFP4 down GEMM), each with its own global scale.
+hipError_t launch_quant_rows_f32(const float* x, int rows, int K, uint8_t* packed, uint8_t* scales, float* gs,
+                                 hipStream_t s);
 // bf16 rows -> fp16 rows scaled by 2^p (p per row puts max|x| in [2^14, 2^15)); xf = 2^-p.
 hipError_t launch_rows_to_f16(const uint16_t* x, int rows, int K, uint16_t* x16, float* xf, hipStream_t s);
 hipError_t launch_quant_groups_f32(const float* x, int groups, int rows_per_group, int K, uint8_t* packed,
@@ -79,8 +82,9 @@ hipError_t launch_pack(const PackArgs& a, hipStream_t s);
 
 // Grouped GEMMs.
 // gate_up modes: F16 = activations pre-scaled into fp16 (x16) and fp16 MFMA; BF16 = the
-// caller's bf16 rows read directly, bf16 MFMA; FP4 = NVFP4 activation rows.
-enum GemmMode { GEMM_GATEUP_F16 = 0, GEMM_GATEUP_FP4 = 1, GEMM_DOWN = 2, GEMM_GATEUP_BF16 = 3 };
+// caller's bf16 rows read directly, bf16 MFMA; FP4 = NVFP4 activation rows. down modes:
+// DOWN = h16 rows; DOWN_FP4 = h row-quantised to NVFP4 (xq/xs/xg indexed by row).
+enum GemmMode { GEMM_GATEUP_F16 = 0, GEMM_GATEUP_FP4 = 1, GEMM_DOWN = 2, GEMM_GATEUP_BF16 = 3, GEMM_DOWN_FP4 = 4 };
 
 struct GemmArgs {
   // weights (packed layout of one projection, G groups)
@@ -92,9 +96,9 @@ struct GemmArgs {
   const int32_t* tok;      // row -> token (gather modes)
   const uint16_t* x;       // activations [T][K]: fp16 rescaled (GATEUP_F16) or bf16 (GATEUP_BF16);
                            // h16 [rows][K] (DOWN)
-  const uint8_t* xq;       // [T][K/2]  (GATEUP_FP4)
-  const uint8_t* xs;       // [T][K/16]
-  const float* xg;         // [T] per-row activation factor applied in the gate_up epilogue
+  const uint8_t* xq;       // [T][K/2]  (GATEUP_FP4; DOWN_FP4: [rows][K/2])
+  const uint8_t* xs;       // [T][K/16] (DOWN_FP4: [rows][K/16])
+  const float* xg;         // [T] per-row activation factor applied in the epilogue (DOWN_FP4: [rows])
   // tile list
   const int32_t* tile_group;
   const int32_t* tile_row0;
@@ -112,6 +116,8 @@ struct GemmArgs {
   uint16_t* out;           // gate_up: h16
   int8_t* hexp;            // [rows][I/16]
   int32_t* hmin;           // [rows] or nullptr
+  float* hf;               // gate_up: when set, h as fp32 [rows][I] in column order instead (the
+                           // input of the row quantiser before DOWN_FP4); out/hexp/hmin unused
   // down: y as fp16 [rows][N] with one exponent per row and 16-column block, the
   // block's largest |y| scaled into [2^14, 2^15): y = y16 * 2^-yexp
   uint16_t* yout;

@@ -111,13 +111,15 @@ __device__ __forceinline__ void wave_quant_row(const T* row, int K, float gs, ui
   }
 }
 
-// One wave per row: global scale of the row, then its blocks.
-__global__ __launch_bounds__(256) void quant_rows_bf16_kernel(const uint16_t* __restrict__ x, int rows, int K,
-                                                              uint8_t* __restrict__ packed,
-                                                              uint8_t* __restrict__ scales, float* __restrict__ gs) {
+// One wave per row: global scale of the row, then its blocks (bf16 activation rows, or
+// the fp32 h rows of the NVFP4 down GEMM).
+template <typename T>
+__global__ __launch_bounds__(256) void quant_rows_kernel(const T* __restrict__ x, int rows, int K,
+                                                         uint8_t* __restrict__ packed,
+                                                         uint8_t* __restrict__ scales, float* __restrict__ gs) {
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= rows) return;
-  const uint16_t* row = x + (size_t)r * K;
+  const T* row = x + (size_t)r * K;
   const float A = wave_row_absmax(row, K);
   const float g = A / 2688.0f;
   if ((threadIdx.x & (WAVE - 1)) == 0) gs[r] = g;
@@ -206,7 +208,15 @@ hipError_t launch_rows_to_f16(const uint16_t* x, int rows, int K, uint16_t* x16,
 hipError_t launch_quant_rows_bf16(const uint16_t* x, int rows, int K, uint8_t* packed, uint8_t* scales,
                                   float* gs, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(quant_rows_bf16_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, x, rows, K, packed, scales,
+  hipLaunchKernelGGL(quant_rows_kernel<uint16_t>, dim3((rows + 3) / 4), dim3(256), 0, s, x, rows, K, packed,
+                     scales, gs);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_rows_f32(const float* x, int rows, int K, uint8_t* packed, uint8_t* scales, float* gs,
+                                 hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(quant_rows_kernel<float>, dim3((rows + 3) / 4), dim3(256), 0, s, x, rows, K, packed, scales,
                      gs);
   return hipGetLastError();
 }

@@ -63,7 +63,7 @@ class MoeLayer:
             expert_offsets=torch.empty(self.E + 1, dtype=torch.int32, device=dev),
             perm=torch.empty(T * self.k, dtype=torch.int32, device=dev),
         )
-        if self.desc.act_format == 1:
+        if self.desc.act_format in (1, 2):
             bufs.update(act_packed=torch.empty((T, self.H // 2), dtype=torch.uint8, device=dev),
                         act_scales=torch.empty((T, self.H // 16), dtype=torch.uint8, device=dev),
                         act_global=torch.empty(T, dtype=torch.float32, device=dev))

@@ -33,6 +33,7 @@ from __future__ import annotations
 import ctypes
 import math
 import os
+import dataclasses
 from dataclasses import dataclass, field
 from typing import Optional
 
@@ -129,6 +130,11 @@ def deepseek_v3() -> MoeConfig:
 def skewed_w4a4() -> MoeConfig:
     return MoeConfig("skewed-w4a4", T=512, H=4096, I=1536, E=64, k=4, act="nvfp4",
                      zipf_s=1.2, seed=501)
+
+
+def skewed_w4a4_all() -> MoeConfig:
+    """The skewed W4A4 layer with h quantised to NVFP4 as well (W4A4 down GEMM)."""
+    return dataclasses.replace(skewed_w4a4(), name="skewed-w4a4-all", act="nvfp4_all")
 
 
 def deepseek_v3_router(T: int = 256) -> MoeConfig:

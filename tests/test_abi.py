@@ -131,6 +131,13 @@ def test_plan_sizes_cover_the_layout():
     rows = 8192 * 9
     # h16 with its block exponents and row minimum, y16 with its block exponents
     assert wb >= rows * (2048 * 2 + 2048 // 16 + 4 + 7168 * 2 + 7168 // 16)
+    # NVFP4 h: fp32 rows, codes, block scales and a global scale per row instead of h16
+    d4 = desc(hidden=7168, inter=2048, num_experts=256, top_k=8, max_tokens=8192, score="sigmoid",
+              num_shared=1, act="nvfp4_all")
+    plan, pb4, wb4 = m.moe_plan(d4)
+    m.moe_plan_destroy(plan)
+    assert pb4 == pb
+    assert wb4 >= rows * (2048 * 4 + 2048 // 2 + 2048 // 16 + 4 + 4 + 7168 * 2 + 7168 // 16) + 8192 * (7168 // 2)
 
 
 def test_run_rejects_before_enqueue():

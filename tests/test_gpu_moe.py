@@ -25,7 +25,7 @@ def _run_and_check(case: Case):
     assert np.array_equal(bufs["expert_counts"].cpu().numpy(), ref["counts"]), "counts"
     assert np.array_equal(bufs["expert_offsets"].cpu().numpy(), ref["offsets"]), "offsets"
     assert np.array_equal(bufs["perm"].cpu().numpy(), ref["perm"]), "perm"
-    if cfg.act == "nvfp4":
+    if cfg.act in ("nvfp4", "nvfp4_all"):
         assert np.array_equal(bufs["act_packed"].cpu().numpy(), ref["xq"]), "quantised activation codes"
         assert np.array_equal(bufs["act_scales"].cpu().numpy(), ref["xs"]), "quantised activation scales"
         assert np.array_equal(bufs["act_global"].cpu().numpy().view(np.uint32), ref["xg"].view(np.uint32))
@@ -190,6 +190,30 @@ def test_run_timed_matches_run(T):
         t = ev[2 * s].elapsed_time(ev[2 * s + 1])
         log(f"T={T} stage {m.STAGE_NAMES[s]}: {t * 1e3:.1f} us")
         assert 0.0 < t < 1000.0
+
+
+# W4A4 down: h of every expert row quantised to NVFP4 before the down GEMM (decode and
+# prefill regimes, a shared expert, skewed routing with the 16-row cold list, clamped SwiGLU,
+# MXFP4 weights, the widest intermediate size)
+W4A4_ALL = [
+    synth.MoeConfig("all-decode", T=8, H=256, I=128, E=16, k=4, act="nvfp4_all", seed=61),
+    synth.MoeConfig("all-prefill-shared", T=300, H=512, I=256, E=8, k=2, shared=1, act="nvfp4_all", seed=62),
+    synth.MoeConfig("all-skewed-cold", T=200, H=256, I=256, E=32, k=4, act="nvfp4_all", zipf_s=1.2, seed=63),
+    synth.MoeConfig("all-clamp-sigmoid", T=100, H=256, I=128, E=16, k=4, score="sigmoid", shared=1,
+                    act="nvfp4_all", swiglu_limit=0.05, seed=64),
+    synth.MoeConfig("all-mx", T=64, H=512, I=256, E=8, k=2, act="nvfp4_all", wfmt="mxfp4", seed=65),
+    synth.MoeConfig("all-max-inter", T=40, H=128, I=16384, E=4, k=2, shared=1, act="nvfp4_all", seed=66),
+]
+
+
+@pytest.mark.parametrize("cfg", W4A4_ALL, ids=lambda c: c.name)
+def test_w4a4_down(cfg):
+    _run_and_check(Case(cfg, tokens=synth.token_sample(cfg, 24) if cfg.I > 4096 else None))
+
+
+def test_skewed_w4a4_down_sampled():
+    cfg = synth.skewed_w4a4_all()
+    _run_and_check(Case(cfg, tokens=synth.token_sample(cfg, 64)))
 
 
 # the descriptor's limits: hidden and intermediate 16384 (128 K chunks), 65536 tokens
