@@ -11,7 +11,8 @@ W warmup steps, then exactly K timed steps between two device synchronisations.
 The step is captured once in a HIP graph and replayed (the serving launch path);
 the eager-launch time of the same step is reported beside it.
 
-Prints one JSON line: tokens/s of the whole step (value), plus
+Prints one JSON line: tokens/s of the whole step (value), the per-step distribution of K
+further replays (median, IQR, samples), plus
   roofline:     the dominant kernel (the gate/up grouped GEMM) timed with HIP
                 events recorded on its launch stream over K further steps:
                 algorithmic bytes per launch / mean launch time vs 8 TB/s HBM
@@ -451,6 +452,15 @@ def main():
     ms = (t1 - t0) * 1e3 / args.steps
     tokens = sum(c.T for c in cfgs)
     value = tokens / (ms / 1e3)
+    # the per-step distribution: K more replays, each between two events on the replay stream
+    step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+    for e0, e1 in step_ev:
+        e0.record()
+        graph.replay()
+        e1.record()
+    torch.cuda.synchronize()
+    step_samples = [e0.elapsed_time(e1) for e0, e1 in step_ev]
 
     # dominant kernel: gate/up GEMM, timed by HIP events recorded on its launch stream
     # (moe_run_timed records them around each stage on the stream moe_run uses)
@@ -508,9 +518,14 @@ def main():
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": args.workload, "T": [c.T for c in cfgs], "H": cfgs[0].H, "I": cfgs[0].I,
                    "E": cfgs[0].E, "top_k": cfgs[0].k, "score": cfgs[0].score, "shared": cfgs[0].shared,
-                   "activations": cfgs[0].act, "weights": "nvfp4 e2m1 + e4m3/16 + fp32 per expert"},
+                   "activations": cfgs[0].act,
+                   "weights": ("mxfp4 e2m1 + e8m0/32" if cfgs[0].wfmt == "mxfp4"
+                               else "nvfp4 e2m1 + e4m3/16 + fp32 per expert")},
         "launch": "hip graph replay of the step (eager: %.4f ms/step)" % eager_ms,
         "eager_ms_per_step": eager_ms,
+        "step_ms_median": float(np.median(step_samples)),
+        "step_ms_iqr": [float(np.percentile(step_samples, 25)), float(np.percentile(step_samples, 75))],
+        "step_ms_samples": [round(v, 5) for v in step_samples],
         "layer_GBps": layer_bytes / (ms / 1e3) / 1e9,
         "layer_TFLOPs": layer_flops / (ms / 1e3) / 1e12,
         "roofline": roof,
