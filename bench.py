@@ -203,7 +203,7 @@ def cpu_baseline(cfgs, budget_s=6.0):
 
 STAGE_OF_MODE = {"0": "gate_up", "1": "gate_up", "3": "gate_up", "2": "down", "4": "down"}
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ("gemm.hip", "common.hpp", "kernels.hpp")
+KERNEL_SOURCES = ("gemm.hip", "common.hpp", "kernels.hpp", "api.cpp")   # kernels + their launch choices
 
 
 def kernel_source_hash():
