@@ -60,6 +60,10 @@ class Oracle:
         L.orc_e2m1_encode.restype = ctypes.c_uint8
         L.orc_e2m1_encode.argtypes = [_f32]
         L.orc_quantize.argtypes = [_vp, _i64, _i32, _i64, _vp, _vp, _vp]
+        L.orc_mxfp8_quantize.argtypes = [_vp, _i64, _i32, _vp, _vp]
+        L.orc_mxfp8.restype = ctypes.c_double
+        L.orc_mxfp8.argtypes = [_u32, _u32]
+        L.orc_mxfp8_rows.argtypes = [_vp, _vp, _i64, _i32, _vp]
         L.orc_route.argtypes = [_vp, _i32, _i32, _i32, _i32, _vp, _vp]
         L.orc_plan.argtypes = [_vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp]
         L.orc_route_general.argtypes = [_vp, _i32, _i32, _i32, _i32, _vp, _i32, _i32, _i32, _f64, _vp, _vp]
@@ -106,6 +110,27 @@ class Oracle:
         self.L.orc_quantize(x.ctypes.data, rows, K, rows_per_gs, packed.ctypes.data,
                             scales.ctypes.data, gs.ctypes.data)
         return packed, scales, gs
+
+    def mxfp8_quantize(self, x: np.ndarray):
+        """float32 [rows][K] -> (codes u8 [rows][K], E8M0 scales u8 [rows][K/32])."""
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        rows, K = x.shape
+        codes = np.zeros((rows, K), np.uint8)
+        scales = np.zeros((rows, K // 32), np.uint8)
+        self.L.orc_mxfp8_quantize(x.ctypes.data, rows, K, codes.ctypes.data, scales.ctypes.data)
+        return codes, scales
+
+    def mxfp8(self, code: int, scale: int) -> float:
+        return self.L.orc_mxfp8(code, scale)
+
+    def mxfp8_rows(self, codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+        """Exact FP64 decode of MXFP8 rows."""
+        codes = np.ascontiguousarray(codes, dtype=np.uint8)
+        scales = np.ascontiguousarray(scales, dtype=np.uint8)
+        rows, K = codes.shape
+        out = np.empty((rows, K), np.float64)
+        self.L.orc_mxfp8_rows(codes.ctypes.data, scales.ctypes.data, rows, K, out.ctypes.data)
+        return out
 
     def weight(self, packed, scales, gs, n, k) -> float:
         K = packed.shape[-1] * 2
@@ -183,7 +208,7 @@ class Oracle:
                    hq: bool = False) -> np.ndarray:
         """W1 = (packed [G][2I][H/2], scales [G][2I][H/16], gs [G]); W2 likewise [G][H][I/..].
         swiglu_limit: None for the plain SwiGLU, else the clamp limit L >= 0; hq: the down
-        projection takes h row-quantised to NVFP4."""
+        projection takes h row-quantised to NVFP4 (True / 1) or MXFP8 (2)."""
         H = W1[0].shape[-1] * 2
         I = W2[0].shape[-1] * 2
         x = np.ascontiguousarray(x, dtype=np.float64)

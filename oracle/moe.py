@@ -8,8 +8,8 @@ functions of ``oracle.c`` in the order the method runs them:
 2. activations: bf16 decoded exactly, or (W4A4) NVFP4 row-quantised with the
    binary32 quantizer and decoded exactly;
 3. per token, the k expert SwiGLU MLPs in FP64 (act "nvfp4_all": h row-quantised the
-   same way before the down projection), weighted sum, plus the shared expert with
-   weight 1.
+   same way before the down projection; act "mxfp8": x and h MXFP8), weighted sum, plus
+   the shared expert with weight 1.
 
 Weights are the synth draws quantised per expert projection by the oracle's
 own quantizer (one global scale per expert projection).
@@ -107,13 +107,18 @@ def forward(cfg: synth.MoeConfig, x_bf16: np.ndarray, logits: np.ndarray, W1, W2
     ids, w = route(cfg, logits, o)
     counts, offsets, perm, inv = o.plan(ids, cfg.E)
     res = dict(ids=ids, w=w, counts=counts, offsets=offsets, perm=perm, inv=inv, tokens=tokens)
-    if cfg.act in ("nvfp4", "nvfp4_all"):
+    if cfg.act == "mxfp8":                               # W4A8: MXFP8 x (and h)
+        xf = o.bf16_rows(x_bf16).astype(np.float32)       # exact: bf16 -> binary32
+        xq, xs = o.mxfp8_quantize(xf)
+        res.update(xq=xq, xs=xs)
+        x_rows = o.mxfp8_rows(xq[tokens], xs[tokens])
+    elif cfg.act in ("nvfp4", "nvfp4_all"):
         xf = o.bf16_rows(x_bf16).astype(np.float32)       # exact: bf16 -> binary32
         xq, xs, xg = o.quantize(xf, rows_per_gs=1)
         res.update(xq=xq, xs=xs, xg=xg)
         x_rows = o.dequant_rows(xq[tokens], xs[tokens], xg[tokens])
     else:
         x_rows = o.bf16_rows(x_bf16[tokens])
-    res["out"] = o.moe_tokens(W1, W2, WS1, WS2, tokens, x_rows, ids, w, cfg.swiglu_limit,
-                              hq=cfg.act == "nvfp4_all")
+    hq = {"nvfp4_all": 1, "mxfp8": 2}.get(cfg.act, 0)
+    res["out"] = o.moe_tokens(W1, W2, WS1, WS2, tokens, x_rows, ids, w, cfg.swiglu_limit, hq=hq)
     return res

@@ -206,6 +206,56 @@ void orc_quantize(const float* x, int64_t rows, int K, int64_t rows_per_gs,
   }
 }
 
+/* ------------------------------------------------------ MXFP8 activations */
+
+/* MXFP8 element: E4M3fn code times the block's E8M0 scale. */
+double orc_mxfp8(uint32_t code, uint32_t scale) { return orc_e4m3fn(code) * orc_e8m0(scale); }
+
+/* Decoded MXFP8 rows: x[r][k] = orc_mxfp8(codes[r][k], scales[r][k / 32]). */
+void orc_mxfp8_rows(const uint8_t* codes, const uint8_t* scales, int64_t rows, int K, double* x) {
+  for (int64_t r = 0; r < rows; ++r)
+    for (int k = 0; k < K; ++k)
+      x[(size_t)r * K + k] = orc_mxfp8(codes[(size_t)r * K + k], scales[(size_t)r * (K / 32) + k / 32]);
+}
+
+/* MXFP8 row quantiser: E4M3fn elements with one E8M0 scale per 32 consecutive k
+ * (the MXFP8 activations of the W4A8 profile: [b12x] "DeepSeek V4 Flash 0731 MoE
+ * reproduction"; E8M0 = 2^(byte-127) over groups of 32: [vllm.cpp] capability table,
+ * MXFP4 row). Per block b of row r, in binary32:
+ *   A_b    = max |x| over the block                          (exact)
+ *   X_b    = floor(log2 A_b) - 8, clamped to [-127, 127]; A_b = 0 gives X_b = -127
+ *            (8 = the exponent of E4M3's largest normal, 448 = 1.75 * 2^8)
+ *   scale  = X_b + 127                                      (the E8M0 byte, value 2^X_b)
+ *   code_k = sign(x_k) << 7 | E4M3_nearest(|x_k| * 2^-X_b)   (exact scaling; ratios above
+ *            448 saturate to 448, ties to the even code)
+ * The shared-exponent rule is the OCP microscaling one. Outputs codes [rows][K],
+ * scales [rows][K/32]. */
+void orc_mxfp8_quantize(const float* x, int64_t rows, int K, uint8_t* codes, uint8_t* scales) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    const float* xr = x + (size_t)r * K;
+    for (int b = 0; b < K / 32; ++b) {
+      float A = 0.0f;
+      for (int j = 0; j < 32; ++j)
+        if (fabsf(xr[b * 32 + j]) > A) A = fabsf(xr[b * 32 + j]);
+      int X = -127;
+      if (A > 0.0f) {
+        int E;
+        frexpf(A, &E);                          /* A = f 2^E, f in [0.5, 1): floor(log2 A) = E - 1 */
+        X = E - 1 - 8;
+        if (X < -127) X = -127;
+        if (X > 127) X = 127;
+      }
+      scales[(size_t)r * (K / 32) + b] = (uint8_t)(X + 127);
+      for (int j = 0; j < 32; ++j) {
+        const float v = xr[b * 32 + j];
+        const uint32_t sign = signbit(v) ? 0x80u : 0u;
+        codes[(size_t)r * K + b * 32 + j] = (uint8_t)(sign | orc_e4m3_encode(ldexpf(fabsf(v), -X)));
+      }
+    }
+  }
+}
+
 /* ----------------------------------------------------------------- routing */
 
 /* Top-k routing of T tokens over E experts.
@@ -405,7 +455,9 @@ static double proj_weight(const orc_proj_set* P, int second, int g, int N, int K
  * activations both E2M1 with E4M3 block scales; [megamoe] README, "NVFP4
  * throughout": FP4 activations once the epilogue quantises them): the row h is
  * rounded to binary32, quantised by orc_quantize as one row with its own global
- * scale (per row, as for x), and y uses its exact decode.
+ * scale (per row, as for x), and y uses its exact decode. hq == 2 quantises the
+ * binary32 h with the MXFP8 quantiser instead (the W4A8 profile: both expert GEMMs
+ * take MXFP8 activations, [b12x] "DeepSeek V4 Flash 0731 MoE reproduction").
  * Weights are decoded element by element in the set's format (orc_weight or
  * orc_weight_mx). */
 void orc_expert_ffn_q(const orc_proj_set* P, int g, int H, int I, const double* x, double* y,
@@ -423,7 +475,17 @@ void orc_expert_ffn_q(const orc_proj_set* P, int g, int H, int I, const double* 
     }
     h[i] = gi / (1.0 + exp(-gi)) * ui;
   }
-  if (hq) {
+  if (hq == 2) {   /* MXFP8 h (W4A8 profile) */
+    float* h32 = (float*)malloc(sizeof(float) * (size_t)I);
+    uint8_t* hc = (uint8_t*)malloc((size_t)I);
+    uint8_t* hs = (uint8_t*)malloc((size_t)I / 32);
+    for (int i = 0; i < I; ++i) h32[i] = (float)h[i];
+    orc_mxfp8_quantize(h32, 1, I, hc, hs);
+    for (int i = 0; i < I; ++i) h[i] = orc_mxfp8(hc[i], hs[i / 32]);
+    free(h32);
+    free(hc);
+    free(hs);
+  } else if (hq) {
     float* h32 = (float*)malloc(sizeof(float) * (size_t)I);
     uint8_t* hp = (uint8_t*)calloc((size_t)I / 2, 1);
     uint8_t* hs = (uint8_t*)malloc((size_t)I / 16);

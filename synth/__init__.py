@@ -83,6 +83,7 @@ class MoeConfig:
     score: str = "softmax"  # "softmax" | "sigmoid" | "sqrt_softplus"
     shared: int = 0         # always-on shared experts (0 or 1), intermediate size I
     act: str = "bf16"       # "bf16" (W4A16) | "nvfp4" (row-quantised x, W4A4) | "nvfp4_all" (x and h)
+                            # | "mxfp8" (x and h MXFP8, with MXFP4 weights: W4A8)
     zipf_s: float = 0.0     # > 0: add -s*ln(rank_e) to every logit of expert e
     seed: int = 0
     # router / activation variants (the defaults are the plain layer)

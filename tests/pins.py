@@ -584,6 +584,97 @@ def pin_moe_hq_every_expert(o):
         assert np.allclose(out[t], ref, rtol=1e-11, atol=1e-13 * np.abs(ref).max())
 
 
+def quantize_mxfp8_brute(row: np.ndarray):
+    """MXFP8 row quantiser written from its definition, independently of the oracle:
+    per 32 consecutive k, X = floor(log2 amax) - 8 from numpy's frexp (clamped to
+    [-127, 127], -127 for an all-zero block), elements by PyTorch's round-to-nearest-even
+    float8_e4m3fn conversion of |x| 2^-X (saturating at 448), sign kept; returns
+    (codes, scale bytes, exact FP64 decode)."""
+    row = np.asarray(row, np.float32)
+    K = row.size
+    codes = np.zeros(K, np.uint8)
+    sc = np.zeros(K // 32, np.uint8)
+    e4 = e4m3_table_torch()
+    for b in range(K // 32):
+        blk = row[32 * b:32 * b + 32]
+        A = float(np.max(np.abs(blk)))
+        X = -127
+        if A > 0:
+            X = int(np.frexp(np.float32(A))[1]) - 1 - 8
+            X = max(-127, min(127, X))
+        sc[b] = X + 127
+        r = np.ldexp(np.abs(blk).astype(np.float64), -X).astype(np.float32)   # exact power-of-two scaling
+        enc = np.where(r >= 448, 0x7E, e4m3_encode_torch(np.minimum(r, np.float32(448))))
+        codes[32 * b:32 * b + 32] = enc.astype(np.uint8) | np.where(np.signbit(blk), 0x80, 0).astype(np.uint8)
+    dec = np.array([e4[c & 0x7F] * (-1.0 if c & 0x80 else 1.0) for c in codes]) * np.repeat(
+        np.ldexp(1.0, sc.astype(np.int64) - 127), 32)
+    return codes, sc, dec
+
+
+def mxfp8_fixture():
+    rng = np.random.default_rng(53)
+    rows = [rng.standard_normal(64).astype(np.float32) for _ in range(4)]
+    rows.append(np.zeros(64, np.float32))                                   # all zero: scale byte 0
+    r = np.zeros(64, np.float32); r[40] = -3.5; r[3] = 1e-30; rows.append(r)  # one non-zero per block
+    r = rng.standard_normal(64).astype(np.float32); r[0] = 500.0; r[1] = 448.0; rows.append(r)  # clipping
+    r = np.full(64, -0.0, np.float32); r[33] = 2.0 ** -120; rows.append(r)  # negative zeros, tiny block
+    rows.append((rng.standard_normal(64) * 1e30).astype(np.float32))       # large
+    rows.append((rng.standard_normal(64) * 1e-20).astype(np.float32))      # small
+    return np.stack(rows)
+
+
+def pin_mxfp8_quantize(o):
+    """Codes and scale bytes bit-exact against the definition written in the test; the row
+    maximum of a block with max 2^e lands on E4M3 256 (0x78) at scale 2^(e-8)."""
+    x = mxfp8_fixture()
+    codes, sc = o.mxfp8_quantize(x)
+    for i, row in enumerate(x):
+        c, s, _ = quantize_mxfp8_brute(row)
+        assert np.array_equal(sc[i], s), (i, sc[i], s)
+        assert np.array_equal(codes[i], c), (i, np.flatnonzero(codes[i] != c))
+    one = np.zeros((1, 32), np.float32)
+    one[0, 5] = 4.0
+    c, s = o.mxfp8_quantize(one)
+    assert s[0, 0] == 127 + 2 - 8 and c[0, 5] == 0x78
+    assert sc[4, 0] == 0 and not codes[4].any()                              # zero block
+    assert codes[6, 0] == 0x7E and codes[6, 1] == 0x7E                       # 500 and 448 saturate / exact
+
+
+def pin_mxfp8_decode(o):
+    """Every E4M3 code times E8M0 scales against PyTorch's float8_e4m3fn decoder."""
+    e4 = e4m3_table_torch()
+    for s in (0, 1, 100, 120, 127, 130, 200, 254):
+        for c in range(256):
+            if (c & 0x7F) == 0x7F:
+                continue
+            want = e4[c] * 2.0 ** (s - 127)
+            assert o.mxfp8(c, s) == want, (c, s)
+
+
+def pin_ffn_mxfp8_textbook(o):
+    """W4A8 MLP: MXFP4 weights, the input and h MXFP8: W2 . Q8(fp32(silu(Wg x) (Wu x)))
+    with Q8 the quantiser written in the test, plain and clamped."""
+    rng = np.random.default_rng(59)
+    H, I = 64, 64
+    W1 = random_mx_weights(rng, 1, 2 * I, H)
+    W2 = random_mx_weights(rng, 1, H, I)
+    D1 = decode_mxfp4(W1[0][0], W1[1][0])
+    D2 = decode_mxfp4(W2[0][0], W2[1][0])
+    for trial in range(3):
+        x = (rng.standard_normal(H) * 4.0 ** trial).astype(np.float32)
+        _, _, xh = quantize_mxfp8_brute(x)
+        for lim in (None, 0.05):
+            gv, uv = D1[:I] @ xh, D1[I:] @ xh
+            if lim is not None:
+                gv, uv = np.minimum(gv, lim), np.clip(uv, -lim, lim)
+            h = silu(gv) * uv
+            _, _, hh = quantize_mxfp8_brute(h.astype(np.float32))
+            assert np.max(np.abs(hh - h)) > 1e-4 * np.max(np.abs(h))          # the quantisation is visible
+            ref = D2 @ hh
+            y = o.expert_ffn((W1[0], W1[1], None), (W2[0], W2[1], None), 0, xh, swiglu_limit=lim, hq=2)
+            assert np.allclose(y, ref, rtol=1e-12, atol=1e-14 * np.abs(ref).max()), np.abs(y - ref).max()
+
+
 # ------------------------------------------------------------ MXFP4 weights
 
 def e8m0_table_torch() -> np.ndarray:

@@ -50,7 +50,12 @@ MUTANTS = {
     "up_clamped_above_only": ("      ui = fmin(fmax(ui, -limit), limit);", "      ui = fmin(ui, limit);"),
     "clamp_on_shared": ("      orc_expert_ffn_q(shared, s, H, I, x + (size_t)i * H, y, 0, 0.0, hq);",
                         "      orc_expert_ffn_q(shared, s, H, I, x + (size_t)i * H, y, clamp, limit, hq);"),
-    "hq_skipped": ("  if (hq) {", "  if (0) {"),
+    "hq_skipped": ("  } else if (hq) {", "  } else if (0) {"),
+    "mx8_exponent_off_by_one": ("        X = E - 1 - 8;", "        X = E - 1 - 7;"),
+    "mx8_amax_half_block": ("      for (int j = 0; j < 32; ++j)\n        if (fabsf(xr[b * 32 + j]) > A)",
+                            "      for (int j = 0; j < 16; ++j)\n        if (fabsf(xr[b * 32 + j]) > A)"),
+    "mx8_sign_lost": ("const uint32_t sign = signbit(v) ? 0x80u : 0u;", "const uint32_t sign = 0u;"),
+    "mx8_h_as_nvfp4": ("  if (hq == 2) {   /* MXFP8 h (W4A8 profile) */", "  if (0) {   /* MXFP8 h (W4A8 profile) */"),
     "hq_not_on_shared": ("      orc_expert_ffn_q(shared, s, H, I, x + (size_t)i * H, y, 0, 0.0, hq);",
                          "      orc_expert_ffn_q(shared, s, H, I, x + (size_t)i * H, y, 0, 0.0, 0);"),
     "hq_decode_gs_halved": ("    orc_quantize(h32, 1, I, 1, hp, hs, &hg);",
