@@ -85,6 +85,13 @@ extern "C" {
 #define MOE_ACT_BF16 0
 #define MOE_ACT_NVFP4_ROWQ 1
 #define MOE_ACT_NVFP4_ALL 2
+#define MOE_ACT_MXFP8 3   /* W4A8 ([b12x] "DeepSeek V4 Flash 0731 MoE reproduction": MXFP4
+                             E8M0/K32 weights with MXFP8 activations); requires
+                             MOE_WEIGHTS_MXFP4. x and h of every expert row are MXFP8-quantised:
+                             per 32 consecutive k an E8M0 scale 2^X, X = floor(log2 max|v|) - 8
+                             (clamped to [-127, 127]; -127 for a zero block), E4M3 codes of
+                             |v| 2^-X rounded to nearest even and saturating at 448, sign kept.
+                             Both GEMMs run gfx950's block-scaled MFMA on the raw codes. */
 
 /* Weight format of every projection ([vllm.cpp] capability table, MXFP4 row: E8M0
  * dequant 2^(byte-127), group 32, no global scale, distinct from NVFP4's group-16 fp8
@@ -179,8 +186,8 @@ typedef struct {
  *   expert_offsets i32 [E+1]   exclusive scan of counts, offsets[E] = T*k
  *   perm           i32 [T*k]   perm[offsets[e] + r] = t*k + j: expert-major,
  *                              tokens ascending inside an expert
- *   act_packed     u8  [T][H/2]   (NVFP4 x only) quantised activations, as
- *   act_scales     u8  [T][H/16]   moe_quantize_nvfp4_rows writes them
+ *   act_packed     u8  [T][H/2]   (NVFP4 x; MXFP8: [T][H] E4M3 codes) quantised activations, as
+ *   act_scales     u8  [T][H/16]   moe_quantize_nvfp4_rows writes them (MXFP8: [T][H/32] E8M0)
  *   act_global     f32 [T]        */
 typedef struct {
   int32_t* topk_ids;

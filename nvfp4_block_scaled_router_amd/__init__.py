@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libnvfp4moe.so")
 
 MOE_ABI_VERSION = 2
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID, MOE_SCORE_SQRT_SOFTPLUS = 0, 1, 2
-MOE_ACT_BF16, MOE_ACT_NVFP4_ROWQ, MOE_ACT_NVFP4_ALL = 0, 1, 2
+MOE_ACT_BF16, MOE_ACT_NVFP4_ROWQ, MOE_ACT_NVFP4_ALL, MOE_ACT_MXFP8 = 0, 1, 2, 3
 MOE_WEIGHTS_NVFP4, MOE_WEIGHTS_MXFP4 = 0, 1
 MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_SIZE, MOE_ERR_TOKENS = 0, -1, -2, -3, -4
 MOE_ERR_ALIGN, MOE_ERR_ABI, MOE_ERR_ENUM, MOE_ERR_WEIGHT = -5, -6, -7, -8
@@ -138,7 +138,8 @@ def make_desc(hidden: int, inter: int, num_experts: int, top_k: int, max_tokens:
     d.score_fn = {"softmax": MOE_SCORE_SOFTMAX, "sigmoid": MOE_SCORE_SIGMOID,
                   "sqrt_softplus": MOE_SCORE_SQRT_SOFTPLUS}.get(score, score)
     d.renormalize = 1 if renormalize else 0
-    d.act_format = {"bf16": MOE_ACT_BF16, "nvfp4": MOE_ACT_NVFP4_ROWQ, "nvfp4_all": MOE_ACT_NVFP4_ALL}.get(act, act)
+    d.act_format = {"bf16": MOE_ACT_BF16, "nvfp4": MOE_ACT_NVFP4_ROWQ, "nvfp4_all": MOE_ACT_NVFP4_ALL,
+                    "mxfp8": MOE_ACT_MXFP8}.get(act, act)
     d.num_shared = num_shared
     d.use_bias = 1 if use_bias else 0
     d.n_group, d.topk_group = n_group, topk_group

@@ -98,7 +98,8 @@ static int load_desc(const moe_desc* in, moe_desc* out) {
   const moe_desc* d = out;
   if (d->score_fn != MOE_SCORE_SOFTMAX && d->score_fn != MOE_SCORE_SIGMOID && d->score_fn != MOE_SCORE_SQRT_SOFTPLUS)
     return MOE_ERR_ENUM;
-  if (d->act_format != MOE_ACT_BF16 && d->act_format != MOE_ACT_NVFP4_ROWQ && d->act_format != MOE_ACT_NVFP4_ALL)
+  if (d->act_format != MOE_ACT_BF16 && d->act_format != MOE_ACT_NVFP4_ROWQ && d->act_format != MOE_ACT_NVFP4_ALL &&
+      d->act_format != MOE_ACT_MXFP8)
     return MOE_ERR_ENUM;
   if (d->hidden < 128 || d->hidden > MAX_HIDDEN || d->hidden % 128) return MOE_ERR_SHAPE;
   if (d->inter < 128 || d->inter > MAX_HIDDEN || d->inter % 128) return MOE_ERR_SHAPE;
@@ -115,6 +116,8 @@ static int load_desc(const moe_desc* in, moe_desc* out) {
   if (!std::isfinite(d->routed_scaling) || d->routed_scaling <= 0.0f) return MOE_ERR_SHAPE;
   if (d->swiglu_clamp && (!std::isfinite(d->swiglu_limit) || d->swiglu_limit < 0.0f)) return MOE_ERR_SHAPE;
   if (d->weight_format != MOE_WEIGHTS_NVFP4 && d->weight_format != MOE_WEIGHTS_MXFP4) return MOE_ERR_ENUM;
+  // MXFP8 activations run the scaled MFMA on native MXFP4 weights only
+  if (d->act_format == MOE_ACT_MXFP8 && d->weight_format != MOE_WEIGHTS_MXFP4) return MOE_ERR_SHAPE;
   return MOE_OK;
 }
 
@@ -166,8 +169,9 @@ int moe_plan(const moe_desc* desc, moe_plan_t** plan, size_t* packed_bytes, size
   p->ws_trow = o; o = align_up(o + 8 * (size_t)p->max_tiles);
   p->ws_tcnt = o; o = align_up(o + 16);
   p->ws_plan = o; o = align_up(o + 4 * plan_scratch_ints(Tm, k, E));
-  const bool fp4x = desc->act_format != MOE_ACT_BF16, fp4h = desc->act_format == MOE_ACT_NVFP4_ALL;
-  p->ws_xq = o; o = align_up(o + (fp4x ? (size_t)Tm * H / 2 : 0));
+  const bool mx8 = desc->act_format == MOE_ACT_MXFP8;
+  const bool fp4x = desc->act_format != MOE_ACT_BF16, fp4h = desc->act_format == MOE_ACT_NVFP4_ALL || mx8;
+  p->ws_xq = o; o = align_up(o + (fp4x ? (size_t)Tm * H / (mx8 ? 1 : 2) : 0));   // codes (MXFP8: a byte each)
   p->ws_xs = o; o = align_up(o + (fp4x ? (size_t)Tm * H / 16 : 0));
   p->ws_xg = o; o = align_up(o + 4 * (size_t)Tm);      // per-row activation factor (either format)
   p->ws_x16 = o; o = align_up(o + (desc->act_format == MOE_ACT_BF16 ? 2 * (size_t)Tm * H : 0));
@@ -175,7 +179,7 @@ int moe_plan(const moe_desc* desc, moe_plan_t** plan, size_t* packed_bytes, size
   p->ws_hexp = o; o = align_up(o + (fp4h ? 0 : rows * (I / 16)));  // per-16-column h exponents
   p->ws_hmin = o; o = align_up(o + 4 * rows);                       // per-row minimum h exponent
   p->ws_hf = o; o = align_up(o + (fp4h ? 4 * rows * I : 0));       // NVFP4 h: fp32 h rows,
-  p->ws_hq = o; o = align_up(o + (fp4h ? rows * I / 2 : 0));       // their codes,
+  p->ws_hq = o; o = align_up(o + (fp4h ? rows * I / (mx8 ? 1 : 2) : 0));   // their codes,
   p->ws_hs = o; o = align_up(o + (fp4h ? rows * (I / 16) : 0));    // block scales
   p->ws_hg = o; o = align_up(o + (fp4h ? 4 * rows : 0));           // and global scales
   p->ws_y = o; o = align_up(o + 2 * rows * H);         // y16
@@ -226,7 +230,7 @@ int moe_pack_weights(const moe_plan_t* plan, const moe_nvfp4_tensor* gate_up, co
       a.N = L.N;
       a.K = L.K;
       a.gate_up = proj == 0;
-      a.mx = mx ? 1 : 0;
+      a.mx = !mx ? 0 : plan->d.act_format == MOE_ACT_MXFP8 ? 2 : 1;   // 2: native for the scaled MFMA
       a.fp4_out = base + (proj ? plan->off_w2f : plan->off_w1f) + g0 * L.fp4_expert;
       a.sc_out = base + (proj ? plan->off_w2s : plan->off_w1s) + g0 * L.sc_expert;
       a.gs_out = (float*)(base + (proj ? plan->off_w2g : plan->off_w1g)) + g0;
@@ -305,30 +309,35 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
   uint8_t* ws = (uint8_t*)workspace;
   const uint8_t* pk = (const uint8_t*)packed;
   const int H = d.hidden, I = d.inter, E = d.num_experts, k = d.top_k, S = d.num_shared;
-  const bool fp4 = d.act_format != MOE_ACT_BF16;            // x row-quantised to NVFP4
+  const bool mx8 = d.act_format == MOE_ACT_MXFP8;           // x and h MXFP8, scaled MFMA (W4A8)
+  const bool fp4 = d.act_format != MOE_ACT_BF16 && !mx8;    // x row-quantised to NVFP4
   const bool fp4h = d.act_format == MOE_ACT_NVFP4_ALL;      // h too, before the down GEMM
   hipError_t e;
 
-  uint8_t* xq = (fp4 && r.act_packed) ? r.act_packed : ws + plan->ws_xq;
-  uint8_t* xs = (fp4 && r.act_scales) ? r.act_scales : ws + plan->ws_xs;
+  uint8_t* xq = ((fp4 || mx8) && r.act_packed) ? r.act_packed : ws + plan->ws_xq;
+  uint8_t* xs = ((fp4 || mx8) && r.act_scales) ? r.act_scales : ws + plan->ws_xs;
   float* xg = (fp4 && r.act_global) ? r.act_global : (float*)(ws + plan->ws_xg);
   uint16_t* x16 = (uint16_t*)(ws + plan->ws_x16);
   const bool decode = use_decode(T, k, E);
   // Activation preparation: NVFP4 row quantisation, or the exact power-of-two rescale into
   // fp16 (its 1-op dequant route); decode batches below DECODE_F16_ROWS rows feed their bf16
   // rows to the GEMM as they are (the extra launch costs more than the dequant saves there).
-  const GemmMode gu_mode = fp4 ? GEMM_GATEUP_FP4
-                               : (decode && T * k < DECODE_F16_ROWS) ? GEMM_GATEUP_BF16 : GEMM_GATEUP_F16;
+  const GemmMode gu_mode = mx8 ? GEMM_GATEUP_MX8
+                          : fp4 ? GEMM_GATEUP_FP4
+                                : (decode && T * k < DECODE_F16_ROWS) ? GEMM_GATEUP_BF16 : GEMM_GATEUP_F16;
   if ((e = mark(ev, 2 * MOE_STAGE_QUANT, s)) != hipSuccess) return (int)e;
-  if (fp4)
+  if (mx8)
+    e = launch_mxfp8_rows_bf16(x, T, H, xq, xs, s);
+  else if (fp4)
     e = launch_quant_rows_bf16(x, T, H, xq, xs, xg, s);
   else if (gu_mode == GEMM_GATEUP_F16)
     e = launch_rows_to_f16(x, T, H, x16, xg, s);
   if (e != hipSuccess) return (int)e;
   if ((e = mark(ev, 2 * MOE_STAGE_QUANT + 1, s)) != hipSuccess) return (int)e;
 
-  const int M = decode ? DECODE_TILE_ROWS : PREFILL_TILE_ROWS;
-  const GemmRegime regime = decode ? REGIME_DECODE_KSPLIT : REGIME_PREFILL;
+  // the MX8 GEMMs run 16-row tiles in every regime
+  const int M = decode || mx8 ? DECODE_TILE_ROWS : PREFILL_TILE_ROWS;
+  const GemmRegime regime = decode || mx8 ? REGIME_DECODE_KSPLIT : REGIME_PREFILL;
   RouteArgs ra;
   ra.logits = router_logits;
   ra.T = T;
@@ -354,7 +363,7 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
   pa.tile_rows = M;
   // prefill batches averaging at most 64 rows per expert: experts with few rows (skewed
   // routing) go to the decode GEMM through a second tile list
-  const bool split = !decode && (long)T * k <= 64L * E;
+  const bool split = !decode && !mx8 && (long)T * k <= 64L * E;
   pa.cold_rows = split ? COLD_ROWS : 0;
   pa.counts = (int32_t*)(ws + plan->ws_counts);
   pa.offsets = (int32_t*)(ws + plan->ws_offsets);
@@ -394,7 +403,7 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
   g1.out = (uint16_t*)(ws + plan->ws_h);
   g1.hexp = (int8_t*)(ws + plan->ws_hexp);
   g1.hmin = decode ? nullptr : pa.hmin;
-  g1.hf = fp4h ? (float*)(ws + plan->ws_hf) : nullptr;
+  g1.hf = fp4h || mx8 ? (float*)(ws + plan->ws_hf) : nullptr;
   g1.clamp_groups = d.swiglu_clamp ? E : 0;      // routed experts only
   g1.swiglu_limit = d.swiglu_limit;
   // second-list (cold) launches: the decode GEMM over list 2
@@ -424,7 +433,7 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
   g2.hf = nullptr;
   g2.yout = (uint16_t*)(ws + plan->ws_y);
   g2.yexp = (int8_t*)(ws + plan->ws_yexp);
-  const GemmMode dn_mode = fp4h ? GEMM_DOWN_FP4 : GEMM_DOWN;
+  const GemmMode dn_mode = mx8 ? GEMM_DOWN_MX8 : fp4h ? GEMM_DOWN_FP4 : GEMM_DOWN;
   {
     const LaunchEvents le = stage_events(ev, MOE_STAGE_DOWN);
     LaunchEvents first = split ? LaunchEvents{le.start, nullptr} : le;
@@ -436,6 +445,12 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
       first.start = nullptr;
       e = launch_quant_rows_f32(g1.hf, T * k + S * T, I, ws + plan->ws_hq, ws + plan->ws_hs,
                                 (float*)(ws + plan->ws_hg), s);
+    } else if (mx8) {   // every h row MXFP8-quantised (E8M0 per 32 columns)
+      g2.xq = ws + plan->ws_hq;
+      g2.xs = ws + plan->ws_hs;
+      if ((e = mark(ev, 2 * MOE_STAGE_DOWN, s)) != hipSuccess) return (int)e;
+      first.start = nullptr;
+      e = launch_mxfp8_rows_f32(g1.hf, T * k + S * T, I, ws + plan->ws_hq, ws + plan->ws_hs, s);
     }
     if (e == hipSuccess) e = launch_gemm(dn_mode, regime, max_tiles, est_tiles, g2, s, first);
     if (e == hipSuccess && split)
@@ -488,7 +503,8 @@ int moe_validate_weights_host(const moe_desc* in, const moe_nvfp4_tensor* t, int
   const size_t N = up ? 2 * (size_t)desc->inter : (size_t)desc->hidden;
   const size_t K = up ? (size_t)desc->hidden : (size_t)desc->inter;
   if (mx) {
-    // E8M0: no NaN byte, and every block within 17 binades of its expert's largest scale
+    // E8M0: no NaN byte, and (when re-expressed as NVFP4 for 16-bit MFMAs, i.e. without
+    // MXFP8 activations) every block within 17 binades of its expert's largest scale
     const size_t per = N * (K / 32);
     for (int g = 0; g < G; ++g) {
       const uint8_t* sc = t->scales + (size_t)g * per;
@@ -497,8 +513,9 @@ int moe_validate_weights_host(const moe_desc* in, const moe_nvfp4_tensor* t, int
         if (sc[i] == 0xFFu) return MOE_ERR_WEIGHT;
         m = std::max(m, (int)sc[i]);
       }
-      for (size_t i = 0; i < per; ++i)
-        if ((int)sc[i] < m - MX_SCALE_SPAN) return MOE_ERR_WEIGHT;
+      if (desc->act_format != MOE_ACT_MXFP8)
+        for (size_t i = 0; i < per; ++i)
+          if ((int)sc[i] < m - MX_SCALE_SPAN) return MOE_ERR_WEIGHT;
     }
     return MOE_OK;
   }

@@ -89,6 +89,20 @@ struct WOps<false> {
   }
 };
 
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// One scaled MFMA 16x16x128 on raw MX codes: A = 16 weight rows of E2M1 (lane l: row l%16,
+// k 32(l/16) .. +31, low nibble first; its E8M0 scale sa in the low byte), B = 16 token rows
+// of E4M3 (lane l: row l%16, k 16(l/16) .. +15 in its first 16 bytes and 64 + 16(l/16) .. +15
+// in the next 16; E8M0 scale sb of the token's block l/16). This pairing of the two operands'
+// k with the scale blocks was measured on gfx950 with one-hot inputs.
+__device__ __forceinline__ f32x4 mfma_mx(const u32x4& a, uint32_t sa, const u32x4& b0, const u32x4& b1, uint32_t sb,
+                                         f32x4 c) {
+  const i32x8 av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+  const i32x8 bv = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 0, 0, (int)sa, 0, (int)sb);
+}
+
 __device__ __forceinline__ f32x4 mfma_any(const f16x8& a, const u32x4& b, f32x4 c) {
   return mfma16x16x32_f16(a, __builtin_bit_cast(f16x8, b), c);
 }
@@ -194,6 +208,8 @@ constexpr int DEC_MAX_WAVES = 4;   // measured best of 4 / 8 / 16 on the decode 
 template <int MODE, int NSUB>
 __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs a) {
   constexpr bool F16 = MODE != GEMM_GATEUP_BF16;           // fp16 MFMA (bf16 x: bf16 MFMA)
+  constexpr bool MX8 = MODE == GEMM_GATEUP_MX8 || MODE == GEMM_DOWN_MX8;   // scaled MFMA on MX codes
+  constexpr bool DOWNM = MODE == GEMM_DOWN || MODE == GEMM_DOWN_FP4 || MODE == GEMM_DOWN_MX8;
   const int slot = blockIdx.y;
   // the slot's entries are read together with the count (slots past it hold stale values
   // that are never used; the tile arrays have room for any grid), saving one dependent
@@ -228,6 +244,10 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs a) {
     qrow = a.xq + (size_t)row * (L.K / 2);
     srow = a.xs + (size_t)row * (L.K / 16);
     sc *= a.xg[row];
+  } else if (MX8) {                                          // MXFP8 rows: codes and E8M0 scales
+    const int t = MODE == GEMM_DOWN_MX8 ? row : a.tok[row];
+    qrow = a.xq + (size_t)t * L.K;
+    srow = a.xs + (size_t)t * (L.K / 32);
   } else {
     const int t = a.tok[row];
     if (MODE == GEMM_GATEUP_FP4) {
@@ -254,6 +274,15 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs a) {
     u32x4 wv[NSUB];
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) wv[s] = *fp4_tile(a, L, g, q0 + s, kc);
+    if constexpr (MX8) {
+      const u32x4 b0 = *(const u32x4*)(qrow + (size_t)kc * KCHUNK + 16 * lg);
+      const u32x4 b1 = *(const u32x4*)(qrow + (size_t)kc * KCHUNK + 64 + 16 * lg);
+      const uint32_t sb = srow[kc * 4 + lg];
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s)
+        acc[s] = mfma_mx(wv[s], chunk_scale_bytes(sgv[s], kc & 7) & 0xFFu, b0, b1, sb, acc[s]);
+      continue;
+    }
     u32x4 bop[4];
     if (MODE == GEMM_GATEUP_FP4 || MODE == GEMM_DOWN_FP4) {
       const u32x4 xv = *(const u32x4*)(qrow + (size_t)kc * 64 + lg * 16);
@@ -292,7 +321,7 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs a) {
   // wave w finishes tiles w, w + NW, ...: fixed-order sum over the K ranges
   if (l16 >= nvalid) return;
   const int orow = row0 + l16;                             // == row on the lanes that remain
-  if (MODE == GEMM_DOWN || MODE == GEMM_DOWN_FP4) {
+  if (DOWNM) {
     for (int s = wave; s < NSUB; s += NW) {
       f32x4 sum = red[0][s][lane];
       for (int w = 1; w < NW; ++w) sum += red[w][s][lane];
@@ -737,6 +766,9 @@ hipError_t launch_gemm(GemmMode mode, GemmRegime regime, int max_tiles, int est_
     case GEMM_GATEUP_FP4: launch_mode<GEMM_GATEUP_FP4>(regime, max_tiles, est_tiles, a, s, ev); break;
     case GEMM_DOWN: launch_mode<GEMM_DOWN>(regime, max_tiles, est_tiles, a, s, ev); break;
     case GEMM_DOWN_FP4: launch_mode<GEMM_DOWN_FP4>(regime, max_tiles, est_tiles, a, s, ev); break;
+    // the MX8 modes run the decode GEMM in every regime (16-row tiles)
+    case GEMM_GATEUP_MX8: launch_decode<GEMM_GATEUP_MX8>(max_tiles, est_tiles, a, s, ev); break;
+    case GEMM_DOWN_MX8: launch_decode<GEMM_DOWN_MX8>(max_tiles, est_tiles, a, s, ev); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -54,6 +54,10 @@ bool plan_small_ok(int T, int k);
 // Activation / weight quantiser.
 hipError_t launch_quant_rows_bf16(const uint16_t* x, int rows, int K, uint8_t* packed, uint8_t* scales,
                                   float* gs, hipStream_t s);
+// MXFP8 rows (codes [rows][K], E8M0 scales [rows][K/32]) from bf16 or fp32 rows.
+hipError_t launch_mxfp8_rows_bf16(const uint16_t* x, int rows, int K, uint8_t* codes, uint8_t* scales,
+                                  hipStream_t s);
+hipError_t launch_mxfp8_rows_f32(const float* x, int rows, int K, uint8_t* codes, uint8_t* scales, hipStream_t s);
 // fp32 rows (h before the NVFP4 down GEMM), each with its own global scale.
 hipError_t launch_quant_rows_f32(const float* x, int rows, int K, uint8_t* packed, uint8_t* scales, float* gs,
                                  hipStream_t s);
@@ -73,7 +77,8 @@ struct PackArgs {
   const float* gs;         // [G] (NVFP4)
   int G, N, K;
   int gate_up;             // 1: interleave gate/up 16-row tiles
-  int mx;                  // 1: MXFP4 input, re-expressed as E4M3 blocks + per-expert gs
+  int mx;                  // 1: MXFP4 input, re-expressed as E4M3 blocks + per-expert gs, or
+                           // 2: MXFP4 kept native (raw E8M0 scale bytes for the scaled MFMA, gs 1)
   uint8_t* fp4_out;        // [G][N/16][KC][64][16]
   uint8_t* sc_out;         // [G][N/16][KSG][64][16]
   float* gs_out;           // [G]
@@ -84,7 +89,13 @@ hipError_t launch_pack(const PackArgs& a, hipStream_t s);
 // gate_up modes: F16 = activations pre-scaled into fp16 (x16) and fp16 MFMA; BF16 = the
 // caller's bf16 rows read directly, bf16 MFMA; FP4 = NVFP4 activation rows. down modes:
 // DOWN = h16 rows; DOWN_FP4 = h row-quantised to NVFP4 (xq/xs/xg indexed by row).
-enum GemmMode { GEMM_GATEUP_F16 = 0, GEMM_GATEUP_FP4 = 1, GEMM_DOWN = 2, GEMM_GATEUP_BF16 = 3, GEMM_DOWN_FP4 = 4 };
+// MX8 modes (MXFP4 weights with MXFP8 activations: xq = E4M3 codes [rows][K], xs = E8M0
+// scales [rows][K/32]; gate_up gathers token rows, down reads its own rows) run the scaled
+// MFMA on the raw codes, no dequantisation.
+enum GemmMode {
+  GEMM_GATEUP_F16 = 0, GEMM_GATEUP_FP4 = 1, GEMM_DOWN = 2, GEMM_GATEUP_BF16 = 3, GEMM_DOWN_FP4 = 4,
+  GEMM_GATEUP_MX8 = 5, GEMM_DOWN_MX8 = 6
+};
 
 struct GemmArgs {
   // weights (packed layout of one projection, G groups)

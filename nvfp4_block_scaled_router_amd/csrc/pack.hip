@@ -12,6 +12,8 @@
 // MXFP4 input (E2M1 codes with E8M0 scales per 32 k, [vllm.cpp] capability table, MXFP4
 // row) is re-expressed exactly in this form: per expert gs = 2^(m - 135), m its largest
 // scale byte, and both E4M3 block scales of a 32-column block = 2^(byte - m + 8).
+// With MXFP8 activations the MXFP4 weights stay native instead: the scale tile holds the
+// raw E8M0 byte of each chunk's block (twice, in the two slots of the chunk) and gs = 1.
 // For gate_up, tile q maps to boundary rows 16*(q/2) + r (q even: gate) or
 // I + 16*(q/2) + r (q odd: up), so gate and up tiles of the same columns alternate.
 #include "common.hpp"
@@ -78,7 +80,17 @@ __global__ __launch_bounds__(256) void pack_scales_kernel(PackArgs a) {
     const int g = (int)(rest / (a.N / 16));
     const int row = boundary_row(q, lane % 16, a.N, a.gate_up);
     uint8_t b[16];
-    if (a.mx) {
+    if (a.mx == 2) {
+      // MXFP4 for the scaled MFMA: the raw E8M0 byte of the lane's 32-column block of chunk kc
+      const uint8_t* src = a.scales + ((size_t)g * a.N + row) * (a.K / 32);
+#pragma unroll
+      for (int c = 0; c < SCALE_GROUP; ++c) {
+        const int kc = sg * SCALE_GROUP + c;
+        const uint8_t e8 = kc < L.KC ? src[kc * 4 + lane / 16] : 0;
+        b[2 * c] = e8;
+        b[2 * c + 1] = e8;
+      }
+    } else if (a.mx) {
       // MXFP4: the lane's 32 columns of chunk kc are one E8M0 block, re-expressed as two
       // equal E4M3 block scales 2^(byte - m + 8) against the expert's gs = 2^(m - 135)
       const int m = ilogbf(a.gs_out[g]) + 135;
@@ -107,14 +119,14 @@ __global__ __launch_bounds__(256) void pack_scales_kernel(PackArgs a) {
     v.w = b[12] | (b[13] << 8) | (b[14] << 16) | ((uint32_t)b[15] << 24);
     *(u32x4*)(a.sc_out + u * 16) = v;
   }
-  if (blockIdx.x == 0 && !a.mx)
-    for (int g = threadIdx.x; g < a.G; g += blockDim.x) a.gs_out[g] = a.gs[g];
+  if (blockIdx.x == 0 && a.mx != 1)   // NVFP4: the boundary's scales; native MXFP4: 1
+    for (int g = threadIdx.x; g < a.G; g += blockDim.x) a.gs_out[g] = a.mx ? 1.0f : a.gs[g];
 }
 
 hipError_t launch_pack(const PackArgs& a, hipStream_t s) {
   if (a.G <= 0) return hipSuccess;
   hipLaunchKernelGGL(pack_fp4_kernel, dim3(2048), dim3(256), 0, s, a);
-  if (a.mx) hipLaunchKernelGGL(pack_mx_gs_kernel, dim3(a.G), dim3(256), 0, s, a);
+  if (a.mx == 1) hipLaunchKernelGGL(pack_mx_gs_kernel, dim3(a.G), dim3(256), 0, s, a);
   hipLaunchKernelGGL(pack_scales_kernel, dim3(1024), dim3(256), 0, s, a);
   return hipGetLastError();
 }

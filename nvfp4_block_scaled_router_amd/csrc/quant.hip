@@ -126,6 +126,46 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const T* __restrict__ x
   wave_quant_row(row, K, g, packed + (size_t)r * (K / 2), scales + (size_t)r * (K / 16));
 }
 
+// MXFP8 rows (the W4A8 profile's activations): per 32 consecutive k one E8M0 scale 2^X with
+// X = floor(log2 max|x|) - 8 (8 = the exponent of E4M3's largest normal, 448 = 1.75 2^8),
+// clamped to [-127, 127] (-127 for a zero block or one below 2^-118), and E4M3 codes of
+// |x| 2^-X (exact power-of-two scaling, round to nearest even, saturating at 448) with the
+// sign of x. One wave per row, a lane per 32-column block.
+template <typename T>
+__global__ __launch_bounds__(256) void mxfp8_rows_kernel(const T* __restrict__ x, int rows, int K,
+                                                         uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const int lane = threadIdx.x & (WAVE - 1);
+  const T* row = x + (size_t)r * K;
+  for (int b = lane; b < K / 32; b += WAVE) {
+    float v[32];
+    load16(row + (size_t)b * 32, v);
+    load16(row + (size_t)b * 32 + 16, v + 16);
+    float A = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) A = fmaxf(A, fabsf(v[i]));
+    // A = f 2^E with f in [0.5, 1): floor(log2 A) = E - 1; below 2^-118 the clamp decides
+    int X = A < 0x1p-118f ? -127 : min(__builtin_amdgcn_frexp_expf(A) - 1 - 8, 127);
+    scales[(size_t)r * (K / 32) + b] = (uint8_t)(X + 127);
+    uint32_t w[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      uint32_t word = 0u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float e = v[4 * q + i];
+        const uint32_t code = ((__float_as_uint(e) >> 31) << 7) | e4m3_encode_rne_sat(__builtin_ldexpf(fabsf(e), -X));
+        word |= code << (8 * i);
+      }
+      w[q] = word;
+    }
+    uint8_t* dst = codes + (size_t)r * K + (size_t)b * 32;
+    *(u32x4*)dst = u32x4{w[0], w[1], w[2], w[3]};
+    *(u32x4*)(dst + 16) = u32x4{w[4], w[5], w[6], w[7]};
+  }
+}
+
 // Group maxima: one 1024-thread workgroup per group, fixed reduction tree.
 __global__ __launch_bounds__(1024) void group_gs_f32_kernel(const float* __restrict__ x, int rows_per_group, int K,
                                                             float* __restrict__ gs) {
@@ -218,6 +258,19 @@ hipError_t launch_quant_rows_f32(const float* x, int rows, int K, uint8_t* packe
   if (rows <= 0) return hipSuccess;
   hipLaunchKernelGGL(quant_rows_kernel<float>, dim3((rows + 3) / 4), dim3(256), 0, s, x, rows, K, packed, scales,
                      gs);
+  return hipGetLastError();
+}
+
+hipError_t launch_mxfp8_rows_bf16(const uint16_t* x, int rows, int K, uint8_t* codes, uint8_t* scales,
+                                  hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(mxfp8_rows_kernel<uint16_t>, dim3((rows + 3) / 4), dim3(256), 0, s, x, rows, K, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_mxfp8_rows_f32(const float* x, int rows, int K, uint8_t* codes, uint8_t* scales, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(mxfp8_rows_kernel<float>, dim3((rows + 3) / 4), dim3(256), 0, s, x, rows, K, codes, scales);
   return hipGetLastError();
 }
 

@@ -59,7 +59,9 @@ def plan_rc(d):
     (dict(max_tokens=0), m.MOE_ERR_SHAPE),
     (dict(num_shared=2), m.MOE_ERR_SHAPE),
     (dict(score=5), m.MOE_ERR_ENUM),
-    (dict(act=3), m.MOE_ERR_ENUM),
+    (dict(act=4), m.MOE_ERR_ENUM),
+    (dict(act="mxfp8"), m.MOE_ERR_SHAPE),                   # MXFP8 activations need MXFP4 weights
+    (dict(act="mxfp8", weights="mxfp4"), m.MOE_OK),
     # router / activation variants (ABI 2)
     (dict(score="sqrt_softplus", use_bias=True, n_group=4, topk_group=2, routed_scaling=2.5,
           swiglu_limit=10.0), m.MOE_OK),
@@ -205,8 +207,11 @@ def test_validate_mxfp4_weights_host():
     assert m.moe_validate_weights_host(d, t, 0) == m.MOE_OK
     scales[2, 5, 1] = 120 - 18
     assert m.moe_validate_weights_host(d, t, 0) == m.MOE_ERR_WEIGHT
+    d8 = desc(weights="mxfp4", act="mxfp8")            # native E8M0 for the scaled MFMA: any span
+    assert m.moe_validate_weights_host(d8, t, 0) == m.MOE_OK
     scales[2, 5, 1] = 0xFF                             # E8M0 NaN
     assert m.moe_validate_weights_host(d, t, 0) == m.MOE_ERR_WEIGHT
+    assert m.moe_validate_weights_host(d8, t, 0) == m.MOE_ERR_WEIGHT
     scales[2, 5, 1] = 120
     t_nv = m.nvfp4_tensor(packed.ctypes.data, scales.ctypes.data, None)
     assert m.moe_validate_weights_host(desc(), t_nv, 0) == m.MOE_ERR_NULL   # NVFP4 needs its global scale

@@ -1,4 +1,6 @@
 """GPU parity of the whole layer against the CPU oracle (through the C ABI)."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -25,6 +27,9 @@ def _run_and_check(case: Case):
     assert np.array_equal(bufs["expert_counts"].cpu().numpy(), ref["counts"]), "counts"
     assert np.array_equal(bufs["expert_offsets"].cpu().numpy(), ref["offsets"]), "offsets"
     assert np.array_equal(bufs["perm"].cpu().numpy(), ref["perm"]), "perm"
+    if cfg.act == "mxfp8":
+        assert np.array_equal(bufs["act_packed"].cpu().numpy(), ref["xq"]), "MXFP8 activation codes"
+        assert np.array_equal(bufs["act_scales"].cpu().numpy(), ref["xs"]), "MXFP8 activation scales"
     if cfg.act in ("nvfp4", "nvfp4_all"):
         assert np.array_equal(bufs["act_packed"].cpu().numpy(), ref["xq"]), "quantised activation codes"
         assert np.array_equal(bufs["act_scales"].cpu().numpy(), ref["xs"]), "quantised activation scales"
@@ -214,6 +219,26 @@ def test_w4a4_down(cfg):
 def test_skewed_w4a4_down_sampled():
     cfg = synth.skewed_w4a4_all()
     _run_and_check(Case(cfg, tokens=synth.token_sample(cfg, 64)))
+
+
+# W4A8: MXFP4 weights with MXFP8 x and h through the block-scaled MFMA (decode-sized and
+# larger batches, a shared expert, the V4-Flash router and clamp, the V4-Flash shape, the
+# widest intermediate size)
+W4A8 = [
+    synth.MoeConfig("w4a8-decode", T=8, H=256, I=128, E=16, k=4, act="mxfp8", wfmt="mxfp4", seed=71),
+    synth.MoeConfig("w4a8-prefill-shared", T=300, H=512, I=256, E=8, k=2, shared=1, act="mxfp8", wfmt="mxfp4",
+                    seed=72),
+    synth.MoeConfig("w4a8-v4-router-clamp", T=64, H=512, I=256, E=32, k=6, shared=1, score="sqrt_softplus",
+                    bias_sigma=0.5, swiglu_limit=10.0, act="mxfp8", wfmt="mxfp4", seed=73),
+    dataclasses.replace(synth.deepseek_v4_flash(8), name="w4a8-deepseek-v4-flash-t8", act="mxfp8"),
+    synth.MoeConfig("w4a8-max-inter", T=40, H=128, I=16384, E=4, k=2, shared=1, act="mxfp8", wfmt="mxfp4",
+                    seed=74),
+]
+
+
+@pytest.mark.parametrize("cfg", W4A8, ids=lambda c: c.name)
+def test_w4a8_mx(cfg):
+    _run_and_check(Case(cfg, tokens=synth.token_sample(cfg, 24) if cfg.I > 4096 else None))
 
 
 # the descriptor's limits: hidden and intermediate 16384 (128 K chunks), 65536 tokens
