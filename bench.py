@@ -61,6 +61,7 @@ from nvfp4_block_scaled_router_amd.weights import quantize_projection  # noqa: E
 METRIC = "NVFP4 fused-MoE tokens/s; decode HBM GB/s and prefill TFLOP/s vs peak"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+FP8_PEAK_TFLOPS = 5000.0        # dense fp8 MFMA (the W4A8 scaled MFMA: E2M1 x E4M3 operands)
 NVFP4_BYTES_PER_WEIGHT = 0.5 + 1.0 / 16.0      # E2M1 nibble + one E4M3 byte per 16
 
 
@@ -85,6 +86,13 @@ def workload(name):
     # DeepSeek-V3's grouped sigmoid router with bias and routed scaling)
     if name == "deepseek-v4-flash-decode":
         return [synth.deepseek_v4_flash(T) for T in synth.DECODE_TOKENS], "hbm"
+    # the V4-Flash layer in its W4A8 profile (MXFP8 x and h, the block-scaled MFMA)
+    if name == "deepseek-v4-flash-w4a8-decode":
+        return [synth.deepseek_v4_flash_w4a8(T) for T in synth.DECODE_TOKENS], "hbm"
+    if name == "deepseek-v4-flash-w4a8-prefill":
+        return [synth.deepseek_v4_flash_w4a8(8192)], "mfma"
+    if name == "deepseek-v4-flash-prefill":           # the same batch in W4A16 (bf16 x, 16-bit MFMA)
+        return [synth.deepseek_v4_flash(8192)], "mfma"
     if name == "deepseek-v3-noaux":
         return [synth.deepseek_v3_router(8192)], "mfma"
     # one rank's routed DeepSeek-V4-Flash MoE on the sharing workloads: T = 6 at 0..100%
@@ -150,8 +158,8 @@ class Batch:
     def gate_up_bytes(self):
         c = self.cfg
         w = (self.touched + c.shared) * self.weight_bytes(2 * c.I * c.H)
-        act = c.T * c.H * (2 if c.act == "bf16" else NVFP4_BYTES_PER_WEIGHT + 4.0 / c.H)
-        h = (self.rows + c.shared * c.T) * c.I * (4 if c.act == "nvfp4_all" else 2)   # fp32 h / h16
+        act = c.T * c.H * {"bf16": 2.0, "mxfp8": 1.0 + 1.0 / 32}.get(c.act, NVFP4_BYTES_PER_WEIGHT + 4.0 / c.H)
+        h = (self.rows + c.shared * c.T) * c.I * (4 if c.act in ("nvfp4_all", "mxfp8") else 2)   # fp32 h / h16
         return w + act + h
 
     def gate_up_flops(self):
@@ -490,8 +498,9 @@ def main():
     else:
         work = sum(b.gate_up_flops() for b in batches)
         achieved = work / (gu_time / 1e3) / 1e12
-        roof = {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None}
+        peak = FP8_PEAK_TFLOPS if cfgs[0].act == "mxfp8" else BF16_PEAK_TFLOPS
+        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                "frac": achieved / peak, "traffic": None}
     roof["kernel"] = "gate_up grouped GEMM (+SwiGLU)"
     roof["launch_ms"] = gu_time / len(batches)
     roof["algorithmic_bytes_per_launch"] = sum(b.gate_up_bytes() for b in batches) / len(batches)
@@ -515,7 +524,7 @@ def main():
     res = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "vs_baseline": None, "dtype": "fp8xfp4" if cfgs[0].act == "mxfp8" else "bf16", "data": "synthetic",
         "config": {"workload": args.workload, "T": [c.T for c in cfgs], "H": cfgs[0].H, "I": cfgs[0].I,
                    "E": cfgs[0].E, "top_k": cfgs[0].k, "score": cfgs[0].score, "shared": cfgs[0].shared,
                    "activations": cfgs[0].act,

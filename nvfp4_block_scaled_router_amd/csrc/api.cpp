@@ -170,17 +170,17 @@ int moe_plan(const moe_desc* desc, moe_plan_t** plan, size_t* packed_bytes, size
   p->ws_tcnt = o; o = align_up(o + 16);
   p->ws_plan = o; o = align_up(o + 4 * plan_scratch_ints(Tm, k, E));
   const bool mx8 = desc->act_format == MOE_ACT_MXFP8;
-  const bool fp4x = desc->act_format != MOE_ACT_BF16, fp4h = desc->act_format == MOE_ACT_NVFP4_ALL || mx8;
+  const bool fp4x = desc->act_format != MOE_ACT_BF16, fp4h = desc->act_format == MOE_ACT_NVFP4_ALL;
   p->ws_xq = o; o = align_up(o + (fp4x ? (size_t)Tm * H / (mx8 ? 1 : 2) : 0));   // codes (MXFP8: a byte each)
   p->ws_xs = o; o = align_up(o + (fp4x ? (size_t)Tm * H / 16 : 0));
   p->ws_xg = o; o = align_up(o + 4 * (size_t)Tm);      // per-row activation factor (either format)
   p->ws_x16 = o; o = align_up(o + (desc->act_format == MOE_ACT_BF16 ? 2 * (size_t)Tm * H : 0));
-  p->ws_h = o; o = align_up(o + (fp4h ? 0 : 2 * rows * I));        // h16
-  p->ws_hexp = o; o = align_up(o + (fp4h ? 0 : rows * (I / 16)));  // per-16-column h exponents
+  p->ws_h = o; o = align_up(o + (fp4h || mx8 ? 0 : 2 * rows * I));        // h16
+  p->ws_hexp = o; o = align_up(o + (fp4h || mx8 ? 0 : rows * (I / 16)));  // per-16-column h exponents
   p->ws_hmin = o; o = align_up(o + 4 * rows);                       // per-row minimum h exponent
-  p->ws_hf = o; o = align_up(o + (fp4h ? 4 * rows * I : 0));       // NVFP4 h: fp32 h rows,
-  p->ws_hq = o; o = align_up(o + (fp4h ? rows * I / (mx8 ? 1 : 2) : 0));   // their codes,
-  p->ws_hs = o; o = align_up(o + (fp4h ? rows * (I / 16) : 0));    // block scales
+  p->ws_hf = o; o = align_up(o + (fp4h || mx8 ? 4 * rows * I : 0));   // NVFP4 / prefill MXFP8 h: fp32 h rows,
+  p->ws_hq = o; o = align_up(o + (fp4h ? rows * I / 2 : mx8 ? rows * I : 0));   // their codes (MXFP8 h too),
+  p->ws_hs = o; o = align_up(o + (fp4h ? rows * (I / 16) : mx8 ? rows * (I / 32) : 0));   // block scales
   p->ws_hg = o; o = align_up(o + (fp4h ? 4 * rows : 0));           // and global scales
   p->ws_y = o; o = align_up(o + 2 * rows * H);         // y16
   p->ws_yexp = o; o = align_up(o + rows * (H / 16));  // per-16-column y exponents
@@ -335,9 +335,10 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
   if (e != hipSuccess) return (int)e;
   if ((e = mark(ev, 2 * MOE_STAGE_QUANT + 1, s)) != hipSuccess) return (int)e;
 
-  // the MX8 GEMMs run 16-row tiles in every regime
-  const int M = decode || mx8 ? DECODE_TILE_ROWS : PREFILL_TILE_ROWS;
-  const GemmRegime regime = decode || mx8 ? REGIME_DECODE_KSPLIT : REGIME_PREFILL;
+  // MX8 prefill batches whose experts average under 80 rows use 64-row tiles (less of the
+  // last tile of each expert left empty)
+  const int M = decode ? DECODE_TILE_ROWS : (mx8 && (long)T * k < 80L * E) ? 64 : PREFILL_TILE_ROWS;
+  const GemmRegime regime = decode ? REGIME_DECODE_KSPLIT : REGIME_PREFILL;
   RouteArgs ra;
   ra.logits = router_logits;
   ra.T = T;
@@ -363,7 +364,7 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
   pa.tile_rows = M;
   // prefill batches averaging at most 64 rows per expert: experts with few rows (skewed
   // routing) go to the decode GEMM through a second tile list
-  const bool split = !decode && !mx8 && (long)T * k <= 64L * E;
+  const bool split = !decode && (long)T * k <= 64L * E;
   pa.cold_rows = split ? COLD_ROWS : 0;
   pa.counts = (int32_t*)(ws + plan->ws_counts);
   pa.offsets = (int32_t*)(ws + plan->ws_offsets);
@@ -400,10 +401,17 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
   g1.tile_row0 = pa.tile_row0;
   g1.tile_count = pa.tile_count;
   g1.offsets = pa.offsets;
+  g1.tile_rows = M;
   g1.out = (uint16_t*)(ws + plan->ws_h);
   g1.hexp = (int8_t*)(ws + plan->ws_hexp);
   g1.hmin = decode ? nullptr : pa.hmin;
-  g1.hf = fp4h || mx8 ? (float*)(ws + plan->ws_hf) : nullptr;
+  // MXFP8 h: quantised in the decode GEMM's epilogue (a workgroup holds whole 32-column
+  // blocks), or written as fp32 by the prefill GEMM and quantised by a row kernel
+  g1.hf = fp4h || (mx8 && !decode) ? (float*)(ws + plan->ws_hf) : nullptr;
+  if (mx8 && decode) {
+    g1.hq8 = ws + plan->ws_hq;
+    g1.hs8 = ws + plan->ws_hs;
+  }
   g1.clamp_groups = d.swiglu_clamp ? E : 0;      // routed experts only
   g1.swiglu_limit = d.swiglu_limit;
   // second-list (cold) launches: the decode GEMM over list 2
@@ -431,6 +439,8 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
   g2.x = g1.out;
   g2.out = nullptr;
   g2.hf = nullptr;
+  g2.hq8 = nullptr;
+  g2.hs8 = nullptr;
   g2.yout = (uint16_t*)(ws + plan->ws_y);
   g2.yexp = (int8_t*)(ws + plan->ws_yexp);
   const GemmMode dn_mode = mx8 ? GEMM_DOWN_MX8 : fp4h ? GEMM_DOWN_FP4 : GEMM_DOWN;
@@ -445,12 +455,14 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
       first.start = nullptr;
       e = launch_quant_rows_f32(g1.hf, T * k + S * T, I, ws + plan->ws_hq, ws + plan->ws_hs,
                                 (float*)(ws + plan->ws_hg), s);
-    } else if (mx8) {   // every h row MXFP8-quantised (E8M0 per 32 columns)
+    } else if (mx8) {
       g2.xq = ws + plan->ws_hq;
       g2.xs = ws + plan->ws_hs;
-      if ((e = mark(ev, 2 * MOE_STAGE_DOWN, s)) != hipSuccess) return (int)e;
-      first.start = nullptr;
-      e = launch_mxfp8_rows_f32(g1.hf, T * k + S * T, I, ws + plan->ws_hq, ws + plan->ws_hs, s);
+      if (!decode) {   // every h row MXFP8-quantised (E8M0 per 32 columns)
+        if ((e = mark(ev, 2 * MOE_STAGE_DOWN, s)) != hipSuccess) return (int)e;
+        first.start = nullptr;
+        e = launch_mxfp8_rows_f32(g1.hf, T * k + S * T, I, ws + plan->ws_hq, ws + plan->ws_hs, s);
+      }
     }
     if (e == hipSuccess) e = launch_gemm(dn_mode, regime, max_tiles, est_tiles, g2, s, first);
     if (e == hipSuccess && split)

@@ -91,6 +91,22 @@ __device__ __forceinline__ f16x8 dequant8_f16(uint32_t w, f16x2 s) {
   return __builtin_bit_cast(f16x8, o);
 }
 
+// Nearest E4M3fn code to v >= 0, ties to even, v >= 448 saturates to 0x7E.
+__device__ __forceinline__ uint32_t e4m3_encode_rne_sat(float v) {
+  if (!(v > 0.0f)) return 0u;
+  if (v >= 448.0f) return 0x7Eu;
+  if (v < 0.015625f) return (uint32_t)__builtin_rintf(v * 512.0f);  // subnormals: multiples of 2^-9
+  const int e = (int)((__float_as_uint(v) >> 23) & 0xFFu) - 127;     // v in [2^e, 2^(e+1))
+  const float scale = __uint_as_float((uint32_t)(3 - e + 127) << 23); // exact 2^(3-e)
+  uint32_t m = (uint32_t)__builtin_rintf(v * scale);                 // 8..16
+  int ee = e;
+  if (m == 16u) {
+    m = 8u;
+    ++ee;
+  }
+  return ((uint32_t)(ee + 7) << 3) | (m - 8u);
+}
+
 __device__ __forceinline__ f32x4 mfma16x16x32_f16(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }

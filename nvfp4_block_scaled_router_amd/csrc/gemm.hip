@@ -156,6 +156,37 @@ __device__ __forceinline__ void epilogue_pair(const GemmArgs& a, const f32x4& ga
   }
 }
 
+// MX8 gate_up epilogue for the two gate/up tile pairs of one aligned 32-column h block
+// (columns 32 blk .. +31; lane: 4 columns of each 16-column half) of token row `row`: h as in
+// epilogue_pair, then MXFP8 in registers: the block's E8M0 scale 2^X with X = floor(log2
+// max|h|) - 8 (clamped to [-127, 127], -127 below 2^-118; the 4 lanes of the row share the max
+// through two lane swaps) and E4M3 codes of |h| 2^-X (nearest even, saturating at 448) with
+// the sign. All 4 lanes of a row must be active together.
+__device__ __forceinline__ void epilogue_mx8(const GemmArgs& a, const f32x4& g0, const f32x4& u0, const f32x4& g1,
+                                             const f32x4& u1, int row, int blk, float lim) {
+  const int lg = (threadIdx.x & (WAVE - 1)) >> 4;
+  const int NO = a.N / 2;
+  auto act = [&](float g, float u) { return silu_mul(fminf(g, lim), fminf(fmaxf(u, -lim), lim)); };
+  const float h[8] = {act(g0.x, u0.x), act(g0.y, u0.y), act(g0.z, u0.z), act(g0.w, u0.w),
+                      act(g1.x, u1.x), act(g1.y, u1.y), act(g1.z, u1.z), act(g1.w, u1.w)};
+  float A = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) A = fmaxf(A, fabsf(h[i]));
+  A = fmaxf(A, __shfl_xor(A, 16));
+  A = fmaxf(A, __shfl_xor(A, 32));
+  const int X = A < 0x1p-118f ? -127 : min(__builtin_amdgcn_frexp_expf(A) - 1 - 8, 127);
+  uint32_t w[2] = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t code = ((__float_as_uint(h[i]) >> 31) << 7) | e4m3_encode_rne_sat(__builtin_ldexpf(fabsf(h[i]), -X));
+    w[i >> 2] |= code << (8 * (i & 3));
+  }
+  uint8_t* dst = a.hq8 + (size_t)row * NO + 32 * blk + 4 * lg;
+  *(uint32_t*)dst = w[0];
+  *(uint32_t*)(dst + 16) = w[1];
+  if (lg == 0) a.hs8[(size_t)row * (NO / 32) + blk] = (uint8_t)(X + 127);
+}
+
 // Smallest h block exponent of a row (nblk bytes, nblk a multiple of 8), read as 8-byte
 // words split over the row's 4 lanes l16 + 16 lg and combined through two lane swaps.
 __device__ __forceinline__ int row_exp_min4(const int8_t* erow, int nblk, int lg) {
@@ -328,8 +359,22 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs a) {
       epilogue_single(a, sum, sc, orow, q0 + s);
     }
   } else {
-    // gate (even tile) and up (odd tile) of the same columns are finished together
     const float lim = g < a.clamp_groups ? a.swiglu_limit : INFINITY;
+    if constexpr (MODE == GEMM_GATEUP_MX8 && NSUB == 4) {
+      if (a.hq8) {   // one wave quantises the 32-column block of both pairs (sc = 1: MX has no global scale)
+        if (wave == 0) {
+          f32x4 t[4];
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            t[s] = red[0][s][lane];
+            for (int w = 1; w < NW; ++w) t[s] += red[w][s][lane];
+          }
+          epilogue_mx8(a, t[0], t[1], t[2], t[3], orow, blockIdx.x, lim);
+        }
+        return;
+      }
+    }
+    // gate (even tile) and up (odd tile) of the same columns are finished together
     for (int s = 2 * wave; s < NSUB; s += 2 * NW) {
       f32x4 gsum = red[0][s][lane], usum = red[0][s + 1][lane];
       for (int w = 1; w < NW; ++w) {
@@ -683,6 +728,163 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void gemm_prefill_kernel(GemmArgs 
   }
 }
 
+// -------------------------------------------------------- prefill GEMM, MX8 modes
+// MXFP4 weights x MXFP8 activations on the block-scaled MFMA (16x16x128, no dequantisation).
+// Tiles of M token rows of one expert (the plan's tile height: 96, or 64 when experts average
+// fewer rows) x (WAVES x NSUB) 16-row weight tiles. Per 128-column chunk the token tile's E4M3
+// codes (M rows x 128 bytes, 16-byte slots, piece c of row r at slot 8 r + (c ^ swz8(r))) and
+// its E8M0 scales (4 bytes per row) arrive in LDS by DMA into a ring of three stages; each
+// wave streams its weight tiles (16 bytes per lane per chunk, the scale tile's byte for the
+// chunk) into three register sets, both two chunks ahead (an MX8 chunk is a quarter of the
+// fp16 kernel's MFMA work per wave, too little to hide a load issued one chunk ahead). An
+// MFMA's B operand is pieces lg and 4 + lg of a row (see mfma_mx); with swz8(r) = (r >> 1) & 7
+// the 16 rows of a read land on 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
+
+template <int MODE, int NSUB, int WAVES, int OCC, int M>
+__global__ __launch_bounds__(64 * WAVES, OCC) void gemm_prefill_mx8_kernel(GemmArgs a) {
+  static_assert(MODE == GEMM_GATEUP_MX8 || MODE == GEMM_DOWN_MX8, "MX8 modes");
+  constexpr int TSUB = M / 16;
+  constexpr int STAGE = M * 8;                        // 16-byte code slots per stage
+  constexpr int SROWS = 128;                          // scale dwords per stage (>= M, two DMA waves)
+  constexpr int NT = 64 * WAVES;
+  constexpr int D = STAGE / NT;                       // code DMA instructions per lane per chunk
+  static_assert(STAGE % NT == 0 && M <= SROWS && WAVES >= 2, "tile size");
+  constexpr int NST = 3;                              // LDS stages (and weight register sets)
+  __shared__ u32x4 tile[NST * STAGE];
+  __shared__ uint32_t stile[NST * SROWS];
+
+  const int ntiles = a.tile_count[0];
+  const PrefillItem item = prefill_item(ntiles);
+  const int slot = item.slot;
+  if (slot >= ntiles) return;
+  const int g = a.tile_group[slot];
+  const int row0 = a.tile_row0[slot];
+  const ProjLayout L = proj_layout(a.N, a.K);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int q0 = (item.nb * WAVES + wave) * NSUB;
+  const int nvalid = min(M, a.offsets[g + 1] - row0);
+  auto src_row = [&](int r) {                          // activation row of tile row r (clamped)
+    const int rr = row0 + min(r, nvalid - 1);
+    return MODE == GEMM_DOWN_MX8 ? rr : a.tok[rr];
+  };
+  // code DMA: instruction i of this wave fills slots (WAVES i + wave) * 64 + lane
+  uint32_t src_off[D];
+#pragma unroll
+  for (int i = 0; i < D; ++i) {
+    const int sl = (WAVES * i + wave) * 64 + lane;
+    const int r = sl >> 3;
+    const int kp = (sl & 7) ^ swz8(r);
+    src_off[i] = (uint32_t)src_row(r) * L.K + kp * 16;
+  }
+  // scale DMA: waves 0 and 1, a row per lane
+  const uint32_t s_off = wave < 2 ? (uint32_t)src_row(wave * 64 + lane) * (L.K / 32) : 0u;
+  auto dma = [&](int kc, int st) {
+    const char* base = (const char*)a.xq + (size_t)kc * KCHUNK;
+#pragma unroll
+    for (int i = 0; i < D; ++i) dma16(base + src_off[i], &tile[st * STAGE + (WAVES * i + wave) * 64]);
+    if (wave < 2)
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(a.xs + s_off + 4 * kc),
+                                       (void __attribute__((address_space(3)))*)&stile[st * SROWS + wave * 64], 4, 0,
+                                       0);
+  };
+
+  const u32x4* wp[NSUB];
+  const uint8_t* sp[NSUB];
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s) {
+    wp[s] = fp4_tile(a, L, g, q0 + s, 0);
+    sp[s] = (const uint8_t*)sc_tile(a, L, g, q0 + s, 0);
+  }
+  auto load_w = [&](int kc, u32x4 (&w)[NSUB], uint32_t (&sb)[NSUB]) {
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) {
+      w[s] = wp[s][(size_t)kc * WAVE];
+      sb[s] = *(const uint32_t*)(sp[s] + (size_t)(kc >> 3) * (WAVE * 16) + (kc & 6) * 2);
+    }
+  };
+
+  auto body = [&](auto tvc) {
+    constexpr int TV = decltype(tvc)::value;
+    f32x4 acc[NSUB][TV];
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s)
+#pragma unroll
+      for (int t = 0; t < TV; ++t) acc[s][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // three register sets and LDS stages: chunk kc + 2 is loaded while chunk kc is consumed.
+    // Each step issues the same loads (clamped to the last chunk near the end), so one wait
+    // count fits every step: chunk kc's DMA and weights must have landed, the newest step's
+    // loads (weights of kc + 1: 2 NSUB ops; its DMA: D, plus the scale DMA on waves 0 and 1)
+    // may still be in flight.
+    u32x4 rw[NST][NSUB];
+    uint32_t rs[NST][NSUB];
+    load_w(0, rw[0], rs[0]);
+    dma(0, 0);
+    load_w(min(1, L.KC - 1), rw[1], rs[1]);
+    dma(min(1, L.KC - 1), 1);
+    __builtin_amdgcn_sched_barrier(0);
+    auto step = [&](int kc, auto setc) {
+      constexpr int C = decltype(setc)::value;          // kc % 3
+      constexpr int NX = (C + 2) % NST;                 // set / stage of chunk kc + 2
+      if (wave < 2) __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * NSUB + D + 1, 0));
+      else __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * NSUB + D, 0));
+      __builtin_amdgcn_s_barrier();                     // chunk kc in LDS for every wave; stage NX free
+      __builtin_amdgcn_sched_barrier(0);
+      load_w(min(kc + 2, L.KC - 1), rw[NX], rs[NX]);
+      dma(min(kc + 2, L.KC - 1), NX);
+      __builtin_amdgcn_sched_barrier(0);
+      const u32x4* T0 = &tile[C * STAGE];
+      const uint8_t* S0 = (const uint8_t*)&stile[C * SROWS];
+#pragma unroll
+      for (int t = 0; t < TV; ++t) {
+        const int r = t * 16 + l16;
+        const u32x4 b0 = T0[r * 8 + (lg ^ swz8(r))];
+        const u32x4 b1 = T0[r * 8 + ((4 + lg) ^ swz8(r))];
+        const uint32_t sbv = S0[r * 4 + lg];
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s)
+          acc[s][t] = mfma_mx(rw[C][s], (rs[C][s] >> ((kc & 1) * 16)) & 0xFFu, b0, b1, sbv, acc[s][t]);
+      }
+    };
+    int kc = 0;
+    for (; kc + NST <= L.KC; kc += NST) {
+      step(kc, IntC<0>());
+      step(kc + 1, IntC<1>());
+      step(kc + 2, IntC<2>());
+    }
+    if (kc < L.KC) step(kc, IntC<0>());
+    if (kc + 1 < L.KC) step(kc + 1, IntC<1>());
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));   // the clamped tail loads land before the workgroup exits
+
+#pragma unroll
+    for (int t = 0; t < TV; ++t) {
+      const int rr = t * 16 + l16;
+      if (rr >= nvalid) continue;
+      const int orow = row0 + rr;
+      if constexpr (MODE == GEMM_DOWN_MX8) {
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s) epilogue_single(a, acc[s][t], 1.0f, orow, q0 + s);
+      } else {
+        const float lim = g < a.clamp_groups ? a.swiglu_limit : INFINITY;
+#pragma unroll
+        for (int s = 0; s < NSUB; s += 2) epilogue_pair<MODE>(a, acc[s][t], acc[s + 1][t], 1.0f, orow, (q0 + s) >> 1, lim);
+      }
+    }
+  };
+  const int tv = (nvalid + 15) >> 4;
+  static_assert(TSUB == 6 || TSUB == 4, "row tiers assume 4 or 6 slices");
+  if constexpr (TSUB == 6) {
+    if (tv > 4) body(IntC<6>());
+    else if (tv > 2) body(IntC<4>());
+    else body(IntC<2>());
+  } else {
+    if (tv > 2) body(IntC<4>());
+    else body(IntC<2>());
+  }
+}
+
 // ---------------------------------------------------------------------- launch
 
 template <typename K>
@@ -715,7 +917,8 @@ template <int MODE>
 static void launch_decode(int max_tiles, int est_tiles, const GemmArgs& a, hipStream_t s,
                           const LaunchEvents& ev) {
   const int nsub16 = a.N / 16, kc = a.K / KCHUNK;
-  const bool wide = nsub16 % 4 == 0 && (long)est_tiles * (nsub16 / 4) >= DEC_MIN_WGS;
+  const bool wide = nsub16 % 4 == 0 && ((long)est_tiles * (nsub16 / 4) >= DEC_MIN_WGS ||
+                                        (MODE == GEMM_GATEUP_MX8 && a.hq8));   // MXFP8 h blocks: 4 tiles
   int nw = kc % 4 == 0 ? 4 : kc % 3 == 0 ? 3 : kc % 2 == 0 ? 2 : 4;
   nw = min(nw, kc);
   if (wide) {
@@ -756,6 +959,26 @@ static void launch_mode(GemmRegime regime, int max_tiles, int est_tiles, const G
   }
 }
 
+constexpr int PRE_WAVES_MX8 = 4;   // MX8 prefill: 4 waves x 2 weight tiles (a 2 x 2 wave layout with the
+constexpr int PRE_NSUB_MX8 = 2;    // token rows split measured 9% slower), 2 workgroups per CU
+constexpr int PRE_OCC_MX8 = 2;
+
+template <int MODE>
+static void launch_mx8(GemmRegime regime, int max_tiles, int est_tiles, const GemmArgs& a, hipStream_t s,
+                       const LaunchEvents& ev) {
+  if (regime == REGIME_DECODE_KSPLIT) {
+    launch_decode<MODE>(max_tiles, est_tiles, a, s, ev);
+    return;
+  }
+  constexpr int W = PRE_WAVES_MX8, NS = PRE_NSUB_MX8;   // N = 2I or H, multiples of 128
+  const int ny = (max_tiles + 7) / 8 * 8;
+  const dim3 grid(a.N / (16 * W * NS), ny);
+  if (a.tile_rows == 64)
+    launch_k(gemm_prefill_mx8_kernel<MODE, NS, W, PRE_OCC_MX8, 64>, grid, dim3(64 * W), s, ev, a);
+  else
+    launch_k(gemm_prefill_mx8_kernel<MODE, NS, W, PRE_OCC_MX8, PREFILL_TILE_ROWS>, grid, dim3(64 * W), s, ev, a);
+}
+
 hipError_t launch_gemm(GemmMode mode, GemmRegime regime, int max_tiles, int est_tiles, const GemmArgs& a,
                        hipStream_t s, const LaunchEvents& ev) {
   if (max_tiles <= 0) return hipSuccess;
@@ -766,9 +989,8 @@ hipError_t launch_gemm(GemmMode mode, GemmRegime regime, int max_tiles, int est_
     case GEMM_GATEUP_FP4: launch_mode<GEMM_GATEUP_FP4>(regime, max_tiles, est_tiles, a, s, ev); break;
     case GEMM_DOWN: launch_mode<GEMM_DOWN>(regime, max_tiles, est_tiles, a, s, ev); break;
     case GEMM_DOWN_FP4: launch_mode<GEMM_DOWN_FP4>(regime, max_tiles, est_tiles, a, s, ev); break;
-    // the MX8 modes run the decode GEMM in every regime (16-row tiles)
-    case GEMM_GATEUP_MX8: launch_decode<GEMM_GATEUP_MX8>(max_tiles, est_tiles, a, s, ev); break;
-    case GEMM_DOWN_MX8: launch_decode<GEMM_DOWN_MX8>(max_tiles, est_tiles, a, s, ev); break;
+    case GEMM_GATEUP_MX8: launch_mx8<GEMM_GATEUP_MX8>(regime, max_tiles, est_tiles, a, s, ev); break;
+    case GEMM_DOWN_MX8: launch_mx8<GEMM_DOWN_MX8>(regime, max_tiles, est_tiles, a, s, ev); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

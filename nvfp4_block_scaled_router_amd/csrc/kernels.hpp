@@ -116,6 +116,7 @@ struct GemmArgs {
   const int32_t* tile_count;
   const int32_t* tile_first; // nullptr, or the index of the launch's first tile (list 2: &tile_count[0])
   const int32_t* offsets;  // [G+1] row ranges of the groups
+  int tile_rows;           // the plan's tile height (prefill: PREFILL_TILE_ROWS, or 64 for the MX8 kernel)
   // h = silu(g) u between the GEMMs, as h16 [rows][I] fp16 (columns permuted inside each
   // 128-column chunk, see h_pos) with, per row and 16-column block b, an exponent
   // hexp[row][b] such that h16 = fp16(h * 2^hexp) has the block's largest |h| in
@@ -129,6 +130,9 @@ struct GemmArgs {
   int32_t* hmin;           // [rows] or nullptr
   float* hf;               // gate_up: when set, h as fp32 [rows][I] in column order instead (the
                            // input of the row quantiser before DOWN_FP4); out/hexp/hmin unused
+  uint8_t* hq8;            // GATEUP_MX8 decode kernel: when set, h MXFP8-quantised in the epilogue,
+  uint8_t* hs8;            // codes [rows][I] and E8M0 scales [rows][I/32] (32-column blocks are
+                           // local to a workgroup of 4 tiles); hf unused
   // down: y as fp16 [rows][N] with one exponent per row and 16-column block, the
   // block's largest |y| scaled into [2^14, 2^15): y = y16 * 2^-yexp
   uint16_t* yout;

@@ -17,22 +17,6 @@
 
 namespace nvmoe {
 
-// Nearest E4M3fn code to v >= 0, ties to even, v >= 448 saturates to 0x7E.
-__device__ __forceinline__ uint32_t e4m3_encode_rne_sat(float v) {
-  if (!(v > 0.0f)) return 0u;
-  if (v >= 448.0f) return 0x7Eu;
-  if (v < 0.015625f) return (uint32_t)__builtin_rintf(v * 512.0f);  // subnormals: multiples of 2^-9
-  const int e = (int)((__float_as_uint(v) >> 23) & 0xFFu) - 127;     // v in [2^e, 2^(e+1))
-  const float scale = __uint_as_float((uint32_t)(3 - e + 127) << 23); // exact 2^(3-e)
-  uint32_t m = (uint32_t)__builtin_rintf(v * scale);                 // 8..16
-  int ee = e;
-  if (m == 16u) {
-    m = 8u;
-    ++ee;
-  }
-  return ((uint32_t)(ee + 7) << 3) | (m - 8u);
-}
-
 // Nearest E2M1 magnitude code to r >= 0 (ties to the even code), saturating at 6.
 __device__ __forceinline__ uint32_t e2m1_encode_rne_sat(float r) {
   return (uint32_t)(r > 0.25f) + (uint32_t)(r >= 0.75f) + (uint32_t)(r > 1.25f) + (uint32_t)(r >= 1.75f) +

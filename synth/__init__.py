@@ -153,6 +153,12 @@ def deepseek_v4_flash(T: int = 64) -> MoeConfig:
                      shared=1, seed=421, bias_sigma=0.5, swiglu_limit=10.0, wfmt="mxfp4")
 
 
+def deepseek_v4_flash_w4a8(T: int = 64) -> MoeConfig:
+    """The DeepSeek-V4-Flash layer in its W4A8 profile: MXFP4 weights with MXFP8 activations
+    (x and h)."""
+    return dataclasses.replace(deepseek_v4_flash(T), name=f"deepseek-v4-flash-w4a8-t{T}", act="mxfp8")
+
+
 SHARING_LEVELS = (0.0, 0.2, 0.4, 0.6, 0.8, 1.0)
 
 

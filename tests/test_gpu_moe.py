@@ -233,6 +233,10 @@ W4A8 = [
     dataclasses.replace(synth.deepseek_v4_flash(8), name="w4a8-deepseek-v4-flash-t8", act="mxfp8"),
     synth.MoeConfig("w4a8-max-inter", T=40, H=128, I=16384, E=4, k=2, shared=1, act="mxfp8", wfmt="mxfp4",
                     seed=74),
+    synth.MoeConfig("w4a8-skewed-cold", T=256, H=256, I=256, E=32, k=4, zipf_s=1.2, act="mxfp8", wfmt="mxfp4",
+                    seed=75),
+    synth.MoeConfig("w4a8-prefill-ragged", T=777, H=384, I=384, E=8, k=2, score="sigmoid", act="mxfp8",
+                    wfmt="mxfp4", seed=76),
 ]
 
 
