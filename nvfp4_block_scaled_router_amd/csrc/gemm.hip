@@ -733,7 +733,8 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void gemm_prefill_kernel(GemmArgs 
 // Tiles of M token rows of one expert (the plan's tile height: 96, or 64 when experts average
 // fewer rows) x (WAVES x NSUB) 16-row weight tiles. Per 128-column chunk the token tile's E4M3
 // codes (M rows x 128 bytes, 16-byte slots, piece c of row r at slot 8 r + (c ^ swz8(r))) and
-// its E8M0 scales (4 bytes per row) arrive in LDS by DMA into a ring of three stages; each
+// its E8M0 scales (4 bytes per row; every wave issues one dword DMA so that no branch splits
+// the wait-count bookkeeping) arrive in LDS by DMA into a ring of three stages; each
 // wave streams its weight tiles (16 bytes per lane per chunk, the scale tile's byte for the
 // chunk) into three register sets, both two chunks ahead (an MX8 chunk is a quarter of the
 // fp16 kernel's MFMA work per wave, too little to hide a load issued one chunk ahead). An
@@ -746,13 +747,23 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void gemm_prefill_mx8_kernel(GemmA
   static_assert(MODE == GEMM_GATEUP_MX8 || MODE == GEMM_DOWN_MX8, "MX8 modes");
   constexpr int TSUB = M / 16;
   constexpr int STAGE = M * 8;                        // 16-byte code slots per stage
-  constexpr int SROWS = 128;                          // scale dwords per stage (>= M, two DMA waves)
+  constexpr int SROWS = 64 * WAVES;                   // scale dwords per stage: a row per lane of every wave
   constexpr int NT = 64 * WAVES;
   constexpr int D = STAGE / NT;                       // code DMA instructions per lane per chunk
   static_assert(STAGE % NT == 0 && M <= SROWS && WAVES >= 2, "tile size");
   constexpr int NST = 3;                              // LDS stages (and weight register sets)
-  __shared__ u32x4 tile[NST * STAGE];
-  __shared__ uint32_t stile[NST * SROWS];
+  // one LDS object per stage, so that the compiler sees that the DMA into one stage and the
+  // reads of another never alias (with one array it waited for every DMA before each read)
+  __shared__ u32x4 tile0[STAGE], tile1[STAGE], tile2[STAGE];
+  __shared__ uint32_t stile0[SROWS], stile1[SROWS], stile2[SROWS];
+  auto stage_tile = [&](auto stc) -> u32x4* {
+    constexpr int S = decltype(stc)::value;
+    return S == 0 ? tile0 : S == 1 ? tile1 : tile2;
+  };
+  auto stage_scales = [&](auto stc) -> uint32_t* {
+    constexpr int S = decltype(stc)::value;
+    return S == 0 ? stile0 : S == 1 ? stile1 : stile2;
+  };
 
   const int ntiles = a.tile_count[0];
   const PrefillItem item = prefill_item(ntiles);
@@ -779,16 +790,16 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void gemm_prefill_mx8_kernel(GemmA
     const int kp = (sl & 7) ^ swz8(r);
     src_off[i] = (uint32_t)src_row(r) * L.K + kp * 16;
   }
-  // scale DMA: waves 0 and 1, a row per lane
-  const uint32_t s_off = wave < 2 ? (uint32_t)src_row(wave * 64 + lane) * (L.K / 32) : 0u;
-  auto dma = [&](int kc, int st) {
+  // scale DMA: a row per lane of every wave (rows past the tile clamp to its last row)
+  const uint32_t s_off = (uint32_t)src_row(wave * 64 + lane) * (L.K / 32);
+  auto dma = [&](int kc, auto stc) {
+    u32x4* T = stage_tile(stc);
+    uint32_t* S = stage_scales(stc);
     const char* base = (const char*)a.xq + (size_t)kc * KCHUNK;
 #pragma unroll
-    for (int i = 0; i < D; ++i) dma16(base + src_off[i], &tile[st * STAGE + (WAVES * i + wave) * 64]);
-    if (wave < 2)
-      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(a.xs + s_off + 4 * kc),
-                                       (void __attribute__((address_space(3)))*)&stile[st * SROWS + wave * 64], 4, 0,
-                                       0);
+    for (int i = 0; i < D; ++i) dma16(base + src_off[i], &T[(WAVES * i + wave) * 64]);
+    __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(a.xs + s_off + 4 * kc),
+                                     (void __attribute__((address_space(3)))*)&S[wave * 64], 4, 0, 0);
   };
 
   const u32x4* wp[NSUB];
@@ -821,22 +832,21 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void gemm_prefill_mx8_kernel(GemmA
     u32x4 rw[NST][NSUB];
     uint32_t rs[NST][NSUB];
     load_w(0, rw[0], rs[0]);
-    dma(0, 0);
+    dma(0, IntC<0>());
     load_w(min(1, L.KC - 1), rw[1], rs[1]);
-    dma(min(1, L.KC - 1), 1);
+    dma(min(1, L.KC - 1), IntC<1>());
     __builtin_amdgcn_sched_barrier(0);
     auto step = [&](int kc, auto setc) {
       constexpr int C = decltype(setc)::value;          // kc % 3
       constexpr int NX = (C + 2) % NST;                 // set / stage of chunk kc + 2
-      if (wave < 2) __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * NSUB + D + 1, 0));
-      else __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * NSUB + D, 0));
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * NSUB + D + 1, 0));
       __builtin_amdgcn_s_barrier();                     // chunk kc in LDS for every wave; stage NX free
       __builtin_amdgcn_sched_barrier(0);
       load_w(min(kc + 2, L.KC - 1), rw[NX], rs[NX]);
-      dma(min(kc + 2, L.KC - 1), NX);
+      dma(min(kc + 2, L.KC - 1), IntC<NX>());
       __builtin_amdgcn_sched_barrier(0);
-      const u32x4* T0 = &tile[C * STAGE];
-      const uint8_t* S0 = (const uint8_t*)&stile[C * SROWS];
+      const u32x4* T0 = stage_tile(IntC<C>());
+      const uint8_t* S0 = (const uint8_t*)stage_scales(IntC<C>());
 #pragma unroll
       for (int t = 0; t < TV; ++t) {
         const int r = t * 16 + l16;
