@@ -209,7 +209,7 @@ def cpu_baseline(cfgs, budget_s=6.0):
 
 # ------------------------------------------------------------ rocprofv3 summaries
 
-STAGE_OF_MODE = {"0": "gate_up", "1": "gate_up", "3": "gate_up", "2": "down", "4": "down"}
+STAGE_OF_MODE = {"0": "gate_up", "1": "gate_up", "3": "gate_up", "5": "gate_up", "2": "down", "4": "down", "6": "down"}
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ("gemm.hip", "common.hpp", "kernels.hpp", "api.cpp")   # kernels + their launch choices
 
@@ -230,8 +230,10 @@ def kernel_stage(name):
     mm = re.search(r"gemm_\w+_kernel<(\d+)", name)
     if mm:
         return STAGE_OF_MODE.get(mm.group(1), "gemm")
-    for key, st in (("plan", "route"), ("route", "route"), ("combine", "combine"), ("quant", "quant"),
-                    ("rows_to_f16", "quant"), ("pack", "pack"), ("group_gs", "pack")):
+    for key, st in (("plan", "route"), ("route", "route"), ("combine", "combine"),
+                    ("quant_rows_kernel<float>", "down"), ("mxfp8_rows_kernel<float>", "down"),   # h before down
+                    ("quant", "quant"), ("mxfp8_rows", "quant"), ("rows_to_f16", "quant"), ("pack", "pack"),
+                    ("group_gs", "pack")):
         if key in name:
             return st
     return "other"
