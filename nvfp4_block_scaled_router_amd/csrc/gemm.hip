@@ -236,8 +236,12 @@ __device__ __forceinline__ void epilogue_single(const GemmArgs& a, const f32x4& 
 // (tiny, shared through L2); each lane's token-operand load is reused by NSUB tiles.
 constexpr int DEC_MAX_WAVES = 4;   // measured best of 4 / 8 / 16 on the decode workloads
 
-template <int MODE, int NSUB>
-__global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs a) {
+// MAXW: the wave count the launch may use (8 for the MX8 gate_up of small batches: its epilogue
+// needs 4 tiles per workgroup, so a small grid has half the workgroups of the 2-tile split and
+// splits K wider instead; the 8-wave instance is kept apart because its reduction buffer halves
+// the workgroups a CU holds).
+template <int MODE, int NSUB, int MAXW = DEC_MAX_WAVES>
+__global__ __launch_bounds__(64 * MAXW) void gemm_decode_kernel(GemmArgs a) {
   constexpr bool F16 = MODE != GEMM_GATEUP_BF16;           // fp16 MFMA (bf16 x: bf16 MFMA)
   constexpr bool MX8 = MODE == GEMM_GATEUP_MX8 || MODE == GEMM_DOWN_MX8;   // scaled MFMA on MX codes
   constexpr bool DOWNM = MODE == GEMM_DOWN || MODE == GEMM_DOWN_FP4 || MODE == GEMM_DOWN_MX8;
@@ -345,7 +349,7 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs a) {
     }
   }
 
-  __shared__ f32x4 red[DEC_MAX_WAVES][NSUB][WAVE];
+  __shared__ f32x4 red[MAXW][NSUB][WAVE];
 #pragma unroll
   for (int s = 0; s < NSUB; ++s) red[wave][s][lane] = acc[s];
   __syncthreads();
@@ -927,10 +931,16 @@ template <int MODE>
 static void launch_decode(int max_tiles, int est_tiles, const GemmArgs& a, hipStream_t s,
                           const LaunchEvents& ev) {
   const int nsub16 = a.N / 16, kc = a.K / KCHUNK;
-  const bool wide = nsub16 % 4 == 0 && ((long)est_tiles * (nsub16 / 4) >= DEC_MIN_WGS ||
-                                        (MODE == GEMM_GATEUP_MX8 && a.hq8));   // MXFP8 h blocks: 4 tiles
+  const bool many = nsub16 % 4 == 0 && (long)est_tiles * (nsub16 / 4) >= DEC_MIN_WGS;
+  const bool wide = many || (MODE == GEMM_GATEUP_MX8 && a.hq8);   // MXFP8 h blocks: 4 tiles
   int nw = kc % 4 == 0 ? 4 : kc % 3 == 0 ? 3 : kc % 2 == 0 ? 2 : 4;
   nw = min(nw, kc);
+  if constexpr (MODE == GEMM_GATEUP_MX8) {
+    if (wide && (long)est_tiles * (nsub16 / 4) < DEC_MIN_WGS / 4 && kc % 8 == 0) {   // a small grid: 8 waves
+      launch_k(gemm_decode_kernel<MODE, 4, 8>, dim3(nsub16 / 4, max_tiles), dim3(64 * 8), s, ev, a);
+      return;
+    }
+  }
   if (wide) {
     launch_k(gemm_decode_kernel<MODE, 4>, dim3(nsub16 / 4, max_tiles), dim3(64 * nw), s, ev, a);
   } else {

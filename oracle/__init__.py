@@ -70,6 +70,7 @@ class Oracle:
         L.orc_expert_ffn.argtypes = [ctypes.POINTER(ProjSet), _i32, _i32, _i32, _vp, _vp]
         L.orc_expert_ffn_clamp.argtypes = [ctypes.POINTER(ProjSet), _i32, _i32, _i32, _vp, _vp, _i32, _f64]
         L.orc_expert_ffn_q.argtypes = [ctypes.POINTER(ProjSet), _i32, _i32, _i32, _vp, _vp, _i32, _f64, _i32]
+        L.orc_expert_h.argtypes = [ctypes.POINTER(ProjSet), _i32, _i32, _i32, _vp, _vp, _i32, _f64]
         L.orc_moe_tokens_clamp.argtypes = [ctypes.POINTER(ProjSet), ctypes.POINTER(ProjSet), _i32, _i32,
                                            _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _f64]
         L.orc_moe_tokens_q.argtypes = [ctypes.POINTER(ProjSet), ctypes.POINTER(ProjSet), _i32, _i32,
@@ -218,6 +219,18 @@ class Oracle:
         self.L.orc_expert_ffn_q(ctypes.byref(ps), g, H, I, x.ctypes.data, y.ctypes.data, int(clamp),
                                 float(swiglu_limit) if clamp else 0.0, int(hq))
         return y
+
+    def expert_h(self, W1, W2, g: int, x: np.ndarray, swiglu_limit: Optional[float] = None) -> np.ndarray:
+        """h = SwiGLU(W1_g x) in FP64, before any quantisation."""
+        H = W1[0].shape[-1] * 2
+        I = W2[0].shape[-1] * 2
+        x = np.ascontiguousarray(x, dtype=np.float64)
+        h = np.zeros(I, np.float64)
+        ps = self._projset(W1, W2)
+        clamp = swiglu_limit is not None
+        self.L.orc_expert_h(ctypes.byref(ps), g, H, I, x.ctypes.data, h.ctypes.data, int(clamp),
+                            float(swiglu_limit) if clamp else 0.0)
+        return h
 
     def moe_tokens(self, W1, W2, WS1, WS2, tokens, x_rows, ids, w,
                    swiglu_limit: Optional[float] = None, hq: bool = False) -> np.ndarray:

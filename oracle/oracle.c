@@ -460,9 +460,9 @@ static double proj_weight(const orc_proj_set* P, int second, int g, int N, int K
  * take MXFP8 activations, [b12x] "DeepSeek V4 Flash 0731 MoE reproduction").
  * Weights are decoded element by element in the set's format (orc_weight or
  * orc_weight_mx). */
-void orc_expert_ffn_q(const orc_proj_set* P, int g, int H, int I, const double* x, double* y,
-                      int clamp, double limit, int hq) {
-  double* h = (double*)malloc(sizeof(double) * (size_t)I);
+/* h = SwiGLU(W1 x) of one expert before any quantisation (the first half of the MLP). */
+void orc_expert_h(const orc_proj_set* P, int g, int H, int I, const double* x, double* h, int clamp,
+                  double limit) {
   for (int i = 0; i < I; ++i) {
     double gi = 0.0, ui = 0.0;
     for (int k = 0; k < H; ++k) {
@@ -475,6 +475,12 @@ void orc_expert_ffn_q(const orc_proj_set* P, int g, int H, int I, const double* 
     }
     h[i] = gi / (1.0 + exp(-gi)) * ui;
   }
+}
+
+void orc_expert_ffn_q(const orc_proj_set* P, int g, int H, int I, const double* x, double* y,
+                      int clamp, double limit, int hq) {
+  double* h = (double*)malloc(sizeof(double) * (size_t)I);
+  orc_expert_h(P, g, H, I, x, h, clamp, limit);
   if (hq == 2) {   /* MXFP8 h (W4A8 profile) */
     float* h32 = (float*)malloc(sizeof(float) * (size_t)I);
     uint8_t* hc = (uint8_t*)malloc((size_t)I);

@@ -443,6 +443,8 @@ def pin_ffn_textbook(o):
     D2 = decode_nvfp4(W2[0][0], W2[1][0], W2[2][0])
     ref = D2 @ (silu(D1[:I] @ x) * (D1[I:] @ x))
     assert np.allclose(y, ref, rtol=1e-12, atol=1e-15 * np.abs(ref).max())
+    h = silu(D1[:I] @ x) * (D1[I:] @ x)                  # the first half alone (orc_expert_h)
+    assert np.allclose(o.expert_h(W1, W2, 0, x), h, rtol=1e-12, atol=1e-15 * np.abs(h).max())
 
 
 def pin_ffn_hand(o):

@@ -25,3 +25,47 @@ def test_half_ulp_values():
     # 1 + 2^-8 is a tie between 1 and 1 + 2^-7: RNE gives 1, an error of exactly the allowance
     x = np.array([1.0 + 2.0 ** -8])
     assert torch.from_numpy(x).to(torch.bfloat16).double().item() == 1.0
+
+
+def _w4a8_case():
+    """The oracle side of a W4A8 case (no device): T=300 with a shared expert."""
+    import synth
+    from gpu_util import Case
+    cfg = synth.MoeConfig("w4a8-capacity", T=300, H=256, I=256, E=8, k=2, shared=1, act="mxfp8", wfmt="mxfp4",
+                          seed=77)
+    case = Case.__new__(Case)
+    case.cfg, case.x, case.logits = cfg, synth.activations(cfg), synth.logits(cfg)
+    case.tokens = np.arange(cfg.T, dtype=np.int32)
+    case.W = [tuple(synth.mxfp4_weights(cfg, w, 0, cfg.shared if w.startswith("ws") else cfg.E)) + (None,)
+              for w in ("w1", "w2", "ws1", "ws2")]
+    return case, case.reference()
+
+
+def test_requant_flip_allowance():
+    """The max check of quantised-h variants accepts an output that differs from the oracle by
+    the other rounding of an h element within FLIP_REL of a code boundary (token 129's shared
+    expert holds one: h = -9.5000483 at scale 2^-5, next to the -9 / -10 midpoint), rejects the
+    same output without the allowance, and rejects a planted error."""
+    import pytest
+    from gpu_util import check_out, h_flip_candidates
+    case, full = _w4a8_case()
+    ref = full["out"]
+    cand = h_flip_candidates(case, full, 129)
+    assert len(cand) >= 1
+    flips = lambda t: h_flip_candidates(case, full, t)   # noqa: E731
+    rms = np.sqrt(np.mean(ref * ref))
+    big = [c for c in cand if np.abs(c).max() > 0.05 * rms]   # the shared expert's element
+    assert len(big) == 1
+    for c in cand:                                       # every boundary element may round either way
+        flipped = ref.copy()
+        flipped[129] += c
+        out = torch.from_numpy(flipped.astype(np.float32)).to(torch.bfloat16)
+        check_out(out, ref, "one boundary flip", flips=flips)
+    flipped = ref.copy()
+    flipped[129] += big[0]
+    with pytest.raises(AssertionError):                 # the same output without the allowance
+        check_out(torch.from_numpy(flipped.astype(np.float32)).to(torch.bfloat16), ref, "without the allowance")
+    bad = ref.copy()
+    bad[5, 17] += 0.05 * rms
+    with pytest.raises(AssertionError):
+        check_out(torch.from_numpy(bad.astype(np.float32)).to(torch.bfloat16), ref, "planted error", flips=flips)
