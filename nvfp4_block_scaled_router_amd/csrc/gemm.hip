@@ -230,8 +230,9 @@ __device__ __forceinline__ void epilogue_single(const GemmArgs& a, const f32x4& 
 // ------------------------------------------------------------------ decode GEMM
 // Small row counts per expert (<= 16 rows per tile): weight streaming bound. A
 // workgroup owns NSUB 16-row weight tiles of one expert and one 16-row token tile; its
-// NW <= 4 waves split K into contiguous chunk ranges (a wider split, up to one chunk per
-// wave, measured slower: fewer workgroups fit a CU). Partial tiles are reduced through
+// NW <= MAXW waves split K into contiguous chunk ranges (a wider split, up to one chunk per
+// wave, measured slower: fewer workgroups fit a CU; and no faster on the smallest grids, a
+// single token's 8 experts). Partial tiles are reduced through
 // LDS in wave order (deterministic). Token operands come straight from global memory
 // (tiny, shared through L2); each lane's token-operand load is reused by NSUB tiles.
 constexpr int DEC_MAX_WAVES = 4;   // measured best of 4 / 8 / 16 on the decode workloads
@@ -422,9 +423,9 @@ __device__ __forceinline__ int lds_swz(int r) {
 }
 
 // ----------------------------------------------------------------- prefill GEMM
-// Tiles of TSUB*16 token rows of one expert x (4 waves x NSUB) 16-row weight tiles. The
+// Tiles of TSUB*16 token rows of one expert x (WAVES x NSUB) 16-row weight tiles. The
 // token tile of each 128-column chunk sits in LDS (rows of 256 bytes: one chunk of 16-bit
-// values, 16-byte piece c of row r at slot c ^ lds_swz(r)), shared by the 4 waves; each
+// values, 16-byte piece c of row r at slot c ^ lds_swz(r)), shared by the waves; each
 // wave streams its own weight tiles straight into registers (two alternating register
 // sets, one chunk ahead) and dequantises them there. Token tiles arrive by
 //  - LDS DMA (fp16 activations, GATEUP_F16): global_load_lds_dwordx4 straight into an
@@ -910,14 +911,16 @@ static void launch_k(K kernel, dim3 grid, dim3 block, hipStream_t s, const Launc
 }
 
 
+// The last launch-bound argument (OCC below) is the minimum number of waves per SIMD, which caps
+// the registers of a wave at 512 / OCC.
 constexpr int PRE_NSUB_GU = 2;    // prefill gate_up: 1 gate + 1 up tile per wave
 constexpr int PRE_NSUB_DN = 2;    // prefill down: 2 tiles per wave (2 workgroups per CU)
-constexpr int PRE_TSUB = 6;       // prefill: 96 token rows per tile (3 fp16 gate_up workgroups fit a CU's
-                                  // LDS; measured 13% faster than 128 rows at 2 per CU)
-constexpr int PRE_NBUF_GU = 2;    // prefill gate_up: LDS DMA ring depth (2 x 32 KiB; measured faster than 1
-                                  // workgroup per CU with 4 tiles per wave and 3 stages)
-constexpr int PRE_WAVES_GU = 4;   // prefill fp16 gate_up: 4 waves,
-constexpr int PRE_OCC_GU = 3;     // 3 workgroups per CU (2 x 24 KiB LDS stages each)
+constexpr int PRE_TSUB = 6;       // prefill: 96 token rows per tile (measured 13% faster than 128 rows)
+constexpr int PRE_NBUF_GU = 3;    // fp16 gate_up: LDS DMA ring depth (3 x 24 KiB; the register-staged modes
+                                  // always use 2 stages)
+constexpr int PRE_WAVES_GU = 8;   // fp16 gate_up: 8 waves x 2 tiles = 256 weight rows per token tile, two
+constexpr int PRE_OCC_GU = 4;     // workgroups per CU (128 registers; a few spill). Against 4 waves x 2
+                                  // tiles at 3 per CU: half the token-tile DMA per MFMA, gate_up 5-11% faster
 constexpr int PRE_WAVES_RS = 8;   // down: 8 waves, 1 workgroup per CU (fewer staged pieces per thread;
 constexpr int PRE_OCC_RS = 1;     // measured faster than 4 waves)
 constexpr int PRE_WAVES_FP4 = 4;  // NVFP4 gate_up: 4 waves (its pieces pair up: 8 waves would split one),
@@ -967,7 +970,7 @@ static void launch_mode(GemmRegime regime, int max_tiles, int est_tiles, const G
       constexpr int W = PRE_WAVES_FP4, NS = PRE_NSUB_DN;
       launch_k(gemm_prefill_kernel<MODE, NS, PRE_TSUB, PRE_NBUF_GU, W, PRE_OCC_FP4>, dim3(a.N / (16 * W * NS), ny),
                dim3(64 * W), s, ev, a);
-    } else if constexpr (MODE == GEMM_GATEUP_F16) {   // N = 2I, a multiple of 256
+    } else if constexpr (MODE == GEMM_GATEUP_F16) {   // N = 2I, a multiple of 256 (16 W NS)
       constexpr int W = PRE_WAVES_GU, NS = PRE_NSUB_GU;
       launch_k(gemm_prefill_kernel<MODE, NS, PRE_TSUB, PRE_NBUF_GU, W, PRE_OCC_GU>, dim3(a.N / (16 * W * NS), ny),
                dim3(64 * W), s, ev, a);
