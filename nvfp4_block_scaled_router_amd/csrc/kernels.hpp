@@ -142,9 +142,8 @@ struct GemmArgs {
   float swiglu_limit;
 };
 // Kernel families: decode (<= 16 rows per tile, K split across the waves of a workgroup,
-// direct token loads), N split with a 16-row LDS token tile (kept for experiments), and
-// prefill (N split, 128-row LDS token tiles).
-enum GemmRegime { REGIME_DECODE_KSPLIT = 0, REGIME_DECODE_NSPLIT = 1, REGIME_PREFILL = 2 };
+// direct token loads) and prefill (N split across the waves, 64- or 96-row token tiles in LDS).
+enum GemmRegime { REGIME_DECODE_KSPLIT = 0, REGIME_PREFILL = 2 };
 constexpr int H_EXP_INIT = 127;   // above any block exponent (start of a minimum)
 constexpr int H_EXP_MAX = 120;    // block exponents are clamped to [-H_EXP_MAX, H_EXP_MAX]
 
