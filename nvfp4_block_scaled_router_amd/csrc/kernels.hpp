@@ -24,6 +24,13 @@ struct RouteArgs {
   const float* bias;     // [E] or nullptr
   int n_group, topk_group, renorm;
   float scaling;
+  // optional side job: MXFP8 codes [T][mx_K] and E8M0 scales [T][mx_K/32] of the bf16 rows
+  // mx_x [T][mx_K], computed by extra workgroups of the first routing launch (one launch
+  // fewer for small batches)
+  const uint16_t* mx_x;
+  uint8_t* mx_q;
+  uint8_t* mx_s;
+  int mx_K;
 };
 
 struct PlanArgs {

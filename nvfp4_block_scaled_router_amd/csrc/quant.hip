@@ -14,6 +14,7 @@
 // reduction kernel has produced the group's global scale (weights).
 #include "common.hpp"
 #include "kernels.hpp"
+#include "rowq_dev.hpp"
 
 namespace nvmoe {
 
@@ -21,28 +22,6 @@ namespace nvmoe {
 __device__ __forceinline__ uint32_t e2m1_encode_rne_sat(float r) {
   return (uint32_t)(r > 0.25f) + (uint32_t)(r >= 0.75f) + (uint32_t)(r > 1.25f) + (uint32_t)(r >= 1.75f) +
          (uint32_t)(r > 2.5f) + (uint32_t)(r >= 3.5f) + (uint32_t)(r > 5.0f);
-}
-
-__device__ __forceinline__ void load16(const uint16_t* p, float* v) {
-  const u32x4 a = *(const u32x4*)p;
-  const u32x4 b = *(const u32x4*)(p + 8);
-  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    v[2 * i] = __uint_as_float(w[i] << 16);
-    v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-  }
-}
-
-__device__ __forceinline__ void load16(const float* p, float* v) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const f32x4 a = *(const f32x4*)(p + 4 * i);
-    v[4 * i] = a.x;
-    v[4 * i + 1] = a.y;
-    v[4 * i + 2] = a.z;
-    v[4 * i + 3] = a.w;
-  }
 }
 
 // Quantise one 16-element block with global scale gs; writes 8 code bytes and 1 scale byte.
@@ -110,44 +89,13 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const T* __restrict__ x
   wave_quant_row(row, K, g, packed + (size_t)r * (K / 2), scales + (size_t)r * (K / 16));
 }
 
-// MXFP8 rows (the W4A8 profile's activations): per 32 consecutive k one E8M0 scale 2^X with
-// X = floor(log2 max|x|) - 8 (8 = the exponent of E4M3's largest normal, 448 = 1.75 2^8),
-// clamped to [-127, 127] (-127 for a zero block or one below 2^-118), and E4M3 codes of
-// |x| 2^-X (exact power-of-two scaling, round to nearest even, saturating at 448) with the
-// sign of x. One wave per row, a lane per 32-column block.
+// MXFP8 rows: one wave per row (mxfp8_row_wave), 4 rows per workgroup.
 template <typename T>
 __global__ __launch_bounds__(256) void mxfp8_rows_kernel(const T* __restrict__ x, int rows, int K,
                                                          uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= rows) return;
-  const int lane = threadIdx.x & (WAVE - 1);
-  const T* row = x + (size_t)r * K;
-  for (int b = lane; b < K / 32; b += WAVE) {
-    float v[32];
-    load16(row + (size_t)b * 32, v);
-    load16(row + (size_t)b * 32 + 16, v + 16);
-    float A = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) A = fmaxf(A, fabsf(v[i]));
-    // A = f 2^E with f in [0.5, 1): floor(log2 A) = E - 1; below 2^-118 the clamp decides
-    int X = A < 0x1p-118f ? -127 : min(__builtin_amdgcn_frexp_expf(A) - 1 - 8, 127);
-    scales[(size_t)r * (K / 32) + b] = (uint8_t)(X + 127);
-    uint32_t w[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      uint32_t word = 0u;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float e = v[4 * q + i];
-        const uint32_t code = ((__float_as_uint(e) >> 31) << 7) | e4m3_encode_rne_sat(__builtin_ldexpf(fabsf(e), -X));
-        word |= code << (8 * i);
-      }
-      w[q] = word;
-    }
-    uint8_t* dst = codes + (size_t)r * K + (size_t)b * 32;
-    *(u32x4*)dst = u32x4{w[0], w[1], w[2], w[3]};
-    *(u32x4*)(dst + 16) = u32x4{w[4], w[5], w[6], w[7]};
-  }
+  mxfp8_row_wave(x + (size_t)r * K, K, codes + (size_t)r * K, scales + (size_t)r * (K / 32), threadIdx.x & (WAVE - 1));
 }
 
 // Group maxima: one 1024-thread workgroup per group, fixed reduction tree.

@@ -12,6 +12,7 @@
 #include "common.hpp"
 #include "kernels.hpp"
 #include "route_dev.hpp"
+#include "rowq_dev.hpp"
 
 namespace nvmoe {
 
@@ -190,8 +191,23 @@ __device__ __forceinline__ void route_token_general(const RouteArgs& r, int t, i
   }
 }
 
+// The side job of a routing launch: workgroup j past the routing workgroups quantises rows
+// j * (waves per workgroup) + wave of mx_x to MXFP8, one wave per row.
+__device__ __forceinline__ void mx_side_rows(const RouteArgs& a, int j) {
+  const int wpb = blockDim.x >> 6;
+  const int t = j * wpb + (int)(threadIdx.x >> 6);
+  if (t >= a.T) return;
+  mxfp8_row_wave(a.mx_x + (size_t)t * a.mx_K, a.mx_K, a.mx_q + (size_t)t * a.mx_K, a.mx_s + (size_t)t * (a.mx_K / 32),
+                 (int)(threadIdx.x & (WAVE - 1)));
+}
+
 template <int EPL>
 __global__ __launch_bounds__(256) void route_general_kernel(RouteArgs a) {
+  const int nb = (a.T + 3) / 4;
+  if ((int)blockIdx.x >= nb) {   // side-job workgroups (grid past the routing ones only when mx_x is set)
+    mx_side_rows(a, blockIdx.x - nb);
+    return;
+  }
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= a.T) return;   // whole waves leave together
   route_token_general<EPL>(a, t, nullptr);
@@ -239,6 +255,10 @@ __device__ __forceinline__ void write_tiles(const PlanArgs& a, const int* cnt, c
 // expert's 64-bit token bitmap.
 template <int EPL>
 __global__ __launch_bounds__(1024) void plan_small_kernel(RouteArgs r, PlanArgs a) {
+  if (blockIdx.x > 0) {   // side-job workgroups (only when r.mx_x is set)
+    mx_side_rows(r, blockIdx.x - 1);
+    return;
+  }
   extern __shared__ int lds[];
   const int G = a.G, E = a.E, T = a.T, k = a.k, rows = T * k, M = a.tile_rows;
   const int tid = threadIdx.x, nthr = blockDim.x;
@@ -405,11 +425,21 @@ bool plan_small_ok(int T, int k) { return T <= 64 && T * k <= 4096; }
 
 template <int EPL>
 static hipError_t launch_route_plan_t(const RouteArgs& r, const PlanArgs& p, int32_t* scratch, hipStream_t s) {
-  if (r.general) hipLaunchKernelGGL(route_general_kernel<EPL>, dim3((r.T + 3) / 4), dim3(256), 0, s, r);
+  // the MXFP8 side job rides on the first launch that can carry it (the general router's,
+  // or the one-workgroup plan's), else it gets a launch of its own
+  bool side = r.mx_x != nullptr;
+  if (r.general) {
+    hipLaunchKernelGGL(route_general_kernel<EPL>, dim3((r.T + 3) / 4 * (side ? 2 : 1)), dim3(256), 0, s, r);
+    side = false;
+  }
   if (plan_small_ok(p.T, p.k)) {
-    hipLaunchKernelGGL(plan_small_kernel<EPL>, dim3(1), dim3(1024), plan_small_lds_bytes(p.T * p.k, p.E, p.G), s,
-                       r, p);
+    hipLaunchKernelGGL(plan_small_kernel<EPL>, dim3(1 + (side ? (r.T + 15) / 16 : 0)), dim3(1024),
+                       plan_small_lds_bytes(p.T * p.k, p.E, p.G), s, r, p);
     return hipGetLastError();
+  }
+  if (side) {
+    const hipError_t e = launch_mxfp8_rows_bf16(r.mx_x, r.T, r.mx_K, r.mx_q, r.mx_s, s);
+    if (e != hipSuccess) return e;
   }
   if (r.general) {
   } else if constexpr (EPL <= 4) {

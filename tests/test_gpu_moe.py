@@ -259,9 +259,12 @@ def test_skewed_w4a4_down_sampled():
 
 # W4A8: MXFP4 weights with MXFP8 x and h through the block-scaled MFMA (decode-sized and
 # larger batches, a shared expert, the V4-Flash router and clamp, the V4-Flash shape, the
-# widest intermediate size)
+# widest intermediate size). The x quantisation of decode-regime batches rides on the routing
+# launch: the one-workgroup plan (w4a8-decode), the general router (w4a8-v4-router-clamp), or
+# its own launch beside the per-token router for more than 64 tokens (w4a8-decode-wide).
 W4A8 = [
     synth.MoeConfig("w4a8-decode", T=8, H=256, I=128, E=16, k=4, act="mxfp8", wfmt="mxfp4", seed=71),
+    synth.MoeConfig("w4a8-decode-wide", T=120, H=256, I=128, E=64, k=2, act="mxfp8", wfmt="mxfp4", seed=77),
     synth.MoeConfig("w4a8-prefill-shared", T=300, H=512, I=256, E=8, k=2, shared=1, act="mxfp8", wfmt="mxfp4",
                     seed=72),
     synth.MoeConfig("w4a8-v4-router-clamp", T=64, H=512, I=256, E=32, k=6, shared=1, score="sqrt_softplus",
