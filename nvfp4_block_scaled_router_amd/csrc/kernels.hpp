@@ -24,14 +24,19 @@ struct RouteArgs {
   const float* bias;     // [E] or nullptr
   int n_group, topk_group, renorm;
   float scaling;
-  // optional side job: MXFP8 codes [T][mx_K] and E8M0 scales [T][mx_K/32] of the bf16 rows
-  // mx_x [T][mx_K], computed by extra workgroups of the first routing launch (one launch
-  // fewer for small batches)
-  const uint16_t* mx_x;
+  // optional side job on the bf16 activation rows side_x [T][side_K], run by extra
+  // workgroups of the first routing launch (one launch fewer for small batches):
+  // SIDE_MXFP8: codes mx_q [T][side_K] and E8M0 scales mx_s [T][side_K/32];
+  // SIDE_F16: fp16 rows x16 [T][side_K] and their factors xf [T]
+  int side;
+  const uint16_t* side_x;
+  int side_K;
   uint8_t* mx_q;
   uint8_t* mx_s;
-  int mx_K;
+  uint16_t* x16;
+  float* xf;
 };
+enum RouteSide { SIDE_NONE = 0, SIDE_MXFP8 = 1, SIDE_F16 = 2 };
 
 struct PlanArgs {
   const int32_t* ids;    // [T][k]

@@ -130,45 +130,12 @@ __global__ __launch_bounds__(256) void quant_rows_f32_kernel(const float* __rest
                  scales + (size_t)r * (K / 16));
 }
 
-// bf16 activation rows -> fp16 for the gate_up MFMA: every row is multiplied by the power
-// of two 2^p that puts its max |x| in [2^14, 2^15) (p clamped to [-126, 126]), which is exact
-// for every element whose scaled magnitude is a normal fp16 (>= 2^-14, i.e. >= 2^-28 of the
-// row maximum; smaller ones round to the fp16 subnormal grid). The epilogue multiplies by
-// xf[r] = 2^-p. One wave per row.
+// bf16 activation rows -> fp16 rows and their factors (f16_row_wave), 4 rows per workgroup.
 __global__ __launch_bounds__(256) void rows_to_f16_kernel(const uint16_t* __restrict__ x, int rows, int K,
                                                           uint16_t* __restrict__ x16, float* __restrict__ xf) {
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= rows) return;
-  const int lane = threadIdx.x & (WAVE - 1);
-  const uint16_t* row = x + (size_t)r * K;
-  float m = 0.0f;
-  for (int c = lane; c < K / 8; c += WAVE) {
-    const u32x4 v = *(const u32x4*)(row + (size_t)c * 8);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      m = fmaxf(m, fmaxf(fabsf(__uint_as_float(w[i] << 16)), fabsf(__uint_as_float(w[i] & 0xFFFF0000u))));
-  }
-#pragma unroll
-  for (int off = WAVE / 2; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, WAVE));
-  int p = 0;
-  if (m > 0.0f) p = 14 - ((int)((__float_as_uint(m) >> 23) & 0xFFu) - 127);
-  p = p < -126 ? -126 : (p > 126 ? 126 : p);
-  const float scale = __uint_as_float((uint32_t)(p + 127) << 23);
-  if (lane == 0) xf[r] = __uint_as_float((uint32_t)(127 - p) << 23);
-  uint16_t* out = x16 + (size_t)r * K;
-  for (int c = lane; c < K / 8; c += WAVE) {
-    const u32x4 v = *(const u32x4*)(row + (size_t)c * 8);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    uint32_t o[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const _Float16 lo = (_Float16)(__uint_as_float(w[i] << 16) * scale);
-      const _Float16 hi = (_Float16)(__uint_as_float(w[i] & 0xFFFF0000u) * scale);
-      o[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-    }
-    *(u32x4*)(out + (size_t)c * 8) = u32x4{o[0], o[1], o[2], o[3]};
-  }
+  f16_row_wave(x + (size_t)r * K, K, x16 + (size_t)r * K, xf + r, threadIdx.x & (WAVE - 1));
 }
 
 hipError_t launch_rows_to_f16(const uint16_t* x, int rows, int K, uint16_t* x16, float* xf, hipStream_t s) {

@@ -191,21 +191,25 @@ __device__ __forceinline__ void route_token_general(const RouteArgs& r, int t, i
   }
 }
 
-// The side job of a routing launch: workgroup j past the routing workgroups quantises rows
-// j * (waves per workgroup) + wave of mx_x to MXFP8, one wave per row.
-__device__ __forceinline__ void mx_side_rows(const RouteArgs& a, int j) {
+// The side job of a routing launch: workgroup j past the routing workgroups converts rows
+// j * (waves per workgroup) + wave of side_x (MXFP8 codes and scales, or fp16 rows and their
+// factors), one wave per row.
+__device__ __forceinline__ void side_rows(const RouteArgs& a, int j) {
   const int wpb = blockDim.x >> 6;
   const int t = j * wpb + (int)(threadIdx.x >> 6);
   if (t >= a.T) return;
-  mxfp8_row_wave(a.mx_x + (size_t)t * a.mx_K, a.mx_K, a.mx_q + (size_t)t * a.mx_K, a.mx_s + (size_t)t * (a.mx_K / 32),
-                 (int)(threadIdx.x & (WAVE - 1)));
+  const int K = a.side_K, lane = (int)(threadIdx.x & (WAVE - 1));
+  if (a.side == SIDE_MXFP8)
+    mxfp8_row_wave(a.side_x + (size_t)t * K, K, a.mx_q + (size_t)t * K, a.mx_s + (size_t)t * (K / 32), lane);
+  else
+    f16_row_wave(a.side_x + (size_t)t * K, K, a.x16 + (size_t)t * K, a.xf + t, lane);
 }
 
 template <int EPL>
 __global__ __launch_bounds__(256) void route_general_kernel(RouteArgs a) {
   const int nb = (a.T + 3) / 4;
-  if ((int)blockIdx.x >= nb) {   // side-job workgroups (grid past the routing ones only when mx_x is set)
-    mx_side_rows(a, blockIdx.x - nb);
+  if ((int)blockIdx.x >= nb) {   // side-job workgroups (grid past the routing ones only with a side job)
+    side_rows(a, blockIdx.x - nb);
     return;
   }
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -255,8 +259,8 @@ __device__ __forceinline__ void write_tiles(const PlanArgs& a, const int* cnt, c
 // expert's 64-bit token bitmap.
 template <int EPL>
 __global__ __launch_bounds__(1024) void plan_small_kernel(RouteArgs r, PlanArgs a) {
-  if (blockIdx.x > 0) {   // side-job workgroups (only when r.mx_x is set)
-    mx_side_rows(r, blockIdx.x - 1);
+  if (blockIdx.x > 0) {   // side-job workgroups (only with a side job)
+    side_rows(r, blockIdx.x - 1);
     return;
   }
   extern __shared__ int lds[];
@@ -425,9 +429,9 @@ bool plan_small_ok(int T, int k) { return T <= 64 && T * k <= 4096; }
 
 template <int EPL>
 static hipError_t launch_route_plan_t(const RouteArgs& r, const PlanArgs& p, int32_t* scratch, hipStream_t s) {
-  // the MXFP8 side job rides on the first launch that can carry it (the general router's,
-  // or the one-workgroup plan's), else it gets a launch of its own
-  bool side = r.mx_x != nullptr;
+  // the side job rides on the first launch that can carry it (the general router's, or the
+  // one-workgroup plan's), else it gets a launch of its own
+  bool side = r.side != SIDE_NONE;
   if (r.general) {
     hipLaunchKernelGGL(route_general_kernel<EPL>, dim3((r.T + 3) / 4 * (side ? 2 : 1)), dim3(256), 0, s, r);
     side = false;
@@ -438,7 +442,8 @@ static hipError_t launch_route_plan_t(const RouteArgs& r, const PlanArgs& p, int
     return hipGetLastError();
   }
   if (side) {
-    const hipError_t e = launch_mxfp8_rows_bf16(r.mx_x, r.T, r.mx_K, r.mx_q, r.mx_s, s);
+    const hipError_t e = r.side == SIDE_MXFP8 ? launch_mxfp8_rows_bf16(r.side_x, r.T, r.side_K, r.mx_q, r.mx_s, s)
+                                              : launch_rows_to_f16(r.side_x, r.T, r.side_K, r.x16, r.xf, s);
     if (e != hipSuccess) return e;
   }
   if (r.general) {

@@ -64,4 +64,39 @@ __device__ __forceinline__ void mxfp8_row_wave(const T* row, int K, uint8_t* cod
   }
 }
 
+// bf16 activation rows -> fp16 for the gate_up MFMA: every row is multiplied by the power
+// of two 2^p that puts its max |x| in [2^14, 2^15) (p clamped to [-126, 126]), which is exact
+// for every element whose scaled magnitude is a normal fp16 (>= 2^-14, i.e. >= 2^-28 of the
+// row maximum; smaller ones round to the fp16 subnormal grid). The epilogue multiplies by
+// xf[r] = 2^-p. One wave per row; xf_out is the row's factor.
+__device__ __forceinline__ void f16_row_wave(const uint16_t* row, int K, uint16_t* out, float* xf_out, int lane) {
+  float m = 0.0f;
+  for (int c = lane; c < K / 8; c += WAVE) {
+    const u32x4 v = *(const u32x4*)(row + (size_t)c * 8);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      m = fmaxf(m, fmaxf(fabsf(__uint_as_float(w[i] << 16)), fabsf(__uint_as_float(w[i] & 0xFFFF0000u))));
+  }
+#pragma unroll
+  for (int off = WAVE / 2; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, WAVE));
+  int p = 0;
+  if (m > 0.0f) p = 14 - ((int)((__float_as_uint(m) >> 23) & 0xFFu) - 127);
+  p = p < -126 ? -126 : (p > 126 ? 126 : p);
+  const float scale = __uint_as_float((uint32_t)(p + 127) << 23);
+  if (lane == 0) *xf_out = __uint_as_float((uint32_t)(127 - p) << 23);
+  for (int c = lane; c < K / 8; c += WAVE) {
+    const u32x4 v = *(const u32x4*)(row + (size_t)c * 8);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const _Float16 lo = (_Float16)(__uint_as_float(w[i] << 16) * scale);
+      const _Float16 hi = (_Float16)(__uint_as_float(w[i] & 0xFFFF0000u) * scale);
+      o[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+    }
+    *(u32x4*)(out + (size_t)c * 8) = u32x4{o[0], o[1], o[2], o[3]};
+  }
+}
+
 }  // namespace nvmoe
