@@ -265,12 +265,12 @@ int moe_run(const moe_plan_t* plan, const void* packed, int32_t T, const uint16_
 /* Stages of moe_run, in launch order (for moe_run_timed). */
 #define MOE_STAGE_QUANT 0      /* activation preparation of prefill-regime batches: NVFP4
                                   quantisation (W4A4), MXFP8 quantisation (W4A8) or the exact
-                                  power-of-two rescale of bf16 rows into fp16 (W4A16); NVFP4
-                                  quantisation of decode-regime batches */
+                                  power-of-two rescale of bf16 rows into fp16 (W4A16) */
 #define MOE_STAGE_ROUTE 1      /* top-k, counts, offsets, permutation, tile list; for
-                                  decode-regime batches also the MXFP8 quantisation of x (W4A8)
-                                  or its fp16 rescale (W4A16 from 256 routed rows up), by extra
-                                  workgroups of the first routing launch */
+                                  decode-regime batches also the activation preparation (NVFP4
+                                  or MXFP8 quantisation of x, or its fp16 rescale from 256
+                                  routed rows up), by extra workgroups of the first routing
+                                  launch */
 #define MOE_STAGE_GATE_UP 2    /* grouped gate/up GEMM + SwiGLU */
 #define MOE_STAGE_DOWN 3       /* grouped down GEMM (with MOE_ACT_NVFP4_ALL: the h row
                                   quantisation before it) */

@@ -326,11 +326,11 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
                           : fp4 ? GEMM_GATEUP_FP4
                                 : (decode && T * k < DECODE_F16_ROWS) ? GEMM_GATEUP_BF16 : GEMM_GATEUP_F16;
   if ((e = mark(ev, 2 * MOE_STAGE_QUANT, s)) != hipSuccess) return (int)e;
-  // MXFP8 x and fp16 x of decode batches are converted by extra workgroups of the routing
-  // stage's first launch instead (one launch fewer)
+  // decode batches convert x in extra workgroups of the routing stage's first launch
+  // instead (one launch fewer)
   if (mx8 && !decode)
     e = launch_mxfp8_rows_bf16(x, T, H, xq, xs, s);
-  else if (fp4)
+  else if (fp4 && !decode)
     e = launch_quant_rows_bf16(x, T, H, xq, xs, xg, s);
   else if (gu_mode == GEMM_GATEUP_F16 && !decode)
     e = launch_rows_to_f16(x, T, H, x16, xg, s);
@@ -357,13 +357,17 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
   ra.topk_group = d.topk_group;
   ra.renorm = d.renormalize;
   ra.scaling = d.routed_scaling;
-  ra.side = !decode ? SIDE_NONE : mx8 ? SIDE_MXFP8 : gu_mode == GEMM_GATEUP_F16 ? SIDE_F16 : SIDE_NONE;
+  ra.side = !decode                       ? SIDE_NONE
+            : mx8                           ? SIDE_MXFP8
+            : fp4                           ? SIDE_NVFP4
+            : gu_mode == GEMM_GATEUP_F16    ? SIDE_F16
+                                            : SIDE_NONE;
   ra.side_x = x;
   ra.side_K = H;
-  ra.mx_q = xq;
-  ra.mx_s = xs;
-  ra.x16 = x16;
-  ra.xf = xg;
+  ra.side_q = xq;
+  ra.side_s = xs;
+  ra.side_f = xg;
+  ra.side_h = x16;
   PlanArgs pa;
   pa.ids = ra.ids;
   pa.T = T;

@@ -26,17 +26,18 @@ struct RouteArgs {
   float scaling;
   // optional side job on the bf16 activation rows side_x [T][side_K], run by extra
   // workgroups of the first routing launch (one launch fewer for small batches):
-  // SIDE_MXFP8: codes mx_q [T][side_K] and E8M0 scales mx_s [T][side_K/32];
-  // SIDE_F16: fp16 rows x16 [T][side_K] and their factors xf [T]
+  // SIDE_MXFP8: codes side_q [T][side_K] and E8M0 scales side_s [T][side_K/32];
+  // SIDE_NVFP4: codes side_q [T][side_K/2], E4M3 scales side_s [T][side_K/16], global scales side_f [T];
+  // SIDE_F16: fp16 rows side_h [T][side_K] and their factors side_f [T]
   int side;
   const uint16_t* side_x;
   int side_K;
-  uint8_t* mx_q;
-  uint8_t* mx_s;
-  uint16_t* x16;
-  float* xf;
+  uint8_t* side_q;
+  uint8_t* side_s;
+  float* side_f;
+  uint16_t* side_h;
 };
-enum RouteSide { SIDE_NONE = 0, SIDE_MXFP8 = 1, SIDE_F16 = 2 };
+enum RouteSide { SIDE_NONE = 0, SIDE_MXFP8 = 1, SIDE_F16 = 2, SIDE_NVFP4 = 3 };
 
 struct PlanArgs {
   const int32_t* ids;    // [T][k]

@@ -18,75 +18,15 @@
 
 namespace nvmoe {
 
-// Nearest E2M1 magnitude code to r >= 0 (ties to the even code), saturating at 6.
-__device__ __forceinline__ uint32_t e2m1_encode_rne_sat(float r) {
-  return (uint32_t)(r > 0.25f) + (uint32_t)(r >= 0.75f) + (uint32_t)(r > 1.25f) + (uint32_t)(r >= 1.75f) +
-         (uint32_t)(r > 2.5f) + (uint32_t)(r >= 3.5f) + (uint32_t)(r > 5.0f);
-}
-
-// Quantise one 16-element block with global scale gs; writes 8 code bytes and 1 scale byte.
-__device__ __forceinline__ void quant_block(const float* v, float gs, uint8_t* packed, uint8_t* scale) {
-  float ab = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) ab = fmaxf(ab, fabsf(v[i]));
-  uint32_t s = 0u;
-  if (gs != 0.0f) {
-    const float six_gs = 6.0f * gs;
-    s = e4m3_encode_rne_sat(ab / six_gs);
-  }
-  const float d = e4m3_to_f32(s) * gs;
-  uint32_t lo = 0u, hi = 0u;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    uint32_t code = (__float_as_uint(v[i]) >> 31) << 3;
-    if (d != 0.0f) code |= e2m1_encode_rne_sat(fabsf(v[i]) / d);
-    if (i < 8)
-      lo |= code << (4 * i);
-    else
-      hi |= code << (4 * (i - 8));
-  }
-  *(u32x2*)packed = u32x2{lo, hi};
-  *scale = (uint8_t)s;
-}
-
-template <typename T>
-__device__ __forceinline__ float wave_row_absmax(const T* row, int K) {
-  const int lane = threadIdx.x & (WAVE - 1);
-  float m = 0.0f;
-  for (int b = lane; b < K / 16; b += WAVE) {
-    float v[16];
-    load16(row + (size_t)b * 16, v);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
-  }
-#pragma unroll
-  for (int off = WAVE / 2; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, WAVE));
-  return m;
-}
-
-template <typename T>
-__device__ __forceinline__ void wave_quant_row(const T* row, int K, float gs, uint8_t* packed, uint8_t* scales) {
-  const int lane = threadIdx.x & (WAVE - 1);
-  for (int b = lane; b < K / 16; b += WAVE) {
-    float v[16];
-    load16(row + (size_t)b * 16, v);
-    quant_block(v, gs, packed + (size_t)b * 8, scales + b);
-  }
-}
-
-// One wave per row: global scale of the row, then its blocks (bf16 activation rows, or
-// the fp32 h rows of the NVFP4 down GEMM).
+// One wave per row (nvfp4_row_wave): bf16 activation rows, or the fp32 h rows of the NVFP4
+// down GEMM.
 template <typename T>
 __global__ __launch_bounds__(256) void quant_rows_kernel(const T* __restrict__ x, int rows, int K,
                                                          uint8_t* __restrict__ packed,
                                                          uint8_t* __restrict__ scales, float* __restrict__ gs) {
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= rows) return;
-  const T* row = x + (size_t)r * K;
-  const float A = wave_row_absmax(row, K);
-  const float g = A / 2688.0f;
-  if ((threadIdx.x & (WAVE - 1)) == 0) gs[r] = g;
-  wave_quant_row(row, K, g, packed + (size_t)r * (K / 2), scales + (size_t)r * (K / 16));
+  nvfp4_row_wave(x + (size_t)r * K, K, packed + (size_t)r * (K / 2), scales + (size_t)r * (K / 16), gs + r);
 }
 
 // MXFP8 rows: one wave per row (mxfp8_row_wave), 4 rows per workgroup.

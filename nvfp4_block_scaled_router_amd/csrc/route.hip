@@ -192,17 +192,20 @@ __device__ __forceinline__ void route_token_general(const RouteArgs& r, int t, i
 }
 
 // The side job of a routing launch: workgroup j past the routing workgroups converts rows
-// j * (waves per workgroup) + wave of side_x (MXFP8 codes and scales, or fp16 rows and their
-// factors), one wave per row.
+// j * (waves per workgroup) + wave of side_x (MXFP8 or NVFP4 codes and scales, or fp16 rows
+// and their factors), one wave per row.
 __device__ __forceinline__ void side_rows(const RouteArgs& a, int j) {
   const int wpb = blockDim.x >> 6;
   const int t = j * wpb + (int)(threadIdx.x >> 6);
   if (t >= a.T) return;
   const int K = a.side_K, lane = (int)(threadIdx.x & (WAVE - 1));
+  const uint16_t* row = a.side_x + (size_t)t * K;
   if (a.side == SIDE_MXFP8)
-    mxfp8_row_wave(a.side_x + (size_t)t * K, K, a.mx_q + (size_t)t * K, a.mx_s + (size_t)t * (K / 32), lane);
+    mxfp8_row_wave(row, K, a.side_q + (size_t)t * K, a.side_s + (size_t)t * (K / 32), lane);
+  else if (a.side == SIDE_NVFP4)
+    nvfp4_row_wave(row, K, a.side_q + (size_t)t * (K / 2), a.side_s + (size_t)t * (K / 16), a.side_f + t);
   else
-    f16_row_wave(a.side_x + (size_t)t * K, K, a.x16 + (size_t)t * K, a.xf + t, lane);
+    f16_row_wave(row, K, a.side_h + (size_t)t * K, a.side_f + t, lane);
 }
 
 template <int EPL>
@@ -442,8 +445,10 @@ static hipError_t launch_route_plan_t(const RouteArgs& r, const PlanArgs& p, int
     return hipGetLastError();
   }
   if (side) {
-    const hipError_t e = r.side == SIDE_MXFP8 ? launch_mxfp8_rows_bf16(r.side_x, r.T, r.side_K, r.mx_q, r.mx_s, s)
-                                              : launch_rows_to_f16(r.side_x, r.T, r.side_K, r.x16, r.xf, s);
+    const hipError_t e =
+        r.side == SIDE_MXFP8   ? launch_mxfp8_rows_bf16(r.side_x, r.T, r.side_K, r.side_q, r.side_s, s)
+        : r.side == SIDE_NVFP4 ? launch_quant_rows_bf16(r.side_x, r.T, r.side_K, r.side_q, r.side_s, r.side_f, s)
+                               : launch_rows_to_f16(r.side_x, r.T, r.side_K, r.side_h, r.side_f, s);
     if (e != hipSuccess) return e;
   }
   if (r.general) {

@@ -54,9 +54,11 @@ SMALL = [
     synth.MoeConfig("decode-shared", T=7, H=256, I=128, E=16, k=4, shared=1, seed=17),
     synth.MoeConfig("decode-e256-k1", T=64, H=256, I=128, E=256, k=1, seed=18),
     synth.MoeConfig("decode-e200-t1", T=1, H=384, I=256, E=200, k=8, score="sigmoid", seed=19),
-    # decode-regime batches over 64 tokens with at least 256 routed rows (fp16 x): the rescale
-    # runs as its own launch beside the per-token router, or in the general router's launch
+    # decode-regime batches over 64 tokens with at least 256 routed rows (fp16 or NVFP4 x): the
+    # conversion runs as its own launch beside the per-token router, or in the general router's
+    # launch
     synth.MoeConfig("decode-wide-f16", T=100, H=256, I=128, E=64, k=4, seed=20),
+    synth.MoeConfig("decode-wide-w4a4", T=100, H=256, I=128, E=64, k=4, act="nvfp4", seed=30),
     synth.MoeConfig("decode-wide-general", T=90, H=256, I=128, E=64, k=4, score="sqrt_softplus", bias_sigma=0.5,
                     seed=29),
     # hidden 128 / 384: the prefill down launch cannot use its widest workgroup and narrows
