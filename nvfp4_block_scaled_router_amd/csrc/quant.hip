@@ -4,14 +4,16 @@
 // "Runtime Activation Global Scale": computed at run time from the activation so
 // that no E4M3 block scale overflows). The blocks follow the NVFP4 format of
 // [megamoe] README "NVFP4 throughout" (16-element microblocks, E4M3 scales, E2M1
-// values). Every step is one binary32 operation rounded to nearest even; this
-// file is compiled without contraction and with correctly rounded division, so
-// the bytes are a pure function of the input bits:
+// values). Every step is one binary32 operation rounded to nearest even (no sums,
+// so FP contraction cannot apply; division is correctly rounded), so the bytes
+// are a pure function of the input bits:
 //   s_b  = gs == 0 ? 0 : E4M3_rne_sat(a_b / (6 * gs))
 //   d_b  = E4M3(s_b) * gs
 //   code = signbit(x) << 3 | (d_b == 0 ? 0 : E2M1_rne_sat(|x| / d_b))
 // One wave quantises one row (activations) or the rows of a group after a
-// reduction kernel has produced the group's global scale (weights).
+// reduction kernel has produced the group's global scale (weights). The per-wave
+// row quantisers sit in rowq_dev.hpp, shared with the routing kernels, which run
+// them for the activation rows of decode batches.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "rowq_dev.hpp"
