@@ -77,6 +77,7 @@ class Oracle:
                                        _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _f64, _i32]
         L.orc_dequant_rows.argtypes = [_vp, _vp, _vp, _i64, _i32, _vp]
         L.orc_bf16_rows.argtypes = [_vp, _i64, _vp]
+        L.orc_decode_proj.argtypes = [ctypes.POINTER(ProjSet), _i32, _i32, _i32, _i32, _vp]
         self.L = L
         self.path = path
 
@@ -194,6 +195,15 @@ class Oracle:
     def weight_mx(self, packed, scales, n, k) -> float:
         K = packed.shape[-1] * 2
         return self.L.orc_weight_mx(packed.ctypes.data, scales.ctypes.data, K, n, k)
+
+    def decode_projection(self, W, g: int) -> np.ndarray:
+        """Expert g of one projection W = (packed [G][N][K/2], scales, gs or None) decoded to
+        FP64 [N][K] by the oracle's element decode (NVFP4, or MXFP4 when gs is None)."""
+        N, K = W[0].shape[1], W[0].shape[2] * 2
+        ps = self._projset(W, W)
+        out = np.empty((N, K), np.float64)
+        self.L.orc_decode_proj(ctypes.byref(ps), 0, g, N, K, out.ctypes.data)
+        return out
 
     @staticmethod
     def _projset(W1, W2):

@@ -13,6 +13,12 @@ functions of ``oracle.c`` in the order the method runs them:
 
 Weights are the synth draws quantised per expert projection by the oracle's
 own quantizer (one global scale per expert projection).
+
+``forward`` evaluates the MLPs per token in the C loops (weights decoded element by
+element at every use); ``forward_by_expert`` evaluates the same definition one expert
+at a time (each expert decoded once, FP64 matrix products as the library step) so that
+full-size layers can be checked on every token. Both are pinned, the second against the
+first and against a dense numpy layer (tests/pins.py).
 """
 from __future__ import annotations
 
@@ -94,6 +100,26 @@ def route(cfg: synth.MoeConfig, logits: np.ndarray, o: Optional[Oracle] = None):
     return o.route(logits, cfg.k, cfg.score)
 
 
+def _prepare(cfg, x_bf16, logits, tokens, o):
+    """forward()'s routing, plan and decoded activation rows (no expert MLP)."""
+    T = x_bf16.shape[0]
+    tokens = np.arange(T, dtype=np.int32) if tokens is None else np.asarray(tokens, np.int32)
+    ids, w = route(cfg, logits, o)
+    counts, offsets, perm, inv = o.plan(ids, cfg.E)
+    res = dict(ids=ids, w=w, counts=counts, offsets=offsets, perm=perm, inv=inv, tokens=tokens)
+    if cfg.act == "mxfp8":
+        xq, xs = o.mxfp8_quantize(o.bf16_rows(x_bf16).astype(np.float32))
+        res.update(xq=xq, xs=xs)
+        res["x_rows"] = o.mxfp8_rows(xq[tokens], xs[tokens])
+    elif cfg.act in ("nvfp4", "nvfp4_all"):
+        xq, xs, xg = o.quantize(o.bf16_rows(x_bf16).astype(np.float32), rows_per_gs=1)
+        res.update(xq=xq, xs=xs, xg=xg)
+        res["x_rows"] = o.dequant_rows(xq[tokens], xs[tokens], xg[tokens])
+    else:
+        res["x_rows"] = o.bf16_rows(x_bf16[tokens])
+    return res
+
+
 def forward(cfg: synth.MoeConfig, x_bf16: np.ndarray, logits: np.ndarray, W1, W2, WS1=None,
             WS2=None, tokens: Optional[np.ndarray] = None, o: Optional[Oracle] = None) -> Dict:
     """Layer output (FP64, never rounded) for `tokens` (all tokens if None).
@@ -102,23 +128,83 @@ def forward(cfg: synth.MoeConfig, x_bf16: np.ndarray, logits: np.ndarray, W1, W2
     offsets [E+1], perm [T*k], inv [T*k], and for W4A4 the quantised
     activations xq [T][H/2], xs [T][H/16], xg [T]."""
     o = o or default()
-    T = x_bf16.shape[0]
-    tokens = np.arange(T, dtype=np.int32) if tokens is None else np.asarray(tokens, np.int32)
-    ids, w = route(cfg, logits, o)
-    counts, offsets, perm, inv = o.plan(ids, cfg.E)
-    res = dict(ids=ids, w=w, counts=counts, offsets=offsets, perm=perm, inv=inv, tokens=tokens)
-    if cfg.act == "mxfp8":                               # W4A8: MXFP8 x (and h)
-        xf = o.bf16_rows(x_bf16).astype(np.float32)       # exact: bf16 -> binary32
-        xq, xs = o.mxfp8_quantize(xf)
-        res.update(xq=xq, xs=xs)
-        x_rows = o.mxfp8_rows(xq[tokens], xs[tokens])
-    elif cfg.act in ("nvfp4", "nvfp4_all"):
-        xf = o.bf16_rows(x_bf16).astype(np.float32)       # exact: bf16 -> binary32
-        xq, xs, xg = o.quantize(xf, rows_per_gs=1)
-        res.update(xq=xq, xs=xs, xg=xg)
-        x_rows = o.dequant_rows(xq[tokens], xs[tokens], xg[tokens])
-    else:
-        x_rows = o.bf16_rows(x_bf16[tokens])
+    res = _prepare(cfg, x_bf16, logits, tokens, o)
+    x_rows = res.pop("x_rows")
     hq = {"nvfp4_all": 1, "mxfp8": 2}.get(cfg.act, 0)
-    res["out"] = o.moe_tokens(W1, W2, WS1, WS2, tokens, x_rows, ids, w, cfg.swiglu_limit, hq=hq)
+    res["out"] = o.moe_tokens(W1, W2, WS1, WS2, res["tokens"], x_rows, res["ids"], res["w"], cfg.swiglu_limit,
+                              hq=hq)
+    return res
+
+
+def _swiglu(g: np.ndarray, u: np.ndarray, limit: Optional[float]) -> np.ndarray:
+    """silu(g) u, or with a limit L the clamped silu(min(g, L)) min(max(u, -L), L), FP64,
+    as the oracle's per-token MLP evaluates it (g / (1 + exp(-g)) u)."""
+    if limit is not None:
+        g = np.minimum(g, limit)
+        u = np.minimum(np.maximum(u, -limit), limit)
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g)) * u
+
+
+def _quantize_h(h: np.ndarray, hq: int, o: Oracle) -> np.ndarray:
+    """h rows rounded to binary32 and quantised as forward()'s MLP does: NVFP4 with one
+    global scale per row (hq 1) or MXFP8 (hq 2), returned as their exact FP64 decode."""
+    h32 = h.astype(np.float32)
+    if hq == 2:
+        return o.mxfp8_rows(*o.mxfp8_quantize(h32))
+    return o.dequant_rows(*o.quantize(h32, rows_per_gs=1))
+
+
+def forward_by_expert(cfg: synth.MoeConfig, x_bf16: np.ndarray, logits: np.ndarray, W1, W2, WS1=None,
+                      WS2=None, tokens: Optional[np.ndarray] = None, o: Optional[Oracle] = None,
+                      progress=None) -> Dict:
+    """forward()'s result evaluated one expert at a time (for full-size checks).
+
+    The layer output out_t = sum_j w_tj FFN_{ids_tj}(x_t) (+ FFN_shared(x_t)) is a sum of
+    one term per (token, pick). Here each expert's two projections are decoded once to FP64
+    by the oracle's element decode (``decode_projection``) and its FFN is applied to every
+    row routed to it with FP64 matrix products as the library step: g = X Wg^T, u = X Wu^T,
+    h = SwiGLU(g, u) (quantised first for the h-quantised variants), y = h W2^T. The terms
+    of a token are then summed in pick order, the shared expert last, as forward() sums
+    them. Routing, the activation rows and every formula are forward()'s; only the order of
+    the FP64 roundings inside each dot product differs (relative differences near 1e-16)."""
+    o = o or default()
+    res = _prepare(cfg, x_bf16, logits, tokens, o)
+    tokens = res["tokens"]
+    ids, w, counts, offsets, perm = res["ids"], res["w"], res["counts"], res["offsets"], res["perm"]
+    T, k = ids.shape
+    H, I = cfg.H, cfg.I
+    x_rows = res.pop("x_rows")                            # decoded inputs of `tokens`, in that order
+    pos = np.full(T, -1, np.int64)                        # token -> its row in x_rows / out
+    pos[tokens] = np.arange(len(tokens))
+    hq = {"nvfp4_all": 1, "mxfp8": 2}.get(cfg.act, 0)
+    routed_limit = cfg.swiglu_limit
+
+    def ffn(Wa, Wb, g, X, limit):
+        A = o.decode_projection(Wa, g)                    # [2I][H]: gate rows, then up rows
+        h = _swiglu(X @ A[:I].T, X @ A[I:].T, limit)
+        del A
+        if hq:
+            h = _quantize_h(h, hq, o)
+        return h @ o.decode_projection(Wb, g).T           # [rows][H]
+
+    Y = np.zeros((len(tokens), k, H), np.float64)         # one term per (token, pick)
+    for e in range(cfg.E):
+        rows = perm[offsets[e]:offsets[e + 1]]
+        t_of, j_of = rows // k, rows % k
+        keep = pos[t_of] >= 0
+        if not keep.any():
+            continue
+        t_of, j_of = pos[t_of[keep]], j_of[keep]
+        Y[t_of, j_of] = ffn(W1, W2, e, x_rows[t_of], routed_limit)
+        if progress and (e % 32 == 31 or e == cfg.E - 1):
+            progress(f"oracle by expert: experts 0..{e} of {cfg.E} done")
+    out = np.zeros((len(tokens), H), np.float64)
+    wt = w[tokens]
+    for j in range(k):                                    # picks in order
+        out += wt[:, j:j + 1] * Y[:, j]
+    del Y
+    for s in range(cfg.shared):                           # shared expert(s) last, weight 1
+        out += ffn(WS1, WS2, s, x_rows, None)
+    res["out"] = out
     return res

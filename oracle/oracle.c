@@ -574,3 +574,13 @@ void orc_dequant_rows(const uint8_t* packed, const uint8_t* scales, const float*
 void orc_bf16_rows(const uint16_t* b, int64_t n, double* x) {
   for (int64_t i = 0; i < n; ++i) x[i] = orc_bf16(b[i]);
 }
+
+/* One expert projection decoded to FP64, row-major [N][K]: element (n, k) exactly as
+ * proj_weight gives it (NVFP4: E2M1 x E4M3 x global scale; MXFP4: E2M1 x E8M0). The
+ * per-expert evaluation of the layer (oracle/moe.py, forward_by_expert) decodes each
+ * expert once with it instead of once per use; the values are the same. */
+void orc_decode_proj(const orc_proj_set* P, int second, int g, int N, int K, double* W) {
+#pragma omp parallel for schedule(static)
+  for (int n = 0; n < N; ++n)
+    for (int k = 0; k < K; ++k) W[(size_t)n * K + k] = proj_weight(P, second, g, N, K, n, k);
+}

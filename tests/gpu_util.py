@@ -162,6 +162,36 @@ def gpu_weights(cfg, which):
                                progress=log)
 
 
+def both_weights(cfg, which, experts=None):
+    """Every expert of one projection quantised by the library's device quantiser (the GPU
+    side's weights) and the experts in `experts` (all if None) from the same fp32 draws by the
+    oracle's (the oracle's weights; the rest stay zero there). The two must agree byte for
+    byte. Returns (oracle arrays, device tensors)."""
+    o = oracle.default()
+    G = cfg.shared if which.startswith("ws") else cfg.E
+    N, K = (2 * cfg.I, cfg.H) if which in ("w1", "ws1") else (cfg.H, cfg.I)
+    host = (np.zeros((G, N, K // 2), np.uint8), np.zeros((G, N, K // 16), np.uint8), np.zeros(G, np.float32))
+    dev = (torch.empty((G, N, K // 2), dtype=torch.uint8, device=DEV),
+           torch.empty((G, N, K // 16), dtype=torch.uint8, device=DEV), torch.empty(G, dtype=torch.float32, device=DEV))
+    per = max(1, (1 << 30) // (4 * N * K))
+    for e0 in range(0, G, per):
+        cnt = min(per, G - e0)
+        w = synth.expert_weights_f32(cfg, which, e0, cnt)
+        m.moe_quantize_nvfp4_weights(torch.from_numpy(w).to(DEV), cnt, N, K, dev[0][e0:e0 + cnt],
+                                     dev[1][e0:e0 + cnt], dev[2][e0:e0 + cnt])
+        sel = [e for e in range(e0, e0 + cnt) if experts is None or e in experts]
+        w = w.reshape(cnt, N, K)
+        for e in sel:
+            p, sc, g = o.quantize(w[e - e0], rows_per_gs=N)
+            host[0][e], host[1][e], host[2][e] = p, sc, g[0]
+            for a, d in zip(host, dev):
+                assert np.array_equal(a[e], d[e].cpu().numpy()), \
+                    f"device weight quantiser differs from the oracle's ({which}, expert {e})"
+        log(f"  {which}: experts {e0}..{e0 + cnt - 1} of {G} quantised on the device, {len(sel)} of them also "
+            f"by the oracle: bytes identical")
+    return host, list(dev)
+
+
 _WCACHE = {}
 
 
@@ -176,10 +206,17 @@ def oracle_weights(cfg, which, experts):
 
 
 class Case:
-    """One configuration on both sides: oracle expectations and the device layer."""
+    """One configuration on both sides: oracle expectations and the device layer.
 
-    def __init__(self, cfg, tokens=None, weights="oracle"):
+    weights: "oracle" -- the oracle's quantiser for both sides (with a token subset, only
+    the experts those tokens use are filled; the rest are zero); "gpu" -- every expert
+    quantised from the same draws by the library's device quantiser for the GPU side and
+    by the oracle's for the oracle side, asserted byte-identical. by_expert: evaluate the
+    oracle one expert at a time (oracle.moe.forward_by_expert), for full-size checks."""
+
+    def __init__(self, cfg, tokens=None, weights="oracle", by_expert=False):
         self.cfg = cfg
+        self.by_expert = by_expert
         self.x = synth.activations(cfg)
         self.logits = synth.logits(cfg)
         o = oracle.default()
@@ -193,17 +230,13 @@ class Case:
                  for w in projs]
             dev = [[up(Wi[0]), up(Wi[1]), None] for Wi in W]
         elif weights == "oracle":
-            W = [oracle_weights(cfg, w, need if w in ("w1", "w2") else None)
-                 for w in (["w1", "w2"] + (["ws1", "ws2"] if cfg.shared else []))]
+            sel = need if tokens is not None else None
+            W = [oracle_weights(cfg, w, sel if w in ("w1", "w2") else None) for w in projs]
             dev = [[up(a) for a in Wi] for Wi in W]
-        else:  # device quantiser for every expert; oracle quantises the experts it needs
-            dev = [gpu_weights(cfg, w) for w in (["w1", "w2"] + (["ws1", "ws2"] if cfg.shared else []))]
-            W = [omoe.quantized_weights(cfg, w, need if w in ("w1", "w2") else None)
-                 for w in (["w1", "w2"] + (["ws1", "ws2"] if cfg.shared else []))]
-            for Wi, Di in zip(W, dev):               # the two quantisers agree on what the oracle uses
-                sel = need if Wi[0].shape[0] == cfg.E else list(range(Wi[0].shape[0]))
-                for a, d in zip(Wi, Di):
-                    assert np.array_equal(a[sel], d[sel].cpu().numpy()), "device weight quantiser differs"
+        else:  # every expert, device and oracle quantisers from the same draws
+            sel = set(need) if tokens is not None else None
+            W, dev = zip(*[both_weights(cfg, w, sel if w in ("w1", "w2") else None) for w in projs])
+            W, dev = list(W), list(dev)
         self.W = W
         self.dev_w = dev
         self.need = need
@@ -211,6 +244,9 @@ class Case:
     def reference(self):
         W1, W2 = self.W[0], self.W[1]
         WS1, WS2 = (self.W[2], self.W[3]) if self.cfg.shared else (None, None)
+        if self.by_expert:
+            return omoe.forward_by_expert(self.cfg, self.x, self.logits, W1, W2, WS1, WS2, tokens=self.tokens,
+                                          progress=log)
         return omoe.forward(self.cfg, self.x, self.logits, W1, W2, WS1, WS2, tokens=self.tokens)
 
     def layer(self, max_tokens=None):

@@ -811,4 +811,77 @@ def pin_dequant_rows(o):
     assert np.array_equal(got, ref)
 
 
+# ---------------------------------------------- per-expert evaluation of the layer
+
+def _by_expert_configs():
+    import synth
+    return [
+        synth.MoeConfig("bx-plain", T=24, H=128, I=128, E=8, k=2, seed=201),
+        synth.MoeConfig("bx-shared-sigmoid", T=20, H=256, I=128, E=16, k=4, score="sigmoid", shared=1, seed=202),
+        synth.MoeConfig("bx-w4a4-clamp", T=16, H=128, I=128, E=8, k=2, act="nvfp4", swiglu_limit=0.05, shared=1,
+                        seed=203),
+        synth.MoeConfig("bx-h-nvfp4", T=16, H=128, I=128, E=8, k=2, act="nvfp4_all", shared=1, seed=204),
+        synth.MoeConfig("bx-w4a8", T=16, H=128, I=128, E=8, k=2, act="mxfp8", wfmt="mxfp4", seed=205),
+        synth.MoeConfig("bx-mx-general", T=16, H=128, I=128, E=16, k=4, wfmt="mxfp4", score="sqrt_softplus",
+                        bias_sigma=0.3, seed=206),
+    ]
+
+
+def _layer_weights(cfg, o):
+    import oracle.moe as omoe
+    W = [omoe.projection_weights(cfg, w, o=o) for w in ("w1", "w2")]
+    S = [omoe.projection_weights(cfg, w, o=o) for w in ("ws1", "ws2")] if cfg.shared else [None, None]
+    return W + S
+
+
+def pin_moe_by_expert_equals_per_token(o):
+    """forward_by_expert (each expert decoded once, FP64 matrix products, terms summed per
+    token in pick order) against forward (per token, per element, the C loops) on small
+    layers of every variant: plain, shared + sigmoid, NVFP4 x + clamp, NVFP4 h, MXFP8 x and h
+    on MXFP4 weights, the generalised router; and on a token subset given out of order."""
+    import synth
+    import oracle.moe as omoe
+    for cfg in _by_expert_configs():
+        x, lg = synth.activations(cfg), synth.logits(cfg)
+        W1, W2, WS1, WS2 = _layer_weights(cfg, o)
+        a = omoe.forward(cfg, x, lg, W1, W2, WS1, WS2, o=o)["out"]
+        b = omoe.forward_by_expert(cfg, x, lg, W1, W2, WS1, WS2, o=o)["out"]
+        rms = np.sqrt(np.mean(a * a))
+        assert rms > 0 and np.abs(a - b).max() <= 1e-12 * rms, (cfg.name, np.abs(a - b).max() / rms)
+        sub = np.array([5, 0, cfg.T - 1, 3], np.int32)
+        c = omoe.forward_by_expert(cfg, x, lg, W1, W2, WS1, WS2, tokens=sub, o=o)["out"]
+        assert np.abs(c - a[sub]).max() <= 1e-12 * rms, cfg.name
+
+
+def pin_moe_by_expert_dense_numpy(o):
+    """forward_by_expert against a dense numpy layer built from the library decoders (torch's
+    float8 decoders for the weights and bf16 inputs): per token, the sum over its picks of
+    w_j W2_e (silu(Wg_e x) * (Wu_e x)), plus the shared expert. Routing ids and weights are
+    taken from the result (they are pinned on their own)."""
+    import synth
+    import oracle.moe as omoe
+    for cfg in _by_expert_configs():
+        if cfg.act not in ("bf16",):
+            continue
+        x, lg = synth.activations(cfg), synth.logits(cfg)
+        W1, W2, WS1, WS2 = _layer_weights(cfg, o)
+        res = omoe.forward_by_expert(cfg, x, lg, W1, W2, WS1, WS2, o=o)
+        dec = (lambda W, e: decode_mxfp4(W[0][e], W[1][e])) if cfg.wfmt == "mxfp4" else \
+            (lambda W, e: decode_nvfp4(W[0][e], W[1][e], W[2][e]))
+        X = bf16_to_f64(x)
+        I = cfg.I
+
+        def mlp(Wa, Wb, e, v):
+            A, B = dec(Wa, e), dec(Wb, e)
+            return B @ (silu(A[:I] @ v) * (A[I:] @ v))
+        ref = np.zeros((cfg.T, cfg.H))
+        for t in range(cfg.T):
+            for j in range(cfg.k):
+                ref[t] += res["w"][t, j] * mlp(W1, W2, res["ids"][t, j], X[t])
+            for s in range(cfg.shared):
+                ref[t] += mlp(WS1, WS2, s, X[t])
+        rms = np.sqrt(np.mean(ref * ref))
+        assert np.abs(ref - res["out"]).max() <= 1e-12 * rms, cfg.name
+
+
 ALL_PINS = [v for k, v in dict(globals()).items() if k.startswith("pin_")]

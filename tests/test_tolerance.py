@@ -35,6 +35,7 @@ def _w4a8_case():
                           seed=77)
     case = Case.__new__(Case)
     case.cfg, case.x, case.logits = cfg, synth.activations(cfg), synth.logits(cfg)
+    case.by_expert = False
     case.tokens = np.arange(cfg.T, dtype=np.int32)
     case.W = [tuple(synth.mxfp4_weights(cfg, w, 0, cfg.shared if w.startswith("ws") else cfg.E)) + (None,)
               for w in ("w1", "w2", "ws1", "ws2")]
