@@ -63,6 +63,7 @@ extern "C" {
 #define MOE_ERR_ABI (-6)       /* desc->abi_version is neither 1 nor MOE_ABI_VERSION */
 #define MOE_ERR_ENUM (-7)      /* invalid enum value */
 #define MOE_ERR_WEIGHT (-8)    /* invalid weight data (host validation) */
+#define MOE_ERR_SCRATCH (-9)   /* moe_run_no_alloc: the plan's workspace exceeds MOE_STATIC_SCRATCH_BYTES */
 
 /* Router score ([b12x] "What's in here": routing scores kept in FP32;
  * [vllm.cpp] capability table: sigmoid noaux_tc routers; [vllm.cpp] DeepSeek-V4
@@ -288,6 +289,24 @@ int moe_run(const moe_plan_t* plan, const void* packed, int32_t T, const uint16_
 int moe_run_timed(const moe_plan_t* plan, const void* packed, int32_t T, const uint16_t* x,
                   const float* router_logits, uint16_t* out, const moe_routing_out* routing,
                   void* workspace, size_t workspace_bytes, void* stream, void* const* stage_events);
+
+/* moe_run without a caller workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation).
+ * The workspace is a fixed array of MOE_STATIC_SCRATCH_BYTES inside the library, one
+ * copy per GPU, held until the process ends; the call uses the copy of the current
+ * device (hipGetDevice), so `stream` must belong to that device. Arguments, results and
+ * error codes are moe_run's; MOE_ERR_SCRATCH if the plan's workspace_bytes exceeds
+ * MOE_STATIC_SCRATCH_BYTES (64 MiB: any T_max of a decode-sized layer; the Qwen3-30B-A3B
+ * shape up to about 1300 tokens). No call allocates or frees anything; the first call on
+ * a device resolves the array's address there (hipGetSymbolAddress, no allocation). The
+ * array keeps the previous call's contents, which the layer never reads: every value it
+ * uses is written earlier in the same call. All calls on one GPU share the array, so calls
+ * that may overlap in time on one GPU (different streams, or different threads) race and
+ * must be serialised by the caller. */
+#define MOE_STATIC_SCRATCH_BYTES (64u << 20)
+int moe_run_no_alloc(const moe_plan_t* plan, const void* packed, int32_t T, const uint16_t* x,
+                     const float* router_logits, uint16_t* out, const moe_routing_out* routing,
+                     void* stream);
 
 /* NVFP4 row quantiser (the W4A4 activation step of moe_run, callable alone):
  * for each of `rows` bf16 rows of K elements (K a multiple of 16, <= 16384):

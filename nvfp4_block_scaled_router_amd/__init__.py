@@ -22,13 +22,15 @@ MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID, MOE_SCORE_SQRT_SOFTPLUS = 0, 1, 2
 MOE_ACT_BF16, MOE_ACT_NVFP4_ROWQ, MOE_ACT_NVFP4_ALL, MOE_ACT_MXFP8 = 0, 1, 2, 3
 MOE_WEIGHTS_NVFP4, MOE_WEIGHTS_MXFP4 = 0, 1
 MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_SIZE, MOE_ERR_TOKENS = 0, -1, -2, -3, -4
-MOE_ERR_ALIGN, MOE_ERR_ABI, MOE_ERR_ENUM, MOE_ERR_WEIGHT = -5, -6, -7, -8
+MOE_ERR_ALIGN, MOE_ERR_ABI, MOE_ERR_ENUM, MOE_ERR_WEIGHT, MOE_ERR_SCRATCH = -5, -6, -7, -8, -9
+MOE_STATIC_SCRATCH_BYTES = 64 << 20
 
 MOE_STAGE_QUANT, MOE_STAGE_ROUTE, MOE_STAGE_GATE_UP, MOE_STAGE_DOWN, MOE_STAGE_COMBINE = 0, 1, 2, 3, 4
 MOE_NUM_STAGES = 5
 STAGE_NAMES = ("quant", "route", "gate_up", "down", "combine")
 
 EXPORTED = ("moe_plan", "moe_plan_destroy", "moe_pack_weights", "moe_pack_router_bias", "moe_run", "moe_run_timed",
+            "moe_run_no_alloc",
             "moe_quantize_nvfp4_rows", "moe_quantize_nvfp4_weights", "moe_validate_weights_host", "moe_strerror",
             "moe_abi_version")
 
@@ -78,6 +80,8 @@ def lib() -> ctypes.CDLL:
         L.moe_run_timed.restype = _i32
         L.moe_run_timed.argtypes = [_vp, _vp, _i32, _vp, _vp, _vp, ctypes.POINTER(moe_routing_out), _vp, _sz, _vp,
                                     ctypes.POINTER(_vp)]
+        L.moe_run_no_alloc.restype = _i32
+        L.moe_run_no_alloc.argtypes = [_vp, _vp, _i32, _vp, _vp, _vp, ctypes.POINTER(moe_routing_out), _vp]
         L.moe_quantize_nvfp4_rows.restype = _i32
         L.moe_quantize_nvfp4_rows.argtypes = [_vp, _i32, _i32, _vp, _vp, _vp, _vp]
         L.moe_quantize_nvfp4_weights.restype = _i32
@@ -206,6 +210,13 @@ def moe_run_timed(plan, packed, T: int, x, router_logits, out, routing: Optional
     _check(lib().moe_run_timed(plan, _ptr(packed), T, _ptr(x), _ptr(router_logits), _ptr(out),
                                None if routing is None else ctypes.byref(routing), _ptr(workspace),
                                workspace_bytes, _stream(stream), arr))
+
+
+def moe_run_no_alloc(plan, packed, T: int, x, router_logits, out, routing: Optional[moe_routing_out],
+                     stream=None) -> None:
+    """moe_run with the library's static device scratch as the workspace (no allocation)."""
+    _check(lib().moe_run_no_alloc(plan, _ptr(packed), T, _ptr(x), _ptr(router_logits), _ptr(out),
+                                  None if routing is None else ctypes.byref(routing), _stream(stream)))
 
 
 def moe_quantize_nvfp4_rows(x, rows: int, K: int, packed, scales, row_global, stream=None) -> None:

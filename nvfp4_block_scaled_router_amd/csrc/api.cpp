@@ -7,6 +7,7 @@
 #include <cstdint>
 #include <cstddef>
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "../../include/nvfp4_moe.h"
@@ -73,6 +74,7 @@ const char* moe_strerror(int code) {
     case MOE_ERR_ABI: return "ABI version mismatch";
     case MOE_ERR_ENUM: return "invalid enum value";
     case MOE_ERR_WEIGHT: return "invalid weight data (NaN/negative scale or bad global scale)";
+    case MOE_ERR_SCRATCH: return "the plan's workspace exceeds the static scratch of moe_run_no_alloc";
     default: break;
   }
   if (code > 0) return hipGetErrorString((hipError_t)code);
@@ -266,6 +268,48 @@ int moe_run_timed(const moe_plan_t* plan, const void* packed, int32_t T, const u
                   size_t workspace_bytes, void* stream, void* const* stage_events) {
   return run_impl(plan, packed, T, x, router_logits, out, routing, workspace, workspace_bytes, stream,
                   stage_events);
+}
+
+// ---------------------------------------------------------------- no-allocation run
+// moe_run_no_alloc runs the layer with the workspace in `scratch`, a fixed device array of
+// the library (each GPU the library runs on holds its own copy until the process ends).
+// Host code never uses the array's name as an address: it stands for a host-side shadow.
+// The device address comes from hipGetSymbolAddress, once per device with that device
+// current, and is kept in scratch_ptr[device].
+static __device__ __align__(256) uint8_t scratch[MOE_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int MAX_DEVICES = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[MAX_DEVICES];
+}  // namespace
+
+// The current device's address of `scratch` (resolved on the first call for the device).
+static int static_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return (int)e;
+  if (dev < 0 || dev >= MAX_DEVICES) return (int)hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return (int)e;
+    if (!p || ((uintptr_t)p & (ALIGN - 1))) return (int)hipErrorInvalidSymbol;
+    scratch_ptr[dev] = p;
+  }
+  *ptr = scratch_ptr[dev];
+  return MOE_OK;
+}
+
+int moe_run_no_alloc(const moe_plan_t* plan, const void* packed, int32_t T, const uint16_t* x,
+                     const float* router_logits, uint16_t* out, const moe_routing_out* routing, void* stream) {
+  if (!plan) return MOE_ERR_NULL;
+  if (plan->ws_bytes > MOE_STATIC_SCRATCH_BYTES) return MOE_ERR_SCRATCH;
+  void* ws = nullptr;
+  const int rc = static_scratch(&ws);
+  if (rc) return rc;
+  return run_impl(plan, packed, T, x, router_logits, out, routing, ws, plan->ws_bytes, stream, nullptr);
 }
 
 // Stages of several (or no) kernels are bracketed by event records on the stream; the

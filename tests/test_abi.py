@@ -159,6 +159,7 @@ def test_run_rejects_before_enqueue():
         t = m.nvfp4_tensor(fake, fake, fake)
         assert L.moe_pack_weights(plan, ctypes.byref(t), ctypes.byref(t), None, None, fake, pb - 1, None) == m.MOE_ERR_SIZE
         assert L.moe_pack_weights(plan, ctypes.byref(t), None, None, None, fake, pb, None) == m.MOE_ERR_NULL
+        assert L.moe_run_no_alloc(None, fake, 4, fake, fake, fake, None, None) == m.MOE_ERR_NULL
         assert L.moe_quantize_nvfp4_rows(fake, 4, 40, fake, fake, fake, None) == m.MOE_ERR_SHAPE
         assert L.moe_quantize_nvfp4_rows(fake + 4, 4, 64, fake, fake, fake, None) == m.MOE_ERR_ALIGN
         assert L.moe_quantize_nvfp4_weights(fake, 1, 0, 64, fake, fake, fake, None) == m.MOE_ERR_SHAPE
@@ -168,6 +169,28 @@ def test_run_rejects_before_enqueue():
         p2, _, w2 = m.moe_plan(desc())
         try:
             m.moe_run(p2, fake, 99, fake, fake, fake, None, fake, w2, stream=0)
+        finally:
+            m.moe_plan_destroy(p2)
+
+
+def test_no_alloc_rejects_oversize_plan():
+    """A plan whose workspace exceeds the static scratch is rejected on the host, before
+    any HIP call; a plan within it is not (checked here up to the first HIP call only
+    through sizes)."""
+    plan, pb, wb = m.moe_plan(desc(hidden=2048, inter=768, num_experts=128, top_k=8, max_tokens=4096))
+    fake = 1 << 20
+    try:
+        assert wb > m.MOE_STATIC_SCRATCH_BYTES
+        assert m.lib().moe_run_no_alloc(plan, fake, 4, fake, fake, fake, None, None) == m.MOE_ERR_SCRATCH
+    finally:
+        m.moe_plan_destroy(plan)
+    plan, pb, wb = m.moe_plan(desc(hidden=2048, inter=768, num_experts=128, top_k=8, max_tokens=64))
+    m.moe_plan_destroy(plan)
+    assert wb <= m.MOE_STATIC_SCRATCH_BYTES
+    with pytest.raises(RuntimeError, match="static scratch"):
+        p2, _, _ = m.moe_plan(desc(hidden=2048, inter=768, num_experts=128, top_k=8, max_tokens=4096))
+        try:
+            m.moe_run_no_alloc(p2, fake, 4, fake, fake, fake, None, stream=0)
         finally:
             m.moe_plan_destroy(p2)
 
@@ -192,7 +215,7 @@ def test_validate_weights_host():
 
 
 def test_strerror_covers_every_code():
-    for code in range(-8, 1):
+    for code in range(-9, 1):
         assert m.moe_strerror(code) and m.moe_strerror(code) != "unknown error"
 
 
