@@ -1,24 +1,41 @@
 """Benchmark of the NVFP4 block-scaled fused-MoE layer on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--headline-only]
+                    [--no-cpu-baseline]
 
-Default workload: the Qwen3-30B-A3B-shaped decode layer (H=2048, I=768, E=128,
-top-8, NVFP4 weights, BF16 activations). One step runs the whole layer once for
-each decode batch T in {1, 8, 32, 64} (105 tokens), each batch with its own
-seeded weights, inputs and logits, so the 1.36 GB of weights the step streams
-exceed the 256 MB Infinity Cache. Inputs are resident in HBM before timing;
-W warmup steps, then exactly K timed steps between two device synchronisations.
-The step is captured once in a HIP graph and replayed (the serving launch path);
-the eager-launch time of the same step is reported beside it.
+Default run: the Qwen3-30B-A3B-shaped decode layer (H=2048, I=768, E=128, top-8, NVFP4
+weights, BF16 activations) as the headline. One step runs the whole layer once for each
+decode batch T in {1, 8, 32, 64} (105 tokens), each batch with its own seeded weights,
+inputs and logits, so the 1.36 GB of weights the step streams exceed the 256 MB Infinity
+Cache. Beside it, in the same JSON line, the same measurement of the prefill
+configurations (the Qwen3 shape at T=4096; the DeepSeek-V3-shaped layer, T=8192, H=7168,
+I=2048, E=256, top-8 sigmoid router, one shared expert) under "prefill", and of the
+skewed W4A4 layer (T=512, H=4096, I=1536, E=64, top-4, Zipf-biased router, NVFP4
+row-quantised activations) under "skewed".
 
-Prints one JSON line: tokens/s of the whole step (value), the per-step distribution of K
-further replays (median, IQR, samples), plus
+Order: every batch is prepared and run once; then the oracle leg (unless
+--no-cpu-baseline) times the CPU oracle on a bounded sample and checks every batch's first
+run against the oracle (routing bit-exact, output within the parity tests' bar: every token
+of a decode batch, a seeded token sample of the prefill-sized ones); a mismatch prints the
+parity record and exits with status 1 before anything is timed. Inputs are resident in HBM
+before timing; each workload first runs untimed for one second (the GPU leaves its idle
+clocks), then W warmup steps, then exactly K timed steps between two device
+synchronisations, eager and as a replayed HIP graph (the serving launch path).
+
+The JSON line holds: tokens/s of the headline step (value, graph replay), the per-step
+distribution of K further replays (median, IQR, samples), the layer's HBM rate and its
+fraction of 8 TB/s, plus
   roofline:     the dominant kernel (the gate/up grouped GEMM) timed with HIP
                 events recorded on its launch stream over K further steps:
                 algorithmic bytes per launch / mean launch time vs 8 TB/s HBM
                 (decode) or algorithmic FLOPs / time vs 2.5 PFLOP/s bf16 MFMA
                 (prefill workloads);
-  cpu_baseline: the CPU oracle (FP64, OpenMP) on a bounded sample of the same
+  prefill / skewed: per workload step time, tokens/s, the layer's TFLOP/s and GB/s against
+                the MFMA and HBM peaks, and each grouped GEMM's (gate_up, down) rate and
+                fractions from the same kernel-stamped events;
+  parity:       the oracle checks the timing was gated on;
+  host:         CPU model and threads, GPU name, clocks, power and use before timing;
+  cpu_baseline: the CPU oracle (FP64, OpenMP) on a bounded sample of the headline
                 workload, on this host's cores.
 Other workloads (--workload qwen3-30b-a3b-prefill | deepseek-v3 | skewed-w4a4 |
 skewed-w4a4-all (h quantised to NVFP4 too) | tiny) print the same line for that configuration, and so do the router/activation
@@ -63,6 +80,7 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 FP8_PEAK_TFLOPS = 5000.0        # dense fp8 MFMA (the W4A8 scaled MFMA: E2M1 x E4M3 operands)
 NVFP4_BYTES_PER_WEIGHT = 0.5 + 1.0 / 16.0      # E2M1 nibble + one E4M3 byte per 16
+PEAK_SCLK_GHZ = 2.4                             # MI355X peak engine clock
 
 
 def log(msg):
@@ -133,7 +151,10 @@ class Batch:
         bufs, rout = self.layer.routing_buffers(cfg.T)
         self.layer(self.x, self.logits, out=self.out, routing=rout)
         torch.cuda.synchronize()
-        counts = bufs["expert_counts"].cpu().numpy()
+        # the first run's results, kept on the host for the parity gate
+        self.first = {k: v.cpu().numpy() for k, v in bufs.items()}
+        self.first_out = self.out.cpu()
+        counts = self.first["expert_counts"]
         self.touched = int((counts > 0).sum())
         self.expert_rows = sorted((int(c) for c in counts if c > 0), reverse=True)
         self.rows = cfg.T * cfg.k
@@ -166,6 +187,20 @@ class Batch:
         c = self.cfg
         return 2.0 * (self.rows + c.shared * c.T) * 2 * c.I * c.H
 
+    def down_bytes(self):
+        """Weights of the touched experts, the h rows read (h16 with its block exponents, or
+        the NVFP4 / MXFP8 h codes and scales) and the y rows written (fp16 + exponents)."""
+        c = self.cfg
+        rows = self.rows + c.shared * c.T
+        w = (self.touched + c.shared) * self.weight_bytes(c.H * c.I)
+        h = rows * {"nvfp4_all": c.I * NVFP4_BYTES_PER_WEIGHT + 4, "mxfp8": c.I * (1 + 1.0 / 32)}.get(
+            c.act, c.I * 2 + c.I / 16)
+        return w + h + rows * (c.H * 2 + c.H / 16)
+
+    def down_flops(self):
+        c = self.cfg
+        return 2.0 * (self.rows + c.shared * c.T) * c.H * c.I
+
     def layer_bytes(self):
         c = self.cfg
         w = (self.touched + c.shared) * (self.weight_bytes(2 * c.I * c.H) + self.weight_bytes(c.H * c.I))
@@ -176,35 +211,119 @@ class Batch:
         return 6.0 * (self.rows + c.shared * c.T) * c.I * c.H
 
 
-def cpu_baseline(cfgs, budget_s=6.0):
-    """The CPU oracle, untouched, on a bounded sample: the largest decode batch of the
-    workload (or 16 tokens of a prefill workload), repeated until budget_s has passed."""
+# Tokens of a prefill-sized batch the parity gate compares with the oracle (decode batches: all)
+PARITY_SAMPLE = {"qwen3-30b-a3b-prefill": 48, "skewed-w4a4": 48, "skewed-w4a4-all": 48, "deepseek-v3": 4,
+                 "deepseek-v3-noaux-t8192": 4, "deepseek-v4-flash-t8192": 8, "deepseek-v4-flash-w4a8-t8192": 8}
+PARITY_REL_L2, PARITY_MAX_OVER_RMS, PARITY_W_ABS = 5e-3, 2e-2, 1e-6
+
+
+def _parity_check(b, ref, tokens):
+    """The first run of batch b against the oracle's result `ref` for `tokens`: routing ids,
+    counts, offsets and permutation bit-exact, routing weights within 1e-6, quantised
+    activations bit-exact, and the output within relL2 <= 5e-3 and a max error beyond the
+    bf16 output rounding <= 2e-2 RMS (the parity tests' bar)."""
+    f = b.first
+    routing_ok = (np.array_equal(f["topk_ids"], ref["ids"]) and np.array_equal(f["expert_counts"], ref["counts"])
+                  and np.array_equal(f["expert_offsets"], ref["offsets"]) and np.array_equal(f["perm"], ref["perm"])
+                  and float(np.abs(f["topk_weights"] - ref["w"]).max()) <= PARITY_W_ABS)
+    act_ok = True
+    if "xq" in ref and "act_packed" in f:
+        act_ok = np.array_equal(f["act_packed"], ref["xq"]) and np.array_equal(f["act_scales"], ref["xs"])
+        if "xg" in ref:
+            act_ok = act_ok and np.array_equal(f["act_global"].view(np.uint32), ref["xg"].view(np.uint32))
+    o = b.first_out[torch.from_numpy(np.asarray(tokens, np.int64))].float().numpy().astype(np.float64)
+    r = ref["out"]
+    d = np.abs(o - r)
+    rms = float(np.sqrt(np.mean(r * r)))
+    _, ex = np.frexp(r)
+    half_ulp = np.where(r == 0, 0.0, np.ldexp(1.0, ex - 9))
+    rel = float(np.linalg.norm(o - r) / np.linalg.norm(r))
+    beyond = float(max((d - half_ulp).max(), 0.0) / rms)
+    ok = bool(routing_ok and act_ok and rel <= PARITY_REL_L2 and beyond <= PARITY_MAX_OVER_RMS and np.isfinite(o).all())
+    return {"batch": b.cfg.name, "tokens_checked": int(len(tokens)), "tokens": int(b.cfg.T),
+            "routing_bit_exact": bool(routing_ok), "activation_codes_bit_exact": bool(act_ok) if "xq" in ref else None,
+            "relL2": rel, "max_over_rms": float(d.max() / rms), "beyond_bf16_over_rms": beyond, "ok": ok}
+
+
+def cpu_baseline_and_parity(headline, extra, budget_s=6.0):
+    """The CPU oracle, untouched, on a bounded sample (the largest batch of the headline
+    workload: all its tokens if it has at most 64, else 16), repeated until budget_s has
+    passed; then the parity gate: that result and the oracle's result for every other batch
+    (every token of a decode batch, a seeded token sample of a prefill-sized one, evaluated
+    one expert at a time) against each batch's first run on the GPU."""
     import oracle
     import oracle.moe as omoe
     o = oracle.default()
-    cfg = max(cfgs, key=lambda c: c.T)
+
+    def weights(cfg, need):
+        W1 = omoe.projection_weights(cfg, "w1", need)
+        W2 = omoe.projection_weights(cfg, "w2", need)
+        WS1 = omoe.projection_weights(cfg, "ws1") if cfg.shared else None
+        WS2 = omoe.projection_weights(cfg, "ws2") if cfg.shared else None
+        return W1, W2, WS1, WS2
+
+    big = max(headline, key=lambda b: b.cfg.T)
+    cfg = big.cfg
     tokens = np.arange(cfg.T, dtype=np.int32) if cfg.T <= 64 else synth.token_sample(cfg, 16)
     logits = synth.logits(cfg)
     ids, _ = omoe.route(cfg, logits, o)
     need = sorted(set(ids[tokens].reshape(-1).tolist()))
     log(f"[bench] cpu baseline: preparing the weights of {len(need)} experts for the oracle (untimed)")
-    W1 = omoe.projection_weights(cfg, "w1", need)
-    W2 = omoe.projection_weights(cfg, "w2", need)
-    WS1 = omoe.projection_weights(cfg, "ws1") if cfg.shared else None
-    WS2 = omoe.projection_weights(cfg, "ws2") if cfg.shared else None
+    W = weights(cfg, need)
     x = synth.activations(cfg)
     n_tok, t0, reps = 0, time.perf_counter(), 0
     while True:
-        omoe.forward(cfg, x, logits, W1, W2, WS1, WS2, tokens=tokens, o=o)
+        ref = omoe.forward(cfg, x, logits, *W, tokens=tokens, o=o)
         n_tok += len(tokens)
         reps += 1
         el = time.perf_counter() - t0
         if el >= budget_s:
             break
-    return {"value": n_tok / el, "unit": "tokens/s", "cores": min(o.threads(), len(tokens)), "kind": "oracle",
-            "sample": f"{cfg.name}: {len(tokens)} tokens (routing, {'activation quantisation, ' if cfg.act != 'bf16' else ''}"
-                      f"FP64 expert MLPs of their {cfg.k} experts, combine) x {reps} repeats, {el:.1f} s; "
-                      f"weight preparation untimed"}
+    baseline = {"value": n_tok / el, "unit": "tokens/s", "cores": min(o.threads(), len(tokens)), "kind": "oracle",
+                "sample": f"{cfg.name}: {len(tokens)} tokens (routing, "
+                          f"{'activation quantisation, ' if cfg.act != 'bf16' else ''}"
+                          f"FP64 expert MLPs of their {cfg.k} experts, combine) x {reps} repeats, {el:.1f} s; "
+                          f"weight preparation untimed"}
+    checks = [_parity_check(big, ref, tokens)]
+    log(f"[bench] parity {checks[-1]}")
+    for b in [b for b in headline if b is not big] + list(extra):
+        cfg = b.cfg
+        n = PARITY_SAMPLE.get(cfg.name, 16)
+        tokens = np.arange(cfg.T, dtype=np.int32) if cfg.T <= 64 else synth.token_sample(cfg, n)
+        logits = synth.logits(cfg)
+        ids, _ = omoe.route(cfg, logits, o)
+        need = sorted(set(ids[tokens].reshape(-1).tolist()))
+        log(f"[bench] parity: oracle for {len(tokens)} tokens of {cfg.name} ({len(need)} experts)")
+        ref = omoe.forward_by_expert(cfg, synth.activations(cfg), logits, *weights(cfg, need), tokens=tokens, o=o)
+        checks.append(_parity_check(b, ref, tokens))
+        log(f"[bench] parity {checks[-1]}")
+    parity = {"status": "ok" if all(c["ok"] for c in checks) else "FAILED",
+              "bar": "routing and activation codes bit-exact; relL2 <= 5e-3; max |d| beyond the bf16 output "
+                     "rounding <= 2e-2 RMS", "checks": checks}
+    return baseline, parity
+
+
+def host_info():
+    """CPU model and thread count of this host; GPU name, clocks, power and use before timing."""
+    info = {"cpu_model": None, "cpu_threads": len(os.sched_getaffinity(0))}
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                info["cpu_model"] = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    info["gpu"] = torch.cuda.get_device_properties(0).name
+    try:
+        import subprocess
+        r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--showuse", "--showtemp", "--json"],
+                           capture_output=True, text=True, timeout=30)
+        card = next(iter(json.loads(r.stdout).values()))
+        keep = ("sclk clock speed:", "mclk clock speed:", "GPU use (%)", "Temperature (Sensor junction) (C)")
+        info["gpu_state"] = {k: v for k, v in card.items() if k in keep or "Power" in k}
+    except Exception as exc:   # the state is a record, not a requirement
+        info["gpu_state"] = f"unavailable: {type(exc).__name__}"
+    return info
 
 
 # ------------------------------------------------------------ rocprofv3 summaries
@@ -327,9 +446,12 @@ def counter_summary(csvs, title, command):
     """Per-kernel means of every counter in one or more rocprofv3 --pmc runs (values summed
     over a dispatch's instances, then averaged over the kernel's dispatches of one grid),
     plus the derived figures the dequant route is judged by: VALU instructions per MFMA,
-    MFMA-pipe busy share (SQ_VALU_MFMA_BUSY_CYCLES over 1024 SIMDs x GRBM_GUI_ACTIVE / 8
-    XCDs), the clock the kernel ran at (GRBM_GUI_ACTIVE / 8 / duration) and LDS
-    instructions per MFMA."""
+    LDS instructions per MFMA, and the MFMA-pipe busy share = SQ_VALU_MFMA_BUSY_CYCLES over
+    (1024 SIMDs x the kernel's cycles). The kernel's cycles are its duration (dispatch
+    timestamps) times its clock; the clock is GRBM_GUI_ACTIVE / 8 XCDs / duration where that
+    is at most the 2.4 GHz peak. GRBM_GUI_ACTIVE counts over a window that can outlast a
+    short kernel, so where it gives more than 2.4 GHz the clock is taken as 2.4 GHz (a lower
+    bound on the busy share) and the row is flagged."""
     import csv
     rows = {}
     for path in csvs:
@@ -357,10 +479,15 @@ def counter_summary(csvs, title, command):
         ndisp = max(len(v) for c, v in agg.items() if c != "dur")
         mf = m.get("SQ_INSTS_MFMA")
         ratio = lambda c: f"{m[c] / mf:.2f}" if mf and c in m else "-"
-        gui = m.get("GRBM_GUI_ACTIVE")
-        busy = (f"{m['SQ_VALU_MFMA_BUSY_CYCLES'] / (1024 * gui / 8):.3f}"
-                if gui and "SQ_VALU_MFMA_BUSY_CYCLES" in m else "-")
-        clk = f"{gui / 8 / m['dur']:.2f}" if gui and m.get("dur") else "-"
+        gui, dur = m.get("GRBM_GUI_ACTIVE"), m.get("dur")
+        busy = clk = "-"
+        if gui and dur:
+            ghz = gui / 8 / dur
+            capped = ghz > PEAK_SCLK_GHZ
+            cycles = dur * min(ghz, PEAK_SCLK_GHZ)
+            clk = f"{min(ghz, PEAK_SCLK_GHZ):.2f}" + (f" (GRBM window {ghz:.2f}: capped)" if capped else "")
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in m:
+                busy = f"{m['SQ_VALU_MFMA_BUSY_CYCLES'] / (1024 * cycles):.3f}" + (" (lower bound)" if capped else "")
         cs = ", ".join(f"{c.replace('SQ_', '')} {v:.4g}" for c, v in sorted(m.items()) if c != "dur")
         out.append(f"| `{n}` | {st} | {g} | {ndisp} | {cs} | {ratio('SQ_INSTS_VALU')} | {ratio('SQ_INSTS_LDS')} | "
                    f"{busy} | {clk} |")
@@ -390,7 +517,10 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="qwen3-30b-a3b-decode")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle leg (the CPU baseline and the parity gate)")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="default workload: time the decode headline only, not the prefill and skewed objects")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one 1 GiB device copy (counter calibration for --pmc runs)")
     ap.add_argument("--trace-summary", metavar="RESULTS_DB", help="summarise a rocprofv3 kernel trace and exit")
@@ -417,8 +547,14 @@ def main():
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
+    host = host_info()
     cfgs, bound = workload(args.workload)
     batches = [Batch(c, dev) for c in cfgs]
+    extras = []                                  # (object, workload name, batches, bound)
+    if args.workload == DEFAULT_WORKLOAD and not args.headline_only:
+        for kind, name in EXTRA_WORKLOADS:
+            ecfgs, ebound = workload(name)
+            extras.append((kind, name, [Batch(c, dev) for c in ecfgs], ebound))
 
     if args.copy_probe:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -427,19 +563,103 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
+    # parity first: no timing unless every batch's first run matched the oracle
+    baseline = parity = None
+    if not args.no_cpu_baseline:
+        baseline, parity = cpu_baseline_and_parity(batches, [b for _, _, bs, _ in extras for b in bs])
+        if parity["status"] != "ok":
+            print(json.dumps({"metric": METRIC, "error": "parity check against the oracle failed", "parity": parity}),
+                  flush=True)
+            sys.exit(1)
+
+    t = time_steps(batches, args.steps, args.warmup)
+    ms = t["ms"]
+    tokens = sum(c.T for c in cfgs)
+    value = tokens / (ms / 1e3)
+    per_launch = t["per_launch"]
+    gu_time = sum(v[m.MOE_STAGE_GATE_UP] for v in per_launch.values())          # ms per step
+    if bound == "hbm":
+        work = sum(b.gate_up_bytes() for b in batches)
+        achieved = work / (gu_time / 1e3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": None}
+    else:
+        work = sum(b.gate_up_flops() for b in batches)
+        achieved = work / (gu_time / 1e3) / 1e12
+        peak = mfma_peak(cfgs[0])
+        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                "frac": achieved / peak, "traffic": None}
+    roof["kernel"] = "gate_up grouped GEMM (+SwiGLU)"
+    roof["launch_ms"] = gu_time / len(batches)
+    roof["algorithmic_bytes_per_launch"] = sum(b.gate_up_bytes() for b in batches) / len(batches)
+    roof["traffic"] = traffic_record(args.workload)
+
+    layer_bytes = sum(b.layer_bytes() for b in batches)
+    layer_flops = sum(b.layer_flops() for b in batches)
+    res = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8xfp4" if cfgs[0].act == "mxfp8" else "bf16", "data": "synthetic",
+        "config": {"workload": args.workload, "T": [c.T for c in cfgs], "H": cfgs[0].H, "I": cfgs[0].I,
+                   "E": cfgs[0].E, "top_k": cfgs[0].k, "score": cfgs[0].score, "shared": cfgs[0].shared,
+                   "activations": cfgs[0].act,
+                   "weights": ("mxfp4 e2m1 + e8m0/32" if cfgs[0].wfmt == "mxfp4"
+                               else "nvfp4 e2m1 + e4m3/16 + fp32 per expert")},
+        "launch": "hip graph replay of the step (eager: %.4f ms/step)" % t["eager_ms"],
+        "eager_ms_per_step": t["eager_ms"],
+        "step_ms_median": float(np.median(t["samples"])),
+        "step_ms_iqr": [float(np.percentile(t["samples"], 25)), float(np.percentile(t["samples"], 75))],
+        "step_ms_samples": [round(v, 5) for v in t["samples"]],
+        "layer_GBps": layer_bytes / (ms / 1e3) / 1e9,
+        "layer_hbm_frac": layer_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+        "layer_TFLOPs": layer_flops / (ms / 1e3) / 1e12,
+        "roofline": roof,
+        "per_batch": {b.cfg.name: batch_record(b, per_launch[b.cfg.name]) for b in batches},
+    }
+    for kind, name, bs, eb in extras:
+        log(f"[bench] timing {name}")
+        res.setdefault(kind, {})[name] = workload_record(bs, time_steps(bs, args.steps, args.warmup), eb)
+    if parity is not None:
+        res["parity"] = parity
+    res["host"] = host
+    if baseline is not None:
+        res["cpu_baseline"] = baseline
+    print(json.dumps(res), flush=True)
+
+
+DEFAULT_WORKLOAD = "qwen3-30b-a3b-decode"
+PRIME_S = 1.0       # untimed seconds of steps before a workload's warmup steps
+# measured beside the decode headline in the default run: the prefill configurations (MFMA
+# bound) and the skewed W4A4 layer (mixed)
+EXTRA_WORKLOADS = (("prefill", "qwen3-30b-a3b-prefill"), ("prefill", "deepseek-v3"), ("skewed", "skewed-w4a4"))
+
+
+def mfma_peak(cfg):
+    return FP8_PEAK_TFLOPS if cfg.act == "mxfp8" else BF16_PEAK_TFLOPS
+
+
+def time_steps(batches, steps, warmup):
+    """Eager and HIP-graph timing of one step (every batch once), the per-step distribution
+    of further replays, and each stage's kernel time per launch from moe_run_timed's events."""
     def step():
         for b in batches:
             b.run()
 
-    # eager launches
-    for _ in range(args.warmup):
+    # bring the GPU out of its idle clocks (the oracle leg before this keeps it idle for tens
+    # of seconds): the step runs untimed for PRIME_S seconds before the warmup steps
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < PRIME_S:
+        for _ in range(8):
+            step()
+        torch.cuda.synchronize()
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for _ in range(steps):
         step()
     torch.cuda.synchronize()
-    eager_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    eager_ms = (time.perf_counter() - t0) * 1e3 / steps
 
     # the same step captured once in a HIP graph and replayed (fixed pointers; the layer
     # enqueues no memset and never synchronises, so it is capturable as is)
@@ -451,29 +671,24 @@ def main():
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         step()
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         graph.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for _ in range(steps):
         graph.replay()
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms = (t1 - t0) * 1e3 / args.steps
-    tokens = sum(c.T for c in cfgs)
-    value = tokens / (ms / 1e3)
-    # the per-step distribution: K more replays, each between two events on the replay stream
-    step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.steps)]
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for e0, e1 in step_ev:
         e0.record()
         graph.replay()
         e1.record()
     torch.cuda.synchronize()
-    step_samples = [e0.elapsed_time(e1) for e0, e1 in step_ev]
+    samples = [e0.elapsed_time(e1) for e0, e1 in step_ev]
+    del graph
 
-    # dominant kernel: gate/up GEMM, timed by HIP events recorded on its launch stream
-    # (moe_run_timed records them around each stage on the stream moe_run uses)
+    # stage times: HIP events recorded by moe_run_timed on the stream the layer launches on
     stage_tot = {b.cfg.name: [0.0] * m.MOE_NUM_STAGES for b in batches}
     all_ev = {b.cfg.name: [torch.cuda.Event(enable_timing=True) for _ in range(2 * m.MOE_NUM_STAGES)]
               for b in batches}
@@ -481,70 +696,65 @@ def main():
         for e in ev:
             e.record()
     torch.cuda.synchronize()
-    for _ in range(args.steps):
+    for _ in range(steps):
         for b in batches:
-            ev = all_ev[b.cfg.name]
-            b.run_timed([e.cuda_event for e in ev])
+            b.run_timed([e.cuda_event for e in all_ev[b.cfg.name]])
         torch.cuda.synchronize()
         for b in batches:
             ev = all_ev[b.cfg.name]
             for s in range(m.MOE_NUM_STAGES):
                 stage_tot[b.cfg.name][s] += ev[2 * s].elapsed_time(ev[2 * s + 1])
-    per_launch = {n: [t / args.steps for t in v] for n, v in stage_tot.items()}
-    gu_time = sum(v[m.MOE_STAGE_GATE_UP] for v in per_launch.values())          # ms per step
-    if bound == "hbm":
-        work = sum(b.gate_up_bytes() for b in batches)
-        achieved = work / (gu_time / 1e3) / 1e9
-        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS, "traffic": None}
-    else:
-        work = sum(b.gate_up_flops() for b in batches)
-        achieved = work / (gu_time / 1e3) / 1e12
-        peak = FP8_PEAK_TFLOPS if cfgs[0].act == "mxfp8" else BF16_PEAK_TFLOPS
-        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                "frac": achieved / peak, "traffic": None}
-    roof["kernel"] = "gate_up grouped GEMM (+SwiGLU)"
-    roof["launch_ms"] = gu_time / len(batches)
-    roof["algorithmic_bytes_per_launch"] = sum(b.gate_up_bytes() for b in batches) / len(batches)
-    roof["traffic"] = traffic_record(args.workload)
+    per_launch = {n: [v / steps for v in tot] for n, tot in stage_tot.items()}
+    return {"eager_ms": eager_ms, "ms": ms, "samples": samples, "per_launch": per_launch}
 
-    layer_bytes = sum(b.layer_bytes() for b in batches)
-    layer_flops = sum(b.layer_flops() for b in batches)
-    detail = {}
-    for b in batches:
-        st = per_launch[b.cfg.name]
-        detail[b.cfg.name] = {
-            "T": b.cfg.T, "touched_experts": b.touched,
-            "stage_ms": {m.STAGE_NAMES[s]: round(st[s], 5) for s in range(m.MOE_NUM_STAGES)},
-            "expert_rows": b.expert_rows,
-            "useful_weight_bytes": (b.touched + b.cfg.shared) * (b.weight_bytes(2 * b.cfg.I * b.cfg.H)
-                                                                 + b.weight_bytes(b.cfg.H * b.cfg.I)),
-            "gate_up_GBps": b.gate_up_bytes() / (st[m.MOE_STAGE_GATE_UP] / 1e3) / 1e9,
-            "gate_up_TFLOPs": b.gate_up_flops() / (st[m.MOE_STAGE_GATE_UP] / 1e3) / 1e12,
-        }
 
-    res = {
-        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "fp8xfp4" if cfgs[0].act == "mxfp8" else "bf16", "data": "synthetic",
-        "config": {"workload": args.workload, "T": [c.T for c in cfgs], "H": cfgs[0].H, "I": cfgs[0].I,
-                   "E": cfgs[0].E, "top_k": cfgs[0].k, "score": cfgs[0].score, "shared": cfgs[0].shared,
-                   "activations": cfgs[0].act,
-                   "weights": ("mxfp4 e2m1 + e8m0/32" if cfgs[0].wfmt == "mxfp4"
-                               else "nvfp4 e2m1 + e4m3/16 + fp32 per expert")},
-        "launch": "hip graph replay of the step (eager: %.4f ms/step)" % eager_ms,
-        "eager_ms_per_step": eager_ms,
-        "step_ms_median": float(np.median(step_samples)),
-        "step_ms_iqr": [float(np.percentile(step_samples, 25)), float(np.percentile(step_samples, 75))],
-        "step_ms_samples": [round(v, 5) for v in step_samples],
-        "layer_GBps": layer_bytes / (ms / 1e3) / 1e9,
-        "layer_TFLOPs": layer_flops / (ms / 1e3) / 1e12,
-        "roofline": roof,
-        "per_batch": detail,
+def batch_record(b, st):
+    """Per-batch detail: stage times, rows per expert, the GEMMs' rates against their roofs."""
+    c = b.cfg
+    gu, dn = st[m.MOE_STAGE_GATE_UP], st[m.MOE_STAGE_DOWN]
+    peak = mfma_peak(c)
+    return {
+        "T": c.T, "touched_experts": b.touched,
+        "stage_ms": {m.STAGE_NAMES[s]: round(st[s], 5) for s in range(m.MOE_NUM_STAGES)},
+        "expert_rows": b.expert_rows if len(b.expert_rows) <= 128 else b.expert_rows[:16] + ["..."],
+        "useful_weight_bytes": (b.touched + c.shared) * (b.weight_bytes(2 * c.I * c.H) + b.weight_bytes(c.H * c.I)),
+        "gate_up_GBps": b.gate_up_bytes() / (gu / 1e3) / 1e9,
+        "gate_up_hbm_frac": b.gate_up_bytes() / (gu / 1e3) / 1e9 / HBM_PEAK_GBS,
+        "gate_up_TFLOPs": b.gate_up_flops() / (gu / 1e3) / 1e12,
+        "gate_up_mfma_frac": b.gate_up_flops() / (gu / 1e3) / 1e12 / peak,
+        "down_GBps": b.down_bytes() / (dn / 1e3) / 1e9,
+        "down_hbm_frac": b.down_bytes() / (dn / 1e3) / 1e9 / HBM_PEAK_GBS,
+        "down_TFLOPs": b.down_flops() / (dn / 1e3) / 1e12,
+        "down_mfma_frac": b.down_flops() / (dn / 1e3) / 1e12 / peak,
     }
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(cfgs)
-    print(json.dumps(res), flush=True)
+
+
+def workload_record(batches, t, bound):
+    """One extra workload of the default run: step time and rates, the layer's and each
+    grouped GEMM's fraction of the MFMA peak (and of HBM bandwidth), per-batch detail."""
+    ms = t["ms"]
+    c = batches[0].cfg
+    peak = mfma_peak(c)
+    flops = sum(b.layer_flops() for b in batches)
+    nbytes = sum(b.layer_bytes() for b in batches)
+    gu = sum(v[m.MOE_STAGE_GATE_UP] for v in t["per_launch"].values())
+    dn = sum(v[m.MOE_STAGE_DOWN] for v in t["per_launch"].values())
+    gu_f, dn_f = sum(b.gate_up_flops() for b in batches), sum(b.down_flops() for b in batches)
+    gu_b, dn_b = sum(b.gate_up_bytes() for b in batches), sum(b.down_bytes() for b in batches)
+    return {
+        "bound": bound, "T": [b.cfg.T for b in batches], "H": c.H, "I": c.I, "E": c.E, "top_k": c.k,
+        "shared": c.shared, "activations": c.act,
+        "ms_per_step": ms, "eager_ms_per_step": t["eager_ms"], "step_ms_median": float(np.median(t["samples"])),
+        "tokens_per_s": sum(b.cfg.T for b in batches) / (ms / 1e3),
+        "layer_TFLOPs": flops / (ms / 1e3) / 1e12, "layer_mfma_frac": flops / (ms / 1e3) / 1e12 / peak,
+        "layer_GBps": nbytes / (ms / 1e3) / 1e9, "layer_hbm_frac": nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+        "mfma_peak_TFLOPs": peak,
+        "gate_up": {"ms": gu, "TFLOPs": gu_f / (gu / 1e3) / 1e12, "mfma_frac": gu_f / (gu / 1e3) / 1e12 / peak,
+                    "GBps": gu_b / (gu / 1e3) / 1e9, "hbm_frac": gu_b / (gu / 1e3) / 1e9 / HBM_PEAK_GBS},
+        "down": {"ms": dn, "TFLOPs": dn_f / (dn / 1e3) / 1e12, "mfma_frac": dn_f / (dn / 1e3) / 1e12 / peak,
+                 "GBps": dn_b / (dn / 1e3) / 1e9, "hbm_frac": dn_b / (dn / 1e3) / 1e9 / HBM_PEAK_GBS},
+        "per_batch": {b.cfg.name: batch_record(b, t["per_launch"][b.cfg.name]) for b in batches},
+    }
 
 
 if __name__ == "__main__":
