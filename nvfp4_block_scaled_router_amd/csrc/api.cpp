@@ -462,6 +462,7 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
   g1.out = (uint16_t*)(ws + plan->ws_h);
   g1.hexp = (int8_t*)(ws + plan->ws_hexp);
   g1.hmin = decode ? nullptr : pa.hmin;
+  g1.h_natural = decode ? 0 : 1;                 // prefill: plain column order, rescaled before down
   // MXFP8 h: quantised in the decode GEMM's epilogue (a workgroup holds whole 32-column
   // blocks), or written as fp32 by the prefill GEMM and quantised by a row kernel
   g1.hf = fp4h || (mx8 && !decode) ? (float*)(ws + plan->ws_hf) : nullptr;
@@ -476,6 +477,7 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
   auto second = [&](GemmArgs g) {
     g.tile_first = pa.tile_count;
     g.tile_count = pa.tile_count + 1;
+    g.h_natural = 0;                             // the decode GEMMs keep h16 permuted
     return g;
   };
   {
@@ -520,6 +522,11 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
         first.start = nullptr;
         e = launch_mxfp8_rows_f32(g1.hf, T * k + S * T, I, ws + plan->ws_hq, ws + plan->ws_hs, s);
       }
+    } else if (!decode) {   // h16 rows of the first tile list to their row's common exponent
+      if ((e = mark(ev, 2 * MOE_STAGE_DOWN, s)) != hipSuccess) return (int)e;
+      first.start = nullptr;
+      e = launch_h_rescale(g1.out, g1.hexp, pa.hmin, pa.tile_group, pa.tile_row0, pa.tile_count, pa.offsets,
+                           max_tiles, M, I, s);
     }
     if (e == hipSuccess) e = launch_gemm(dn_mode, regime, max_tiles, est_tiles, g2, s, first);
     if (e == hipSuccess && split)

@@ -132,7 +132,8 @@ __device__ __forceinline__ void epilogue_pair(const GemmArgs& a, const f32x4& ga
                                               int row, int hs, float lim) {
   const int lg = (threadIdx.x & (WAVE - 1)) >> 4;
   const int NO = a.N / 2;
-  const size_t off = (size_t)row * NO + h_pos(hs * 16 + 4 * lg);   // 4 columns stay contiguous
+  const int col = hs * 16 + 4 * lg;
+  const size_t off = (size_t)row * NO + (a.h_natural ? col : h_pos(col));   // 4 columns stay contiguous
   auto act = [&](float g, float u) {
     return silu_mul(fminf(g * sc, lim), fminf(fmaxf(u * sc, -lim), lim));
   };
@@ -428,14 +429,15 @@ __device__ __forceinline__ int lds_swz(int r) {
 // values, 16-byte piece c of row r at slot c ^ lds_swz(r)), shared by the waves; each
 // wave streams its own weight tiles straight into registers (two alternating register
 // sets, one chunk ahead) and dequantises them there. Token tiles arrive by
-//  - LDS DMA (fp16 activations, GATEUP_F16): global_load_lds_dwordx4 straight into an
-//    NBUF-deep ring of stages, no staging registers, chunk kc + NBUF - 1 in flight while
-//    chunk kc is consumed. One DMA instruction writes 64 consecutive 16-byte slots (lane i
-//    -> slot i), so the swizzle is applied on the global side: the lane that fills slot
-//    (r, c) fetches piece c ^ lds_swz(r) of row r;
-//  - registers (NVFP4 activations, GATEUP_FP4; h16, DOWN), converted on the way in: E2M1
-//    codes x E4M3 block scale -> fp16, or h16 x 2^(P - hexp) -> the row's common scale 2^P;
-//    two stages, chunk kc + 1 loaded while chunk kc is consumed.
+//  - LDS DMA (fp16 rows: the rescaled activations of GATEUP_F16 gathered through the
+//    row -> token map, or DOWN's own h16 rows, already at each row's common scale 2^P):
+//    global_load_lds_dwordx4 straight into an NBUF-deep ring of stages, no staging
+//    registers, chunk kc + NBUF - 1 in flight while chunk kc is consumed. One DMA instruction
+//    writes 64 consecutive 16-byte slots (lane i -> slot i), so the swizzle is applied on the
+//    global side: the lane that fills slot (r, c) fetches piece c ^ lds_swz(r) of row r;
+//  - registers (NVFP4 activations, GATEUP_FP4 and DOWN_FP4), converted on the way in: E2M1
+//    codes x E4M3 block scale -> fp16; two stages, chunk kc + 1 loaded while chunk kc is
+//    consumed.
 // Issue order inside a chunk is pinned with scheduling barriers (the wait counts rely on it).
 __device__ __forceinline__ void dma16(const void* src, const void* lds_dst) {
   __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
@@ -443,6 +445,42 @@ __device__ __forceinline__ void dma16(const void* src, const void* lds_dst) {
 }
 
 template <int V> struct IntC { static constexpr int value = V; };
+
+// The K loop of the three-stage pipelines: step(kc, set kc % 3, kind) for kc = 0 .. KC - 1, the
+// set and the kind as compile-time constants. Every chunk but the last two issues the loads of
+// chunk kc + 2 (STEP_FULL); chunk KC - 2 issues nothing and may leave chunk KC - 1's loads in
+// flight (STEP_NEXT_TO_LAST); chunk KC - 1 waits for everything (STEP_LAST). The steady state
+// runs in groups of three with no branch; the remaining 1 to 4 chunks are spelled out.
+constexpr int STEP_FULL = 0, STEP_NEXT_TO_LAST = 1, STEP_LAST = 2;
+template <typename F>
+__device__ __forceinline__ void run_chunks(int KC, F&& step) {
+  int kc = 0;
+  for (; kc + 5 <= KC; kc += 3) {
+    step(kc, IntC<0>(), IntC<STEP_FULL>());
+    step(kc + 1, IntC<1>(), IntC<STEP_FULL>());
+    step(kc + 2, IntC<2>(), IntC<STEP_FULL>());
+  }
+  switch (KC - kc) {   // kc is a multiple of 3 here
+    case 4:
+      step(kc, IntC<0>(), IntC<STEP_FULL>());
+      step(kc + 1, IntC<1>(), IntC<STEP_FULL>());
+      step(kc + 2, IntC<2>(), IntC<STEP_NEXT_TO_LAST>());
+      step(kc + 3, IntC<0>(), IntC<STEP_LAST>());
+      break;
+    case 3:
+      step(kc, IntC<0>(), IntC<STEP_FULL>());
+      step(kc + 1, IntC<1>(), IntC<STEP_NEXT_TO_LAST>());
+      step(kc + 2, IntC<2>(), IntC<STEP_LAST>());
+      break;
+    case 2:
+      step(kc, IntC<0>(), IntC<STEP_NEXT_TO_LAST>());
+      step(kc + 1, IntC<1>(), IntC<STEP_LAST>());
+      break;
+    default:
+      step(kc, IntC<0>(), IntC<STEP_LAST>());
+      break;
+  }
+}
 
 // s_waitcnt immediate: vmcnt(vm) lgkmcnt(lgkm), expcnt not waited.
 constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8); }
@@ -452,17 +490,17 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void gemm_prefill_kernel(GemmArgs 
   static_assert(MODE == GEMM_GATEUP_F16 || MODE == GEMM_GATEUP_FP4 || MODE == GEMM_DOWN || MODE == GEMM_DOWN_FP4,
                 "prefill modes");
   constexpr bool FP4A = MODE == GEMM_GATEUP_FP4 || MODE == GEMM_DOWN_FP4;   // NVFP4 activation rows
+  constexpr bool DOWNM = MODE == GEMM_DOWN || MODE == GEMM_DOWN_FP4;        // rows addressed directly
   static_assert(WAVES == 4 || WAVES == 8, "4 or 8 waves");
-  constexpr bool DMA = MODE == GEMM_GATEUP_F16;
+  constexpr bool DMA = !FP4A;                         // fp16 token rows: x16 (gate_up) or rescaled h16 (down)
   static_assert(!DMA || NBUF == 2 || NBUF == 3, "LDS ring depth");
   constexpr int NST = DMA ? NBUF : 2;                 // LDS stages
   constexpr int M = TSUB * 16;
   constexpr int STAGE = M * 16;                       // 16-byte slots per stage
   constexpr int NT = 64 * WAVES;                      // threads
   constexpr int D = STAGE / NT;                       // DMA instructions per lane per chunk
-  // register staging: DOWN moves 16-byte h16 pieces (D per thread), FP4 moves 16-column
-  // pieces (8 code bytes + 1 scale byte, D/2 per thread)
-  constexpr int NPC = MODE == GEMM_DOWN ? D : D / 2;
+  // register staging (FP4): 16-column pieces (8 code bytes + 1 scale byte), D/2 per thread
+  constexpr int NPC = D / 2;
   static_assert(D >= 2 && STAGE % NT == 0, "tile size");
   static_assert(!FP4A || D % 2 == 0, "NVFP4 pieces pair up");
   __shared__ u32x4 tile[NST * STAGE];
@@ -480,77 +518,63 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void gemm_prefill_kernel(GemmArgs 
   const int q0 = (item.nb * WAVES + wave) * NSUB;         // the launch covers N exactly
   const int nvalid = min(M, a.offsets[g + 1] - row0);
 
-  // ---- token-tile staging
+  // ---- token-tile staging. Byte offsets are 32-bit: gather modes address token rows from the
+  // activation base (T K 2 < 2^32 bytes), the down modes their own rows from the tile's first
+  // row (64-bit base; offsets within the tile).
   // DMA: instruction i of this wave fills slots (WAVES i + wave) * 64 .. +63: row
   // r = 4 (WAVES i + wave) + lane / 16, slot column lane % 16; byte offsets from the chunk base.
   uint32_t src_off[DMA ? D : 1];
-  // registers: piece i of this thread is piece (threadIdx.x + NT i) of the tile, in row
-  // r0 + (NT/16) i (DOWN) or r0 + (NT/8) i (FP4): the same r % 16 for every i, so one slot
-  // base (+ NT i or 2 NT i) serves all; sources as 32-bit offsets from the chunk-0 base
-  uint32_t poff[DMA || MODE == GEMM_DOWN ? 1 : NPC];     // FP4: bytes into xq
-  int phm[MODE == GEMM_DOWN ? NPC : 1];                   // DOWN: the row's common exponent P
-  const int pcol = MODE == GEMM_DOWN ? (int)(threadIdx.x & 15) : (int)(threadIdx.x & 7);
-  const int r0 = MODE == GEMM_DOWN ? (int)(threadIdx.x >> 4) : (int)(threadIdx.x >> 3);
+  // registers (FP4): piece i of this thread is piece (threadIdx.x + NT i) of the tile, in row
+  // r0 + (NT/8) i: the same r % 16 for every i, so one slot base (+ 2 NT i) serves all
+  uint32_t poff[DMA ? 1 : NPC];                          // FP4: bytes into xq from qbase
+  const int pcol = (int)(threadIdx.x & 7);
+  const int r0 = (int)(threadIdx.x >> 3);
   const int swz0 = lds_swz(r0);
-  // DOWN: stored piece pcol of a chunk holds k-piece h_piece(pcol), of h block 8 kc + kp / 2
+  const char* xbase = (const char*)a.x + (MODE == GEMM_DOWN ? (size_t)row0 * L.K * 2 : 0);
+  const uint8_t* qbase = a.xq + (MODE == GEMM_DOWN_FP4 ? (size_t)row0 * (L.K / 2) : 0);
+  const uint8_t* sbase = a.xs + (MODE == GEMM_DOWN_FP4 ? (size_t)row0 * (L.K / 16) : 0);
   if constexpr (DMA) {
 #pragma unroll
     for (int i = 0; i < D; ++i) {
       const int r = 4 * (WAVES * i + wave) + lg;
-      const int rr = row0 + min(r, nvalid - 1);          // rows past the group repeat its last row
+      const int rl = min(r, nvalid - 1);                 // rows past the group repeat its last row
       const int kp = l16 ^ lds_swz(r);                   // k-order piece this slot holds
-      src_off[i] = ((uint32_t)a.tok[rr] * L.K + kp * 8) * 2;
+      const uint32_t src = DOWNM ? (uint32_t)rl : (uint32_t)a.tok[row0 + rl];
+      src_off[i] = (src * (uint32_t)L.K + kp * 8) * 2;
     }
   } else {
 #pragma unroll
     for (int i = 0; i < NPC; ++i) {
-      const int r = r0 + (MODE == GEMM_DOWN ? NT / 16 : NT / 8) * i;
-      const int rr = row0 + min(r, nvalid - 1);
-      if constexpr (MODE == GEMM_DOWN) {
-        phm[i] = a.hmin[rr];                             // prefill: gate_up kept the row minimum
-      } else {
-        // its scale byte: poff / 8 into xs; gate_up gathers token rows, down reads its own rows
-        poff[i] = (uint32_t)(MODE == GEMM_DOWN_FP4 ? rr : a.tok[rr]) * (L.K / 2) + pcol * 8;
-      }
+      const int rl = min(r0 + (NT / 8) * i, nvalid - 1);
+      // its scale byte: poff / 8 into xs; gate_up gathers token rows, down reads its own rows
+      poff[i] = (uint32_t)(DOWNM ? rl : a.tok[row0 + rl]) * (L.K / 2) + pcol * 8;
     }
   }
-  const int slot0 = MODE == GEMM_DOWN ? r0 * 16 + (h_piece(pcol) ^ swz0) : r0 * 16;
+  const int slot0 = r0 * 16;
   auto dma = [&](int kc, int st) {
-    const char* base = (const char*)a.x + (size_t)kc * (KCHUNK * 2);
+    const char* base = xbase + (size_t)kc * (KCHUNK * 2);
 #pragma unroll
     for (int i = 0; i < D; ++i) dma16(base + src_off[i], &tile[st * STAGE + (WAVES * i + wave) * 64]);
   };
-  u32x4 sv[DMA ? 1 : NPC];      // staged pieces (DOWN: 8 h16; FP4: codes in .x .y)
-  uint32_t se[DMA ? 1 : NPC];   // DOWN: block exponent byte; FP4: scale byte
-  const int kp_blk = h_piece(pcol) >> 1;
+  u32x4 sv[DMA ? 1 : NPC];      // staged pieces (FP4: codes in .x .y)
+  uint32_t se[DMA ? 1 : NPC];   // FP4: scale byte
   auto stage_load = [&](int kc) {
 #pragma unroll
     for (int i = 0; i < NPC; ++i) {
-      if constexpr (MODE == GEMM_DOWN) {   // row offsets recomputed per chunk: fewer live registers
-        const uint32_t rr = row0 + min(r0 + (NT / 16) * i, nvalid - 1);
-        sv[i] = *(const u32x4*)((const char*)a.x + (size_t)kc * (KCHUNK * 2) + (rr * L.K + pcol * 8) * 2);
-        se[i] = *(const uint8_t*)((const uint8_t*)a.hexp + kc * 8 + rr * (L.K / 16) + kp_blk);
-      } else {
-        const u32x2 q = *(const u32x2*)(a.xq + (size_t)kc * 64 + poff[i]);
-        sv[i] = u32x4{q.x, q.y, 0u, 0u};
-        se[i] = a.xs[(size_t)kc * 8 + poff[i] / 8];
-      }
+      const u32x2 q = *(const u32x2*)(qbase + (size_t)kc * 64 + poff[i]);
+      sv[i] = u32x4{q.x, q.y, 0u, 0u};
+      se[i] = sbase[(size_t)kc * 8 + poff[i] / 8];
     }
   };
   auto stage_store = [&](int st) {
 #pragma unroll
     for (int i = 0; i < NPC; ++i) {
-      if constexpr (MODE == GEMM_DOWN) {
-        const _Float16 f = h_factor(phm[i] - (int)(int8_t)se[i]);
-        tile[st * STAGE + slot0 + NT * i] = __builtin_bit_cast(u32x4, __builtin_bit_cast(f16x8, sv[i]) * f);
-      } else {
-        const f16x2 s1 = e4m3x2_to_f16x2(se[i]);
-        const f16x2 s2 = {s1.x, s1.x};
-        const f16x8 lo = dequant8_f16(sv[i].x, s2), hi = dequant8_f16(sv[i].y, s2);
-        const int c = 2 * pcol;
-        tile[st * STAGE + slot0 + 2 * NT * i + (c ^ swz0)] = __builtin_bit_cast(u32x4, lo);
-        tile[st * STAGE + slot0 + 2 * NT * i + ((c + 1) ^ swz0)] = __builtin_bit_cast(u32x4, hi);
-      }
+      const f16x2 s1 = e4m3x2_to_f16x2(se[i]);
+      const f16x2 s2 = {s1.x, s1.x};
+      const f16x8 lo = dequant8_f16(sv[i].x, s2), hi = dequant8_f16(sv[i].y, s2);
+      const int c = 2 * pcol;
+      tile[st * STAGE + slot0 + 2 * NT * i + (c ^ swz0)] = __builtin_bit_cast(u32x4, lo);
+      tile[st * STAGE + slot0 + 2 * NT * i + ((c + 1) ^ swz0)] = __builtin_bit_cast(u32x4, hi);
     }
   };
 
@@ -586,32 +610,6 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void gemm_prefill_kernel(GemmArgs 
 #pragma unroll
       for (int t = 0; t < TV; ++t) acc[s][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // Weights: two raw register sets (rA/rB, chunk parity). With PIPE (NVFP4 activations),
-    // also two dequantised sets (WA/WB): chunk kc + 2's raw weights are fetched at the start
-    // of chunk kc and chunk kc + 1's are dequantised in the middle of chunk kc, between its
-    // MFMAs, so the VALU work of the dequant runs beside the MFMA pipe instead of ahead of
-    // it. Without PIPE, chunk kc + 1's raw weights are fetched at the start of chunk kc and
-    // chunk kc's are dequantised right before its MFMAs: down has no registers left for a
-    // second set, and the fp16 gate_up measured slower pipelined (its second workgroup on
-    // the CU already fills the MFMA pipe during the dequant).
-    constexpr bool PIPE = FP4A;
-    u32x4 rA[NSUB], rB[NSUB];
-    uint32_t sA[NSUB], sB[NSUB];
-    WOps<true> WA[NSUB], WB[PIPE ? NSUB : 1];
-    load_w(0, rA, sA);
-    if constexpr (PIPE) {
-      load_w(min(1, L.KC - 1), rB, sB);
-#pragma unroll
-      for (int s = 0; s < NSUB; ++s) WA[s].make(rA[s], sA[s]);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (DMA) {
-#pragma unroll
-      for (int c = 0; c < NBUF - 1; ++c) dma(min(c, L.KC - 1), c);
-    } else {
-      stage_load(0);
-    }
-
     auto mma = [&](int kc, int j, const WOps<true> (&W)[NSUB]) {
       const u32x4* T0 = &tile[(kc % NST) * STAGE];
       const int c = (lg * 4 + j) ^ lds_swz(l16);
@@ -623,37 +621,33 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void gemm_prefill_kernel(GemmArgs 
 #pragma unroll
         for (int t = 0; t < TV; ++t) acc[s][t] = mfma_any(W[s].v[j], bop[t], acc[s][t]);
     };
-    // DMA chunk kc: wait for chunk kc in LDS (older loads complete, the newest NBUF - 2
-    // chunks may stay in flight), barrier, issue the raw weights ahead and the DMA of
-    // kc + NBUF - 1 (both clamped to the last chunk near the end, so every chunk issues the
-    // same loads and one wait count fits all), consume chunk kc.
-    // Register chunk kc: store the staged chunk kc (its loads were issued one chunk
-    // earlier), issue the loads of chunk kc + 1 and the raw weights ahead, barrier,
-    // consume chunk kc. Register roles alternate with the chunk parity (no copies, which
-    // would wait for loads in flight).
-    auto sync = [&](int kc, int kw, u32x4 (&rf)[NSUB], uint32_t (&sf)[NSUB]) {
-      if constexpr (DMA) {
-        __builtin_amdgcn_s_waitcnt(waitcnt_imm(D * (NBUF - 2), 0));
-        __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-        load_w(min(kw, L.KC - 1), rf, sf);
-        __builtin_amdgcn_sched_barrier(0);
-        dma(min(kc + NBUF - 1, L.KC - 1), (kc + NBUF - 1) % NBUF);
-        __builtin_amdgcn_sched_barrier(0);
-      } else {
+    if constexpr (!DMA) {
+      // NVFP4 activations (register-staged tiles). Weights: two raw register sets (rA/rB,
+      // chunk parity) and two dequantised sets (WA/WB): chunk kc + 2's raw weights are
+      // fetched at the start of chunk kc and chunk kc + 1's are dequantised in the middle of
+      // chunk kc, between its MFMAs, so the VALU work of the dequant runs beside the MFMA pipe
+      // instead of ahead of it. Chunk kc: store the staged chunk kc (its loads were issued one
+      // chunk earlier), issue the loads of chunk kc + 1 and the raw weights ahead, barrier,
+      // consume chunk kc. Register roles alternate with the chunk parity (no copies, which
+      // would wait for loads in flight).
+      u32x4 rA[NSUB], rB[NSUB];
+      uint32_t sA[NSUB], sB[NSUB];
+      WOps<true> WA[NSUB], WB[NSUB];
+      load_w(0, rA, sA);
+      load_w(min(1, L.KC - 1), rB, sB);
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s) WA[s].make(rA[s], sA[s]);
+      __builtin_amdgcn_sched_barrier(0);
+      stage_load(0);
+      auto step = [&](int kc, const WOps<true> (&Wc)[NSUB], WOps<true> (&Wn)[NSUB], const u32x4 (&rn)[NSUB],
+                      const uint32_t (&sn)[NSUB], u32x4 (&rf)[NSUB], uint32_t (&sf)[NSUB]) {
         stage_store(kc & 1);
         __builtin_amdgcn_sched_barrier(0);
         stage_load(min(kc + 1, L.KC - 1));
-        load_w(min(kw, L.KC - 1), rf, sf);
+        load_w(min(kc + 2, L.KC - 1), rf, sf);
         __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));      // this thread's LDS stores done
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
-      }
-    };
-    if constexpr (PIPE) {
-      auto step = [&](int kc, const WOps<true> (&Wc)[NSUB], WOps<true> (&Wn)[NSUB], const u32x4 (&rn)[NSUB],
-                      const uint32_t (&sn)[NSUB], u32x4 (&rf)[NSUB], uint32_t (&sf)[NSUB]) {
-        sync(kc, kc + 2, rf, sf);
         mma(kc, 0, Wc);
         mma(kc, 1, Wc);
 #pragma unroll
@@ -675,13 +669,35 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void gemm_prefill_kernel(GemmArgs 
         }
       }
     } else {
+      // fp16 rows by LDS DMA into an NBUF-deep ring; raw weights one chunk ahead in two
+      // register sets (chunk parity), dequantised right before the chunk's MFMAs. Chunk kc:
+      // wait for chunk kc in LDS and its weights (older loads complete, the newest NBUF - 2
+      // chunks' DMA may stay in flight), barrier, issue the raw weights of kc + 1 and the DMA
+      // of kc + NBUF - 1 (both clamped to the last chunk near the end, so every chunk issues
+      // the same loads and one wait count fits all; the clamped loads at the end feed no later
+      // wait), consume chunk kc. Issue order is pinned with scheduling barriers: the wait count
+      // covers the LDS stages written by DMA, which the compiler does not track.
+      u32x4 rA[NSUB], rB[NSUB];
+      uint32_t sA[NSUB], sB[NSUB];
+      WOps<true> W[NSUB];
+      load_w(0, rA, sA);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int c = 0; c < NBUF - 1; ++c) dma(min(c, L.KC - 1), c);
+      __builtin_amdgcn_sched_barrier(0);
       auto step = [&](int kc, const u32x4 (&rc)[NSUB], const uint32_t (&sc)[NSUB], u32x4 (&rf)[NSUB],
                       uint32_t (&sf)[NSUB]) {
-        sync(kc, kc + 1, rf, sf);
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(D * (NBUF - 2), 0));
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        load_w(min(kc + 1, L.KC - 1), rf, sf);
+        __builtin_amdgcn_sched_barrier(0);
+        dma(min(kc + NBUF - 1, L.KC - 1), (kc + NBUF - 1) % NBUF);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int s = 0; s < NSUB; ++s) WA[s].make(rc[s], sc[s] >> ((kc & 1) * 16));
+        for (int s = 0; s < NSUB; ++s) W[s].make(rc[s], sc[s] >> ((kc & 1) * 16));
 #pragma unroll
-        for (int j = 0; j < 4; ++j) mma(kc, j, WA);
+        for (int j = 0; j < 4; ++j) mma(kc, j, W);
       };
       if (L.KC & 1) {
         step(0, rA, sA, rB, sB);
@@ -696,7 +712,7 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void gemm_prefill_kernel(GemmArgs 
         }
       }
     }
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));   // the clamped tail loads land before the workgroup exits
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));   // every load in flight lands before the workgroup exits
 
     const float wgs = a.wgs[g];
 #pragma unroll
@@ -704,7 +720,7 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void gemm_prefill_kernel(GemmArgs 
       const int rr = t * 16 + l16;
       if (rr >= nvalid) continue;
       const int orow = row0 + rr;
-      if (MODE == GEMM_DOWN || MODE == GEMM_DOWN_FP4) {
+      if (DOWNM) {
         const float scl = MODE == GEMM_DOWN ? __builtin_ldexpf(wgs, -a.hmin[orow]) : wgs * a.xg[orow];
 #pragma unroll
         for (int s = 0; s < NSUB; ++s) epilogue_single(a, acc[s][t], scl, orow, q0 + s);
@@ -782,10 +798,15 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void gemm_prefill_mx8_kernel(GemmA
   const int l16 = lane & 15, lg = lane >> 4;
   const int q0 = (item.nb * WAVES + wave) * NSUB;
   const int nvalid = min(M, a.offsets[g + 1] - row0);
-  auto src_row = [&](int r) {                          // activation row of tile row r (clamped)
-    const int rr = row0 + min(r, nvalid - 1);
-    return MODE == GEMM_DOWN_MX8 ? rr : a.tok[rr];
+  // activation row of tile row r (clamped): gate_up gathers token rows (offsets from the
+  // activation base: T K < 2^32 bytes), down its own rows relative to the tile's first row
+  // (64-bit bases below, 32-bit offsets within the tile)
+  auto src_row = [&](int r) {
+    const int rl = min(r, nvalid - 1);
+    return MODE == GEMM_DOWN_MX8 ? rl : a.tok[row0 + rl];
   };
+  const uint8_t* qbase = a.xq + (MODE == GEMM_DOWN_MX8 ? (size_t)row0 * L.K : 0);
+  const uint8_t* sbase = a.xs + (MODE == GEMM_DOWN_MX8 ? (size_t)row0 * (L.K / 32) : 0);
   // code DMA: instruction i of this wave fills slots (WAVES i + wave) * 64 + lane
   uint32_t src_off[D];
 #pragma unroll
@@ -800,10 +821,10 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void gemm_prefill_mx8_kernel(GemmA
   auto dma = [&](int kc, auto stc) {
     u32x4* T = stage_tile(stc);
     uint32_t* S = stage_scales(stc);
-    const char* base = (const char*)a.xq + (size_t)kc * KCHUNK;
+    const char* base = (const char*)qbase + (size_t)kc * KCHUNK;
 #pragma unroll
     for (int i = 0; i < D; ++i) dma16(base + src_off[i], &T[(WAVES * i + wave) * 64]);
-    __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(a.xs + s_off + 4 * kc),
+    __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(sbase + s_off + 4 * kc),
                                      (void __attribute__((address_space(3)))*)&S[wave * 64], 4, 0, 0);
   };
 
@@ -830,26 +851,35 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void gemm_prefill_mx8_kernel(GemmA
 #pragma unroll
       for (int t = 0; t < TV; ++t) acc[s][t] = f32x4{0.f, 0.f, 0.f, 0.f};
     // three register sets and LDS stages: chunk kc + 2 is loaded while chunk kc is consumed.
-    // Each step issues the same loads (clamped to the last chunk near the end), so one wait
-    // count fits every step: chunk kc's DMA and weights must have landed, the newest step's
-    // loads (weights of kc + 1: 2 NSUB ops; its DMA: D, plus the scale DMA on waves 0 and 1)
-    // may still be in flight.
+    // Chunk kc's DMA must have landed; the loads of chunk kc + 1 (weights: 2 NSUB ops; its DMA:
+    // D code ops and one scale op) may still be in flight; past the last chunk nothing more is
+    // issued and the wait is for everything. Issue order is pinned with scheduling barriers
+    // (the wait count covers the LDS stages written by DMA, which the compiler does not track).
     u32x4 rw[NST][NSUB];
     uint32_t rs[NST][NSUB];
     load_w(0, rw[0], rs[0]);
-    dma(0, IntC<0>());
-    load_w(min(1, L.KC - 1), rw[1], rs[1]);
-    dma(min(1, L.KC - 1), IntC<1>());
     __builtin_amdgcn_sched_barrier(0);
-    auto step = [&](int kc, auto setc) {
+    dma(0, IntC<0>());
+    __builtin_amdgcn_sched_barrier(0);
+    if (L.KC > 1) {
+      load_w(1, rw[1], rs[1]);
+      __builtin_amdgcn_sched_barrier(0);
+      dma(1, IntC<1>());
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    auto step = [&](int kc, auto setc, auto kindc) {
       constexpr int C = decltype(setc)::value;          // kc % 3
+      constexpr int KIND = decltype(kindc)::value;
       constexpr int NX = (C + 2) % NST;                 // set / stage of chunk kc + 2
-      __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * NSUB + D + 1, 0));
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(KIND == STEP_LAST ? 0 : 2 * NSUB + D + 1, 0));
       __builtin_amdgcn_s_barrier();                     // chunk kc in LDS for every wave; stage NX free
       __builtin_amdgcn_sched_barrier(0);
-      load_w(min(kc + 2, L.KC - 1), rw[NX], rs[NX]);
-      dma(min(kc + 2, L.KC - 1), IntC<NX>());
-      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (KIND == STEP_FULL) {
+        load_w(kc + 2, rw[NX], rs[NX]);
+        __builtin_amdgcn_sched_barrier(0);
+        dma(kc + 2, IntC<NX>());
+        __builtin_amdgcn_sched_barrier(0);
+      }
       const u32x4* T0 = stage_tile(IntC<C>());
       const uint8_t* S0 = (const uint8_t*)stage_scales(IntC<C>());
 #pragma unroll
@@ -863,15 +893,8 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void gemm_prefill_mx8_kernel(GemmA
           acc[s][t] = mfma_mx(rw[C][s], (rs[C][s] >> ((kc & 1) * 16)) & 0xFFu, b0, b1, sbv, acc[s][t]);
       }
     };
-    int kc = 0;
-    for (; kc + NST <= L.KC; kc += NST) {
-      step(kc, IntC<0>());
-      step(kc + 1, IntC<1>());
-      step(kc + 2, IntC<2>());
-    }
-    if (kc < L.KC) step(kc, IntC<0>());
-    if (kc + 1 < L.KC) step(kc + 1, IntC<1>());
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));   // the clamped tail loads land before the workgroup exits
+    run_chunks(L.KC, step);
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));   // every load in flight lands before the workgroup exits
 
 #pragma unroll
     for (int t = 0; t < TV; ++t) {
@@ -914,15 +937,14 @@ static void launch_k(K kernel, dim3 grid, dim3 block, hipStream_t s, const Launc
 // The last launch-bound argument (OCC below) is the minimum number of waves per SIMD, which caps
 // the registers of a wave at 512 / OCC.
 constexpr int PRE_NSUB_GU = 2;    // prefill gate_up: 1 gate + 1 up tile per wave
-constexpr int PRE_NSUB_DN = 2;    // prefill down: 2 tiles per wave (2 workgroups per CU)
+constexpr int PRE_NSUB_DN = 2;    // prefill down: 2 tiles per wave
 constexpr int PRE_TSUB = 6;       // prefill: 96 token rows per tile (measured 13% faster than 128 rows)
 constexpr int PRE_NBUF_GU = 3;    // fp16 gate_up: LDS DMA ring depth (3 x 24 KiB; the register-staged modes
                                   // always use 2 stages)
-constexpr int PRE_WAVES_GU = 8;   // fp16 gate_up: 8 waves x 2 tiles = 256 weight rows per token tile, two
-constexpr int PRE_OCC_GU = 4;     // workgroups per CU (128 registers; a few spill). Against 4 waves x 2
-                                  // tiles at 3 per CU: half the token-tile DMA per MFMA, gate_up 5-11% faster
-constexpr int PRE_WAVES_RS = 8;   // down: 8 waves, 1 workgroup per CU (fewer staged pieces per thread;
-constexpr int PRE_OCC_RS = 1;     // measured faster than 4 waves)
+constexpr int PRE_WAVES_GU = 8;   // fp16 gate_up and down: 8 waves x 2 tiles = 256 weight rows per token
+constexpr int PRE_OCC_GU = 4;     // tile, two workgroups per CU (128 registers; a few spill). Against 4 waves
+                                  // x 2 tiles at 3 per CU: half the token-tile DMA per MFMA, gate_up 5-11%
+                                  // faster
 constexpr int PRE_WAVES_FP4 = 4;  // NVFP4 gate_up: 4 waves (its pieces pair up: 8 waves would split one),
 constexpr int PRE_OCC_FP4 = 2;    // 2 workgroups per CU
 constexpr int DEC_MIN_WGS = 2048; // decode: 8 workgroups per CU before 4 tiles per workgroup are used
@@ -958,13 +980,13 @@ static void launch_mode(GemmRegime regime, int max_tiles, int est_tiles, const G
     launch_decode<MODE>(max_tiles, est_tiles, a, s, ev);
   } else if constexpr (MODE != GEMM_GATEUP_BF16) {
     const int ny = (max_tiles + 7) / 8 * 8;
-    if constexpr (MODE == GEMM_DOWN) {
-      constexpr int W = PRE_WAVES_RS, NS = PRE_NSUB_DN;
+    if constexpr (MODE == GEMM_DOWN) {                // rescaled h16 rows by LDS DMA, as gate_up
+      constexpr int W = PRE_WAVES_GU, NS = PRE_NSUB_DN;
       if (a.N % (16 * W * NS) == 0)
-        launch_k(gemm_prefill_kernel<MODE, NS, PRE_TSUB, PRE_NBUF_GU, W, PRE_OCC_RS>,
+        launch_k(gemm_prefill_kernel<MODE, NS, PRE_TSUB, PRE_NBUF_GU, W, PRE_OCC_GU>,
                  dim3(a.N / (16 * W * NS), ny), dim3(64 * W), s, ev, a);
       else   // hidden a multiple of 128 only: one 16-column tile per wave covers it exactly
-        launch_k(gemm_prefill_kernel<MODE, 1, PRE_TSUB, PRE_NBUF_GU, W, PRE_OCC_RS>, dim3(a.N / (16 * W), ny),
+        launch_k(gemm_prefill_kernel<MODE, 1, PRE_TSUB, PRE_NBUF_GU, W, PRE_OCC_GU>, dim3(a.N / (16 * W), ny),
                  dim3(64 * W), s, ev, a);
     } else if constexpr (MODE == GEMM_DOWN_FP4) {     // N = H, a multiple of 128
       constexpr int W = PRE_WAVES_FP4, NS = PRE_NSUB_DN;
@@ -1016,6 +1038,43 @@ hipError_t launch_gemm(GemmMode mode, GemmRegime regime, int max_tiles, int est_
     case GEMM_DOWN_MX8: launch_mx8<GEMM_DOWN_MX8>(regime, max_tiles, est_tiles, a, s, ev); break;
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------- h rescale
+// Between the prefill GEMMs: h16 rows of the first tile list's groups (plain column order, a
+// power-of-two exponent per 16-column block) brought in place to the row's common exponent
+// P = hmin[row] (the smallest block exponent, i.e. the scale of the row's largest block):
+// h16 *= 2^(P - hexp[block]). The down GEMM then streams whole rows by LDS DMA and applies
+// gs_e 2^-P in its epilogue. Grid (I / 128, tile bound): workgroup (c, slot) takes chunk c of
+// the valid rows of tile `slot`; a thread rescales one 16-byte piece (8 columns of one block)
+// at a time, so every element is read and written by the same thread.
+__global__ __launch_bounds__(256) void h_rescale_kernel(uint16_t* __restrict__ h, const int8_t* __restrict__ hexp,
+                                                        const int32_t* __restrict__ hmin,
+                                                        const int32_t* __restrict__ tile_group,
+                                                        const int32_t* __restrict__ tile_row0,
+                                                        const int32_t* __restrict__ tile_count,
+                                                        const int32_t* __restrict__ offsets, int tile_rows, int I) {
+  const int slot = blockIdx.y;
+  if (slot >= tile_count[0]) return;
+  const int g = tile_group[slot], row0 = tile_row0[slot];
+  const int nvalid = min(tile_rows, offsets[g + 1] - row0);
+  const int c = blockIdx.x;
+  for (int i = threadIdx.x; i < nvalid * 16; i += blockDim.x) {
+    const size_t r = (size_t)row0 + (i >> 4);
+    const int p = i & 15;
+    uint16_t* ptr = h + r * I + c * KCHUNK + p * 8;
+    const _Float16 f = h_factor(hmin[r] - (int)hexp[r * (I / 16) + c * 8 + (p >> 1)]);
+    *(f16x8*)ptr = *(const f16x8*)ptr * f;
+  }
+}
+
+hipError_t launch_h_rescale(uint16_t* h, const int8_t* hexp, const int32_t* hmin, const int32_t* tile_group,
+                            const int32_t* tile_row0, const int32_t* tile_count, const int32_t* offsets,
+                            int max_tiles, int tile_rows, int I, hipStream_t s) {
+  if (max_tiles <= 0) return hipSuccess;
+  hipLaunchKernelGGL(h_rescale_kernel, dim3(I / KCHUNK, max_tiles), dim3(256), 0, s, h, hexp, hmin, tile_group,
+                     tile_row0, tile_count, offsets, tile_rows, I);
   return hipGetLastError();
 }
 

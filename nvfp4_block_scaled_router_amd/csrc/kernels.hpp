@@ -138,9 +138,13 @@ struct GemmArgs {
   // in its epilogue. With hmin set (large batches), gate_up also folds each block exponent
   // into hmin[row] (atomicMin) and down reads P there; without it (small batches, where a
   // few rows would take every block's atomic) down takes the minimum over the row's hexp.
+  // The prefill GEMMs keep h16 in plain column order instead (h_natural = 1): a rescale pass
+  // between the GEMMs (launch_h_rescale) brings every block of a row to the row's exponent
+  // P = hmin[row] in place, and the prefill down GEMM streams those rows by LDS DMA.
   uint16_t* out;           // gate_up: h16
   int8_t* hexp;            // [rows][I/16]
   int32_t* hmin;           // [rows] or nullptr
+  int h_natural;           // gate_up: 1 = h16 in plain column order (prefill), 0 = permuted (decode)
   float* hf;               // gate_up: when set, h as fp32 [rows][I] in column order instead (the
                            // input of the row quantiser before DOWN_FP4); out/hexp/hmin unused
   uint8_t* hq8;            // GATEUP_MX8 decode kernel: when set, h MXFP8-quantised in the epilogue,
@@ -180,6 +184,14 @@ struct CombineArgs {
   uint16_t* out;           // bf16 [T][H]
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s, const LaunchEvents& ev = LaunchEvents());
+
+// h16 rows of the first tile list's groups (plain column order, one exponent per 16 columns)
+// brought in place to each row's common exponent P = hmin[row]: h16 *= 2^(P - hexp), exactly
+// (a power of two; values that fall below fp16's normal range lose bits, as in the GEMM's own
+// conversion of the decode path). I = columns per row.
+hipError_t launch_h_rescale(uint16_t* h, const int8_t* hexp, const int32_t* hmin, const int32_t* tile_group,
+                            const int32_t* tile_row0, const int32_t* tile_count, const int32_t* offsets,
+                            int max_tiles, int tile_rows, int I, hipStream_t s);
 
 
 }  // namespace nvmoe
