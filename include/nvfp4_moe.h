@@ -170,7 +170,9 @@ typedef struct moe_plan moe_plan_t;
  * read: per-expert global scale 2^(m - 135), m = the expert's largest scale byte,
  * and E4M3 block scales 2^(byte - m + 8), exact while byte >= m - 17 (E4M3's
  * smallest power of two is 2^-9); moe_validate_weights_host rejects wider spans and
- * the NaN byte 0xFF, and packing flushes blocks below the span to zero.
+ * the NaN byte 0xFF, and packing gives such an expert a NaN global scale, so that
+ * every output reading it is NaN (never a silently different value). With
+ * MOE_ACT_MXFP8 the scale bytes are used as they are and any span is exact.
  * gate_up: N = 2I, K = H, rows 0..I-1 are the gate, rows I..2I-1 the up
  * projection; down: N = H, K = I. */
 typedef struct {
@@ -249,8 +251,11 @@ int moe_pack_router_bias(const moe_plan_t* plan, const float* bias, void* packed
  *                 are ignored, on return undefined
  * Intermediates: gate/up accumulate in FP32 and stay in registers through the
  * SwiGLU; h = silu(g*gs)*(u*gs) is stored as fp16 with one power-of-two exponent
- * per 16 columns (the block's largest |h| scaled into [2^14, 2^15)), which the
- * down GEMM brings to a common per-row exponent exactly before its fp16 MFMAs;
+ * per 16 columns (the block's largest |h| scaled into [2^14, 2^15)); before the fp16
+ * MFMAs of the down GEMM every block is brought to the row's common exponent (that of
+ * its largest block) by a power-of-two factor, which is exact except that values
+ * pushed below fp16's normal range (more than 14 binades under the row's largest
+ * block) lose low bits and those more than 24 binades under it become 0;
  * expert outputs are stored the same way (fp16 with a power-of-two exponent per 16
  * columns) and summed by the combine in fp32. With MOE_ACT_NVFP4_ALL, h is stored
  * as fp32, row-quantised (codes, E4M3 block scales, FP32 row global scale) and the
@@ -273,8 +278,10 @@ int moe_run(const moe_plan_t* plan, const void* packed, int32_t T, const uint16_
                                   routed rows up), by extra workgroups of the first routing
                                   launch */
 #define MOE_STAGE_GATE_UP 2    /* grouped gate/up GEMM + SwiGLU */
-#define MOE_STAGE_DOWN 3       /* grouped down GEMM (with MOE_ACT_NVFP4_ALL: the h row
-                                  quantisation before it) */
+#define MOE_STAGE_DOWN 3       /* grouped down GEMM, with what prepares h for it in
+                                  prefill-regime batches: the h row quantisation
+                                  (MOE_ACT_NVFP4_ALL, MXFP8) or the rescale of the h16 rows
+                                  to their row exponent (16-bit h) */
 #define MOE_STAGE_COMBINE 4    /* weighted combine */
 #define MOE_NUM_STAGES 5
 
@@ -282,8 +289,9 @@ int moe_run(const moe_plan_t* plan, const void* packed, int32_t T, const uint16_
  * handles (as void*, any may be NULL), created by the caller with timing enabled.
  * For the single-kernel stages (GATE_UP, DOWN, COMBINE) events[2s] and events[2s+1]
  * are stamped by the kernel launch itself at the kernel's start and end, so their
- * elapsed time is the kernel's duration (DOWN with MOE_ACT_NVFP4_ALL: the start is
- * recorded on `stream` before the h quantisation); for the others (QUANT, ROUTE: zero
+ * elapsed time is the kernel's duration (DOWN with MOE_ACT_NVFP4_ALL or MXFP8, or any
+ * prefill-regime DOWN: the start is recorded on `stream` before the h quantisation or the
+ * h rescale that precedes the GEMM); for the others (QUANT, ROUTE: zero
  * to four kernels) they are recorded on `stream` right before and after the stage. Results
  * are identical to moe_run. ([b12x] "Using it": per-kernel timing logs for tuning.) */
 int moe_run_timed(const moe_plan_t* plan, const void* packed, int32_t T, const uint16_t* x,

@@ -26,6 +26,7 @@ constexpr int MAX_TOKENS = 65536;
 constexpr int MAX_GROUPS = 64;
 // prefill: experts with at most this many rows run through the decode GEMM (second tile list)
 constexpr int COLD_ROWS = 16;
+constexpr int SPLIT_TILE_ROWS = 64;   // the first list's tile height in skewed and MX8 batches
 // decode batches with at least this many routed rows take bf16 activations through the exact
 // fp16 rescale (one more launch, half the dequant VALU work in the gate_up GEMM): measured
 // 3% faster per step at T = 32 and 64 (top-8), slower at T = 8
@@ -176,8 +177,8 @@ int moe_plan(const moe_desc* desc, moe_plan_t** plan, size_t* packed_bytes, size
   p->ws_xq = o; o = align_up(o + (fp4x ? (size_t)Tm * H / (mx8 ? 1 : 2) : 0));   // codes (MXFP8: a byte each)
   p->ws_xs = o; o = align_up(o + (fp4x ? (size_t)Tm * H / 16 : 0));
   p->ws_xg = o; o = align_up(o + 4 * (size_t)Tm);      // per-row activation factor (either format)
-  p->ws_x16 = o; o = align_up(o + (desc->act_format == MOE_ACT_BF16 ? 2 * (size_t)Tm * H : 0));
-  p->ws_h = o; o = align_up(o + (fp4h || mx8 ? 0 : 2 * rows * I));        // h16
+  p->ws_x16 = o; o = align_up(o + (mx8 ? 0 : 2 * (size_t)Tm * H));   // fp16 x rows (rescaled bf16 or NVFP4 decode)
+  p->ws_h = o; o = align_up(o + (mx8 ? 0 : 2 * rows * I));              // h16 (NVFP4 h: its fp16 decode)
   p->ws_hexp = o; o = align_up(o + (fp4h || mx8 ? 0 : rows * (I / 16)));  // per-16-column h exponents
   p->ws_hmin = o; o = align_up(o + 4 * rows);                       // per-row minimum h exponent
   p->ws_hf = o; o = align_up(o + (fp4h || mx8 ? 4 * rows * I : 0));   // NVFP4 / prefill MXFP8 h: fp32 h rows,
@@ -366,8 +367,11 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
   // Activation preparation: NVFP4 row quantisation, or the exact power-of-two rescale into
   // fp16 (its 1-op dequant route); decode batches below DECODE_F16_ROWS rows feed their bf16
   // rows to the GEMM as they are (the extra launch costs more than the dequant saves there).
+  // Prefill batches with NVFP4 x take its exact fp16 decode (written by the quantiser beside
+  // the codes, the row's global scale in the epilogue) through the fp16 GEMM, whose token
+  // tiles arrive by LDS DMA; decode batches read the codes.
   const GemmMode gu_mode = mx8 ? GEMM_GATEUP_MX8
-                          : fp4 ? GEMM_GATEUP_FP4
+                          : fp4 ? (decode ? GEMM_GATEUP_FP4 : GEMM_GATEUP_F16)
                                 : (decode && T * k < DECODE_F16_ROWS) ? GEMM_GATEUP_BF16 : GEMM_GATEUP_F16;
   if ((e = mark(ev, 2 * MOE_STAGE_QUANT, s)) != hipSuccess) return (int)e;
   // decode batches convert x in extra workgroups of the routing stage's first launch
@@ -375,15 +379,19 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
   if (mx8 && !decode)
     e = launch_mxfp8_rows_bf16(x, T, H, xq, xs, s);
   else if (fp4 && !decode)
-    e = launch_quant_rows_bf16(x, T, H, xq, xs, xg, s);
+    e = launch_quant_rows_bf16(x, T, H, xq, xs, xg, s, x16);
   else if (gu_mode == GEMM_GATEUP_F16 && !decode)
     e = launch_rows_to_f16(x, T, H, x16, xg, s);
   if (e != hipSuccess) return (int)e;
   if ((e = mark(ev, 2 * MOE_STAGE_QUANT + 1, s)) != hipSuccess) return (int)e;
 
-  // MX8 prefill batches whose experts average under 80 rows use 64-row tiles (less of the
-  // last tile of each expert left empty)
-  const int M = decode ? DECODE_TILE_ROWS : (mx8 && (long)T * k < 80L * E) ? 64 : PREFILL_TILE_ROWS;
+  // prefill batches averaging at most 64 rows per expert: experts with few rows (skewed
+  // routing) go to the decode GEMM through a second tile list, in the same launch as the first
+  const bool split = !decode && (long)T * k <= 64L * E;
+  // MX8 prefill batches whose experts average under 80 rows, and the skewed batches, use
+  // 64-row tiles (less of the last tile of each expert left empty, more workgroups)
+  const int M = decode ? DECODE_TILE_ROWS
+                       : ((mx8 && (long)T * k < 80L * E) || (split && !mx8)) ? SPLIT_TILE_ROWS : PREFILL_TILE_ROWS;
   const GemmRegime regime = decode ? REGIME_DECODE_KSPLIT : REGIME_PREFILL;
   RouteArgs ra;
   ra.logits = router_logits;
@@ -419,9 +427,6 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
   pa.k = k;
   pa.G = plan->G;
   pa.tile_rows = M;
-  // prefill batches averaging at most 64 rows per expert: experts with few rows (skewed
-  // routing) go to the decode GEMM through a second tile list
-  const bool split = !decode && (long)T * k <= 64L * E;
   pa.cold_rows = split ? COLD_ROWS : 0;
   pa.counts = (int32_t*)(ws + plan->ws_counts);
   pa.offsets = (int32_t*)(ws + plan->ws_offsets);
@@ -480,12 +485,22 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
     g.h_natural = 0;                             // the decode GEMMs keep h16 permuted
     return g;
   };
+  // the two lists of a skewed batch run in one launch where the split kernel takes the shapes
+  // (the fp16 modes), else one after the other
+  auto both_lists = [&](GemmMode hot_mode, GemmMode cold_mode, const GemmArgs& g, const LaunchEvents& le) {
+    if (!mx8) {
+      const hipError_t r = launch_gemm_split(hot_mode, cold_mode, max_tiles, cold_tiles, g, second(g), s, le);
+      if (r != hipErrorNotSupported) return r;
+    }
+    hipError_t r = launch_gemm(hot_mode, regime, max_tiles, est_tiles, g, s, LaunchEvents{le.start, nullptr});
+    if (r == hipSuccess)
+      r = launch_gemm(cold_mode, REGIME_DECODE_KSPLIT, cold_tiles, cold_tiles, second(g), s,
+                      LaunchEvents{nullptr, le.stop});
+    return r;
+  };
   {
     const LaunchEvents le = stage_events(ev, MOE_STAGE_GATE_UP);
-    e = launch_gemm(gu_mode, regime, max_tiles, est_tiles, g1, s, split ? LaunchEvents{le.start, nullptr} : le);
-    if (e == hipSuccess && split)
-      e = launch_gemm(gu_mode, REGIME_DECODE_KSPLIT, cold_tiles, cold_tiles, second(g1), s,
-                      LaunchEvents{nullptr, le.stop});
+    e = split ? both_lists(gu_mode, gu_mode, g1, le) : launch_gemm(gu_mode, regime, max_tiles, est_tiles, g1, s, le);
   }
   if (e != hipSuccess) return (int)e;
 
@@ -502,10 +517,14 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
   g2.hs8 = nullptr;
   g2.yout = (uint16_t*)(ws + plan->ws_y);
   g2.yexp = (int8_t*)(ws + plan->ws_yexp);
-  const GemmMode dn_mode = mx8 ? GEMM_DOWN_MX8 : fp4h ? GEMM_DOWN_FP4 : GEMM_DOWN;
+  // NVFP4 h: decode batches read the codes; prefill batches take the quantiser's exact fp16
+  // decode of every h row (the row's global scale in the epilogue) through the fp16 GEMM, and
+  // their cold list (decode GEMM) reads the codes
+  const GemmMode dn_mode = mx8 ? GEMM_DOWN_MX8 : (fp4h && decode) ? GEMM_DOWN_FP4 : GEMM_DOWN;
+  const GemmMode dn_cold = fp4h ? GEMM_DOWN_FP4 : dn_mode;
   {
     const LaunchEvents le = stage_events(ev, MOE_STAGE_DOWN);
-    LaunchEvents first = split ? LaunchEvents{le.start, nullptr} : le;
+    LaunchEvents first = le;
     if (fp4h) {   // every h row (T*k routed, T per shared expert) quantised with its own global scale
       g2.xq = ws + plan->ws_hq;
       g2.xs = ws + plan->ws_hs;
@@ -513,7 +532,11 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
       if ((e = mark(ev, 2 * MOE_STAGE_DOWN, s)) != hipSuccess) return (int)e;
       first.start = nullptr;
       e = launch_quant_rows_f32(g1.hf, T * k + S * T, I, ws + plan->ws_hq, ws + plan->ws_hs,
-                                (float*)(ws + plan->ws_hg), s);
+                                (float*)(ws + plan->ws_hg), s, decode ? nullptr : (uint16_t*)(ws + plan->ws_h));
+      if (!decode) {   // the fp16 decode, scaled per row by hg in the epilogue
+        g2.x = (const uint16_t*)(ws + plan->ws_h);
+        g2.hmin = nullptr;
+      }
     } else if (mx8) {
       g2.xq = ws + plan->ws_hq;
       g2.xs = ws + plan->ws_hs;
@@ -528,10 +551,9 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
       e = launch_h_rescale(g1.out, g1.hexp, pa.hmin, pa.tile_group, pa.tile_row0, pa.tile_count, pa.offsets,
                            max_tiles, M, I, s);
     }
-    if (e == hipSuccess) e = launch_gemm(dn_mode, regime, max_tiles, est_tiles, g2, s, first);
-    if (e == hipSuccess && split)
-      e = launch_gemm(dn_mode, REGIME_DECODE_KSPLIT, cold_tiles, cold_tiles, second(g2), s,
-                      LaunchEvents{nullptr, le.stop});
+    if (e == hipSuccess)
+      e = split ? both_lists(dn_mode, dn_cold, g2, LaunchEvents{first.start, le.stop})
+                : launch_gemm(dn_mode, regime, max_tiles, est_tiles, g2, s, first);
   }
   if (e != hipSuccess) return (int)e;
 

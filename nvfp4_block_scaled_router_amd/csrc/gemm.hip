@@ -242,12 +242,14 @@ constexpr int DEC_MAX_WAVES = 4;   // measured best of 4 / 8 / 16 on the decode 
 // needs 4 tiles per workgroup, so a small grid has half the workgroups of the 2-tile split and
 // splits K wider instead; the 8-wave instance is kept apart because its reduction buffer halves
 // the workgroups a CU holds).
-template <int MODE, int NSUB, int MAXW = DEC_MAX_WAVES>
-__global__ __launch_bounds__(64 * MAXW) void gemm_decode_kernel(GemmArgs a) {
+// The decode GEMM's work for one workgroup: slot `slot` of its tile list, weight tiles
+// bx * NSUB .. +NSUB-1, the workgroup's waves splitting K; `red` holds MAXW x NSUB x 64 f32x4
+// of LDS for the reduction.
+template <int MODE, int NSUB, int MAXW>
+__device__ __forceinline__ void decode_body(const GemmArgs& a, int bx, int slot, f32x4* red_lds) {
   constexpr bool F16 = MODE != GEMM_GATEUP_BF16;           // fp16 MFMA (bf16 x: bf16 MFMA)
   constexpr bool MX8 = MODE == GEMM_GATEUP_MX8 || MODE == GEMM_DOWN_MX8;   // scaled MFMA on MX codes
   constexpr bool DOWNM = MODE == GEMM_DOWN || MODE == GEMM_DOWN_FP4 || MODE == GEMM_DOWN_MX8;
-  const int slot = blockIdx.y;
   // the slot's entries are read together with the count (slots past it hold stale values
   // that are never used; the tile arrays have room for any grid), saving one dependent
   // round trip before the weight loads; a second-list launch starts after the first list
@@ -258,7 +260,7 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_decode_kernel(GemmArgs a) {
   if (slot >= ntiles) return;
   const ProjLayout L = proj_layout(a.N, a.K);
   const int NW = blockDim.x >> 6;
-  const int q0 = blockIdx.x * NSUB;
+  const int q0 = bx * NSUB;
   const float wgs = a.wgs[g];
   const int nvalid = min(DECODE_TILE_ROWS, a.offsets[g + 1] - row0);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & (WAVE - 1);
@@ -351,7 +353,7 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_decode_kernel(GemmArgs a) {
     }
   }
 
-  __shared__ f32x4 red[MAXW][NSUB][WAVE];
+  f32x4 (*red)[NSUB][WAVE] = (f32x4 (*)[NSUB][WAVE])red_lds;
 #pragma unroll
   for (int s = 0; s < NSUB; ++s) red[wave][s][lane] = acc[s];
   __syncthreads();
@@ -375,7 +377,7 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_decode_kernel(GemmArgs a) {
             t[s] = red[0][s][lane];
             for (int w = 1; w < NW; ++w) t[s] += red[w][s][lane];
           }
-          epilogue_mx8(a, t[0], t[1], t[2], t[3], orow, blockIdx.x, lim);
+          epilogue_mx8(a, t[0], t[1], t[2], t[3], orow, bx, lim);
         }
         return;
       }
@@ -392,6 +394,12 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_decode_kernel(GemmArgs a) {
   }
 }
 
+template <int MODE, int NSUB, int MAXW = DEC_MAX_WAVES>
+__global__ __launch_bounds__(64 * MAXW) void gemm_decode_kernel(GemmArgs a) {
+  __shared__ f32x4 red[MAXW * NSUB * WAVE];
+  decode_body<MODE, NSUB, MAXW>(a, blockIdx.x, blockIdx.y, red);
+}
+
 // XCD-aware work order of the prefill GEMMs. Workgroups are handed to the 8 XCDs (each
 // with its own L2) round-robin by linear id, so consecutive ids never share an L2. The
 // grid is (n-blocks) x (slot bound rounded up to 8); workgroup id i runs on XCD i % 8 and
@@ -401,9 +409,7 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_decode_kernel(GemmArgs a) {
 struct PrefillItem {
   int slot, nb;
 };
-__device__ __forceinline__ PrefillItem prefill_item(int ntiles) {
-  const int NB = gridDim.x;
-  const int lin = blockIdx.y * NB + blockIdx.x;
+__device__ __forceinline__ PrefillItem prefill_item(int ntiles, int lin, int NB) {
   const int xcd = lin & 7, j = lin >> 3;
   const int per_xcd = (ntiles + 7) >> 3;
   PrefillItem it;
@@ -435,9 +441,9 @@ __device__ __forceinline__ int lds_swz(int r) {
 //    registers, chunk kc + NBUF - 1 in flight while chunk kc is consumed. One DMA instruction
 //    writes 64 consecutive 16-byte slots (lane i -> slot i), so the swizzle is applied on the
 //    global side: the lane that fills slot (r, c) fetches piece c ^ lds_swz(r) of row r;
-//  - registers (NVFP4 activations, GATEUP_FP4 and DOWN_FP4), converted on the way in: E2M1
-//    codes x E4M3 block scale -> fp16; two stages, chunk kc + 1 loaded while chunk kc is
-//    consumed.
+//  NVFP4 rows (x of W4A4, h of W4A4 down) arrive the same way as their exact fp16 decode,
+//  written by the row quantiser beside the codes, with the row's global scale applied in
+//  the epilogue.
 // Issue order inside a chunk is pinned with scheduling barriers (the wait counts rely on it).
 __device__ __forceinline__ void dma16(const void* src, const void* lds_dst) {
   __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
@@ -485,28 +491,22 @@ __device__ __forceinline__ void run_chunks(int KC, F&& step) {
 // s_waitcnt immediate: vmcnt(vm) lgkmcnt(lgkm), expcnt not waited.
 constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8); }
 
-template <int MODE, int NSUB, int TSUB, int NBUF, int WAVES, int OCC>
-__global__ __launch_bounds__(64 * WAVES, OCC) void gemm_prefill_kernel(GemmArgs a) {
-  static_assert(MODE == GEMM_GATEUP_F16 || MODE == GEMM_GATEUP_FP4 || MODE == GEMM_DOWN || MODE == GEMM_DOWN_FP4,
-                "prefill modes");
-  constexpr bool FP4A = MODE == GEMM_GATEUP_FP4 || MODE == GEMM_DOWN_FP4;   // NVFP4 activation rows
-  constexpr bool DOWNM = MODE == GEMM_DOWN || MODE == GEMM_DOWN_FP4;        // rows addressed directly
+// The prefill GEMM's work for the workgroup of linear id `lin` in a grid of NB n-blocks per
+// row of slots (see prefill_item); `tile` is NBUF x TSUB*16*16 16-byte slots of LDS.
+template <int MODE, int NSUB, int TSUB, int NBUF, int WAVES>
+__device__ __forceinline__ void prefill_body(const GemmArgs& a, int lin, int NB, u32x4* tile) {
+  static_assert(MODE == GEMM_GATEUP_F16 || MODE == GEMM_DOWN, "prefill modes: fp16 rows by LDS DMA");
+  constexpr bool DOWNM = MODE == GEMM_DOWN;           // rows addressed directly (gate_up gathers tokens)
   static_assert(WAVES == 4 || WAVES == 8, "4 or 8 waves");
-  constexpr bool DMA = !FP4A;                         // fp16 token rows: x16 (gate_up) or rescaled h16 (down)
-  static_assert(!DMA || NBUF == 2 || NBUF == 3, "LDS ring depth");
-  constexpr int NST = DMA ? NBUF : 2;                 // LDS stages
+  static_assert(NBUF == 2 || NBUF == 3, "LDS ring depth");
   constexpr int M = TSUB * 16;
   constexpr int STAGE = M * 16;                       // 16-byte slots per stage
   constexpr int NT = 64 * WAVES;                      // threads
   constexpr int D = STAGE / NT;                       // DMA instructions per lane per chunk
-  // register staging (FP4): 16-column pieces (8 code bytes + 1 scale byte), D/2 per thread
-  constexpr int NPC = D / 2;
-  static_assert(D >= 2 && STAGE % NT == 0, "tile size");
-  static_assert(!FP4A || D % 2 == 0, "NVFP4 pieces pair up");
-  __shared__ u32x4 tile[NST * STAGE];
+  static_assert(D >= 1 && STAGE % NT == 0, "tile size");
 
   const int ntiles = a.tile_count[0];
-  const PrefillItem item = prefill_item(ntiles);
+  const PrefillItem item = prefill_item(ntiles, lin, NB);
   const int slot = item.slot;
   if (slot >= ntiles) return;
   const int g = a.tile_group[slot];
@@ -518,64 +518,24 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void gemm_prefill_kernel(GemmArgs 
   const int q0 = (item.nb * WAVES + wave) * NSUB;         // the launch covers N exactly
   const int nvalid = min(M, a.offsets[g + 1] - row0);
 
-  // ---- token-tile staging. Byte offsets are 32-bit: gather modes address token rows from the
-  // activation base (T K 2 < 2^32 bytes), the down modes their own rows from the tile's first
-  // row (64-bit base; offsets within the tile).
-  // DMA: instruction i of this wave fills slots (WAVES i + wave) * 64 .. +63: row
-  // r = 4 (WAVES i + wave) + lane / 16, slot column lane % 16; byte offsets from the chunk base.
-  uint32_t src_off[DMA ? D : 1];
-  // registers (FP4): piece i of this thread is piece (threadIdx.x + NT i) of the tile, in row
-  // r0 + (NT/8) i: the same r % 16 for every i, so one slot base (+ 2 NT i) serves all
-  uint32_t poff[DMA ? 1 : NPC];                          // FP4: bytes into xq from qbase
-  const int pcol = (int)(threadIdx.x & 7);
-  const int r0 = (int)(threadIdx.x >> 3);
-  const int swz0 = lds_swz(r0);
-  const char* xbase = (const char*)a.x + (MODE == GEMM_DOWN ? (size_t)row0 * L.K * 2 : 0);
-  const uint8_t* qbase = a.xq + (MODE == GEMM_DOWN_FP4 ? (size_t)row0 * (L.K / 2) : 0);
-  const uint8_t* sbase = a.xs + (MODE == GEMM_DOWN_FP4 ? (size_t)row0 * (L.K / 16) : 0);
-  if constexpr (DMA) {
+  // ---- token-tile DMA. Instruction i of this wave fills slots (WAVES i + wave) * 64 .. +63:
+  // row r = 4 (WAVES i + wave) + lane / 16, slot column lane % 16. Byte offsets are 32-bit: the
+  // gate_up gathers token rows from the activation base (T K 2 < 2^32 bytes), the down GEMM
+  // reads its own rows from the tile's first row (a 64-bit base; offsets within the tile).
+  uint32_t src_off[D];
+  const char* xbase = (const char*)a.x + (DOWNM ? (size_t)row0 * L.K * 2 : 0);
 #pragma unroll
-    for (int i = 0; i < D; ++i) {
-      const int r = 4 * (WAVES * i + wave) + lg;
-      const int rl = min(r, nvalid - 1);                 // rows past the group repeat its last row
-      const int kp = l16 ^ lds_swz(r);                   // k-order piece this slot holds
-      const uint32_t src = DOWNM ? (uint32_t)rl : (uint32_t)a.tok[row0 + rl];
-      src_off[i] = (src * (uint32_t)L.K + kp * 8) * 2;
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < NPC; ++i) {
-      const int rl = min(r0 + (NT / 8) * i, nvalid - 1);
-      // its scale byte: poff / 8 into xs; gate_up gathers token rows, down reads its own rows
-      poff[i] = (uint32_t)(DOWNM ? rl : a.tok[row0 + rl]) * (L.K / 2) + pcol * 8;
-    }
+  for (int i = 0; i < D; ++i) {
+    const int r = 4 * (WAVES * i + wave) + lg;
+    const int rl = min(r, nvalid - 1);                   // rows past the group repeat its last row
+    const int kp = l16 ^ lds_swz(r);                     // k-order piece this slot holds
+    const uint32_t src = DOWNM ? (uint32_t)rl : (uint32_t)a.tok[row0 + rl];
+    src_off[i] = (src * (uint32_t)L.K + kp * 8) * 2;
   }
-  const int slot0 = r0 * 16;
   auto dma = [&](int kc, int st) {
     const char* base = xbase + (size_t)kc * (KCHUNK * 2);
 #pragma unroll
     for (int i = 0; i < D; ++i) dma16(base + src_off[i], &tile[st * STAGE + (WAVES * i + wave) * 64]);
-  };
-  u32x4 sv[DMA ? 1 : NPC];      // staged pieces (FP4: codes in .x .y)
-  uint32_t se[DMA ? 1 : NPC];   // FP4: scale byte
-  auto stage_load = [&](int kc) {
-#pragma unroll
-    for (int i = 0; i < NPC; ++i) {
-      const u32x2 q = *(const u32x2*)(qbase + (size_t)kc * 64 + poff[i]);
-      sv[i] = u32x4{q.x, q.y, 0u, 0u};
-      se[i] = sbase[(size_t)kc * 8 + poff[i] / 8];
-    }
-  };
-  auto stage_store = [&](int st) {
-#pragma unroll
-    for (int i = 0; i < NPC; ++i) {
-      const f16x2 s1 = e4m3x2_to_f16x2(se[i]);
-      const f16x2 s2 = {s1.x, s1.x};
-      const f16x8 lo = dequant8_f16(sv[i].x, s2), hi = dequant8_f16(sv[i].y, s2);
-      const int c = 2 * pcol;
-      tile[st * STAGE + slot0 + 2 * NT * i + (c ^ swz0)] = __builtin_bit_cast(u32x4, lo);
-      tile[st * STAGE + slot0 + 2 * NT * i + ((c + 1) ^ swz0)] = __builtin_bit_cast(u32x4, hi);
-    }
   };
 
   // ---- weights of this wave: fp4 16 B per lane per chunk; the chunk's two block-scale
@@ -601,7 +561,6 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void gemm_prefill_kernel(GemmArgs 
   // expert on average), and the staging above still moves whole tiles so that every
   // workgroup issues the same loads and waits.
   static_assert(TSUB == 8 || TSUB == 6 || TSUB == 4, "row tiers assume 4, 6 or 8 slices");
-  static_assert(TSUB * 16 == PREFILL_TILE_ROWS, "the plan's tile height");
   auto body = [&](auto tvc) {
     constexpr int TV = decltype(tvc)::value;
     f32x4 acc[NSUB][TV];
@@ -611,7 +570,7 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void gemm_prefill_kernel(GemmArgs 
       for (int t = 0; t < TV; ++t) acc[s][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     auto mma = [&](int kc, int j, const WOps<true> (&W)[NSUB]) {
-      const u32x4* T0 = &tile[(kc % NST) * STAGE];
+      const u32x4* T0 = &tile[(kc % NBUF) * STAGE];
       const int c = (lg * 4 + j) ^ lds_swz(l16);
       u32x4 bop[TV];
 #pragma unroll
@@ -621,54 +580,7 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void gemm_prefill_kernel(GemmArgs 
 #pragma unroll
         for (int t = 0; t < TV; ++t) acc[s][t] = mfma_any(W[s].v[j], bop[t], acc[s][t]);
     };
-    if constexpr (!DMA) {
-      // NVFP4 activations (register-staged tiles). Weights: two raw register sets (rA/rB,
-      // chunk parity) and two dequantised sets (WA/WB): chunk kc + 2's raw weights are
-      // fetched at the start of chunk kc and chunk kc + 1's are dequantised in the middle of
-      // chunk kc, between its MFMAs, so the VALU work of the dequant runs beside the MFMA pipe
-      // instead of ahead of it. Chunk kc: store the staged chunk kc (its loads were issued one
-      // chunk earlier), issue the loads of chunk kc + 1 and the raw weights ahead, barrier,
-      // consume chunk kc. Register roles alternate with the chunk parity (no copies, which
-      // would wait for loads in flight).
-      u32x4 rA[NSUB], rB[NSUB];
-      uint32_t sA[NSUB], sB[NSUB];
-      WOps<true> WA[NSUB], WB[NSUB];
-      load_w(0, rA, sA);
-      load_w(min(1, L.KC - 1), rB, sB);
-#pragma unroll
-      for (int s = 0; s < NSUB; ++s) WA[s].make(rA[s], sA[s]);
-      __builtin_amdgcn_sched_barrier(0);
-      stage_load(0);
-      auto step = [&](int kc, const WOps<true> (&Wc)[NSUB], WOps<true> (&Wn)[NSUB], const u32x4 (&rn)[NSUB],
-                      const uint32_t (&sn)[NSUB], u32x4 (&rf)[NSUB], uint32_t (&sf)[NSUB]) {
-        stage_store(kc & 1);
-        __builtin_amdgcn_sched_barrier(0);
-        stage_load(min(kc + 1, L.KC - 1));
-        load_w(min(kc + 2, L.KC - 1), rf, sf);
-        __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));      // this thread's LDS stores done
-        __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-        mma(kc, 0, Wc);
-        mma(kc, 1, Wc);
-#pragma unroll
-        for (int s = 0; s < NSUB; ++s) Wn[s].make(rn[s], sn[s] >> (((kc + 1) & 1) * 16));
-        mma(kc, 2, Wc);
-        mma(kc, 3, Wc);
-      };
-      // pairs of steps with fixed register roles; an odd count peels chunk 0
-      if (L.KC & 1) {
-        step(0, WA, WB, rB, sB, rA, sA);
-        for (int kc = 1; kc < L.KC; kc += 2) {
-          step(kc, WB, WA, rA, sA, rB, sB);
-          step(kc + 1, WA, WB, rB, sB, rA, sA);
-        }
-      } else {
-        for (int kc = 0; kc < L.KC; kc += 2) {
-          step(kc, WA, WB, rB, sB, rA, sA);
-          step(kc + 1, WB, WA, rA, sA, rB, sB);
-        }
-      }
-    } else {
+    {
       // fp16 rows by LDS DMA into an NBUF-deep ring; raw weights one chunk ahead in two
       // register sets (chunk parity), dequantised right before the chunk's MFMAs. Chunk kc:
       // wait for chunk kc in LDS and its weights (older loads complete, the newest NBUF - 2
@@ -721,7 +633,9 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void gemm_prefill_kernel(GemmArgs 
       if (rr >= nvalid) continue;
       const int orow = row0 + rr;
       if (DOWNM) {
-        const float scl = MODE == GEMM_DOWN ? __builtin_ldexpf(wgs, -a.hmin[orow]) : wgs * a.xg[orow];
+        // h16 from gate_up: the row's exponent P (2^-P); NVFP4 h: its fp16 decode, the row's
+        // global scale
+        const float scl = a.hmin ? __builtin_ldexpf(wgs, -a.hmin[orow]) : wgs * a.xg[orow];
 #pragma unroll
         for (int s = 0; s < NSUB; ++s) epilogue_single(a, acc[s][t], scl, orow, q0 + s);
       } else {
@@ -746,6 +660,34 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void gemm_prefill_kernel(GemmArgs 
   } else {
     if (tv > 2) body(IntC<4>());
     else body(IntC<2>());
+  }
+}
+
+template <int MODE, int NSUB, int TSUB, int NBUF, int WAVES, int OCC>
+__global__ __launch_bounds__(64 * WAVES, OCC) void gemm_prefill_kernel(GemmArgs a) {
+  __shared__ u32x4 tile[NBUF * TSUB * 16 * 16];
+  prefill_body<MODE, NSUB, TSUB, NBUF, WAVES>(a, blockIdx.y * gridDim.x + blockIdx.x, gridDim.x, tile);
+}
+
+// Skewed prefill batches in one launch: workgroups 0 .. n_hot - 1 run the prefill GEMM over
+// the first tile list (experts with many rows: compute bound), the rest the decode GEMM over
+// the second (experts with a few rows: weight streaming), so the streaming work takes the
+// compute units the hot tiles leave free and follows them as they finish, instead of waiting
+// for the whole list. (Alternating the two kinds of work in groups of eight ids measured 25%
+// slower than the hot tiles first.) Both parts use the workgroup's 8 waves (the decode part
+// splits K eight ways) and one LDS buffer.
+template <int MODE_HOT, int MODE_COLD, int TSUB, int NSUB_COLD>
+__global__ __launch_bounds__(512, 4) void gemm_split_kernel(GemmArgs hot, GemmArgs cold, int n_hot, int NB,
+                                                            int nbx) {
+  constexpr int HOT_SLOTS = 3 * TSUB * 16 * 16;
+  constexpr int COLD_SLOTS = 8 * NSUB_COLD * WAVE;
+  __shared__ u32x4 smem[HOT_SLOTS > COLD_SLOTS ? HOT_SLOTS : COLD_SLOTS];
+  const int lin = blockIdx.x;
+  if (lin < n_hot) {
+    prefill_body<MODE_HOT, 2, TSUB, 3, 8>(hot, lin, NB, smem);
+  } else {
+    const int c = lin - n_hot;
+    decode_body<MODE_COLD, NSUB_COLD, 8>(cold, c % nbx, c / nbx, (f32x4*)smem);
   }
 }
 
@@ -787,7 +729,7 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void gemm_prefill_mx8_kernel(GemmA
   };
 
   const int ntiles = a.tile_count[0];
-  const PrefillItem item = prefill_item(ntiles);
+  const PrefillItem item = prefill_item(ntiles, blockIdx.y * gridDim.x + blockIdx.x, gridDim.x);
   const int slot = item.slot;
   if (slot >= ntiles) return;
   const int g = a.tile_group[slot];
@@ -939,14 +881,11 @@ static void launch_k(K kernel, dim3 grid, dim3 block, hipStream_t s, const Launc
 constexpr int PRE_NSUB_GU = 2;    // prefill gate_up: 1 gate + 1 up tile per wave
 constexpr int PRE_NSUB_DN = 2;    // prefill down: 2 tiles per wave
 constexpr int PRE_TSUB = 6;       // prefill: 96 token rows per tile (measured 13% faster than 128 rows)
-constexpr int PRE_NBUF_GU = 3;    // fp16 gate_up: LDS DMA ring depth (3 x 24 KiB; the register-staged modes
-                                  // always use 2 stages)
+constexpr int PRE_NBUF_GU = 3;    // prefill GEMMs: LDS DMA ring depth (3 x 24 KiB)
 constexpr int PRE_WAVES_GU = 8;   // fp16 gate_up and down: 8 waves x 2 tiles = 256 weight rows per token
 constexpr int PRE_OCC_GU = 4;     // tile, two workgroups per CU (128 registers; a few spill). Against 4 waves
                                   // x 2 tiles at 3 per CU: half the token-tile DMA per MFMA, gate_up 5-11%
                                   // faster
-constexpr int PRE_WAVES_FP4 = 4;  // NVFP4 gate_up: 4 waves (its pieces pair up: 8 waves would split one),
-constexpr int PRE_OCC_FP4 = 2;    // 2 workgroups per CU
 constexpr int DEC_MIN_WGS = 2048; // decode: 8 workgroups per CU before 4 tiles per workgroup are used
 
 // Decode split: 4 weight tiles per workgroup (twice the reuse of each token-operand load)
@@ -974,34 +913,29 @@ static void launch_decode(int max_tiles, int est_tiles, const GemmArgs& a, hipSt
 }
 
 template <int MODE>
-static void launch_mode(GemmRegime regime, int max_tiles, int est_tiles, const GemmArgs& a, hipStream_t s,
-                        const LaunchEvents& ev) {
+static hipError_t launch_mode(GemmRegime regime, int max_tiles, int est_tiles, const GemmArgs& a, hipStream_t s,
+                              const LaunchEvents& ev) {
   if (regime == REGIME_DECODE_KSPLIT) {
     launch_decode<MODE>(max_tiles, est_tiles, a, s, ev);
-  } else if constexpr (MODE != GEMM_GATEUP_BF16) {
+  } else if constexpr (MODE == GEMM_GATEUP_F16 || MODE == GEMM_DOWN) {   // the prefill GEMMs: fp16 rows
     const int ny = (max_tiles + 7) / 8 * 8;
-    if constexpr (MODE == GEMM_DOWN) {                // rescaled h16 rows by LDS DMA, as gate_up
-      constexpr int W = PRE_WAVES_GU, NS = PRE_NSUB_DN;
-      if (a.N % (16 * W * NS) == 0)
-        launch_k(gemm_prefill_kernel<MODE, NS, PRE_TSUB, PRE_NBUF_GU, W, PRE_OCC_GU>,
-                 dim3(a.N / (16 * W * NS), ny), dim3(64 * W), s, ev, a);
-      else   // hidden a multiple of 128 only: one 16-column tile per wave covers it exactly
-        launch_k(gemm_prefill_kernel<MODE, 1, PRE_TSUB, PRE_NBUF_GU, W, PRE_OCC_GU>, dim3(a.N / (16 * W), ny),
-                 dim3(64 * W), s, ev, a);
-    } else if constexpr (MODE == GEMM_DOWN_FP4) {     // N = H, a multiple of 128
-      constexpr int W = PRE_WAVES_FP4, NS = PRE_NSUB_DN;
-      launch_k(gemm_prefill_kernel<MODE, NS, PRE_TSUB, PRE_NBUF_GU, W, PRE_OCC_FP4>, dim3(a.N / (16 * W * NS), ny),
-               dim3(64 * W), s, ev, a);
-    } else if constexpr (MODE == GEMM_GATEUP_F16) {   // N = 2I, a multiple of 256 (16 W NS)
-      constexpr int W = PRE_WAVES_GU, NS = PRE_NSUB_GU;
-      launch_k(gemm_prefill_kernel<MODE, NS, PRE_TSUB, PRE_NBUF_GU, W, PRE_OCC_GU>, dim3(a.N / (16 * W * NS), ny),
-               dim3(64 * W), s, ev, a);
-    } else {
-      constexpr int W = PRE_WAVES_FP4, NS = PRE_NSUB_GU;
-      launch_k(gemm_prefill_kernel<MODE, NS, PRE_TSUB, PRE_NBUF_GU, W, PRE_OCC_FP4>, dim3(a.N / (16 * W * NS), ny),
-               dim3(64 * W), s, ev, a);
-    }
+    constexpr int W = PRE_WAVES_GU, NS = MODE == GEMM_DOWN ? PRE_NSUB_DN : PRE_NSUB_GU;
+    const bool t64 = a.tile_rows == 64;
+    if (!t64 && a.tile_rows != PREFILL_TILE_ROWS) return hipErrorInvalidValue;
+    if (a.N % (16 * W * NS) == 0)
+      launch_k(t64 ? gemm_prefill_kernel<MODE, NS, 4, PRE_NBUF_GU, W, PRE_OCC_GU>
+                   : gemm_prefill_kernel<MODE, NS, PRE_TSUB, PRE_NBUF_GU, W, PRE_OCC_GU>,
+               dim3(a.N / (16 * W * NS), ny), dim3(64 * W), s, ev, a);
+    else if (MODE == GEMM_DOWN)   // hidden a multiple of 128 only: one 16-column tile per wave covers it exactly
+      launch_k(t64 ? gemm_prefill_kernel<MODE, 1, 4, PRE_NBUF_GU, W, PRE_OCC_GU>
+                   : gemm_prefill_kernel<MODE, 1, PRE_TSUB, PRE_NBUF_GU, W, PRE_OCC_GU>,
+               dim3(a.N / (16 * W), ny), dim3(64 * W), s, ev, a);
+    else
+      return hipErrorInvalidValue;   // gate_up: N = 2I, a multiple of 256
+  } else {
+    return hipErrorInvalidValue;     // the NVFP4 and bf16 modes run in the decode regime only
   }
+  return hipSuccess;
 }
 
 constexpr int PRE_WAVES_MX8 = 4;   // MX8 prefill: 4 waves x 2 weight tiles (a 2 x 2 wave layout with the
@@ -1027,17 +961,18 @@ static void launch_mx8(GemmRegime regime, int max_tiles, int est_tiles, const Ge
 hipError_t launch_gemm(GemmMode mode, GemmRegime regime, int max_tiles, int est_tiles, const GemmArgs& a,
                        hipStream_t s, const LaunchEvents& ev) {
   if (max_tiles <= 0) return hipSuccess;
-  if (mode == GEMM_GATEUP_BF16 && regime != REGIME_DECODE_KSPLIT) return hipErrorInvalidValue;
+  hipError_t e = hipSuccess;
   switch (mode) {
-    case GEMM_GATEUP_F16: launch_mode<GEMM_GATEUP_F16>(regime, max_tiles, est_tiles, a, s, ev); break;
-    case GEMM_GATEUP_BF16: launch_mode<GEMM_GATEUP_BF16>(regime, max_tiles, est_tiles, a, s, ev); break;
-    case GEMM_GATEUP_FP4: launch_mode<GEMM_GATEUP_FP4>(regime, max_tiles, est_tiles, a, s, ev); break;
-    case GEMM_DOWN: launch_mode<GEMM_DOWN>(regime, max_tiles, est_tiles, a, s, ev); break;
-    case GEMM_DOWN_FP4: launch_mode<GEMM_DOWN_FP4>(regime, max_tiles, est_tiles, a, s, ev); break;
+    case GEMM_GATEUP_F16: e = launch_mode<GEMM_GATEUP_F16>(regime, max_tiles, est_tiles, a, s, ev); break;
+    case GEMM_GATEUP_BF16: e = launch_mode<GEMM_GATEUP_BF16>(regime, max_tiles, est_tiles, a, s, ev); break;
+    case GEMM_GATEUP_FP4: e = launch_mode<GEMM_GATEUP_FP4>(regime, max_tiles, est_tiles, a, s, ev); break;
+    case GEMM_DOWN: e = launch_mode<GEMM_DOWN>(regime, max_tiles, est_tiles, a, s, ev); break;
+    case GEMM_DOWN_FP4: e = launch_mode<GEMM_DOWN_FP4>(regime, max_tiles, est_tiles, a, s, ev); break;
     case GEMM_GATEUP_MX8: launch_mx8<GEMM_GATEUP_MX8>(regime, max_tiles, est_tiles, a, s, ev); break;
     case GEMM_DOWN_MX8: launch_mx8<GEMM_DOWN_MX8>(regime, max_tiles, est_tiles, a, s, ev); break;
     default: return hipErrorInvalidValue;
   }
+  if (e != hipSuccess) return e;
   return hipGetLastError();
 }
 
@@ -1075,6 +1010,46 @@ hipError_t launch_h_rescale(uint16_t* h, const int8_t* hexp, const int32_t* hmin
   if (max_tiles <= 0) return hipSuccess;
   hipLaunchKernelGGL(h_rescale_kernel, dim3(I / KCHUNK, max_tiles), dim3(256), 0, s, h, hexp, hmin, tile_group,
                      tile_row0, tile_count, offsets, tile_rows, I);
+  return hipGetLastError();
+}
+
+// Skewed prefill batches: both tile lists in one launch (gemm_split_kernel). The hot part is
+// the prefill GEMM at 8 waves x 2 tiles (N a multiple of 256); the cold part the decode GEMM at
+// 4 tiles per workgroup (N a multiple of 64).
+template <int MODE_HOT, int MODE_COLD>
+static void launch_split_modes(int tsub, dim3 grid, const GemmArgs& hot, const GemmArgs& cold, int n_hot, int NB,
+                               int nbx, hipStream_t s, const LaunchEvents& ev) {
+  auto go = [&](auto kernel) {
+    if (ev.start || ev.stop)
+      hipExtLaunchKernelGGL(kernel, grid, dim3(512), 0, s, ev.start, ev.stop, 0, hot, cold, n_hot, NB, nbx);
+    else
+      hipLaunchKernelGGL(kernel, grid, dim3(512), 0, s, hot, cold, n_hot, NB, nbx);
+  };
+  if (tsub == 4)
+    go(gemm_split_kernel<MODE_HOT, MODE_COLD, 4, 4>);
+  else
+    go(gemm_split_kernel<MODE_HOT, MODE_COLD, 6, 4>);
+}
+
+hipError_t launch_gemm_split(GemmMode hot_mode, GemmMode cold_mode, int max_tiles, int cold_tiles,
+                             const GemmArgs& hot, const GemmArgs& cold, hipStream_t s, const LaunchEvents& ev) {
+  if (hot.N % (16 * PRE_WAVES_GU * 2) || cold.N % 64 || (hot.tile_rows != 64 && hot.tile_rows != 96))
+    return hipErrorNotSupported;   // declined: nothing launched
+  const int NB = hot.N / (16 * PRE_WAVES_GU * 2);
+  const int n_hot = NB * ((max_tiles + 7) / 8 * 8);
+  const int nbx = cold.N / 64;
+  const long total = (long)n_hot + (long)nbx * cold_tiles;
+  if (total <= 0 || total > (1L << 31) - 1) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)total);
+  const int tsub = hot.tile_rows / 16;
+  if (hot_mode == GEMM_GATEUP_F16 && cold_mode == GEMM_GATEUP_F16)
+    launch_split_modes<GEMM_GATEUP_F16, GEMM_GATEUP_F16>(tsub, grid, hot, cold, n_hot, NB, nbx, s, ev);
+  else if (hot_mode == GEMM_DOWN && cold_mode == GEMM_DOWN)
+    launch_split_modes<GEMM_DOWN, GEMM_DOWN>(tsub, grid, hot, cold, n_hot, NB, nbx, s, ev);
+  else if (hot_mode == GEMM_DOWN && cold_mode == GEMM_DOWN_FP4)
+    launch_split_modes<GEMM_DOWN, GEMM_DOWN_FP4>(tsub, grid, hot, cold, n_hot, NB, nbx, s, ev);
+  else
+    return hipErrorNotSupported;
   return hipGetLastError();
 }
 

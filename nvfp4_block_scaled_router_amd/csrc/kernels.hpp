@@ -65,15 +65,17 @@ size_t plan_scratch_ints(int T, int k, int E);
 bool plan_small_ok(int T, int k);
 
 // Activation / weight quantiser.
+// With x16 != nullptr also the rows' exact fp16 decode without the global scale,
+// E2M1 x E4M3 per element ([rows][K], plain column order).
 hipError_t launch_quant_rows_bf16(const uint16_t* x, int rows, int K, uint8_t* packed, uint8_t* scales,
-                                  float* gs, hipStream_t s);
+                                  float* gs, hipStream_t s, uint16_t* x16 = nullptr);
 // MXFP8 rows (codes [rows][K], E8M0 scales [rows][K/32]) from bf16 or fp32 rows.
 hipError_t launch_mxfp8_rows_bf16(const uint16_t* x, int rows, int K, uint8_t* codes, uint8_t* scales,
                                   hipStream_t s);
 hipError_t launch_mxfp8_rows_f32(const float* x, int rows, int K, uint8_t* codes, uint8_t* scales, hipStream_t s);
 // fp32 rows (h before the NVFP4 down GEMM), each with its own global scale.
 hipError_t launch_quant_rows_f32(const float* x, int rows, int K, uint8_t* packed, uint8_t* scales, float* gs,
-                                 hipStream_t s);
+                                 hipStream_t s, uint16_t* x16 = nullptr);
 // bf16 rows -> fp16 rows scaled by 2^p (p per row puts max|x| in [2^14, 2^15)); xf = 2^-p.
 hipError_t launch_rows_to_f16(const uint16_t* x, int rows, int K, uint16_t* x16, float* xf, hipStream_t s);
 hipError_t launch_quant_groups_f32(const float* x, int groups, int rows_per_group, int K, uint8_t* packed,
@@ -129,7 +131,7 @@ struct GemmArgs {
   const int32_t* tile_count;
   const int32_t* tile_first; // nullptr, or the index of the launch's first tile (list 2: &tile_count[0])
   const int32_t* offsets;  // [G+1] row ranges of the groups
-  int tile_rows;           // the plan's tile height (prefill: PREFILL_TILE_ROWS, or 64 for the MX8 kernel)
+  int tile_rows;           // the plan's tile height (prefill: PREFILL_TILE_ROWS, or 64 for skewed batches)
   // h = silu(g) u between the GEMMs, as h16 [rows][I] fp16 (columns permuted inside each
   // 128-column chunk, see h_pos) with, per row and 16-column block b, an exponent
   // hexp[row][b] such that h16 = fp16(h * 2^hexp) has the block's largest |h| in
@@ -174,6 +176,14 @@ struct LaunchEvents {
 // est_tiles: expected number of valid tile slots (sizes the decode split); max_tiles: grid bound.
 hipError_t launch_gemm(GemmMode mode, GemmRegime regime, int max_tiles, int est_tiles, const GemmArgs& a,
                        hipStream_t s, const LaunchEvents& ev = LaunchEvents());
+
+// Skewed prefill batches: the first tile list with the prefill GEMM (hot_mode: GATEUP_F16 or
+// DOWN) and the second with the decode GEMM (cold_mode: GATEUP_F16, DOWN or DOWN_FP4) in one
+// launch. hipErrorNotSupported (nothing launched) for shapes it does not take: hot N not a
+// multiple of 256, tile rows other than 64 or 96; the caller then launches the lists apart.
+hipError_t launch_gemm_split(GemmMode hot_mode, GemmMode cold_mode, int max_tiles, int cold_tiles,
+                             const GemmArgs& hot, const GemmArgs& cold, hipStream_t s,
+                             const LaunchEvents& ev = LaunchEvents());
 
 struct CombineArgs {
   const uint16_t* y;       // fp16 [rows_total][H] expert outputs, scaled per 16-column block

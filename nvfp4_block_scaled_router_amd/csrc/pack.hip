@@ -43,7 +43,7 @@ __global__ __launch_bounds__(256) void pack_fp4_kernel(PackArgs a) {
 }
 
 // E4M3 byte of 2^p: normal for p in [-6, 8] (exponent field p + 7), subnormal m 2^-9 for
-// p in [-9, -7]; below that 0 (outside the span the host validation admits).
+// p in [-9, -7]; below that 0 (only for an expert whose global scale is NaN).
 __device__ __forceinline__ uint8_t e4m3_pow2(int p) {
   if (p >= -6) return (uint8_t)((p + 7) << 3);
   if (p >= -9) return (uint8_t)(1 << (p + 9));
@@ -51,21 +51,34 @@ __device__ __forceinline__ uint8_t e4m3_pow2(int p) {
 }
 
 // MXFP4: per expert the largest E8M0 byte m -> gs_out[g] = 2^(m - 135) (one workgroup per
-// expert, a max over its N x K/32 scale bytes).
+// expert, a max and a min over its N x K/32 scale bytes). An expert the NVFP4 form cannot hold
+// exactly -- a byte more than MX_SCALE_SPAN below m, or the NaN byte 0xFF -- gets a NaN global
+// scale instead, so that every output that reads it is NaN rather than silently different
+// (the host validation rejects such weights before they get here).
 __global__ __launch_bounds__(256) void pack_mx_gs_kernel(PackArgs a) {
-  __shared__ int red[256];
+  __shared__ int red_max[256], red_min[256];
   const int g = blockIdx.x;
   const size_t per = (size_t)a.N * (a.K / 32);
   const uint8_t* sc = a.scales + (size_t)g * per;
-  int m = 0;
-  for (size_t i = threadIdx.x; i < per; i += blockDim.x) m = max(m, (int)sc[i]);
-  red[threadIdx.x] = m;
+  int m = 0, mn = 255;
+  for (size_t i = threadIdx.x; i < per; i += blockDim.x) {
+    m = max(m, (int)sc[i]);
+    mn = min(mn, (int)sc[i]);
+  }
+  red_max[threadIdx.x] = m;
+  red_min[threadIdx.x] = mn;
   __syncthreads();
   for (int w = 128; w > 0; w >>= 1) {
-    if ((int)threadIdx.x < w) red[threadIdx.x] = max(red[threadIdx.x], red[threadIdx.x + w]);
+    if ((int)threadIdx.x < w) {
+      red_max[threadIdx.x] = max(red_max[threadIdx.x], red_max[threadIdx.x + w]);
+      red_min[threadIdx.x] = min(red_min[threadIdx.x], red_min[threadIdx.x + w]);
+    }
     __syncthreads();
   }
-  if (threadIdx.x == 0) a.gs_out[g] = ldexpf(1.0f, red[0] - 135);
+  if (threadIdx.x == 0) {
+    const bool exact = red_max[0] != 0xFF && red_max[0] - red_min[0] <= MX_SCALE_SPAN;
+    a.gs_out[g] = exact ? ldexpf(1.0f, red_max[0] - 135) : __builtin_nanf("");
+  }
 }
 
 __global__ __launch_bounds__(256) void pack_scales_kernel(PackArgs a) {
@@ -93,7 +106,8 @@ __global__ __launch_bounds__(256) void pack_scales_kernel(PackArgs a) {
     } else if (a.mx) {
       // MXFP4: the lane's 32 columns of chunk kc are one E8M0 block, re-expressed as two
       // equal E4M3 block scales 2^(byte - m + 8) against the expert's gs = 2^(m - 135)
-      const int m = ilogbf(a.gs_out[g]) + 135;
+      const float gsv = a.gs_out[g];
+      const int m = isfinite(gsv) ? ilogbf(gsv) + 135 : 255;   // NaN gs: the expert's outputs are NaN
       const uint8_t* src = a.scales + ((size_t)g * a.N + row) * (a.K / 32);
 #pragma unroll
       for (int c = 0; c < SCALE_GROUP; ++c) {

@@ -21,14 +21,17 @@
 namespace nvmoe {
 
 // One wave per row (nvfp4_row_wave): bf16 activation rows, or the fp32 h rows of the NVFP4
-// down GEMM.
+// down GEMM; with x16 also the rows' exact fp16 decode without the global scale (the
+// operands of the prefill GEMMs).
 template <typename T>
 __global__ __launch_bounds__(256) void quant_rows_kernel(const T* __restrict__ x, int rows, int K,
                                                          uint8_t* __restrict__ packed,
-                                                         uint8_t* __restrict__ scales, float* __restrict__ gs) {
+                                                         uint8_t* __restrict__ scales, float* __restrict__ gs,
+                                                         uint16_t* __restrict__ x16) {
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= rows) return;
-  nvfp4_row_wave(x + (size_t)r * K, K, packed + (size_t)r * (K / 2), scales + (size_t)r * (K / 16), gs + r);
+  nvfp4_row_wave(x + (size_t)r * K, K, packed + (size_t)r * (K / 2), scales + (size_t)r * (K / 16), gs + r,
+                 x16 ? x16 + (size_t)r * K : nullptr);
 }
 
 // MXFP8 rows: one wave per row (mxfp8_row_wave), 4 rows per workgroup.
@@ -69,7 +72,7 @@ __global__ __launch_bounds__(256) void quant_rows_f32_kernel(const float* __rest
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= rows) return;
   wave_quant_row(x + (size_t)r * K, K, gs[r / rows_per_group], packed + (size_t)r * (K / 2),
-                 scales + (size_t)r * (K / 16));
+                 scales + (size_t)r * (K / 16), (uint16_t*)nullptr);
 }
 
 // bf16 activation rows -> fp16 rows and their factors (f16_row_wave), 4 rows per workgroup.
@@ -87,18 +90,18 @@ hipError_t launch_rows_to_f16(const uint16_t* x, int rows, int K, uint16_t* x16,
 }
 
 hipError_t launch_quant_rows_bf16(const uint16_t* x, int rows, int K, uint8_t* packed, uint8_t* scales,
-                                  float* gs, hipStream_t s) {
+                                  float* gs, hipStream_t s, uint16_t* x16) {
   if (rows <= 0) return hipSuccess;
   hipLaunchKernelGGL(quant_rows_kernel<uint16_t>, dim3((rows + 3) / 4), dim3(256), 0, s, x, rows, K, packed,
-                     scales, gs);
+                     scales, gs, x16);
   return hipGetLastError();
 }
 
 hipError_t launch_quant_rows_f32(const float* x, int rows, int K, uint8_t* packed, uint8_t* scales, float* gs,
-                                 hipStream_t s) {
+                                 hipStream_t s, uint16_t* x16) {
   if (rows <= 0) return hipSuccess;
   hipLaunchKernelGGL(quant_rows_kernel<float>, dim3((rows + 3) / 4), dim3(256), 0, s, x, rows, K, packed, scales,
-                     gs);
+                     gs, x16);
   return hipGetLastError();
 }
 

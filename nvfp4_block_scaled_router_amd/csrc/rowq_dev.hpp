@@ -1,7 +1,8 @@
 // Device helpers of the row quantisers shared by the quantiser kernels and the routing
 // kernels (which quantise the activation rows of small batches beside the routing work).
-// Every step is a comparison, a maximum, an exact power-of-two scaling or a rounding: no
-// sums, so FP contraction cannot change a byte.
+// The steps are comparisons, maxima, exact power-of-two scalings, roundings, and the
+// binary32 products and quotients of the NVFP4 rule (6 gs, E4M3(s) gs, |v| / d); no product
+// feeds an addition, so FP contraction cannot fuse anything and change a byte.
 #pragma once
 #include "common.hpp"
 
@@ -30,13 +31,24 @@ __device__ __forceinline__ void load16(const float* p, float* v) {
 }
 
 // Nearest E2M1 magnitude code to r >= 0 (ties to the even code), saturating at 6.
+// Signed E2M1 value of a code (sign in bit 3): 0, 0.5, 1, 1.5, 2, 3, 4, 6.
+__device__ __forceinline__ float e2m1_value(uint32_t c) {
+  const uint32_t m = c & 7u;   // m >= 2: (1 or 1.5) 2^(m/2 - 1); m = 1: 0.5; m = 0: 0
+  const float v = m < 2u ? 0.5f * (float)m : __builtin_ldexpf((m & 1u) ? 1.5f : 1.0f, (int)(m >> 1) - 1);
+  return (c & 8u) ? -v : v;
+}
+
 __device__ __forceinline__ uint32_t e2m1_encode_rne_sat(float r) {
   return (uint32_t)(r > 0.25f) + (uint32_t)(r >= 0.75f) + (uint32_t)(r > 1.25f) + (uint32_t)(r >= 1.75f) +
          (uint32_t)(r > 2.5f) + (uint32_t)(r >= 3.5f) + (uint32_t)(r > 5.0f);
 }
 
-// Quantise one 16-element block with global scale gs; writes 8 code bytes and 1 scale byte.
-__device__ __forceinline__ void quant_block(const float* v, float gs, uint8_t* packed, uint8_t* scale) {
+// Quantise one 16-element block with global scale gs; writes 8 code bytes and 1 scale byte,
+// and with x16 != nullptr the 16 decoded values without the global scale, E2M1(code) x
+// E4M3(s), as fp16 (at most 6 significant bits in [2^-10, 2688]: exact), the operands of the
+// fp16 MFMAs of the prefill GEMMs, whose epilogue applies gs.
+__device__ __forceinline__ void quant_block(const float* v, float gs, uint8_t* packed, uint8_t* scale,
+                                            uint16_t* x16 = nullptr) {
   float ab = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) ab = fmaxf(ab, fabsf(v[i]));
@@ -58,6 +70,19 @@ __device__ __forceinline__ void quant_block(const float* v, float gs, uint8_t* p
   }
   *(u32x2*)packed = u32x2{lo, hi};
   *scale = (uint8_t)s;
+  if (x16) {
+    const float sv = e4m3_to_f32(s);
+    uint32_t q[8];
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+      const uint32_t c0 = ((i < 8 ? lo : hi) >> (4 * (i & 7))) & 15u, c1 = ((i < 8 ? lo : hi) >> (4 * ((i + 1) & 7))) & 15u;
+      const uint32_t h0 = __builtin_bit_cast(uint16_t, (_Float16)(e2m1_value(c0) * sv));
+      const uint32_t h1 = __builtin_bit_cast(uint16_t, (_Float16)(e2m1_value(c1) * sv));
+      q[i / 2] = h0 | (h1 << 16);
+    }
+    *(u32x4*)x16 = u32x4{q[0], q[1], q[2], q[3]};
+    *(u32x4*)(x16 + 8) = u32x4{q[4], q[5], q[6], q[7]};
+  }
 }
 
 template <typename T>
@@ -76,22 +101,24 @@ __device__ __forceinline__ float wave_row_absmax(const T* row, int K) {
 }
 
 template <typename T>
-__device__ __forceinline__ void wave_quant_row(const T* row, int K, float gs, uint8_t* packed, uint8_t* scales) {
+__device__ __forceinline__ void wave_quant_row(const T* row, int K, float gs, uint8_t* packed, uint8_t* scales,
+                                               uint16_t* x16) {
   const int lane = threadIdx.x & (WAVE - 1);
   for (int b = lane; b < K / 16; b += WAVE) {
     float v[16];
     load16(row + (size_t)b * 16, v);
-    quant_block(v, gs, packed + (size_t)b * 8, scales + b);
+    quant_block(v, gs, packed + (size_t)b * 8, scales + b, x16 ? x16 + (size_t)b * 16 : nullptr);
   }
 }
 
 // One wave quantises one row: its global scale gs = max|x| / 2688 (written to *gs_out by
-// lane 0), then its 16-column blocks.
+// lane 0), then its 16-column blocks (and, with x16, their decoded fp16 values).
 template <typename T>
-__device__ __forceinline__ void nvfp4_row_wave(const T* row, int K, uint8_t* packed, uint8_t* scales, float* gs_out) {
+__device__ __forceinline__ void nvfp4_row_wave(const T* row, int K, uint8_t* packed, uint8_t* scales, float* gs_out,
+                                               uint16_t* x16 = nullptr) {
   const float g = wave_row_absmax(row, K) / 2688.0f;
   if ((threadIdx.x & (WAVE - 1)) == 0) *gs_out = g;
-  wave_quant_row(row, K, g, packed, scales);
+  wave_quant_row(row, K, g, packed, scales, x16);
 }
 
 // MXFP8 rows (the W4A8 profile's activations): per 32 consecutive k one E8M0 scale 2^X with

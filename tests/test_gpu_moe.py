@@ -312,3 +312,28 @@ def test_max_tokens_sampled():
     permutation of 524288 rows) bit-exact, sampled outputs."""
     cfg = synth.MoeConfig("max-tokens", T=65536, H=128, I=128, E=64, k=8, seed=34)
     _run_and_check(Case(cfg, tokens=synth.token_sample(cfg, 24)))
+
+
+def test_mxfp4_span_too_wide_is_loud():
+    """An MXFP4 expert whose E8M0 bytes span more than the NVFP4 form holds exactly (here one
+    byte 20 binades under the expert's largest) is rejected by the host validation, and if
+    packed anyway every output that reads it is NaN; the other tokens still match the oracle."""
+    import nvfp4_block_scaled_router_amd as m
+    cfg = synth.MoeConfig("mx-wide-span", T=40, H=256, I=128, E=4, k=1, seed=81, wfmt="mxfp4")
+    case = Case(cfg)
+    W1 = case.W[0]
+    codes, scales = W1[0].copy(), W1[1].copy()
+    scales[0, 3, 2] = int(scales[0].max()) - 20
+    desc = m.make_desc(cfg.H, cfg.I, cfg.E, cfg.k, cfg.T, weights="mxfp4")
+    t = m.nvfp4_tensor(codes.ctypes.data, scales.ctypes.data, None)
+    assert m.moe_validate_weights_host(desc, t, 0) == m.MOE_ERR_WEIGHT
+    case.dev_w[0] = [up(codes), up(scales), None]
+    L = case.layer()
+    out = L(bf16(case.x), up(case.logits))
+    torch.cuda.synchronize()
+    o = out.float().cpu().numpy()
+    on0 = case.ids_ref[:, 0] == 0
+    assert on0.any() and (~on0).any()
+    assert np.isnan(o[on0]).all(), "outputs of the too-wide expert must be NaN"
+    ref = case.reference()
+    check_out(out[torch.from_numpy(np.where(~on0)[0]).long().to(DEV)], ref["out"][~on0], cfg.name + " other experts")
