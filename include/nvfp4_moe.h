@@ -269,14 +269,13 @@ int moe_run(const moe_plan_t* plan, const void* packed, int32_t T, const uint16_
             void* workspace, size_t workspace_bytes, void* stream);
 
 /* Stages of moe_run, in launch order (for moe_run_timed). */
-#define MOE_STAGE_QUANT 0      /* activation preparation of prefill-regime batches: NVFP4
-                                  quantisation (W4A4), MXFP8 quantisation (W4A8) or the exact
-                                  power-of-two rescale of bf16 rows into fp16 (W4A16) */
-#define MOE_STAGE_ROUTE 1      /* top-k, counts, offsets, permutation, tile list; for
-                                  decode-regime batches also the activation preparation (NVFP4
-                                  or MXFP8 quantisation of x, or its fp16 rescale from 256
-                                  routed rows up), by extra workgroups of the first routing
-                                  launch */
+#define MOE_STAGE_QUANT 0      /* empty: the activation preparation runs in the ROUTE stage
+                                  (the index is kept for the stage layout) */
+#define MOE_STAGE_ROUTE 1      /* top-k, counts, offsets, permutation, tile list, and the
+                                  activation preparation (NVFP4 quantisation of x with, for
+                                  prefill-regime batches, its exact fp16 decode; MXFP8
+                                  quantisation; or the exact power-of-two rescale of bf16 rows
+                                  into fp16) by extra workgroups of the first routing launch */
 #define MOE_STAGE_GATE_UP 2    /* grouped gate/up GEMM + SwiGLU */
 #define MOE_STAGE_DOWN 3       /* grouped down GEMM, with what prepares h for it in
                                   prefill-regime batches: the h row quantisation

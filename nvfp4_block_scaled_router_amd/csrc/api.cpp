@@ -373,16 +373,9 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
   const GemmMode gu_mode = mx8 ? GEMM_GATEUP_MX8
                           : fp4 ? (decode ? GEMM_GATEUP_FP4 : GEMM_GATEUP_F16)
                                 : (decode && T * k < DECODE_F16_ROWS) ? GEMM_GATEUP_BF16 : GEMM_GATEUP_F16;
+  // the activation preparation runs in extra workgroups of the routing stage's first launch
+  // (one wave per row); the QUANT stage is empty
   if ((e = mark(ev, 2 * MOE_STAGE_QUANT, s)) != hipSuccess) return (int)e;
-  // decode batches convert x in extra workgroups of the routing stage's first launch
-  // instead (one launch fewer)
-  if (mx8 && !decode)
-    e = launch_mxfp8_rows_bf16(x, T, H, xq, xs, s);
-  else if (fp4 && !decode)
-    e = launch_quant_rows_bf16(x, T, H, xq, xs, xg, s, x16);
-  else if (gu_mode == GEMM_GATEUP_F16 && !decode)
-    e = launch_rows_to_f16(x, T, H, x16, xg, s);
-  if (e != hipSuccess) return (int)e;
   if ((e = mark(ev, 2 * MOE_STAGE_QUANT + 1, s)) != hipSuccess) return (int)e;
 
   // prefill batches averaging at most 64 rows per expert: experts with few rows (skewed
@@ -409,8 +402,7 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
   ra.topk_group = d.topk_group;
   ra.renorm = d.renormalize;
   ra.scaling = d.routed_scaling;
-  ra.side = !decode                       ? SIDE_NONE
-            : mx8                           ? SIDE_MXFP8
+  ra.side = mx8                           ? SIDE_MXFP8
             : fp4                           ? SIDE_NVFP4
             : gu_mode == GEMM_GATEUP_F16    ? SIDE_F16
                                             : SIDE_NONE;
@@ -419,7 +411,7 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
   ra.side_q = xq;
   ra.side_s = xs;
   ra.side_f = xg;
-  ra.side_h = x16;
+  ra.side_h = (fp4 && decode) ? nullptr : x16;   // NVFP4 x of prefill batches: also its fp16 decode
   PlanArgs pa;
   pa.ids = ra.ids;
   pa.T = T;

@@ -27,7 +27,8 @@ struct RouteArgs {
   // optional side job on the bf16 activation rows side_x [T][side_K], run by extra
   // workgroups of the first routing launch (one launch fewer for small batches):
   // SIDE_MXFP8: codes side_q [T][side_K] and E8M0 scales side_s [T][side_K/32];
-  // SIDE_NVFP4: codes side_q [T][side_K/2], E4M3 scales side_s [T][side_K/16], global scales side_f [T];
+  // SIDE_NVFP4: codes side_q [T][side_K/2], E4M3 scales side_s [T][side_K/16], global scales side_f [T]
+  //   (and, with side_h set, the rows' exact fp16 decode without the global scale);
   // SIDE_F16: fp16 rows side_h [T][side_K] and their factors side_f [T]
   int side;
   const uint16_t* side_x;
@@ -69,15 +70,12 @@ bool plan_small_ok(int T, int k);
 // E2M1 x E4M3 per element ([rows][K], plain column order).
 hipError_t launch_quant_rows_bf16(const uint16_t* x, int rows, int K, uint8_t* packed, uint8_t* scales,
                                   float* gs, hipStream_t s, uint16_t* x16 = nullptr);
-// MXFP8 rows (codes [rows][K], E8M0 scales [rows][K/32]) from bf16 or fp32 rows.
-hipError_t launch_mxfp8_rows_bf16(const uint16_t* x, int rows, int K, uint8_t* codes, uint8_t* scales,
-                                  hipStream_t s);
+// MXFP8 rows (codes [rows][K], E8M0 scales [rows][K/32]) from fp32 rows (h before the W4A8 down
+// GEMM); the activation rows are converted by the routing launch (RouteArgs side jobs).
 hipError_t launch_mxfp8_rows_f32(const float* x, int rows, int K, uint8_t* codes, uint8_t* scales, hipStream_t s);
 // fp32 rows (h before the NVFP4 down GEMM), each with its own global scale.
 hipError_t launch_quant_rows_f32(const float* x, int rows, int K, uint8_t* packed, uint8_t* scales, float* gs,
                                  hipStream_t s, uint16_t* x16 = nullptr);
-// bf16 rows -> fp16 rows scaled by 2^p (p per row puts max|x| in [2^14, 2^15)); xf = 2^-p.
-hipError_t launch_rows_to_f16(const uint16_t* x, int rows, int K, uint16_t* x16, float* xf, hipStream_t s);
 hipError_t launch_quant_groups_f32(const float* x, int groups, int rows_per_group, int K, uint8_t* packed,
                                    uint8_t* scales, float* gs, hipStream_t s);
 

@@ -75,20 +75,6 @@ __global__ __launch_bounds__(256) void quant_rows_f32_kernel(const float* __rest
                  scales + (size_t)r * (K / 16), (uint16_t*)nullptr);
 }
 
-// bf16 activation rows -> fp16 rows and their factors (f16_row_wave), 4 rows per workgroup.
-__global__ __launch_bounds__(256) void rows_to_f16_kernel(const uint16_t* __restrict__ x, int rows, int K,
-                                                          uint16_t* __restrict__ x16, float* __restrict__ xf) {
-  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (r >= rows) return;
-  f16_row_wave(x + (size_t)r * K, K, x16 + (size_t)r * K, xf + r, threadIdx.x & (WAVE - 1));
-}
-
-hipError_t launch_rows_to_f16(const uint16_t* x, int rows, int K, uint16_t* x16, float* xf, hipStream_t s) {
-  if (rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(rows_to_f16_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, x, rows, K, x16, xf);
-  return hipGetLastError();
-}
-
 hipError_t launch_quant_rows_bf16(const uint16_t* x, int rows, int K, uint8_t* packed, uint8_t* scales,
                                   float* gs, hipStream_t s, uint16_t* x16) {
   if (rows <= 0) return hipSuccess;
@@ -102,13 +88,6 @@ hipError_t launch_quant_rows_f32(const float* x, int rows, int K, uint8_t* packe
   if (rows <= 0) return hipSuccess;
   hipLaunchKernelGGL(quant_rows_kernel<float>, dim3((rows + 3) / 4), dim3(256), 0, s, x, rows, K, packed, scales,
                      gs, x16);
-  return hipGetLastError();
-}
-
-hipError_t launch_mxfp8_rows_bf16(const uint16_t* x, int rows, int K, uint8_t* codes, uint8_t* scales,
-                                  hipStream_t s) {
-  if (rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(mxfp8_rows_kernel<uint16_t>, dim3((rows + 3) / 4), dim3(256), 0, s, x, rows, K, codes, scales);
   return hipGetLastError();
 }
 

@@ -16,9 +16,17 @@
 
 namespace nvmoe {
 
-// 256 threads = 16 rows = 16 tokens per workgroup.
+__device__ __forceinline__ void side_rows(const RouteArgs& a, int j);
+
+// 256 threads = 16 rows = 16 tokens per workgroup; with a side job, the workgroups past the
+// routing ones convert the activation rows (side_rows).
 template <int EPR>
 __global__ __launch_bounds__(256) void route_row_kernel(RouteArgs a) {
+  const int nb = (a.T + 15) / 16;
+  if ((int)blockIdx.x >= nb) {
+    side_rows(a, blockIdx.x - nb);
+    return;
+  }
   const int t = blockIdx.x * 16 + (threadIdx.x >> 4);
   if (t >= a.T) return;   // whole rows leave together
   route_token_row<EPR>(a.logits, a.E, a.k, a.score, t, a.ids, a.w, a.ids_user, a.w_user, nullptr);
@@ -26,6 +34,11 @@ __global__ __launch_bounds__(256) void route_row_kernel(RouteArgs a) {
 
 template <int EPL>
 __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
+  const int nb = (a.T + 3) / 4;
+  if ((int)blockIdx.x >= nb) {
+    side_rows(a, blockIdx.x - nb);
+    return;
+  }
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= a.T) return;
   route_token<EPL>(a.logits, a.E, a.k, a.score, a.ids, a.w, a.ids_user, a.w_user, t);
@@ -202,8 +215,9 @@ __device__ __forceinline__ void side_rows(const RouteArgs& a, int j) {
   const uint16_t* row = a.side_x + (size_t)t * K;
   if (a.side == SIDE_MXFP8)
     mxfp8_row_wave(row, K, a.side_q + (size_t)t * K, a.side_s + (size_t)t * (K / 32), lane);
-  else if (a.side == SIDE_NVFP4)
-    nvfp4_row_wave(row, K, a.side_q + (size_t)t * (K / 2), a.side_s + (size_t)t * (K / 16), a.side_f + t);
+  else if (a.side == SIDE_NVFP4)   // with side_h also the rows' fp16 decode (prefill batches)
+    nvfp4_row_wave(row, K, a.side_q + (size_t)t * (K / 2), a.side_s + (size_t)t * (K / 16), a.side_f + t,
+                   a.side_h ? a.side_h + (size_t)t * K : nullptr);
   else
     f16_row_wave(row, K, a.side_h + (size_t)t * K, a.side_f + t, lane);
 }
@@ -432,8 +446,8 @@ bool plan_small_ok(int T, int k) { return T <= 64 && T * k <= 4096; }
 
 template <int EPL>
 static hipError_t launch_route_plan_t(const RouteArgs& r, const PlanArgs& p, int32_t* scratch, hipStream_t s) {
-  // the side job rides on the first launch that can carry it (the general router's, or the
-  // one-workgroup plan's), else it gets a launch of its own
+  // the side job rides on the first launch: the general router's, the one-workgroup plan's
+  // or the per-token router's
   bool side = r.side != SIDE_NONE;
   if (r.general) {
     hipLaunchKernelGGL(route_general_kernel<EPL>, dim3((r.T + 3) / 4 * (side ? 2 : 1)), dim3(256), 0, s, r);
@@ -444,18 +458,13 @@ static hipError_t launch_route_plan_t(const RouteArgs& r, const PlanArgs& p, int
                        plan_small_lds_bytes(p.T * p.k, p.E, p.G), s, r, p);
     return hipGetLastError();
   }
-  if (side) {
-    const hipError_t e =
-        r.side == SIDE_MXFP8   ? launch_mxfp8_rows_bf16(r.side_x, r.T, r.side_K, r.side_q, r.side_s, s)
-        : r.side == SIDE_NVFP4 ? launch_quant_rows_bf16(r.side_x, r.T, r.side_K, r.side_q, r.side_s, r.side_f, s)
-                               : launch_rows_to_f16(r.side_x, r.T, r.side_K, r.side_h, r.side_f, s);
-    if (e != hipSuccess) return e;
-  }
+  // the side job's workgroups (4 rows each) follow the routing ones in the same launch
+  const int side_wgs = side ? (r.T + 3) / 4 : 0;
   if (r.general) {
   } else if constexpr (EPL <= 4) {
-    hipLaunchKernelGGL(route_row_kernel<EPL * 4>, dim3((r.T + 15) / 16), dim3(256), 0, s, r);
+    hipLaunchKernelGGL(route_row_kernel<EPL * 4>, dim3((r.T + 15) / 16 + side_wgs), dim3(256), 0, s, r);
   } else {
-    hipLaunchKernelGGL(route_kernel<EPL>, dim3((r.T + 3) / 4), dim3(256), 0, s, r);
+    hipLaunchKernelGGL(route_kernel<EPL>, dim3((r.T + 3) / 4 + side_wgs), dim3(256), 0, s, r);
   }
   const int nb = (p.T + PLAN_BLOCK - 1) / PLAN_BLOCK;
   int32_t* local_rank = scratch;
