@@ -78,6 +78,8 @@ class Oracle:
         L.orc_dequant_rows.argtypes = [_vp, _vp, _vp, _i64, _i32, _vp]
         L.orc_bf16_rows.argtypes = [_vp, _i64, _vp]
         L.orc_decode_proj.argtypes = [ctypes.POINTER(ProjSet), _i32, _i32, _i32, _i32, _vp]
+        L.orc_fp8_rows_quantize.argtypes = [_vp, _i64, _i32, _vp, _vp]
+        L.orc_fp8_rows.argtypes = [_vp, _vp, _i64, _i32, _vp]
         self.L = L
         self.path = path
 
@@ -121,6 +123,24 @@ class Oracle:
         scales = np.zeros((rows, K // 32), np.uint8)
         self.L.orc_mxfp8_quantize(x.ctypes.data, rows, K, codes.ctypes.data, scales.ctypes.data)
         return codes, scales
+
+    def fp8_rows_quantize(self, x: np.ndarray):
+        """float32 [rows][K] -> (E4M3 codes u8 [rows][K], per-row FP32 scales [rows])."""
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        rows, K = x.shape
+        codes = np.zeros((rows, K), np.uint8)
+        scale = np.zeros(rows, np.float32)
+        self.L.orc_fp8_rows_quantize(x.ctypes.data, rows, K, codes.ctypes.data, scale.ctypes.data)
+        return codes, scale
+
+    def fp8_rows(self, codes: np.ndarray, scale: np.ndarray) -> np.ndarray:
+        """Exact FP64 decode of per-row-scaled FP8 rows."""
+        codes = np.ascontiguousarray(codes, dtype=np.uint8)
+        scale = np.ascontiguousarray(scale, dtype=np.float32)
+        rows, K = codes.shape
+        out = np.empty((rows, K), np.float64)
+        self.L.orc_fp8_rows(codes.ctypes.data, scale.ctypes.data, rows, K, out.ctypes.data)
+        return out
 
     def mxfp8(self, code: int, scale: int) -> float:
         return self.L.orc_mxfp8(code, scale)
@@ -216,10 +236,10 @@ class Oracle:
         return ps
 
     def expert_ffn(self, W1, W2, g: int, x: np.ndarray, swiglu_limit: Optional[float] = None,
-                   hq: bool = False) -> np.ndarray:
+                   hq: int = 0) -> np.ndarray:
         """W1 = (packed [G][2I][H/2], scales [G][2I][H/16], gs [G]); W2 likewise [G][H][I/..].
         swiglu_limit: None for the plain SwiGLU, else the clamp limit L >= 0; hq: the down
-        projection takes h row-quantised to NVFP4 (True / 1) or MXFP8 (2)."""
+        projection takes h row-quantised to NVFP4 (True / 1), MXFP8 (2) or per-row FP8 (3)."""
         H = W1[0].shape[-1] * 2
         I = W2[0].shape[-1] * 2
         x = np.ascontiguousarray(x, dtype=np.float64)

@@ -6,10 +6,11 @@ functions of ``oracle.c`` in the order the method runs them:
 1. route the FP32 logits (top-k, renormalised weights; or the generalised router of the
    variant layers), then count/offset/permute;
 2. activations: bf16 decoded exactly, or (W4A4) NVFP4 row-quantised with the
-   binary32 quantizer and decoded exactly;
+   binary32 quantizer and decoded exactly, or MXFP8 (act "mxfp8", MXFP4 weights), or FP8
+   with one scale per row (act "fp8", NVFP4 weights: the W4A8 path on NVFP4);
 3. per token, the k expert SwiGLU MLPs in FP64 (act "nvfp4_all": h row-quantised the
-   same way before the down projection; act "mxfp8": x and h MXFP8), weighted sum, plus
-   the shared expert with weight 1.
+   same way before the down projection; "mxfp8" and "fp8": h in x's format), weighted
+   sum, plus the shared expert with weight 1.
 
 Weights are the synth draws quantised per expert projection by the oracle's
 own quantizer (one global scale per expert projection).
@@ -111,6 +112,10 @@ def _prepare(cfg, x_bf16, logits, tokens, o):
         xq, xs = o.mxfp8_quantize(o.bf16_rows(x_bf16).astype(np.float32))
         res.update(xq=xq, xs=xs)
         res["x_rows"] = o.mxfp8_rows(xq[tokens], xs[tokens])
+    elif cfg.act == "fp8":                               # NVFP4 weights, FP8 x (and h) per row
+        xq, xg = o.fp8_rows_quantize(o.bf16_rows(x_bf16).astype(np.float32))
+        res.update(xq=xq, xg=xg)
+        res["x_rows"] = o.fp8_rows(xq[tokens], xg[tokens])
     elif cfg.act in ("nvfp4", "nvfp4_all"):
         xq, xs, xg = o.quantize(o.bf16_rows(x_bf16).astype(np.float32), rows_per_gs=1)
         res.update(xq=xq, xs=xs, xg=xg)
@@ -130,10 +135,14 @@ def forward(cfg: synth.MoeConfig, x_bf16: np.ndarray, logits: np.ndarray, W1, W2
     o = o or default()
     res = _prepare(cfg, x_bf16, logits, tokens, o)
     x_rows = res.pop("x_rows")
-    hq = {"nvfp4_all": 1, "mxfp8": 2}.get(cfg.act, 0)
+    hq = HQ.get(cfg.act, 0)
     res["out"] = o.moe_tokens(W1, W2, WS1, WS2, res["tokens"], x_rows, res["ids"], res["w"], cfg.swiglu_limit,
                               hq=hq)
     return res
+
+
+# h quantisation of each activation format: NVFP4 rows (1), MXFP8 (2), per-row FP8 (3)
+HQ = {"nvfp4_all": 1, "mxfp8": 2, "fp8": 3}
 
 
 def _swiglu(g: np.ndarray, u: np.ndarray, limit: Optional[float]) -> np.ndarray:
@@ -148,8 +157,11 @@ def _swiglu(g: np.ndarray, u: np.ndarray, limit: Optional[float]) -> np.ndarray:
 
 def _quantize_h(h: np.ndarray, hq: int, o: Oracle) -> np.ndarray:
     """h rows rounded to binary32 and quantised as forward()'s MLP does: NVFP4 with one
-    global scale per row (hq 1) or MXFP8 (hq 2), returned as their exact FP64 decode."""
+    global scale per row (hq 1), MXFP8 (hq 2) or FP8 with one scale per row (hq 3),
+    returned as their exact FP64 decode."""
     h32 = h.astype(np.float32)
+    if hq == 3:
+        return o.fp8_rows(*o.fp8_rows_quantize(h32))
     if hq == 2:
         return o.mxfp8_rows(*o.mxfp8_quantize(h32))
     return o.dequant_rows(*o.quantize(h32, rows_per_gs=1))
@@ -177,7 +189,7 @@ def forward_by_expert(cfg: synth.MoeConfig, x_bf16: np.ndarray, logits: np.ndarr
     x_rows = res.pop("x_rows")                            # decoded inputs of `tokens`, in that order
     pos = np.full(T, -1, np.int64)                        # token -> its row in x_rows / out
     pos[tokens] = np.arange(len(tokens))
-    hq = {"nvfp4_all": 1, "mxfp8": 2}.get(cfg.act, 0)
+    hq = HQ.get(cfg.act, 0)
     routed_limit = cfg.swiglu_limit
 
     def ffn(Wa, Wb, g, X, limit):

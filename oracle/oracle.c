@@ -256,6 +256,42 @@ void orc_mxfp8_quantize(const float* x, int64_t rows, int K, uint8_t* codes, uin
   }
 }
 
+/* ------------------------------------------- FP8 rows with a per-row scale */
+
+/* FP8 row quantiser of the NVFP4-weight W4A8 path ([b12x] "What's in here": the unified
+ * dynamic path's w4a8_nvfp4 variant, NVFP4 weights with FP8 activations; the pages name it
+ * without its activation rule). Reading: E4M3fn codes with one FP32 scale per row taken
+ * from the row's largest magnitude, which maps onto E4M3's largest value 448 -- the FP8
+ * rule the same project applies to its KV rows ([megamoe] archived CORRECTNESS_BACKLOG,
+ * section 7 "NVFP4 Quantization": FP8 KV quantisation with a per-row float32 scale from the
+ * row amax), here applied to the activation rows. Per row r, in binary32:
+ *   A      = max |x| over the row                           (exact)
+ *   s      = A / 448                                        (binary32 division)
+ *   code_k = sign(x_k) << 7 | (s == 0 ? 0 : E4M3_nearest(|x_k| / s))
+ *            (binary32 division; ratios above 448 saturate to 448, ties to the even code)
+ * Outputs codes [rows][K], scale [rows]. */
+void orc_fp8_rows_quantize(const float* x, int64_t rows, int K, uint8_t* codes, float* scale) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    const float* xr = x + (size_t)r * K;
+    float A = 0.0f;
+    for (int k = 0; k < K; ++k)
+      if (fabsf(xr[k]) > A) A = fabsf(xr[k]);
+    const float s = A / 448.0f;
+    scale[r] = s;
+    for (int k = 0; k < K; ++k) {
+      const uint32_t sign = signbit(xr[k]) ? 0x80u : 0u;
+      codes[(size_t)r * K + k] = (uint8_t)(sign | (s == 0.0f ? 0u : orc_e4m3_encode(fabsf(xr[k]) / s)));
+    }
+  }
+}
+
+/* Decoded FP8 rows: x[r][k] = E4M3fn(codes[r][k]) * scale[r] (exact in FP64). */
+void orc_fp8_rows(const uint8_t* codes, const float* scale, int64_t rows, int K, double* x) {
+  for (int64_t r = 0; r < rows; ++r)
+    for (int k = 0; k < K; ++k) x[(size_t)r * K + k] = orc_e4m3fn(codes[(size_t)r * K + k]) * (double)scale[r];
+}
+
 /* ----------------------------------------------------------------- routing */
 
 /* Top-k routing of T tokens over E experts.
@@ -457,7 +493,8 @@ static double proj_weight(const orc_proj_set* P, int second, int g, int N, int K
  * rounded to binary32, quantised by orc_quantize as one row with its own global
  * scale (per row, as for x), and y uses its exact decode. hq == 2 quantises the
  * binary32 h with the MXFP8 quantiser instead (the W4A8 profile: both expert GEMMs
- * take MXFP8 activations, [b12x] "DeepSeek V4 Flash 0731 MoE reproduction").
+ * take MXFP8 activations, [b12x] "DeepSeek V4 Flash 0731 MoE reproduction"); hq == 3
+ * with the per-row FP8 quantiser (orc_fp8_rows_quantize: the NVFP4-weight W4A8 path).
  * Weights are decoded element by element in the set's format (orc_weight or
  * orc_weight_mx). */
 /* h = SwiGLU(W1 x) of one expert before any quantisation (the first half of the MLP). */
@@ -481,7 +518,16 @@ void orc_expert_ffn_q(const orc_proj_set* P, int g, int H, int I, const double* 
                       int clamp, double limit, int hq) {
   double* h = (double*)malloc(sizeof(double) * (size_t)I);
   orc_expert_h(P, g, H, I, x, h, clamp, limit);
-  if (hq == 2) {   /* MXFP8 h (W4A8 profile) */
+  if (hq == 3) {   /* FP8 h with a per-row scale (the NVFP4-weight W4A8 path) */
+    float* h32 = (float*)malloc(sizeof(float) * (size_t)I);
+    uint8_t* hc = (uint8_t*)malloc((size_t)I);
+    float hs;
+    for (int i = 0; i < I; ++i) h32[i] = (float)h[i];
+    orc_fp8_rows_quantize(h32, 1, I, hc, &hs);
+    orc_fp8_rows(hc, &hs, 1, I, h);
+    free(h32);
+    free(hc);
+  } else if (hq == 2) {   /* MXFP8 h (W4A8 profile) */
     float* h32 = (float*)malloc(sizeof(float) * (size_t)I);
     uint8_t* hc = (uint8_t*)malloc((size_t)I);
     uint8_t* hs = (uint8_t*)malloc((size_t)I / 32);

@@ -84,6 +84,7 @@ class MoeConfig:
     shared: int = 0         # always-on shared experts (0 or 1), intermediate size I
     act: str = "bf16"       # "bf16" (W4A16) | "nvfp4" (row-quantised x, W4A4) | "nvfp4_all" (x and h)
                             # | "mxfp8" (x and h MXFP8, with MXFP4 weights: W4A8)
+                            # | "fp8" (x and h FP8 with a per-row scale, NVFP4 weights: W4A8)
     zipf_s: float = 0.0     # > 0: add -s*ln(rank_e) to every logit of expert e
     seed: int = 0
     # router / activation variants (the defaults are the plain layer)
@@ -157,6 +158,12 @@ def deepseek_v4_flash_w4a8(T: int = 64) -> MoeConfig:
     """The DeepSeek-V4-Flash layer in its W4A8 profile: MXFP4 weights with MXFP8 activations
     (x and h)."""
     return dataclasses.replace(deepseek_v4_flash(T), name=f"deepseek-v4-flash-w4a8-t{T}", act="mxfp8")
+
+
+def qwen3_w4a8(T: int) -> MoeConfig:
+    """The Qwen3-30B-A3B layer on the W4A8 path with NVFP4 weights: x and h FP8 with one
+    scale per row."""
+    return MoeConfig(f"qwen3-30b-a3b-w4a8-t{T}", T=T, H=2048, I=768, E=128, k=8, act="fp8", seed=600 + T % 97)
 
 
 SHARING_LEVELS = (0.0, 0.2, 0.4, 0.6, 0.8, 1.0)

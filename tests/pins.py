@@ -677,6 +677,121 @@ def pin_ffn_mxfp8_textbook(o):
             assert np.allclose(y, ref, rtol=1e-12, atol=1e-14 * np.abs(ref).max()), np.abs(y - ref).max()
 
 
+# ------------------------------------------- FP8 rows with a per-row scale (W4A8 on NVFP4)
+
+def quantize_fp8_row_brute(row: np.ndarray):
+    """Per-row FP8 quantiser written from its definition, independently of the oracle:
+    s = float32(max|x|) / 448 in float32, codes by PyTorch's round-to-nearest-even
+    float8_e4m3fn conversion of float32(|x| / s) (ratios of 448 and above: 0x7E), sign kept,
+    all codes 0 when s is 0; returns (codes, s, exact FP64 decode)."""
+    row = np.asarray(row, np.float32)
+    A = np.float32(np.max(np.abs(row))) if row.size else np.float32(0)
+    s = np.float32(A / np.float32(448.0))
+    if s == 0:
+        codes = np.where(np.signbit(row), 0x80, 0).astype(np.uint8)
+    else:
+        r = (np.abs(row) / s).astype(np.float32)
+        enc = np.where(r >= 448, 0x7E, e4m3_encode_torch(np.minimum(r, np.float32(448))))
+        codes = enc.astype(np.uint8) | np.where(np.signbit(row), 0x80, 0).astype(np.uint8)
+    e4 = e4m3_table_torch()
+    return codes, s, e4[codes] * np.float64(s)
+
+
+def fp8_rows_fixture():
+    rng = np.random.default_rng(61)
+    rows = [rng.standard_normal(96).astype(np.float32) for _ in range(4)]
+    rows.append(np.zeros(96, np.float32))                                    # all zero: s = 0
+    r = np.full(96, -0.0, np.float32); rows.append(r)                        # negative zeros
+    r = np.zeros(96, np.float32); r[17] = -3.0; r[50] = 1e-6; rows.append(r)  # tiny next to the max
+    rows.append((rng.standard_normal(96) * 1e30).astype(np.float32))         # large
+    rows.append((rng.standard_normal(96) * 1e-30).astype(np.float32))        # small (s subnormal-free)
+    r = rng.standard_normal(96).astype(np.float32); r[3] = 7.0; r[4] = -7.0; rows.append(r)  # tied maxima
+    rows.append(np.ldexp(1.0, rng.integers(-12, 4, 96)).astype(np.float32) * rng.choice([-1, 1], 96))  # powers of 2
+    r = rng.standard_normal(96).astype(np.float32); r[0] = 5.0; r[-1] = -9.0; rows.append(r)  # max at either end
+    return np.stack(rows)
+
+
+def pin_fp8_rows_quantize(o):
+    """Codes and scales bit-exact against the definition written in the test; the row's
+    largest magnitude always encodes as 448 (0x7E), and a zero row has scale 0."""
+    x = fp8_rows_fixture()
+    codes, s = o.fp8_rows_quantize(x)
+    for i, row in enumerate(x):
+        c, si, _ = quantize_fp8_row_brute(row)
+        assert s[i] == si, (i, s[i], si)
+        assert np.array_equal(codes[i], c), (i, np.flatnonzero(codes[i] != c))
+        if si > 0:
+            assert (codes[i][np.abs(row) == np.abs(row).max()] & 0x7F == 0x7E).all(), i
+    assert s[4] == 0 and not codes[4].any()
+    assert s[5] == 0 and (codes[5] == 0x80).all()
+
+
+def pin_fp8_rows_decode_and_bound(o):
+    """The decode is E4M3 (PyTorch's decoder) times the row scale, and it lies within E4M3's
+    rounding bound of x: relative 2^-4 for |x| >= 2^-6 s, absolute 2^-10 s below that."""
+    x = fp8_rows_fixture()
+    codes, s = o.fp8_rows_quantize(x)
+    dec = o.fp8_rows(codes, s)
+    e4 = e4m3_table_torch()
+    assert np.array_equal(dec, e4[codes] * s[:, None].astype(np.float64))
+    for i in range(x.shape[0]):
+        si = float(s[i])
+        xi = x[i].astype(np.float64)
+        big = np.abs(xi) >= si * 2.0 ** -6
+        err = np.abs(dec[i] - xi)
+        tol_rel = 2.0 ** -4 * np.abs(xi) * (1 + 1e-6)
+        assert (err[big] <= tol_rel[big] + 1e-300).all(), i
+        assert (err[~big] <= si * 2.0 ** -10 * (1 + 1e-6)).all(), i
+
+
+def pin_ffn_fp8_textbook(o):
+    """W4A8 on NVFP4 weights: the input and h quantised to FP8 per row,
+    W2 . Q(fp32(silu(Wg x) (Wu x))) with Q the quantiser written in the test, plain and
+    clamped, NVFP4 weights decoded by the test's own decoder."""
+    rng = np.random.default_rng(67)
+    H, I = 64, 96
+    W1 = random_weights(rng, 1, 2 * I, H)
+    W2 = random_weights(rng, 1, H, I)
+    D1 = decode_nvfp4(W1[0][0], W1[1][0], W1[2][0])
+    D2 = decode_nvfp4(W2[0][0], W2[1][0], W2[2][0])
+    for trial in range(3):
+        x = (rng.standard_normal(H) * 4.0 ** trial).astype(np.float32)
+        _, _, xh = quantize_fp8_row_brute(x)
+        for lim in (None, 0.05):
+            gv, uv = D1[:I] @ xh, D1[I:] @ xh
+            if lim is not None:
+                gv, uv = np.minimum(gv, lim), np.clip(uv, -lim, lim)
+            h = silu(gv) * uv
+            _, _, hh = quantize_fp8_row_brute(h.astype(np.float32))
+            assert np.max(np.abs(hh - h)) > 1e-4 * np.max(np.abs(h))          # the quantisation is visible
+            ref = D2 @ hh
+            y = o.expert_ffn(W1, W2, 0, xh, swiglu_limit=lim, hq=3)
+            assert np.allclose(y, ref, rtol=1e-12, atol=1e-14 * np.abs(ref).max()), np.abs(y - ref).max()
+
+
+def pin_moe_fp8_layer(o):
+    """The layer with act "fp8" equals, per token, the textbook sum over its picks with x
+    and h quantised by the test's FP8 quantiser (routing ids and weights from the result)."""
+    import synth
+    import oracle.moe as omoe
+    cfg = synth.MoeConfig("pin-w4a8-nvfp4", T=10, H=64, I=64, E=6, k=2, shared=1, act="fp8", seed=209)
+    x, lg = synth.activations(cfg), synth.logits(cfg)
+    W1, W2, WS1, WS2 = _layer_weights(cfg, o)
+    res = omoe.forward(cfg, x, lg, W1, W2, WS1, WS2, o=o)
+    I = cfg.I
+
+    def mlp(Wa, Wb, e, v):
+        A = decode_nvfp4(Wa[0][e], Wa[1][e], Wa[2][e])
+        B = decode_nvfp4(Wb[0][e], Wb[1][e], Wb[2][e])
+        h = silu(A[:I] @ v) * (A[I:] @ v)
+        return B @ quantize_fp8_row_brute(h.astype(np.float32))[2]
+    X = bf16_to_f64(x).astype(np.float32)
+    for t in range(cfg.T):
+        xt = quantize_fp8_row_brute(X[t])[2]
+        ref = sum(res["w"][t, j] * mlp(W1, W2, res["ids"][t, j], xt) for j in range(cfg.k)) + mlp(WS1, WS2, 0, xt)
+        assert np.allclose(res["out"][t], ref, rtol=1e-11, atol=1e-12 * np.abs(ref).max()), t
+
+
 # ------------------------------------------------------------ MXFP4 weights
 
 def e8m0_table_torch() -> np.ndarray:
@@ -822,6 +937,8 @@ def _by_expert_configs():
                         seed=203),
         synth.MoeConfig("bx-h-nvfp4", T=16, H=128, I=128, E=8, k=2, act="nvfp4_all", shared=1, seed=204),
         synth.MoeConfig("bx-w4a8", T=16, H=128, I=128, E=8, k=2, act="mxfp8", wfmt="mxfp4", seed=205),
+        synth.MoeConfig("bx-w4a8-nvfp4", T=16, H=128, I=128, E=8, k=2, act="fp8", shared=1, swiglu_limit=0.05,
+                        seed=207),
         synth.MoeConfig("bx-mx-general", T=16, H=128, I=128, E=16, k=4, wfmt="mxfp4", score="sqrt_softplus",
                         bias_sigma=0.3, seed=206),
     ]

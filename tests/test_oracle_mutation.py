@@ -55,7 +55,15 @@ MUTANTS = {
     "mx8_amax_half_block": ("      for (int j = 0; j < 32; ++j)\n        if (fabsf(xr[b * 32 + j]) > A)",
                             "      for (int j = 0; j < 16; ++j)\n        if (fabsf(xr[b * 32 + j]) > A)"),
     "mx8_sign_lost": ("const uint32_t sign = signbit(v) ? 0x80u : 0u;", "const uint32_t sign = 0u;"),
-    "mx8_h_as_nvfp4": ("  if (hq == 2) {   /* MXFP8 h (W4A8 profile) */", "  if (0) {   /* MXFP8 h (W4A8 profile) */"),
+    "mx8_h_as_nvfp4": ("  } else if (hq == 2) {   /* MXFP8 h (W4A8 profile) */",
+                       "  } else if (0) {   /* MXFP8 h (W4A8 profile) */"),
+    "fp8_divisor": ("const float s = A / 448.0f;", "const float s = A / 447.0f;"),
+    "fp8_amax_skips_last": ("    for (int k = 0; k < K; ++k)\n      if (fabsf(xr[k]) > A) A = fabsf(xr[k]);",
+                            "    for (int k = 0; k + 1 < K; ++k)\n      if (fabsf(xr[k]) > A) A = fabsf(xr[k]);"),
+    "fp8_sign_lost": ("const uint32_t sign = signbit(xr[k]) ? 0x80u : 0u;", "const uint32_t sign = 0u;"),
+    "fp8_decode_scale_dropped": ("orc_e4m3fn(codes[(size_t)r * K + k]) * (double)scale[r];",
+                                 "orc_e4m3fn(codes[(size_t)r * K + k]);"),
+    "fp8_h_skipped": ("  if (hq == 3) {", "  if (0) {"),
     "hq_not_on_shared": ("      orc_expert_ffn_q(shared, s, H, I, x + (size_t)i * H, y, 0, 0.0, hq);",
                          "      orc_expert_ffn_q(shared, s, H, I, x + (size_t)i * H, y, 0, 0.0, 0);"),
     "hq_decode_gs_halved": ("    orc_quantize(h32, 1, I, 1, hp, hs, &hg);",
