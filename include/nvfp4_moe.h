@@ -93,6 +93,15 @@ extern "C" {
                              (clamped to [-127, 127]; -127 for a zero block), E4M3 codes of
                              |v| 2^-X rounded to nearest even and saturating at 448, sign kept.
                              Both GEMMs run gfx950's block-scaled MFMA on the raw codes. */
+#define MOE_ACT_FP8_ROW 4 /* W4A8 on NVFP4 weights ([b12x] "What's in here", moe: the unified
+                             dynamic path's w4a8_nvfp4 variant, NVFP4 weights with FP8
+                             activations). x and h of every expert row are FP8 E4M3 with one FP32
+                             scale per row, s = max|v| / 448 (binary32), codes sign | E4M3 of
+                             |v| / s rounded to nearest even and saturating at 448 (0 if s == 0),
+                             the per-row amax rule of [megamoe] archived CORRECTNESS_BACKLOG
+                             section 7 (FP8 rows with a per-row float32 scale). Any weight format;
+                             the GEMMs take the codes' exact fp16 decode and apply s in the
+                             epilogue. */
 
 /* Weight format of every projection ([vllm.cpp] capability table, MXFP4 row: E8M0
  * dequant 2^(byte-127), group 32, no global scale, distinct from NVFP4's group-16 fp8
@@ -189,9 +198,10 @@ typedef struct {
  *   expert_offsets i32 [E+1]   exclusive scan of counts, offsets[E] = T*k
  *   perm           i32 [T*k]   perm[offsets[e] + r] = t*k + j: expert-major,
  *                              tokens ascending inside an expert
- *   act_packed     u8  [T][H/2]   (NVFP4 x; MXFP8: [T][H] E4M3 codes) quantised activations, as
- *   act_scales     u8  [T][H/16]   moe_quantize_nvfp4_rows writes them (MXFP8: [T][H/32] E8M0)
- *   act_global     f32 [T]        */
+ *   act_packed     u8  [T][H/2]   (NVFP4 x; MXFP8 and FP8 rows: [T][H] E4M3 codes) quantised
+ *   act_scales     u8  [T][H/16]   activations, as moe_quantize_nvfp4_rows writes them (MXFP8:
+ *   act_global     f32 [T]         [T][H/32] E8M0; FP8 rows: no block scales, act_global = the
+ *                                  row scales, as moe_quantize_fp8_rows writes them) */
 typedef struct {
   int32_t* topk_ids;
   float* topk_weights;
@@ -328,6 +338,18 @@ int moe_run_no_alloc(const moe_plan_t* plan, const void* packed, int32_t T, cons
  * row_global f32 [rows]; all device pointers 16-byte aligned. */
 int moe_quantize_nvfp4_rows(const uint16_t* x, int32_t rows, int32_t K, uint8_t* packed,
                             uint8_t* scales, float* row_global, void* stream);
+
+/* FP8 row quantiser of MOE_ACT_FP8_ROW (NVFP4-weight W4A8; [b12x] "What's in here", moe,
+ * w4a8_nvfp4; per-row amax scale as in [megamoe] archived CORRECTNESS_BACKLOG section 7):
+ * per bf16 row of K columns,
+ *   s    = max|x| / 448 (binary32)
+ *   code = sign << 7 | E4M3 nearest-even of |x| / s (binary32 division), saturating at 448;
+ *          0 if s == 0
+ * Outputs codes u8 [rows][K] and row_scale f32 [rows] (device, caller-owned); x and codes
+ * 16-byte aligned, row_scale 4-byte aligned; K a multiple of 16 up to 16384 (MOE_ERR_SHAPE
+ * otherwise). Enqueued on `stream`; returns a HIP error code if the launch fails. */
+int moe_quantize_fp8_rows(const uint16_t* x, int32_t rows, int32_t K, uint8_t* codes, float* row_scale,
+                          void* stream);
 
 /* The same quantiser with one global scale per group of `rows_per_group`
  * consecutive fp32 rows (a weight projection [N][K] is one group of N rows):

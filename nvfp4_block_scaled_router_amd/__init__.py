@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libnvfp4moe.so")
 
 MOE_ABI_VERSION = 2
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID, MOE_SCORE_SQRT_SOFTPLUS = 0, 1, 2
-MOE_ACT_BF16, MOE_ACT_NVFP4_ROWQ, MOE_ACT_NVFP4_ALL, MOE_ACT_MXFP8 = 0, 1, 2, 3
+MOE_ACT_BF16, MOE_ACT_NVFP4_ROWQ, MOE_ACT_NVFP4_ALL, MOE_ACT_MXFP8, MOE_ACT_FP8_ROW = 0, 1, 2, 3, 4
 MOE_WEIGHTS_NVFP4, MOE_WEIGHTS_MXFP4 = 0, 1
 MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_SIZE, MOE_ERR_TOKENS = 0, -1, -2, -3, -4
 MOE_ERR_ALIGN, MOE_ERR_ABI, MOE_ERR_ENUM, MOE_ERR_WEIGHT, MOE_ERR_SCRATCH = -5, -6, -7, -8, -9
@@ -31,7 +31,7 @@ STAGE_NAMES = ("quant", "route", "gate_up", "down", "combine")
 
 EXPORTED = ("moe_plan", "moe_plan_destroy", "moe_pack_weights", "moe_pack_router_bias", "moe_run", "moe_run_timed",
             "moe_run_no_alloc",
-            "moe_quantize_nvfp4_rows", "moe_quantize_nvfp4_weights", "moe_validate_weights_host", "moe_strerror",
+            "moe_quantize_nvfp4_rows", "moe_quantize_fp8_rows", "moe_quantize_nvfp4_weights", "moe_validate_weights_host", "moe_strerror",
             "moe_abi_version")
 
 _i32, _u32, _sz, _vp = ctypes.c_int32, ctypes.c_uint32, ctypes.c_size_t, ctypes.c_void_p
@@ -84,6 +84,8 @@ def lib() -> ctypes.CDLL:
         L.moe_run_no_alloc.argtypes = [_vp, _vp, _i32, _vp, _vp, _vp, ctypes.POINTER(moe_routing_out), _vp]
         L.moe_quantize_nvfp4_rows.restype = _i32
         L.moe_quantize_nvfp4_rows.argtypes = [_vp, _i32, _i32, _vp, _vp, _vp, _vp]
+        L.moe_quantize_fp8_rows.restype = _i32
+        L.moe_quantize_fp8_rows.argtypes = [_vp, _i32, _i32, _vp, _vp, _vp]
         L.moe_quantize_nvfp4_weights.restype = _i32
         L.moe_quantize_nvfp4_weights.argtypes = [_vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp]
         L.moe_validate_weights_host.restype = _i32
@@ -143,7 +145,7 @@ def make_desc(hidden: int, inter: int, num_experts: int, top_k: int, max_tokens:
                   "sqrt_softplus": MOE_SCORE_SQRT_SOFTPLUS}.get(score, score)
     d.renormalize = 1 if renormalize else 0
     d.act_format = {"bf16": MOE_ACT_BF16, "nvfp4": MOE_ACT_NVFP4_ROWQ, "nvfp4_all": MOE_ACT_NVFP4_ALL,
-                    "mxfp8": MOE_ACT_MXFP8}.get(act, act)
+                    "mxfp8": MOE_ACT_MXFP8, "fp8": MOE_ACT_FP8_ROW}.get(act, act)
     d.num_shared = num_shared
     d.use_bias = 1 if use_bias else 0
     d.n_group, d.topk_group = n_group, topk_group
@@ -222,6 +224,10 @@ def moe_run_no_alloc(plan, packed, T: int, x, router_logits, out, routing: Optio
 def moe_quantize_nvfp4_rows(x, rows: int, K: int, packed, scales, row_global, stream=None) -> None:
     _check(lib().moe_quantize_nvfp4_rows(_ptr(x), rows, K, _ptr(packed), _ptr(scales), _ptr(row_global),
                                          _stream(stream)))
+
+
+def moe_quantize_fp8_rows(x, rows: int, K: int, codes, row_scale, stream=None) -> None:
+    _check(lib().moe_quantize_fp8_rows(_ptr(x), rows, K, _ptr(codes), _ptr(row_scale), _stream(stream)))
 
 
 def moe_quantize_nvfp4_weights(w, groups: int, rows_per_group: int, K: int, packed, scales, group_global,

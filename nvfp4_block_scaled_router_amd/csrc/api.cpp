@@ -102,7 +102,7 @@ static int load_desc(const moe_desc* in, moe_desc* out) {
   if (d->score_fn != MOE_SCORE_SOFTMAX && d->score_fn != MOE_SCORE_SIGMOID && d->score_fn != MOE_SCORE_SQRT_SOFTPLUS)
     return MOE_ERR_ENUM;
   if (d->act_format != MOE_ACT_BF16 && d->act_format != MOE_ACT_NVFP4_ROWQ && d->act_format != MOE_ACT_NVFP4_ALL &&
-      d->act_format != MOE_ACT_MXFP8)
+      d->act_format != MOE_ACT_MXFP8 && d->act_format != MOE_ACT_FP8_ROW)
     return MOE_ERR_ENUM;
   if (d->hidden < 128 || d->hidden > MAX_HIDDEN || d->hidden % 128) return MOE_ERR_SHAPE;
   if (d->inter < 128 || d->inter > MAX_HIDDEN || d->inter % 128) return MOE_ERR_SHAPE;
@@ -172,19 +172,20 @@ int moe_plan(const moe_desc* desc, moe_plan_t** plan, size_t* packed_bytes, size
   p->ws_trow = o; o = align_up(o + 8 * (size_t)p->max_tiles);
   p->ws_tcnt = o; o = align_up(o + 16);
   p->ws_plan = o; o = align_up(o + 4 * plan_scratch_ints(Tm, k, E));
-  const bool mx8 = desc->act_format == MOE_ACT_MXFP8;
-  const bool fp4x = desc->act_format != MOE_ACT_BF16, fp4h = desc->act_format == MOE_ACT_NVFP4_ALL;
+  const bool mx8 = desc->act_format == MOE_ACT_MXFP8, f8 = desc->act_format == MOE_ACT_FP8_ROW;
+  const bool fp4x = desc->act_format != MOE_ACT_BF16 && !f8, fp4h = desc->act_format == MOE_ACT_NVFP4_ALL;
+  // FP8 rows: x codes only go to the caller's act_packed; the GEMMs read the fp16 decode
   p->ws_xq = o; o = align_up(o + (fp4x ? (size_t)Tm * H / (mx8 ? 1 : 2) : 0));   // codes (MXFP8: a byte each)
   p->ws_xs = o; o = align_up(o + (fp4x ? (size_t)Tm * H / 16 : 0));
   p->ws_xg = o; o = align_up(o + 4 * (size_t)Tm);      // per-row activation factor (either format)
   p->ws_x16 = o; o = align_up(o + (mx8 ? 0 : 2 * (size_t)Tm * H));   // fp16 x rows (rescaled bf16 or NVFP4 decode)
-  p->ws_h = o; o = align_up(o + (mx8 ? 0 : 2 * rows * I));              // h16 (NVFP4 h: its fp16 decode)
-  p->ws_hexp = o; o = align_up(o + (fp4h || mx8 ? 0 : rows * (I / 16)));  // per-16-column h exponents
+  p->ws_h = o; o = align_up(o + (mx8 ? 0 : 2 * rows * I));              // h16 (NVFP4 / FP8 h: its fp16 decode)
+  p->ws_hexp = o; o = align_up(o + (fp4h || mx8 || f8 ? 0 : rows * (I / 16)));  // per-16-column h exponents
   p->ws_hmin = o; o = align_up(o + 4 * rows);                       // per-row minimum h exponent
-  p->ws_hf = o; o = align_up(o + (fp4h || mx8 ? 4 * rows * I : 0));   // NVFP4 / prefill MXFP8 h: fp32 h rows,
-  p->ws_hq = o; o = align_up(o + (fp4h ? rows * I / 2 : mx8 ? rows * I : 0));   // their codes (MXFP8 h too),
+  p->ws_hf = o; o = align_up(o + (fp4h || mx8 || f8 ? 4 * rows * I : 0));   // NVFP4 / FP8 / prefill MXFP8 h: fp32
+  p->ws_hq = o; o = align_up(o + (fp4h ? rows * I / 2 : mx8 ? rows * I : 0));   // h rows, their codes,
   p->ws_hs = o; o = align_up(o + (fp4h ? rows * (I / 16) : mx8 ? rows * (I / 32) : 0));   // block scales
-  p->ws_hg = o; o = align_up(o + (fp4h ? 4 * rows : 0));           // and global scales
+  p->ws_hg = o; o = align_up(o + (fp4h || f8 ? 4 * rows : 0));     // and per-row scales
   p->ws_y = o; o = align_up(o + 2 * rows * H);         // y16
   p->ws_yexp = o; o = align_up(o + rows * (H / 16));  // per-16-column y exponents
   p->ws_bytes = o;
@@ -355,13 +356,14 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
   const uint8_t* pk = (const uint8_t*)packed;
   const int H = d.hidden, I = d.inter, E = d.num_experts, k = d.top_k, S = d.num_shared;
   const bool mx8 = d.act_format == MOE_ACT_MXFP8;           // x and h MXFP8, scaled MFMA (W4A8)
-  const bool fp4 = d.act_format != MOE_ACT_BF16 && !mx8;    // x row-quantised to NVFP4
+  const bool f8 = d.act_format == MOE_ACT_FP8_ROW;          // x and h FP8 with a per-row scale (W4A8, NVFP4)
+  const bool fp4 = d.act_format != MOE_ACT_BF16 && !mx8 && !f8;   // x row-quantised to NVFP4
   const bool fp4h = d.act_format == MOE_ACT_NVFP4_ALL;      // h too, before the down GEMM
   hipError_t e;
 
   uint8_t* xq = ((fp4 || mx8) && r.act_packed) ? r.act_packed : ws + plan->ws_xq;
   uint8_t* xs = ((fp4 || mx8) && r.act_scales) ? r.act_scales : ws + plan->ws_xs;
-  float* xg = (fp4 && r.act_global) ? r.act_global : (float*)(ws + plan->ws_xg);
+  float* xg = ((fp4 || f8) && r.act_global) ? r.act_global : (float*)(ws + plan->ws_xg);
   uint16_t* x16 = (uint16_t*)(ws + plan->ws_x16);
   const bool decode = use_decode(T, k, E);
   // Activation preparation: NVFP4 row quantisation, or the exact power-of-two rescale into
@@ -370,7 +372,9 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
   // Prefill batches with NVFP4 x take its exact fp16 decode (written by the quantiser beside
   // the codes, the row's global scale in the epilogue) through the fp16 GEMM, whose token
   // tiles arrive by LDS DMA; decode batches read the codes.
+  // FP8 x: its exact fp16 decode through the fp16 GEMM, the row's scale in the epilogue.
   const GemmMode gu_mode = mx8 ? GEMM_GATEUP_MX8
+                          : f8 ? GEMM_GATEUP_F16
                           : fp4 ? (decode ? GEMM_GATEUP_FP4 : GEMM_GATEUP_F16)
                                 : (decode && T * k < DECODE_F16_ROWS) ? GEMM_GATEUP_BF16 : GEMM_GATEUP_F16;
   // the activation preparation runs in extra workgroups of the routing stage's first launch
@@ -403,12 +407,13 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
   ra.renorm = d.renormalize;
   ra.scaling = d.routed_scaling;
   ra.side = mx8                           ? SIDE_MXFP8
+            : f8                            ? SIDE_FP8
             : fp4                           ? SIDE_NVFP4
             : gu_mode == GEMM_GATEUP_F16    ? SIDE_F16
                                             : SIDE_NONE;
   ra.side_x = x;
   ra.side_K = H;
-  ra.side_q = xq;
+  ra.side_q = f8 ? r.act_packed : xq;      // FP8 codes only when the caller asks for them
   ra.side_s = xs;
   ra.side_f = xg;
   ra.side_h = (fp4 && decode) ? nullptr : x16;   // NVFP4 x of prefill batches: also its fp16 decode
@@ -462,7 +467,7 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
   g1.h_natural = decode ? 0 : 1;                 // prefill: plain column order, rescaled before down
   // MXFP8 h: quantised in the decode GEMM's epilogue (a workgroup holds whole 32-column
   // blocks), or written as fp32 by the prefill GEMM and quantised by a row kernel
-  g1.hf = fp4h || (mx8 && !decode) ? (float*)(ws + plan->ws_hf) : nullptr;
+  g1.hf = fp4h || f8 || (mx8 && !decode) ? (float*)(ws + plan->ws_hf) : nullptr;
   if (mx8 && decode) {
     g1.hq8 = ws + plan->ws_hq;
     g1.hs8 = ws + plan->ws_hs;
@@ -529,6 +534,15 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
         g2.x = (const uint16_t*)(ws + plan->ws_h);
         g2.hmin = nullptr;
       }
+    } else if (f8) {   // every h row FP8-quantised with its own scale; the GEMMs take its fp16 decode
+      if ((e = mark(ev, 2 * MOE_STAGE_DOWN, s)) != hipSuccess) return (int)e;
+      first.start = nullptr;
+      e = launch_fp8_rows_f32(g1.hf, T * k + S * T, I, nullptr, (float*)(ws + plan->ws_hg),
+                              (uint16_t*)(ws + plan->ws_h), s);
+      g2.x = (const uint16_t*)(ws + plan->ws_h);
+      g2.xg = (const float*)(ws + plan->ws_hg);
+      g2.hexp = nullptr;
+      g2.hmin = nullptr;
     } else if (mx8) {
       g2.xq = ws + plan->ws_hq;
       g2.xs = ws + plan->ws_hs;
@@ -568,6 +582,14 @@ int moe_quantize_nvfp4_rows(const uint16_t* x, int32_t rows, int32_t K, uint8_t*
   if (rows < 0 || K < 16 || K > MAX_HIDDEN || K % 16) return MOE_ERR_SHAPE;
   if (!aligned16(x) || !aligned16(packed) || !aligned4(row_global)) return MOE_ERR_ALIGN;
   return (int)launch_quant_rows_bf16(x, rows, K, packed, scales, row_global, (hipStream_t)stream);
+}
+
+int moe_quantize_fp8_rows(const uint16_t* x, int32_t rows, int32_t K, uint8_t* codes, float* row_scale,
+                          void* stream) {
+  if (!x || !codes || !row_scale) return MOE_ERR_NULL;
+  if (rows < 0 || K < 16 || K > MAX_HIDDEN || K % 16) return MOE_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(codes) || !aligned4(row_scale)) return MOE_ERR_ALIGN;
+  return (int)launch_fp8_rows_bf16(x, rows, K, codes, row_scale, nullptr, (hipStream_t)stream);
 }
 
 int moe_quantize_nvfp4_weights(const float* w, int32_t groups, int32_t rows_per_group, int32_t K, uint8_t* packed,

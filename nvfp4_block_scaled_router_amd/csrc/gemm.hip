@@ -276,9 +276,13 @@ __device__ __forceinline__ void decode_body(const GemmArgs& a, int bx, int slot,
   int hm = 0;                                              // the row's common h exponent
   if (MODE == GEMM_DOWN) {
     xrow = a.x + (size_t)row * L.K;
-    erow = a.hexp + (size_t)row * (L.K / 16);
-    hm = a.hmin ? a.hmin[row] : row_exp_min4(erow, L.K / 16, lg);
-    sc = __builtin_ldexpf(wgs, -hm);
+    if (a.hexp) {                                          // permuted h16 with block exponents
+      erow = a.hexp + (size_t)row * (L.K / 16);
+      hm = a.hmin ? a.hmin[row] : row_exp_min4(erow, L.K / 16, lg);
+      sc = __builtin_ldexpf(wgs, -hm);
+    } else {                                               // plain rows with one factor each
+      sc *= a.xg[row];
+    }
   } else if (MODE == GEMM_DOWN_FP4) {                       // NVFP4 h rows, addressed by row
     qrow = a.xq + (size_t)row * (L.K / 2);
     srow = a.xs + (size_t)row * (L.K / 16);
@@ -330,7 +334,7 @@ __device__ __forceinline__ void decode_body(const GemmArgs& a, int bx, int slot,
       xo.make(xv, sp);
 #pragma unroll
       for (int j = 0; j < 4; ++j) bop[j] = __builtin_bit_cast(u32x4, xo.v[j]);
-    } else if (MODE == GEMM_DOWN) {   // h16: piece (g, j) at 4j + g; blocks 2g (j < 2), 2g + 1
+    } else if (MODE == GEMM_DOWN && erow) {   // h16: piece (g, j) at 4j + g; blocks 2g (j < 2), 2g + 1
       const uint16_t* src = xrow + (size_t)kc * KCHUNK + lg * 8;
       const uint32_t eb = *(const uint16_t*)(erow + kc * 8 + 2 * lg);
       const _Float16 f0 = h_factor(hm - (int)(int8_t)(eb & 0xFFu)), f1 = h_factor(hm - (int)(int8_t)(eb >> 8));

@@ -29,7 +29,9 @@ struct RouteArgs {
   // SIDE_MXFP8: codes side_q [T][side_K] and E8M0 scales side_s [T][side_K/32];
   // SIDE_NVFP4: codes side_q [T][side_K/2], E4M3 scales side_s [T][side_K/16], global scales side_f [T]
   //   (and, with side_h set, the rows' exact fp16 decode without the global scale);
-  // SIDE_F16: fp16 rows side_h [T][side_K] and their factors side_f [T]
+  // SIDE_F16: fp16 rows side_h [T][side_K] and their factors side_f [T];
+  // SIDE_FP8: per-row FP8: scales side_f [T], fp16 decode side_h [T][side_K] and, when
+  //   side_q is set, the E4M3 codes side_q [T][side_K]
   int side;
   const uint16_t* side_x;
   int side_K;
@@ -38,7 +40,7 @@ struct RouteArgs {
   float* side_f;
   uint16_t* side_h;
 };
-enum RouteSide { SIDE_NONE = 0, SIDE_MXFP8 = 1, SIDE_F16 = 2, SIDE_NVFP4 = 3 };
+enum RouteSide { SIDE_NONE = 0, SIDE_MXFP8 = 1, SIDE_F16 = 2, SIDE_NVFP4 = 3, SIDE_FP8 = 4 };
 
 struct PlanArgs {
   const int32_t* ids;    // [T][k]
@@ -73,6 +75,12 @@ hipError_t launch_quant_rows_bf16(const uint16_t* x, int rows, int K, uint8_t* p
 // MXFP8 rows (codes [rows][K], E8M0 scales [rows][K/32]) from fp32 rows (h before the W4A8 down
 // GEMM); the activation rows are converted by the routing launch (RouteArgs side jobs).
 hipError_t launch_mxfp8_rows_f32(const float* x, int rows, int K, uint8_t* codes, uint8_t* scales, hipStream_t s);
+// FP8 rows with one scale per row (scale = max|x| / 448); codes [rows][K] and the fp16 decode
+// x16 [rows][K] (without the scale) are each written when non-null
+hipError_t launch_fp8_rows_bf16(const uint16_t* x, int rows, int K, uint8_t* codes, float* scale, uint16_t* x16,
+                               hipStream_t s);
+hipError_t launch_fp8_rows_f32(const float* x, int rows, int K, uint8_t* codes, float* scale, uint16_t* x16,
+                               hipStream_t s);
 // fp32 rows (h before the NVFP4 down GEMM), each with its own global scale.
 hipError_t launch_quant_rows_f32(const float* x, int rows, int K, uint8_t* packed, uint8_t* scales, float* gs,
                                  hipStream_t s, uint16_t* x16 = nullptr);
@@ -141,6 +149,8 @@ struct GemmArgs {
   // The prefill GEMMs keep h16 in plain column order instead (h_natural = 1): a rescale pass
   // between the GEMMs (launch_h_rescale) brings every block of a row to the row's exponent
   // P = hmin[row] in place, and the prefill down GEMM streams those rows by LDS DMA.
+  // DOWN with hexp and hmin both null: h16 rows in plain column order, each with one factor
+  // xg[row] applied in the epilogue (the fp16 decode of h rows quantised with a per-row scale).
   uint16_t* out;           // gate_up: h16
   int8_t* hexp;            // [rows][I/16]
   int32_t* hmin;           // [rows] or nullptr

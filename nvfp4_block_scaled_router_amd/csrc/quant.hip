@@ -43,6 +43,17 @@ __global__ __launch_bounds__(256) void mxfp8_rows_kernel(const T* __restrict__ x
   mxfp8_row_wave(x + (size_t)r * K, K, codes + (size_t)r * K, scales + (size_t)r * (K / 32), threadIdx.x & (WAVE - 1));
 }
 
+// FP8 rows with a per-row scale: one wave per row (fp8_row_wave), 4 rows per workgroup.
+template <typename T>
+__global__ __launch_bounds__(256) void fp8_rows_kernel(const T* __restrict__ x, int rows, int K,
+                                                       uint8_t* __restrict__ codes, float* __restrict__ scale,
+                                                       uint16_t* __restrict__ x16) {
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  fp8_row_wave(x + (size_t)r * K, K, codes ? codes + (size_t)r * K : nullptr, scale + r,
+               x16 ? x16 + (size_t)r * K : nullptr, threadIdx.x & (WAVE - 1));
+}
+
 // Group maxima: one 1024-thread workgroup per group, fixed reduction tree.
 __global__ __launch_bounds__(1024) void group_gs_f32_kernel(const float* __restrict__ x, int rows_per_group, int K,
                                                             float* __restrict__ gs) {
@@ -94,6 +105,20 @@ hipError_t launch_quant_rows_f32(const float* x, int rows, int K, uint8_t* packe
 hipError_t launch_mxfp8_rows_f32(const float* x, int rows, int K, uint8_t* codes, uint8_t* scales, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   hipLaunchKernelGGL(mxfp8_rows_kernel<float>, dim3((rows + 3) / 4), dim3(256), 0, s, x, rows, K, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_fp8_rows_bf16(const uint16_t* x, int rows, int K, uint8_t* codes, float* scale, uint16_t* x16,
+                               hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fp8_rows_kernel<uint16_t>, dim3((rows + 3) / 4), dim3(256), 0, s, x, rows, K, codes, scale, x16);
+  return hipGetLastError();
+}
+
+hipError_t launch_fp8_rows_f32(const float* x, int rows, int K, uint8_t* codes, float* scale, uint16_t* x16,
+                               hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fp8_rows_kernel<float>, dim3((rows + 3) / 4), dim3(256), 0, s, x, rows, K, codes, scale, x16);
   return hipGetLastError();
 }
 

@@ -215,6 +215,8 @@ __device__ __forceinline__ void side_rows(const RouteArgs& a, int j) {
   const uint16_t* row = a.side_x + (size_t)t * K;
   if (a.side == SIDE_MXFP8)
     mxfp8_row_wave(row, K, a.side_q + (size_t)t * K, a.side_s + (size_t)t * (K / 32), lane);
+  else if (a.side == SIDE_FP8)
+    fp8_row_wave(row, K, a.side_q ? a.side_q + (size_t)t * K : nullptr, a.side_f + t, a.side_h + (size_t)t * K, lane);
   else if (a.side == SIDE_NVFP4)   // with side_h also the rows' fp16 decode (prefill batches)
     nvfp4_row_wave(row, K, a.side_q + (size_t)t * (K / 2), a.side_s + (size_t)t * (K / 16), a.side_f + t,
                    a.side_h ? a.side_h + (size_t)t * K : nullptr);

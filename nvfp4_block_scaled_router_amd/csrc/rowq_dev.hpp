@@ -156,6 +156,40 @@ __device__ __forceinline__ void mxfp8_row_wave(const T* row, int K, uint8_t* cod
   }
 }
 
+// FP8 rows with one scale per row (the W4A8 path on NVFP4 weights): s = max|x| / 448 in
+// binary32 (448 = E4M3's largest value), codes sign << 7 | E4M3_rne_sat(|x| / s) (binary32
+// division; 0 where s is 0). One wave per row, a lane per 16-column block; writes the scale
+// (lane 0), the codes when `codes` is set and, when `x16` is set, their exact fp16 decode
+// E4M3(code) without the scale (E4M3 is a subset of fp16), the operands of the fp16 MFMAs,
+// whose epilogue applies s.
+template <typename T>
+__device__ __forceinline__ void fp8_row_wave(const T* row, int K, uint8_t* codes, float* s_out, uint16_t* x16,
+                                             int lane) {
+  const float s = wave_row_absmax(row, K) / 448.0f;
+  if (lane == 0) *s_out = s;
+  for (int b = lane; b < K / 16; b += WAVE) {
+    float v[16];
+    load16(row + (size_t)b * 16, v);
+    uint32_t w[4] = {0u, 0u, 0u, 0u}, h[8];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t sign = (__float_as_uint(v[i]) >> 31) << 7;
+      const uint32_t code = sign | (s != 0.0f ? e4m3_encode_rne_sat(fabsf(v[i]) / s) : 0u);
+      w[i >> 2] |= code << (8 * (i & 3));
+      const uint32_t f = __builtin_bit_cast(uint16_t, (_Float16)e4m3_to_f32(code));
+      if (i & 1)
+        h[i >> 1] |= f << 16;
+      else
+        h[i >> 1] = f;
+    }
+    if (codes) *(u32x4*)(codes + (size_t)b * 16) = u32x4{w[0], w[1], w[2], w[3]};
+    if (x16) {
+      *(u32x4*)(x16 + (size_t)b * 16) = u32x4{h[0], h[1], h[2], h[3]};
+      *(u32x4*)(x16 + (size_t)b * 16 + 8) = u32x4{h[4], h[5], h[6], h[7]};
+    }
+  }
+}
+
 // bf16 activation rows -> fp16 for the gate_up MFMA: every row is multiplied by the power
 // of two 2^p that puts its max |x| in [2^14, 2^15) (p clamped to [-126, 126]), which is exact
 // for every element whose scaled magnitude is a normal fp16 (>= 2^-14, i.e. >= 2^-28 of the

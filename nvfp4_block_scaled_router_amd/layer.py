@@ -66,6 +66,9 @@ class MoeLayer:
         if self.desc.act_format == 3:       # MXFP8: E4M3 codes and E8M0 scales per 32
             bufs.update(act_packed=torch.empty((T, self.H), dtype=torch.uint8, device=dev),
                         act_scales=torch.empty((T, self.H // 32), dtype=torch.uint8, device=dev))
+        elif self.desc.act_format == 4:     # FP8 rows: E4M3 codes and one scale per row
+            bufs.update(act_packed=torch.empty((T, self.H), dtype=torch.uint8, device=dev),
+                        act_global=torch.empty(T, dtype=torch.float32, device=dev))
         elif self.desc.act_format in (1, 2):
             bufs.update(act_packed=torch.empty((T, self.H // 2), dtype=torch.uint8, device=dev),
                         act_scales=torch.empty((T, self.H // 16), dtype=torch.uint8, device=dev),

@@ -107,12 +107,14 @@ def _e4m3_values():
 
 def h_flip_candidates(case, ref, t):
     """Output changes of the alternative roundings of token t's h elements that lie within
-    FLIP_REL of a code boundary (MXFP8 or NVFP4 h), from the oracle's FP64 h."""
+    FLIP_REL of a code boundary (MXFP8, FP8-row or NVFP4 h), from the oracle's FP64 h."""
     import pins
     cfg, o = case.cfg, oracle.default()
     tok = int(case.tokens[t])
     if cfg.act == "mxfp8":
         x_t = o.mxfp8_rows(ref["xq"][tok:tok + 1], ref["xs"][tok:tok + 1])[0]
+    elif cfg.act == "fp8":
+        x_t = o.fp8_rows(ref["xq"][tok:tok + 1], ref["xg"][tok:tok + 1])[0]
     else:
         x_t = o.dequant_rows(ref["xq"][tok:tok + 1], ref["xs"][tok:tok + 1], ref["xg"][tok:tok + 1])[0]
     experts = [(case.W[0], case.W[1], int(e), float(wj), cfg.swiglu_limit)
@@ -128,11 +130,11 @@ def h_flip_candidates(case, ref, t):
             D2 = pins.decode_mxfp4(W2[0][e], W2[1][e])
         else:
             D2 = pins.decode_nvfp4(W2[0][e], W2[1][e], W2[2][e])
-        if cfg.act == "mxfp8":
-            codes, sc = o.mxfp8_quantize(h32[None])
+        if cfg.act in ("mxfp8", "fp8"):
+            codes, sc = o.mxfp8_quantize(h32[None]) if cfg.act == "mxfp8" else o.fp8_rows_quantize(h32[None])
             for i in range(I):
                 c = int(codes[0, i]) & 0x7F
-                step = np.ldexp(1.0, int(sc[0, i // 32]) - 127)
+                step = np.ldexp(1.0, int(sc[0, i // 32]) - 127) if cfg.act == "mxfp8" else float(sc[0])
                 v = abs(float(h32[i])) / step
                 for c2 in (c - 1, c + 1):
                     if 0 <= c2 <= 0x7E and v > 0 and abs(v - (e4[c] + e4[c2]) / 2) <= FLIP_REL * v:

@@ -59,9 +59,12 @@ def plan_rc(d):
     (dict(max_tokens=0), m.MOE_ERR_SHAPE),
     (dict(num_shared=2), m.MOE_ERR_SHAPE),
     (dict(score=5), m.MOE_ERR_ENUM),
-    (dict(act=4), m.MOE_ERR_ENUM),
+    (dict(act=5), m.MOE_ERR_ENUM),
+    (dict(act=-1), m.MOE_ERR_ENUM),
     (dict(act="mxfp8"), m.MOE_ERR_SHAPE),                   # MXFP8 activations need MXFP4 weights
     (dict(act="mxfp8", weights="mxfp4"), m.MOE_OK),
+    (dict(act="fp8"), m.MOE_OK),                            # FP8 rows: NVFP4 weights ...
+    (dict(act="fp8", weights="mxfp4"), m.MOE_OK),           # ... or MXFP4 ones
     # router / activation variants (ABI 2)
     (dict(score="sqrt_softplus", use_bias=True, n_group=4, topk_group=2, routed_scaling=2.5,
           swiglu_limit=10.0), m.MOE_OK),
@@ -140,6 +143,30 @@ def test_plan_sizes_cover_the_layout():
     m.moe_plan_destroy(plan)
     assert pb4 == pb
     assert wb4 >= rows * (2048 * 4 + 2048 // 2 + 2048 // 16 + 4 + 4 + 7168 * 2 + 7168 // 16) + 8192 * (7168 // 2)
+
+
+def test_fp8_rows_workspace():
+    """FP8 rows: the fp32 h rows, their fp16 decode and one scale per row; no block exponents."""
+    kw = dict(hidden=2048, inter=768, num_experts=128, top_k=8, max_tokens=4096)
+    plan, _, wb = m.moe_plan(desc(**kw))
+    m.moe_plan_destroy(plan)
+    plan, _, wb8 = m.moe_plan(desc(act="fp8", **kw))
+    m.moe_plan_destroy(plan)
+    rows = 4096 * 8
+    assert wb8 >= rows * (768 * 4 + 768 * 2 + 4 + 4 + 2048 * 2 + 2048 // 16) + 4096 * 2048 * 2
+    assert wb8 - wb >= rows * (768 * 4 + 4 - 768 // 16)
+
+
+def test_quantize_fp8_rows_rejects():
+    L = m.lib()
+    fake = 1 << 20
+    assert L.moe_quantize_fp8_rows(None, 4, 64, fake, fake, None) == m.MOE_ERR_NULL
+    assert L.moe_quantize_fp8_rows(fake, 4, 60, fake, fake, None) == m.MOE_ERR_SHAPE
+    assert L.moe_quantize_fp8_rows(fake, -1, 64, fake, fake, None) == m.MOE_ERR_SHAPE
+    assert L.moe_quantize_fp8_rows(fake, 4, 16384 + 16, fake, fake, None) == m.MOE_ERR_SHAPE
+    assert L.moe_quantize_fp8_rows(fake + 2, 4, 64, fake, fake, None) == m.MOE_ERR_ALIGN
+    assert L.moe_quantize_fp8_rows(fake, 4, 64, fake + 4, fake, None) == m.MOE_ERR_ALIGN
+    assert L.moe_quantize_fp8_rows(fake, 4, 64, fake, fake + 2, None) == m.MOE_ERR_ALIGN
 
 
 def test_run_rejects_before_enqueue():

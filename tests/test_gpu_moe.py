@@ -32,11 +32,15 @@ def _run_and_check(case: Case):
     if cfg.act == "mxfp8":
         assert np.array_equal(bufs["act_packed"].cpu().numpy(), ref["xq"]), "MXFP8 activation codes"
         assert np.array_equal(bufs["act_scales"].cpu().numpy(), ref["xs"]), "MXFP8 activation scales"
+    if cfg.act == "fp8":
+        assert np.array_equal(bufs["act_packed"].cpu().numpy(), ref["xq"]), "FP8 activation codes"
+        assert np.array_equal(bufs["act_global"].cpu().numpy().view(np.uint32), ref["xg"].view(np.uint32)), \
+            "FP8 activation row scales"
     if cfg.act in ("nvfp4", "nvfp4_all"):
         assert np.array_equal(bufs["act_packed"].cpu().numpy(), ref["xq"]), "quantised activation codes"
         assert np.array_equal(bufs["act_scales"].cpu().numpy(), ref["xs"]), "quantised activation scales"
         assert np.array_equal(bufs["act_global"].cpu().numpy().view(np.uint32), ref["xg"].view(np.uint32))
-    flips = (lambda t: h_flip_candidates(case, ref, t)) if cfg.act in ("mxfp8", "nvfp4_all") else None
+    flips = (lambda t: h_flip_candidates(case, ref, t)) if cfg.act in ("mxfp8", "nvfp4_all", "fp8") else None
     check_out(out[torch.from_numpy(case.tokens).long().to(DEV)], ref["out"], cfg.name, flips=flips)
     return L, x, lg, out
 
@@ -291,6 +295,35 @@ W4A8 = [
 @pytest.mark.parametrize("cfg", W4A8, ids=lambda c: c.name)
 def test_w4a8_mx(cfg):
     _run_and_check(Case(cfg, tokens=synth.token_sample(cfg, 24) if cfg.I > 4096 else None))
+
+
+# W4A8 on NVFP4 weights: x and h FP8 with one scale per row, through the fp16 GEMMs (decode
+# and prefill regimes, the skewed split launch, a shared expert, clamped SwiGLU, MXFP4
+# weights, the widest intermediate size, a ragged prefill batch)
+W4A8_NVFP4 = [
+    synth.MoeConfig("fp8-decode", T=8, H=256, I=128, E=16, k=4, act="fp8", seed=91),
+    synth.MoeConfig("fp8-decode-t1", T=1, H=384, I=256, E=32, k=8, score="sigmoid", shared=1, act="fp8", seed=92),
+    synth.MoeConfig("fp8-decode-wide", T=120, H=256, I=128, E=64, k=2, act="fp8", seed=93),
+    synth.MoeConfig("fp8-prefill-shared", T=300, H=512, I=256, E=8, k=2, shared=1, act="fp8", seed=94),
+    synth.MoeConfig("fp8-skewed-split", T=256, H=256, I=256, E=32, k=4, zipf_s=1.2, act="fp8", seed=95),
+    synth.MoeConfig("fp8-clamp-general", T=64, H=512, I=256, E=32, k=6, shared=1, score="sqrt_softplus",
+                    bias_sigma=0.5, swiglu_limit=0.05, act="fp8", seed=96),
+    synth.MoeConfig("fp8-mx-weights", T=64, H=512, I=256, E=8, k=2, act="fp8", wfmt="mxfp4", seed=97),
+    synth.MoeConfig("fp8-max-inter", T=40, H=128, I=16384, E=4, k=2, shared=1, act="fp8", seed=98),
+    synth.MoeConfig("fp8-prefill-ragged", T=777, H=384, I=384, E=8, k=2, score="sigmoid", act="fp8", seed=99),
+]
+
+
+@pytest.mark.parametrize("cfg", W4A8_NVFP4, ids=lambda c: c.name)
+def test_w4a8_nvfp4(cfg):
+    _run_and_check(Case(cfg, tokens=synth.token_sample(cfg, 24) if cfg.I > 4096 else None))
+
+
+@pytest.mark.parametrize("T", [64, 4096])
+def test_w4a8_nvfp4_qwen3_full(T):
+    """The Qwen3-30B-A3B layer on the NVFP4-weight W4A8 path, decode (64 tokens) and prefill
+    (4096 tokens), every token against the oracle."""
+    _run_and_check(Case(synth.qwen3_w4a8(T), by_expert=True))
 
 
 # the descriptor's limits: hidden and intermediate 16384 (128 K chunks), 65536 tokens

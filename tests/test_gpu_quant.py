@@ -76,3 +76,47 @@ def test_weight_quantiser(which):
     dev = quantize_projection(8, N, K, lambda e0, c: synth.expert_weights_f32(cfg, which, e0, c), DEV)
     for a, d in zip(ref, dev):
         assert np.array_equal(a[:8], d.cpu().numpy()), which
+
+
+# ---------------------------------------------- FP8 rows with a per-row scale (W4A8 on NVFP4)
+
+def _check_fp8(x_u16, what):
+    o = oracle.default()
+    rows, K = x_u16.shape
+    rc, rs = o.fp8_rows_quantize(o.bf16_rows(x_u16).astype(np.float32))
+    c = torch.empty((rows, K), dtype=torch.uint8, device=DEV)
+    s = torch.empty(rows, dtype=torch.float32, device=DEV)
+    m.moe_quantize_fp8_rows(bf16(x_u16), rows, K, c, s)
+    torch.cuda.synchronize()
+    log(f"  {what}: rows {rows} K {K}")
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), rs.view(np.uint32)), "row scales"
+    assert np.array_equal(c.cpu().numpy(), rc), "codes"
+
+
+def test_fp8_rows_workload_activations():
+    _check_fp8(synth.activations(synth.qwen3_w4a8(4096)), "qwen3 w4a8 x [4096][2048]")
+
+
+def test_fp8_rows_edge_cases():
+    _check_fp8(_bf16_bits(pins.fp8_rows_fixture()), "edge rows")
+
+
+def test_fp8_rows_ties_and_saturation():
+    """Rows whose maximum is 448 2^j (scale exactly 2^j) and whose other values sit on E4M3
+    rounding midpoints (ties to the even code), on codes, and between them."""
+    rng = np.random.default_rng(5)
+    e4 = pins.e4m3_table_torch()[:0x7F]
+    mids = (e4[:-1] + e4[1:]) / 2
+    vals = np.concatenate([mids, e4, mids * (1 + 2.0 ** -6)])
+    base = rng.choice(vals, size=(64, 256))
+    base[:, 0] = 448.0
+    sign = rng.choice([-1.0, 1.0], size=base.shape)
+    scale = 2.0 ** rng.integers(-10, 10, size=(64, 1))
+    _check_fp8(_bf16_bits(base * sign * scale), "E4M3 midpoints")
+
+
+def test_fp8_rows_tiny_magnitudes():
+    """Rows whose scale max|x| / 448 is a binary32 subnormal."""
+    rng = np.random.default_rng(6)
+    x = (rng.standard_normal((8, 64)) * 1e-37).astype(np.float32)
+    _check_fp8(_bf16_bits(x), "subnormal row scale")
