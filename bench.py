@@ -38,7 +38,9 @@ fraction of 8 TB/s, plus
   cpu_baseline: the CPU oracle (FP64, OpenMP) on a bounded sample of the headline
                 workload, on this host's cores.
 Other workloads (--workload qwen3-30b-a3b-prefill | deepseek-v3 | skewed-w4a4 |
-skewed-w4a4-all (h quantised to NVFP4 too) | tiny) print the same line for that configuration, and so do the router/activation
+skewed-w4a4-all (h quantised to NVFP4 too) | tiny) print the same line for that configuration, and so
+do qwen3-30b-a3b-w4a8-decode / -prefill (the Qwen3 layer with x and h FP8 with one scale per
+row on NVFP4 weights: T in {1, 8, 32, 64}, and T = 4096) and the router/activation
 variants deepseek-v4-flash-decode (256 experts, top-6, H=4096, I=1024, sqrt-softplus
 scores with a selection bias, SwiGLU clamped at 10, one shared expert; T in
 {1, 8, 32, 64}) and deepseek-v3-noaux (the DeepSeek-V3 layer with its grouped
@@ -111,6 +113,11 @@ def workload(name):
         return [synth.deepseek_v4_flash_w4a8(8192)], "mfma"
     if name == "deepseek-v4-flash-prefill":           # the same batch in W4A16 (bf16 x, 16-bit MFMA)
         return [synth.deepseek_v4_flash(8192)], "mfma"
+    # the Qwen3 layer on the W4A8 path with NVFP4 weights (x and h FP8 with a per-row scale)
+    if name == "qwen3-30b-a3b-w4a8-decode":
+        return [synth.qwen3_w4a8(T) for T in synth.DECODE_TOKENS], "hbm"
+    if name == "qwen3-30b-a3b-w4a8-prefill":
+        return [synth.qwen3_w4a8(4096)], "mfma"
     if name == "deepseek-v3-noaux":
         return [synth.deepseek_v3_router(8192)], "mfma"
     # one rank's routed DeepSeek-V4-Flash MoE on the sharing workloads: T = 6 at 0..100%
@@ -179,8 +186,9 @@ class Batch:
     def gate_up_bytes(self):
         c = self.cfg
         w = (self.touched + c.shared) * self.weight_bytes(2 * c.I * c.H)
-        act = c.T * c.H * {"bf16": 2.0, "mxfp8": 1.0 + 1.0 / 32}.get(c.act, NVFP4_BYTES_PER_WEIGHT + 4.0 / c.H)
-        h = (self.rows + c.shared * c.T) * c.I * (4 if c.act in ("nvfp4_all", "mxfp8") else 2)   # fp32 h / h16
+        act = c.T * c.H * {"bf16": 2.0, "mxfp8": 1.0 + 1.0 / 32, "fp8": 1.0 + 4.0 / c.H}.get(
+            c.act, NVFP4_BYTES_PER_WEIGHT + 4.0 / c.H)
+        h = (self.rows + c.shared * c.T) * c.I * (4 if c.act in ("nvfp4_all", "mxfp8", "fp8") else 2)   # fp32 h / h16
         return w + act + h
 
     def gate_up_flops(self):
@@ -189,12 +197,12 @@ class Batch:
 
     def down_bytes(self):
         """Weights of the touched experts, the h rows read (h16 with its block exponents, or
-        the NVFP4 / MXFP8 h codes and scales) and the y rows written (fp16 + exponents)."""
+        the NVFP4 / MXFP8 / FP8-row h codes and scales) and the y rows written (fp16 + exponents)."""
         c = self.cfg
         rows = self.rows + c.shared * c.T
         w = (self.touched + c.shared) * self.weight_bytes(c.H * c.I)
-        h = rows * {"nvfp4_all": c.I * NVFP4_BYTES_PER_WEIGHT + 4, "mxfp8": c.I * (1 + 1.0 / 32)}.get(
-            c.act, c.I * 2 + c.I / 16)
+        h = rows * {"nvfp4_all": c.I * NVFP4_BYTES_PER_WEIGHT + 4, "mxfp8": c.I * (1 + 1.0 / 32),
+                    "fp8": c.I + 4.0}.get(c.act, c.I * 2 + c.I / 16)
         return w + h + rows * (c.H * 2 + c.H / 16)
 
     def down_flops(self):
@@ -213,7 +221,8 @@ class Batch:
 
 # Tokens of a prefill-sized batch the parity gate compares with the oracle (decode batches: all)
 PARITY_SAMPLE = {"qwen3-30b-a3b-prefill": 48, "skewed-w4a4": 48, "skewed-w4a4-all": 48, "deepseek-v3": 4,
-                 "deepseek-v3-noaux-t8192": 4, "deepseek-v4-flash-t8192": 8, "deepseek-v4-flash-w4a8-t8192": 8}
+                 "deepseek-v3-noaux-t8192": 4, "deepseek-v4-flash-t8192": 8, "deepseek-v4-flash-w4a8-t8192": 8,
+                 "qwen3-30b-a3b-w4a8-t4096": 48}
 PARITY_REL_L2, PARITY_MAX_OVER_RMS, PARITY_W_ABS = 5e-3, 2e-2, 1e-6
 
 
@@ -228,7 +237,9 @@ def _parity_check(b, ref, tokens):
                   and float(np.abs(f["topk_weights"] - ref["w"]).max()) <= PARITY_W_ABS)
     act_ok = True
     if "xq" in ref and "act_packed" in f:
-        act_ok = np.array_equal(f["act_packed"], ref["xq"]) and np.array_equal(f["act_scales"], ref["xs"])
+        act_ok = np.array_equal(f["act_packed"], ref["xq"])
+        if "xs" in ref:
+            act_ok = act_ok and np.array_equal(f["act_scales"], ref["xs"])
         if "xg" in ref:
             act_ok = act_ok and np.array_equal(f["act_global"].view(np.uint32), ref["xg"].view(np.uint32))
     o = b.first_out[torch.from_numpy(np.asarray(tokens, np.int64))].float().numpy().astype(np.float64)
@@ -315,8 +326,12 @@ def host_info():
         pass
     info["gpu"] = torch.cuda.get_device_properties(0).name
     try:
+        import shutil
         import subprocess
-        r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--showuse", "--showtemp", "--json"],
+        # rocm-smi is a Python script: run it with this interpreter as a child process (its
+        # "#!/usr/bin/env python3" line would re-exec, which a profiled process must not do)
+        smi = os.path.realpath(shutil.which("rocm-smi") or "/opt/rocm/bin/rocm-smi")
+        r = subprocess.run([sys.executable, smi, "--showclocks", "--showpower", "--showuse", "--showtemp", "--json"],
                            capture_output=True, text=True, timeout=30)
         card = next(iter(json.loads(r.stdout).values()))
         keep = ("sclk clock speed:", "mclk clock speed:", "GPU use (%)", "Temperature (Sensor junction) (C)")
@@ -599,7 +614,7 @@ def main():
     res = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "fp8xfp4" if cfgs[0].act == "mxfp8" else "bf16", "data": "synthetic",
+        "vs_baseline": None, "dtype": {"mxfp8": "fp8xfp4", "fp8": "f16"}.get(cfgs[0].act, "bf16"), "data": "synthetic",
         "config": {"workload": args.workload, "T": [c.T for c in cfgs], "H": cfgs[0].H, "I": cfgs[0].I,
                    "E": cfgs[0].E, "top_k": cfgs[0].k, "score": cfgs[0].score, "shared": cfgs[0].shared,
                    "activations": cfgs[0].act,
