@@ -33,6 +33,13 @@ struct ProjLayout {
   size_t fp4_expert, sc_expert;    // bytes per expert
 };
 
+// Raw buffer resource (base, byte range; stride 0, 32-bit data format) for buffer loads with
+// a 32-bit per-lane offset and a scalar offset: the base stays in SGPRs, and an access at or
+// past `bytes` reads 0 instead of memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 __host__ __device__ inline ProjLayout proj_layout(int N, int K) {
   ProjLayout p;
   p.N = N;

@@ -453,8 +453,14 @@ __device__ __forceinline__ void dma16(const void* src, const void* lds_dst) {
   __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
                                    (void __attribute__((address_space(3)))*)lds_dst, 16, 0, 0);
 }
+// The same through a buffer resource: byte offset voff (per lane) + soff (uniform).
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, const void* lds_dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (void __attribute__((address_space(3)))*)lds_dst, 16, (int)voff,
+                                           (int)soff, 0, 0);
+}
 
 template <int V> struct IntC { static constexpr int value = V; };
+
 
 // The K loop of the three-stage pipelines: step(kc, set kc % 3, kind) for kc = 0 .. KC - 1, the
 // set and the kind as compile-time constants. Every chunk but the last two issues the loads of
@@ -522,12 +528,16 @@ __device__ __forceinline__ void prefill_body(const GemmArgs& a, int lin, int NB,
   const int q0 = (item.nb * WAVES + wave) * NSUB;         // the launch covers N exactly
   const int nvalid = min(M, a.offsets[g + 1] - row0);
 
+  // Every load goes through a buffer resource (base and range in SGPRs, a 32-bit offset per
+  // lane, the chunk's offset as the scalar offset): no 64-bit address registers, and no
+  // address arithmetic per chunk.
   // ---- token-tile DMA. Instruction i of this wave fills slots (WAVES i + wave) * 64 .. +63:
-  // row r = 4 (WAVES i + wave) + lane / 16, slot column lane % 16. Byte offsets are 32-bit: the
-  // gate_up gathers token rows from the activation base (T K 2 < 2^32 bytes), the down GEMM
-  // reads its own rows from the tile's first row (a 64-bit base; offsets within the tile).
+  // row r = 4 (WAVES i + wave) + lane / 16, slot column lane % 16. The gate_up gathers token
+  // rows from the activation base (T K 2 <= 2^31 bytes), the down GEMM reads its own rows from
+  // the tile's first row (a 64-bit base; offsets within the tile's nvalid rows).
   uint32_t src_off[D];
-  const char* xbase = (const char*)a.x + (DOWNM ? (size_t)row0 * L.K * 2 : 0);
+  const __amdgpu_buffer_rsrc_t xr =
+      DOWNM ? buffer_rsrc(a.x + (size_t)row0 * L.K, (uint32_t)nvalid * L.K * 2) : buffer_rsrc(a.x, 0xFFFFFFFFu);
 #pragma unroll
   for (int i = 0; i < D; ++i) {
     const int r = 4 * (WAVES * i + wave) + lg;
@@ -537,26 +547,25 @@ __device__ __forceinline__ void prefill_body(const GemmArgs& a, int lin, int NB,
     src_off[i] = (src * (uint32_t)L.K + kp * 8) * 2;
   }
   auto dma = [&](int kc, int st) {
-    const char* base = xbase + (size_t)kc * (KCHUNK * 2);
 #pragma unroll
-    for (int i = 0; i < D; ++i) dma16(base + src_off[i], &tile[st * STAGE + (WAVES * i + wave) * 64]);
+    for (int i = 0; i < D; ++i)
+      dma16(xr, src_off[i], (uint32_t)kc * (KCHUNK * 2), &tile[st * STAGE + (WAVES * i + wave) * 64]);
   };
 
   // ---- weights of this wave: fp4 16 B per lane per chunk; the chunk's two block-scale
   // bytes come from the dword holding them (a 16-bit load would be zero-extended right
-  // after it, which makes the compiler wait for the load at once)
-  const u32x4* wp[NSUB];
-  const uint8_t* sp[NSUB];
-#pragma unroll
-  for (int s = 0; s < NSUB; ++s) {
-    wp[s] = fp4_tile(a, L, g, q0 + s, 0);
-    sp[s] = (const uint8_t*)sc_tile(a, L, g, q0 + s, 0);
-  }
+  // after it, which makes the compiler wait for the load at once). Tile (q, kc) of the group
+  // sits at (q KC + kc) 1 KiB, its scale tile (q, kc / 8) at (q KSG + kc / 8) 1 KiB.
+  const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(a.wfp4 + (size_t)g * L.fp4_expert, (uint32_t)L.fp4_expert);
+  const __amdgpu_buffer_rsrc_t sr = buffer_rsrc(a.wsc + (size_t)g * L.sc_expert, (uint32_t)L.sc_expert);
+  const uint32_t lane_off = (uint32_t)lane * 16;
   auto load_w = [&](int kc, u32x4 (&w)[NSUB], uint32_t (&sb)[NSUB]) {
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) {
-      w[s] = wp[s][(size_t)kc * WAVE];
-      sb[s] = *(const uint32_t*)(sp[s] + (size_t)(kc >> 3) * (WAVE * 16) + (kc & 6) * 2);
+      w[s] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr, lane_off, (uint32_t)((q0 + s) * L.KC + kc) * 1024u, 0));
+      sb[s] = __builtin_amdgcn_raw_buffer_load_b32(
+          sr, lane_off, (uint32_t)((q0 + s) * L.KSG + (kc >> 3)) * 1024u + (uint32_t)(kc & 6) * 2u, 0);
     }
   };
 
@@ -573,16 +582,22 @@ __device__ __forceinline__ void prefill_body(const GemmArgs& a, int lin, int NB,
 #pragma unroll
       for (int t = 0; t < TV; ++t) acc[s][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto mma = [&](int kc, int j, const WOps<true> (&W)[NSUB]) {
-      const u32x4* T0 = &tile[(kc % NBUF) * STAGE];
+    // MFMA step j of the chunk in LDS stage st: the weight operands of step j only are dequantised here (raw
+    // dword j of each tile times its block scale), which keeps 8 fp16 operand registers live
+    // per tile instead of the chunk's 32
+    auto mma = [&](int st, int j, const u32x4 (&rc)[NSUB], const f16x2 (&s2)[NSUB]) {
+      const u32x4* T0 = &tile[st * STAGE];
       const int c = (lg * 4 + j) ^ lds_swz(l16);
       u32x4 bop[TV];
 #pragma unroll
       for (int t = 0; t < TV; ++t) bop[t] = T0[(t * 16 + l16) * 16 + c];
 #pragma unroll
-      for (int s = 0; s < NSUB; ++s)
+      for (int s = 0; s < NSUB; ++s) {
+        const f16x2 sj = j < 2 ? f16x2{s2[s].x, s2[s].x} : f16x2{s2[s].y, s2[s].y};
+        const f16x8 w = dequant8_f16(pick_dword(rc[s], j), sj);
 #pragma unroll
-        for (int t = 0; t < TV; ++t) acc[s][t] = mfma_any(W[s].v[j], bop[t], acc[s][t]);
+        for (int t = 0; t < TV; ++t) acc[s][t] = mfma16x16x32_f16(w, __builtin_bit_cast(f16x8, bop[t]), acc[s][t]);
+      }
     };
     {
       // fp16 rows by LDS DMA into an NBUF-deep ring; raw weights one chunk ahead in two
@@ -595,7 +610,6 @@ __device__ __forceinline__ void prefill_body(const GemmArgs& a, int lin, int NB,
       // covers the LDS stages written by DMA, which the compiler does not track.
       u32x4 rA[NSUB], rB[NSUB];
       uint32_t sA[NSUB], sB[NSUB];
-      WOps<true> W[NSUB];
       load_w(0, rA, sA);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -610,10 +624,11 @@ __device__ __forceinline__ void prefill_body(const GemmArgs& a, int lin, int NB,
         __builtin_amdgcn_sched_barrier(0);
         dma(min(kc + NBUF - 1, L.KC - 1), (kc + NBUF - 1) % NBUF);
         __builtin_amdgcn_sched_barrier(0);
+        f16x2 s2[NSUB];
 #pragma unroll
-        for (int s = 0; s < NSUB; ++s) W[s].make(rc[s], sc[s] >> ((kc & 1) * 16));
+        for (int s = 0; s < NSUB; ++s) s2[s] = e4m3x2_to_f16x2(sc[s] >> ((kc & 1) * 16));   // the low 16 bits
 #pragma unroll
-        for (int j = 0; j < 4; ++j) mma(kc, j, W);
+        for (int j = 0; j < 4; ++j) mma(kc % NBUF, j, rc, s2);
       };
       if (L.KC & 1) {
         step(0, rA, sA, rB, sB);
@@ -887,9 +902,10 @@ constexpr int PRE_NSUB_DN = 2;    // prefill down: 2 tiles per wave
 constexpr int PRE_TSUB = 6;       // prefill: 96 token rows per tile (measured 13% faster than 128 rows)
 constexpr int PRE_NBUF_GU = 3;    // prefill GEMMs: LDS DMA ring depth (3 x 24 KiB)
 constexpr int PRE_WAVES_GU = 8;   // fp16 gate_up and down: 8 waves x 2 tiles = 256 weight rows per token
-constexpr int PRE_OCC_GU = 4;     // tile, two workgroups per CU (128 registers; a few spill). Against 4 waves
-                                  // x 2 tiles at 3 per CU: half the token-tile DMA per MFMA, gate_up 5-11%
-                                  // faster
+constexpr int PRE_OCC_GU = 4;     // tile, two workgroups per CU (128 registers). Against 4 waves x 2 tiles
+                                  // at 3 per CU: half the token-tile DMA per MFMA, gate_up 5-11% faster.
+                                  // One workgroup per CU with weights and tiles two chunks ahead in three
+                                  // sets (192 registers) measured 20% slower: occupancy hides more latency
 constexpr int DEC_MIN_WGS = 2048; // decode: 8 workgroups per CU before 4 tiles per workgroup are used
 
 // Decode split: 4 weight tiles per workgroup (twice the reuse of each token-operand load)
@@ -1021,23 +1037,19 @@ hipError_t launch_h_rescale(uint16_t* h, const int8_t* hexp, const int32_t* hmin
 // the prefill GEMM at 8 waves x 2 tiles (N a multiple of 256); the cold part the decode GEMM at
 // 4 tiles per workgroup (N a multiple of 64).
 template <int MODE_HOT, int MODE_COLD>
-static void launch_split_modes(int tsub, dim3 grid, const GemmArgs& hot, const GemmArgs& cold, int n_hot, int NB,
-                               int nbx, hipStream_t s, const LaunchEvents& ev) {
-  auto go = [&](auto kernel) {
-    if (ev.start || ev.stop)
-      hipExtLaunchKernelGGL(kernel, grid, dim3(512), 0, s, ev.start, ev.stop, 0, hot, cold, n_hot, NB, nbx);
-    else
-      hipLaunchKernelGGL(kernel, grid, dim3(512), 0, s, hot, cold, n_hot, NB, nbx);
-  };
-  if (tsub == 4)
-    go(gemm_split_kernel<MODE_HOT, MODE_COLD, 4, 4>);
+static void launch_split_modes(dim3 grid, const GemmArgs& hot, const GemmArgs& cold, int n_hot, int NB, int nbx,
+                               hipStream_t s, const LaunchEvents& ev) {
+  auto kernel = gemm_split_kernel<MODE_HOT, MODE_COLD, 4, 4>;
+  if (ev.start || ev.stop)
+    hipExtLaunchKernelGGL(kernel, grid, dim3(512), 0, s, ev.start, ev.stop, 0, hot, cold, n_hot, NB, nbx);
   else
-    go(gemm_split_kernel<MODE_HOT, MODE_COLD, 6, 4>);
+    hipLaunchKernelGGL(kernel, grid, dim3(512), 0, s, hot, cold, n_hot, NB, nbx);
 }
 
 hipError_t launch_gemm_split(GemmMode hot_mode, GemmMode cold_mode, int max_tiles, int cold_tiles,
                              const GemmArgs& hot, const GemmArgs& cold, hipStream_t s, const LaunchEvents& ev) {
-  if (hot.N % (16 * PRE_WAVES_GU * 2) || cold.N % 64 || (hot.tile_rows != 64 && hot.tile_rows != 96))
+  // 64-row hot tiles only (the plan's tile height for skewed batches)
+  if (hot.N % (16 * PRE_WAVES_GU * 2) || cold.N % 64 || hot.tile_rows != 64)
     return hipErrorNotSupported;   // declined: nothing launched
   const int NB = hot.N / (16 * PRE_WAVES_GU * 2);
   const int n_hot = NB * ((max_tiles + 7) / 8 * 8);
@@ -1045,13 +1057,12 @@ hipError_t launch_gemm_split(GemmMode hot_mode, GemmMode cold_mode, int max_tile
   const long total = (long)n_hot + (long)nbx * cold_tiles;
   if (total <= 0 || total > (1L << 31) - 1) return hipErrorInvalidValue;
   const dim3 grid((unsigned)total);
-  const int tsub = hot.tile_rows / 16;
   if (hot_mode == GEMM_GATEUP_F16 && cold_mode == GEMM_GATEUP_F16)
-    launch_split_modes<GEMM_GATEUP_F16, GEMM_GATEUP_F16>(tsub, grid, hot, cold, n_hot, NB, nbx, s, ev);
+    launch_split_modes<GEMM_GATEUP_F16, GEMM_GATEUP_F16>(grid, hot, cold, n_hot, NB, nbx, s, ev);
   else if (hot_mode == GEMM_DOWN && cold_mode == GEMM_DOWN)
-    launch_split_modes<GEMM_DOWN, GEMM_DOWN>(tsub, grid, hot, cold, n_hot, NB, nbx, s, ev);
+    launch_split_modes<GEMM_DOWN, GEMM_DOWN>(grid, hot, cold, n_hot, NB, nbx, s, ev);
   else if (hot_mode == GEMM_DOWN && cold_mode == GEMM_DOWN_FP4)
-    launch_split_modes<GEMM_DOWN, GEMM_DOWN_FP4>(tsub, grid, hot, cold, n_hot, NB, nbx, s, ev);
+    launch_split_modes<GEMM_DOWN, GEMM_DOWN_FP4>(grid, hot, cold, n_hot, NB, nbx, s, ev);
   else
     return hipErrorNotSupported;
   return hipGetLastError();

@@ -188,7 +188,7 @@ hipError_t launch_gemm(GemmMode mode, GemmRegime regime, int max_tiles, int est_
 // Skewed prefill batches: the first tile list with the prefill GEMM (hot_mode: GATEUP_F16 or
 // DOWN) and the second with the decode GEMM (cold_mode: GATEUP_F16, DOWN or DOWN_FP4) in one
 // launch. hipErrorNotSupported (nothing launched) for shapes it does not take: hot N not a
-// multiple of 256, tile rows other than 64 or 96; the caller then launches the lists apart.
+// multiple of 256, tile rows other than 64; the caller then launches the lists apart.
 hipError_t launch_gemm_split(GemmMode hot_mode, GemmMode cold_mode, int max_tiles, int cold_tiles,
                              const GemmArgs& hot, const GemmArgs& cold, hipStream_t s,
                              const LaunchEvents& ev = LaunchEvents());
