@@ -89,6 +89,16 @@ struct WOps<false> {
   }
 };
 
+// Operand j (columns 32 (l / 16) + 8j .. +7 of the lane) of one weight tile alone, for loops
+// that dequantise right before each MFMA step: sb holds the chunk's two block-scale bytes.
+__device__ __forceinline__ f16x8 wop_j(const u32x4& w, uint32_t sb, int j, f16x8*) {
+  const f16x2 s = e4m3x2_to_f16x2(sb);
+  return dequant8_f16(pick_dword(w, j), j < 2 ? f16x2{s.x, s.x} : f16x2{s.y, s.y});
+}
+__device__ __forceinline__ bf16x8 wop_j(const u32x4& w, uint32_t sb, int j, bf16x8*) {
+  return dequant8(pick_dword(w, j), e4m3_to_f32(j < 2 ? (sb & 0xFFu) : ((sb >> 8) & 0xFFu)));
+}
+
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 // One scaled MFMA 16x16x128 on raw MX codes: A = 16 weight rows of E2M1 (lane l: row l%16,
@@ -255,15 +265,17 @@ __device__ __forceinline__ void decode_body(const GemmArgs& a, int bx, int slot,
   // round trip before the weight loads; a second-list launch starts after the first list
   const int first = a.tile_first ? a.tile_first[0] : 0;
   const int ntiles = a.tile_count[0];
-  const int g = a.tile_group[first + slot];
-  const int row0 = a.tile_row0[first + slot];
+  // the slot's group and first row are the same for the whole workgroup (readfirstlane tells
+  // the compiler, which keeps them in SGPRs for the buffer resources and addresses)
+  const int g = __builtin_amdgcn_readfirstlane(a.tile_group[first + slot]);
+  const int row0 = __builtin_amdgcn_readfirstlane(a.tile_row0[first + slot]);
   if (slot >= ntiles) return;
   const ProjLayout L = proj_layout(a.N, a.K);
   const int NW = blockDim.x >> 6;
   const int q0 = bx * NSUB;
   const float wgs = a.wgs[g];
   const int nvalid = min(DECODE_TILE_ROWS, a.offsets[g + 1] - row0);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & (WAVE - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & (WAVE - 1);
   const int l16 = lane & 15, lg = lane >> 4;
   const int row = row0 + min(l16, nvalid - 1);            // clamp: extra columns are never stored
   const int kc0 = (wave * L.KC) / NW, kc1 = ((wave + 1) * L.KC) / NW;
@@ -306,17 +318,26 @@ __device__ __forceinline__ void decode_body(const GemmArgs& a, int bx, int slot,
 #pragma unroll
   for (int s = 0; s < NSUB; ++s) acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // weight and block-scale tiles through buffer resources of the group (base in SGPRs; tile
+  // (q, kc) at (q KC + kc) 1 KiB, scale tile (q, kc / 8) at (q KSG + kc / 8) 1 KiB)
+  const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(a.wfp4 + (size_t)g * L.fp4_expert, (uint32_t)L.fp4_expert);
+  const __amdgpu_buffer_rsrc_t sr = buffer_rsrc(a.wsc + (size_t)g * L.sc_expert, (uint32_t)L.sc_expert);
+  const uint32_t lane_off = (uint32_t)lane * 16;
   u32x4 sgv[NSUB];
   int sg_loaded = -1;
   for (int kc = kc0; kc < kc1; ++kc) {
     if ((kc >> 3) != sg_loaded) {
       sg_loaded = kc >> 3;
 #pragma unroll
-      for (int s = 0; s < NSUB; ++s) sgv[s] = *sc_tile(a, L, g, q0 + s, sg_loaded);
+      for (int s = 0; s < NSUB; ++s)
+        sgv[s] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(sr, lane_off, (uint32_t)((q0 + s) * L.KSG + sg_loaded) * 1024u, 0));
     }
     u32x4 wv[NSUB];
 #pragma unroll
-    for (int s = 0; s < NSUB; ++s) wv[s] = *fp4_tile(a, L, g, q0 + s, kc);
+    for (int s = 0; s < NSUB; ++s)
+      wv[s] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr, lane_off, (uint32_t)((q0 + s) * L.KC + kc) * 1024u, 0));
     if constexpr (MX8) {
       const u32x4 b0 = *(const u32x4*)(qrow + (size_t)kc * KCHUNK + 16 * lg);
       const u32x4 b1 = *(const u32x4*)(qrow + (size_t)kc * KCHUNK + 64 + 16 * lg);
@@ -348,13 +369,14 @@ __device__ __forceinline__ void decode_body(const GemmArgs& a, int bx, int slot,
 #pragma unroll
       for (int j = 0; j < 4; ++j) bop[j] = src[j];
     }
+    // step j's weight operands only are dequantised right before its MFMAs (8 live operand
+    // registers per tile, not 32)
+    using WV = std::remove_reference_t<decltype(WOps<F16>::v[0])>;
 #pragma unroll
-    for (int s = 0; s < NSUB; ++s) {
-      WOps<F16> w;
-      w.make(wv[s], chunk_scale_bytes(sgv[s], kc & 7));
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[s] = mfma_any(w.v[j], bop[j], acc[s]);
-    }
+      for (int s = 0; s < NSUB; ++s)
+        acc[s] = mfma_any(wop_j(wv[s], chunk_scale_bytes(sgv[s], kc & 7), j, (WV*)nullptr), bop[j], acc[s]);
   }
 
   f32x4 (*red)[NSUB][WAVE] = (f32x4 (*)[NSUB][WAVE])red_lds;
@@ -519,8 +541,8 @@ __device__ __forceinline__ void prefill_body(const GemmArgs& a, int lin, int NB,
   const PrefillItem item = prefill_item(ntiles, lin, NB);
   const int slot = item.slot;
   if (slot >= ntiles) return;
-  const int g = a.tile_group[slot];
-  const int row0 = a.tile_row0[slot];
+  const int g = __builtin_amdgcn_readfirstlane(a.tile_group[slot]);      // uniform: kept in SGPRs
+  const int row0 = __builtin_amdgcn_readfirstlane(a.tile_row0[slot]);
   const ProjLayout L = proj_layout(a.N, a.K);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & (WAVE - 1);
@@ -751,8 +773,8 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void gemm_prefill_mx8_kernel(GemmA
   const PrefillItem item = prefill_item(ntiles, blockIdx.y * gridDim.x + blockIdx.x, gridDim.x);
   const int slot = item.slot;
   if (slot >= ntiles) return;
-  const int g = a.tile_group[slot];
-  const int row0 = a.tile_row0[slot];
+  const int g = __builtin_amdgcn_readfirstlane(a.tile_group[slot]);      // uniform: kept in SGPRs
+  const int row0 = __builtin_amdgcn_readfirstlane(a.tile_row0[slot]);
   const ProjLayout L = proj_layout(a.N, a.K);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & (WAVE - 1);
