@@ -130,6 +130,23 @@ __device__ __forceinline__ const u32x4* sc_tile(const GemmArgs& a, const ProjLay
   return (const u32x4*)(a.wsc + tile * (WAVE * 16)) + (threadIdx.x & (WAVE - 1));
 }
 
+// The maximum / minimum over lanes l, l ^ 16, l ^ 32 and l ^ 48: the four lanes that hold one
+// token row's 16 columns of a D tile. Cross-row lane swaps (v_permlane16_swap, then
+// v_permlane32_swap, each with both operands the value: the pair then holds the values of
+// lanes l and l ^ 16, resp. l and l ^ 32), no LDS traffic.
+__device__ __forceinline__ float max_row4(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ int min_row4(int v) {
+  const auto a = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
+  const int m = min((int)a[0], (int)a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap((uint32_t)m, (uint32_t)m, false, false);
+  return min((int)b[0], (int)b[1]);
+}
+
 // Epilogue for one 16-feature x 16-token D tile pair (gate, up) of gate_up: h = silu(g) u,
 // or with a finite limit L the clamped silu(min(g, L)) min(max(u, -L), L) (L = +inf leaves
 // g and u as they are), for the 16 h columns hs*16 .. +15 of token row `row` (lane: 4 of
@@ -137,6 +154,25 @@ __device__ __forceinline__ const u32x4* sc_tile(const GemmArgs& a, const ProjLay
 // scaled by 2^e with e chosen on the block's largest |h| (the 4 lanes of the row share it
 // through two lane swaps) and recorded in hexp. All 4 lanes of a row must be active
 // together (they are: they hold the same token).
+// The 4 h values of this lane for a gate/up D tile pair (see epilogue_pair).
+__device__ __forceinline__ f32x4 h_pair(const f32x4& gacc, const f32x4& uacc, float sc, float lim) {
+  auto act = [&](float g, float u) { return silu_mul(fminf(g * sc, lim), fminf(fmaxf(u * sc, -lim), lim)); };
+  return f32x4{act(gacc.x, uacc.x), act(gacc.y, uacc.y), act(gacc.z, uacc.z), act(gacc.w, uacc.w)};
+}
+// The fp16 form of 4 h values of a 16-column block: scaled by 2^e, e putting the block's
+// largest |h| (over the row's 4 lanes) in [2^14, 2^15). Returns e.
+__device__ __forceinline__ int h16_tile(const f32x4& h, u32x2& packed) {
+  const float mx = max_row4(fmaxf(fmaxf(fabsf(h.x), fabsf(h.y)), fmaxf(fabsf(h.z), fabsf(h.w))));
+  // mx = f 2^x with f in [0.5, 1): mx 2^(15 - x) lies in [2^14, 2^15)
+  const int e = min(max(15 - __builtin_amdgcn_frexp_expf(mx), -H_EXP_MAX), H_EXP_MAX);
+  const uint32_t q0 = __builtin_bit_cast(uint16_t, (_Float16)__builtin_ldexpf(h.x, e));
+  const uint32_t q1 = __builtin_bit_cast(uint16_t, (_Float16)__builtin_ldexpf(h.y, e));
+  const uint32_t q2 = __builtin_bit_cast(uint16_t, (_Float16)__builtin_ldexpf(h.z, e));
+  const uint32_t q3 = __builtin_bit_cast(uint16_t, (_Float16)__builtin_ldexpf(h.w, e));
+  packed = u32x2{q0 | (q1 << 16), q2 | (q3 << 16)};
+  return e;
+}
+
 template <int MODE>
 __device__ __forceinline__ void epilogue_pair(const GemmArgs& a, const f32x4& gacc, const f32x4& uacc, float sc,
                                               int row, int hs, float lim) {
@@ -144,17 +180,13 @@ __device__ __forceinline__ void epilogue_pair(const GemmArgs& a, const f32x4& ga
   const int NO = a.N / 2;
   const int col = hs * 16 + 4 * lg;
   const size_t off = (size_t)row * NO + (a.h_natural ? col : h_pos(col));   // 4 columns stay contiguous
-  auto act = [&](float g, float u) {
-    return silu_mul(fminf(g * sc, lim), fminf(fmaxf(u * sc, -lim), lim));
-  };
-  const float h[4] = {act(gacc.x, uacc.x), act(gacc.y, uacc.y), act(gacc.z, uacc.z), act(gacc.w, uacc.w)};
+  const f32x4 hv = h_pair(gacc, uacc, sc, lim);
   if (a.hf) {   // fp32 h in column order for the row quantiser (NVFP4 down GEMM)
-    *(f32x4*)(a.hf + (size_t)row * NO + hs * 16 + 4 * lg) = f32x4{h[0], h[1], h[2], h[3]};
+    *(f32x4*)(a.hf + (size_t)row * NO + hs * 16 + 4 * lg) = hv;
     return;
   }
-  float mx = fmaxf(fmaxf(fabsf(h[0]), fabsf(h[1])), fmaxf(fabsf(h[2]), fabsf(h[3])));
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float h[4] = {hv.x, hv.y, hv.z, hv.w};
+  const float mx = max_row4(fmaxf(fmaxf(fabsf(h[0]), fabsf(h[1])), fmaxf(fabsf(h[2]), fabsf(h[3]))));
   // mx = f 2^x with f in [0.5, 1): mx 2^(15 - x) lies in [2^14, 2^15)
   const int e = min(max(15 - __builtin_amdgcn_frexp_expf(mx), -H_EXP_MAX), H_EXP_MAX);
   uint32_t q[4];
@@ -183,8 +215,7 @@ __device__ __forceinline__ void epilogue_mx8(const GemmArgs& a, const f32x4& g0,
   float A = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) A = fmaxf(A, fabsf(h[i]));
-  A = fmaxf(A, __shfl_xor(A, 16));
-  A = fmaxf(A, __shfl_xor(A, 32));
+  A = max_row4(A);
   const int X = A < 0x1p-118f ? -127 : min(__builtin_amdgcn_frexp_expf(A) - 1 - 8, 127);
   uint32_t w[2] = {0u, 0u};
 #pragma unroll
@@ -210,8 +241,7 @@ __device__ __forceinline__ int row_exp_min4(const int8_t* erow, int nblk, int lg
       m = min(m, (int)(int8_t)(v.y >> (8 * b)));
     }
   }
-  m = min(m, __shfl_xor(m, 16));
-  return min(m, __shfl_xor(m, 32));
+  return min_row4(m);
 }
 
 // 2^d for d <= 0 as fp16 (0 below the fp16 range): the per-block factor that brings h16
@@ -220,21 +250,31 @@ __device__ __forceinline__ _Float16 h_factor(int d) { return (_Float16)__builtin
 
 // Down epilogue for one 16-feature x 16-token D tile: y = acc * sc for the features
 // q*16 .. +15 of token row `row` (lane: 4 of them), stored as fp16 scaled by 2^e with e
-// chosen on the block's largest |y| (shared by the row's 4 lanes through two lane swaps,
-// as for h) and recorded in yexp; half the bytes of fp32 y for the combine to read, with
-// an 11-bit significand. All 4 lanes of a row must be active together.
+// chosen on the block's largest |y| (shared by the row's 4 lanes, as for h) and recorded in
+// yexp; half the bytes of fp32 y for the combine to read, with an 11-bit significand. sc >= 0
+// (or NaN), so max|acc * sc| = max|acc| * sc (rounding is monotone), and acc * (sc 2^e) is
+// acc * sc scaled by 2^e rounded once: the same fp16 values as scaling the rounded product
+// (fp32 underflow aside), for one multiply per value. e is also capped so that sc 2^e stays
+// finite: the cap binds only where max|acc| is below about 2^-112 (never for fp16 products,
+// whose sums are multiples of 2^-48), and then the stored values sit that many binades lower
+// in fp16's range. All 4 lanes of a row must be active together.
+__device__ __forceinline__ int y16_tile(const f32x4& acc, float sc, u32x2& packed) {
+  const float mx = max_row4(fmaxf(fmaxf(fabsf(acc.x), fabsf(acc.y)), fmaxf(fabsf(acc.z), fabsf(acc.w))) * sc);
+  const int e = min(max(15 - __builtin_amdgcn_frexp_expf(mx), -H_EXP_MAX),
+                    min(H_EXP_MAX, 127 - __builtin_amdgcn_frexp_expf(sc)));
+  const float f = __builtin_ldexpf(sc, e);
+  const uint32_t q0 = __builtin_bit_cast(uint16_t, (_Float16)(acc.x * f));
+  const uint32_t q1 = __builtin_bit_cast(uint16_t, (_Float16)(acc.y * f));
+  const uint32_t q2 = __builtin_bit_cast(uint16_t, (_Float16)(acc.z * f));
+  const uint32_t q3 = __builtin_bit_cast(uint16_t, (_Float16)(acc.w * f));
+  packed = u32x2{q0 | (q1 << 16), q2 | (q3 << 16)};
+  return e;
+}
 __device__ __forceinline__ void epilogue_single(const GemmArgs& a, const f32x4& acc, float sc, int row, int q) {
   const int lg = (threadIdx.x & (WAVE - 1)) >> 4;
-  const f32x4 v = acc * sc;
-  float mx = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const int e = min(max(15 - __builtin_amdgcn_frexp_expf(mx), -H_EXP_MAX), H_EXP_MAX);
-  const uint32_t q0 = __builtin_bit_cast(uint16_t, (_Float16)__builtin_ldexpf(v.x, e));
-  const uint32_t q1 = __builtin_bit_cast(uint16_t, (_Float16)__builtin_ldexpf(v.y, e));
-  const uint32_t q2 = __builtin_bit_cast(uint16_t, (_Float16)__builtin_ldexpf(v.z, e));
-  const uint32_t q3 = __builtin_bit_cast(uint16_t, (_Float16)__builtin_ldexpf(v.w, e));
-  *(u32x2*)(a.yout + (size_t)row * a.N + q * 16 + 4 * lg) = u32x2{q0 | (q1 << 16), q2 | (q3 << 16)};
+  u32x2 p;
+  const int e = y16_tile(acc, sc, p);
+  *(u32x2*)(a.yout + (size_t)row * a.N + q * 16 + 4 * lg) = p;
   if (lg == 0) a.yexp[(size_t)row * (a.N / 16) + q] = (int8_t)e;
 }
 
@@ -668,24 +708,109 @@ __device__ __forceinline__ void prefill_body(const GemmArgs& a, int lin, int NB,
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));   // every load in flight lands before the workgroup exits
 
     const float wgs = a.wgs[g];
+    if constexpr (DOWNM) {
+      // y16 of the workgroup's M x COLS block goes through LDS (the ring is free once every
+      // wave is past its last chunk) and leaves as whole row segments of COLS * 2 bytes, 16
+      // bytes per lane, instead of 32-byte pieces of 16 rows per store instruction; the block
+      // exponents follow as COLS / 16 bytes per row. Rows past the tile's valid ones are not
+      // written.
+      constexpr int COLS = WAVES * NSUB * 16, YP = COLS + 8, NBLK = COLS / 16;   // YP: +16 B per row
+      static_assert(M * YP * 2 + M * NBLK <= NBUF * STAGE * 16, "the y block fits the LDS ring");
+      uint16_t* ys = (uint16_t*)tile;
+      int8_t* es = (int8_t*)(ys + M * YP);
+      __syncthreads();   // every wave is done reading the ring
+#pragma unroll
+      for (int t = 0; t < TV; ++t) {
+        const int rr = t * 16 + l16;
+        if (rr >= nvalid) continue;
+        // h16 from gate_up: the row's exponent P (2^-P); NVFP4 / FP8 h: its fp16 decode, the
+        // row's scale
+        const float scl = a.hmin ? __builtin_ldexpf(wgs, -a.hmin[row0 + rr]) : wgs * a.xg[row0 + rr];
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s) {
+          u32x2 p;
+          const int e = y16_tile(acc[s][t], scl, p);
+          *(u32x2*)(ys + rr * YP + (wave * NSUB + s) * 16 + 4 * lg) = p;
+          if (lg == 0) es[rr * NBLK + wave * NSUB + s] = (int8_t)e;
+        }
+      }
+      __syncthreads();
+      const int col0 = item.nb * COLS;
+      for (int i = threadIdx.x; i < nvalid * (COLS / 8); i += NT) {
+        const int r = i / (COLS / 8), c = i - r * (COLS / 8);
+        *(u32x4*)(a.yout + (size_t)(row0 + r) * a.N + col0 + c * 8) = *(const u32x4*)(ys + r * YP + c * 8);
+      }
+      for (int r = threadIdx.x; r < nvalid; r += NT) {
+        int8_t* dst = a.yexp + (size_t)(row0 + r) * (a.N / 16) + col0 / 16;
+        if constexpr (NBLK == 16)
+          *(u32x4*)dst = *(const u32x4*)(es + r * NBLK);
+        else
+          *(u32x2*)dst = *(const u32x2*)(es + r * NBLK);
+      }
+      return;
+    }
+    // gate_up: h of the workgroup's M x HC block (HC = its h columns) likewise through LDS:
+    // fp32 rows for the row quantisers (a.hf), or h16 in plain column order with one exponent
+    // per 16-column block, whose minimum over the workgroup's blocks of a row is folded into
+    // hmin[row] by one atomic per row
+    constexpr int HC = WAVES * NSUB * 8, HNB = HC / 16;
+    const int NO = a.N / 2, hcol0 = item.nb * HC;
+    const float lim = g < a.clamp_groups ? a.swiglu_limit : INFINITY;
+    __syncthreads();   // every wave is done reading the ring
+    if (a.hf) {
+      constexpr int FP = HC + 4;                         // floats per staged row (+16 B)
+      static_assert(M * FP * 4 <= NBUF * STAGE * 16, "the fp32 h block fits the LDS ring");
+      float* hs = (float*)tile;
+#pragma unroll
+      for (int t = 0; t < TV; ++t) {
+        const int rr = t * 16 + l16;
+        if (rr >= nvalid) continue;
+        const float scl = wgs * a.xg[a.tok[row0 + rr]];
+#pragma unroll
+        for (int s = 0; s < NSUB; s += 2)
+          *(f32x4*)(hs + rr * FP + ((wave * NSUB + s) >> 1) * 16 + 4 * lg) = h_pair(acc[s][t], acc[s + 1][t], scl, lim);
+      }
+      __syncthreads();
+      for (int i = threadIdx.x; i < nvalid * (HC / 4); i += NT) {
+        const int r = i / (HC / 4), c = i - r * (HC / 4);
+        *(f32x4*)(a.hf + (size_t)(row0 + r) * NO + hcol0 + c * 4) = *(const f32x4*)(hs + r * FP + c * 4);
+      }
+      return;
+    }
+    constexpr int HP = HC + 8;                           // halfs per staged row (+16 B)
+    static_assert(M * HP * 2 + M * HNB <= NBUF * STAGE * 16, "the h16 block fits the LDS ring");
+    uint16_t* hs = (uint16_t*)tile;
+    int8_t* es = (int8_t*)(hs + M * HP);
 #pragma unroll
     for (int t = 0; t < TV; ++t) {
       const int rr = t * 16 + l16;
       if (rr >= nvalid) continue;
-      const int orow = row0 + rr;
-      if (DOWNM) {
-        // h16 from gate_up: the row's exponent P (2^-P); NVFP4 h: its fp16 decode, the row's
-        // global scale
-        const float scl = a.hmin ? __builtin_ldexpf(wgs, -a.hmin[orow]) : wgs * a.xg[orow];
+      const float scl = wgs * a.xg[a.tok[row0 + rr]];
 #pragma unroll
-        for (int s = 0; s < NSUB; ++s) epilogue_single(a, acc[s][t], scl, orow, q0 + s);
-      } else {
-        const float scl = wgs * a.xg[a.tok[orow]];
-        const float lim = g < a.clamp_groups ? a.swiglu_limit : INFINITY;
-#pragma unroll
-        for (int s = 0; s < NSUB; s += 2)
-          epilogue_pair<MODE>(a, acc[s][t], acc[s + 1][t], scl, orow, (q0 + s) >> 1, lim);
+      for (int s = 0; s < NSUB; s += 2) {
+        u32x2 p;
+        const int e = h16_tile(h_pair(acc[s][t], acc[s + 1][t], scl, lim), p);
+        const int hb = (wave * NSUB + s) >> 1;
+        *(u32x2*)(hs + rr * HP + hb * 16 + 4 * lg) = p;
+        if (lg == 0) es[rr * HNB + hb] = (int8_t)e;
       }
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < nvalid * (HC / 8); i += NT) {
+      const int r = i / (HC / 8), c = i - r * (HC / 8);
+      *(u32x4*)(a.out + (size_t)(row0 + r) * NO + hcol0 + c * 8) = *(const u32x4*)(hs + r * HP + c * 8);
+    }
+    for (int r = threadIdx.x; r < nvalid; r += NT) {
+      const int8_t* er = es + r * HNB;
+      int m = H_EXP_INIT;
+#pragma unroll
+      for (int b = 0; b < HNB; ++b) m = min(m, (int)er[b]);
+      int8_t* dst = a.hexp + (size_t)(row0 + r) * (NO / 16) + hcol0 / 16;
+      if constexpr (HNB == 8)
+        *(u32x2*)dst = *(const u32x2*)er;
+      else
+        *(uint32_t*)dst = *(const uint32_t*)er;
+      if (a.hmin) atomicMin(&a.hmin[row0 + r], m);
     }
   };
   const int tv = (nvalid + 15) >> 4;
