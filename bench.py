@@ -20,7 +20,9 @@ of a decode batch, a seeded token sample of the prefill-sized ones); a mismatch 
 parity record and exits with status 1 before anything is timed. Inputs are resident in HBM
 before timing; each workload first runs untimed for one second (the GPU leaves its idle
 clocks), then W warmup steps, then exactly K timed steps between two device
-synchronisations, eager and as a replayed HIP graph (the serving launch path).
+synchronisations, eager and as a replayed HIP graph (the serving launch path; after its
+capture the graph replays untimed for another second, since the capture's idle time drops
+the clocks again).
 
 The JSON line holds: tokens/s of the headline step (value, graph replay), the per-step
 distribution of K further replays (median, IQR, samples), the layer's HBM rate and its
@@ -686,6 +688,14 @@ def time_steps(batches, steps, warmup):
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         step()
+    # the capture leaves the GPU idle long enough to drop its clocks: replay untimed for
+    # PRIME_S seconds again (without it the first replays of a prefill step ran ~15% slower,
+    # eager steps after the same pause likewise)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < PRIME_S:
+        for _ in range(8):
+            graph.replay()
+        torch.cuda.synchronize()
     for _ in range(warmup):
         graph.replay()
     torch.cuda.synchronize()
@@ -704,6 +714,7 @@ def time_steps(batches, steps, warmup):
     del graph
 
     # stage times: HIP events recorded by moe_run_timed on the stream the layer launches on
+    # (after the replays above, so at the same working clocks)
     stage_tot = {b.cfg.name: [0.0] * m.MOE_NUM_STAGES for b in batches}
     all_ev = {b.cfg.name: [torch.cuda.Event(enable_timing=True) for _ in range(2 * m.MOE_NUM_STAGES)]
               for b in batches}
