@@ -367,8 +367,9 @@ def kernel_stage(name):
     if mm:
         return STAGE_OF_MODE.get(mm.group(1), "gemm")
     for key, st in (("plan", "route"), ("route", "route"), ("combine", "combine"),
-                    ("quant_rows_kernel<float>", "down"), ("mxfp8_rows_kernel<float>", "down"),   # h before down
-                    ("quant", "quant"), ("mxfp8_rows", "quant"), ("rows_to_f16", "quant"), ("pack", "pack"),
+                    ("quant_rows_kernel<float>", "h_prep"), ("mxfp8_rows_kernel<float>", "h_prep"),   # h before down
+                    ("fp8_rows_kernel<float>", "h_prep"), ("h_rescale", "h_prep"),
+                    ("quant", "quant"), ("mxfp8_rows", "quant"), ("fp8_rows", "quant"), ("pack", "pack"),
                     ("group_gs", "pack")):
         if key in name:
             return st

@@ -278,19 +278,19 @@ int moe_run(const moe_plan_t* plan, const void* packed, int32_t T, const uint16_
             const float* router_logits, uint16_t* out, const moe_routing_out* routing,
             void* workspace, size_t workspace_bytes, void* stream);
 
-/* Stages of moe_run, in launch order (for moe_run_timed). */
-#define MOE_STAGE_QUANT 0      /* empty: the activation preparation runs in the ROUTE stage
-                                  (the index is kept for the stage layout) */
+/* Stages of moe_run (for moe_run_timed); launch order ROUTE, GATE_UP, QUANT, DOWN, COMBINE. */
+#define MOE_STAGE_QUANT 0      /* the preparation of h for the down GEMM: the h row quantisation
+                                  (MOE_ACT_NVFP4_ALL, MOE_ACT_FP8_ROW, MOE_ACT_MXFP8 in the
+                                  prefill regime) or the rescale of the h16 rows to their row
+                                  exponent (16-bit h, prefill regime); empty otherwise (the
+                                  activation preparation of x runs in the ROUTE stage) */
 #define MOE_STAGE_ROUTE 1      /* top-k, counts, offsets, permutation, tile list, and the
                                   activation preparation (NVFP4 quantisation of x with, for
                                   prefill-regime batches, its exact fp16 decode; MXFP8
                                   quantisation; or the exact power-of-two rescale of bf16 rows
                                   into fp16) by extra workgroups of the first routing launch */
 #define MOE_STAGE_GATE_UP 2    /* grouped gate/up GEMM + SwiGLU */
-#define MOE_STAGE_DOWN 3       /* grouped down GEMM, with what prepares h for it in
-                                  prefill-regime batches: the h row quantisation
-                                  (MOE_ACT_NVFP4_ALL, MXFP8) or the rescale of the h16 rows
-                                  to their row exponent (16-bit h) */
+#define MOE_STAGE_DOWN 3       /* grouped down GEMM */
 #define MOE_STAGE_COMBINE 4    /* weighted combine */
 #define MOE_NUM_STAGES 5
 
@@ -298,10 +298,10 @@ int moe_run(const moe_plan_t* plan, const void* packed, int32_t T, const uint16_
  * handles (as void*, any may be NULL), created by the caller with timing enabled.
  * For the single-kernel stages (GATE_UP, DOWN, COMBINE) events[2s] and events[2s+1]
  * are stamped by the kernel launch itself at the kernel's start and end, so their
- * elapsed time is the kernel's duration (DOWN with MOE_ACT_NVFP4_ALL or MXFP8, or any
- * prefill-regime DOWN: the start is recorded on `stream` before the h quantisation or the
- * h rescale that precedes the GEMM); for the others (QUANT, ROUTE: zero
- * to four kernels) they are recorded on `stream` right before and after the stage. Results
+ * elapsed time is the kernel's duration (a skewed batch's two tile lists run in one kernel;
+ * where they run as two, the events stamp the first one's start and the second one's end);
+ * for the others (QUANT: zero or one kernel, ROUTE: one to four kernels) they are recorded
+ * on `stream` right before and after the stage. Results
  * are identical to moe_run. ([b12x] "Using it": per-kernel timing logs for tuning.) */
 int moe_run_timed(const moe_plan_t* plan, const void* packed, int32_t T, const uint16_t* x,
                   const float* router_logits, uint16_t* out, const moe_routing_out* routing,

@@ -27,7 +27,7 @@ MOE_STATIC_SCRATCH_BYTES = 64 << 20
 
 MOE_STAGE_QUANT, MOE_STAGE_ROUTE, MOE_STAGE_GATE_UP, MOE_STAGE_DOWN, MOE_STAGE_COMBINE = 0, 1, 2, 3, 4
 MOE_NUM_STAGES = 5
-STAGE_NAMES = ("quant", "route", "gate_up", "down", "combine")
+STAGE_NAMES = ("h_prep", "route", "gate_up", "down", "combine")   # h_prep: MOE_STAGE_QUANT
 
 EXPORTED = ("moe_plan", "moe_plan_destroy", "moe_pack_weights", "moe_pack_router_bias", "moe_run", "moe_run_timed",
             "moe_run_no_alloc",

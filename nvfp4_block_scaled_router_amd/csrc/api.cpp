@@ -378,9 +378,7 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
                           : fp4 ? (decode ? GEMM_GATEUP_FP4 : GEMM_GATEUP_F16)
                                 : (decode && T * k < DECODE_F16_ROWS) ? GEMM_GATEUP_BF16 : GEMM_GATEUP_F16;
   // the activation preparation runs in extra workgroups of the routing stage's first launch
-  // (one wave per row); the QUANT stage is empty
-  if ((e = mark(ev, 2 * MOE_STAGE_QUANT, s)) != hipSuccess) return (int)e;
-  if ((e = mark(ev, 2 * MOE_STAGE_QUANT + 1, s)) != hipSuccess) return (int)e;
+  // (one wave per row); the QUANT stage times the preparation of h between the GEMMs
 
   // prefill batches averaging at most 64 rows per expert: experts with few rows (skewed
   // routing) go to the decode GEMM through a second tile list, in the same launch as the first
@@ -520,14 +518,12 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
   const GemmMode dn_mode = mx8 ? GEMM_DOWN_MX8 : (fp4h && decode) ? GEMM_DOWN_FP4 : GEMM_DOWN;
   const GemmMode dn_cold = fp4h ? GEMM_DOWN_FP4 : dn_mode;
   {
-    const LaunchEvents le = stage_events(ev, MOE_STAGE_DOWN);
-    LaunchEvents first = le;
+    // the QUANT stage brackets the preparation of h (none in the decode regime with 16-bit h)
+    if ((e = mark(ev, 2 * MOE_STAGE_QUANT, s)) != hipSuccess) return (int)e;
     if (fp4h) {   // every h row (T*k routed, T per shared expert) quantised with its own global scale
       g2.xq = ws + plan->ws_hq;
       g2.xs = ws + plan->ws_hs;
       g2.xg = (const float*)(ws + plan->ws_hg);
-      if ((e = mark(ev, 2 * MOE_STAGE_DOWN, s)) != hipSuccess) return (int)e;
-      first.start = nullptr;
       e = launch_quant_rows_f32(g1.hf, T * k + S * T, I, ws + plan->ws_hq, ws + plan->ws_hs,
                                 (float*)(ws + plan->ws_hg), s, decode ? nullptr : (uint16_t*)(ws + plan->ws_h));
       if (!decode) {   // the fp16 decode, scaled per row by hg in the epilogue
@@ -535,8 +531,6 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
         g2.hmin = nullptr;
       }
     } else if (f8) {   // every h row FP8-quantised with its own scale; the GEMMs take its fp16 decode
-      if ((e = mark(ev, 2 * MOE_STAGE_DOWN, s)) != hipSuccess) return (int)e;
-      first.start = nullptr;
       e = launch_fp8_rows_f32(g1.hf, T * k + S * T, I, nullptr, (float*)(ws + plan->ws_hg),
                               (uint16_t*)(ws + plan->ws_h), s);
       g2.x = (const uint16_t*)(ws + plan->ws_h);
@@ -547,19 +541,16 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
       g2.xq = ws + plan->ws_hq;
       g2.xs = ws + plan->ws_hs;
       if (!decode) {   // every h row MXFP8-quantised (E8M0 per 32 columns)
-        if ((e = mark(ev, 2 * MOE_STAGE_DOWN, s)) != hipSuccess) return (int)e;
-        first.start = nullptr;
         e = launch_mxfp8_rows_f32(g1.hf, T * k + S * T, I, ws + plan->ws_hq, ws + plan->ws_hs, s);
       }
     } else if (!decode) {   // h16 rows of the first tile list to their row's common exponent
-      if ((e = mark(ev, 2 * MOE_STAGE_DOWN, s)) != hipSuccess) return (int)e;
-      first.start = nullptr;
       e = launch_h_rescale(g1.out, g1.hexp, pa.hmin, pa.tile_group, pa.tile_row0, pa.tile_count, pa.offsets,
                            max_tiles, M, I, s);
     }
-    if (e == hipSuccess)
-      e = split ? both_lists(dn_mode, dn_cold, g2, LaunchEvents{first.start, le.stop})
-                : launch_gemm(dn_mode, regime, max_tiles, est_tiles, g2, s, first);
+    if (e != hipSuccess) return (int)e;
+    if ((e = mark(ev, 2 * MOE_STAGE_QUANT + 1, s)) != hipSuccess) return (int)e;
+    const LaunchEvents le = stage_events(ev, MOE_STAGE_DOWN);
+    e = split ? both_lists(dn_mode, dn_cold, g2, le) : launch_gemm(dn_mode, regime, max_tiles, est_tiles, g2, s, le);
   }
   if (e != hipSuccess) return (int)e;
 
