@@ -347,6 +347,16 @@ def test_max_tokens_sampled():
     _run_and_check(Case(cfg, tokens=synth.token_sample(cfg, 24)))
 
 
+def test_h16_past_4gib_sampled():
+    """h16 beyond 4 GiB: 20000 tokens x (8 of 8 experts + a shared one) x I = 16384 gives
+    180000 h rows (5.9 GB of h16); every token has rows past byte 2^32 (the later experts' and
+    the shared expert's), which the GEMMs, the rescale and the combine address from 64-bit row
+    bases. Sampled tokens against the oracle."""
+    cfg = synth.MoeConfig("h16-past-4gib", T=20000, H=128, I=16384, E=8, k=8, shared=1, seed=36)
+    assert (cfg.T * cfg.k + cfg.T) * cfg.I * 2 > 2 ** 32
+    _run_and_check(Case(cfg, tokens=synth.token_sample(cfg, 16)))
+
+
 def test_mxfp4_span_too_wide_is_loud():
     """An MXFP4 expert whose E8M0 bytes span more than the NVFP4 form holds exactly (here one
     byte 20 binades under the expert's largest) is rejected by the host validation, and if
