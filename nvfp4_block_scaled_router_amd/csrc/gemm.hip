@@ -835,6 +835,284 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void gemm_prefill_kernel(GemmArgs 
   prefill_body<MODE, NSUB, TSUB, NBUF, WAVES>(a, blockIdx.y * gridDim.x + blockIdx.x, gridDim.x, tile);
 }
 
+// ---------------------------------------------------------------- persistent prefill down
+// The prefill down GEMM with P resident workgroups that each run a sequence of work items
+// (tile slot, column block) and carry the load pipeline across them: the last chunks of an
+// item issue the first weights and token chunks of the next, so its epilogue (y16 staging
+// and the stores of the M x COLS block) runs while that data is in flight, and the stores
+// drain under the next item's MFMAs instead of in one burst per round of workgroups.
+// Items of XCD x (workgroups lin with lin % 8 = x, as the hardware deals them out) are the
+// XCD's slots x per_xcd .. +per_xcd - 1 times the NB column blocks, taken in turn by the
+// XCD's P / 8 workgroups, so the workgroups of an XCD share the tiles' rows and the experts'
+// weights in its L2 as in the one-item-per-workgroup launch. The K chunk count is even (the
+// two weight register sets then start every item in the same order).
+// The epilogue stages y16 through the ring stage of the item's last chunk (the other two
+// hold the next item's first chunks) in passes of 32 rows; block exponents and the rows'
+// factors (hmin or xg, copied by a 4-byte LDS DMA at the item's start) have LDS arrays of
+// their own. Stores go through buffer resources bounded at the item's valid rows, so every
+// lane issues the same number of them (the hardware drops rows past the range) and the wait
+// count of the next item's first chunk is a constant.
+template <int NSUB, int TSUB, int NBUF, int WAVES>
+__device__ __forceinline__ void prefill_down_run(const GemmArgs& a, int lin, int P, int NB, u32x4* tile,
+                                                 int8_t* es, uint32_t* rowf) {
+  static_assert(NBUF == 3 && TSUB == 6 && WAVES == 8 && (NSUB == 2 || NSUB == 1), "the 96-row 8-wave ring");
+  constexpr int M = TSUB * 16, STAGE = M * 16, NT = 64 * WAVES, D = STAGE / NT;
+  constexpr int COLS = WAVES * NSUB * 16, YP = COLS + 8, NBLK = COLS / 16;
+  constexpr int PASS_T = 2, NPASS = TSUB / PASS_T, PASS_ROWS = PASS_T * 16;
+  static_assert(PASS_ROWS * YP * 2 <= STAGE * 16, "a staging pass fits one ring stage");
+  constexpr int SPP = PASS_ROWS * (COLS / 8) / NT;           // 16-byte y stores per thread and pass
+  static_assert(SPP >= 1 && SPP * NT == PASS_ROWS * (COLS / 8), "whole store rounds");
+  constexpr int S = NPASS * SPP + 1;                         // vector stores per thread per epilogue
+  constexpr int W_ISSUE = D * (NBUF - 2);                    // loads a chunk may leave in flight
+  constexpr int NO_LGKM = 15;                                // lgkmcnt field: no wait
+
+  const int ntiles = a.tile_count[0];
+  const int xcd = lin & 7, PX = P >> 3;
+  const int per_xcd = (ntiles + 7) >> 3;
+  const int slot_lo = xcd * per_xcd, slot_hi = min(ntiles, slot_lo + per_xcd);
+  const ProjLayout L = proj_layout(a.N, a.K);
+  const int KC = L.KC;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int l16 = lane & 15, lg = lane >> 4;
+  const uint32_t lane_off = (uint32_t)lane * 16;
+
+  // An item's slot, column block, group and first row are read one item before its row
+  // count and weight scale, which are first needed in the previous item's last chunks and in
+  // its epilogue: neither read waits on the other inside one item.
+  struct Item {
+    int ok, g, row0, nb, nvalid;
+    float wgs;
+  };
+  // The plan's arrays and the weight scales are not written during the launch: read through
+  // the constant address space they become scalar loads, which a vector memory wait (the
+  // epilogue's stores, the next chunks in flight) never has to cover.
+  typedef const int __attribute__((address_space(4))) cint;
+  typedef const float __attribute__((address_space(4))) cfloat;
+  auto item_head = [&](int m) {
+    Item it;
+    const int k = m / NB;
+    it.ok = slot_lo + k < slot_hi;
+    const int slot = it.ok ? slot_lo + k : 0;
+    it.nb = m - k * NB;
+    it.g = ((cint*)a.tile_group)[slot];
+    it.row0 = ((cint*)a.tile_row0)[slot];
+    it.nvalid = 1;
+    it.wgs = 0.f;
+    return it;
+  };
+  auto item_finish = [&](Item& it) {
+    if (it.ok) {
+      it.nvalid = min(M, ((cint*)a.offsets)[it.g + 1] - it.row0);
+      it.wgs = ((cfloat*)a.wgs)[it.g];
+    }
+  };
+
+  // loads of an item: weights of chunk kc into a register set; token rows of chunk kc into
+  // ring stage st (rows past the item's valid ones repeat its last row); the rows' factors
+  auto load_w = [&](const Item& it, int kc, u32x4 (&w)[NSUB], uint32_t (&sb)[NSUB]) {
+    const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(a.wfp4 + (size_t)it.g * L.fp4_expert, (uint32_t)L.fp4_expert);
+    const __amdgpu_buffer_rsrc_t sr = buffer_rsrc(a.wsc + (size_t)it.g * L.sc_expert, (uint32_t)L.sc_expert);
+    const int q0 = (it.nb * WAVES + wave) * NSUB;
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) {
+      w[s] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr, lane_off, (uint32_t)((q0 + s) * L.KC + kc) * 1024u, 0));
+      sb[s] = __builtin_amdgcn_raw_buffer_load_b32(
+          sr, lane_off, (uint32_t)((q0 + s) * L.KSG + (kc >> 3)) * 1024u + (uint32_t)(kc & 6) * 2u, 0);
+    }
+  };
+  auto dma = [&](const Item& it, int kc, int st) {
+    const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(a.x + (size_t)it.row0 * L.K, (uint32_t)it.nvalid * L.K * 2);
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      const int r = 4 * (WAVES * i + wave) + lg;
+      const uint32_t off = ((uint32_t)min(r, it.nvalid - 1) * (uint32_t)L.K + (l16 ^ lds_swz(r)) * 8) * 2;
+      dma16(xr, off, (uint32_t)kc * (KCHUNK * 2), &tile[st * STAGE + (WAVES * i + wave) * 64]);
+    }
+  };
+  // the rows' factors: wave w copies rows 64 w .. 64 w + 63 (zeros past the valid rows)
+  auto dma_rowf = [&](const Item& it) {
+    const void* src = a.hmin ? (const void*)(a.hmin + it.row0) : (const void*)(a.xg + it.row0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(buffer_rsrc(src, (uint32_t)it.nvalid * 4u),
+                                             (void __attribute__((address_space(3)))*)(rowf + wave * 64), 4,
+                                             (int)((wave * 64 + lane) * 4), 0, 0, 0);
+  };
+
+  int m = lin >> 3;
+  Item cur = item_head(m);
+  if (!cur.ok) return;
+  item_finish(cur);
+  Item nxt = item_head(m + PX);
+  u32x4 rA[NSUB], rB[NSUB];
+  uint32_t sA[NSUB], sB[NSUB];
+  load_w(cur, 0, rA, sA);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int c = 0; c < NBUF - 1; ++c) dma(cur, min(c, KC - 1), c);
+  dma_rowf(cur);
+  __builtin_amdgcn_sched_barrier(0);
+  int ring = 0;             // ring stage of the current item's chunk 0
+  int first_wait = W_ISSUE + 1;   // chunk 0: the last token chunk, the factors (+ an epilogue's stores)
+
+  auto run = [&](auto tvc) {
+    constexpr int TV = decltype(tvc)::value;
+    f32x4 acc[NSUB][TV];
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s)
+#pragma unroll
+      for (int t = 0; t < TV; ++t) acc[s][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto mma = [&](int st, int j, const u32x4 (&rc)[NSUB], const f16x2 (&s2)[NSUB]) {
+      const u32x4* T0 = &tile[st * STAGE];
+      const int c = (lg * 4 + j) ^ lds_swz(l16);
+      u32x4 bop[TV];
+#pragma unroll
+      for (int t = 0; t < TV; ++t) bop[t] = T0[(t * 16 + l16) * 16 + c];
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s) {
+        const f16x2 sj = j < 2 ? f16x2{s2[s].x, s2[s].x} : f16x2{s2[s].y, s2[s].y};
+        const f16x8 w = dequant8_f16(pick_dword(rc[s], j), sj);
+#pragma unroll
+        for (int t = 0; t < TV; ++t) acc[s][t] = mfma16x16x32_f16(w, __builtin_bit_cast(f16x8, bop[t]), acc[s][t]);
+      }
+    };
+    // chunk kc in ring stage rs: wait for its data, barrier, issue the weights (wi, wk) and
+    // the token rows (di, dk) into stage ds, consume chunk kc. The body pairs load chunks of
+    // this item only; the last pair issues the next item's first chunks (or this item's last
+    // chunk again when there is none), so the per-chunk work of the body is that of a single
+    // item. The LDS reads of chunk kc - 1 are complete (its MFMAs used them): only vmcnt is
+    // waited.
+    auto step = [&](int kc, int rs, int wait, const Item& wi, int wk, const Item& di, int dk, int ds,
+                    const u32x4 (&rc)[NSUB], const uint32_t (&sc)[NSUB], u32x4 (&rf)[NSUB], uint32_t (&sf)[NSUB]) {
+      if (wait == W_ISSUE + 1) __builtin_amdgcn_s_waitcnt(waitcnt_imm(W_ISSUE + 1, NO_LGKM));
+      else if (wait == W_ISSUE + 1 + S) __builtin_amdgcn_s_waitcnt(waitcnt_imm(W_ISSUE + 1 + S, NO_LGKM));
+      else __builtin_amdgcn_s_waitcnt(waitcnt_imm(W_ISSUE, NO_LGKM));
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      load_w(wi, wk, rf, sf);
+      __builtin_amdgcn_sched_barrier(0);
+      dma(di, dk, ds);
+      __builtin_amdgcn_sched_barrier(0);
+      f16x2 s2[NSUB];
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s) s2[s] = e4m3x2_to_f16x2(sc[s] >> ((kc & 1) * 16));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) mma(rs, j, rc, s2);
+    };
+    // ring stages: chunk kc of the item sits in stage (st0 + kc) % 3; a step's DMA goes two
+    // stages on, which is the stage read one step before
+    const int st0 = ring;
+    int rs = st0;
+    auto adv = [](int x) { return x == NBUF - 1 ? 0 : x + 1; };
+    int kc = 0;
+    for (; kc < KC - 2; kc += 2) {
+      const int r1 = adv(rs), r2 = adv(r1), r3 = adv(r2);
+      step(kc, rs, kc == 0 ? first_wait : W_ISSUE, cur, kc + 1, cur, kc + 2, r2, rA, sA, rB, sB);
+      step(kc + 1, r1, W_ISSUE, cur, kc + 2, cur, kc + 3, r3, rB, sB, rA, sA);
+      rs = r2;
+    }
+    {
+      // the last pair: the next item's weights of chunk 0 and its token chunks 0 and 1
+      const bool n = nxt.ok;
+      const Item& ti = n ? nxt : cur;
+      const int r1 = adv(rs), r2 = adv(r1), r3 = adv(r2);
+      step(kc, rs, kc == 0 ? first_wait : W_ISSUE, cur, kc + 1, ti, n ? 0 : KC - 1, r2, rA, sA, rB, sB);
+      step(kc + 1, r1, W_ISSUE, ti, n ? 0 : KC - 1, ti, n ? 1 : KC - 1, r3, rB, sB, rA, sA);
+    }
+
+    // ---- epilogue of the item through the ring stage of its last chunk. Its per-lane
+    // addresses derive from an opaque copy of the thread id, which keeps the compiler from
+    // computing them once before the item loop and holding them through the K loop.
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int el16 = tid & 15, elg = (tid >> 4) & 3;
+    // y16 of every slice first, packed (half the registers of the fp32 accumulators, which
+    // leaves room for the next item's weights in flight), block exponents straight to LDS
+    u32x2 ypk[NSUB][TV];
+#pragma unroll
+    for (int t = 0; t < TV; ++t) {
+      const uint32_t f = rowf[t * 16 + el16];
+      const float scl = a.hmin ? __builtin_ldexpf(cur.wgs, -(int)f) : cur.wgs * __uint_as_float(f);
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s) {
+        const int e = y16_tile(acc[s][t], scl, ypk[s][t]);
+        if (elg == 0) es[(t * 16 + el16) * NBLK + wave * NSUB + s] = (int8_t)e;
+      }
+    }
+    uint16_t* ys = (uint16_t*)&tile[((st0 + KC - 1) % NBUF) * STAGE];
+    const __amdgpu_buffer_rsrc_t yr =
+        buffer_rsrc(a.yout + (size_t)cur.row0 * a.N, (uint32_t)cur.nvalid * (uint32_t)a.N * 2u);
+    const int col0 = cur.nb * COLS;
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));   // this wave's LDS reads are done
+    __builtin_amdgcn_s_barrier();                      // ... and every wave's: the stage is free
+#pragma unroll
+    for (int p = 0; p < NPASS; ++p) {
+#pragma unroll
+      for (int tt = 0; tt < PASS_T; ++tt) {
+        const int t = p * PASS_T + tt;
+        if (t < TV) {
+#pragma unroll
+          for (int s = 0; s < NSUB; ++s)
+            *(u32x2*)(ys + (tt * 16 + el16) * YP + (wave * NSUB + s) * 16 + 4 * elg) = ypk[s][t];
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+      __builtin_amdgcn_s_barrier();
+#pragma unroll
+      for (int k = 0; k < SPP; ++k) {
+        const int i = tid + k * NT;
+        const int r = i / (COLS / 8), c = i - r * (COLS / 8);
+        const u32x4 v = *(const u32x4*)(ys + r * YP + c * 8);
+        __builtin_amdgcn_raw_buffer_store_b128(v, yr, (uint32_t)((p * PASS_ROWS + r) * a.N + col0 + c * 8) * 2u,
+                                               0, 0);
+      }
+      if (p + 1 < NPASS) {
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));   // the pass's LDS reads are done
+        __builtin_amdgcn_s_barrier();
+      }
+    }
+    {
+      // block exponents: one row of NBLK bytes per thread (threads past the rows store out of range)
+      const __amdgpu_buffer_rsrc_t er =
+          buffer_rsrc(a.yexp + (size_t)cur.row0 * (a.N / 16), (uint32_t)cur.nvalid * (uint32_t)(a.N / 16));
+      const int r = tid;
+      const uint32_t off = r < M ? (uint32_t)(r * (a.N / 16) + col0 / 16) : 0x7FFFFFF0u;
+      const int rs = min(r, M - 1);
+      if constexpr (NBLK == 16)
+        __builtin_amdgcn_raw_buffer_store_b128(*(const u32x4*)(es + rs * NBLK), er, off, 0, 0);
+      else
+        __builtin_amdgcn_raw_buffer_store_b64(*(const u32x2*)(es + rs * NBLK), er, off, 0, 0);
+    }
+  };
+
+  while (true) {
+    item_finish(nxt);
+    const Item nn = item_head(m + 2 * PX);
+    const int tv = (cur.nvalid + 15) >> 4;
+    if (tv > 4) run(IntC<6>());
+    else if (tv > 2) run(IntC<4>());
+    else run(IntC<2>());
+    if (!nxt.ok) break;
+    dma_rowf(nxt);
+    m += PX;
+    ring = (ring + KC) % NBUF;
+    cur = nxt;
+    nxt = nn;
+    first_wait = W_ISSUE + 1 + S;
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));   // every load in flight lands before the workgroup exits
+}
+
+template <int NSUB, int TSUB, int NBUF, int WAVES, int OCC>
+__global__ __launch_bounds__(64 * WAVES, OCC) void gemm_prefill_down_persist_kernel(GemmArgs a, int NB) {
+  // one LDS object (ring, then block exponents, then row factors): with several, the
+  // compiler's LDS-DMA wait tracking puts a vmcnt(0) before every ring read
+  constexpr int RING = NBUF * TSUB * 16 * 16, ES = TSUB * 16 * WAVES * NSUB / 16, RF = 64 * WAVES / 4;
+  __shared__ u32x4 lds[RING + ES + RF];
+  prefill_down_run<NSUB, TSUB, NBUF, WAVES>(a, blockIdx.x, gridDim.x, NB, lds, (int8_t*)(lds + RING),
+                                            (uint32_t*)(lds + RING + ES));
+}
+
 // Skewed prefill batches in one launch: workgroups 0 .. n_hot - 1 run the prefill GEMM over
 // the first tile list (experts with many rows: compute bound), the rest the decode GEMM over
 // the second (experts with a few rows: weight streaming), so the streaming work takes the
@@ -1033,12 +1311,25 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void gemm_prefill_mx8_kernel(GemmA
 
 // ---------------------------------------------------------------------- launch
 
-template <typename K>
-static void launch_k(K kernel, dim3 grid, dim3 block, hipStream_t s, const LaunchEvents& ev, const GemmArgs& a) {
+template <typename K, typename... Args>
+static void launch_k(K kernel, dim3 grid, dim3 block, hipStream_t s, const LaunchEvents& ev, const Args&... args) {
   if (ev.start || ev.stop)
-    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, ev.start, ev.stop, 0, a);
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, ev.start, ev.stop, 0, args...);
   else
-    hipLaunchKernelGGL(kernel, grid, block, 0, s, a);
+    hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
+}
+
+// Compute units of the current device (read once per device).
+static int device_cus() {
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
 }
 
 
@@ -1054,6 +1345,9 @@ constexpr int PRE_OCC_GU = 4;     // tile, two workgroups per CU (128 registers)
                                   // One workgroup per CU with weights and tiles two chunks ahead in three
                                   // sets (192 registers) measured 20% slower: occupancy hides more latency
 constexpr int DEC_MIN_WGS = 2048; // decode: 8 workgroups per CU before 4 tiles per workgroup are used
+constexpr int PERSIST_MAX_KC = 8; // prefill down with at most 8 K chunks (K <= 1024): the persistent
+                                  // launch (Qwen3 K = 768: 133 -> 130 us; FP8 rows 130 -> 124 us). At
+                                  // K = 2048 it measured 5% slower than one workgroup per item
 
 // Decode split: 4 weight tiles per workgroup (twice the reuse of each token-operand load)
 // when that still gives about 8 workgroups per CU, else 2; the K chunks go to the largest
@@ -1089,7 +1383,14 @@ static hipError_t launch_mode(GemmRegime regime, int max_tiles, int est_tiles, c
     constexpr int W = PRE_WAVES_GU, NS = MODE == GEMM_DOWN ? PRE_NSUB_DN : PRE_NSUB_GU;
     const bool t64 = a.tile_rows == 64;
     if (!t64 && a.tile_rows != PREFILL_TILE_ROWS) return hipErrorInvalidValue;
-    if (a.N % (16 * W * NS) == 0)
+    const int NB = a.N / (16 * W * NS);
+    const int kcs = a.K / KCHUNK;
+    if (MODE == GEMM_DOWN && !t64 && a.N % (16 * W * NS) == 0 && kcs % 2 == 0 && kcs <= PERSIST_MAX_KC) {
+      // resident workgroups, two per CU, each running a sequence of (tile, column block) items
+      const int P = min(2 * device_cus() / 8 * 8, ny * NB);
+      launch_k(gemm_prefill_down_persist_kernel<NS, PRE_TSUB, PRE_NBUF_GU, W, PRE_OCC_GU>, dim3(P), dim3(64 * W), s,
+               ev, a, NB);
+    } else if (a.N % (16 * W * NS) == 0)
       launch_k(t64 ? gemm_prefill_kernel<MODE, NS, 4, PRE_NBUF_GU, W, PRE_OCC_GU>
                    : gemm_prefill_kernel<MODE, NS, PRE_TSUB, PRE_NBUF_GU, W, PRE_OCC_GU>,
                dim3(a.N / (16 * W * NS), ny), dim3(64 * W), s, ev, a);

@@ -70,6 +70,12 @@ SMALL = [
     # hidden 128 / 384: the prefill down launch cannot use its widest workgroup and narrows
     synth.MoeConfig("prefill-h128", T=260, H=128, I=256, E=4, k=2, seed=15),
     synth.MoeConfig("prefill-h384-w4a4", T=300, H=384, I=128, E=4, k=2, act="nvfp4", seed=16),
+    # prefill down with at most 8 K chunks runs as resident workgroups over (tile, column
+    # block) items: 2 and 8 chunks, one and two column blocks, tile counts that leave XCDs
+    # without items, ragged last tiles, h16 rows (row exponent) and FP8 rows (row scale)
+    synth.MoeConfig("prefill-persist-kc2", T=700, H=512, I=256, E=8, k=2, seed=31),
+    synth.MoeConfig("prefill-persist-kc8", T=500, H=256, I=1024, E=4, k=2, shared=1, seed=32),
+    synth.MoeConfig("prefill-persist-fp8", T=600, H=512, I=512, E=8, k=2, act="fp8", seed=33),
 ]
 
 
