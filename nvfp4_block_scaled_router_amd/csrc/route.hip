@@ -364,12 +364,21 @@ __global__ __launch_bounds__(PLAN_BLOCK) void plan_count_kernel(PlanArgs a, int3
   if (t < a.T)
     for (int j = 0; j < k; ++j) atomicOr(&bmp[a.ids[(size_t)t * k + j] * WORDS + (tid >> 5)], 1u << (tid & 31));
   __syncthreads();
+  // the picks' ids are read 8 at a time before their ranks are stored (a store between two
+  // reads would make each read wait for the one before it)
   if (t < a.T)
-    for (int j = 0; j < k; ++j) {
-      const uint32_t* be = bmp + a.ids[(size_t)t * k + j] * WORDS;
-      int rank = __popc(be[tid >> 5] & ((1u << (tid & 31)) - 1u));
-      for (int q = 0; q < (tid >> 5); ++q) rank += __popc(be[q]);
-      local_rank[(size_t)t * k + j] = rank;
+    for (int j0 = 0; j0 < k; j0 += 8) {
+      int id[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) id[u] = a.ids[(size_t)t * k + min(j0 + u, k - 1)];   // in bounds: no branch
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (j0 + u < k) {
+          const uint32_t* be = bmp + id[u] * WORDS;
+          int rank = __popc(be[tid >> 5] & ((1u << (tid & 31)) - 1u));
+          for (int q = 0; q < (tid >> 5); ++q) rank += __popc(be[q]);
+          local_rank[(size_t)t * k + j0 + u] = rank;
+        }
     }
   for (int e = tid; e < E; e += PLAN_BLOCK) {
     int c = 0;
@@ -386,14 +395,22 @@ __global__ __launch_bounds__(1024) void plan_scan_kernel(PlanArgs a, int32_t* bl
   int* off = cnt + G;          // [G+1]
   int* tl = off + G + 1;       // [G+1]
   int* ct = tl + G + 1;        // [G+1]
-  // per expert: running base over blocks (block_counts -> exclusive prefix in place)
+  // per expert: running base over blocks (block_counts -> exclusive prefix in place). The
+  // counts of 16 blocks are loaded together before their prefixes are stored: a store to the
+  // array between two loads would make each load wait for the one before it.
   for (int e = tid; e < G; e += blockDim.x) {
     if (e < E) {
       int run = 0;
-      for (int b = 0; b < nblocks; ++b) {
-        const int c = block_counts[(size_t)b * E + e];
-        block_counts[(size_t)b * E + e] = run;
-        run += c;
+      for (int b0 = 0; b0 < nblocks; b0 += 16) {
+        int c[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) c[j] = block_counts[(size_t)min(b0 + j, nblocks - 1) * E + e];
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (b0 + j < nblocks) {
+            block_counts[(size_t)(b0 + j) * E + e] = run;
+            run += c[j];
+          }
       }
       cnt[e] = run;
     } else {
