@@ -155,9 +155,21 @@ __device__ __forceinline__ int min_row4(int v) {
 // through two lane swaps) and recorded in hexp. All 4 lanes of a row must be active
 // together (they are: they hold the same token).
 // The 4 h values of this lane for a gate/up D tile pair (see epilogue_pair).
+// CLAMP false: the limit is +inf (no min / max: the same values for finite g and u).
+template <bool CLAMP = true>
 __device__ __forceinline__ f32x4 h_pair(const f32x4& gacc, const f32x4& uacc, float sc, float lim) {
-  auto act = [&](float g, float u) { return silu_mul(fminf(g * sc, lim), fminf(fmaxf(u * sc, -lim), lim)); };
+  auto act = [&](float g, float u) {
+    return CLAMP ? silu_mul(fminf(g * sc, lim), fminf(fmaxf(u * sc, -lim), lim)) : silu_mul(g * sc, u * sc);
+  };
   return f32x4{act(gacc.x, uacc.x), act(gacc.y, uacc.y), act(gacc.z, uacc.z), act(gacc.w, uacc.w)};
+}
+// Four fp32 values times 2^e (exact) as packed fp16, two per packed convert.
+__device__ __forceinline__ u32x2 pack_f16x4(float a, float b, float c, float d, int e) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const f2 lo = {__builtin_ldexpf(a, e), __builtin_ldexpf(b, e)}, hi = {__builtin_ldexpf(c, e), __builtin_ldexpf(d, e)};
+  return u32x2{__builtin_bit_cast(uint32_t, __builtin_convertvector(lo, h2)),
+               __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, h2))};
 }
 // The fp16 form of 4 h values of a 16-column block: scaled by 2^e, e putting the block's
 // largest |h| (over the row's 4 lanes) in [2^14, 2^15). Returns e.
@@ -165,11 +177,7 @@ __device__ __forceinline__ int h16_tile(const f32x4& h, u32x2& packed) {
   const float mx = max_row4(fmaxf(fmaxf(fabsf(h.x), fabsf(h.y)), fmaxf(fabsf(h.z), fabsf(h.w))));
   // mx = f 2^x with f in [0.5, 1): mx 2^(15 - x) lies in [2^14, 2^15)
   const int e = min(max(15 - __builtin_amdgcn_frexp_expf(mx), -H_EXP_MAX), H_EXP_MAX);
-  const uint32_t q0 = __builtin_bit_cast(uint16_t, (_Float16)__builtin_ldexpf(h.x, e));
-  const uint32_t q1 = __builtin_bit_cast(uint16_t, (_Float16)__builtin_ldexpf(h.y, e));
-  const uint32_t q2 = __builtin_bit_cast(uint16_t, (_Float16)__builtin_ldexpf(h.z, e));
-  const uint32_t q3 = __builtin_bit_cast(uint16_t, (_Float16)__builtin_ldexpf(h.w, e));
-  packed = u32x2{q0 | (q1 << 16), q2 | (q3 << 16)};
+  packed = pack_f16x4(h.x, h.y, h.z, h.w, e);
   return e;
 }
 
@@ -180,7 +188,7 @@ __device__ __forceinline__ void epilogue_pair(const GemmArgs& a, const f32x4& ga
   const int NO = a.N / 2;
   const int col = hs * 16 + 4 * lg;
   const size_t off = (size_t)row * NO + (a.h_natural ? col : h_pos(col));   // 4 columns stay contiguous
-  const f32x4 hv = h_pair(gacc, uacc, sc, lim);
+  const f32x4 hv = lim == INFINITY ? h_pair<false>(gacc, uacc, sc, lim) : h_pair<true>(gacc, uacc, sc, lim);
   if (a.hf) {   // fp32 h in column order for the row quantiser (NVFP4 down GEMM)
     *(f32x4*)(a.hf + (size_t)row * NO + hs * 16 + 4 * lg) = hv;
     return;
@@ -189,10 +197,7 @@ __device__ __forceinline__ void epilogue_pair(const GemmArgs& a, const f32x4& ga
   const float mx = max_row4(fmaxf(fmaxf(fabsf(h[0]), fabsf(h[1])), fmaxf(fabsf(h[2]), fabsf(h[3]))));
   // mx = f 2^x with f in [0.5, 1): mx 2^(15 - x) lies in [2^14, 2^15)
   const int e = min(max(15 - __builtin_amdgcn_frexp_expf(mx), -H_EXP_MAX), H_EXP_MAX);
-  uint32_t q[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) q[i] = __builtin_bit_cast(uint16_t, (_Float16)__builtin_ldexpf(h[i], e));
-  *(u32x2*)(a.out + off) = u32x2{q[0] | (q[1] << 16), q[2] | (q[3] << 16)};
+  *(u32x2*)(a.out + off) = pack_f16x4(h[0], h[1], h[2], h[3], e);
   if (lg == 0) {
     a.hexp[(size_t)row * (NO / 16) + hs] = (int8_t)e;
     if (a.hmin) atomicMin(&a.hmin[row], e);
@@ -761,15 +766,21 @@ __device__ __forceinline__ void prefill_body(const GemmArgs& a, int lin, int NB,
       constexpr int FP = HC + 4;                         // floats per staged row (+16 B)
       static_assert(M * FP * 4 <= NBUF * STAGE * 16, "the fp32 h block fits the LDS ring");
       float* hs = (float*)tile;
+      auto stage = [&](auto clampc) {
+        constexpr bool CL = decltype(clampc)::value != 0;
 #pragma unroll
-      for (int t = 0; t < TV; ++t) {
-        const int rr = t * 16 + l16;
-        if (rr >= nvalid) continue;
-        const float scl = wgs * a.xg[a.tok[row0 + rr]];
+        for (int t = 0; t < TV; ++t) {
+          const int rr = t * 16 + l16;
+          if (rr >= nvalid) continue;
+          const float scl = wgs * a.xg[a.tok[row0 + rr]];
 #pragma unroll
-        for (int s = 0; s < NSUB; s += 2)
-          *(f32x4*)(hs + rr * FP + ((wave * NSUB + s) >> 1) * 16 + 4 * lg) = h_pair(acc[s][t], acc[s + 1][t], scl, lim);
-      }
+          for (int s = 0; s < NSUB; s += 2)
+            *(f32x4*)(hs + rr * FP + ((wave * NSUB + s) >> 1) * 16 + 4 * lg) =
+                h_pair<CL>(acc[s][t], acc[s + 1][t], scl, lim);
+        }
+      };
+      if (lim == INFINITY) stage(IntC<0>());
+      else stage(IntC<1>());
       __syncthreads();
       for (int i = threadIdx.x; i < nvalid * (HC / 4); i += NT) {
         const int r = i / (HC / 4), c = i - r * (HC / 4);
@@ -781,20 +792,25 @@ __device__ __forceinline__ void prefill_body(const GemmArgs& a, int lin, int NB,
     static_assert(M * HP * 2 + M * HNB <= NBUF * STAGE * 16, "the h16 block fits the LDS ring");
     uint16_t* hs = (uint16_t*)tile;
     int8_t* es = (int8_t*)(hs + M * HP);
+    auto stage = [&](auto clampc) {
+      constexpr bool CL = decltype(clampc)::value != 0;
 #pragma unroll
-    for (int t = 0; t < TV; ++t) {
-      const int rr = t * 16 + l16;
-      if (rr >= nvalid) continue;
-      const float scl = wgs * a.xg[a.tok[row0 + rr]];
+      for (int t = 0; t < TV; ++t) {
+        const int rr = t * 16 + l16;
+        if (rr >= nvalid) continue;
+        const float scl = wgs * a.xg[a.tok[row0 + rr]];
 #pragma unroll
-      for (int s = 0; s < NSUB; s += 2) {
-        u32x2 p;
-        const int e = h16_tile(h_pair(acc[s][t], acc[s + 1][t], scl, lim), p);
-        const int hb = (wave * NSUB + s) >> 1;
-        *(u32x2*)(hs + rr * HP + hb * 16 + 4 * lg) = p;
-        if (lg == 0) es[rr * HNB + hb] = (int8_t)e;
+        for (int s = 0; s < NSUB; s += 2) {
+          u32x2 p;
+          const int e = h16_tile(h_pair<CL>(acc[s][t], acc[s + 1][t], scl, lim), p);
+          const int hb = (wave * NSUB + s) >> 1;
+          *(u32x2*)(hs + rr * HP + hb * 16 + 4 * lg) = p;
+          if (lg == 0) es[rr * HNB + hb] = (int8_t)e;
+        }
       }
-    }
+    };
+    if (lim == INFINITY) stage(IntC<0>());   // groups without a SwiGLU limit
+    else stage(IntC<1>());
     __syncthreads();
     for (int i = threadIdx.x; i < nvalid * (HC / 8); i += NT) {
       const int r = i / (HC / 8), c = i - r * (HC / 8);
