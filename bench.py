@@ -363,6 +363,8 @@ def kernel_source_hash():
 def kernel_stage(name):
     """Layer stage of a kernel name from the trace (gate_up / down / route / ...)."""
     import re
+    if "down_persist" in name:    # the persistent prefill down GEMM (its first argument is not a mode)
+        return "down"
     mm = re.search(r"gemm_\w+_kernel<(\d+)", name)
     if mm:
         return STAGE_OF_MODE.get(mm.group(1), "gemm")
