@@ -67,6 +67,11 @@ SMALL = [
     synth.MoeConfig("decode-wide-w4a4", T=100, H=256, I=128, E=64, k=4, act="nvfp4", seed=30),
     synth.MoeConfig("decode-wide-general", T=90, H=256, I=128, E=64, k=4, score="sqrt_softplus", bias_sigma=0.5,
                     seed=29),
+    # small decode grids load all K chunks of a wave at once: 2 chunks per wave (bf16 x),
+    # 3 per wave with one wave's range across an 8-chunk scale group, fp16 x (256 rows)
+    synth.MoeConfig("decode-pf-h1024", T=5, H=1024, I=256, E=16, k=4, seed=34),
+    synth.MoeConfig("decode-pf-h1536", T=6, H=1536, I=256, E=16, k=4, score="sigmoid", seed=35),
+    synth.MoeConfig("decode-pf-f16", T=64, H=1024, I=128, E=64, k=4, seed=36),
     # hidden 128 / 384: the prefill down launch cannot use its widest workgroup and narrows
     synth.MoeConfig("prefill-h128", T=260, H=128, I=256, E=4, k=2, seed=15),
     synth.MoeConfig("prefill-h384-w4a4", T=300, H=384, I=128, E=4, k=2, act="nvfp4", seed=16),
