@@ -235,16 +235,23 @@ __device__ __forceinline__ void epilogue_mx8(const GemmArgs& a, const f32x4& g0,
 }
 
 // Smallest h block exponent of a row (nblk bytes, nblk a multiple of 8), read as 8-byte
-// words split over the row's 4 lanes l16 + 16 lg and combined through two lane swaps.
+// words split over the row's 4 lanes l16 + 16 lg and combined through two lane swaps. Up to
+// four words per lane are loaded together (indices clamped to the row: a repeated word leaves
+// the minimum as it is), so a row of up to 128 blocks takes one memory round trip.
 __device__ __forceinline__ int row_exp_min4(const int8_t* erow, int nblk, int lg) {
+  const int nw = nblk / 8;
   int m = H_EXP_INIT;
-  for (int w = lg; w < nblk / 8; w += 4) {
-    const u32x2 v = *(const u32x2*)(erow + 8 * w);
+  for (int w0 = lg; w0 < nw; w0 += 16) {
+    u32x2 v[4];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      m = min(m, (int)(int8_t)(v.x >> (8 * b)));
-      m = min(m, (int)(int8_t)(v.y >> (8 * b)));
-    }
+    for (int u = 0; u < 4; ++u) v[u] = *(const u32x2*)(erow + 8 * min(w0 + 4 * u, nw - 1));
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        m = min(m, (int)(int8_t)(v[u].x >> (8 * b)));
+        m = min(m, (int)(int8_t)(v[u].y >> (8 * b)));
+      }
   }
   return min_row4(m);
 }
