@@ -345,7 +345,7 @@ def host_info():
 
 # ------------------------------------------------------------ rocprofv3 summaries
 
-STAGE_OF_MODE = {"0": "gate_up", "1": "gate_up", "3": "gate_up", "5": "gate_up", "2": "down", "4": "down", "6": "down"}
+STAGE_OF_MODE = {"0": "gate_up", "1": "gate_up", "5": "gate_up", "2": "down", "4": "down", "6": "down"}
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ("gemm.hip", "common.hpp", "kernels.hpp", "api.cpp")   # kernels + their launch choices
 

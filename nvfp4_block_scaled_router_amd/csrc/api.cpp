@@ -27,11 +27,6 @@ constexpr int MAX_GROUPS = 64;
 // prefill: experts with at most this many rows run through the decode GEMM (second tile list)
 constexpr int COLD_ROWS = 16;
 constexpr int SPLIT_TILE_ROWS = 64;   // the first list's tile height in skewed and MX8 batches
-// decode batches with at least this many routed rows take bf16 activations through the exact
-// fp16 rescale (one more launch, half the dequant VALU work in the gate_up GEMM): measured
-// 3% faster per step at T = 32 and 64 (top-8), slower at T = 8
-constexpr int DECODE_F16_ROWS = 256;
-
 size_t align_up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -366,9 +361,10 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
   float* xg = ((fp4 || f8) && r.act_global) ? r.act_global : (float*)(ws + plan->ws_xg);
   uint16_t* x16 = (uint16_t*)(ws + plan->ws_x16);
   const bool decode = use_decode(T, k, E);
-  // Activation preparation: NVFP4 row quantisation, or the exact power-of-two rescale into
-  // fp16 (its 1-op dequant route); decode batches below DECODE_F16_ROWS rows feed their bf16
-  // rows to the GEMM as they are (the extra launch costs more than the dequant saves there).
+  // Activation preparation: NVFP4 row quantisation, or the exact power-of-two rescale of bf16
+  // rows into fp16 (its 1-op dequant route) for every batch: it rides on the routing launch,
+  // and feeding small decode batches' bf16 rows to a bf16 MFMA instead (twice the dequant
+  // work) measured slower (Qwen3 decode step at T = 1, 8, 32, 64: 0.2362 vs 0.2401 ms).
   // Prefill batches with NVFP4 x take its exact fp16 decode (written by the quantiser beside
   // the codes, the row's global scale in the epilogue) through the fp16 GEMM, whose token
   // tiles arrive by LDS DMA; decode batches read the codes.
@@ -376,7 +372,7 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
   const GemmMode gu_mode = mx8 ? GEMM_GATEUP_MX8
                           : f8 ? GEMM_GATEUP_F16
                           : fp4 ? (decode ? GEMM_GATEUP_FP4 : GEMM_GATEUP_F16)
-                                : (decode && T * k < DECODE_F16_ROWS) ? GEMM_GATEUP_BF16 : GEMM_GATEUP_F16;
+                                : GEMM_GATEUP_F16;
   // the activation preparation runs in extra workgroups of the routing stage's first launch
   // (one wave per row); the QUANT stage times the preparation of h between the GEMMs
 
@@ -407,8 +403,7 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
   ra.side = mx8                           ? SIDE_MXFP8
             : f8                            ? SIDE_FP8
             : fp4                           ? SIDE_NVFP4
-            : gu_mode == GEMM_GATEUP_F16    ? SIDE_F16
-                                            : SIDE_NONE;
+                                            : SIDE_F16;
   ra.side_x = x;
   ra.side_K = H;
   ra.side_q = f8 ? r.act_packed : xq;      // FP8 codes only when the caller asks for them
@@ -450,7 +445,7 @@ static int run_impl(const moe_plan_t* plan, const void* packed, int32_t T, const
   g1.N = 2 * I;
   g1.K = H;
   g1.tok = pa.tok;
-  g1.x = gu_mode == GEMM_GATEUP_BF16 ? x : x16;
+  g1.x = x16;
   g1.xq = xq;
   g1.xs = xs;
   g1.xg = xg;

@@ -6,11 +6,9 @@
 
 namespace nvmoe {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -63,23 +61,6 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
   return (b & 0x80u) ? -v : v;
 }
 
-// Eight E2M1 codes (nibble i of w = element i) times one fp32 block scale, as bf16.
-// q * s has at most 2 + 4 significant bits and lies in [2^-10, 2688], so the fp32
-// product is exact and its upper half is the exact bf16 value.
-__device__ __forceinline__ bf16x8 dequant8(uint32_t w, float s) {
-  u32x4 o;
-  f32x2 f;
-  f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
-  o.x = __builtin_amdgcn_perm(__float_as_uint(f.y * s), __float_as_uint(f.x * s), 0x07060302u);
-  f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
-  o.y = __builtin_amdgcn_perm(__float_as_uint(f.y * s), __float_as_uint(f.x * s), 0x07060302u);
-  f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
-  o.z = __builtin_amdgcn_perm(__float_as_uint(f.y * s), __float_as_uint(f.x * s), 0x07060302u);
-  f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
-  o.w = __builtin_amdgcn_perm(__float_as_uint(f.y * s), __float_as_uint(f.x * s), 0x07060302u);
-  return __builtin_bit_cast(bf16x8, o);
-}
-
 // Two E4M3fn bytes (bits 0..15) -> two fp16 values, by the hardware fp8 convert (scale
 // operand 1). Every E4M3 value, subnormals included, is exact in fp16.
 __device__ __forceinline__ f16x2 e4m3x2_to_f16x2(uint32_t b2) {
@@ -123,12 +104,6 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
   u += 0x7FFFu + ((u >> 16) & 1u);
   return u >> 16;
-}
-
-__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
-
-__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 // silu(g) * u with the hardware reciprocal (about 1 ulp); exp(-g) = inf gives -0.

@@ -15,17 +15,15 @@
 //
 // Dequant route: the per-16 E4M3 block scale is not a power of two and covers half
 // an E8M0 block of the scaled MFMA, so each weight q*s (at most 6 significant bits) is
-// rebuilt exactly in registers and fed to a 16-bit MFMA with fp32 accumulation:
-//  - fp16 (prefill GEMMs, decode down, NVFP4 activations): the convert applies the power
-//    of two of s (its scale operand is exponent-only), one packed fp16 multiply the
-//    significand: 1 VALU op per weight. Activations are fp16 too: bf16 rows rescaled
-//    exactly by a power of two into fp16 range (undone in the epilogue), NVFP4 rows
-//    decoded the same way as the weights, h16 as stored. V_MFMA_F32_16X16X32_F16.
-//  - bf16 (gate_up of small bf16 batches, weight-streaming bound): the caller's bf16 rows
-//    go straight into the MFMA with no activation pass; fp4->fp32 convert, fp32 multiply,
-//    truncating pack, 2 VALU ops per weight. V_MFMA_F32_16X16X32_BF16.
-// Both routes form every product q*s*x exactly. Global scales (per expert, per activation
-// row) are constant over K and are applied once in the epilogue.
+// rebuilt exactly in registers as fp16 and fed to the fp16 MFMA (V_MFMA_F32_16X16X32_F16)
+// with fp32 accumulation: the convert applies the power of two of s (its scale operand is
+// exponent-only), one packed fp16 multiply the significand, 1 VALU op per weight.
+// Activations are fp16 too: bf16 rows rescaled exactly by a power of two into fp16 range
+// (undone in the epilogue), NVFP4 and FP8 rows decoded exactly, h16 as stored. (A bf16 route
+// for small decode batches, bf16 rows straight into a bf16 MFMA at 2 VALU ops per weight,
+// measured slower once the rescale rode on the routing launch.) Every product q*s*x is
+// formed exactly. Global scales (per expert, per activation row) are constant over K and
+// are applied once in the epilogue.
 //
 // Operand roles: MFMA A = 16 weight rows x 32 k (one lane: row l%16, 8 consecutive
 // k of a 32-wide lane group), MFMA B = 32 k x 16 tokens (lane: token l%16, the same
@@ -61,12 +59,9 @@ __device__ __forceinline__ int h_pos(int f) {
 // 16-byte piece index inside a chunk: stored piece p holds k-piece h_piece(p).
 __device__ __forceinline__ int h_piece(int p) { return ((p & 3) << 2) | (p >> 2); }
 
-// Dequantised MFMA A operands of one 16-row weight tile for one 128-column chunk: fp16
-// for gate_up, bf16 for down (j-th operand = columns 32*(l/16) + 8j .. +7 of the lane).
-template <bool F16>
-struct WOps;
-template <>
-struct WOps<true> {
+// Dequantised fp16 MFMA operands of one 16-row NVFP4 tile for one 128-column chunk (j-th
+// operand = columns 32*(l/16) + 8j .. +7 of the lane).
+struct WOps {
   f16x8 v[4];
   __device__ __forceinline__ void make(const u32x4& w, uint32_t sb) {
     const f16x2 s = e4m3x2_to_f16x2(sb);
@@ -77,26 +72,12 @@ struct WOps<true> {
     v[3] = dequant8_f16(w.w, sc);
   }
 };
-template <>
-struct WOps<false> {
-  bf16x8 v[4];
-  __device__ __forceinline__ void make(const u32x4& w, uint32_t sb) {
-    const float s0 = e4m3_to_f32(sb & 0xFFu), s1 = e4m3_to_f32((sb >> 8) & 0xFFu);
-    v[0] = dequant8(w.x, s0);
-    v[1] = dequant8(w.y, s0);
-    v[2] = dequant8(w.z, s1);
-    v[3] = dequant8(w.w, s1);
-  }
-};
 
 // Operand j (columns 32 (l / 16) + 8j .. +7 of the lane) of one weight tile alone, for loops
 // that dequantise right before each MFMA step: sb holds the chunk's two block-scale bytes.
-__device__ __forceinline__ f16x8 wop_j(const u32x4& w, uint32_t sb, int j, f16x8*) {
+__device__ __forceinline__ f16x8 wop_j(const u32x4& w, uint32_t sb, int j) {
   const f16x2 s = e4m3x2_to_f16x2(sb);
   return dequant8_f16(pick_dword(w, j), j < 2 ? f16x2{s.x, s.x} : f16x2{s.y, s.y});
-}
-__device__ __forceinline__ bf16x8 wop_j(const u32x4& w, uint32_t sb, int j, bf16x8*) {
-  return dequant8(pick_dword(w, j), e4m3_to_f32(j < 2 ? (sb & 0xFFu) : ((sb >> 8) & 0xFFu)));
 }
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
@@ -113,11 +94,8 @@ __device__ __forceinline__ f32x4 mfma_mx(const u32x4& a, uint32_t sa, const u32x
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 0, 0, (int)sa, 0, (int)sb);
 }
 
-__device__ __forceinline__ f32x4 mfma_any(const f16x8& a, const u32x4& b, f32x4 c) {
+__device__ __forceinline__ f32x4 mfma_f16(const f16x8& a, const u32x4& b, f32x4 c) {
   return mfma16x16x32_f16(a, __builtin_bit_cast(f16x8, b), c);
-}
-__device__ __forceinline__ f32x4 mfma_any(const bf16x8& a, const u32x4& b, f32x4 c) {
-  return mfma16x16x32(a, __builtin_bit_cast(bf16x8, b), c);
 }
 
 __device__ __forceinline__ const u32x4* fp4_tile(const GemmArgs& a, const ProjLayout& L, int g, int q, int kc) {
@@ -309,7 +287,6 @@ constexpr int DEC_MAX_WAVES = 4;   // measured best of 4 / 8 / 16 on the decode 
 // of LDS for the reduction.
 template <int MODE, int NSUB, int MAXW>
 __device__ __forceinline__ void decode_body(const GemmArgs& a, int bx, int slot, f32x4* red_lds) {
-  constexpr bool F16 = MODE != GEMM_GATEUP_BF16;           // fp16 MFMA (bf16 x: bf16 MFMA)
   constexpr bool MX8 = MODE == GEMM_GATEUP_MX8 || MODE == GEMM_DOWN_MX8;   // scaled MFMA on MX codes
   constexpr bool DOWNM = MODE == GEMM_DOWN || MODE == GEMM_DOWN_FP4 || MODE == GEMM_DOWN_MX8;
   // the slot's entries are read together with the count (slots past it hold stale values
@@ -332,7 +309,7 @@ __device__ __forceinline__ void decode_body(const GemmArgs& a, int bx, int slot,
   const int row = row0 + min(l16, nvalid - 1);            // clamp: extra columns are never stored
   const int kc0 = (wave * L.KC) / NW, kc1 = ((wave + 1) * L.KC) / NW;
 
-  const uint16_t* xrow = nullptr;                          // 16-bit token rows (fp16/bf16 x, h16)
+  const uint16_t* xrow = nullptr;                          // 16-bit token rows (fp16 x, h16)
   const int8_t* erow = nullptr;                            // h block exponents of the row
   const uint8_t* qrow = nullptr;
   const uint8_t* srow = nullptr;
@@ -363,7 +340,7 @@ __device__ __forceinline__ void decode_body(const GemmArgs& a, int bx, int slot,
     } else {
       xrow = a.x + (size_t)t * L.K;
     }
-    if (F16) sc *= a.xg[t];
+    sc *= a.xg[t];
   }
 
   f32x4 acc[NSUB];
@@ -403,7 +380,7 @@ __device__ __forceinline__ void decode_body(const GemmArgs& a, int bx, int slot,
     if (MODE == GEMM_GATEUP_FP4 || MODE == GEMM_DOWN_FP4) {
       const u32x4 xv = *(const u32x4*)(qrow + (size_t)kc * 64 + lg * 16);
       const uint32_t sp = *(const uint16_t*)(srow + (size_t)kc * 8 + 2 * lg);
-      WOps<true> xo;
+      WOps xo;
       xo.make(xv, sp);
 #pragma unroll
       for (int j = 0; j < 4; ++j) bop[j] = __builtin_bit_cast(u32x4, xo.v[j]);
@@ -423,12 +400,11 @@ __device__ __forceinline__ void decode_body(const GemmArgs& a, int bx, int slot,
     }
     // step j's weight operands only are dequantised right before its MFMAs (8 live operand
     // registers per tile, not 32)
-    using WV = std::remove_reference_t<decltype(WOps<F16>::v[0])>;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int s = 0; s < NSUB; ++s)
-        acc[s] = mfma_any(wop_j(wv[s], chunk_scale_bytes(sgv[s], kc & 7), j, (WV*)nullptr), bop[j], acc[s]);
+        acc[s] = mfma_f16(wop_j(wv[s], chunk_scale_bytes(sgv[s], kc & 7), j), bop[j], acc[s]);
   }
 
   f32x4 (*red)[NSUB][WAVE] = (f32x4 (*)[NSUB][WAVE])red_lds;
@@ -1424,7 +1400,7 @@ static hipError_t launch_mode(GemmRegime regime, int max_tiles, int est_tiles, c
     else
       return hipErrorInvalidValue;   // gate_up: N = 2I, a multiple of 256
   } else {
-    return hipErrorInvalidValue;     // the NVFP4 and bf16 modes run in the decode regime only
+    return hipErrorInvalidValue;     // the NVFP4 modes run in the decode regime only
   }
   return hipSuccess;
 }
@@ -1455,7 +1431,6 @@ hipError_t launch_gemm(GemmMode mode, GemmRegime regime, int max_tiles, int est_
   hipError_t e = hipSuccess;
   switch (mode) {
     case GEMM_GATEUP_F16: e = launch_mode<GEMM_GATEUP_F16>(regime, max_tiles, est_tiles, a, s, ev); break;
-    case GEMM_GATEUP_BF16: e = launch_mode<GEMM_GATEUP_BF16>(regime, max_tiles, est_tiles, a, s, ev); break;
     case GEMM_GATEUP_FP4: e = launch_mode<GEMM_GATEUP_FP4>(regime, max_tiles, est_tiles, a, s, ev); break;
     case GEMM_DOWN: e = launch_mode<GEMM_DOWN>(regime, max_tiles, est_tiles, a, s, ev); break;
     case GEMM_DOWN_FP4: e = launch_mode<GEMM_DOWN_FP4>(regime, max_tiles, est_tiles, a, s, ev); break;

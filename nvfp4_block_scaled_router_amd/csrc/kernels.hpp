@@ -114,8 +114,8 @@ hipError_t launch_pack(const PackArgs& a, hipStream_t s);
 // scales [rows][K/32]; gate_up gathers token rows, down reads its own rows) run the scaled
 // MFMA on the raw codes, no dequantisation.
 enum GemmMode {
-  GEMM_GATEUP_F16 = 0, GEMM_GATEUP_FP4 = 1, GEMM_DOWN = 2, GEMM_GATEUP_BF16 = 3, GEMM_DOWN_FP4 = 4,
-  GEMM_GATEUP_MX8 = 5, GEMM_DOWN_MX8 = 6
+  GEMM_GATEUP_F16 = 0, GEMM_GATEUP_FP4 = 1, GEMM_DOWN = 2, GEMM_DOWN_FP4 = 4, GEMM_GATEUP_MX8 = 5,
+  GEMM_DOWN_MX8 = 6
 };
 
 struct GemmArgs {
@@ -126,8 +126,7 @@ struct GemmArgs {
   int N, K;                // projection rows, columns
   // token rows
   const int32_t* tok;      // row -> token (gather modes)
-  const uint16_t* x;       // activations [T][K]: fp16 rescaled (GATEUP_F16) or bf16 (GATEUP_BF16);
-                           // h16 [rows][K] (DOWN)
+  const uint16_t* x;       // activations [T][K]: fp16 rescaled (GATEUP_F16); h16 [rows][K] (DOWN)
   const uint8_t* xq;       // [T][K/2]  (GATEUP_FP4; DOWN_FP4: [rows][K/2])
   const uint8_t* xs;       // [T][K/16] (DOWN_FP4: [rows][K/16])
   const float* xg;         // [T] per-row activation factor applied in the epilogue (DOWN_FP4: [rows])

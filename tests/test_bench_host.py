@@ -18,7 +18,7 @@ import bench  # noqa: E402
     # GEMM kernels: the first template argument is the GEMM mode
     ("void nvmoe::gemm_prefill_kernel<0, 2, 6, 3, 8, 4>(nvmoe::GemmArgs)", "gate_up"),
     ("void nvmoe::gemm_prefill_kernel<2, 2, 6, 3, 8, 4>(nvmoe::GemmArgs)", "down"),
-    ("void nvmoe::gemm_decode_kernel<3, 2, 4>(nvmoe::GemmArgs)", "gate_up"),
+    ("void nvmoe::gemm_decode_kernel<0, 2, 4>(nvmoe::GemmArgs)", "gate_up"),
     ("void nvmoe::gemm_decode_kernel<4, 2, 4>(nvmoe::GemmArgs)", "down"),
     ("void nvmoe::gemm_prefill_mx8_kernel<5, 2, 4, 2, 96>(nvmoe::GemmArgs)", "gate_up"),
     ("void nvmoe::gemm_split_kernel<2, 4, 4, 4>(nvmoe::GemmArgs, nvmoe::GemmArgs, int, int, int)", "down"),
