@@ -287,8 +287,9 @@ int moe_run(const moe_plan_t* plan, const void* packed, int32_t T, const uint16_
 #define MOE_STAGE_ROUTE 1      /* top-k, counts, offsets, permutation, tile list, and the
                                   activation preparation (NVFP4 quantisation of x with, for
                                   prefill-regime batches, its exact fp16 decode; MXFP8
-                                  quantisation; or the exact power-of-two rescale of bf16 rows
-                                  into fp16) by extra workgroups of the first routing launch */
+                                  quantisation; FP8 row quantisation with its exact fp16 decode;
+                                  or the exact power-of-two rescale of bf16 rows into fp16) by
+                                  extra workgroups of the first routing launch */
 #define MOE_STAGE_GATE_UP 2    /* grouped gate/up GEMM + SwiGLU */
 #define MOE_STAGE_DOWN 3       /* grouped down GEMM */
 #define MOE_STAGE_COMBINE 4    /* weighted combine */
