@@ -89,6 +89,32 @@ def test_small(cfg):
     _run_and_check(Case(cfg))
 
 
+def _random_configs(n, seed=20261203):
+    """Seeded layer shapes across the regimes (decode / skewed / prefill tiles, persistent and
+    one-item down, 1-2 column blocks), activation formats and routers; every token is checked.
+    T is capped so that the FP64 oracle stays within about a second per case."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        H = int(rng.choice([128, 256, 384, 512, 768, 1024, 2048]))
+        I = int(rng.choice([128, 256, 384, 512, 768, 1024]))
+        E = int(rng.integers(1, 65))
+        k = int(rng.integers(1, min(8, E) + 1))
+        act = str(rng.choice(["bf16", "bf16", "nvfp4", "nvfp4_all", "fp8", "mxfp8"]))
+        wfmt = "mxfp4" if act == "mxfp8" else "nvfp4"
+        T = int(rng.integers(1, 2001))
+        T = max(1, min(T, int(3e8 // (k * H * I))))
+        out.append(synth.MoeConfig(f"rand{i}-T{T}-H{H}-I{I}-E{E}-k{k}-{act}", T=T, H=H, I=I, E=E, k=k,
+                                   score=str(rng.choice(["softmax", "sigmoid"])), shared=int(rng.integers(0, 2)),
+                                   act=act, wfmt=wfmt, seed=700 + i))
+    return out
+
+
+@pytest.mark.parametrize("cfg", _random_configs(32), ids=lambda c: c.name)
+def test_random_shapes(cfg):
+    _run_and_check(Case(cfg))
+
+
 # router and activation variants: sqrt-softplus scores, selection-only bias, the group step,
 # routed scaling, un-renormalised weights, clamped SwiGLU (routed experts only)
 VARIANTS = [
