@@ -115,6 +115,40 @@ def test_random_shapes(cfg):
     _run_and_check(Case(cfg))
 
 
+def _random_variant_configs(n, seed=20261204):
+    """Seeded layers with the router and activation variants drawn at random: sqrt-softplus
+    scores, a selection-only bias, the group step, routed scaling, no renormalisation, a
+    clamped SwiGLU, MXFP4 weights; every token is checked."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        H = int(rng.choice([128, 256, 512, 1024]))
+        I = int(rng.choice([128, 256, 384, 512]))
+        n_group = int(rng.choice([1, 1, 2, 4, 8]))
+        E = n_group * int(rng.integers(max(1, 4 // n_group), 65 // n_group + 1))
+        topk_group = int(rng.integers(1, n_group + 1))
+        k = int(rng.integers(1, min(8, topk_group * (E // n_group)) + 1))
+        act = str(rng.choice(["bf16", "nvfp4", "nvfp4_all", "fp8", "mxfp8"]))
+        wfmt = "mxfp4" if act == "mxfp8" or rng.random() < 0.3 else "nvfp4"
+        if act == "fp8":
+            wfmt = "nvfp4"
+        T = int(rng.integers(1, 1201))
+        T = max(1, min(T, int(3e8 // (k * H * I))))
+        out.append(synth.MoeConfig(
+            f"rvar{i}-T{T}-H{H}-I{I}-E{E}-k{k}-{act}-{wfmt}", T=T, H=H, I=I, E=E, k=k,
+            score=str(rng.choice(["softmax", "sigmoid", "sqrt_softplus"])), shared=int(rng.integers(0, 2)),
+            act=act, wfmt=wfmt, seed=800 + i,
+            bias_sigma=float(rng.choice([0.0, 0.0, 0.3])), n_group=n_group, topk_group=topk_group,
+            renorm=bool(rng.random() < 0.8), routed_scaling=float(rng.choice([1.0, 1.0, 2.5])),
+            swiglu_limit=(None if rng.random() < 0.6 else float(rng.choice([0.0, 0.05, 7.0])))))
+    return out
+
+
+@pytest.mark.parametrize("cfg", _random_variant_configs(16), ids=lambda c: c.name)
+def test_random_variants(cfg):
+    _run_and_check(Case(cfg))
+
+
 # router and activation variants: sqrt-softplus scores, selection-only bias, the group step,
 # routed scaling, un-renormalised weights, clamped SwiGLU (routed experts only)
 VARIANTS = [
