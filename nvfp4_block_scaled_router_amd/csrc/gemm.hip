@@ -1535,36 +1535,46 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
   const int c = blockIdx.y * (COMBINE_COLS / 4) + threadIdx.x;   // 4-column group index
   if (c >= a.H / 4) return;
   // row r's columns 4c .. 4c+3: fp16 values and their block's exponent, exactly in fp32
-  auto load = [&](int r) {
-    const u32x2 q = *(const u32x2*)(a.y + (size_t)r * a.H + c * 4);
-    const int e = a.yexp[(size_t)r * (a.H / 16) + (c >> 2)];
-    auto f = [&](uint32_t b) { return __builtin_ldexpf((float)__builtin_bit_cast(_Float16, (uint16_t)b), -e); };
-    return f32x4{f(q.x & 0xFFFFu), f(q.x >> 16), f(q.y & 0xFFFFu), f(q.y >> 16)};
+  struct Raw {
+    u32x2 q;
+    int e;
+  };
+  auto fetch = [&](int r) {
+    Raw v;
+    v.q = *(const u32x2*)(a.y + (size_t)r * a.H + c * 4);
+    v.e = a.yexp[(size_t)r * (a.H / 16) + (c >> 2)];
+    return v;
+  };
+  auto decode = [](const Raw& v) {
+    auto f = [&](uint32_t b) { return __builtin_ldexpf((float)__builtin_bit_cast(_Float16, (uint16_t)b), -v.e); };
+    return f32x4{f(v.q.x & 0xFFFFu), f(v.q.x >> 16), f(v.q.y & 0xFFFFu), f(v.q.y >> 16)};
   };
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  int j = 0;
-  for (; j + 4 <= a.k; j += 4) {
-    f32x4 v[4];
+  // 8 rows per round, all loaded before any is summed: indices past k are clamped to the
+  // last row and the loaded values pinned (otherwise each load is sunk into the branch of its
+  // term and waited for there); the terms past k are skipped, so the sum runs in j order
+  for (int j = 0; j < a.k; j += 8) {
+    Raw v[8];
+    float wq[8];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) v[q] = load(s_inv[j + q]);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float wj = s_w[j + q];
-      acc.x = __builtin_fmaf(wj, v[q].x, acc.x);
-      acc.y = __builtin_fmaf(wj, v[q].y, acc.y);
-      acc.z = __builtin_fmaf(wj, v[q].z, acc.z);
-      acc.w = __builtin_fmaf(wj, v[q].w, acc.w);
+    for (int q = 0; q < 8; ++q) {
+      v[q] = fetch(s_inv[min(j + q, a.k - 1)]);
+      wq[q] = s_w[min(j + q, a.k - 1)];
     }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) asm volatile("" : "+v"(v[q].q.x), "+v"(v[q].q.y), "+v"(v[q].e), "+v"(wq[q]));
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (j + q < a.k) {
+        const f32x4 d = decode(v[q]);
+        const float wj = wq[q];
+        acc.x = __builtin_fmaf(wj, d.x, acc.x);
+        acc.y = __builtin_fmaf(wj, d.y, acc.y);
+        acc.z = __builtin_fmaf(wj, d.z, acc.z);
+        acc.w = __builtin_fmaf(wj, d.w, acc.w);
+      }
   }
-  for (; j < a.k; ++j) {
-    const f32x4 v = load(s_inv[j]);
-    const float wj = s_w[j];
-    acc.x = __builtin_fmaf(wj, v.x, acc.x);
-    acc.y = __builtin_fmaf(wj, v.y, acc.y);
-    acc.z = __builtin_fmaf(wj, v.z, acc.z);
-    acc.w = __builtin_fmaf(wj, v.w, acc.w);
-  }
-  for (int sh = 0; sh < a.S; ++sh) acc += load(rows + sh * a.T + t);
+  for (int sh = 0; sh < a.S; ++sh) acc += decode(fetch(rows + sh * a.T + t));
   *(u32x2*)(a.out + (size_t)t * a.H + c * 4) =
       u32x2{f32_to_bf16_rne(acc.x) | (f32_to_bf16_rne(acc.y) << 16),
             f32_to_bf16_rne(acc.z) | (f32_to_bf16_rne(acc.w) << 16)};

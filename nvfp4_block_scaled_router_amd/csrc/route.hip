@@ -77,14 +77,21 @@ __device__ __forceinline__ void route_token_general(const RouteArgs& r, int t, i
   const int lane = threadIdx.x & (WAVE - 1);
   const int E = r.E, k = r.k;
   const float* lg = r.logits + (size_t)t * E;
-  float lv[EPL];
-  float lmax = -INFINITY;
+  // logits and biases at clamped indices, not guarded ones, so that all loads issue together
+  // (values past E are never used)
+  float lv[EPL], bv[EPL];
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
-    const int e = lane + WAVE * i;
-    lv[i] = e < E ? lg[e] : 0.0f;
-    if (e < E) lmax = fmaxf(lmax, lv[i]);
+    lv[i] = lg[min(lane + WAVE * i, E - 1)];
+    bv[i] = 0.0f;
   }
+  if (r.bias)
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) bv[i] = r.bias[min(lane + WAVE * i, E - 1)];
+  float lmax = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i)
+    if (lane + WAVE * i < E) lmax = fmaxf(lmax, lv[i]);
   double denom = 1.0;
   if (r.score == 0) {
     lmax = wave_max_f32(lmax);
@@ -109,7 +116,7 @@ __device__ __forceinline__ void route_token_general(const RouteArgs& r, int t, i
       else v = sqrt(fmax(l, 0.0) + log1p(exp(-fabs(l))));
       sc[i] = v;
       float kf = (float)v;
-      if (r.bias) kf = kf + r.bias[e];
+      if (r.bias) kf = kf + bv[i];
       key[i] = order_key(kf);
     }
   }
@@ -270,6 +277,50 @@ __device__ __forceinline__ void write_tiles(const PlanArgs& a, const int* cnt, c
   }
 }
 
+// One wave: from the group counts cnt[0..G), the exclusive prefix sums of the counts (off),
+// of the list-1 tile counts (tl) and of the list-2 tile counts (ct), each with its total at
+// [G]. Lane l holds the run of ceil(G/64) <= OFFSETS_SEG consecutive groups from l ceil(G/64)
+// in registers: the counts are read together (indices clamped, not guarded), the three scans
+// run side by side, and every array is written once.
+constexpr int OFFSETS_SEG = 8;
+__device__ __forceinline__ void offsets_wave(const int* cnt, int* off, int* tl, int* ct, int G, int M, int cold) {
+  const int lane = threadIdx.x & 63;
+  const int seg = (G + 63) / 64, i0 = lane * seg;
+  int c[OFFSETS_SEG], t1[OFFSETS_SEG], t2[OFFSETS_SEG];
+#pragma unroll
+  for (int u = 0; u < OFFSETS_SEG; ++u) c[u] = cnt[min(i0 + u, G - 1)];
+  int s0 = 0, s1 = 0, s2 = 0;
+#pragma unroll
+  for (int u = 0; u < OFFSETS_SEG; ++u) {
+    t1[u] = 0;
+    t2[u] = 0;
+    if (u < seg) {                              // the run length is the same in every lane
+      if (i0 + u >= G) c[u] = 0;               // past the end: contributes nothing
+      tile_counts(c[u], M, cold, &t1[u], &t2[u]);
+      s0 += c[u];
+      s1 += t1[u];
+      s2 += t2[u];
+    }
+  }
+  const int e0 = wave_inclusive_scan(s0), e1 = wave_inclusive_scan(s1), e2 = wave_inclusive_scan(s2);
+  int r0 = e0 - s0, r1 = e1 - s1, r2 = e2 - s2;
+#pragma unroll
+  for (int u = 0; u < OFFSETS_SEG; ++u)
+    if (u < seg && i0 + u < G) {
+      off[i0 + u] = r0;
+      tl[i0 + u] = r1;
+      ct[i0 + u] = r2;
+      r0 += c[u];
+      r1 += t1[u];
+      r2 += t2[u];
+    }
+  if (lane == 63) {
+    off[G] = e0;
+    tl[G] = e1;
+    ct[G] = e2;
+  }
+}
+
 // Small batches (T <= 64, T*k <= 4096): routing, counts, offsets, permutation and tile
 // list in one 1024-thread workgroup, everything in LDS. 64 DPP rows route up to 64 tokens
 // at once (E <= 256; wider expert sets use one wave per token); one wave runs the two
@@ -311,12 +362,16 @@ __global__ __launch_bounds__(1024) void plan_small_kernel(RouteArgs r, PlanArgs 
   }
   __syncthreads();
   if (tid < 64) {
-    for (int g = tid; g < G; g += 64) {
-      off[g] = cnt[g];
-      tile_counts(cnt[g], M, a.cold_rows, &tl[g], &ct[g]);
+    if (G <= 64 * OFFSETS_SEG) {
+      offsets_wave(cnt, off, tl, ct, G, M, a.cold_rows);
+    } else {
+      for (int g = tid; g < G; g += 64) {
+        off[g] = cnt[g];
+        tile_counts(cnt[g], M, a.cold_rows, &tl[g], &ct[g]);
+      }
+      wave_dual_scan(off, tl, G);   // same wave wrote the inputs: no barrier needed
+      wave_scan(ct, G);
     }
-    wave_dual_scan(off, tl, G);   // same wave wrote the inputs: no barrier needed
-    wave_scan(ct, G);
   }
   __syncthreads();
   for (int i = tid; i < rows; i += nthr) {

@@ -15,6 +15,19 @@ __device__ __forceinline__ uint32_t order_key(float v) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Logits l, l + STRIDE, ... of one token (lane l of a group of STRIDE lanes). The indices
+// are clamped to the last expert rather than guarded, and each value is pinned by an empty
+// asm statement: a load whose value is used only where e < E is otherwise sunk into a branch
+// of its own and waited for there, one memory round trip per load. The values past E are
+// never used.
+template <int N, int STRIDE>
+__device__ __forceinline__ void load_logits(const float* __restrict__ row, int E, int l, float* v) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = row[min(l + STRIDE * i, E - 1)];
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" : "+v"(v[i]));
+}
+
 // Inverse of order_key (the value of a pick, without touching memory again).
 __device__ __forceinline__ float key_value(uint32_t key) {
   return __uint_as_float((key & 0x80000000u) ? (key ^ 0x80000000u) : ~key);
@@ -103,12 +116,11 @@ __device__ __forceinline__ void route_token(const float* __restrict__ lg, int E,
                                             int32_t* __restrict__ ids_user, float* __restrict__ w_user,
                                             int t, int32_t* s_ids = nullptr, float* s_w = nullptr) {
   const int lane = threadIdx.x & (WAVE - 1);
+  float v[EPL];
+  load_logits<EPL, WAVE>(lg + (size_t)t * E, E, lane, v);
   uint32_t key[EPL];
 #pragma unroll
-  for (int i = 0; i < EPL; ++i) {
-    const int e = lane + WAVE * i;
-    key[i] = e < E ? order_key(lg[(size_t)t * E + e]) : 0u;
-  }
+  for (int i = 0; i < EPL; ++i) key[i] = lane + WAVE * i < E ? order_key(v[i]) : 0u;
   uint32_t taken = 0;
   auto local_best = [&](uint32_t& bh, uint32_t& bl) {
     bh = 0u;
@@ -172,35 +184,81 @@ __device__ __forceinline__ float row_sum(float v) {
   return v;
 }
 
+// Descending sort of a lane's N keys in registers: Batcher's odd-even merge sort, a fixed
+// network of compare-exchanges (19 for N = 8), fully unrolled.
+template <int N>
+__device__ __forceinline__ void sort_desc(uint64_t* a) {
+#pragma unroll
+  for (int p = 1; p < N; p <<= 1)
+#pragma unroll
+    for (int kk = p; kk >= 1; kk >>= 1)
+#pragma unroll
+      for (int j = kk % p; j + kk < N; j += 2 * kk)
+#pragma unroll
+        for (int i = 0; i < kk; ++i)
+          if (i + j + kk < N && (i + j) / (2 * p) == (i + j + kk) / (2 * p)) {
+            const uint64_t x = a[i + j], y = a[i + j + kk];
+            a[i + j] = x > y ? x : y;
+            a[i + j + kk] = x > y ? y : x;
+          }
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_max_u32(uint32_t v) {
+  // old value 0, the identity of an unsigned max, so that the move fuses into v_max_u32_dpp
+  const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+  return o > v ? o : v;
+}
+// Max over the 16 lanes of a row; every lane of the row gets it.
+__device__ __forceinline__ uint32_t row_max_u32(uint32_t v) {
+  v = dpp_max_u32<0xB1>(v);    // quad_perm [1,0,3,2]
+  v = dpp_max_u32<0x4E>(v);    // quad_perm [2,3,0,1]
+  v = dpp_max_u32<0x141>(v);   // row_half_mirror
+  return dpp_max_u32<0x140>(v);   // row_mirror
+}
+
 // Lane r16 of the row holds experts r16, r16+16, ... (EPR = ceil(E/16) <= 16) as 64-bit
-// pick keys; its candidate is the max of its keys, a picked expert's key is cleared to 0.
-// Everything is branch free except the final stores. Pick j (k <= 64) is kept by lane
-// j % 16 in slot j / 16.
+// pick keys, sorted descending in registers, so its best untaken key is always key[0].
+// A pick is the row maximum of the lanes' first keys, found word by word: the largest
+// high word (the logit), then among the lanes holding it the largest low word (the lowest
+// expert id); the winning lane shifts its keys up by one. Everything is branch free except
+// the final stores. Pick j (k <= 64) is kept by lane j % 16 in slot j / 16.
 template <int EPR>
 __device__ __forceinline__ void route_token_row(const float* __restrict__ lg, int E, int k, int score, int t,
                                                 int32_t* __restrict__ ids, float* __restrict__ w,
                                                 int32_t* __restrict__ ids_user, float* __restrict__ w_user,
                                                 int32_t* s_ids) {
   const int r16 = threadIdx.x & 15;
+  float v[EPR];
+  load_logits<EPR, 16>(lg + (size_t)t * E, E, r16, v);
   uint64_t key[EPR];
 #pragma unroll
   for (int i = 0; i < EPR; ++i) {
     const int e = r16 + 16 * i;
-    key[i] = e < E ? pick_key(order_key(lg[(size_t)t * E + e]), e) : 0ull;
+    key[i] = e < E ? pick_key(order_key(v[i]), e) : 0ull;
   }
+  sort_desc<EPR>(key);
   uint64_t pk[4] = {0ull, 0ull, 0ull, 0ull};
   uint64_t key0 = 0ull;
-  for (int j = 0; j < k; ++j) {
-    uint64_t cand = key[0];
 #pragma unroll
-    for (int i = 1; i < EPR; ++i) cand = key[i] > cand ? key[i] : cand;
-    const uint64_t win = row_max_u64(cand);           // row-uniform
-    const int e = (int)~(uint32_t)win;
-    if (j == 0) key0 = win;
+  for (int q = 0; q < 4; ++q) {
+    const int jend = min(k, 16 * q + 16);
+    for (int j = 16 * q; j < jend; ++j) {
+      const uint32_t hi = (uint32_t)(key[0] >> 32), lo = (uint32_t)key[0];
+      const uint32_t mh = row_max_u32(hi);
+      const uint32_t ml = row_max_u32(hi == mh ? lo : 0u);
+      const uint64_t win = ((uint64_t)mh << 32) | ml;   // row-uniform
+      // the shift as a bit mask made opaque to the compiler: written as selects, it becomes an
+      // indexed extract (a compare chain per key)
+      uint32_t m = key[0] == win ? 0xFFFFFFFFu : 0u;
+      asm volatile("" : "+v"(m));
+      const uint64_t m64 = ((uint64_t)m << 32) | m;
 #pragma unroll
-    for (int i = 0; i < EPR; ++i) key[i] = (r16 + 16 * i == e) ? 0ull : key[i];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) pk[q] = (16 * q + r16 == j) ? win : pk[q];
+      for (int i = 0; i + 1 < EPR; ++i) key[i] = (key[i + 1] & m64) | (key[i] & ~m64);
+      key[EPR - 1] &= ~m64;
+      if (q == 0 && j == 0) key0 = win;
+      pk[q] = r16 == j - 16 * q ? win : pk[q];
+    }
   }
   const float lmax = key_value((uint32_t)(key0 >> 32));
   float sv[4];
