@@ -577,6 +577,7 @@ __device__ __forceinline__ void prefill_body(const GemmArgs& a, int lin, int NB,
   const int l16 = lane & 15, lg = lane >> 4;
   const int q0 = (item.nb * WAVES + wave) * NSUB;         // the launch covers N exactly
   const int nvalid = min(M, a.offsets[g + 1] - row0);
+  const float wgs = a.wgs[g];                             // read with the tile entry, not after the K loop
 
   // Every load goes through a buffer resource (base and range in SGPRs, a 32-bit offset per
   // lane, the chunk's offset as the scalar offset): no 64-bit address registers, and no
@@ -695,7 +696,41 @@ __device__ __forceinline__ void prefill_body(const GemmArgs& a, int lin, int NB,
     }
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));   // every load in flight lands before the workgroup exits
 
-    const float wgs = a.wgs[g];
+    // the epilogue factors of the lane's rows t * 16 + l16, t < TV, all loaded together (row
+    // indices clamped to the tile's valid rows, values pinned: a load used only where the row
+    // is valid is otherwise sunk into that branch and waited for there, one round trip per
+    // slice, two for the gate_up's token -> row-scale chain)
+    float rsc[TV];
+    if constexpr (DOWNM) {
+      if (a.hmin) {
+        int hm[TV];
+#pragma unroll
+        for (int t = 0; t < TV; ++t) hm[t] = a.hmin[row0 + min(t * 16 + l16, nvalid - 1)];
+#pragma unroll
+        for (int t = 0; t < TV; ++t) asm volatile("" : "+v"(hm[t]));
+#pragma unroll
+        for (int t = 0; t < TV; ++t) rsc[t] = __builtin_ldexpf(wgs, -hm[t]);
+      } else {
+#pragma unroll
+        for (int t = 0; t < TV; ++t) rsc[t] = a.xg[row0 + min(t * 16 + l16, nvalid - 1)];
+#pragma unroll
+        for (int t = 0; t < TV; ++t) asm volatile("" : "+v"(rsc[t]));
+#pragma unroll
+        for (int t = 0; t < TV; ++t) rsc[t] *= wgs;
+      }
+    } else {
+      int tk[TV];
+#pragma unroll
+      for (int t = 0; t < TV; ++t) tk[t] = a.tok[row0 + min(t * 16 + l16, nvalid - 1)];
+#pragma unroll
+      for (int t = 0; t < TV; ++t) asm volatile("" : "+v"(tk[t]));
+#pragma unroll
+      for (int t = 0; t < TV; ++t) rsc[t] = a.xg[tk[t]];
+#pragma unroll
+      for (int t = 0; t < TV; ++t) asm volatile("" : "+v"(rsc[t]));
+#pragma unroll
+      for (int t = 0; t < TV; ++t) rsc[t] *= wgs;
+    }
     if constexpr (DOWNM) {
       // y16 of the workgroup's M x COLS block goes through LDS (the ring is free once every
       // wave is past its last chunk) and leaves as whole row segments of COLS * 2 bytes, 16
@@ -713,7 +748,7 @@ __device__ __forceinline__ void prefill_body(const GemmArgs& a, int lin, int NB,
         if (rr >= nvalid) continue;
         // h16 from gate_up: the row's exponent P (2^-P); NVFP4 / FP8 h: its fp16 decode, the
         // row's scale
-        const float scl = a.hmin ? __builtin_ldexpf(wgs, -a.hmin[row0 + rr]) : wgs * a.xg[row0 + rr];
+        const float scl = rsc[t];
 #pragma unroll
         for (int s = 0; s < NSUB; ++s) {
           u32x2 p;
@@ -755,7 +790,7 @@ __device__ __forceinline__ void prefill_body(const GemmArgs& a, int lin, int NB,
         for (int t = 0; t < TV; ++t) {
           const int rr = t * 16 + l16;
           if (rr >= nvalid) continue;
-          const float scl = wgs * a.xg[a.tok[row0 + rr]];
+          const float scl = rsc[t];
 #pragma unroll
           for (int s = 0; s < NSUB; s += 2)
             *(f32x4*)(hs + rr * FP + ((wave * NSUB + s) >> 1) * 16 + 4 * lg) =
@@ -781,7 +816,7 @@ __device__ __forceinline__ void prefill_body(const GemmArgs& a, int lin, int NB,
       for (int t = 0; t < TV; ++t) {
         const int rr = t * 16 + l16;
         if (rr >= nvalid) continue;
-        const float scl = wgs * a.xg[a.tok[row0 + rr]];
+        const float scl = rsc[t];
 #pragma unroll
         for (int s = 0; s < NSUB; s += 2) {
           u32x2 p;
