@@ -226,13 +226,24 @@ PARITY_SAMPLE = {"qwen3-30b-a3b-prefill": 48, "skewed-w4a4": 48, "skewed-w4a4-al
                  "deepseek-v3-noaux-t8192": 4, "deepseek-v4-flash-t8192": 8, "deepseek-v4-flash-w4a8-t8192": 8,
                  "qwen3-30b-a3b-w4a8-t4096": 48}
 PARITY_REL_L2, PARITY_MAX_OVER_RMS, PARITY_W_ABS = 5e-3, 2e-2, 1e-6
+PARITY_MAX_FLIPS = 2     # h codes per token that may lie on the other side of a rounding boundary
 
 
-def _parity_check(b, ref, tokens):
+def _beyond_bf16(o, r, rms):
+    """max(|o - r| - half a bf16 ulp of r) / rms: the error beyond the output's own rounding."""
+    _, ex = np.frexp(r)
+    half_ulp = np.where(r == 0, 0.0, np.ldexp(1.0, ex - 9))
+    return float(max((np.abs(o - r) - half_ulp).max(), 0.0) / rms)
+
+
+def _parity_check(b, ref, tokens, flips=None):
     """The first run of batch b against the oracle's result `ref` for `tokens`: routing ids,
     counts, offsets and permutation bit-exact, routing weights within 1e-6, quantised
     activations bit-exact, and the output within relL2 <= 5e-3 and a max error beyond the
-    bf16 output rounding <= 2e-2 RMS (the parity tests' bar)."""
+    bf16 output rounding <= 2e-2 RMS (the parity tests' bar). For the variants that quantise
+    h, `flips(t)` lists the output changes of the other rounding of token position t's h
+    elements within a tiny distance of a code boundary (found on the oracle side): as in the
+    parity tests, a token over the max bar may take up to two of them."""
     f = b.first
     routing_ok = (np.array_equal(f["topk_ids"], ref["ids"]) and np.array_equal(f["expert_counts"], ref["counts"])
                   and np.array_equal(f["expert_offsets"], ref["offsets"]) and np.array_equal(f["perm"], ref["perm"])
@@ -252,10 +263,28 @@ def _parity_check(b, ref, tokens):
     half_ulp = np.where(r == 0, 0.0, np.ldexp(1.0, ex - 9))
     rel = float(np.linalg.norm(o - r) / np.linalg.norm(r))
     beyond = float(max((d - half_ulp).max(), 0.0) / rms)
+    used = 0
+    if flips is not None and beyond > PARITY_MAX_OVER_RMS:
+        worst = 0.0
+        for t in range(r.shape[0]):
+            alt = r[t].copy()
+            if _beyond_bf16(o[t], alt, rms) > PARITY_MAX_OVER_RMS:
+                cand = flips(t)
+                for _ in range(PARITY_MAX_FLIPS):
+                    if not cand or _beyond_bf16(o[t], alt, rms) <= PARITY_MAX_OVER_RMS:
+                        break
+                    best = min(range(len(cand)), key=lambda c: _beyond_bf16(o[t], alt + cand[c], rms))
+                    alt = alt + cand.pop(best)
+                    used += 1
+            worst = max(worst, _beyond_bf16(o[t], alt, rms))
+        beyond = worst
     ok = bool(routing_ok and act_ok and rel <= PARITY_REL_L2 and beyond <= PARITY_MAX_OVER_RMS and np.isfinite(o).all())
-    return {"batch": b.cfg.name, "tokens_checked": int(len(tokens)), "tokens": int(b.cfg.T),
-            "routing_bit_exact": bool(routing_ok), "activation_codes_bit_exact": bool(act_ok) if "xq" in ref else None,
-            "relL2": rel, "max_over_rms": float(d.max() / rms), "beyond_bf16_over_rms": beyond, "ok": ok}
+    res = {"batch": b.cfg.name, "tokens_checked": int(len(tokens)), "tokens": int(b.cfg.T),
+           "routing_bit_exact": bool(routing_ok), "activation_codes_bit_exact": bool(act_ok) if "xq" in ref else None,
+           "relL2": rel, "max_over_rms": float(d.max() / rms), "beyond_bf16_over_rms": beyond, "ok": ok}
+    if used:
+        res["h_codes_across_a_boundary"] = used
+    return res
 
 
 def cpu_baseline_and_parity(headline, extra, budget_s=6.0):
@@ -297,7 +326,12 @@ def cpu_baseline_and_parity(headline, extra, budget_s=6.0):
                           f"{'activation quantisation, ' if cfg.act != 'bf16' else ''}"
                           f"FP64 expert MLPs of their {cfg.k} experts, combine) x {reps} repeats, {el:.1f} s; "
                           f"weight preparation untimed"}
-    checks = [_parity_check(big, ref, tokens)]
+    def flips(cfg, ref, W, tokens):
+        if cfg.act not in omoe.HQ:                       # h is not quantised: no boundary to cross
+            return None
+        return lambda t: omoe.h_flip_candidates(cfg, ref, W, int(tokens[t]), o)
+
+    checks = [_parity_check(big, ref, tokens, flips(cfg, ref, W, tokens))]
     log(f"[bench] parity {checks[-1]}")
     for b in [b for b in headline if b is not big] + list(extra):
         cfg = b.cfg
@@ -307,12 +341,14 @@ def cpu_baseline_and_parity(headline, extra, budget_s=6.0):
         ids, _ = omoe.route(cfg, logits, o)
         need = sorted(set(ids[tokens].reshape(-1).tolist()))
         log(f"[bench] parity: oracle for {len(tokens)} tokens of {cfg.name} ({len(need)} experts)")
-        ref = omoe.forward_by_expert(cfg, synth.activations(cfg), logits, *weights(cfg, need), tokens=tokens, o=o)
-        checks.append(_parity_check(b, ref, tokens))
+        Wn = weights(cfg, need)
+        ref = omoe.forward_by_expert(cfg, synth.activations(cfg), logits, *Wn, tokens=tokens, o=o)
+        checks.append(_parity_check(b, ref, tokens, flips(cfg, ref, Wn, tokens)))
         log(f"[bench] parity {checks[-1]}")
     parity = {"status": "ok" if all(c["ok"] for c in checks) else "FAILED",
               "bar": "routing and activation codes bit-exact; relL2 <= 5e-3; max |d| beyond the bf16 output "
-                     "rounding <= 2e-2 RMS", "checks": checks}
+                     "rounding <= 2e-2 RMS (quantised-h variants: up to 2 h codes per token on the other side of "
+                     "a rounding boundary they lie within 2e-5 of)", "checks": checks}
     return baseline, parity
 
 

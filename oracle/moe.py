@@ -220,3 +220,61 @@ def forward_by_expert(cfg: synth.MoeConfig, x_bf16: np.ndarray, logits: np.ndarr
         out += ffn(WS1, WS2, s, x_rows, None)
     res["out"] = out
     return res
+
+
+# Variants that quantise h (NVFP4, MXFP8 or per-row FP8 h) decide each h code on an
+# intermediate that the device computes in binary32 arithmetic and the oracle in FP64: an h
+# value within FLIP_REL (relative) of a rounding boundary may take either neighbouring code,
+# and both results are correct. A parity check may take such alternative roundings, each found
+# here on the oracle side (its FP64 h, rounded to binary32 as its own quantiser does, and its
+# quantiser), never from the device.
+FLIP_REL = 2e-5
+
+
+def h_flip_candidates(cfg: synth.MoeConfig, ref: Dict, W, tok: int, o: Optional[Oracle] = None):
+    """Output changes of the alternative roundings of token tok's h elements that lie within
+    FLIP_REL of a code boundary: for each such element of each of the token's experts (its
+    routed picks, then the shared expert), w_j D2[:, i] sign (q' - q) step, with q, q' the
+    element's code value and its neighbour across the boundary and step the element's scale.
+    W = (W1, W2, WS1, WS2) as forward() takes them; ref is forward()'s result (its quantised
+    activation rows cover every token)."""
+    o = o or default()
+    W1, W2, WS1, WS2 = W
+    if cfg.act == "mxfp8":
+        x_t = o.mxfp8_rows(ref["xq"][tok:tok + 1], ref["xs"][tok:tok + 1])[0]
+    elif cfg.act == "fp8":
+        x_t = o.fp8_rows(ref["xq"][tok:tok + 1], ref["xg"][tok:tok + 1])[0]
+    else:
+        x_t = o.dequant_rows(ref["xq"][tok:tok + 1], ref["xs"][tok:tok + 1], ref["xg"][tok:tok + 1])[0]
+    experts = [(W1, W2, int(e), float(wj), cfg.swiglu_limit) for e, wj in zip(ref["ids"][tok], ref["w"][tok])]
+    if cfg.shared:
+        experts.append((WS1, WS2, 0, 1.0, None))
+    e4 = np.array([o.e4m3fn(c) for c in range(0x7F)])        # E4M3 magnitudes of codes 0x00..0x7E
+    e2 = np.array([0, .5, 1, 1.5, 2, 3, 4, 6])                 # E2M1 magnitudes
+    out = []
+    for Wa, Wb, e, wj, lim in experts:
+        h32 = o.expert_h(Wa, Wb, e, x_t, lim).astype(np.float32)
+        D2 = o.decode_projection(Wb, e)                        # [H][I]
+        if cfg.act in ("mxfp8", "fp8"):
+            codes, sc = o.mxfp8_quantize(h32[None]) if cfg.act == "mxfp8" else o.fp8_rows_quantize(h32[None])
+            for i in range(h32.size):
+                c = int(codes[0, i]) & 0x7F
+                step = np.ldexp(1.0, int(sc[0, i // 32]) - 127) if cfg.act == "mxfp8" else float(sc[0])
+                v = abs(float(h32[i])) / step
+                for c2 in (c - 1, c + 1):
+                    if 0 <= c2 <= 0x7E and v > 0 and abs(v - (e4[c] + e4[c2]) / 2) <= FLIP_REL * v:
+                        sgn = -1.0 if h32[i] < 0 else 1.0
+                        out.append(wj * D2[:, i] * sgn * (e4[c2] - e4[c]) * step)
+        else:
+            packed, scales, gs = o.quantize(h32[None], rows_per_gs=1)
+            for i in range(h32.size):
+                c = (int(packed[0, i // 2]) >> (4 * (i & 1))) & 7
+                d = float(np.float32(np.float32(o.e4m3fn(int(scales[0, i // 16]))) * gs[0]))
+                if d == 0:
+                    continue
+                v = abs(float(h32[i])) / d
+                for c2 in (c - 1, c + 1):
+                    if 0 <= c2 <= 7 and v > 0 and abs(v - (e2[c] + e2[c2]) / 2) <= FLIP_REL * v:
+                        sgn = -1.0 if h32[i] < 0 else 1.0
+                        out.append(wj * D2[:, i] * sgn * (e2[c2] - e2[c]) * d)
+    return out

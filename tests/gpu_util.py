@@ -59,7 +59,7 @@ def out_metrics(o_gpu: torch.Tensor, ref: np.ndarray):
 # token over the max bound the check may take up to MAX_FLIPS such alternative roundings of
 # its h elements, each found on the oracle side (its FP64 h and its quantiser), never from
 # the device.
-FLIP_REL = 2e-5
+FLIP_REL = omoe.FLIP_REL
 MAX_FLIPS = 2
 
 
@@ -94,66 +94,10 @@ def check_out(o_gpu, ref, what="", flips=None):
     assert np.all(np.isfinite(g))
 
 
-_E4M3 = None
-
-
-def _e4m3_values():
-    global _E4M3
-    if _E4M3 is None:
-        o = oracle.default()
-        _E4M3 = np.array([o.e4m3fn(c) for c in range(0x7F)])     # magnitudes of codes 0x00..0x7E
-    return _E4M3
-
-
 def h_flip_candidates(case, ref, t):
     """Output changes of the alternative roundings of token t's h elements that lie within
     FLIP_REL of a code boundary (MXFP8, FP8-row or NVFP4 h), from the oracle's FP64 h."""
-    import pins
-    cfg, o = case.cfg, oracle.default()
-    tok = int(case.tokens[t])
-    if cfg.act == "mxfp8":
-        x_t = o.mxfp8_rows(ref["xq"][tok:tok + 1], ref["xs"][tok:tok + 1])[0]
-    elif cfg.act == "fp8":
-        x_t = o.fp8_rows(ref["xq"][tok:tok + 1], ref["xg"][tok:tok + 1])[0]
-    else:
-        x_t = o.dequant_rows(ref["xq"][tok:tok + 1], ref["xs"][tok:tok + 1], ref["xg"][tok:tok + 1])[0]
-    experts = [(case.W[0], case.W[1], int(e), float(wj), cfg.swiglu_limit)
-               for e, wj in zip(ref["ids"][tok], ref["w"][tok])]
-    if cfg.shared:
-        experts.append((case.W[2], case.W[3], 0, 1.0, None))
-    e4 = _e4m3_values()
-    out = []
-    for W1, W2, e, wj, lim in experts:
-        h32 = o.expert_h(W1, W2, e, x_t, lim).astype(np.float32)
-        I = h32.size
-        if W2[2] is None:
-            D2 = pins.decode_mxfp4(W2[0][e], W2[1][e])
-        else:
-            D2 = pins.decode_nvfp4(W2[0][e], W2[1][e], W2[2][e])
-        if cfg.act in ("mxfp8", "fp8"):
-            codes, sc = o.mxfp8_quantize(h32[None]) if cfg.act == "mxfp8" else o.fp8_rows_quantize(h32[None])
-            for i in range(I):
-                c = int(codes[0, i]) & 0x7F
-                step = np.ldexp(1.0, int(sc[0, i // 32]) - 127) if cfg.act == "mxfp8" else float(sc[0])
-                v = abs(float(h32[i])) / step
-                for c2 in (c - 1, c + 1):
-                    if 0 <= c2 <= 0x7E and v > 0 and abs(v - (e4[c] + e4[c2]) / 2) <= FLIP_REL * v:
-                        sgn = -1.0 if h32[i] < 0 else 1.0
-                        out.append(wj * D2[:, i] * sgn * (e4[c2] - e4[c]) * step)
-        else:
-            packed, scales, gs = o.quantize(h32[None], rows_per_gs=1)
-            e2 = np.array([0, .5, 1, 1.5, 2, 3, 4, 6])
-            for i in range(I):
-                c = (int(packed[0, i // 2]) >> (4 * (i & 1))) & 7
-                d = float(np.float32(np.float32(o.e4m3fn(int(scales[0, i // 16]))) * gs[0]))
-                if d == 0:
-                    continue
-                v = abs(float(h32[i])) / d
-                for c2 in (c - 1, c + 1):
-                    if 0 <= c2 <= 7 and v > 0 and abs(v - (e2[c] + e2[c2]) / 2) <= FLIP_REL * v:
-                        sgn = -1.0 if h32[i] < 0 else 1.0
-                        out.append(wj * D2[:, i] * sgn * (e2[c2] - e2[c]) * d)
-    return out
+    return omoe.h_flip_candidates(case.cfg, ref, case.W, int(case.tokens[t]), oracle.default())
 
 
 def gpu_weights(cfg, which):

@@ -43,3 +43,40 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=300)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_parity_gate_h_boundary_allowance():
+    """bench.py's parity gate on a quantised-h variant (oracle side only, no device): an output
+    that takes the other rounding of an h element lying next to a code boundary passes with
+    the allowance and fails without it; a planted error fails either way."""
+    import types
+    import numpy as np
+    import torch
+    import oracle
+    import oracle.moe as omoe
+    from test_tolerance import _w4a8_case
+    case, full = _w4a8_case()
+    ref = full["out"]
+    tokens = case.tokens
+    o = oracle.default()
+    flips = lambda t: omoe.h_flip_candidates(case.cfg, full, case.W, int(tokens[t]), o)   # noqa: E731
+    rms = np.sqrt(np.mean(ref * ref))
+    big = [c for c in flips(129) if np.abs(c).max() > 0.05 * rms]    # the shared expert's boundary element
+    assert len(big) == 1
+
+    def batch(out):
+        b = types.SimpleNamespace(cfg=case.cfg)
+        b.first = {"topk_ids": full["ids"], "expert_counts": full["counts"], "expert_offsets": full["offsets"],
+                   "perm": full["perm"], "topk_weights": full["w"]}
+        b.first_out = torch.from_numpy(out.astype(np.float32)).to(torch.bfloat16)
+        return b
+
+    flipped = ref.copy()
+    flipped[129] += big[0]
+    with_allowance = bench._parity_check(batch(flipped), full, tokens, flips)
+    assert with_allowance["ok"] and with_allowance["h_codes_across_a_boundary"] == 1
+    assert not bench._parity_check(batch(flipped), full, tokens)["ok"]
+    bad = ref.copy()
+    bad[5, 17] += 0.05 * rms
+    assert not bench._parity_check(batch(bad), full, tokens, flips)["ok"]
+    assert bench._parity_check(batch(ref), full, tokens, flips)["ok"]
