@@ -236,10 +236,11 @@ def h_flip_candidates(cfg: synth.MoeConfig, ref: Dict, W, tok: int, o: Optional[
     FLIP_REL of a code boundary: for each such element of each of the token's experts (its
     routed picks, then the shared expert), w_j D2[:, i] sign (q' - q) step, with q, q' the
     element's code value and its neighbour across the boundary and step the element's scale.
-    W = (W1, W2, WS1, WS2) as forward() takes them; ref is forward()'s result (its quantised
-    activation rows cover every token)."""
+    W = (W1, W2) or, with a shared expert, (W1, W2, WS1, WS2) as forward() takes them; ref is
+    forward()'s result (its quantised activation rows cover every token)."""
     o = o or default()
-    W1, W2, WS1, WS2 = W
+    W1, W2 = W[0], W[1]
+    WS1, WS2 = (W[2], W[3]) if cfg.shared else (None, None)
     if cfg.act == "mxfp8":
         x_t = o.mxfp8_rows(ref["xq"][tok:tok + 1], ref["xs"][tok:tok + 1])[0]
     elif cfg.act == "fp8":
