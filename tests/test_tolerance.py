@@ -70,3 +70,20 @@ def test_requant_flip_allowance():
     bad[5, 17] += 0.05 * rms
     with pytest.raises(AssertionError):
         check_out(torch.from_numpy(bad.astype(np.float32)).to(torch.bfloat16), ref, "planted error", flips=flips)
+
+
+def test_flip_candidates_without_shared_expert():
+    """A quantised-h layer without a shared expert holds two projection sets only; the
+    candidate search takes them and finds boundary elements (oracle side, no device)."""
+    import synth
+    import oracle.moe as omoe
+    from gpu_util import Case
+    cfg = synth.MoeConfig("w4a8-noshared", T=40, H=256, I=256, E=8, k=2, shared=0, act="mxfp8", wfmt="mxfp4",
+                          seed=78)
+    case = Case.__new__(Case)
+    case.cfg, case.x, case.logits = cfg, synth.activations(cfg), synth.logits(cfg)
+    case.by_expert = False
+    case.tokens = np.arange(cfg.T, dtype=np.int32)
+    case.W = [tuple(synth.mxfp4_weights(cfg, w, 0, cfg.E)) + (None,) for w in ("w1", "w2")]
+    full = case.reference()
+    assert sum(len(omoe.h_flip_candidates(cfg, full, case.W, t)) for t in range(cfg.T)) > 0
