@@ -162,42 +162,35 @@ __device__ __forceinline__ void route_token_general(const RouteArgs& r, int t, i
       if (e < E && !((kept >> (e / gsz)) & 1ull)) key[i] = 0u;
     }
   }
-  // k picks: each lane keeps its best untaken candidate, only the owner rescans
-  uint32_t taken = 0;
-  auto local_best = [&](uint32_t& bh, uint32_t& bl) {
-    bh = 0u;
-    bl = 0u;
+  // k picks over the 64-bit keys (key, ~e), empty slots 0: each lane's keys sorted
+  // descending in registers, so its best untaken one is always the first; a pick is the wave
+  // maximum of the lanes' first keys, word by word (the largest key, then among its holders
+  // the largest ~e, i.e. the lowest expert id); the winning lane shifts its keys up by one.
+  // Pick j is recorded by lane j; its FP64 score is fetched from the expert's lane afterwards.
+  uint64_t kk[EPL];
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      const int e = lane + WAVE * i;
-      const uint32_t l = ~(uint32_t)e;
-      if (key[i] != 0u && !((taken >> i) & 1u) && (key[i] > bh || (key[i] == bh && l > bl))) {
-        bh = key[i];
-        bl = l;
-      }
-    }
-  };
-  uint32_t ch, cl;
-  local_best(ch, cl);
-  double my_s = 0.0;
+  for (int i = 0; i < EPL; ++i) kk[i] = key[i] != 0u ? pick_key(key[i], lane + WAVE * i) : 0ull;
+  sort_desc<EPL>(kk);
   int my_id = 0;
   for (int j = 0; j < k; ++j) {
-    uint32_t wh = ch, wl = cl;
-    wave_max64(wh, wl);
-    const int e = (int)~wl;
-    const int owner = e & (WAVE - 1), slot = e / WAVE;
-    double se = 0.0;
+    const uint32_t hi = (uint32_t)(kk[0] >> 32), lo = (uint32_t)kk[0];
+    const uint32_t mh = wave_max_u32(hi);
+    const uint32_t ml = wave_max_u32(hi == mh ? lo : 0u);
+    uint32_t m = kk[0] == (((uint64_t)mh << 32) | ml) ? 0xFFFFFFFFu : 0u;
+    asm volatile("" : "+v"(m));   // a bit mask, not a select (see route_token_row)
+    const uint64_t m64 = ((uint64_t)m << 32) | m;
 #pragma unroll
-    for (int i = 0; i < EPL; ++i)
-      if (i == slot) se = sc[i];
-    se = __shfl(se, owner);
-    if (lane == owner) {
-      taken |= 1u << slot;
-      local_best(ch, cl);
-    }
-    if (lane == j) {
-      my_id = e;
-      my_s = se;
+    for (int i = 0; i + 1 < EPL; ++i) kk[i] = (kk[i + 1] & m64) | (kk[i] & ~m64);
+    kk[EPL - 1] &= ~m64;
+    my_id = lane == j ? (int)~ml : my_id;
+  }
+  double my_s = 0.0;
+  {
+    const int owner = my_id & (WAVE - 1), slot = my_id / WAVE;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const double v = __shfl(sc[i], owner);
+      my_s = i == slot ? v : my_s;
     }
   }
   const double sum = wave_sum_f64(lane < k ? my_s : 0.0);

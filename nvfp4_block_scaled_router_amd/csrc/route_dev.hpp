@@ -217,6 +217,15 @@ __device__ __forceinline__ uint32_t row_max_u32(uint32_t v) {
   return dpp_max_u32<0x140>(v);   // row_mirror
 }
 
+// Max over the wave, uniform: the row maxima, then the four rows' through lane reads.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = row_max_u32(v);
+  uint32_t m = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+#pragma unroll
+  for (int r = 16; r < 64; r += 16) m = max(m, (uint32_t)__builtin_amdgcn_readlane((int)v, r));
+  return m;
+}
+
 // Lane r16 of the row holds experts r16, r16+16, ... (EPR = ceil(E/16) <= 16) as 64-bit
 // pick keys, sorted descending in registers, so its best untaken key is always key[0].
 // A pick is the row maximum of the lanes' first keys, found word by word: the largest

@@ -190,19 +190,37 @@ __device__ __forceinline__ void fp8_row_wave(const T* row, int K, uint8_t* codes
   }
 }
 
-// bf16 activation rows -> fp16 for the gate_up MFMA: every row is multiplied by the power
-// of two 2^p that puts its max |x| in [2^14, 2^15) (p clamped to [-126, 126]), which is exact
-// for every element whose scaled magnitude is a normal fp16 (>= 2^-14, i.e. >= 2^-28 of the
-// row maximum; smaller ones round to the fp16 subnormal grid). The epilogue multiplies by
-// xf[r] = 2^-p. One wave per row; xf_out is the row's factor.
-__device__ __forceinline__ void f16_row_wave(const uint16_t* row, int K, uint16_t* out, float* xf_out, int lane) {
+__device__ __forceinline__ float bf16x8_absmax(const u32x4& v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
   float m = 0.0f;
-  for (int c = lane; c < K / 8; c += WAVE) {
-    const u32x4 v = *(const u32x4*)(row + (size_t)c * 8);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      m = fmaxf(m, fmaxf(fabsf(__uint_as_float(w[i] << 16)), fabsf(__uint_as_float(w[i] & 0xFFFF0000u))));
+  for (int i = 0; i < 4; ++i)
+    m = fmaxf(m, fmaxf(fabsf(__uint_as_float(w[i] << 16)), fabsf(__uint_as_float(w[i] & 0xFFFF0000u))));
+  return m;
+}
+__device__ __forceinline__ u32x4 bf16x8_to_f16(const u32x4& v, float scale) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const _Float16 lo = (_Float16)(__uint_as_float(w[i] << 16) * scale);
+    const _Float16 hi = (_Float16)(__uint_as_float(w[i] & 0xFFFF0000u) * scale);
+    o[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+  }
+  return u32x4{o[0], o[1], o[2], o[3]};
+}
+// NV 16-byte pieces per lane per pass, all loaded before any is used (indices clamped to the
+// last piece, so no load is conditional and the repeats change no maximum); a row of at most
+// 64 NV pieces is converted from the registers of its first read.
+template <int NV>
+__device__ __forceinline__ void f16_row_wave_nv(const uint16_t* row, int npc, uint16_t* out, float* xf_out, int lane) {
+  u32x4 v[NV];
+  float m = 0.0f;
+  for (int c0 = 0; c0 < npc; c0 += WAVE * NV) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) v[i] = *(const u32x4*)(row + (size_t)min(c0 + lane + WAVE * i, npc - 1) * 8);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) m = fmaxf(m, bf16x8_absmax(v[i]));
   }
 #pragma unroll
   for (int off = WAVE / 2; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, WAVE));
@@ -211,18 +229,32 @@ __device__ __forceinline__ void f16_row_wave(const uint16_t* row, int K, uint16_
   p = p < -126 ? -126 : (p > 126 ? 126 : p);
   const float scale = __uint_as_float((uint32_t)(p + 127) << 23);
   if (lane == 0) *xf_out = __uint_as_float((uint32_t)(127 - p) << 23);
-  for (int c = lane; c < K / 8; c += WAVE) {
-    const u32x4 v = *(const u32x4*)(row + (size_t)c * 8);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    uint32_t o[4];
+  const bool held = npc <= WAVE * NV;
+  for (int c0 = 0; c0 < npc; c0 += WAVE * NV) {
+    if (!held) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const _Float16 lo = (_Float16)(__uint_as_float(w[i] << 16) * scale);
-      const _Float16 hi = (_Float16)(__uint_as_float(w[i] & 0xFFFF0000u) * scale);
-      o[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+      for (int i = 0; i < NV; ++i) v[i] = *(const u32x4*)(row + (size_t)min(c0 + lane + WAVE * i, npc - 1) * 8);
     }
-    *(u32x4*)(out + (size_t)c * 8) = u32x4{o[0], o[1], o[2], o[3]};
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int c = c0 + lane + WAVE * i;
+      if (c < npc) *(u32x4*)(out + (size_t)c * 8) = bf16x8_to_f16(v[i], scale);
+    }
   }
+}
+// bf16 activation rows -> fp16 for the gate_up MFMA: every row is multiplied by the power
+// of two 2^p that puts its max |x| in [2^14, 2^15) (p clamped to [-126, 126]), which is exact
+// for every element whose scaled magnitude is a normal fp16 (>= 2^-14, i.e. >= 2^-28 of the
+// row maximum; smaller ones round to the fp16 subnormal grid). The epilogue multiplies by
+// xf[r] = 2^-p. One wave per row; xf_out is the row's factor.
+__device__ __forceinline__ void f16_row_wave(const uint16_t* row, int K, uint16_t* out, float* xf_out, int lane) {
+  const int npc = K / 8;
+  if (npc <= WAVE * 2)
+    f16_row_wave_nv<2>(row, npc, out, xf_out, lane);
+  else if (npc <= WAVE * 4)
+    f16_row_wave_nv<4>(row, npc, out, xf_out, lane);
+  else
+    f16_row_wave_nv<8>(row, npc, out, xf_out, lane);
 }
 
 }  // namespace nvmoe
