@@ -316,8 +316,8 @@ __device__ __forceinline__ void offsets_wave(const int* cnt, int* off, int* tl, 
 
 // Small batches (T <= 64, T*k <= 4096): routing, counts, offsets, permutation and tile
 // list in one 1024-thread workgroup, everything in LDS. 64 DPP rows route up to 64 tokens
-// at once (E <= 256; wider expert sets use one wave per token); one wave runs the two
-// scans; global memory is read once (logits) and written at the end. A token's experts
+// at once (E <= 256; wider expert sets use one wave per token); one wave runs the offset and
+// tile-count scans; global memory is read once (logits) and written at the end. A token's experts
 // are distinct, so an expert's rank of token t is the number of earlier tokens in that
 // expert's 64-bit token bitmap.
 template <int EPL>
